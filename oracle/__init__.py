@@ -1,0 +1,168 @@
+"""CPU oracle of the hierarchical KV cache and of its sparse-attention consumer.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library (``hierarchical_kv_cache_amd``) and imports nothing
+from it; the only inputs both sides share come from ``synth``.
+
+* ``Cache``        -- one (request, layer) cache; plain C model in
+                      ``hs_oracle.c`` (stamp-based LRU, sort per step).
+* ``expand_blocks``, ``replay`` -- block-id expansion and shared-layer copy.
+* ``brute``        -- an independently written pure-Python model used to pin
+                      ``Cache`` on exhaustive tiny traces.
+* ``attention``    -- float64 NumPy sparse decode attention.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from . import attention, brute  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "_hso.so")
+_lib = None
+
+ERR_DUP, ERR_RANGE, ERR_CAPACITY = 1, 2, 4
+
+
+class OracleError(ValueError):
+    def __init__(self, code: int):
+        names = [n for b, n in ((ERR_DUP, "duplicate position"), (ERR_RANGE, "position out of range"),
+                                (ERR_CAPACITY, "selection larger than the buffer")) if code & b]
+        super().__init__(", ".join(names) or "error %d" % code)
+        self.code = code
+
+
+def build() -> None:
+    """Compile the C model with gcc."""
+    src = os.path.join(_HERE, "hs_oracle.c")
+    tmp = _SO + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-Wall", "-o", tmp, src])
+    os.replace(tmp, _SO)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    src = os.path.join(_HERE, "hs_oracle.c")
+    if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
+        build()
+    lib = ctypes.CDLL(_SO)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.hso_create.argtypes = [i32, i64, i32, i32]
+    lib.hso_create.restype = vp
+    lib.hso_destroy.argtypes = [vp]
+    lib.hso_destroy.restype = None
+    lib.hso_resolve.argtypes = [vp, vp, i32, i64, vp, vp, vp, vp, vp]
+    lib.hso_resolve.restype = i32
+    lib.hso_append.argtypes = [vp, i64, vp, vp]
+    lib.hso_append.restype = i32
+    lib.hso_replay.argtypes = [vp, vp, i32, vp, vp, i32]
+    lib.hso_replay.restype = None
+    lib.hso_expand_blocks.argtypes = [vp, i32, i32, vp]
+    lib.hso_expand_blocks.restype = None
+    lib.hso_export.argtypes = [vp, vp, vp, vp]
+    lib.hso_export.restype = None
+    for name in ("hso_page_table", "hso_hot"):
+        getattr(lib, name).argtypes = [vp]
+        getattr(lib, name).restype = vp
+    for name in ("hso_newest", "hso_step"):
+        getattr(lib, name).argtypes = [vp]
+        getattr(lib, name).restype = i64
+    _lib = lib
+    return lib
+
+
+def _addr(buf) -> int:
+    if isinstance(buf, int):
+        return buf
+    if not isinstance(buf, np.ndarray) or not buf.flags["C_CONTIGUOUS"]:
+        raise TypeError("expected a C-contiguous numpy array or an address")
+    return buf.ctypes.data
+
+
+class Cache:
+    """One (request, layer) cache: B LRU slots, optional newest slot at index B,
+    page table over ``max_positions`` positions, host mirror of the slot bytes."""
+
+    def __init__(self, B: int, max_positions: int, rec_bytes: int = 1152, newest_slot: bool = False):
+        self._lib = _load()
+        self.B, self.max_positions, self.rec_bytes = B, max_positions, rec_bytes
+        self._h = self._lib.hso_create(B, max_positions, rec_bytes, 1 if newest_slot else 0)
+        if not self._h:
+            raise MemoryError("oracle cache allocation failed")
+
+    def close(self):
+        if self._h:
+            self._lib.hso_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def resolve(self, sel, ctx_len: int, host):
+        """Resolve one selection (token positions).  ``host`` is the layer's
+        [max_positions][rec_bytes] record array (numpy uint8 or address).
+        Returns (out, hits, misses, plan_pos, plan_slot); raises OracleError."""
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        k = sel.size
+        out = np.empty(k, np.int32)
+        ppos = np.empty(k, np.int32)
+        pslot = np.empty(k, np.int32)
+        counts = np.zeros(2, np.int32)
+        err = self._lib.hso_resolve(self._h, sel.ctypes.data, k, ctx_len, _addr(host), out.ctypes.data,
+                                    ppos.ctypes.data, pslot.ctypes.data, counts.ctypes.data)
+        if err:
+            raise OracleError(err)
+        m = int(counts[1])
+        return out, int(counts[0]), m, ppos[:m].copy(), pslot[:m].copy()
+
+    def append(self, pos: int, record: np.ndarray, host=None):
+        rec = np.ascontiguousarray(record, dtype=np.uint8)
+        err = self._lib.hso_append(self._h, pos, rec.ctypes.data, 0 if host is None else _addr(host))
+        if err:
+            raise OracleError(err)
+
+    def export(self) -> dict:
+        slot_pos = np.empty(self.B, np.int32)
+        stamp = np.empty(self.B, np.int64)
+        lru = np.empty(self.B, np.int32)
+        self._lib.hso_export(self._h, slot_pos.ctypes.data, stamp.ctypes.data, lru.ctypes.data)
+        return {"slot_pos": slot_pos, "stamp": stamp, "lru": lru,
+                "newest_pos": int(self._lib.hso_newest(self._h)), "step": int(self._lib.hso_step(self._h))}
+
+    @property
+    def page_table(self) -> np.ndarray:
+        """Live view of the page table (int32 [max_positions]; -1 = host only)."""
+        p = self._lib.hso_page_table(self._h)
+        return np.ctypeslib.as_array(ctypes.cast(p, ctypes.POINTER(ctypes.c_int32)),
+                                     shape=(self.max_positions,))
+
+    @property
+    def hot(self) -> np.ndarray:
+        """Live view of the slot bytes (uint8 [B+1][rec_bytes])."""
+        p = self._lib.hso_hot(self._h)
+        return np.ctypeslib.as_array(ctypes.cast(p, ctypes.POINTER(ctypes.c_uint8)),
+                                     shape=(self.B + 1, self.rec_bytes))
+
+
+def expand_blocks(blocks, block_tokens: int) -> np.ndarray:
+    blocks = np.ascontiguousarray(blocks, dtype=np.int32)
+    out = np.empty(blocks.size * block_tokens, np.int32)
+    _load().hso_expand_blocks(blocks.ctypes.data, blocks.size, block_tokens, out.ctypes.data)
+    return out
+
+
+def replay(plan_pos, plan_slot, host, hot: np.ndarray, rec_bytes: int = 1152) -> None:
+    plan_pos = np.ascontiguousarray(plan_pos, dtype=np.int32)
+    plan_slot = np.ascontiguousarray(plan_slot, dtype=np.int32)
+    _load().hso_replay(plan_pos.ctypes.data, plan_slot.ctypes.data, plan_pos.size, _addr(host),
+                       _addr(hot), rec_bytes)
