@@ -1,0 +1,236 @@
+"""Python binding of libhisparse (hierarchical KV cache for top-k sparse-attention
+decode on MI355X).
+
+The functions below carry the C ABI's names (``include/hisparse.h``) and only
+marshal arguments: integers are device or host addresses, streams are
+``hipStream_t`` handles (``torch.cuda.Stream.cuda_stream``).  Every step of
+the path runs in the HIP library; when it is missing, importing this package
+raises instead of falling back to anything else.
+
+``HiSparse`` is a convenience owner: it allocates the hot buffer and the
+workspace as torch tensors (torch is only the device-memory and stream
+provider) and forwards to the C calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import _build
+
+LIB_PATH = _build.LIB
+
+HS_OK, HS_EINVAL, HS_ENOMEM, HS_EHIP, HS_ESTATE = 0, -1, -2, -3, -4
+HS_CFG_NEWEST_SLOT = 1
+HS_RECORD_PLAN, HS_SKIP_IO = 1, 2
+HS_ERR_DUP, HS_ERR_RANGE = 1, 2
+
+
+class hs_config(ctypes.Structure):
+    _fields_ = [
+        ("num_requests", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("max_positions", ctypes.c_int64),
+        ("record_bytes", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32),
+        ("buffer_slots", ctypes.c_int32),
+        ("layer_group", ctypes.c_int32),
+        ("wgs_per_request", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+HS_STATS_DTYPE = np.dtype([("hits", np.uint32), ("misses", np.uint32), ("error", np.uint32),
+                           ("reserved", np.uint32)])
+
+# every symbol include/hisparse.h declares
+EXPORTS = (
+    "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_append", "hs_prefetch_shared",
+    "hs_wait_layer", "hs_sparse_attn", "hs_export_state", "hs_page_table", "hs_plan", "hs_reset_request",
+    "hs_destroy", "hs_last_error", "hs_resolve_wgs", "hs_probe_host_read", "hs_probe_copy",
+    "hs_probe_empty",
+)
+
+
+class HsError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (status %d)" % (msg, code))
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libhisparse.so is not built: run hierarchical_kv_cache_amd._build.build() "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(hs_config)
+    sig = {
+        "hs_workspace_bytes": (sz, [cfgp]),
+        "hs_create": (i32, [cfgp, vp, vp, ctypes.POINTER(vp)]),
+        "hs_host_pool": (vp, [vp, i32]),
+        "hs_resolve": (i32, [vp, i32, vp, vp, vp, vp, vp, u32, vp]),
+        "hs_append": (i32, [vp, vp, vp, vp, vp]),
+        "hs_prefetch_shared": (i32, [vp, i32, vp, vp]),
+        "hs_wait_layer": (i32, [vp, i32, vp]),
+        "hs_sparse_attn": (i32, [vp, i32, vp, i32, i32, vp, vp, ctypes.c_float, vp, vp]),
+        "hs_export_state": (i32, [vp, i32, vp, vp, vp, vp]),
+        "hs_page_table": (vp, [vp, i32]),
+        "hs_plan": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp)]),
+        "hs_reset_request": (i32, [vp, i32, vp]),
+        "hs_destroy": (i32, [vp]),
+        "hs_last_error": (ctypes.c_char_p, []),
+        "hs_resolve_wgs": (i32, [vp]),
+        "hs_probe_host_read": (i32, [vp, sz, vp, i32, vp]),
+        "hs_probe_copy": (i32, [vp, vp, sz, vp]),
+        "hs_probe_empty": (i32, [vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != HS_OK:
+        raise HsError(status, _lib.hs_last_error().decode())
+
+
+# ---- C ABI, same names -------------------------------------------------------------------
+
+def hs_workspace_bytes(cfg: hs_config) -> int:
+    n = _lib.hs_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise HsError(HS_EINVAL, _lib.hs_last_error().decode())
+    return n
+
+
+def hs_create(cfg: hs_config, d_hot: int, d_workspace: int) -> int:
+    h = ctypes.c_void_p()
+    _check(_lib.hs_create(ctypes.byref(cfg), d_hot, d_workspace, ctypes.byref(h)))
+    return h.value
+
+
+def hs_host_pool(h: int, request: int) -> int:
+    return _lib.hs_host_pool(h, request) or 0
+
+
+def hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, stream):
+    _check(_lib.hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats or None, d_num_reqs or None,
+                           flags, stream or None))
+
+
+def hs_append(h, d_new_kv, d_new_pos, compute, backup):
+    _check(_lib.hs_append(h, d_new_kv, d_new_pos, compute or None, backup or None))
+
+
+def hs_prefetch_shared(h, anchor_layer, compute, prefetch):
+    _check(_lib.hs_prefetch_shared(h, anchor_layer, compute or None, prefetch or None))
+
+
+def hs_wait_layer(h, layer, stream):
+    _check(_lib.hs_wait_layer(h, layer, stream or None))
+
+
+def hs_sparse_attn(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num_reqs, stream):
+    _check(_lib.hs_sparse_attn(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num_reqs or None,
+                               stream or None))
+
+
+def hs_export_state(h, layer, d_slot_pos, d_lru, d_newest, stream):
+    _check(_lib.hs_export_state(h, layer, d_slot_pos or None, d_lru or None, d_newest or None, stream or None))
+
+
+def hs_page_table(h, layer) -> int:
+    p = _lib.hs_page_table(h, layer)
+    if not p:
+        raise HsError(HS_EINVAL, "no page table for layer %d" % layer)
+    return p
+
+
+def hs_plan(h, layer):
+    plan, counts = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(_lib.hs_plan(h, layer, ctypes.byref(plan), ctypes.byref(counts)))
+    return plan.value, counts.value
+
+
+def hs_reset_request(h, request, stream):
+    _check(_lib.hs_reset_request(h, request, stream or None))
+
+
+def hs_destroy(h):
+    _check(_lib.hs_destroy(h))
+
+
+def hs_last_error() -> str:
+    return _lib.hs_last_error().decode()
+
+
+def hs_resolve_wgs(h) -> int:
+    return _lib.hs_resolve_wgs(h)
+
+
+def hs_probe_host_read(host_src, nbytes, d_sink, wgs, stream):
+    _check(_lib.hs_probe_host_read(host_src, nbytes, d_sink, wgs, stream or None))
+
+
+def hs_probe_copy(d_src, d_dst, nbytes, stream):
+    _check(_lib.hs_probe_copy(d_src, d_dst, nbytes, stream or None))
+
+
+def hs_probe_empty(stream):
+    _check(_lib.hs_probe_empty(stream or None))
+
+
+# ---- convenience owner --------------------------------------------------------------------
+
+def make_config(R, L, max_positions, top_k, buffer_slots, record_bytes=1152, block_tokens=1, layer_group=1,
+                wgs_per_request=0, newest_slot=False) -> hs_config:
+    return hs_config(R, L, max_positions, record_bytes, top_k, block_tokens, buffer_slots, layer_group,
+                     wgs_per_request, HS_CFG_NEWEST_SLOT if newest_slot else 0)
+
+
+class HiSparse:
+    """Owns a handle plus the torch tensors it runs on (hot buffer, workspace)."""
+
+    def __init__(self, cfg: hs_config, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.R, self.L, self.B, self.k = cfg.num_requests, cfg.num_layers, cfg.buffer_slots, cfg.top_k
+        self.rec = cfg.record_bytes
+        self.max_positions = cfg.max_positions
+        ws_bytes = hs_workspace_bytes(cfg)
+        self.hot = torch.empty((self.R, self.L, self.B + 1, self.rec), dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        self.h = hs_create(cfg, self.hot.data_ptr(), self.workspace.data_ptr())
+
+    def host_pool(self, request: int) -> np.ndarray:
+        """numpy view [L][max_positions][record_bytes] of request's pinned region."""
+        addr = hs_host_pool(self.h, request)
+        n = self.L * self.max_positions * self.rec
+        buf = (ctypes.c_uint8 * n).from_address(addr)
+        return np.frombuffer(buf, dtype=np.uint8).reshape(self.L, self.max_positions, self.rec)
+
+    def host_pool_address(self, request: int) -> int:
+        return hs_host_pool(self.h, request)
+
+    @property
+    def wgs(self) -> int:
+        return hs_resolve_wgs(self.h)
+
+    def close(self):
+        if getattr(self, "h", None):
+            hs_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

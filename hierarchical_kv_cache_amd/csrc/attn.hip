@@ -1,0 +1,242 @@
+// Sparse decode attention over the slots RESOLVE published ("HiSparse 深度解析"
+// (gentlecold.top) §5.4: attention reads the physical slots aligned with the
+// top-k order).  Per request, H <= 16 query heads share one latent KV record
+// per token: the key is all 576 bf16 of the record, the value its first 512.
+//
+// Work split (split-k over the top-k entries): workgroup (r, s) owns a chunk
+// of request r's entries and walks it in tiles of 64 tokens.  A tile's
+// records are gathered from HBM into LDS; each of the 4 waves computes the
+// 16 x 16 score block of 16 tokens with v_mfma_f32_16x16x32_bf16 (18 k-steps
+// over the 576 key dims), the block keeps a running max / sum per head, and
+// each wave then accumulates P V for its 128 output channels, again on MFMA.
+// P is split into bf16 hi + lo parts so the fp32 probabilities survive the
+// bf16 operand.  The last workgroup of a request to finish merges the
+// per-chunk partials.  With R >= 8 all chunks of a request are placed on one
+// XCD so the merge reads partials from that XCD's L2.
+#include "hs_internal.h"
+
+namespace hs {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int AT = 256;                 // 4 waves
+constexpr int TT = 64;                  // tokens per tile
+constexpr int RS = 1184;                // LDS row stride: 1152 + 32 bytes keeps quarter-waves on
+                                        // disjoint banks in the P V operand reads
+constexpr int KSTEPS = kAttnDk / 32;    // 18
+constexpr int CHUNKS = kAttnDk * 2 / 16;  // 72 16-byte chunks per record
+constexpr int CT = kAttnDv / 4 / 16;    // 8 channel tiles of 16 per wave
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (finite inputs)
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__global__ void __launch_bounds__(AT, 2) attn_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char rows[TT * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t phi[2][16][32];  // [32-token block][head][k]
+  __shared__ __attribute__((aligned(16))) uint16_t plo[2][16][32];
+  __shared__ float smax[4][16];
+  __shared__ float ssum[4][16];
+  __shared__ int s_last;
+
+  int r, s;
+  if (p.R >= 8) {  // chunks of one request on one XCD (workgroups go round-robin over 8 XCDs)
+    const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    r = (loc / p.S) * 8 + x;
+    s = loc % p.S;
+    if (r >= p.R) return;
+  } else {
+    r = blockIdx.x / p.S;
+    s = blockIdx.x % p.S;
+  }
+  if (p.num_reqs && r >= *p.num_reqs) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, col = lane & 15, qd = lane >> 4;
+  const int t_begin = s * p.chunk;
+  const int t_end = min(p.k, t_begin + p.chunk);
+
+  // Q fragments (A operand of the score MFMA): lane holds q[head = col][32 ks + 8 qd + 0..7]
+  bf16x8 qa[KSTEPS];
+  {
+    const uint16_t* qr = p.q + ((size_t)r * p.heads + col) * kAttnDk + qd * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (col < p.heads) qa[ks] = *(const bf16x8*)(qr + ks * 32);
+      else for (int j = 0; j < 8; ++j) qa[ks][j] = (__bf16)0.0f;
+    }
+  }
+
+  const float sl2 = p.scale * 1.4426950408889634f;  // scores kept in log2 units
+  float m_run[4], l_lane[4];
+  f32x4 o[CT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_lane[i] = 0.0f; }
+#pragma unroll
+  for (int c = 0; c < CT; ++c) o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const uint8_t* hot_r = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+  const int32_t* slots_r = p.slots + (size_t)r * p.k;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+
+  for (int t0 = t_begin; t0 < t_end; t0 += TT) {
+    __syncthreads();  // the previous tile is no longer read
+    // gather the tile's records into LDS (18 16-byte chunks per thread)
+#pragma unroll 6
+    for (int f = tid; f < TT * CHUNKS; f += AT) {
+      const int row = f / CHUNKS, c = f - row * CHUNKS;
+      const int tok = t0 + row;
+      u32x4 v = zero4;  // tokens past the end contribute exact zeros
+      if (tok < t_end) {
+        const int sl = slots_r[tok];
+        v = (sl >= 0 && sl <= p.B) ? *((const u32x4*)(hot_r + (size_t)sl * p.rec_bytes) + c) : nan4;
+      }
+      *(u32x4*)(rows + row * RS + c * 16) = v;
+    }
+    __syncthreads();
+
+    // scores of tokens 16w .. 16w+15: lane gets s[head = 4 qd + i][token = col]
+    f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const unsigned char* krow = rows + (16 * w + col) * RS + qd * 16;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 kb = *(const bf16x8*)(krow + ks * 64);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc, 0, 0, 0);
+    }
+    const bool valid = (t0 + 16 * w + col) < t_end;
+    float sv[4], mx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = valid ? sacc[i] * sl2 : -INFINITY;
+      mx[i] = sv[i];
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], d));
+    }
+    if (col == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) smax[w][qd * 4 + i] = mx[i];
+    __syncthreads();
+
+    float alpha[4];
+    const int tl = 16 * w + col;  // token within the tile
+    const int bk = tl >> 5, t32 = tl & 31;
+    const int kk = (t32 & 3) * 8 + (t32 >> 2);  // P V operands pair k index 8 qd + j with token 4 j + qd
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = qd * 4 + i;
+      float mn = fmaxf(fmaxf(smax[0][hh], smax[1][hh]), fmaxf(smax[2][hh], smax[3][hh]));
+      mn = fmaxf(mn, m_run[i]);
+      alpha[i] = exp2f(m_run[i] - mn);
+      m_run[i] = mn;
+      const float pv = exp2f(sv[i] - mn);
+      l_lane[i] = l_lane[i] * alpha[i] + pv;
+      const uint16_t hi = f32_to_bf16_bits(pv);
+      phi[bk][hh][kk] = hi;
+      plo[bk][hh][kk] = f32_to_bf16_bits(pv - bf16_bits_to_f32(hi));
+    }
+    __syncthreads();
+
+    // o[head][channel] += p v over this tile; wave w owns channels 128 w .. 128 w + 127
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[c][i] *= alpha[i];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const bf16x8 ahi = *(const bf16x8*)&phi[b][col][qd * 8];
+      const bf16x8 alo = *(const bf16x8*)&plo[b][col][qd * 8];
+      const unsigned char* vb = rows + (b * 32 + qd) * RS + (w * 128 + col) * 2;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        bf16x8 vv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vv[j] = *(const __bf16*)(vb + 4 * j * RS + c * 32);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, vv, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vv, o[c], 0, 0, 0);
+      }
+    }
+  }
+
+  // per-head sums: over the 16 token columns of a quarter-wave, then over waves
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = l_lane[i];
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d);
+    l_lane[i] = v;
+  }
+  __syncthreads();
+  if (col == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ssum[w][qd * 4 + i] = l_lane[i];
+  __syncthreads();
+
+  if (p.S == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = qd * 4 + i;
+      if (hh >= p.heads) continue;
+      const float inv = 1.0f / (ssum[0][hh] + ssum[1][hh] + ssum[2][hh] + ssum[3][hh]);
+      float* orow = p.out + ((size_t)r * p.heads + hh) * p.value_dim + w * 128 + col;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) orow[c * 16] = o[c][i] * inv;
+    }
+    return;
+  }
+
+  float* part = p.part + ((size_t)r * p.S + s) * kPartStride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = qd * 4 + i;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) part[hh * kAttnDv + w * 128 + c * 16 + col] = o[c][i];
+  }
+  if (w == 0 && col == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = qd * 4 + i;
+      part[16 * kAttnDv + hh] = m_run[i];
+      part[16 * kAttnDv + 16 + hh] = ssum[0][hh] + ssum[1][hh] + ssum[2][hh] + ssum[3][hh];
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&p.counter[r], 1u) == (unsigned)(p.S - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // merge the S partials of request r
+  const float* pr = p.part + (size_t)r * p.S * kPartStride;
+  for (int idx = tid; idx < p.heads * kAttnDv; idx += AT) {
+    const int hh = idx / kAttnDv, c = idx - hh * kAttnDv;
+    float M = -INFINITY;
+    for (int q = 0; q < p.S; ++q) M = fmaxf(M, pr[q * kPartStride + 16 * kAttnDv + hh]);
+    float num = 0.0f, den = 0.0f;
+    for (int q = 0; q < p.S; ++q) {
+      const float* pq = pr + q * kPartStride;
+      const float e = exp2f(pq[16 * kAttnDv + hh] - M);
+      num += e * pq[hh * kAttnDv + c];
+      den += e * pq[16 * kAttnDv + 16 + hh];
+    }
+    p.out[((size_t)r * p.heads + hh) * p.value_dim + c] = num / den;
+  }
+  if (tid == 0) p.counter[r] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
+  const int grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * p.S : p.R * p.S;
+  hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(AT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -1,0 +1,222 @@
+// Byte-moving kernels around RESOLVE: write-through of the newest token,
+// copy-only replay of an anchor's miss plan, metadata init/export, and the
+// link/latency probes used for measurement.
+#include "hs_internal.h"
+
+namespace hs {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCopyThreads = 256;
+
+// Division of a flattened chunk index by the chunks per record (C <= 1024,
+// indices < 2^24): float estimate, then one correction step.
+__device__ __forceinline__ void split_index(int f, int C, float invC, int& j, int& c) {
+  j = (int)((float)f * invC);
+  c = f - j * C;
+  if (c < 0) { --j; c += C; }
+  if (c >= C) { ++j; c -= C; }
+}
+
+// New token -> slot B of every (request, layer); the newest position is set
+// ("HiSparse 深度解析" (gentlecold.top) §3.4: written into the GPU's reserved
+// slot first).  Flattened over (request, layer, 16-byte chunk).
+__global__ void __launch_bounds__(kCopyThreads) append_kernel(AppendParams p) {
+  const int C = p.rec_bytes >> 4;
+  const int per_req = p.L * C;
+  const int total = p.R * per_req;
+  const float invC = 1.0f / (float)per_req;
+  for (int f = blockIdx.x * blockDim.x + threadIdx.x; f < total; f += gridDim.x * blockDim.x) {
+    int r, rest;
+    split_index(f, per_req, invC, r, rest);
+    const int32_t pos = p.new_pos[r];
+    if (pos < 0 || pos >= p.max_positions) continue;  // rejected: this request is left as it was
+    const int l = rest / C, c = rest - l * C;
+    const u32x4* src = (const u32x4*)(p.new_kv + ((size_t)r * p.L + l) * p.rec_bytes) + c;
+    u32x4* dst = (u32x4*)(p.hot + (((size_t)r * p.L + l) * (p.B + 1) + p.B) * p.rec_bytes) + c;
+    *dst = *src;
+    if (rest == 0) p.newest[r] = pos;
+  }
+}
+
+// Slot B -> host pool at the newest position (write-through on the backup
+// stream, gentlecold.top §3.4 and §5.4).  Non-temporal stores into the
+// coherent pinned pool, then a system-scope fence.
+__global__ void __launch_bounds__(kCopyThreads) backup_kernel(AppendParams p) {
+  const int C = p.rec_bytes >> 4;
+  const int per_req = p.L * C;
+  const int total = p.R * per_req;
+  const float invC = 1.0f / (float)per_req;
+  for (int f = blockIdx.x * blockDim.x + threadIdx.x; f < total; f += gridDim.x * blockDim.x) {
+    int r, rest;
+    split_index(f, per_req, invC, r, rest);
+    const int32_t pos = p.new_pos[r];
+    if (pos < 0 || pos >= p.max_positions) continue;
+    const int l = rest / C, c = rest - l * C;
+    const u32x4* src =
+        (const u32x4*)(p.hot + (((size_t)r * p.L + l) * (p.B + 1) + p.B) * p.rec_bytes) + c;
+    u32x4* dst = (u32x4*)(p.host_base[r] + ((size_t)l * p.max_positions + pos) * p.rec_bytes) + c;
+    __builtin_nontemporal_store(*src, dst);
+  }
+  __threadfence_system();
+}
+
+// Copy-only replay of an anchor's miss plan into one shared layer
+// (gentlecold.top §3.6 and §5.6): the same (position, slot) pairs, this
+// layer's own records.  A small fixed number of workgroups strides over the
+// flattened (request, miss, 16-byte chunk) space so the copy leaves most of
+// the GPU to the compute stream.
+__global__ void __launch_bounds__(kCopyThreads) replay_kernel(ReplayParams p) {
+  const int C = p.rec_bytes >> 4;
+  const float invC = 1.0f / (float)C;
+  const int stride = gridDim.x * blockDim.x;
+  const int t0 = blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int U = 4;
+  for (int r = 0; r < p.R; ++r) {
+    const int m = (int)p.ctrl[r * 4 + 2];
+    const int total = m * C;
+    const int32_t* ppos = p.plan + (size_t)r * 2 * p.k;
+    const int32_t* pslot = ppos + p.k;
+    const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
+    uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+    for (int f0 = t0; f0 < total; f0 += stride * U) {
+      u32x4 v[U];
+      int jj[U], cc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int f = f0 + u * stride;
+        if (f < total) {
+          split_index(f, C, invC, jj[u], cc[u]);
+          v[u] = __builtin_nontemporal_load(
+              (const u32x4*)(hbase + (size_t)ppos[jj[u]] * p.rec_bytes) + cc[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (f0 + u * stride < total)
+          *((u32x4*)(dbase + (size_t)pslot[jj[u]] * p.rec_bytes) + cc[u]) = v[u];
+    }
+  }
+}
+
+// Admission state ("HiSparse 深度解析" (gentlecold.top) §5.3, §5.4 release):
+// every slot empty, every position host-only, LRU in slot order, no newest.
+// grid.y = anchor, grid.z = request (or the one request being reset).
+__global__ void __launch_bounds__(kCopyThreads) init_kernel(InitParams p) {
+  const int a = blockIdx.y;
+  const int r = p.request >= 0 ? p.request : (int)blockIdx.z;
+  const size_t ar = (size_t)a * p.R + r;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nt = gridDim.x * blockDim.x;
+  for (int s = t; s < p.B; s += nt) {
+    p.slot_pos[(ar * 2 + 0) * p.B + s] = -1;
+    p.slot_pos[(ar * 2 + 1) * p.B + s] = -1;
+    p.lru[(ar * 2 + 0) * p.Bpad + s] = (int16_t)s;
+    p.lru[(ar * 2 + 1) * p.Bpad + s] = (int16_t)s;
+  }
+  int32_t* pt = p.page_table + ar * (size_t)p.max_positions;
+  for (int64_t q = t; q < p.max_positions; q += nt) pt[q] = -1;
+  if (t == 0) {
+    p.ctrl[ar * 4 + 0] = 0;
+    p.ctrl[ar * 4 + 1] = 0;
+    p.ctrl[ar * 4 + 2] = 0;
+    p.ctrl[ar * 4 + 3] = 0;
+    if (a == 0) p.newest[r] = -1;
+  }
+}
+
+__global__ void __launch_bounds__(kCopyThreads) export_kernel(ExportParams p) {
+  const int r = blockIdx.y;
+  const int cur = p.ctrl[r * 4] & 1;
+  for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < p.B; s += gridDim.x * blockDim.x) {
+    if (p.out_slot_pos) p.out_slot_pos[(size_t)r * p.B + s] = p.slot_pos[((size_t)r * 2 + cur) * p.B + s];
+    if (p.out_lru) p.out_lru[(size_t)r * p.B + s] = p.lru[((size_t)r * 2 + cur) * p.Bpad + s];
+  }
+  if (p.out_newest && blockIdx.x == 0 && threadIdx.x == 0) p.out_newest[r] = p.newest ? p.newest[r] : -1;
+}
+
+template <int U>
+__global__ void __launch_bounds__(kCopyThreads) probe_host_read_kernel(const u32x4* __restrict__ src,
+                                                                       size_t n16, u32x4* sink) {
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t base = tid; base < n16; base += stride * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t idx = base + (size_t)u * stride;
+      v[u] = idx < n16 ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  // keep the loads: a store that is (almost) never taken
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[tid & 1023] = acc;
+}
+
+__global__ void __launch_bounds__(kCopyThreads) probe_copy_kernel(const u32x4* __restrict__ src,
+                                                                  u32x4* __restrict__ dst, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+__global__ void probe_empty_kernel() {}
+
+int grid_for(size_t work, int per_block, int cap) {
+  size_t b = (work + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > (size_t)cap) b = cap;
+  return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+  const size_t work = (size_t)p.R * p.L * (p.rec_bytes >> 4);
+  hipLaunchKernelGGL(append_kernel, dim3(grid_for(work, kCopyThreads, 1024)), dim3(kCopyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_backup(const AppendParams& p, hipStream_t s) {
+  const size_t work = (size_t)p.R * p.L * (p.rec_bytes >> 4);
+  hipLaunchKernelGGL(backup_kernel, dim3(grid_for(work, kCopyThreads, 256)), dim3(kCopyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s) {
+  hipLaunchKernelGGL(replay_kernel, dim3(wgs), dim3(kCopyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_init(const InitParams& p, hipStream_t s) {
+  const int bx = grid_for((size_t)(p.max_positions > p.B ? p.max_positions : p.B), kCopyThreads * 8, 256);
+  dim3 grid(bx, p.A, p.request >= 0 ? 1 : p.R);
+  hipLaunchKernelGGL(init_kernel, grid, dim3(kCopyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_export(const ExportParams& p, hipStream_t s) {
+  dim3 grid(grid_for((size_t)p.B, kCopyThreads, 64), p.R);
+  hipLaunchKernelGGL(export_kernel, grid, dim3(kCopyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_host_read(const void* src, size_t bytes, void* sink, int wgs, hipStream_t s) {
+  hipLaunchKernelGGL(probe_host_read_kernel<8>, dim3(wgs), dim3(kCopyThreads), 0, s,
+                     (const u32x4*)src, bytes / 16, (u32x4*)sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  hipLaunchKernelGGL(probe_copy_kernel, dim3(grid_for(bytes / 16, kCopyThreads, 4096)), dim3(kCopyThreads),
+                     0, s, (const u32x4*)src, (u32x4*)dst, bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_empty(hipStream_t s) {
+  hipLaunchKernelGGL(probe_empty_kernel, dim3(1), dim3(64), 0, s);
+  return hipGetLastError();
+}
+
+}  // namespace hs

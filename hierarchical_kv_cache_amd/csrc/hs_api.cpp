@@ -1,0 +1,473 @@
+// Host side of the C ABI: argument validation, workspace layout, the pinned
+// host pool, stream/event ordering, kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "hs_internal.h"
+
+using namespace hs;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hs_status fail(hs_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+hs_status hip_fail(hipError_t e, const char* what) {
+  return fail(HS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HS_HIP(call)                              \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, #call); \
+  } while (0)
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int64_t x) { int b = 0; while ((int64_t(1) << b) < x) ++b; return b; }
+
+// Offsets (bytes) of every array in the caller's workspace.
+struct Layout {
+  int A = 0;        // anchor layers
+  int Bpad = 0;
+  int S = 1;        // attention chunks per request
+  size_t ctrl = 0, slot_pos = 0, lru = 0, plan = 0, page_table = 0, newest = 0, host_base = 0,
+         attn_part = 0, attn_counter = 0, total = 0;
+};
+
+int attn_chunks(const hs_config& c) {
+  // enough workgroups to cover the GPU's 256 CUs about twice, chunks of >= 64 tokens
+  int S = (512 + c.num_requests - 1) / c.num_requests;
+  const int max_s = (c.top_k + 63) / 64;
+  if (S > max_s) S = max_s;
+  if (S < 1) S = 1;
+  return S;
+}
+
+Layout make_layout(const hs_config& c) {
+  Layout L;
+  const size_t R = c.num_requests, B = c.buffer_slots, k = c.top_k;
+  L.A = (c.num_layers + c.layer_group - 1) / c.layer_group;
+  L.Bpad = (int)align_up(B, 8);
+  L.S = attn_chunks(c);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  L.ctrl = take(size_t(L.A) * R * 4 * sizeof(uint32_t));
+  L.slot_pos = take(size_t(L.A) * R * 2 * B * sizeof(int32_t));
+  L.lru = take(size_t(L.A) * R * 2 * L.Bpad * sizeof(int16_t));
+  L.plan = take(size_t(L.A) * R * 2 * k * sizeof(int32_t));
+  L.page_table = take(size_t(L.A) * R * size_t(c.max_positions) * sizeof(int32_t));
+  L.newest = take(R * sizeof(int32_t));
+  L.host_base = take(R * sizeof(void*));
+  L.attn_part = take(size_t(c.num_layers) * R * L.S * kPartStride * sizeof(float));
+  L.attn_counter = take(size_t(c.num_layers) * R * sizeof(uint32_t));
+  L.total = o;
+  return L;
+}
+
+hs_status validate(const hs_config* c) {
+  if (!c) return fail(HS_EINVAL, "null config");
+  if (c->num_requests < 1 || c->num_requests > 65535) return fail(HS_EINVAL, "num_requests must be in [1, 65535]");
+  if (c->num_layers < 1 || c->num_layers > 4096) return fail(HS_EINVAL, "num_layers must be in [1, 4096]");
+  if (c->record_bytes < 16 || c->record_bytes > kMaxRecordBytes || c->record_bytes % 16)
+    return fail(HS_EINVAL, "record_bytes must be a multiple of 16 in [16, %d]", kMaxRecordBytes);
+  if (c->top_k < 1 || c->top_k > kMaxTopK) return fail(HS_EINVAL, "top_k must be in [1, %d]", kMaxTopK);
+  if (c->buffer_slots < c->top_k || c->buffer_slots > kMaxSlots)
+    return fail(HS_EINVAL, "buffer_slots must be in [top_k, %d]", kMaxSlots);
+  if (c->block_tokens < 1 || !is_pow2(c->block_tokens) || c->block_tokens > 1024 ||
+      c->top_k % c->block_tokens)
+    return fail(HS_EINVAL, "block_tokens must be a power of two <= 1024 dividing top_k");
+  if (c->max_positions < c->top_k || c->max_positions >= (int64_t(1) << 31))
+    return fail(HS_EINVAL, "max_positions must be in [top_k, 2^31)");
+  if (c->layer_group < 1 || c->layer_group > c->num_layers)
+    return fail(HS_EINVAL, "layer_group must be in [1, num_layers]");
+  if (c->wgs_per_request < 0 || c->wgs_per_request > 256)
+    return fail(HS_EINVAL, "wgs_per_request must be in [0, 256]");
+  if (c->flags & ~HS_CFG_NEWEST_SLOT) return fail(HS_EINVAL, "unknown config flags");
+  // every flattened copy index stays below 2^24 (kernels divide it in float)
+  if (int64_t(c->top_k) * (c->record_bytes / 16) >= (int64_t(1) << 24) ||
+      int64_t(c->num_requests) * c->num_layers * (c->record_bytes / 16) >= (int64_t(1) << 24))
+    return fail(HS_EINVAL, "top_k * record_bytes / 16 and R * L * record_bytes / 16 must be < 2^24");
+  return HS_OK;
+}
+
+int resolve_hash_bits(int k) {
+  // table of >= 4k entries: at most a quarter full, short probe chains
+  int bits = ilog2(int64_t(k) * 4);
+  if (bits < 6) bits = 6;
+  return bits;
+}
+
+}  // namespace
+
+struct hs_ctx {
+  hs_config cfg;
+  Layout lay;
+  int G = 1;
+  int hash_bits = 0;
+  size_t lds_bytes = 0;
+  int device = 0;
+  uint8_t* hot = nullptr;
+  uint8_t* ws = nullptr;
+  std::vector<void*> pool;  // per request pinned region
+  hipEvent_t ev_appended = nullptr, ev_backup_done = nullptr;
+  std::vector<hipEvent_t> ev_plan, ev_plan_free, ev_layer;  // per anchor, per anchor, per layer
+  std::vector<char> plan_free_pending;
+  int replay_wgs = 32;
+
+  uint32_t* ctrl(int a) { return (uint32_t*)(ws + lay.ctrl) + size_t(a) * cfg.num_requests * 4; }
+  int32_t* slot_pos(int a) {
+    return (int32_t*)(ws + lay.slot_pos) + size_t(a) * cfg.num_requests * 2 * cfg.buffer_slots;
+  }
+  int16_t* lru(int a) { return (int16_t*)(ws + lay.lru) + size_t(a) * cfg.num_requests * 2 * lay.Bpad; }
+  int32_t* plan(int a) { return (int32_t*)(ws + lay.plan) + size_t(a) * cfg.num_requests * 2 * cfg.top_k; }
+  int32_t* page_table(int a) {
+    return (int32_t*)(ws + lay.page_table) + size_t(a) * cfg.num_requests * size_t(cfg.max_positions);
+  }
+  int32_t* newest() { return (int32_t*)(ws + lay.newest); }
+  const uint8_t* const* host_base() { return (const uint8_t* const*)(ws + lay.host_base); }
+  float* attn_part(int l) {
+    return (float*)(ws + lay.attn_part) + size_t(l) * cfg.num_requests * lay.S * kPartStride;
+  }
+  uint32_t* attn_counter(int l) { return (uint32_t*)(ws + lay.attn_counter) + size_t(l) * cfg.num_requests; }
+  int64_t host_layer_off(int l) const { return int64_t(l) * cfg.max_positions * cfg.record_bytes; }
+  int64_t hot_req_stride() const { return int64_t(cfg.num_layers) * (cfg.buffer_slots + 1) * cfg.record_bytes; }
+  int64_t hot_layer_off(int l) const { return int64_t(l) * (cfg.buffer_slots + 1) * cfg.record_bytes; }
+  bool is_anchor(int l) const { return l % cfg.layer_group == 0; }
+};
+
+namespace {
+
+void destroy_events(hs_ctx* h) {
+  if (h->ev_appended) (void)hipEventDestroy(h->ev_appended);
+  if (h->ev_backup_done) (void)hipEventDestroy(h->ev_backup_done);
+  for (auto e : h->ev_plan) if (e) (void)hipEventDestroy(e);
+  for (auto e : h->ev_plan_free) if (e) (void)hipEventDestroy(e);
+  for (auto e : h->ev_layer) if (e) (void)hipEventDestroy(e);
+}
+
+void free_ctx(hs_ctx* h) {
+  if (!h) return;
+  destroy_events(h);
+  for (void* p : h->pool) if (p) (void)hipHostFree(p);
+  delete h;
+}
+
+hs_status check_handle(hs_ctx* h) {
+  if (!h) return fail(HS_EINVAL, "null handle");
+  return HS_OK;
+}
+
+hs_status check_layer(hs_ctx* h, int32_t layer) {
+  if (layer < 0 || layer >= h->cfg.num_layers) return fail(HS_EINVAL, "layer %d out of range", layer);
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hs_workspace_bytes(const hs_config* cfg) {
+  if (validate(cfg) != HS_OK) return 0;
+  return make_layout(*cfg).total;
+}
+
+hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_handle* out) {
+  if (!out) return fail(HS_EINVAL, "null output handle");
+  *out = nullptr;
+  hs_status st = validate(cfg);
+  if (st != HS_OK) return st;
+  if (!d_hot || !d_workspace) return fail(HS_EINVAL, "null hot buffer or workspace");
+  if ((uintptr_t)d_hot % 16 || (uintptr_t)d_workspace % 256)
+    return fail(HS_EINVAL, "hot buffer must be 16-byte and workspace 256-byte aligned");
+
+  hs_ctx* h = new (std::nothrow) hs_ctx();
+  if (!h) return fail(HS_ENOMEM, "handle allocation failed");
+  h->cfg = *cfg;
+  h->lay = make_layout(*cfg);
+  h->hot = (uint8_t*)d_hot;
+  h->ws = (uint8_t*)d_workspace;
+  h->hash_bits = resolve_hash_bits(cfg->top_k);
+  h->lds_bytes = resolve_lds(cfg->top_k, cfg->buffer_slots, h->hash_bits).total;
+  if (cfg->wgs_per_request > 0) {
+    h->G = cfg->wgs_per_request;
+  } else {
+    // enough workgroups per request to keep the host link busy on a miss-heavy step
+    int G = 128 / cfg->num_requests;
+    h->G = G < 1 ? 1 : (G > 32 ? 32 : G);
+  }
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetDevice"); }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, h->device);
+  if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetDeviceProperties"); }
+  if (h->lds_bytes > prop.sharedMemPerBlock) {
+    size_t need = h->lds_bytes;
+    free_ctx(h);
+    return fail(HS_EINVAL, "resolve needs %zu bytes of LDS, device allows %zu", need, (size_t)prop.sharedMemPerBlock);
+  }
+  // the limit is per kernel, not per handle: allow the device maximum once
+  e = set_resolve_lds_limit(prop.sharedMemPerBlock);
+  if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipFuncSetAttribute(resolve)"); }
+
+  // pinned host pool: one allocation per request (the driver refuses single pins near 80 GiB)
+  const size_t per_req = size_t(cfg->num_layers) * size_t(cfg->max_positions) * size_t(cfg->record_bytes);
+  h->pool.assign(cfg->num_requests, nullptr);
+  std::vector<const void*> dev_bases(cfg->num_requests);
+  for (int r = 0; r < cfg->num_requests; ++r) {
+    e = hipHostMalloc(&h->pool[r], per_req, hipHostMallocCoherent | hipHostMallocMapped);
+    if (e != hipSuccess) {
+      h->pool[r] = nullptr;
+      (void)hipGetLastError();
+      free_ctx(h);
+      return fail(HS_ENOMEM, "pinning %zu bytes for request %d failed: %s", per_req, r, hipGetErrorString(e));
+    }
+    void* dptr = nullptr;
+    e = hipHostGetDevicePointer(&dptr, h->pool[r], 0);
+    if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipHostGetDevicePointer"); }
+    dev_bases[r] = dptr;
+  }
+
+  // events (timing disabled: ordering only)
+  const int A = h->lay.A;
+  h->ev_plan.assign(A, nullptr);
+  h->ev_plan_free.assign(A, nullptr);
+  h->plan_free_pending.assign(A, 0);
+  h->ev_layer.assign(cfg->num_layers, nullptr);
+  auto mk = [&](hipEvent_t* ev) { return hipEventCreateWithFlags(ev, hipEventDisableTiming); };
+  if ((e = mk(&h->ev_appended)) != hipSuccess || (e = mk(&h->ev_backup_done)) != hipSuccess) {
+    free_ctx(h);
+    return hip_fail(e, "hipEventCreate");
+  }
+  for (int a = 0; a < A; ++a)
+    if ((e = mk(&h->ev_plan[a])) != hipSuccess || (e = mk(&h->ev_plan_free[a])) != hipSuccess) {
+      free_ctx(h);
+      return hip_fail(e, "hipEventCreate");
+    }
+  for (int l = 0; l < cfg->num_layers; ++l)
+    if (!h->is_anchor(l) && (e = mk(&h->ev_layer[l])) != hipSuccess) {
+      free_ctx(h);
+      return hip_fail(e, "hipEventCreate");
+    }
+
+  // workspace: zero, then the admission state; host base table
+  e = hipMemset(h->ws, 0, h->lay.total);
+  if (e == hipSuccess)
+    e = hipMemcpy(h->ws + h->lay.host_base, dev_bases.data(), sizeof(void*) * cfg->num_requests,
+                  hipMemcpyHostToDevice);
+  if (e == hipSuccess) {
+    InitParams ip{};
+    ip.ctrl = h->ctrl(0); ip.slot_pos = h->slot_pos(0); ip.lru = h->lru(0);
+    ip.page_table = h->page_table(0); ip.newest = h->newest();
+    ip.max_positions = cfg->max_positions; ip.R = cfg->num_requests; ip.B = cfg->buffer_slots;
+    ip.Bpad = h->lay.Bpad; ip.A = A; ip.request = -1;
+    e = launch_init(ip, nullptr);
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "workspace initialisation"); }
+  *out = h;
+  g_last_error.clear();
+  return HS_OK;
+}
+
+void* hs_host_pool(hs_handle h, int32_t request) {
+  if (!h || request < 0 || request >= h->cfg.num_requests) return nullptr;
+  return h->pool[request];
+}
+
+int32_t hs_resolve_wgs(hs_handle h) { return h ? h->G : 0; }
+
+hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
+                     int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs, uint32_t flags,
+                     void* stream) {
+  hs_status st;
+  if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
+  if (!h->is_anchor(layer))
+    return fail(HS_ESTATE, "layer %d shares its anchor's selection: use hs_prefetch_shared", layer);
+  if (!d_sel || !d_ctx_len || !d_slots_out) return fail(HS_EINVAL, "null selection, ctx_len or output");
+  if (flags & ~(HS_RECORD_PLAN | HS_SKIP_IO)) return fail(HS_EINVAL, "unknown resolve flags");
+  hipStream_t s = (hipStream_t)stream;
+  const int a = layer / h->cfg.layer_group;
+  if ((flags & HS_RECORD_PLAN) && h->plan_free_pending[a]) {
+    // the previous plan of this anchor must be replayed before it is overwritten
+    HS_HIP(hipStreamWaitEvent(s, h->ev_plan_free[a], 0));
+  }
+  ResolveParams p{};
+  p.sel = d_sel; p.ctx_len = d_ctx_len; p.out = d_slots_out; p.stats = d_stats; p.num_reqs = d_num_reqs;
+  p.ctrl = h->ctrl(a); p.slot_pos = h->slot_pos(a); p.lru = h->lru(a); p.plan = h->plan(a);
+  p.page_table = h->page_table(a); p.newest = h->newest(); p.host_base = h->host_base(); p.hot = h->hot;
+  p.host_layer_off = h->host_layer_off(layer); p.hot_req_stride = h->hot_req_stride();
+  p.hot_layer_off = h->hot_layer_off(layer); p.max_positions = h->cfg.max_positions;
+  p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad; p.k = h->cfg.top_k;
+  p.kb = h->cfg.top_k / h->cfg.block_tokens; p.bt_shift = ilog2(h->cfg.block_tokens);
+  p.rec_bytes = h->cfg.record_bytes; p.G = h->G; p.hash_bits = h->hash_bits;
+  p.flags = flags | ((h->cfg.flags & HS_CFG_NEWEST_SLOT) ? kHasNewest : 0u);
+  HS_HIP(launch_resolve(p, h->lds_bytes, s));
+  return HS_OK;
+}
+
+hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos, void* compute, void* backup) {
+  hs_status st;
+  if ((st = check_handle(h))) return st;
+  if (!(h->cfg.flags & HS_CFG_NEWEST_SLOT)) return fail(HS_ESTATE, "hs_append needs HS_CFG_NEWEST_SLOT");
+  if (!d_new_kv || !d_new_pos) return fail(HS_EINVAL, "null new record or position");
+  if (compute == backup) return fail(HS_EINVAL, "write-through needs a backup stream distinct from compute");
+  hipStream_t cs = (hipStream_t)compute, bs = (hipStream_t)backup;
+  AppendParams p{};
+  p.new_kv = (const uint8_t*)d_new_kv; p.new_pos = d_new_pos; p.newest = h->newest(); p.hot = h->hot;
+  p.host_base = h->host_base(); p.max_positions = h->cfg.max_positions; p.R = h->cfg.num_requests;
+  p.L = h->cfg.num_layers; p.B = h->cfg.buffer_slots; p.rec_bytes = h->cfg.record_bytes;
+  // slot B may only be overwritten once the previous write-through has read it (and then every
+  // later fetch of the previous newest position finds its bytes on the host)
+  HS_HIP(hipStreamWaitEvent(cs, h->ev_backup_done, 0));
+  HS_HIP(launch_append(p, cs));
+  HS_HIP(hipEventRecord(h->ev_appended, cs));
+  HS_HIP(hipStreamWaitEvent(bs, h->ev_appended, 0));
+  HS_HIP(launch_backup(p, bs));
+  HS_HIP(hipEventRecord(h->ev_backup_done, bs));
+  return HS_OK;
+}
+
+hs_status hs_prefetch_shared(hs_handle h, int32_t anchor_layer, void* compute, void* prefetch) {
+  hs_status st;
+  if ((st = check_handle(h)) || (st = check_layer(h, anchor_layer))) return st;
+  if (!h->is_anchor(anchor_layer)) return fail(HS_EINVAL, "layer %d is not an anchor", anchor_layer);
+  const int a = anchor_layer / h->cfg.layer_group;
+  const int last = anchor_layer + h->cfg.layer_group - 1 < h->cfg.num_layers
+                       ? anchor_layer + h->cfg.layer_group - 1 : h->cfg.num_layers - 1;
+  if (last == anchor_layer) return HS_OK;  // no shared layers
+  hipStream_t cs = (hipStream_t)compute, ps = (hipStream_t)prefetch;
+  HS_HIP(hipEventRecord(h->ev_plan[a], cs));
+  HS_HIP(hipStreamWaitEvent(ps, h->ev_plan[a], 0));
+  for (int l = anchor_layer + 1; l <= last; ++l) {
+    ReplayParams p{};
+    p.plan = h->plan(a); p.ctrl = h->ctrl(a); p.host_base = h->host_base(); p.hot = h->hot;
+    p.host_layer_off = h->host_layer_off(l); p.hot_req_stride = h->hot_req_stride();
+    p.hot_layer_off = h->hot_layer_off(l); p.R = h->cfg.num_requests; p.k = h->cfg.top_k;
+    p.rec_bytes = h->cfg.record_bytes;
+    HS_HIP(launch_replay(p, h->replay_wgs, ps));
+    HS_HIP(hipEventRecord(h->ev_layer[l], ps));
+  }
+  HS_HIP(hipEventRecord(h->ev_plan_free[a], ps));
+  h->plan_free_pending[a] = 1;
+  return HS_OK;
+}
+
+hs_status hs_wait_layer(hs_handle h, int32_t layer, void* stream) {
+  hs_status st;
+  if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
+  if (h->is_anchor(layer)) return HS_OK;  // an anchor's bytes are in place when its resolve ends
+  HS_HIP(hipStreamWaitEvent((hipStream_t)stream, h->ev_layer[layer], 0));
+  return HS_OK;
+}
+
+hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t heads, int32_t value_dim,
+                         const int32_t* d_slots, float* d_out, float scale, const int32_t* d_num_reqs,
+                         void* stream) {
+  hs_status st;
+  if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
+  if (h->cfg.record_bytes != kAttnDk * 2) return fail(HS_EINVAL, "attention needs 576-element bf16 records");
+  if (heads < 1 || heads > kAttnMaxHeads) return fail(HS_EINVAL, "heads must be in [1, %d]", kAttnMaxHeads);
+  if (value_dim != kAttnDv) return fail(HS_EINVAL, "value_dim must be %d", kAttnDv);
+  if (!d_q || !d_slots || !d_out) return fail(HS_EINVAL, "null q, slots or output");
+  if ((uintptr_t)d_q % 16) return fail(HS_EINVAL, "q must be 16-byte aligned");
+  AttnParams p{};
+  p.q = (const uint16_t*)d_q; p.slots = d_slots; p.out = d_out; p.part = h->attn_part(layer);
+  p.counter = h->attn_counter(layer); p.num_reqs = d_num_reqs; p.hot = h->hot;
+  p.hot_req_stride = h->hot_req_stride(); p.hot_layer_off = h->hot_layer_off(layer);
+  p.R = h->cfg.num_requests; p.k = h->cfg.top_k; p.B = h->cfg.buffer_slots; p.heads = heads;
+  p.value_dim = value_dim; p.S = h->lay.S;
+  p.chunk = (int)align_up((size_t)((h->cfg.top_k + p.S - 1) / p.S), 64);
+  p.S = (h->cfg.top_k + p.chunk - 1) / p.chunk;  // no empty chunk
+  p.rec_bytes = h->cfg.record_bytes; p.scale = scale;
+  HS_HIP(launch_attn(p, (hipStream_t)stream));
+  return HS_OK;
+}
+
+hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32_t* d_lru, int32_t* d_newest,
+                          void* stream) {
+  hs_status st;
+  if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
+  if (!h->is_anchor(layer)) return fail(HS_ESTATE, "layer %d has no metadata of its own", layer);
+  const int a = layer / h->cfg.layer_group;
+  ExportParams p{};
+  p.ctrl = h->ctrl(a); p.slot_pos = h->slot_pos(a); p.lru = h->lru(a);
+  p.newest = (h->cfg.flags & HS_CFG_NEWEST_SLOT) ? h->newest() : nullptr;
+  p.out_slot_pos = d_slot_pos; p.out_lru = d_lru; p.out_newest = d_newest;
+  p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad;
+  HS_HIP(launch_export(p, (hipStream_t)stream));
+  return HS_OK;
+}
+
+const int32_t* hs_page_table(hs_handle h, int32_t layer) {
+  if (!h || layer < 0 || layer >= h->cfg.num_layers || !h->is_anchor(layer)) return nullptr;
+  return h->page_table(layer / h->cfg.layer_group);
+}
+
+hs_status hs_plan(hs_handle h, int32_t layer, const int32_t** d_plan, const uint32_t** d_counts) {
+  hs_status st;
+  if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
+  if (!h->is_anchor(layer)) return fail(HS_ESTATE, "layer %d has no plan of its own", layer);
+  const int a = layer / h->cfg.layer_group;
+  if (d_plan) *d_plan = h->plan(a);
+  if (d_counts) *d_counts = h->ctrl(a) + 2;
+  return HS_OK;
+}
+
+hs_status hs_reset_request(hs_handle h, int32_t request, void* stream) {
+  hs_status st;
+  if ((st = check_handle(h))) return st;
+  if (request < 0 || request >= h->cfg.num_requests) return fail(HS_EINVAL, "request out of range");
+  InitParams ip{};
+  ip.ctrl = h->ctrl(0); ip.slot_pos = h->slot_pos(0); ip.lru = h->lru(0); ip.page_table = h->page_table(0);
+  ip.newest = h->newest(); ip.max_positions = h->cfg.max_positions; ip.R = h->cfg.num_requests;
+  ip.B = h->cfg.buffer_slots; ip.Bpad = h->lay.Bpad; ip.A = h->lay.A; ip.request = request;
+  HS_HIP(launch_init(ip, (hipStream_t)stream));
+  return HS_OK;
+}
+
+hs_status hs_destroy(hs_handle h) {
+  if (!h) return HS_OK;
+  // the library's own work (write-through into the pool, replays) must end before the pool goes
+  hipError_t e = hipEventSynchronize(h->ev_backup_done);
+  for (size_t a = 0; e == hipSuccess && a < h->ev_plan_free.size(); ++a)
+    e = hipEventSynchronize(h->ev_plan_free[a]);
+  free_ctx(h);
+  if (e != hipSuccess) return hip_fail(e, "hs_destroy: waiting for library events");
+  return HS_OK;
+}
+
+const char* hs_last_error(void) { return g_last_error.c_str(); }
+
+hs_status hs_probe_host_read(const void* host_src, size_t bytes, void* d_sink, int32_t wgs, void* stream) {
+  if (!host_src || !d_sink || wgs < 1 || bytes % 16) return fail(HS_EINVAL, "bad probe arguments");
+  HS_HIP(launch_probe_host_read(host_src, bytes, d_sink, wgs, (hipStream_t)stream));
+  return HS_OK;
+}
+
+hs_status hs_probe_copy(const void* d_src, void* d_dst, size_t bytes, void* stream) {
+  if (!d_src || !d_dst || bytes % 16) return fail(HS_EINVAL, "bad probe arguments");
+  HS_HIP(launch_probe_copy(d_src, d_dst, bytes, (hipStream_t)stream));
+  return HS_OK;
+}
+
+hs_status hs_probe_empty(void* stream) {
+  HS_HIP(launch_probe_empty((hipStream_t)stream));
+  return HS_OK;
+}
+
+}  // extern "C"

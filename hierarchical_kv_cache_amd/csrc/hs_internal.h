@@ -1,0 +1,137 @@
+// Internal declarations shared by the host API and the kernels of libhisparse.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hisparse.h"
+
+namespace hs {
+
+constexpr int kResolveThreads = 1024;  // 16 wave64s: one workgroup resolves one request
+constexpr int kMaxScanPasses = 16;     // block scans cover up to 16 * 1024 elements (B, k <= 16384)
+constexpr int kMaxSlots = 16384;
+constexpr int kMaxTopK = 16384;
+constexpr int kMaxRecordBytes = 16384;
+constexpr uint32_t kHasNewest = 1u << 8;  // internal resolve flag: slot B holds the newest token
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// LDS carve-up of the resolve kernel (shared by host sizing and device code).
+struct ResolveLds {
+  size_t hkey, selp, selslot, hval, victim, missidx, sflag, scratch, total;
+};
+__host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits) {
+  ResolveLds L;
+  size_t o = 0;
+  const size_t H = size_t(1) << hash_bits;
+  L.hkey = o;    o = align_up(o + 4 * H, 16);
+  L.selp = o;    o = align_up(o + 4 * size_t(k), 16);
+  L.selslot = o; o = align_up(o + 4 * size_t(k), 16);
+  L.hval = o;    o = align_up(o + 2 * H, 16);
+  L.victim = o;  o = align_up(o + 2 * size_t(k), 16);
+  L.missidx = o; o = align_up(o + 2 * size_t(k), 16);
+  L.sflag = o;   o = align_up(o + size_t(B), 16);
+  L.scratch = o; o = align_up(o + 4 * size_t(kMaxScanPasses * (kResolveThreads / 64) + 8), 16);
+  L.total = o;
+  return L;
+}
+
+// Per-anchor metadata in the caller's workspace.  ctrl per request:
+// [0] epoch (which ping-pong half is current), [1] workgroups arrived this launch,
+// [2] miss-plan count, [3] unused.
+struct ResolveParams {
+  const int32_t* sel;        // [R][kb]
+  const int32_t* ctx_len;    // [R]
+  int32_t* out;              // [R][k]
+  hs_stats* stats;           // [R] or null
+  const int32_t* num_reqs;   // scalar or null
+  uint32_t* ctrl;            // [R][4]
+  int32_t* slot_pos;         // [R][2][B]
+  int16_t* lru;              // [R][2][Bpad]
+  int32_t* plan;             // [R][2][k]
+  int32_t* page_table;       // [R][max_positions]
+  const int32_t* newest;     // [R]
+  const uint8_t* const* host_base;  // [R] device-usable addresses of each request's host region
+  uint8_t* hot;              // hot buffer base [R][L][B+1][rec]
+  int64_t host_layer_off;    // layer offset inside a request's host region (bytes)
+  int64_t hot_req_stride;    // bytes per request in the hot buffer
+  int64_t hot_layer_off;     // layer offset inside a request's hot buffer (bytes)
+  int64_t max_positions;
+  int32_t R, B, Bpad, k, kb, bt_shift, rec_bytes, G, hash_bits;
+  uint32_t flags;            // HS_RECORD_PLAN | HS_SKIP_IO | kHasNewest
+};
+
+struct AppendParams {
+  const uint8_t* new_kv;     // [R][L][rec]
+  const int32_t* new_pos;    // [R]
+  int32_t* newest;           // [R]
+  uint8_t* hot;
+  const uint8_t* const* host_base;
+  int64_t max_positions;
+  int32_t R, L, B, rec_bytes;
+};
+
+struct ReplayParams {
+  const int32_t* plan;       // anchor's [R][2][k]
+  const uint32_t* ctrl;      // anchor's [R][4]
+  const uint8_t* const* host_base;
+  uint8_t* hot;
+  int64_t host_layer_off, hot_req_stride, hot_layer_off;
+  int32_t R, k, rec_bytes;
+};
+
+struct AttnParams {
+  const uint16_t* q;         // [R][heads][576] bf16
+  const int32_t* slots;      // [R][k]
+  float* out;                // [R][heads][value_dim]
+  float* part;               // [R][S][kPartStride] partial results
+  uint32_t* counter;         // [R] workgroups done (reset by the combining workgroup)
+  const int32_t* num_reqs;
+  const uint8_t* hot;        // layer 0 base
+  int64_t hot_req_stride, hot_layer_off;
+  int32_t R, k, B, heads, value_dim, S, chunk, rec_bytes;
+  float scale;
+};
+
+struct ExportParams {
+  const uint32_t* ctrl;
+  const int32_t* slot_pos;
+  const int16_t* lru;
+  const int32_t* newest;
+  int32_t* out_slot_pos;
+  int32_t* out_lru;
+  int32_t* out_newest;
+  int32_t R, B, Bpad;
+};
+
+struct InitParams {
+  uint32_t* ctrl;
+  int32_t* slot_pos;
+  int16_t* lru;
+  int32_t* page_table;
+  int32_t* newest;
+  int64_t max_positions;
+  int32_t R, B, Bpad, A, request;  // request < 0: all
+};
+
+hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s);
+hipError_t set_resolve_lds_limit(size_t lds_bytes);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_backup(const AppendParams& p, hipStream_t s);
+hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s);
+hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_export(const ExportParams& p, hipStream_t s);
+hipError_t launch_init(const InitParams& p, hipStream_t s);
+hipError_t launch_probe_host_read(const void* src, size_t bytes, void* sink, int wgs, hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_probe_empty(hipStream_t s);
+
+// attention partial record: [16][512] output accumulators, then [16] max, [16] sum
+constexpr int kAttnMaxHeads = 16;
+constexpr int kAttnDk = 576;
+constexpr int kAttnDv = 512;
+constexpr int kPartStride = kAttnMaxHeads * kAttnDv + 2 * kAttnMaxHeads;
+
+}  // namespace hs

@@ -1,0 +1,218 @@
+/*
+ * hisparse.h -- C ABI of the hierarchical KV cache for top-k sparse-attention
+ * decode on AMD Instinct MI355X (gfx950).
+ *
+ * What it computes is defined on these pages:
+ *   [GC]  "HiSparse 深度解析：论文、SGLang 实现与 vLLM Hybrid HiSparse"
+ *         (gentlecold.top)
+ *   [VD]  "HiSparse local KV offload architecture" (docs.vllm.ai)
+ *   [NJ]  "推理系统基础设施手记（六）：HiSparse" (naphjohn.github.io)
+ *   [KJ]  "HiSparse：稀疏注意力的分层 KV Cache 管理" (notes.kuangjux.top)
+ *
+ * Model ([GC] §3.2, [NJ] §2 and Fig. 3): the full KV history of every
+ * (request, layer) lives in pinned host memory and is authoritative.  Each
+ * (request, layer) also owns B device slots in HBM (B >= k), a page table
+ * position -> slot (or host only) and an LRU order of its slots.  One call per
+ * layer (RESOLVE, [GC] §3.5) turns the k selected logical positions into the
+ * k physical slots, fetching the records that miss straight from host memory.
+ *
+ * Conventions
+ *   - "device" pointers point to GPU memory (HBM); "host" pointers to host
+ *     memory.  Streams are hipStream_t passed as void*; NULL is the null stream.
+ *   - Every call that takes a stream is asynchronous on it and performs no
+ *     device-to-host readback.  Argument and state errors are detected on the
+ *     host and returned synchronously (nothing is enqueued then).  Data errors
+ *     (bad positions) are detected on the device and reported in
+ *     hs_stats.error; they are never read back by the library.
+ *   - The caller owns the hot buffer, the workspace and all streams; the
+ *     library owns the pinned host pool and its events.
+ *   - Positions and slot indices are int32.  B <= 32767, top_k <= 16384,
+ *     max_positions < 2^31, record_bytes a multiple of 16.
+ *   - A handle may be used from one host thread at a time.
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hs_ctx* hs_handle;
+typedef int32_t hs_status;
+
+#define HS_OK 0
+#define HS_EINVAL (-1) /* bad argument or configuration */
+#define HS_ENOMEM (-2) /* pinned host allocation failed */
+#define HS_EHIP (-3)   /* a HIP runtime call failed; see hs_last_error() */
+#define HS_ESTATE (-4) /* call not valid for this handle or layer */
+
+/* hs_config.flags */
+#define HS_CFG_NEWEST_SLOT 1u /* slot B of every (request, layer) holds the newest token ([GC] §3.4, §5.2) */
+
+/* hs_resolve flags ([GC] §5.5: compile-time switches of the pages' kernel) */
+#define HS_RECORD_PLAN 1u /* anchor layer: record the miss plan for its shared layers ([GC] §3.6, §5.5) */
+#define HS_SKIP_IO 2u     /* timing aid ([GC] §4.4, §5.6 no-IO oracle): all metadata as usual, no record
+                             bytes move, so the hot buffer is stale afterwards */
+
+/* hs_stats.error bits */
+#define HS_ERR_DUP 1u   /* a position (or block) selected twice */
+#define HS_ERR_RANGE 2u /* a position outside [0, ctx_len) */
+
+typedef struct {
+  int32_t num_requests;    /* R: requests resolved together in one launch per layer */
+  int32_t num_layers;      /* L */
+  int64_t max_positions;   /* positions per (request, layer) in the host pool */
+  int32_t record_bytes;    /* bytes of one token's KV record (1152 = 576 bf16) */
+  int32_t top_k;           /* k: selected tokens per (request, layer, call) */
+  int32_t block_tokens;    /* 1: selections are token positions; n > 1 (power of two): block ids of
+                              n tokens, expanded in the kernel ([GC] §5.5) */
+  int32_t buffer_slots;    /* B: LRU slots per (request, layer), top_k <= B */
+  int32_t layer_group;     /* 1: every layer resolves its own selection.  g > 1: layers g*i are
+                              anchors and layers g*i+1 .. g*i+g-1 share the anchor's selection and
+                              slot layout ([GC] §3.6 IndexCache / IndexShare) */
+  int32_t wgs_per_request; /* workgroups per request in hs_resolve; 0 chooses */
+  uint32_t flags;          /* HS_CFG_* */
+} hs_config;
+
+/* Per-request result of one hs_resolve call (device memory, overwritten per call). */
+typedef struct {
+  uint32_t hits;   /* selected tokens already on the device (newest slot included) */
+  uint32_t misses; /* selected tokens fetched from host (record_bytes each) */
+  uint32_t error;  /* HS_ERR_* bits; when set, nothing of this request changed and its
+                      slots_out row is -1 */
+  uint32_t reserved;
+} hs_stats;
+
+/* Bytes of device workspace hs_create needs for cfg (0 when cfg is invalid). */
+size_t hs_workspace_bytes(const hs_config* cfg);
+
+/*
+ * Creates a cache.
+ *   d_hot       device, caller-owned, [R][L][B+1][record_bytes]: the hot buffers
+ *               ([GC] §3.2; slot B is the reserved newest slot, [GC] §5.2).
+ *   d_workspace device, caller-owned, hs_workspace_bytes(cfg) bytes, 256-byte
+ *               aligned: metadata (slot map, LRU order, page table, miss plans,
+ *               attention partials).  hs_create initialises it synchronously:
+ *               every slot empty, every position host-only ([GC] §5.3).
+ * Allocates the pinned host pool, one allocation per request of
+ * [L][max_positions][record_bytes] ([NJ] §2.1: contiguous by (request, layer,
+ * position)).  The caller fills it with the prefill records (hs_host_pool)
+ * before the first hs_resolve.  Returns HS_ENOMEM when pinning fails.
+ */
+hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_handle* out);
+
+/* Host address of request r's pool region [L][max_positions][record_bytes]; NULL if r is out of
+ * range.  Valid until hs_destroy. */
+void* hs_host_pool(hs_handle h, int32_t request);
+
+/*
+ * RESOLVE of one layer for all requests ([GC] §3.5, [NJ] §3, [KJ] §7.1):
+ * stage the selected positions in an LDS hash table, mark hit and evictable
+ * slots, assign LRU victims to the misses by wavefront scans, fetch the missed
+ * records from pinned host memory, publish the physical slots.
+ *   layer        an anchor (or, with layer_group 1, any) layer
+ *   d_sel        device [R][top_k / block_tokens] int32 positions (or block ids), distinct
+ *   d_ctx_len    device [R] int32: positions of request r must be < d_ctx_len[r]
+ *   d_slots_out  device [R][top_k] int32: slot of each selected token, in selection order
+ *                (B for the newest token); the layer's KV of entry i is
+ *                d_hot[r][layer][d_slots_out[r][i]]
+ *   d_stats      device [R] hs_stats, or NULL
+ *   d_num_reqs   device int32 scalar, or NULL: requests >= *d_num_reqs are left untouched
+ *                (padding of a captured batch, [GC] §5.5)
+ *   flags        HS_RECORD_PLAN | HS_SKIP_IO
+ * Replacement ([GC] §3.3): empty slots first; this call's hits rank newer than
+ * this call's fetched entries; victims are the least recent slots not selected
+ * now, ties by lower slot index; misses take victims in selection order.
+ * With HS_RECORD_PLAN the stream first waits until the previous plan of this
+ * anchor has been replayed.
+ */
+hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
+                     int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs,
+                     uint32_t flags, void* stream);
+
+/*
+ * Write-through of one new token per request, for every layer ([GC] §3.4, §5.4;
+ * [KJ] §7.1).  Needs HS_CFG_NEWEST_SLOT.
+ *   d_new_kv   device [R][L][record_bytes]: the new token's records
+ *   d_new_pos  device [R] int32: its position (< max_positions)
+ * On `compute`: waits for the previous write-through to finish reading slot B,
+ * copies d_new_kv into slot B of every layer and makes d_new_pos the newest
+ * position.  On `backup`: waits for that copy, then writes slot B to the host
+ * pool at d_new_pos.  A later hs_append on `compute` waits for this backup,
+ * so any later resolve that fetches that position reads the written bytes.
+ */
+hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos, void* compute,
+                    void* backup);
+
+/*
+ * Exact layer-wise prefetch ([GC] §3.6, §5.6): `prefetch` waits for the
+ * anchor's last hs_resolve (which must have used HS_RECORD_PLAN), then for
+ * each shared layer of the anchor's group copies that layer's own records of
+ * the plan into the same slots, and records the layer's event.  Shared layers
+ * reuse the anchor's d_slots_out.
+ */
+hs_status hs_prefetch_shared(hs_handle h, int32_t anchor_layer, void* compute, void* prefetch);
+
+/* `stream` waits until the prefetch of shared layer `layer` is done. */
+hs_status hs_wait_layer(hs_handle h, int32_t layer, void* stream);
+
+/*
+ * Sparse decode attention over the published slots ([GC] §5.4: attention reads
+ * the slots aligned with the top-k order).  For each request: the key of entry
+ * i is the first key_dim bf16 of the record in slot d_slots[r][i] of this
+ * layer, its value the first value_dim of them; s = scale * q k^T, softmax over
+ * the top_k entries, o = p v.
+ *   d_q     device [R][heads][key_dim] bf16, heads 1..16, key_dim = record_bytes/2 = 576
+ *   d_slots device [R][top_k] int32 (the layer's, or its anchor's, d_slots_out)
+ *   d_out   device [R][heads][value_dim] float32, value_dim = 512
+ *   d_num_reqs as for hs_resolve (rows of skipped requests are not written)
+ * Slots outside [0, B] make the request's output rows NaN.
+ */
+hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t heads,
+                         int32_t value_dim, const int32_t* d_slots, float* d_out, float scale,
+                         const int32_t* d_num_reqs, void* stream);
+
+/* Copies the current metadata of an anchor layer into caller buffers (device):
+ * d_slot_pos [R][B] position held by each slot (-1 empty), d_lru [R][B] slots
+ * from least to most recent, d_newest [R] newest position (-1 none).  Any may be NULL. */
+hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32_t* d_lru,
+                          int32_t* d_newest, void* stream);
+
+/* Device address of an anchor layer's page table, int32 [R][max_positions], -1 = host only. */
+const int32_t* hs_page_table(hs_handle h, int32_t layer);
+
+/* Device address of an anchor layer's miss plan: int32 [R][2][top_k] (positions, then slots,
+ * in miss order) and uint32 counts (stride 4 per request, count first). */
+hs_status hs_plan(hs_handle h, int32_t layer, const int32_t** d_plan, const uint32_t** d_counts);
+
+/* Request release ([GC] §5.4): every layer of request r back to the admission state (all
+ * slots empty, all positions host-only, LRU in slot order, no newest token). */
+hs_status hs_reset_request(hs_handle h, int32_t request, void* stream);
+
+/* Waits for the library's own events, frees the pinned pool and the handle. */
+hs_status hs_destroy(hs_handle h);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* hs_last_error(void);
+
+/* Workgroups per request hs_resolve launches for this handle. */
+int32_t hs_resolve_wgs(hs_handle h);
+
+/* ---- measurement aids (no part of the cache) ---------------------------------------------- */
+
+/* Streams `bytes` of pinned host memory through the GPU with 16-byte non-temporal loads from
+ * `wgs` workgroups (a zero-copy link probe).  d_sink: device, >= 16 KiB. */
+hs_status hs_probe_host_read(const void* host_src, size_t bytes, void* d_sink, int32_t wgs,
+                             void* stream);
+/* Plain device-to-device copy kernel (16-byte vectors), for counter calibration. */
+hs_status hs_probe_copy(const void* d_src, void* d_dst, size_t bytes, void* stream);
+/* An empty kernel (launch-latency probe). */
+hs_status hs_probe_empty(void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HISPARSE_H */

@@ -11,7 +11,8 @@ step (never-used slots are the least recent of all, lowest index first);
 misses are served in list order; after the step the slots filled by misses
 move to the recent end, then the slots hit in this step (hits rank newer than
 fetched misses).  Slots that become recent together are ordered by slot index.
-The newest token (§3.4) sits in slot B outside the list.
+The newest token (§3.4) sits in slot B outside the list; an LRU slot that
+holds the same position is treated as not selected.
 """
 from __future__ import annotations
 
@@ -32,7 +33,8 @@ class ListCache:
         sel = [int(p) for p in sel]
         if len(set(sel)) != len(sel):
             raise ValueError("duplicate position")
-        chosen = set(sel)
+        # the newest token is served from slot B, never through an LRU slot
+        chosen = set(sel) - ({self.newest} if self.newest_slot else set())
         where = {p: s for s, p in enumerate(self.holds) if p is not None}
         out = [None] * len(sel)
         hit_slots, miss_idx = [], []

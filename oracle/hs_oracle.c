@@ -151,8 +151,13 @@ int32_t hso_resolve(hso_cache* c, const int32_t* sel, int32_t k, int64_t ctx_len
 
   /* 3. evictable slots (empty or not selected now), oldest stamp first, ties by slot */
   int32_t n_ev = 0;
-  for (int32_t s = 0; s < B; ++s)
-    if (c->slot_pos[s] < 0 || !c->selected[c->slot_pos[s]]) evictable[n_ev++] = s;
+  for (int32_t s = 0; s < B; ++s) {
+    const int32_t p = c->slot_pos[s];
+    /* the newest token is served from slot B, so an LRU slot that happens to
+     * hold the same position is not selected through the LRU */
+    const int32_t is_newest = c->newest_slot && c->newest_pos >= 0 && p == c->newest_pos;
+    if (p < 0 || !c->selected[p] || is_newest) evictable[n_ev++] = s;
+  }
   sort_evictable(evictable, n_ev, c->stamp);
 
   /* 4. the j-th miss takes the j-th evictable slot and its record is copied in */

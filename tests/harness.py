@@ -1,0 +1,190 @@
+"""Drives a workload through the HIP library (C ABI) and the CPU oracle side by side.
+
+Test infrastructure: imports both sides; neither side imports the other.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import hierarchical_kv_cache_amd as hk
+import oracle
+import synth
+
+SCALE = 576 ** -0.5
+
+
+def expand(sel_row, bt):
+    return oracle.expand_blocks(sel_row, bt) if bt > 1 else np.asarray(sel_row, np.int32)
+
+
+class Pair:
+    """One HiSparse handle plus the matching oracle caches for a workload."""
+
+    def __init__(self, w: synth.Workload, steps: int | None = None, wgs: int = 0, all_hit=False,
+                 oracle_host_copy: bool | None = None, compare_hot=True):
+        self.w = w
+        self.steps = w.steps if steps is None else steps
+        self.lmax = w.max_positions(self.steps)
+        self.R, self.L, self.B, self.k, self.kb = w.R, w.L, w.B, w.k, w.kb
+        self.rec = synth.RECORD_BYTES
+        self.compare_hot = compare_hot
+        cfg = hk.make_config(w.R, w.L, self.lmax, w.k, w.B, record_bytes=self.rec,
+                             block_tokens=w.block_tokens, layer_group=w.group, wgs_per_request=wgs,
+                             newest_slot=w.append)
+        self.gpu = hk.HiSparse(cfg)
+        self.h = self.gpu.h
+        self.dev = torch.device("cuda")
+        self.compute = torch.cuda.current_stream()
+        self.side = torch.cuda.Stream()
+        # host pools: the prefill records, written by the input generator
+        for r in range(w.R):
+            synth.fill_request(self.gpu.host_pool_address(r), r, w.L, self.lmax, w.ctx)
+        # the oracle reads the same input bytes; with write-through the GPU also writes the
+        # pinned pool, so the oracle then keeps a pool of its own
+        if oracle_host_copy is None:
+            oracle_host_copy = w.append
+        if oracle_host_copy:
+            self.ohost = []
+            for r in range(w.R):
+                a = np.empty((w.L, self.lmax, self.rec), np.uint8)
+                synth.fill_request(a, r, w.L, self.lmax, w.ctx)
+                self.ohost.append(a)
+        else:
+            self.ohost = [self.gpu.host_pool(r) for r in range(w.R)]
+        self.anchors = [l for l in range(w.L) if l % w.group == 0]
+        self.caches = {(r, l): oracle.Cache(w.B, self.lmax, self.rec, newest_slot=w.append)
+                       for r in range(w.R) for l in self.anchors}
+        self.ohot_shared = {(r, l): np.zeros((w.B + 1, self.rec), np.uint8)
+                            for r in range(w.R) for l in range(w.L) if l % w.group}
+        # selection traces, resident on the device: [steps][anchors][R][kb]
+        tr = np.stack([np.stack([synth.selection_trace(w, r, l, self.steps, all_hit=all_hit)
+                                 for r in range(w.R)], axis=1) for l in self.anchors], axis=1)
+        self.trace = tr  # numpy [steps][A][R][kb]
+        self.d_trace = torch.from_numpy(tr).to(self.dev)
+        self.d_out = torch.empty((len(self.anchors), w.R, w.k), dtype=torch.int32, device=self.dev)
+        self.d_stats = torch.zeros((w.R, 4), dtype=torch.int32, device=self.dev)
+        self.t = 0
+        self.newest = None
+
+    # ---- one decode step ------------------------------------------------------------------
+    def ctx_len(self):
+        return self.w.ctx + (self.t + 1 if self.w.append else 0)
+
+    def step_gpu_and_oracle(self, flags=0, check=True, num_reqs=None):
+        w, t = self.w, self.t
+        ctx = self.ctx_len()
+        d_ctx = torch.full((w.R,), ctx, dtype=torch.int32, device=self.dev)
+        results = {}
+        if w.append:
+            p = w.ctx + t
+            recs = synth.records_at(w.R, w.L, [p] * w.R)
+            d_new = torch.from_numpy(recs).to(self.dev)
+            d_pos = torch.full((w.R,), p, dtype=torch.int32, device=self.dev)
+            hk.hs_append(self.h, d_new.data_ptr(), d_pos.data_ptr(), self.compute.cuda_stream,
+                         self.side.cuda_stream)
+            for r in range(w.R):
+                for l in self.anchors:
+                    self.caches[(r, l)].append(p, recs[r, l], self.ohost[r][l])
+            self.newest = p
+            self._keep = (d_new, d_pos)
+        d_nr = None
+        if num_reqs is not None:
+            d_nr = torch.tensor([num_reqs], dtype=torch.int32, device=self.dev)
+        for ai, l in enumerate(self.anchors):
+            d_sel = self.d_trace[t, ai]
+            hk.hs_resolve(self.h, l, d_sel.data_ptr(), d_ctx.data_ptr(), self.d_out[ai].data_ptr(),
+                          self.d_stats.data_ptr(), d_nr.data_ptr() if d_nr is not None else 0,
+                          flags | (hk.HS_RECORD_PLAN if w.group > 1 else 0), self.compute.cuda_stream)
+            if w.group > 1:
+                hk.hs_prefetch_shared(self.h, l, self.compute.cuda_stream, self.side.cuda_stream)
+            stats = self.d_stats.cpu().numpy().copy() if check else None
+            nr = w.R if num_reqs is None else num_reqs
+            for r in range(nr):
+                pos = expand(self.trace[t, ai, r], w.block_tokens)
+                out, hits, misses, ppos, pslot = self.caches[(r, l)].resolve(pos, ctx, self.ohost[r][l])
+                results[(r, l)] = (out, hits, misses, ppos, pslot)
+                for ls in range(l + 1, min(l + w.group, w.L)):
+                    oracle.replay(ppos, pslot, self.ohost[r][ls], self.ohot_shared[(r, ls)], self.rec)
+                if check:
+                    assert stats[r, 0] == hits and stats[r, 1] == misses and stats[r, 2] == 0, \
+                        (t, r, l, stats[r], hits, misses)
+            if check:
+                got = self.d_out[ai].cpu().numpy()
+                for r in range(nr):
+                    exp = results[(r, l)][0]
+                    if not np.array_equal(got[r], exp):
+                        bad = np.nonzero(got[r] != exp)[0]
+                        raise AssertionError("slots differ at step %d r %d l %d: %d entries, first %s"
+                                             % (t, r, l, bad.size, [(int(i), int(got[r][i]), int(exp[i]))
+                                                                      for i in bad[:5]]))
+        for l in range(w.L):
+            hk.hs_wait_layer(self.h, l, self.compute.cuda_stream)
+        self.t += 1
+        return results
+
+    # ---- state comparison ---------------------------------------------------------------
+    def check_state(self, layers=None, hot=True, page_table=True, requests=None):
+        w = self.w
+        torch.cuda.synchronize()
+        layers = self.anchors if layers is None else layers
+        requests = range(w.R) if requests is None else requests
+        for l in layers:
+            sp = torch.empty((w.R, w.B), dtype=torch.int32, device=self.dev)
+            lru = torch.empty((w.R, w.B), dtype=torch.int32, device=self.dev)
+            nw = torch.empty((w.R,), dtype=torch.int32, device=self.dev)
+            hk.hs_export_state(self.h, l, sp.data_ptr(), lru.data_ptr(), nw.data_ptr(), self.compute.cuda_stream)
+            torch.cuda.synchronize()
+            sp, lru, nw = sp.cpu().numpy(), lru.cpu().numpy(), nw.cpu().numpy()
+            if page_table:
+                pt_addr = hk.hs_page_table(self.h, l)
+                pt = torch.empty((w.R, self.lmax), dtype=torch.int32, device=self.dev)
+                torch.cuda.synchronize()
+                _copy_dev(pt_addr, pt)
+                pt = pt.cpu().numpy()
+            for r in requests:
+                st = self.caches[(r, l)].export()
+                assert np.array_equal(sp[r], st["slot_pos"]), ("slot_pos", r, l)
+                assert np.array_equal(lru[r], st["lru"]), ("lru", r, l)
+                if w.append:
+                    assert nw[r] == st["newest_pos"], ("newest", r, l)
+                if page_table:
+                    assert np.array_equal(pt[r], self.caches[(r, l)].page_table), ("page_table", r, l)
+        if hot and self.compare_hot:
+            self.check_hot(layers, requests)
+
+    def check_hot(self, layers=None, requests=None):
+        w = self.w
+        torch.cuda.synchronize()
+        layers = range(w.L) if layers is None else layers
+        requests = range(w.R) if requests is None else requests
+        for r in requests:
+            for l in layers:
+                a = l - l % w.group
+                st = self.caches[(r, a)].export()
+                occ = np.nonzero(st["slot_pos"] >= 0)[0]
+                g = self.gpu.hot[r, l].cpu().numpy()
+                ref = self.caches[(r, l)].hot if l == a else self.ohot_shared[(r, l)]
+                if not np.array_equal(g[occ], ref[occ]):
+                    bad = [int(s) for s in occ if not np.array_equal(g[s], ref[s])]
+                    raise AssertionError("hot bytes differ r %d l %d: %d slots, first %s"
+                                         % (r, l, len(bad), bad[:5]))
+                # the bytes are the record of the position the slot holds (input generator)
+                for s in occ[:: max(1, occ.size // 16)]:
+                    assert np.array_equal(g[s], synth.record(r, l, int(st["slot_pos"][s]))), (r, l, s)
+                if w.append and st["newest_pos"] >= 0:
+                    assert np.array_equal(g[w.B], synth.record(r, l, st["newest_pos"]))
+
+    def close(self):
+        torch.cuda.synchronize()
+        self.gpu.close()
+
+
+def _copy_dev(addr, dst: torch.Tensor):
+    """Copy device memory at `addr` into `dst` (same byte size) with hipMemcpy via torch."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipMemcpy.restype = ctypes.c_int
+    rc = hip.hipMemcpy(dst.data_ptr(), addr, dst.numel() * dst.element_size(), 3)  # device to device
+    assert rc == 0, rc

@@ -1,0 +1,317 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Slot maps, LRU orders, page tables, hit/miss counts and copied bytes must match
+bit for bit; attention within 2e-3 * max|o_ref| per (request, layer) (bf16 in,
+fp32 accumulate).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu]
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import hierarchical_kv_cache_amd as hk  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from harness import Pair, SCALE  # noqa: E402
+
+W = synth.WORKLOADS
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ---- worked example of the pages -------------------------------------------------------
+
+def test_example_a_through_the_c_abi(golden):
+    """gentlecold.top §3.5, B=8, k=4 walk-through, run on the GPU."""
+    g = dict(golden("example_a.txt"))
+    B, newest = int(g["B"][0]), int(g["newest"][0])
+    toks = [int(x) for x in g["before_tokens"]]
+    cfg = hk.make_config(1, 1, 64, 4, B, newest_slot=True)
+    c = hk.HiSparse(cfg)
+    synth.fill_request(c.host_pool_address(0), 0, 1, 64, newest)
+    dev = torch.device("cuda")
+    out = torch.empty((1, 4), dtype=torch.int32, device=dev)
+    st = torch.zeros((1, 4), dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+
+    def resolve(sel, ctx):
+        d_sel = torch.tensor([sel], dtype=torch.int32, device=dev)
+        d_ctx = torch.tensor([ctx], dtype=torch.int32, device=dev)
+        hk.hs_resolve(c.h, 0, d_sel.data_ptr(), d_ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0, 0)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()[0].tolist(), st.cpu().numpy()[0].tolist()
+
+    resolve(toks[:4], newest)
+    resolve(toks[4:], newest)
+    rec = torch.from_numpy(synth.records_at(1, 1, [newest])).to(dev)
+    pos = torch.tensor([newest], dtype=torch.int32, device=dev)
+    hk.hs_append(c.h, rec.data_ptr(), pos.data_ptr(), 0, side.cuda_stream)
+    slots, stats = resolve([int(x) for x in g["selection"]], newest + 1)
+    assert slots == [int(x) for x in g["expect_slots"]]
+    assert stats[:3] == [int(g["expect_hits"][0]), int(g["expect_misses"][0]), 0]
+    lru = torch.empty((1, B), dtype=torch.int32, device=dev)
+    sp = torch.empty((1, B), dtype=torch.int32, device=dev)
+    hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0)
+    torch.cuda.synchronize()
+    assert lru.cpu().numpy()[0].tolist() == [int(x) for x in g["expect_lru"]]
+    assert sp.cpu().numpy()[0].tolist() == [25, 11, 12, 13, 14, 15, 16, 17]
+    hot = c.hot[0, 0].cpu().numpy()
+    assert np.array_equal(hot[0], synth.record(0, 0, 25))   # t25 fetched into s0
+    assert np.array_equal(hot[B], synth.record(0, 0, 30))   # newest slot
+    torch.cuda.synchronize()
+    # write-through reached the host pool
+    assert np.array_equal(c.host_pool(0)[0, 30], synth.record(0, 0, 30))
+    c.close()
+
+
+# ---- the workloads ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,wgs", [(64, 1), (100, 3), (128, 0), (128, 7), (256, 2)])
+def test_tiny_every_step(B, wgs):
+    """Tiny workload (1 x 1, ctx 4096, k 64, 32 steps) at several B and workgroup counts:
+    slots, counts, slot map, LRU, page table and hot bytes after every step."""
+    w = W["tiny"].scaled(B=B)
+    log("tiny B=%d wgs=%d" % (B, wgs))
+    p = Pair(w, wgs=wgs)
+    for _ in range(w.steps):
+        p.step_gpu_and_oracle()
+        p.check_state()
+    p.close()
+
+
+def test_long_with_write_through_scaled():
+    """Long-request shape (k 2048, B 4096, one token appended and written through per step,
+    always selected) on 2 layers and a 16K context, state checked every step."""
+    w = W["long"].scaled(L=2, ctx=16384, steps=12)
+    log("long scaled")
+    p = Pair(w)
+    for _ in range(w.steps):
+        p.step_gpu_and_oracle()
+        p.check_state()
+    # the appended tokens are on the host, in the pinned pool the GPU wrote
+    for t in range(w.steps):
+        pos = w.ctx + t
+        for l in range(w.L):
+            assert np.array_equal(p.gpu.host_pool(0)[l, pos], synth.record(0, l, pos))
+    p.close()
+
+
+def test_long_full_size():
+    """The long-request workload at full size (1 x 8 layers, ctx 131072, k 2048, B 4096) for
+    24 steps: every slot vector and count each step, the whole state every 8 steps."""
+    w = W["long"]
+    log("long full size")
+    p = Pair(w, steps=24)
+    for t in range(24):
+        p.step_gpu_and_oracle()
+        if t % 8 == 7:
+            p.check_state()
+    p.close()
+
+
+@pytest.mark.parametrize("B", synth.BATCHED_B_SWEEP)
+def test_batched_sweep(B):
+    """Batched shape: 32 requests resolved in one launch per layer, B in {2048, 4096, 8192};
+    2 of the 16 layers, 4 steps."""
+    w = W["batched"].scaled(L=2, B=B)
+    log("batched B=%d" % B)
+    p = Pair(w, steps=4)
+    for _ in range(4):
+        p.step_gpu_and_oracle()
+    p.check_state()
+    p.close()
+
+
+def test_shared_index_prefetch_scaled():
+    """Shared-index shape: 8 layers = 2 x (anchor + 3 shared), 4 requests, ctx 16384; the
+    shared layers follow the anchor's plan with their own records on a side stream."""
+    w = W["shared"].scaled(R=4, L=8, ctx=16384)
+    log("shared scaled")
+    p = Pair(w, steps=6)
+    for _ in range(6):
+        p.step_gpu_and_oracle()
+        p.check_state()
+    p.check_hot(layers=range(w.L))
+    p.close()
+
+
+def test_capacity_blocks_scaled():
+    """Block-id selections (32 blocks of 64 tokens), recency-Zipf trace, on 2 x 2 caches with
+    a 64K context; blocks are expanded in the kernel."""
+    w = W["capacity"].scaled(R=2, L=2, ctx=65536)
+    log("capacity scaled")
+    p = Pair(w, steps=8)
+    for _ in range(8):
+        p.step_gpu_and_oracle()
+        p.check_state()
+    p.close()
+
+
+# ---- semantics at the edges -------------------------------------------------------------
+
+def _single(B=16, k=8, newest=False, lmax=256, wgs=2):
+    cfg = hk.make_config(2, 1, lmax, k, B, newest_slot=newest, wgs_per_request=wgs)
+    c = hk.HiSparse(cfg)
+    for r in range(2):
+        synth.fill_request(c.host_pool_address(r), r, 1, lmax, lmax)
+    return c
+
+
+def test_bad_selections_set_error_and_change_nothing():
+    dev = torch.device("cuda")
+    c = _single()
+    out = torch.empty((2, 8), dtype=torch.int32, device=dev)
+    st = torch.zeros((2, 4), dtype=torch.int32, device=dev)
+    ctx = torch.tensor([200, 200], dtype=torch.int32, device=dev)
+    good = torch.tensor([list(range(8)), list(range(50, 58))], dtype=torch.int32, device=dev)
+    hk.hs_resolve(c.h, 0, good.data_ptr(), ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0, 0)
+    sp0 = torch.empty((2, 16), dtype=torch.int32, device=dev)
+    lru0 = torch.empty((2, 16), dtype=torch.int32, device=dev)
+    hk.hs_export_state(c.h, 0, sp0.data_ptr(), lru0.data_ptr(), 0, 0)
+    bad = torch.tensor([[1, 2, 3, 4, 5, 6, 7, 3], [50, 51, 52, 53, 54, 55, 56, 250]], dtype=torch.int32,
+                       device=dev)
+    hk.hs_resolve(c.h, 0, bad.data_ptr(), ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0, 0)
+    torch.cuda.synchronize()
+    s = st.cpu().numpy()
+    assert s[0, 2] == hk.HS_ERR_DUP and s[1, 2] == hk.HS_ERR_RANGE
+    assert (out.cpu().numpy() == -1).all()
+    sp1 = torch.empty_like(sp0)
+    lru1 = torch.empty_like(lru0)
+    hk.hs_export_state(c.h, 0, sp1.data_ptr(), lru1.data_ptr(), 0, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(sp0, sp1) and torch.equal(lru0, lru1)
+    # the oracle agrees on the error bits
+    oc = oracle.Cache(16, 256, 1152)
+    with pytest.raises(oracle.OracleError) as e:
+        oc.resolve(bad.cpu().numpy()[0], 200, np.zeros((256, 1152), np.uint8))
+    assert e.value.code == hk.HS_ERR_DUP
+    with pytest.raises(oracle.OracleError) as e:
+        oc.resolve(bad.cpu().numpy()[1], 200, np.zeros((256, 1152), np.uint8))
+    assert e.value.code == hk.HS_ERR_RANGE
+    c.close()
+
+
+def test_padded_requests_are_untouched():
+    """A device request count below R leaves the padded requests exactly as they were
+    (gentlecold.top §5.5: padded blocks of a captured batch return early)."""
+    w = W["tiny"].scaled(R=3)
+    p = Pair(w, wgs=2)
+    p.step_gpu_and_oracle()
+    for _ in range(4):
+        p.step_gpu_and_oracle(num_reqs=2)
+    p.check_state(requests=[0, 1])
+    # request 2 still has its state after step 1 only
+    sp = torch.empty((3, w.B), dtype=torch.int32, device="cuda")
+    hk.hs_export_state(p.h, 0, sp.data_ptr(), 0, 0, 0)
+    torch.cuda.synchronize()
+    oc = oracle.Cache(w.B, p.lmax, 1152)
+    oc.resolve(p.trace[0, 0, 2], w.ctx, p.ohost[2][0])
+    assert np.array_equal(sp.cpu().numpy()[2], oc.export()["slot_pos"])
+    p.close()
+
+
+def test_skip_io_moves_metadata_not_bytes():
+    """The timing aid (gentlecold.top §4.4 no-IO oracle): same metadata, no record bytes."""
+    w = W["tiny"]
+    a = Pair(w)
+    b = Pair(w)
+    b.gpu.hot.fill_(0x5A)
+    for _ in range(6):
+        ra = a.step_gpu_and_oracle()
+        rb = b.step_gpu_and_oracle(flags=hk.HS_SKIP_IO)
+    a.check_state(hot=True)
+    b.check_state(hot=False)
+    torch.cuda.synchronize()
+    assert (b.gpu.hot.cpu().numpy() == 0x5A).all()
+    a.close()
+    b.close()
+
+
+def test_reset_request_returns_to_admission_state():
+    w = W["tiny"].scaled(R=2)
+    p = Pair(w)
+    for _ in range(3):
+        p.step_gpu_and_oracle()
+    hk.hs_reset_request(p.h, 1, 0)
+    sp = torch.empty((2, w.B), dtype=torch.int32, device="cuda")
+    lru = torch.empty((2, w.B), dtype=torch.int32, device="cuda")
+    hk.hs_export_state(p.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0)
+    torch.cuda.synchronize()
+    assert (sp.cpu().numpy()[1] == -1).all()
+    assert lru.cpu().numpy()[1].tolist() == list(range(w.B))
+    assert np.array_equal(sp.cpu().numpy()[0], p.caches[(0, 0)].export()["slot_pos"])
+    p.close()
+
+
+def test_shared_layer_is_refused_by_resolve():
+    cfg = hk.make_config(1, 4, 4096, 64, 128, layer_group=4)
+    c = hk.HiSparse(cfg)
+    x = torch.zeros((1, 64), dtype=torch.int32, device="cuda")
+    with pytest.raises(hk.HsError) as e:
+        hk.hs_resolve(c.h, 1, x.data_ptr(), x.data_ptr(), x.data_ptr(), 0, 0, 0, 0)
+    assert e.value.code == hk.HS_ESTATE
+    c.close()
+
+
+# ---- the sparse-attention consumer -------------------------------------------------------
+
+def _attn_check(p, step, layers, heads=16):
+    w = p.w
+    q = synth.queries(w.R, w.L, step, heads=heads)
+    d_q = torch.from_numpy(q.view(np.int16)).to("cuda")
+    out = torch.empty((w.R, heads, 512), dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for l in layers:
+        a = l - l % w.group
+        ai = p.anchors.index(a)
+        hk.hs_wait_layer(p.h, l, 0)
+        hk.hs_sparse_attn(p.h, l, d_q[:, l].contiguous().data_ptr(), heads, 512, p.d_out[ai].data_ptr(),
+                          out.data_ptr(), SCALE, 0, 0)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        slots = p.d_out[ai].cpu().numpy()
+        for r in range(w.R):
+            hot = p.caches[(r, l)].hot if l == a else p.ohot_shared[(r, l)]
+            ref = oracle.attention.sparse_decode_attention(q[r, l], hot, slots[r], SCALE)
+            err = np.abs(o[r] - ref).max() / np.abs(ref).max()
+            worst = max(worst, err)
+            assert err <= 2e-3, (r, l, err)
+    return worst
+
+
+def test_attention_batched():
+    w = W["batched"].scaled(L=2)
+    p = Pair(w, steps=2)
+    for t in range(2):
+        p.step_gpu_and_oracle()
+        worst = _attn_check(p, t, range(w.L))
+    log("attention batched worst rel err %.2e" % worst)
+    p.close()
+
+
+def test_attention_single_request_and_shared_layers():
+    w = W["shared"].scaled(R=2, L=4, ctx=16384)
+    p = Pair(w, steps=2)
+    for t in range(2):
+        p.step_gpu_and_oracle()
+        worst = _attn_check(p, t, range(w.L))
+    log("attention shared worst rel err %.2e" % worst)
+    p.close()
+
+
+@pytest.mark.parametrize("k,heads", [(64, 16), (100, 5), (1000, 16)])
+def test_attention_ragged(k, heads):
+    """Entry counts that leave a ragged last tile, and fewer than 16 heads."""
+    w = W["tiny"].scaled(k=k, B=max(128, k + 40), R=3, forced_last=min(16, k))
+    p = Pair(w, steps=3)
+    for t in range(3):
+        p.step_gpu_and_oracle()
+        _attn_check(p, t, [0], heads=heads)
+    p.close()

@@ -1,0 +1,58 @@
+"""CPU checks of the C-ABI library: it loads, and exports every symbol include/hisparse.h
+declares (no compute calls: this host has no GPU)."""
+import ctypes
+import os
+import re
+
+import hierarchical_kv_cache_amd as hk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hisparse.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(hk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hk.LIB_PATH)
+    missing = [name for name in declared_functions() if not hasattr(lib, name)]
+    assert not missing, missing
+
+
+def test_workspace_sizing_and_validation_without_gpu():
+    cfg = hk.make_config(R=32, L=16, max_positions=32768, top_k=2048, buffer_slots=4096)
+    n = hk.hs_workspace_bytes(cfg)
+    # page tables dominate: 32 * 16 * 32768 int32
+    assert n >= 32 * 16 * 32768 * 4
+    bad = hk.make_config(R=1, L=1, max_positions=4096, top_k=128, buffer_slots=64)  # B < k
+    try:
+        hk.hs_workspace_bytes(bad)
+    except hk.HsError as e:
+        assert e.code == hk.HS_EINVAL and "buffer_slots" in str(e)
+    else:
+        raise AssertionError("B < k accepted")
+    bad = hk.make_config(R=1, L=1, max_positions=4096, top_k=96, buffer_slots=128, block_tokens=64)
+    try:
+        hk.hs_workspace_bytes(bad)
+    except hk.HsError as e:
+        assert "block_tokens" in str(e)
+    else:
+        raise AssertionError("block size not dividing k accepted")
+
+
+def test_capacity_closed_form():
+    """Device footprint per request is L * (B + 1) * record bytes, independent of the context
+    ("推理系统基础设施手记（六）：HiSparse" (naphjohn.github.io) §2: HBM = N_l * B * W_KV * s;
+    its worked figure: 4096 of 131072 tokens per layer, about 3.1 %, about 32x)."""
+    import synth
+    w = synth.WORKLOADS["long"]
+    assert w.B / w.ctx == 4096 / 131072
+    assert round(100 * w.B / w.ctx, 1) == 3.1 and w.ctx // w.B == 32
+    assert w.hot_bytes() == w.R * w.L * (w.B + 1) * 1152
+    assert synth.WORKLOADS["capacity"].host_bytes() == 4 * 4 * 1048576 * 1152

@@ -215,6 +215,17 @@ def test_random_traces_with_newest_slot():
         run_both(seqs, B, universe, newest)
 
 
+def test_newest_position_also_in_an_lru_slot():
+    """Corner case the pages leave open: appending a position that an LRU slot
+    already holds.  Reading: the newest slot serves it and the LRU slot counts as
+    not selected (evictable), in both models."""
+    for seqs, newest in [([[1, 2], [2, 3], [1, 2]], [None, 2, 2]),
+                         ([[0, 1, 2], [2, 4, 5], [5, 0, 2]], [None, 2, 5])]:
+        for B in (2, 3, 4, 6):
+            if B >= len(seqs[0]):
+                run_both(seqs, B, 8, newest)
+
+
 # --- invariants over synthetic workloads ----------------------------------------
 
 @pytest.mark.parametrize("B", [64, 96, 128, 256])
