@@ -1,0 +1,424 @@
+"""Benchmark of the per-layer RESOLVE hot path on one MI355X.
+
+Workload: the long-request configuration -- 1 request x 8 layers, 131072-token
+context, 1152-byte bf16 records, k = 2048, B = 4096, one token appended and
+written through per step.  One step is one decode step of the whole path:
+write-through of the new token, then for each layer RESOLVE (stage, mark,
+scan, fetch, publish) and the sparse-attention consumer over the published
+slots.  Inputs (selection traces, new records, queries) are resident in HBM
+before the timed region starts.
+
+Prints one JSON line.  `value` is resolved selections per second over the K
+timed steps.  Also reported: per-kernel durations from HIP events on the
+launch stream, miss-fetch GB/s against the measured host-link ceiling, the
+all-hit RESOLVE latency per layer (k = 2048, B = 4096) against the launch and
+HBM bounds, a roofline entry for the dominant kernel, and the CPU oracle on
+this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+REC = 1152
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing")
+    ap.add_argument("--quick", action="store_true", help="skip the secondary measurements")
+    return ap.parse_args()
+
+
+def sync_barrier(torch):
+    torch.cuda.synchronize()
+
+
+def profile_traffic(kernel: str, src_files):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, or None when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "%s_traffic.json" % kernel)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for s in src_files:
+        with open(os.path.join(ROOT, s), "rb") as g:
+            h.update(g.read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each (request, layer) "
+              "cache is independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hierarchical_kv_cache_amd as hk
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS["long"]
+    W, K = args.warmup, args.steps
+    n_steps = W + K
+    R, L, k, B = w.R, w.L, w.k, w.B
+    lmax = w.max_positions(n_steps)
+    heads, scale = w.heads, 576 ** -0.5
+
+    # ---- inputs (host generation, then resident in HBM) ------------------------------
+    t_in = time.time()
+    cfg = hk.make_config(R, L, lmax, k, B, newest_slot=True)
+    cache = hk.HiSparse(cfg)
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    trace = np.stack([np.stack([synth.selection_trace(w, r, l, n_steps) for r in range(R)], axis=1)
+                      for l in range(L)], axis=1)  # [steps][L][R][k]
+    d_trace = torch.from_numpy(trace).to(dev)
+    new_pos = w.ctx + np.arange(n_steps)
+    d_new_kv = torch.from_numpy(np.stack([synth.records_at(R, L, [p] * R) for p in new_pos])).to(dev)
+    d_new_pos = torch.from_numpy(np.repeat(new_pos[:, None], R, axis=1).astype(np.int32)).to(dev)
+    d_ctx = torch.from_numpy((new_pos[:, None] + 1).repeat(R, axis=1).astype(np.int32)).to(dev)
+    d_q = torch.from_numpy(np.stack([synth.queries(R, L, t, heads=heads) for t in range(n_steps)])
+                           .view(np.int16)).to(dev)  # [steps][R][L][H][576]
+    d_q = d_q.permute(0, 2, 1, 3, 4).contiguous()   # [steps][L][R][H][576]
+    d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n_steps, L, R, 4), dtype=torch.int32, device=dev)
+    d_out = torch.empty((L, R, heads, 512), dtype=torch.float32, device=dev)
+    compute = torch.cuda.current_stream()
+    backup = torch.cuda.Stream()
+    cs, bs = compute.cuda_stream, backup.cuda_stream
+    input_s = time.time() - t_in
+
+    ev = {name: [[torch.cuda.Event(enable_timing=True) for _ in range(L)] for _ in range(K)]
+          for name in ("r0", "r1", "a1")}
+
+    def step(t, timed_idx=None):
+        hk.hs_append(cache.h, d_new_kv[t].data_ptr(), d_new_pos[t].data_ptr(), cs, bs)
+        for l in range(L):
+            if timed_idx is not None:
+                ev["r0"][timed_idx][l].record(compute)
+            hk.hs_resolve(cache.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
+                          d_stats[t, l].data_ptr(), 0, 0, cs)
+            if timed_idx is not None:
+                ev["r1"][timed_idx][l].record(compute)
+            hk.hs_sparse_attn(cache.h, l, d_q[t, l].data_ptr(), heads, 512, d_slots[l].data_ptr(),
+                              d_out[l].data_ptr(), scale, 0, cs)
+            if timed_idx is not None:
+                ev["a1"][timed_idx][l].record(compute)
+
+    for t in range(W):
+        step(t)
+    sync_barrier(torch)
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, timed_idx=i)
+    sync_barrier(torch)
+    elapsed = time.perf_counter() - t0
+    backup.synchronize()
+
+    res_us = [ev["r0"][i][l].elapsed_time(ev["r1"][i][l]) * 1e3 for i in range(K) for l in range(L)]
+    att_us = [ev["r1"][i][l].elapsed_time(ev["a1"][i][l]) * 1e3 for i in range(K) for l in range(L)]
+    stats = d_stats.cpu().numpy()
+    errors = int(stats[..., 2].any())
+    misses_timed = int(stats[W:, :, :, 1].sum())
+    hits_timed = int(stats[W:, :, :, 0].sum())
+    selections = K * L * R * k
+    value = selections / elapsed
+    miss_rate = misses_timed / max(1, misses_timed + hits_timed)
+
+    detail = {
+        "resolve_us_per_layer_mean": statistics.fmean(res_us),
+        "resolve_us_per_layer_median": statistics.median(res_us),
+        "attention_us_per_layer_mean": statistics.fmean(att_us),
+        "miss_rate": miss_rate,
+        "misses_per_layer_step": misses_timed / (K * L * R),
+        "cold_step_misses": int(stats[0, :, :, 1].sum()),
+        "errors": errors,
+        "resolve_wgs_per_request": cache.wgs,
+        "input_setup_s": round(input_s, 2),
+    }
+
+    # ---- secondary measurements --------------------------------------------------------
+    link = {}
+    if not args.quick:
+        link = measure_link(torch, hk, dev)
+        detail.update(measure_fetch(torch, hk, synth, w, dev, trace, lmax))
+        detail.update(measure_fetch_heavy(torch, hk, synth, dev))
+        detail.update(measure_all_hit(torch, hk, synth, dev))
+        detail["launch_latency_us"] = measure_empty(torch, hk)
+        detail["hbm_copy_GBps"] = measure_hbm(torch, hk, dev)
+        detail["link_ceiling_GBps"] = link["ceiling_GBps"]
+        detail["link_dma_h2d_GBps"] = link["dma_GBps"]
+        detail["link_zero_copy_GBps"] = link["zero_copy_GBps"]
+        for key in ("batched_cold_fetch_GBps", "batched_cold_fetch_GBps_whole_kernel", "long_cold_fetch_GBps"):
+            detail[key.replace("GBps", "frac_of_link")] = detail[key] / link["ceiling_GBps"]
+
+    # ---- roofline of the dominant kernel -------------------------------------------------
+    res_total = sum(res_us)
+    att_total = sum(att_us)
+    steady_misses = misses_timed / (K * L * R)
+    if att_total >= res_total:
+        # attention reads k records from HBM per (request, layer), plus q and the output
+        alg_bytes = R * (k * REC + heads * 576 * 2 + heads * 512 * 4)
+        t_us = statistics.fmean(att_us)
+        roof = {"kernel": "attn_kernel", "bound": "hbm", "achieved": alg_bytes / (t_us * 1e-6) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "traffic": profile_traffic("attn_kernel", ["hierarchical_kv_cache_amd/csrc/attn.hip"])}
+    else:
+        # RESOLVE: selection in, slot map + LRU read and written, slots out, 2 page-table
+        # writes + one record written per miss
+        alg_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + steady_misses * (REC + 8 + 8))
+        t_us = statistics.fmean(res_us)
+        roof = {"kernel": "resolve_kernel", "bound": "hbm", "achieved": alg_bytes / (t_us * 1e-6) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "traffic": profile_traffic("resolve_kernel", ["hierarchical_kv_cache_amd/csrc/resolve.hip"])}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["algorithmic_bytes_per_launch"] = alg_bytes
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(synth, w, trace, n_steps, W, K, args.cpu_seconds)
+
+    cache.close()
+    line = {
+        "metric": "resolved selections/s",
+        "value": value,
+        "unit": "selections/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32 index + bf16 records (fp32 attention accumulate)",
+        "data": "synthetic (seeded selection traces; counter-based N(0,1) bf16 records)",
+        "config": {"workload": "long request: 1 req x 8 layers, ctx 131072, k 2048, B 4096, "
+                               "write-through + sparse attention (16 heads)",
+                   "requests": R, "layers": L, "ctx": w.ctx, "top_k": k, "buffer_slots": B,
+                   "record_bytes": REC, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line))
+
+
+def measure_link(torch, hk, dev):
+    """Host-link ceiling: max of a DMA copy and a zero-copy streaming read, 1 GiB pinned."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    src.fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    sink = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream()
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    e1.record(s)
+    torch.cuda.synchronize()
+    dma = 3 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    hk.hs_probe_host_read(src.data_ptr(), n, sink.data_ptr(), 256, s.cuda_stream)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(3):
+        hk.hs_probe_host_read(src.data_ptr(), n, sink.data_ptr(), 256, s.cuda_stream)
+    e1.record(s)
+    torch.cuda.synchronize()
+    zc = 3 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return {"dma_GBps": dma, "zero_copy_GBps": zc, "ceiling_GBps": max(dma, zc)}
+
+
+def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, hits_only=False):
+    """RESOLVE alone over `steps` steps of a trace on a fresh cache; per-launch µs per step."""
+    R, L, k, B = w.R, w.L, w.k, w.B
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, newest_slot=w.append))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    d_trace = torch.from_numpy(np.ascontiguousarray(trace[:steps])).to(dev)
+    d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ctx = torch.from_numpy((w.ctx + 1 + np.arange(steps))[:, None].repeat(R, 1).astype(np.int32)).to(dev) \
+        if w.append else torch.full((steps, R), w.ctx, dtype=torch.int32, device=dev)
+    if w.append:
+        pos = w.ctx + np.arange(steps)
+        new_kv = torch.from_numpy(np.stack([synth.records_at(R, L, [p] * R) for p in pos])).to(dev)
+        new_pos = torch.from_numpy(pos[:, None].repeat(R, 1).astype(np.int32)).to(dev)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for t in range(steps):
+        if w.append:
+            hk.hs_append(cache.h, new_kv[t].data_ptr(), new_pos[t].data_ptr(), s.cuda_stream, side.cuda_stream)
+        for l in range(L):
+            evs[t][l][0].record(s)
+            hk.hs_resolve(cache.h, l, d_trace[t, l].data_ptr(), ctx[t].data_ptr(), d_slots.data_ptr(),
+                          d_stats[t, l].data_ptr(), 0, flags, s.cuda_stream)
+            evs[t][l][1].record(s)
+    torch.cuda.synchronize()
+    us = np.array([[evs[t][l][0].elapsed_time(evs[t][l][1]) * 1e3 for l in range(L)] for t in range(steps)])
+    st = d_stats.cpu().numpy()
+    cache.close()
+    return us, st
+
+
+def measure_fetch(torch, hk, synth, w, dev, trace, lmax):
+    """IO cost inside RESOLVE on identical metadata states (the same trace from the same empty
+    start, run once normally and once with SKIP_IO), for the long workload."""
+    steps = min(64, trace.shape[0])
+    us_io, st = run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, 0)
+    us_skip, st2 = run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, hk.HS_SKIP_IO)
+    assert np.array_equal(st, st2)
+    miss_bytes = st[..., 1].sum(axis=2) * REC  # [steps][L]
+    return {"long_cold_resolve_us_per_layer": float(us_io[0].mean()),
+            "long_cold_resolve_skip_io_us_per_layer": float(us_skip[0].mean()),
+            "long_cold_fetch_GBps": float(miss_bytes[0].sum() / ((us_io[0] - us_skip[0]).sum() * 1e-6) / 1e9),
+            "long_steady_resolve_us_per_layer": float(us_io[8:].mean()),
+            "long_steady_resolve_skip_io_us_per_layer": float(us_skip[8:].mean()),
+            "long_steady_miss_bytes_per_layer": float(miss_bytes[8:].mean())}
+
+
+def measure_fetch_heavy(torch, hk, synth, dev):
+    """The fetch-heavy launch: 32 requests, cold (every one of the 32 x 2048 entries misses),
+    75.5 MB through the host link in one RESOLVE launch."""
+    wl = synth.WORKLOADS["batched"].scaled(L=1)
+    tr = np.stack([np.stack([synth.selection_trace(wl, r, 0, 2) for r in range(wl.R)], axis=1)], axis=1)
+    us_io, st = run_resolve_only(torch, hk, synth, wl, dev, tr, wl.max_positions(2), 2, 0)
+    us_skip, _ = run_resolve_only(torch, hk, synth, wl, dev, tr, wl.max_positions(2), 2, hk.HS_SKIP_IO)
+    b = float(st[0, :, :, 1].sum() * REC)
+    return {"batched_cold_launch_bytes": b,
+            "batched_cold_resolve_us": float(us_io[0, 0]),
+            "batched_cold_resolve_skip_io_us": float(us_skip[0, 0]),
+            "batched_cold_fetch_GBps": b / ((us_io[0, 0] - us_skip[0, 0]) * 1e-6) / 1e9,
+            "batched_cold_fetch_GBps_whole_kernel": b / (us_io[0, 0] * 1e-6) / 1e9}
+
+
+def measure_all_hit(torch, hk, synth, dev):
+    """All-hit RESOLVE µs per layer at k = 2048, B = 4096: after one warm step every step
+    repeats the selection.  Single request (long shape) and 32 requests (batched shape)."""
+    out = {}
+    for name, wl in (("r1", synth.WORKLOADS["long"].scaled(append=False, force_newest=False, L=4)),
+                     ("r32", synth.WORKLOADS["batched"].scaled(L=1))):
+        steps = 128
+        tr = np.stack([np.stack([synth.selection_trace(wl, r, l, steps, all_hit=True) for r in range(wl.R)],
+                                axis=1) for l in range(wl.L)], axis=1)
+        us, st = run_resolve_only(torch, hk, synth, wl, dev, tr, wl.max_positions(steps), steps, 0)
+        assert st[1:, :, :, 1].sum() == 0
+        out["all_hit_us_per_layer_%s" % name] = float(np.median(us[2:]))
+        # algorithmic HBM bytes of an all-hit launch: selection, slot map + LRU read and written, slots
+        b = wl.R * (wl.k * 4 * 2 + wl.B * (4 + 2) * 2)
+        out["all_hit_hbm_bound_us_%s" % name] = b / (HBM_PEAK_GBS * 1e9) * 1e6
+    return out
+
+
+def measure_empty(torch, hk):
+    s = torch.cuda.current_stream()
+    for _ in range(100):
+        hk.hs_probe_empty(s.cuda_stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(2000):
+        hk.hs_probe_empty(s.cuda_stream)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / 2000
+
+
+def measure_hbm(torch, hk, dev):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream()
+    hk.hs_probe_copy(a.data_ptr(), b.data_ptr(), n, s.cuda_stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(5):
+        hk.hs_probe_copy(a.data_ptr(), b.data_ptr(), n, s.cuda_stream)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return 5 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cpu_baseline(synth, w, trace, n_steps, W, K, budget_s):
+    """The oracle as it stands, on this host's cores: one thread per layer cache, the same
+    trace; untimed through the warmup steps, then timed over the first timed steps that
+    fit the budget.  Same step: append + write-through, resolve, float64 attention."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    R, L, k, B = w.R, w.L, w.k, w.B
+    lmax = w.max_positions(n_steps)
+    host = [np.empty((L, lmax, REC), np.uint8) for _ in range(R)]
+    for r in range(R):
+        synth.fill_request(host[r], r, L, lmax, w.ctx)
+    caches = {(r, l): oracle.Cache(B, lmax, REC, newest_slot=True) for r in range(R) for l in range(L)}
+    threads = min(L * R, os.cpu_count() or 1)
+    pool = ThreadPoolExecutor(max_workers=threads)
+
+    def layer_step(args):
+        t, r, l, q = args
+        p = w.ctx + t
+        c = caches[(r, l)]
+        c.append(p, synth.record(r, l, p), host[r][l])
+        out, _, _, _, _ = c.resolve(trace[t, l, r], p + 1, host[r][l])
+        oracle.attention.sparse_decode_attention(q[r, l], c.hot, out, 576 ** -0.5)
+        return out.size
+
+    def run_step(t):
+        q = synth.queries(R, L, t, heads=w.heads)
+        return sum(pool.map(layer_step, [(t, r, l, q) for r in range(R) for l in range(L)]))
+
+    for t in range(W):
+        run_step(t)
+    done, sel = 0, 0
+    t0 = time.perf_counter()
+    while done < K and time.perf_counter() - t0 < budget_s:
+        sel += run_step(W + done)
+        done += 1
+    el = time.perf_counter() - t0
+    pool.shutdown()
+    for c in caches.values():
+        c.close()
+    return {"value": sel / el, "unit": "selections/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of the %d timed decode steps (after the same %d warmup steps), all %d layers; "
+                      "append + resolve + float64 attention per layer" % (done, K, W, L)}
+
+
+if __name__ == "__main__":
+    main()

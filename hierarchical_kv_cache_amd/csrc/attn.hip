@@ -10,9 +10,9 @@
 // over the 576 key dims), the block keeps a running max / sum per head, and
 // each wave then accumulates P V for its 128 output channels, again on MFMA.
 // P is split into bf16 hi + lo parts so the fp32 probabilities survive the
-// bf16 operand.  The last workgroup of a request to finish merges the
-// per-chunk partials.  With R >= 8 all chunks of a request are placed on one
-// XCD so the merge reads partials from that XCD's L2.
+// bf16 operand.  A second small kernel merges the per-chunk partials (max,
+// sum, unnormalised output) of each (request, head).  With R >= 8 all chunks
+// of a request run on one XCD.
 #include "hs_internal.h"
 
 namespace hs {
@@ -29,6 +29,7 @@ constexpr int RS = 1184;                // LDS row stride: 1152 + 32 bytes keeps
 constexpr int KSTEPS = kAttnDk / 32;    // 18
 constexpr int CHUNKS = kAttnDk * 2 / 16;  // 72 16-byte chunks per record
 constexpr int CT = kAttnDv / 4 / 16;    // 8 channel tiles of 16 per wave
+constexpr int GATHER = TT * CHUNKS / AT;  // 18 16-byte chunks per thread per tile
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   uint32_t u = __float_as_uint(x);
@@ -43,7 +44,7 @@ __global__ void __launch_bounds__(AT, 2) attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t plo[2][16][32];
   __shared__ float smax[4][16];
   __shared__ float ssum[4][16];
-  __shared__ int s_last;
+  __shared__ int s_slot[TT];
 
   int r, s;
   if (p.R >= 8) {  // chunks of one request on one XCD (workgroups go round-robin over 8 XCDs)
@@ -88,17 +89,28 @@ __global__ void __launch_bounds__(AT, 2) attn_kernel(AttnParams p) {
 
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     __syncthreads();  // the previous tile is no longer read
-    // gather the tile's records into LDS (18 16-byte chunks per thread)
-#pragma unroll 6
-    for (int f = tid; f < TT * CHUNKS; f += AT) {
-      const int row = f / CHUNKS, c = f - row * CHUNKS;
-      const int tok = t0 + row;
-      u32x4 v = zero4;  // tokens past the end contribute exact zeros
-      if (tok < t_end) {
-        const int sl = slots_r[tok];
-        v = (sl >= 0 && sl <= p.B) ? *((const u32x4*)(hot_r + (size_t)sl * p.rec_bytes) + c) : nan4;
+    if (tid < TT) s_slot[tid] = (t0 + tid < t_end) ? slots_r[t0 + tid] : -2;
+    __syncthreads();
+    // gather the tile's records into LDS: two rounds of 9 16-byte loads per thread in flight
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 v[GATHER / 2];
+#pragma unroll
+      for (int u = 0; u < GATHER / 2; ++u) {
+        const int f = tid + (half * (GATHER / 2) + u) * AT;
+        const int row = f / CHUNKS, c = f - row * CHUNKS;
+        const int sl = s_slot[row];
+        // past the end: exact zeros; a slot outside [0, B]: NaN, so the output shows it
+        v[u] = sl == -2 ? zero4
+                        : ((sl >= 0 && sl <= p.B) ? *((const u32x4*)(hot_r + (size_t)sl * p.rec_bytes) + c)
+                                                  : nan4);
       }
-      *(u32x4*)(rows + row * RS + c * 16) = v;
+#pragma unroll
+      for (int u = 0; u < GATHER / 2; ++u) {
+        const int f = tid + (half * (GATHER / 2) + u) * AT;
+        const int row = f / CHUNKS, c = f - row * CHUNKS;
+        *(u32x4*)(rows + row * RS + c * 16) = v[u];
+      }
     }
     __syncthreads();
 
@@ -206,29 +218,41 @@ __global__ void __launch_bounds__(AT, 2) attn_kernel(AttnParams p) {
       part[16 * kAttnDv + 16 + hh] = ssum[0][hh] + ssum[1][hh] + ssum[2][hh] + ssum[3][hh];
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&p.counter[r], 1u) == (unsigned)(p.S - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
-  // merge the S partials of request r
+// Merge of the S chunk partials of one (request, head): o = sum_s 2^(m_s - M) o_s /
+// sum_s 2^(m_s - M) l_s.  One workgroup of 128 threads per (request, head), 4 channels each.
+__global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p) {
+  __shared__ float fac[kAttnMaxChunks];
+  __shared__ float s_den;
+  const int r = blockIdx.x / p.heads, hh = blockIdx.x - r * p.heads;
+  if (p.num_reqs && r >= *p.num_reqs) return;
   const float* pr = p.part + (size_t)r * p.S * kPartStride;
-  for (int idx = tid; idx < p.heads * kAttnDv; idx += AT) {
-    const int hh = idx / kAttnDv, c = idx - hh * kAttnDv;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
     float M = -INFINITY;
-    for (int q = 0; q < p.S; ++q) M = fmaxf(M, pr[q * kPartStride + 16 * kAttnDv + hh]);
-    float num = 0.0f, den = 0.0f;
-    for (int q = 0; q < p.S; ++q) {
-      const float* pq = pr + q * kPartStride;
-      const float e = exp2f(pq[16 * kAttnDv + hh] - M);
-      num += e * pq[hh * kAttnDv + c];
-      den += e * pq[16 * kAttnDv + 16 + hh];
+    for (int q = tid; q < p.S; q += 64) M = fmaxf(M, pr[(size_t)q * kPartStride + 16 * kAttnDv + hh]);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
+    float den = 0.0f;
+    for (int q = tid; q < p.S; q += 64) {
+      const float* pq = pr + (size_t)q * kPartStride;
+      const float f = exp2f(pq[16 * kAttnDv + hh] - M);
+      fac[q] = f;
+      den += f * pq[16 * kAttnDv + 16 + hh];
     }
-    p.out[((size_t)r * p.heads + hh) * p.value_dim + c] = num / den;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) den += __shfl_xor(den, d);
+    if (tid == 0) s_den = den;
   }
-  if (tid == 0) p.counter[r] = 0u;
+  __syncthreads();
+  const int c = tid * 4;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float* base = pr + hh * kAttnDv + c;
+#pragma unroll 8
+  for (int q = 0; q < p.S; ++q) acc += fac[q] * *(const f32x4*)(base + (size_t)q * kPartStride);
+  const float inv = 1.0f / s_den;
+  *(f32x4*)(p.out + ((size_t)r * p.heads + hh) * p.value_dim + c) = acc * inv;
 }
 
 }  // namespace
@@ -236,6 +260,9 @@ __global__ void __launch_bounds__(AT, 2) attn_kernel(AttnParams p) {
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   const int grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * p.S : p.R * p.S;
   hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(AT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.S == 1) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(p.R * p.heads), dim3(128), 0, s, p);
   return hipGetLastError();
 }
 

@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(kCopyThreads) init_kernel(InitParams p) {
 
 __global__ void __launch_bounds__(kCopyThreads) export_kernel(ExportParams p) {
   const int r = blockIdx.y;
-  const int cur = p.ctrl[r * 4] & 1;
+  const int cur = (int)((*(const uint64_t*)&p.ctrl[r * 4] / (uint64_t)p.G) & 1u);
   for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < p.B; s += gridDim.x * blockDim.x) {
     if (p.out_slot_pos) p.out_slot_pos[(size_t)r * p.B + s] = p.slot_pos[((size_t)r * 2 + cur) * p.B + s];
     if (p.out_lru) p.out_lru[(size_t)r * p.B + s] = p.lru[((size_t)r * 2 + cur) * p.Bpad + s];

@@ -46,12 +46,12 @@ struct Layout {
   int Bpad = 0;
   int S = 1;        // attention chunks per request
   size_t ctrl = 0, slot_pos = 0, lru = 0, plan = 0, page_table = 0, newest = 0, host_base = 0,
-         attn_part = 0, attn_counter = 0, total = 0;
+         attn_part = 0, total = 0;
 };
 
 int attn_chunks(const hs_config& c) {
-  // enough workgroups to cover the GPU's 256 CUs about twice, chunks of >= 64 tokens
-  int S = (512 + c.num_requests - 1) / c.num_requests;
+  // about one workgroup per CU (256 CUs) over all requests, chunks of >= 64 entries
+  int S = (256 + c.num_requests - 1) / c.num_requests;
   const int max_s = (c.top_k + 63) / 64;
   if (S > max_s) S = max_s;
   if (S < 1) S = 1;
@@ -74,7 +74,6 @@ Layout make_layout(const hs_config& c) {
   L.newest = take(R * sizeof(int32_t));
   L.host_base = take(R * sizeof(void*));
   L.attn_part = take(size_t(c.num_layers) * R * L.S * kPartStride * sizeof(float));
-  L.attn_counter = take(size_t(c.num_layers) * R * sizeof(uint32_t));
   L.total = o;
   return L;
 }
@@ -143,7 +142,6 @@ struct hs_ctx {
   float* attn_part(int l) {
     return (float*)(ws + lay.attn_part) + size_t(l) * cfg.num_requests * lay.S * kPartStride;
   }
-  uint32_t* attn_counter(int l) { return (uint32_t*)(ws + lay.attn_counter) + size_t(l) * cfg.num_requests; }
   int64_t host_layer_off(int l) const { return int64_t(l) * cfg.max_positions * cfg.record_bytes; }
   int64_t hot_req_stride() const { return int64_t(cfg.num_layers) * (cfg.buffer_slots + 1) * cfg.record_bytes; }
   int64_t hot_layer_off(int l) const { return int64_t(l) * (cfg.buffer_slots + 1) * cfg.record_bytes; }
@@ -202,7 +200,6 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
   h->hot = (uint8_t*)d_hot;
   h->ws = (uint8_t*)d_workspace;
   h->hash_bits = resolve_hash_bits(cfg->top_k);
-  h->lds_bytes = resolve_lds(cfg->top_k, cfg->buffer_slots, h->hash_bits).total;
   if (cfg->wgs_per_request > 0) {
     h->G = cfg->wgs_per_request;
   } else {
@@ -215,6 +212,12 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, h->device);
   if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetDeviceProperties"); }
+  // hash table of 4k entries (a quarter full), or 2k (half full) when LDS is short
+  h->lds_bytes = resolve_lds(cfg->top_k, cfg->buffer_slots, h->hash_bits).total;
+  if (h->lds_bytes > prop.sharedMemPerBlock) {
+    h->hash_bits -= 1;
+    h->lds_bytes = resolve_lds(cfg->top_k, cfg->buffer_slots, h->hash_bits).total;
+  }
   if (h->lds_bytes > prop.sharedMemPerBlock) {
     size_t need = h->lds_bytes;
     free_ctx(h);
@@ -387,7 +390,7 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
   if ((uintptr_t)d_q % 16) return fail(HS_EINVAL, "q must be 16-byte aligned");
   AttnParams p{};
   p.q = (const uint16_t*)d_q; p.slots = d_slots; p.out = d_out; p.part = h->attn_part(layer);
-  p.counter = h->attn_counter(layer); p.num_reqs = d_num_reqs; p.hot = h->hot;
+  p.num_reqs = d_num_reqs; p.hot = h->hot;
   p.hot_req_stride = h->hot_req_stride(); p.hot_layer_off = h->hot_layer_off(layer);
   p.R = h->cfg.num_requests; p.k = h->cfg.top_k; p.B = h->cfg.buffer_slots; p.heads = heads;
   p.value_dim = value_dim; p.S = h->lay.S;
@@ -408,7 +411,7 @@ hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32
   p.ctrl = h->ctrl(a); p.slot_pos = h->slot_pos(a); p.lru = h->lru(a);
   p.newest = (h->cfg.flags & HS_CFG_NEWEST_SLOT) ? h->newest() : nullptr;
   p.out_slot_pos = d_slot_pos; p.out_lru = d_lru; p.out_newest = d_newest;
-  p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad;
+  p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad; p.G = h->G;
   HS_HIP(launch_export(p, (hipStream_t)stream));
   return HS_OK;
 }

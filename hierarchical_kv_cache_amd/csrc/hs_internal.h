@@ -10,7 +10,6 @@
 namespace hs {
 
 constexpr int kResolveThreads = 1024;  // 16 wave64s: one workgroup resolves one request
-constexpr int kMaxScanPasses = 16;     // block scans cover up to 16 * 1024 elements (B, k <= 16384)
 constexpr int kMaxSlots = 16384;
 constexpr int kMaxTopK = 16384;
 constexpr int kMaxRecordBytes = 16384;
@@ -20,26 +19,28 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // LDS carve-up of the resolve kernel (shared by host sizing and device code).
 struct ResolveLds {
-  size_t hkey, selp, selslot, hval, victim, missidx, sflag, scratch, total;
+  size_t htab, selp, selslot, victim, missidx, vmiss, sflag, scratch, total;
 };
 __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits) {
   ResolveLds L;
   size_t o = 0;
   const size_t H = size_t(1) << hash_bits;
-  L.hkey = o;    o = align_up(o + 4 * H, 16);
+  L.htab = o;    o = align_up(o + 4 * H, 16);
   L.selp = o;    o = align_up(o + 4 * size_t(k), 16);
   L.selslot = o; o = align_up(o + 4 * size_t(k), 16);
-  L.hval = o;    o = align_up(o + 2 * H, 16);
   L.victim = o;  o = align_up(o + 2 * size_t(k), 16);
   L.missidx = o; o = align_up(o + 2 * size_t(k), 16);
+  L.vmiss = o;   o = align_up(o + 2 * size_t(B), 16);
   L.sflag = o;   o = align_up(o + size_t(B), 16);
-  L.scratch = o; o = align_up(o + 4 * size_t(kMaxScanPasses * (kResolveThreads / 64) + 8), 16);
+  L.scratch = o; o = align_up(o + 4 * size_t(4 * (kResolveThreads / 64) + 8), 16);
   L.total = o;
   return L;
 }
+int resolve_elems_per_thread(int k, int B);
 
-// Per-anchor metadata in the caller's workspace.  ctrl per request:
-// [0] epoch (which ping-pong half is current), [1] workgroups arrived this launch,
+// Per-anchor metadata in the caller's workspace.  ctrl per request (uint32 x 4):
+// [0..1] 64-bit count of resolve workgroups run (launches = count / G; the parity of
+// the launch count names the ping-pong half holding the current metadata),
 // [2] miss-plan count, [3] unused.
 struct ResolveParams {
   const int32_t* sel;        // [R][kb]
@@ -86,8 +87,7 @@ struct AttnParams {
   const uint16_t* q;         // [R][heads][576] bf16
   const int32_t* slots;      // [R][k]
   float* out;                // [R][heads][value_dim]
-  float* part;               // [R][S][kPartStride] partial results
-  uint32_t* counter;         // [R] workgroups done (reset by the combining workgroup)
+  float* part;               // [R][S][kPartStride] partial results of the S chunks
   const int32_t* num_reqs;
   const uint8_t* hot;        // layer 0 base
   int64_t hot_req_stride, hot_layer_off;
@@ -103,7 +103,7 @@ struct ExportParams {
   int32_t* out_slot_pos;
   int32_t* out_lru;
   int32_t* out_newest;
-  int32_t R, B, Bpad;
+  int32_t R, B, Bpad, G;
 };
 
 struct InitParams {
@@ -133,5 +133,6 @@ constexpr int kAttnMaxHeads = 16;
 constexpr int kAttnDk = 576;
 constexpr int kAttnDv = 512;
 constexpr int kPartStride = kAttnMaxHeads * kAttnDv + 2 * kAttnMaxHeads;
+constexpr int kAttnMaxChunks = 256;  // top_k <= 16384 in chunks of >= 64 entries
 
 }  // namespace hs

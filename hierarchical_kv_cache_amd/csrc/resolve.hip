@@ -4,24 +4,34 @@
 // Stages ("HiSparse 深度解析" (gentlecold.top) §3.5; "推理系统基础设施手记（六）：
 // HiSparse" (naphjohn.github.io) §3):
 //   1 stage    selected positions -> LDS open-addressing hash (Knuth
-//              multiplicative hash, compare-and-swap insertion)
+//              multiplicative hash, linear probing)
 //   2 mark     every slot's stored position probed in the hash: hit or evictable
-//   3 scan     wave64 ballot/popcount ranks: misses numbered in list order,
-//              evictable slots numbered in LRU order, the j-th evictable is the
-//              victim of the j-th miss; new LRU order = untouched evictables (old
-//              order), then filled victims, then hits (§3.3: hits rank newer)
+//   3 scan     block-wide ranks (wave64 ballot + mbcnt, one LDS carry step):
+//              misses numbered in list order, evictable slots numbered in LRU
+//              order, the j-th evictable is the victim of the j-th miss; new LRU
+//              order = untouched evictables (old order), then filled victims,
+//              then hits (§3.3: hits rank newer than this step's fetches)
 //   4 fetch    missed records copied from pinned host memory with 16-byte
 //              non-temporal loads, flattened over (miss, 16-byte chunk)
 //   5 publish  page table, slot map, slots aligned with the selection order
 //
 // MI355X layout of the work.  G workgroups serve one request.  Each of them
 // recomputes stages 1-3 from the current metadata (cheap, all in LDS) and
-// copies its 1/G share of the missed bytes, so that a single request can
-// keep enough loads in flight to fill the host link; only workgroup 0 writes
-// the new metadata.  The slot map and the LRU order are ping-ponged: readers
-// use half `epoch & 1`, workgroup 0 writes the other half, and the last
-// workgroup of a request to arrive flips the epoch.  No workgroup ever waits
-// on another.
+// copies its 1/G share of the missed bytes, so that a single request keeps
+// enough loads in flight to fill the host link; only workgroup 0 writes the
+// new metadata.  The slot map and the LRU order are ping-ponged: a 64-bit
+// launch counter per request (each workgroup adds one) numbers the launch,
+// its parity names the half holding the current metadata, workgroup 0
+// writes the other half.  No workgroup waits on another.
+//
+// Latency shape (the all-hit call is bounded by launch and memory latency,
+// not bandwidth): every global read the kernel needs -- the selection, both
+// halves of the slot map and LRU order, the launch counter -- is issued at entry, so
+// the kernel pays about one memory round trip before its LDS work.  Threads
+// own contiguous runs of slots / LRU positions / selection entries, loaded
+// as vectors; hash insertion uses plain LDS stores and a read-back instead
+// of atomics (which the LDS serialises lane by lane); all probes of a thread
+// are in flight together; two two-field rank scans order everything.
 #include "hs_internal.h"
 
 namespace hs {
@@ -29,82 +39,124 @@ namespace {
 
 constexpr int NT = kResolveThreads;
 constexpr int NW = NT / 64;
-constexpr int32_t kEmpty = -1;
+constexpr uint64_t kEmpty = ~0ull;  // hash entry: low 32 bits position, high 32 bits list index
 constexpr int kUnroll = 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t hash_pos(int32_t pos, int bits) {
   return ((uint32_t)pos * 2654435761u) >> (32 - bits);  // Knuth multiplicative hash
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt() {
-  const int lane = threadIdx.x & 63;
-  return lane ? (~0ull >> (64 - lane)) : 0ull;
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Exclusive block-wide ranks of flags.  Element e = p * NT + threadIdx.x for
-// pass p < P; bit p of fbits is its flag.  rank[p] gets the number of set
-// flags at smaller e.  Returns the total.  Contains barriers: every thread of
-// the workgroup must call it.
-__device__ int block_ranks(uint32_t fbits, int P, int (&rank)[kMaxScanPasses], int* scratch) {
+// Exclusive block-wide ranks for two flag sets at once.  Thread t owns elements
+// [t*E, t*E+E) of each set (bit j of a / b = element t*E+j).  Within a wave the
+// rank is the number of set bits in lower lanes (one ballot + mbcnt per bit
+// position); across waves one carry step through LDS.  `buf` holds 2*NW ints
+// and alternates between consecutive calls, so one barrier suffices.
+template <int E>
+__device__ __forceinline__ void block_ranks2(uint32_t a, uint32_t b, uint32_t* buf, int& ra, int& rb,
+                                             int& ta, int& tb) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const uint64_t lt = lanemask_lt();
+  int wa = 0, wb = 0, la = 0, lb = 0;
 #pragma unroll
-  for (int p = 0; p < kMaxScanPasses; ++p) {
-    if (p < P) {
-      const uint64_t m = __ballot((fbits >> p) & 1u);
-      rank[p] = __popcll(m & lt);
-      if (lane == 0) scratch[p * NW + wid] = __popcll(m);
-    }
+  for (int j = 0; j < E; ++j) {
+    const uint64_t ma = __ballot((a >> j) & 1u);
+    const uint64_t mb = __ballot((b >> j) & 1u);
+    la += lanes_below(ma);
+    lb += lanes_below(mb);
+    wa += __popcll(ma);
+    wb += __popcll(mb);
+  }
+  if (lane == 0) {
+    buf[wid] = (uint32_t)wa;
+    buf[NW + wid] = (uint32_t)wb;
   }
   __syncthreads();
-  if (wid == 0) {
-    // exclusive scan of the n = P * NW wave counts, four per lane (n <= 256)
-    const int n = P * NW;
-    int v[4], s = 0;
+  int ba = 0, bb = 0;
+  ta = 0;
+  tb = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = lane * 4 + j;
-      v[j] = idx < n ? scratch[idx] : 0;
-      s += v[j];
-    }
-    int incl = s;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
-    int run = incl - s;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = lane * 4 + j;
-      if (idx < n) scratch[idx] = run;
-      run += v[j];
-    }
-    if (lane == 63) scratch[kMaxScanPasses * NW] = incl;
+  for (int w = 0; w < NW; ++w) {
+    const int ca = (int)buf[w], cb = (int)buf[NW + w];
+    if (w < wid) { ba += ca; bb += cb; }
+    ta += ca;
+    tb += cb;
   }
-  __syncthreads();
-#pragma unroll
-  for (int p = 0; p < kMaxScanPasses; ++p)
-    if (p < P) rank[p] += scratch[p * NW + wid];
-  const int total = scratch[kMaxScanPasses * NW];
-  __syncthreads();
-  return total;
+  ra = ba + la;
+  rb = bb + lb;
 }
 
+// E consecutive int32 elements base .. base+E-1 of src (n valid, `fill` past the end);
+// 16-byte vector loads when the run is whole and aligned.
+template <int E>
+__device__ __forceinline__ void load_run32(const int32_t* __restrict__ src, int n, int base, bool vec,
+                                           int32_t (&out)[E], int32_t fill) {
+  if constexpr (E % 4 == 0) {
+    if (vec && base + E <= n) {
+#pragma unroll
+      for (int v = 0; v < E / 4; ++v) {
+        const u32x4 x = *((const u32x4*)(src + base) + v);
+        out[4 * v + 0] = (int32_t)x[0];
+        out[4 * v + 1] = (int32_t)x[1];
+        out[4 * v + 2] = (int32_t)x[2];
+        out[4 * v + 3] = (int32_t)x[3];
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < E; ++j) out[j] = (base + j < n) ? src[base + j] : fill;
+}
+
+// The same for int16 elements (8 per 16-byte load, 4 per 8-byte load).
+template <int E>
+__device__ __forceinline__ void load_run16(const int16_t* __restrict__ src, int n, int base, bool vec,
+                                           int16_t (&out)[E], int16_t fill) {
+  if constexpr (E >= 4) {
+    if (vec && base + E <= n) {
+      if constexpr (E == 4) {
+        const u32x2 x = *(const u32x2*)(src + base);
+        out[0] = (int16_t)(x[0] & 0xFFFFu); out[1] = (int16_t)(x[0] >> 16);
+        out[2] = (int16_t)(x[1] & 0xFFFFu); out[3] = (int16_t)(x[1] >> 16);
+      } else {
+#pragma unroll
+        for (int v = 0; v < E / 8; ++v) {
+          const u32x4 x = *((const u32x4*)(src + base) + v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            out[8 * v + 2 * q] = (int16_t)(x[q] & 0xFFFFu);
+            out[8 * v + 2 * q + 1] = (int16_t)(x[q] >> 16);
+          }
+        }
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < E; ++j) out[j] = (base + j < n) ? src[base + j] : fill;
+}
+
+// E: slots (and LRU positions) per thread, a power of two; selection entries per
+// thread EK = ceil(k / NT) <= E.
+template <int E>
 __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits);
-  int32_t* hkey = (int32_t*)(smem + Ly.hkey);        // [H] selected positions (keys)
-  int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] expanded selection
-  int32_t* selslot = (int32_t*)(smem + Ly.selslot);  // [k] >= 0 slot of a hit, -1 miss
-  int16_t* hval = (int16_t*)(smem + Ly.hval);        // [H] list index of each key
+  int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
+  int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] expanded selection (the hash keys)
+  int32_t* selslot = (int32_t*)(smem + Ly.selslot);  // [k] slot of a hit or the newest, -1 miss
   int16_t* victim = (int16_t*)(smem + Ly.victim);    // [k] slot given to miss j
   int16_t* missidx = (int16_t*)(smem + Ly.missidx);  // [k] list index of miss j
+  int16_t* vmiss = (int16_t*)(smem + Ly.vmiss);      // [B] miss served by a victim slot
   uint8_t* sflag = (uint8_t*)(smem + Ly.sflag);      // [B] 0 evictable, 1 hit, 2 victim
-  int* scratch = (int*)(smem + Ly.scratch);          // scan carries + shared scalars
-  int* sh = scratch + kMaxScanPasses * NW + 1;       // [0] epoch [1] error bits [2] newest hits
+  uint32_t* carry = (uint32_t*)(smem + Ly.scratch);  // 2 x 2 x NW scan carries
+  int* sh = (int*)(carry + 4 * NW);                  // [0] error bits [1] newest hits [2] half
 
   const int tid = threadIdx.x;
   const int r = blockIdx.x % p.R;
@@ -117,68 +169,138 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   }
   const int H = 1 << p.hash_bits;
   const uint32_t hmask = (uint32_t)H - 1;
+  const int e0 = tid * E;  // first slot / LRU position of this thread
+  const int EK = (p.k + NT - 1) / NT;
+  const int i0 = tid * EK;  // first selection entry of this thread
 
-  if (tid == 0) {
-    sh[0] = (int)__hip_atomic_load(&p.ctrl[r * 4], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    sh[1] = 0;
-    sh[2] = 0;
-  }
-  for (int h = tid; h < H; h += NT) hkey[h] = kEmpty;
-  __syncthreads();
-
-  const uint32_t epoch = (uint32_t)sh[0];
-  const int cur = epoch & 1, nxt = cur ^ 1;
-  const int32_t* sp_old = p.slot_pos + ((size_t)r * 2 + cur) * p.B;
-  int32_t* sp_new = p.slot_pos + ((size_t)r * 2 + nxt) * p.B;
-  const int16_t* lru_old = p.lru + ((size_t)r * 2 + cur) * p.Bpad;
-  int16_t* lru_new = p.lru + ((size_t)r * 2 + nxt) * p.Bpad;
+  // ---- every global read up front -------------------------------------------------------
+  // Launch counter: every launch adds G per request, so (count before / G) numbers this
+  // launch; its parity picks the ping-pong half that holds the current metadata.  The
+  // returned value is needed only after stage 1, so its latency hides behind the loads.
+  uint64_t launches = 0;
+  if (tid == 0)
+    launches = __hip_atomic_fetch_add((uint64_t*)&p.ctrl[r * 4], 1ull, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) / (uint64_t)p.G;
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
-
-  // ---- stage 1: expand blocks, validate, hash the selected positions ----
-  uint32_t err = 0;
   const int32_t* selr = p.sel + (size_t)r * p.kb;
-  for (int i = tid; i < p.k; i += NT) {
-    int64_t pos64;
-    if (p.bt_shift) {
-      const int32_t b = selr[i >> p.bt_shift];
-      pos64 = ((int64_t)b << p.bt_shift) + (i & ((1 << p.bt_shift) - 1));
-    } else {
-      pos64 = selr[i];
-    }
+  int32_t raw[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int i = i0 + j;
+    raw[j] = (j < EK && i < p.k) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
+  }
+  const bool bvec = (p.B % E) == 0;
+  int32_t spa[E], spb[E];
+  int16_t lra[E], lrb[E];
+  load_run32<E>(p.slot_pos + ((size_t)r * 2 + 0) * p.B, p.B, e0, bvec, spa, -1);
+  load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
+  load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, e0, bvec, lra, 0);
+  load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, e0, bvec, lrb, 0);
+  {
+    u32x4* h4 = (u32x4*)htab;
+    const u32x4 e4 = {~0u, ~0u, ~0u, ~0u};
+    for (int h = tid; h < H / 4; h += NT) h4[h] = e4;
+  }
+  if (tid == 0) { sh[0] = 0; sh[1] = 0; }
+  __syncthreads();
+
+  // ---- stage 1: expand blocks, validate, hash the selected positions ----------------------
+  // Insertion in two steps.  (a) Every entry stores its list index into its home bucket of
+  // the empty table with a plain store; after a barrier an entry whose index reads back owns
+  // that bucket, and one that finds another entry of the same position there is a
+  // duplicate.  (b) The entries that lost their home bucket (a small fraction: the table is
+  // at most a quarter full) insert with compare-and-swap linear probing, which never
+  // overwrites a bucket.  LDS atomics are serialised lane by lane, so step (a) keeps most
+  // of the table build off them.
+  uint32_t err = 0;
+  uint32_t pending = 0;
+  uint32_t hh[E];
+  int32_t pos[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int i = i0 + j;
+    pos[j] = -1;
+    hh[j] = 0;
+    if (j >= EK || i >= p.k) continue;
+    const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                     : (int64_t)raw[j];
     if (pos64 < 0 || pos64 >= ctx) {
       err |= HS_ERR_RANGE;
       selp[i] = -1;
       selslot[i] = -2;
       continue;
     }
-    const int32_t pos = (int32_t)pos64;
-    selp[i] = pos;
-    if (pos == newest) {  // the newest token sits in slot B, outside the LRU
+    pos[j] = (int32_t)pos64;
+    selp[i] = pos[j];
+    if (pos[j] == newest) {  // the newest token sits in slot B, outside the LRU
       selslot[i] = p.B;
-      atomicAdd(&sh[2], 1);
+      atomicAdd(&sh[1], 1);
       continue;
     }
     selslot[i] = -1;
-    uint32_t h = hash_pos(pos, p.hash_bits);
-    while (true) {  // the table has >= H/2 empty entries, so the probe ends
-      const int32_t prev = atomicCAS(&hkey[h], kEmpty, pos);
-      if (prev == kEmpty) {
-        hval[h] = (int16_t)i;
-        break;
-      }
-      if (prev == pos) {
-        err |= HS_ERR_DUP;
-        break;
-      }
-      h = (h + 1) & hmask;
+    hh[j] = hash_pos(pos[j], p.hash_bits);
+    htab[hh[j]] = i;
+    pending |= 1u << j;
+  }
+  __syncthreads();  // home-bucket stores and every key (selp) are visible
+  {
+    // branch-free read-back: every read issued before any result is used
+    int32_t own[E], key[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) own[j] = htab[hh[j]];
+#pragma unroll
+    for (int j = 0; j < E; ++j) key[j] = selp[own[j] < 0 ? 0 : own[j]];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const bool act = (pending >> j) & 1u;
+      const bool mine = own[j] == i0 + j;
+      const bool dup = !mine && key[j] == pos[j];
+      if (act && dup) err |= HS_ERR_DUP;
+      if (act && (mine || dup)) pending &= ~(1u << j);
+      if (act && !mine && !dup) hh[j] = (hh[j] + 1) & hmask;
     }
   }
-  if (err) atomicOr((unsigned*)&sh[1], err);
+  // (no barrier: compare-and-swap only fills empty buckets, and every home bucket read
+  // above is already non-empty)
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    while ((pending >> j) & 1u) {
+      const int32_t prev = atomicCAS(&htab[hh[j]], -1, i0 + j);
+      if (prev == -1) {
+        pending &= ~(1u << j);
+      } else if (selp[prev] == pos[j]) {
+        err |= HS_ERR_DUP;
+        pending &= ~(1u << j);
+      } else {
+        hh[j] = (hh[j] + 1) & hmask;
+      }
+    }
+  }
+  if (err) atomicOr((unsigned*)&sh[0], err);
+  if (tid == 0) sh[2] = (int)(launches & 1u);
   __syncthreads();
-  err = (uint32_t)sh[1] | (sh[2] > 1 ? HS_ERR_DUP : 0u);
-  if (err) {  // every workgroup of the request sees the same error: nothing changes
+  err = (uint32_t)sh[0] | (sh[1] > 1 ? HS_ERR_DUP : 0u);
+  const bool h1 = sh[2] != 0;  // current metadata in half 1, new metadata goes to half 0
+  int32_t spo[E];
+  int16_t lro[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    spo[j] = h1 ? spb[j] : spa[j];
+    lro[j] = h1 ? lrb[j] : lra[j];
+  }
+  int16_t* lru_new = p.lru + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.Bpad;
+  int32_t* sp_new = p.slot_pos + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.B;
+
+  if (err) {  // every workgroup of the request sees the same error: the state is carried over
     if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        if (e0 + j < p.B) {
+          sp_new[e0 + j] = spo[j];
+          lru_new[e0 + j] = lro[j];
+        }
+      }
       for (int i = tid; i < p.k; i += NT) p.out[(size_t)r * p.k + i] = -1;
       if (tid == 0 && p.stats) {
         hs_stats st = {0u, 0u, err, 0u};
@@ -188,123 +310,156 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     }
     return;
   }
-  if (tid == 0) {
-    // every workgroup has read the epoch; the last one to arrive flips it for the next launch
-    const uint32_t arrived =
-        __hip_atomic_fetch_add(&p.ctrl[r * 4 + 1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (arrived == (uint32_t)p.G - 1) {
-      __hip_atomic_store(&p.ctrl[r * 4 + 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.ctrl[r * 4], epoch + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- stage 2: mark each slot hit (its position is selected) or evictable --------------
+  uint32_t probing = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    hh[j] = spo[j] >= 0 ? hash_pos(spo[j], p.hash_bits) : 0;
+    if (e0 + j < p.B && spo[j] >= 0) probing |= 1u << j;
+  }
+  uint32_t hitbits = 0;
+  while (probing) {
+    // branch-free probe step: all reads of the thread in flight together
+    int32_t ent[E], key[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) ent[j] = htab[hh[j]];
+#pragma unroll
+    for (int j = 0; j < E; ++j) key[j] = selp[ent[j] < 0 ? 0 : ent[j]];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const bool act = (probing >> j) & 1u;
+      const bool empty = ent[j] < 0;
+      const bool match = !empty && key[j] == spo[j];
+      if (act && match) {
+        selslot[ent[j]] = e0 + j;
+        hitbits |= 1u << j;
+      }
+      if (act && (empty || match)) probing &= ~(1u << j);
+      if (act && !empty && !match) hh[j] = (hh[j] + 1) & hmask;
     }
   }
-
-  // ---- stage 2: mark each slot hit (its position is selected) or evictable ----
-  const int PB = (p.B + NT - 1) / NT;
-  for (int s = tid; s < p.B; s += NT) {
-    const int32_t ps = sp_old[s];
-    uint8_t f = 0;
-    if (ps >= 0) {
-      uint32_t h = hash_pos(ps, p.hash_bits);
-      int32_t key;
-      while ((key = hkey[h]) != kEmpty) {
-        if (key == ps) {
-          selslot[hval[h]] = s;
-          f = 1;
-          break;
-        }
-        h = (h + 1) & hmask;
+  if (e0 < p.B) {
+    bool stored = false;
+    if constexpr (E >= 4) {
+      if (bvec) {
+#pragma unroll
+        for (int v = 0; v < E / 4; ++v)  // four flag bytes per 32-bit LDS store
+          *(uint32_t*)(sflag + e0 + 4 * v) = ((hitbits >> (4 * v)) & 1u) | (((hitbits >> (4 * v + 1)) & 1u) << 8) |
+                                             (((hitbits >> (4 * v + 2)) & 1u) << 16) |
+                                             (((hitbits >> (4 * v + 3)) & 1u) << 24);
+        stored = true;
       }
     }
-    sflag[s] = f;
+    if (!stored) {
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (e0 + j < p.B) sflag[e0 + j] = (hitbits >> j) & 1u;
+    }
   }
   __syncthreads();
 
-  // ---- stage 3: misses in list order, evictables in LRU order, victims ----
-  int rk[kMaxScanPasses];
-  const int PK = (p.k + NT - 1) / NT;
-  uint32_t fb = 0;
+  // ---- stage 3: misses in list order and evictables in LRU order, one scan -------------
+  uint32_t mbits = 0, ebits = 0;
+  {
+    int32_t ss[E];
+    uint8_t sf[E];
 #pragma unroll
-  for (int q = 0; q < kMaxScanPasses; ++q) {
-    const int i = q * NT + tid;
-    if (q < PK && i < p.k && selslot[i] == -1) fb |= 1u << q;
-  }
-  const int m = block_ranks(fb, PK, rk, scratch);
+    for (int j = 0; j < E; ++j) {
+      ss[j] = selslot[min(i0 + j, p.k - 1)];
+      sf[j] = sflag[lro[j]];
+    }
 #pragma unroll
-  for (int q = 0; q < kMaxScanPasses; ++q)
-    if ((fb >> q) & 1u) missidx[rk[q]] = (int16_t)(q * NT + tid);
-
-  int16_t lslot[kMaxScanPasses];
-  fb = 0;
-#pragma unroll
-  for (int q = 0; q < kMaxScanPasses; ++q) {
-    const int e = q * NT + tid;
-    lslot[q] = 0;
-    if (q < PB && e < p.B) {
-      lslot[q] = lru_old[e];
-      if (sflag[lslot[q]] == 0) fb |= 1u << q;
+    for (int j = 0; j < E; ++j) {
+      if (j < EK && i0 + j < p.k && ss[j] == -1) mbits |= 1u << j;
+      if (e0 + j < p.B && sf[j] == 0) ebits |= 1u << j;
     }
   }
-  const int E = block_ranks(fb, PB, rk, scratch);
+  int rm, re, m, E_;
+  block_ranks2<E>(mbits, ebits, carry, rm, re, m, E_);  // m misses, E_ evictable slots
 #pragma unroll
-  for (int q = 0; q < kMaxScanPasses; ++q) {
-    if ((fb >> q) & 1u) {
-      if (rk[q] < m) {
-        victim[rk[q]] = lslot[q];
-        sflag[lslot[q]] = 2;
+  for (int j = 0; j < E; ++j) {
+    if ((mbits >> j) & 1u) missidx[rm++] = (int16_t)(i0 + j);
+    if ((ebits >> j) & 1u) {
+      const int s = lro[j];
+      if (re < m) {
+        victim[re] = (int16_t)s;
+        vmiss[s] = (int16_t)re;
+        sflag[s] = 2;
       } else if (g == 0) {
-        lru_new[rk[q] - m] = lslot[q];  // untouched evictables keep their old order
+        lru_new[re - m] = (int16_t)s;  // untouched evictables keep their old order
       }
+      ++re;
     }
   }
   __syncthreads();
 
+  // with several workgroups, workgroup 0 publishes while the others fetch
   if (g == 0) {
-    // filled victims then hits, each group by slot index, after the untouched evictables
-    uint32_t fv = 0, fh = 0;
+    // filled victims, then hits, each by slot index, after the untouched evictables
+    uint32_t vb = 0, hb = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxScanPasses; ++q) {
-      const int s = q * NT + tid;
-      if (q < PB && s < p.B) {
-        const uint8_t f = sflag[s];
-        if (f == 2) fv |= 1u << q;
-        if (f == 1) fh |= 1u << q;
-      }
+    for (int j = 0; j < E; ++j) {
+      const uint8_t f = (e0 + j < p.B) ? sflag[e0 + j] : 0;
+      vb |= (uint32_t)(f == 2) << j;
+      hb |= (uint32_t)(f == 1) << j;
     }
-    int rv[kMaxScanPasses];
-    block_ranks(fv, PB, rv, scratch);
-    block_ranks(fh, PB, rk, scratch);
-#pragma unroll
-    for (int q = 0; q < kMaxScanPasses; ++q) {
-      const int s = q * NT + tid;
-      if ((fv >> q) & 1u) lru_new[E - m + rv[q]] = (int16_t)s;
-      if ((fh >> q) & 1u) lru_new[E + rk[q]] = (int16_t)s;
-    }
-
-    // ---- stage 5: publish ----
+    int rv, rh, tv, th;
+    block_ranks2<E>(vb, hb, carry + 2 * NW, rv, rh, tv, th);
     int32_t* pt = p.page_table + (size_t)r * p.max_positions;
     int32_t* outr = p.out + (size_t)r * p.k;
     int32_t* plan_pos = p.plan + (size_t)r * 2 * p.k;
     int32_t* plan_slot = plan_pos + p.k;
-    for (int j = tid; j < m; j += NT) {
-      const int i = missidx[j];
-      const int v = victim[j];
-      const int32_t pos = selp[i];
-      const int32_t old = sp_old[v];
-      if (old >= 0) pt[old] = -1;  // evicted position: host only again
-      pt[pos] = v;
-      sp_new[v] = pos;
-      outr[i] = v;
-      if (record) {
-        plan_pos[j] = pos;
-        plan_slot[j] = v;
+
+    // ---- stage 5: publish (every value is already on chip) ----
+    int32_t spn[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int s = e0 + j;
+      spn[j] = spo[j];
+      if (s >= p.B) continue;
+      if ((vb >> j) & 1u) {
+        lru_new[E_ - m + rv++] = (int16_t)s;
+        const int jm = vmiss[s];
+        const int i = missidx[jm];
+        const int32_t np = selp[i];
+        if (spo[j] >= 0) pt[spo[j]] = -1;  // the evicted position is host-only again
+        pt[np] = s;
+        spn[j] = np;
+        outr[i] = s;
+        if (record) {
+          plan_pos[jm] = np;
+          plan_slot[jm] = s;
+        }
+      } else if ((hb >> j) & 1u) {
+        lru_new[E_ + rh++] = (int16_t)s;
       }
     }
-    for (int i = tid; i < p.k; i += NT) {
-      const int s = selslot[i];
-      if (s >= 0) outr[i] = s;
+    bool stored = false;
+    if constexpr (E % 4 == 0) {
+      if (bvec && e0 + E <= p.B) {
+#pragma unroll
+        for (int v = 0; v < E / 4; ++v) {
+          const u32x4 x = {(uint32_t)spn[4 * v], (uint32_t)spn[4 * v + 1], (uint32_t)spn[4 * v + 2],
+                           (uint32_t)spn[4 * v + 3]};
+          *((u32x4*)(sp_new + e0) + v) = x;
+        }
+        stored = true;
+      }
     }
-    for (int s = tid; s < p.B; s += NT)
-      if (sflag[s] != 2) sp_new[s] = sp_old[s];
+    if (!stored) {
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (e0 + j < p.B) sp_new[e0 + j] = spn[j];
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = i0 + j;
+      if (j < EK && i < p.k) {
+        const int s = selslot[i];
+        if (s >= 0) outr[i] = s;
+      }
+    }
     if (tid == 0) {
       if (p.stats) {
         hs_stats st = {(uint32_t)(p.k - m), (uint32_t)m, 0u, 0u};
@@ -312,17 +467,20 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       }
       if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;
     }
+    if (p.G > 1) return;
   }
 
-  // ---- stage 4: fetch the missed records from pinned host memory ----
+  // ---- stage 4: fetch the missed records from pinned host memory ----------------------
   if (!(p.flags & HS_SKIP_IO) && m > 0) {
+    const int nf = p.G > 1 ? p.G - 1 : 1;  // fetching workgroups
+    const int gf = p.G > 1 ? g - 1 : 0;
     const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
     uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
     const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
     const float invC = 1.0f / (float)C;
-    const int total = m * C;  // <= 2^24: exact in float
-    const int stride = p.G * NT;
-    for (int f0 = g * NT + tid; f0 < total; f0 += stride * kUnroll) {
+    const int total = m * C;  // < 2^24: exact in float
+    const int stride = nf * NT;
+    for (int f0 = gf * NT + tid; f0 < total; f0 += stride * kUnroll) {
       u32x4 v[kUnroll];
       int jj[kUnroll], cc[kUnroll];
 #pragma unroll
@@ -351,16 +509,40 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   }
 }
 
+template <int E>
+hipError_t launch_e(const ResolveParams& p, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL(resolve_kernel<E>, dim3(p.R * p.G), dim3(NT), lds, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+int resolve_elems_per_thread(int k, int B) {
+  const int n = (k > B ? k : B);  // one run of E covers both the selection and the slots
+  const int e = (n + NT - 1) / NT;
+  int E = 1;
+  while (E < e) E <<= 1;
+  return E;
+}
+
 hipError_t set_resolve_lds_limit(size_t lds_bytes) {
-  return hipFuncSetAttribute((const void*)resolve_kernel,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+  const int v = (int)lds_bytes;
+  hipError_t e;
+  if ((e = hipFuncSetAttribute((const void*)resolve_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, v)) != hipSuccess) return e;
+  if ((e = hipFuncSetAttribute((const void*)resolve_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, v)) != hipSuccess) return e;
+  if ((e = hipFuncSetAttribute((const void*)resolve_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, v)) != hipSuccess) return e;
+  if ((e = hipFuncSetAttribute((const void*)resolve_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, v)) != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)resolve_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
 }
 
 hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s) {
-  hipLaunchKernelGGL(resolve_kernel, dim3(p.R * p.G), dim3(NT), lds_bytes, s, p);
-  return hipGetLastError();
+  switch (resolve_elems_per_thread(p.k, p.B)) {
+    case 1: return launch_e<1>(p, lds_bytes, s);
+    case 2: return launch_e<2>(p, lds_bytes, s);
+    case 4: return launch_e<4>(p, lds_bytes, s);
+    case 8: return launch_e<8>(p, lds_bytes, s);
+    default: return launch_e<16>(p, lds_bytes, s);
+  }
 }
 
 }  // namespace hs

@@ -315,3 +315,90 @@ def test_attention_ragged(k, heads):
         p.step_gpu_and_oracle()
         _attn_check(p, t, [0], heads=heads)
     p.close()
+
+
+def test_duplicates_in_many_patterns_then_valid_steps():
+    """Duplicate and out-of-range entries in varied places (home-bucket contests, the
+    compare-and-swap fallback, the newest slot); every request's error bits match the
+    oracle, nothing changes, and later valid steps still agree with the oracle."""
+    R, k, B, lmax = 8, 256, 512, 8192
+    cfg = hk.make_config(R, 1, lmax, k, B, newest_slot=True, wgs_per_request=3)
+    c = hk.HiSparse(cfg)
+    for r in range(R):
+        synth.fill_request(c.host_pool_address(r), r, 1, lmax, lmax)
+    caches = [oracle.Cache(B, lmax, 1152, newest_slot=True) for _ in range(R)]
+    dev = torch.device("cuda")
+    out = torch.empty((R, k), dtype=torch.int32, device=dev)
+    st = torch.zeros((R, 4), dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+    rng = np.random.default_rng(5)
+    ctx = 6000
+    d_ctx = torch.full((R,), ctx, dtype=torch.int32, device=dev)
+
+    def step(sels, newest=None):
+        if newest is not None:
+            recs = synth.records_at(R, 1, [newest] * R)
+            d_new = torch.from_numpy(recs).to(dev)
+            d_pos = torch.full((R,), newest, dtype=torch.int32, device=dev)
+            hk.hs_append(c.h, d_new.data_ptr(), d_pos.data_ptr(), 0, side.cuda_stream)
+            for r in range(R):
+                caches[r].append(newest, recs[r, 0], None)
+        d_sel = torch.from_numpy(np.stack(sels).astype(np.int32)).to(dev)
+        hk.hs_resolve(c.h, 0, d_sel.data_ptr(), d_ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0, 0)
+        torch.cuda.synchronize()
+        got, s = out.cpu().numpy(), st.cpu().numpy()
+        for r in range(R):
+            try:
+                ref = caches[r].resolve(sels[r], ctx, c.host_pool(r)[0])[0]
+                assert s[r, 2] == 0 and np.array_equal(got[r], ref), r
+            except oracle.OracleError as e:
+                assert s[r, 2] == e.code, (r, s[r], e.code)
+                assert (got[r] == -1).all()
+        sp = torch.empty((R, B), dtype=torch.int32, device=dev)
+        lru = torch.empty((R, B), dtype=torch.int32, device=dev)
+        hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0)
+        torch.cuda.synchronize()
+        for r in range(R):
+            ex = caches[r].export()
+            assert np.array_equal(sp.cpu().numpy()[r], ex["slot_pos"]) and \
+                np.array_equal(lru.cpu().numpy()[r], ex["lru"]), r
+
+    def fresh():
+        return [rng.choice(ctx - 1, size=k, replace=False) for _ in range(R)]
+
+    step(fresh())
+    for trial in range(6):
+        sels = fresh()
+        for r in range(R):
+            kind = (trial + r) % 5
+            if kind == 0:   # one pair
+                a, b = rng.choice(k, 2, replace=False)
+                sels[r][b] = sels[r][a]
+            elif kind == 1:  # a triple
+                a, b, d = rng.choice(k, 3, replace=False)
+                sels[r][b] = sels[r][d] = sels[r][a]
+            elif kind == 2:  # many pairs
+                idx = rng.choice(k, 40, replace=False)
+                sels[r][idx[20:]] = sels[r][idx[:20]]
+            elif kind == 3:  # out of range
+                sels[r][rng.integers(k)] = ctx + 5
+            # kind 4: valid
+        step(sels)
+        step(fresh())
+    # the newest position selected twice is a duplicate too
+    sels = fresh()
+    for r in range(R):
+        sels[r][0] = sels[r][1] = ctx - 1
+    step(sels, newest=ctx - 1)
+    step(fresh())
+    c.close()
+
+
+def test_buffer_above_8192_slots():
+    """B = 12000 (16 slots per thread in the kernel's blocked layout), k = 512."""
+    w = W["tiny"].scaled(B=12000, k=512, ctx=65536, steps=6, R=2)
+    p = Pair(w, wgs=2)
+    for _ in range(w.steps):
+        p.step_gpu_and_oracle()
+        p.check_state()
+    p.close()
