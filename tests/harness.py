@@ -4,6 +4,9 @@ Test infrastructure: imports both sides; neither side imports the other.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -66,6 +69,8 @@ class Pair:
         self.d_stats = torch.zeros((w.R, 4), dtype=torch.int32, device=self.dev)
         self.t = 0
         self.newest = None
+        # the oracle's C calls release the GIL: independent caches resolve in parallel
+        self.pool = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
 
     # ---- one decode step ------------------------------------------------------------------
     def ctx_len(self):
@@ -100,15 +105,19 @@ class Pair:
                 hk.hs_prefetch_shared(self.h, l, self.compute.cuda_stream, self.side.cuda_stream)
             stats = self.d_stats.cpu().numpy().copy() if check else None
             nr = w.R if num_reqs is None else num_reqs
-            for r in range(nr):
+
+            def one(r, l=l, ai=ai):
                 pos = expand(self.trace[t, ai, r], w.block_tokens)
-                out, hits, misses, ppos, pslot = self.caches[(r, l)].resolve(pos, ctx, self.ohost[r][l])
-                results[(r, l)] = (out, hits, misses, ppos, pslot)
+                res = self.caches[(r, l)].resolve(pos, ctx, self.ohost[r][l])
                 for ls in range(l + 1, min(l + w.group, w.L)):
-                    oracle.replay(ppos, pslot, self.ohost[r][ls], self.ohot_shared[(r, ls)], self.rec)
+                    oracle.replay(res[3], res[4], self.ohost[r][ls], self.ohot_shared[(r, ls)], self.rec)
+                return res
+
+            for r, res in zip(range(nr), self.pool.map(one, range(nr))):
+                results[(r, l)] = res
                 if check:
-                    assert stats[r, 0] == hits and stats[r, 1] == misses and stats[r, 2] == 0, \
-                        (t, r, l, stats[r], hits, misses)
+                    assert stats[r, 0] == res[1] and stats[r, 1] == res[2] and stats[r, 2] == 0, \
+                        (t, r, l, stats[r], res[1], res[2])
             if check:
                 got = self.d_out[ai].cpu().numpy()
                 for r in range(nr):
@@ -177,6 +186,7 @@ class Pair:
 
     def close(self):
         torch.cuda.synchronize()
+        self.pool.shutdown()
         self.gpu.close()
 
 

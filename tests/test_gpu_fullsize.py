@@ -1,0 +1,89 @@
+"""The workloads at their full sizes, through the C ABI, against the oracle.
+
+Every slot vector and hit/miss count is compared each step; slot maps, LRU
+orders and page tables of every anchor cache at the end; hot-buffer bytes for
+a sample of caches (the whole buffer is gigabytes) plus, for every cache, the
+property that each published slot holds the record of its position.
+"""
+import time
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu]
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import synth  # noqa: E402
+from harness import Pair  # noqa: E402
+
+W = synth.WORKLOADS
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def published_slots_hold_their_records(p, results, samples=64, seed=0):
+    """For every (request, anchor layer): sampled entries of the last step's published slots
+    hold exactly the record of the selected position (the pages' exactness invariant)."""
+    rng = np.random.default_rng(seed)
+    torch.cuda.synchronize()
+    for (r, l), res in results.items():
+        out = res[0]
+        idx = rng.choice(out.size, size=min(samples, out.size), replace=False)
+        pos = p.trace[p.t - 1, p.anchors.index(l), r]
+        if p.w.block_tokens > 1:
+            pos = np.repeat(pos, p.w.block_tokens) * p.w.block_tokens + np.tile(
+                np.arange(p.w.block_tokens), pos.size)
+        rows = p.gpu.hot[r, l, torch.from_numpy(out[idx].astype(np.int64)).cuda()].cpu().numpy()
+        for n, i in enumerate(idx):
+            assert np.array_equal(rows[n], synth.record(r, l, int(pos[i]))), (r, l, i)
+
+
+def run(w, steps, sample_hot, label):
+    t0 = time.time()
+    p = Pair(w, steps=steps)
+    log("%s: set-up %.1f s (host pool %.1f GB)" % (label, time.time() - t0, w.host_bytes(steps) / 1e9))
+    res = None
+    for _ in range(steps):
+        res = p.step_gpu_and_oracle()
+    log("%s: %d steps %.1f s" % (label, steps, time.time() - t0))
+    p.check_state(hot=False)
+    published_slots_hold_their_records(p, res)
+    p.check_hot(*sample_hot)
+    log("%s: checked %.1f s" % (label, time.time() - t0))
+    p.close()
+
+
+@pytest.mark.parametrize("B", synth.BATCHED_B_SWEEP)
+def test_batched_full(B):
+    """32 requests x 16 layers, ctx 32768, k 2048, B in {2048, 4096, 8192}; 6 steps."""
+    run(W["batched"].scaled(B=B), 6, (range(16)[::5], [0, 17, 31]), "batched B=%d" % B)
+
+
+def test_capacity_full():
+    """4 x 4, ctx 1048576 (19.3 GB pinned), 32 blocks of 64 tokens, all 64 steps."""
+    run(W["capacity"], 64, (range(4), range(4)), "capacity")
+
+
+def test_long_full_all_steps():
+    """1 x 8, ctx 131072 (+256), write-through every step, all 256 steps."""
+    w = W["long"]
+    p = Pair(w)
+    for t in range(w.steps):
+        p.step_gpu_and_oracle()
+        if t % 64 == 63:
+            p.check_state()
+    p.close()
+
+
+def test_shared_full_shape():
+    """16 requests x 32 layers (8 anchors + 24 shared), the shared-index workload's full shape
+    except the context: the box pins at most about 64 GiB of host memory, so the 131072-token
+    context (77.3 GB of pinned records) is cut to 98304 tokens (58.0 GB, 16 per-request
+    pinned allocations).  12 steps, shared layers replayed on a side stream."""
+    run(W["shared"].scaled(ctx=98304), 12, (range(0, 32, 5), [0, 9, 15]), "shared ctx 98304")
