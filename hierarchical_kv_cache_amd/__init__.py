@@ -25,7 +25,7 @@ LIB_PATH = _build.LIB
 HS_OK, HS_EINVAL, HS_ENOMEM, HS_EHIP, HS_ESTATE = 0, -1, -2, -3, -4
 HS_CFG_NEWEST_SLOT = 1
 HS_RECORD_PLAN, HS_SKIP_IO = 1, 2
-HS_ERR_DUP, HS_ERR_RANGE = 1, 2
+HS_ERR_DUP, HS_ERR_RANGE, HS_ERR_STATE = 1, 2, 4
 
 
 class hs_config(ctypes.Structure):

@@ -30,6 +30,7 @@ constexpr int KSTEPS = kAttnDk / 32;    // 18
 constexpr int CHUNKS = kAttnDk * 2 / 16;  // 72 16-byte chunks per record
 constexpr int CT = kAttnDv / 4 / 16;    // 8 channel tiles of 16 per wave
 constexpr int GATHER = TT * CHUNKS / AT;  // 18 16-byte chunks per thread per tile
+constexpr int QS = kAttnDk * 2 + 16;       // LDS stride of a query row (padded off the bank period)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   uint32_t u = __float_as_uint(x);
@@ -38,13 +39,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__global__ void __launch_bounds__(AT, 2) attn_kernel(AttnParams p) {
+__global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char rows[TT * RS];
+  __shared__ __attribute__((aligned(16))) unsigned char qs[16 * QS];  // q rows, zero past `heads`
   __shared__ __attribute__((aligned(16))) uint16_t phi[2][16][32];  // [32-token block][head][k]
   __shared__ __attribute__((aligned(16))) uint16_t plo[2][16][32];
   __shared__ float smax[4][16];
   __shared__ float ssum[4][16];
-  __shared__ int s_slot[TT];
+  __shared__ int s_slot[kAttnMaxChunk];
 
   int r, s;
   if (p.R >= 8) {  // chunks of one request on one XCD (workgroups go round-robin over 8 XCDs)
@@ -62,17 +64,60 @@ __global__ void __launch_bounds__(AT, 2) attn_kernel(AttnParams p) {
   const int lane = tid & 63, w = tid >> 6, col = lane & 15, qd = lane >> 4;
   const int t_begin = s * p.chunk;
   const int t_end = min(p.k, t_begin + p.chunk);
+  const int n_tok = t_end - t_begin;
 
-  // Q fragments (A operand of the score MFMA): lane holds q[head = col][32 ks + 8 qd + 0..7]
-  bf16x8 qa[KSTEPS];
+  const uint8_t* hot_r = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+  const int32_t* slots_r = p.slots + (size_t)r * p.k;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+
+  // the chunk's slots and the queries, both in LDS, loaded together
   {
-    const uint16_t* qr = p.q + ((size_t)r * p.heads + col) * kAttnDk + qd * 8;
+    constexpr int QL = (16 * CHUNKS + AT - 1) / AT;  // 5 query chunks per thread
+    constexpr int SL = kAttnMaxChunk / AT;           // 4 slots per thread
+    u32x4 qv[QL];
+    int sv[SL];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      if (col < p.heads) qa[ks] = *(const bf16x8*)(qr + ks * 32);
-      else for (int j = 0; j < 8; ++j) qa[ks][j] = (__bf16)0.0f;
+    for (int u = 0; u < SL; ++u) {
+      const int i = tid + u * AT;
+      sv[u] = i < n_tok ? slots_r[t_begin + i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < QL; ++u) {
+      const int f = tid + u * AT;
+      const int h = f / CHUNKS, c = f - h * CHUNKS;
+      qv[u] = (f < 16 * CHUNKS && h < p.heads)
+                  ? *((const u32x4*)(p.q + ((size_t)r * p.heads + h) * kAttnDk) + c) : zero4;
+    }
+#pragma unroll
+    for (int u = 0; u < SL; ++u)
+      if (tid + u * AT < n_tok) s_slot[tid + u * AT] = sv[u];
+#pragma unroll
+    for (int u = 0; u < QL; ++u) {
+      const int f = tid + u * AT;
+      const int h = f / CHUNKS, c = f - h * CHUNKS;
+      if (f < 16 * CHUNKS) *(u32x4*)(qs + h * QS + c * 16) = qv[u];
     }
   }
+  __syncthreads();
+
+  // records of the tile starting at token t0: 18 16-byte loads per thread, all in flight
+  u32x4 stage[GATHER];
+  auto gather = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < GATHER; ++u) {
+      const int f = tid + u * AT;
+      const int row = f / CHUNKS, c = f - row * CHUNKS;
+      const int tok = t0 + row;
+      // past the end: exact zeros; a slot outside [0, B]: NaN, so the output shows it
+      if (tok >= t_end) {
+        stage[u] = zero4;
+      } else {
+        const int sl = s_slot[tok - t_begin];
+        stage[u] = (sl >= 0 && sl <= p.B) ? *((const u32x4*)(hot_r + (size_t)sl * p.rec_bytes) + c) : nan4;
+      }
+    }
+  };
 
   const float sl2 = p.scale * 1.4426950408889634f;  // scores kept in log2 units
   float m_run[4], l_lane[4];
@@ -82,45 +127,27 @@ __global__ void __launch_bounds__(AT, 2) attn_kernel(AttnParams p) {
 #pragma unroll
   for (int c = 0; c < CT; ++c) o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const uint8_t* hot_r = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
-  const int32_t* slots_r = p.slots + (size_t)r * p.k;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-
+  gather(t_begin);
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     __syncthreads();  // the previous tile is no longer read
-    if (tid < TT) s_slot[tid] = (t0 + tid < t_end) ? slots_r[t0 + tid] : -2;
-    __syncthreads();
-    // gather the tile's records into LDS: two rounds of 9 16-byte loads per thread in flight
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 v[GATHER / 2];
-#pragma unroll
-      for (int u = 0; u < GATHER / 2; ++u) {
-        const int f = tid + (half * (GATHER / 2) + u) * AT;
-        const int row = f / CHUNKS, c = f - row * CHUNKS;
-        const int sl = s_slot[row];
-        // past the end: exact zeros; a slot outside [0, B]: NaN, so the output shows it
-        v[u] = sl == -2 ? zero4
-                        : ((sl >= 0 && sl <= p.B) ? *((const u32x4*)(hot_r + (size_t)sl * p.rec_bytes) + c)
-                                                  : nan4);
-      }
-#pragma unroll
-      for (int u = 0; u < GATHER / 2; ++u) {
-        const int f = tid + (half * (GATHER / 2) + u) * AT;
-        const int row = f / CHUNKS, c = f - row * CHUNKS;
-        *(u32x4*)(rows + row * RS + c * 16) = v[u];
-      }
+    for (int u = 0; u < GATHER; ++u) {
+      const int f = tid + u * AT;
+      const int row = f / CHUNKS, c = f - row * CHUNKS;
+      *(u32x4*)(rows + row * RS + c * 16) = stage[u];
     }
     __syncthreads();
+    if (t0 + TT < t_end) gather(t0 + TT);  // the next tile's loads fly during this tile's math
 
     // scores of tokens 16w .. 16w+15: lane gets s[head = 4 qd + i][token = col]
     f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
     const unsigned char* krow = rows + (16 * w + col) * RS + qd * 16;
+    const unsigned char* qrow = qs + col * QS + qd * 16;  // A operand: q[head = col][32 ks + 8 qd + j]
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 qa = *(const bf16x8*)(qrow + ks * 64);
       const bf16x8 kb = *(const bf16x8*)(krow + ks * 64);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, sacc, 0, 0, 0);
     }
     const bool valid = (t0 + 16 * w + col) < t_end;
     float sv[4], mx[4];
@@ -249,8 +276,15 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p) {
   const int c = tid * 4;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   const float* base = pr + hh * kAttnDv + c;
-#pragma unroll 8
-  for (int q = 0; q < p.S; ++q) acc += fac[q] * *(const f32x4*)(base + (size_t)q * kPartStride);
+  for (int q0 = 0; q0 < p.S; q0 += 16) {
+    f32x4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      v[u] = q0 + u < p.S ? *(const f32x4*)(base + (size_t)(q0 + u) * kPartStride) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (q0 + u < p.S) acc += fac[q0 + u] * v[u];
+  }
   const float inv = 1.0f / s_den;
   *(f32x4*)(p.out + ((size_t)r * p.heads + hh) * p.value_dim + c) = acc * inv;
 }

@@ -54,6 +54,8 @@ int attn_chunks(const hs_config& c) {
   int S = (256 + c.num_requests - 1) / c.num_requests;
   const int max_s = (c.top_k + 63) / 64;
   if (S > max_s) S = max_s;
+  const int min_s = (c.top_k + kAttnMaxChunk - 1) / kAttnMaxChunk;  // chunks of <= 1024 entries
+  if (S < min_s) S = min_s;
   if (S < 1) S = 1;
   return S;
 }

@@ -19,20 +19,25 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // LDS carve-up of the resolve kernel (shared by host sizing and device code).
 struct ResolveLds {
-  size_t htab, selp, selslot, victim, missidx, vmiss, sflag, scratch, total;
+  size_t htab, selp, selslot, victim, missidx, mrank, vmiss, sflag, wpos, widx, wcap, scratch, total;
 };
 __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits) {
   ResolveLds L;
   size_t o = 0;
   const size_t H = size_t(1) << hash_bits;
+  const int NWv = kResolveThreads / 64;
+  L.wcap = 64 * ((size_t(k) + kResolveThreads - 1) / kResolveThreads);  // misses one wave can own
   L.htab = o;    o = align_up(o + 4 * H, 16);
   L.selp = o;    o = align_up(o + 4 * size_t(k), 16);
   L.selslot = o; o = align_up(o + 4 * size_t(k), 16);
   L.victim = o;  o = align_up(o + 2 * size_t(k), 16);
   L.missidx = o; o = align_up(o + 2 * size_t(k), 16);
+  L.mrank = o;   o = align_up(o + 2 * size_t(k), 16);
   L.vmiss = o;   o = align_up(o + 2 * size_t(B), 16);
   L.sflag = o;   o = align_up(o + size_t(B), 16);
-  L.scratch = o; o = align_up(o + 4 * size_t(4 * (kResolveThreads / 64) + 8), 16);
+  L.wpos = o;    o = align_up(o + 4 * NWv * L.wcap, 16);
+  L.widx = o;    o = align_up(o + 2 * NWv * L.wcap, 16);
+  L.scratch = o; o = align_up(o + 4 * size_t(4 * NWv + 8), 16);
   L.total = o;
   return L;
 }
@@ -134,5 +139,6 @@ constexpr int kAttnDk = 576;
 constexpr int kAttnDv = 512;
 constexpr int kPartStride = kAttnMaxHeads * kAttnDv + 2 * kAttnMaxHeads;
 constexpr int kAttnMaxChunks = 256;  // top_k <= 16384 in chunks of >= 64 entries
+constexpr int kAttnMaxChunk = 1024;  // entries per chunk (their slots are staged in LDS)
 
 }  // namespace hs

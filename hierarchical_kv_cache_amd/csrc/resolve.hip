@@ -41,6 +41,7 @@ constexpr int NT = kResolveThreads;
 constexpr int NW = NT / 64;
 constexpr uint64_t kEmpty = ~0ull;  // hash entry: low 32 bits position, high 32 bits list index
 constexpr int kUnroll = 4;
+constexpr int kEarly = 4;  // 16-byte chunks per lane loaded before the victims are known
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -142,9 +143,9 @@ __device__ __forceinline__ void load_run16(const int16_t* __restrict__ src, int 
   for (int j = 0; j < E; ++j) out[j] = (base + j < n) ? src[base + j] : fill;
 }
 
-// E: slots (and LRU positions) per thread, a power of two; selection entries per
-// thread EK = ceil(k / NT) <= E.
-template <int E>
+// E: slots (and LRU positions) per thread, KE: selection entries per thread (both powers
+// of two, KE <= E, EK = ceil(k / NT) <= KE).
+template <int E, int KE>
 __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits);
@@ -154,6 +155,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   int16_t* victim = (int16_t*)(smem + Ly.victim);    // [k] slot given to miss j
   int16_t* missidx = (int16_t*)(smem + Ly.missidx);  // [k] list index of miss j
   int16_t* vmiss = (int16_t*)(smem + Ly.vmiss);      // [B] miss served by a victim slot
+  int16_t* mrank = (int16_t*)(smem + Ly.mrank);      // [k] miss rank of a list entry
   uint8_t* sflag = (uint8_t*)(smem + Ly.sflag);      // [B] 0 evictable, 1 hit, 2 victim
   uint32_t* carry = (uint32_t*)(smem + Ly.scratch);  // 2 x 2 x NW scan carries
   int* sh = (int*)(carry + 4 * NW);                  // [0] error bits [1] newest hits [2] half
@@ -184,11 +186,28 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
   const int32_t* selr = p.sel + (size_t)r * p.kb;
-  int32_t raw[E];
+  int32_t raw[KE];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
+  for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
     raw[j] = (j < EK && i < p.k) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
+  }
+  // Fetch workgroups (all but workgroup 0 when G > 1) also read the selection entries of
+  // their share of the list, spread over the waves: entry e of the share belongs to wave
+  // e % NW, lane (e / NW) % 64, slot e / NT.
+  const bool io = !(p.flags & HS_SKIP_IO);
+  const bool fetcher = io && (p.G == 1 || g > 0);
+  const int nf = p.G > 1 ? p.G - 1 : 1;
+  const int gf = p.G > 1 ? g - 1 : 0;
+  const int f_lo = (int)((int64_t)p.k * gf / nf);
+  const int f_n = (int)((int64_t)p.k * (gf + 1) / nf) - f_lo;
+  const int wid = tid >> 6, lane = tid & 63;
+  int32_t fraw[KE];
+#pragma unroll
+  for (int q = 0; q < KE; ++q) {
+    const int e = q * NT + lane * NW + wid;
+    const int i = f_lo + e;
+    fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
   }
   const bool bvec = (p.B % E) == 0;
   int32_t spa[E], spb[E];
@@ -203,6 +222,22 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     for (int h = tid; h < H / 4; h += NT) h4[h] = e4;
   }
   if (tid == 0) { sh[0] = 0; sh[1] = 0; }
+  // Misses known early from the page table (kept the exact inverse of the slot map): a
+  // selected position whose entry is -1 is not resident.  Their host loads start right
+  // after stage 1 and land while stages 2-3 run; stage 3 names the slots they go to.
+  int32_t fpos[KE], fpt[KE];
+  const int32_t* ptr = p.page_table + (size_t)r * p.max_positions;
+#pragma unroll
+  for (int q = 0; q < KE; ++q) {
+    const int e = q * NT + lane * NW + wid;
+    const int i = f_lo + e;
+    int64_t pos64 = -1;
+    if (fetcher && e < f_n)
+      pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
+    const bool ok = pos64 >= 0 && pos64 < ctx && pos64 != newest;
+    fpos[q] = ok ? (int32_t)pos64 : -1;
+    fpt[q] = ok ? ptr[pos64] : 0;
+  }
   __syncthreads();
 
   // ---- stage 1: expand blocks, validate, hash the selected positions ----------------------
@@ -215,10 +250,10 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   // of the table build off them.
   uint32_t err = 0;
   uint32_t pending = 0;
-  uint32_t hh[E];
-  int32_t pos[E];
+  uint32_t hh[KE];
+  int32_t pos[KE];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
+  for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
     pos[j] = -1;
     hh[j] = 0;
@@ -246,13 +281,13 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   __syncthreads();  // home-bucket stores and every key (selp) are visible
   {
     // branch-free read-back: every read issued before any result is used
-    int32_t own[E], key[E];
+    int32_t own[KE], key[KE];
 #pragma unroll
-    for (int j = 0; j < E; ++j) own[j] = htab[hh[j]];
+    for (int j = 0; j < KE; ++j) own[j] = htab[hh[j]];
 #pragma unroll
-    for (int j = 0; j < E; ++j) key[j] = selp[own[j] < 0 ? 0 : own[j]];
+    for (int j = 0; j < KE; ++j) key[j] = selp[own[j] < 0 ? 0 : own[j]];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
+    for (int j = 0; j < KE; ++j) {
       const bool act = (pending >> j) & 1u;
       const bool mine = own[j] == i0 + j;
       const bool dup = !mine && key[j] == pos[j];
@@ -264,7 +299,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   // (no barrier: compare-and-swap only fills empty buckets, and every home bucket read
   // above is already non-empty)
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
+  for (int j = 0; j < KE; ++j) {
     while ((pending >> j) & 1u) {
       const int32_t prev = atomicCAS(&htab[hh[j]], -1, i0 + j);
       if (prev == -1) {
@@ -277,6 +312,45 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       }
     }
   }
+  // ---- stage 4, first part: per-wave lists of the page-table misses, host loads issued ----
+  int32_t* wpos = (int32_t*)(smem + Ly.wpos) + wid * Ly.wcap;  // this wave's misses: position
+  int16_t* widx = (int16_t*)(smem + Ly.widx) + wid * Ly.wcap;  // and list index
+  const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
+  const float invC = 1.0f / (float)C;
+  uint32_t fmiss = 0;
+  int mw = 0;  // misses of this wave
+  {
+#pragma unroll
+    for (int q = 0; q < KE; ++q) {
+      const bool miss = fpos[q] >= 0 && fpt[q] < 0;
+      const uint64_t b = __ballot(miss);
+      if (miss) {
+        fmiss |= 1u << q;
+        const int at = mw + lanes_below(b);
+        wpos[at] = fpos[q];
+        widx[at] = (int16_t)(f_lo + q * NT + lane * NW + wid);
+      }
+      mw += __popcll(b);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
+  uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+  const int wtotal = mw * C;  // 16-byte chunks of this wave's misses
+  u32x4 early[kEarly];
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u) {
+    const int c = lane + 64 * u;
+    if (c < wtotal) {
+      int l = (int)((float)c * invC);
+      int cc = c - l * C;
+      if (cc < 0) { --l; cc += C; }
+      if (cc >= C) { ++l; cc -= C; }
+      early[u] = __builtin_nontemporal_load((const u32x4*)(hbase + (size_t)wpos[l] * (size_t)p.rec_bytes) + cc);
+    }
+  }
+
   if (err) atomicOr((unsigned*)&sh[0], err);
   if (tid == 0) sh[2] = (int)(launches & 1u);
   __syncthreads();
@@ -313,9 +387,10 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
 
   // ---- stage 2: mark each slot hit (its position is selected) or evictable --------------
   uint32_t probing = 0;
+  uint32_t hs2[E];
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    hh[j] = spo[j] >= 0 ? hash_pos(spo[j], p.hash_bits) : 0;
+    hs2[j] = spo[j] >= 0 ? hash_pos(spo[j], p.hash_bits) : 0;
     if (e0 + j < p.B && spo[j] >= 0) probing |= 1u << j;
   }
   uint32_t hitbits = 0;
@@ -323,7 +398,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     // branch-free probe step: all reads of the thread in flight together
     int32_t ent[E], key[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) ent[j] = htab[hh[j]];
+    for (int j = 0; j < E; ++j) ent[j] = htab[hs2[j]];
 #pragma unroll
     for (int j = 0; j < E; ++j) key[j] = selp[ent[j] < 0 ? 0 : ent[j]];
 #pragma unroll
@@ -336,7 +411,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
         hitbits |= 1u << j;
       }
       if (act && (empty || match)) probing &= ~(1u << j);
-      if (act && !empty && !match) hh[j] = (hh[j] + 1) & hmask;
+      if (act && !empty && !match) hs2[j] = (hs2[j] + 1) & hmask;
     }
   }
   if (e0 < p.B) {
@@ -362,24 +437,28 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   // ---- stage 3: misses in list order and evictables in LRU order, one scan -------------
   uint32_t mbits = 0, ebits = 0;
   {
-    int32_t ss[E];
+    int32_t ss[KE];
     uint8_t sf[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      ss[j] = selslot[min(i0 + j, p.k - 1)];
-      sf[j] = sflag[lro[j]];
-    }
+    for (int j = 0; j < KE; ++j) ss[j] = selslot[min(i0 + j, p.k - 1)];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
+    for (int j = 0; j < E; ++j) sf[j] = sflag[lro[j]];
+#pragma unroll
+    for (int j = 0; j < KE; ++j)
       if (j < EK && i0 + j < p.k && ss[j] == -1) mbits |= 1u << j;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
       if (e0 + j < p.B && sf[j] == 0) ebits |= 1u << j;
-    }
   }
   int rm, re, m, E_;
   block_ranks2<E>(mbits, ebits, carry, rm, re, m, E_);  // m misses, E_ evictable slots
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    if ((mbits >> j) & 1u) missidx[rm++] = (int16_t)(i0 + j);
+    if ((mbits >> j) & 1u) {
+      missidx[rm] = (int16_t)(i0 + j);
+      mrank[i0 + j] = (int16_t)rm;
+      ++rm;
+    }
     if ((ebits >> j) & 1u) {
       const int s = lro[j];
       if (re < m) {
@@ -453,7 +532,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
         if (e0 + j < p.B) sp_new[e0 + j] = spn[j];
     }
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
+    for (int j = 0; j < KE; ++j) {
       const int i = i0 + j;
       if (j < EK && i < p.k) {
         const int s = selslot[i];
@@ -470,78 +549,114 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     if (p.G > 1) return;
   }
 
-  // ---- stage 4: fetch the missed records from pinned host memory ----------------------
-  if (!(p.flags & HS_SKIP_IO) && m > 0) {
-    const int nf = p.G > 1 ? p.G - 1 : 1;  // fetching workgroups
-    const int gf = p.G > 1 ? g - 1 : 0;
-    const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
-    uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
-    const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
-    const float invC = 1.0f / (float)C;
-    const int total = m * C;  // < 2^24: exact in float
-    const int stride = nf * NT;
-    for (int f0 = gf * NT + tid; f0 < total; f0 += stride * kUnroll) {
+  // ---- stage 4, second part: the fetched records go to the slots stage 3 chose --------
+  if (fetcher) {
+    // the page table and the hash must agree on every miss of this share
+    uint32_t bad = 0;
+#pragma unroll
+    for (int q = 0; q < KE; ++q) {
+      const int e = q * NT + lane * NW + wid;
+      if (e < f_n && fpos[q] >= 0) bad |= (uint32_t)(((fmiss >> q) & 1u) != (selslot[f_lo + e] == -1));
+    }
+    if (bad && p.stats) atomicOr(&p.stats[r].error, HS_ERR_STATE);
+#pragma unroll
+    for (int u = 0; u < kEarly; ++u) {
+      const int c = lane + 64 * u;
+      if (c < wtotal) {
+        int l = (int)((float)c * invC);
+        int cc = c - l * C;
+        if (cc < 0) { --l; cc += C; }
+        if (cc >= C) { ++l; cc -= C; }
+        const int slot = victim[mrank[widx[l]]];
+        *((u32x4*)(dbase + (size_t)slot * (size_t)p.rec_bytes) + cc) = early[u];
+      }
+    }
+    // a wave with more than kEarly chunks per lane (miss-heavy steps) continues here
+    for (int c0 = lane + 64 * kEarly; c0 < wtotal; c0 += 64 * kUnroll) {
       u32x4 v[kUnroll];
-      int jj[kUnroll], cc[kUnroll];
+      int ll[kUnroll], cc[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int f = f0 + u * stride;
-        if (f < total) {
-          int j = (int)((float)f * invC);
-          int c = f - j * C;
-          if (c < 0) { --j; c += C; }
-          if (c >= C) { ++j; c -= C; }
-          jj[u] = j;
-          cc[u] = c;
-          const u32x4* src =
-              (const u32x4*)(hbase + (size_t)selp[missidx[j]] * (size_t)p.rec_bytes) + c;
-          v[u] = __builtin_nontemporal_load(src);
+        const int c = c0 + 64 * u;
+        if (c < wtotal) {
+          int l = (int)((float)c * invC);
+          int x = c - l * C;
+          if (x < 0) { --l; x += C; }
+          if (x >= C) { ++l; x -= C; }
+          ll[u] = l;
+          cc[u] = x;
+          v[u] = __builtin_nontemporal_load((const u32x4*)(hbase + (size_t)wpos[l] * (size_t)p.rec_bytes) + x);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (f0 + u * stride < total) {
-          u32x4* dst = (u32x4*)(dbase + (size_t)victim[jj[u]] * (size_t)p.rec_bytes) + cc[u];
-          *dst = v[u];
-        }
-      }
+      for (int u = 0; u < kUnroll; ++u)
+        if (c0 + 64 * u < wtotal)
+          *((u32x4*)(dbase + (size_t)victim[mrank[widx[ll[u]]]] * (size_t)p.rec_bytes) + cc[u]) = v[u];
     }
   }
 }
 
-template <int E>
+template <int E, int KE>
 hipError_t launch_e(const ResolveParams& p, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL(resolve_kernel<E>, dim3(p.R * p.G), dim3(NT), lds, s, p);
+  hipLaunchKernelGGL((resolve_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), lds, s, p);
   return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_ke(const ResolveParams& p, size_t lds, hipStream_t s, int KE) {
+  if constexpr (E >= 1) if (KE <= 1) return launch_e<E, 1>(p, lds, s);
+  if constexpr (E >= 2) if (KE <= 2) return launch_e<E, 2>(p, lds, s);
+  if constexpr (E >= 4) if (KE <= 4) return launch_e<E, 4>(p, lds, s);
+  if constexpr (E >= 8) if (KE <= 8) return launch_e<E, 8>(p, lds, s);
+  if constexpr (E >= 16) return launch_e<E, 16>(p, lds, s);
+  return hipErrorInvalidValue;
+}
+
+template <int E>
+hipError_t set_limit_ke(int v) {
+  hipError_t e = hipSuccess;
+  if constexpr (E >= 1) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+  if constexpr (E >= 2) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+  if constexpr (E >= 4) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+  if constexpr (E >= 8) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+  if constexpr (E >= 16) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+  return e;
 }
 
 }  // namespace
 
 int resolve_elems_per_thread(int k, int B) {
-  const int n = (k > B ? k : B);  // one run of E covers both the selection and the slots
+  const int n = (k > B ? k : B);
   const int e = (n + NT - 1) / NT;
   int E = 1;
   while (E < e) E <<= 1;
   return E;
 }
 
+static int pow2_at_least(int x) {
+  int v = 1;
+  while (v < x) v <<= 1;
+  return v;
+}
+
 hipError_t set_resolve_lds_limit(size_t lds_bytes) {
   const int v = (int)lds_bytes;
   hipError_t e;
-  if ((e = hipFuncSetAttribute((const void*)resolve_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, v)) != hipSuccess) return e;
-  if ((e = hipFuncSetAttribute((const void*)resolve_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, v)) != hipSuccess) return e;
-  if ((e = hipFuncSetAttribute((const void*)resolve_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, v)) != hipSuccess) return e;
-  if ((e = hipFuncSetAttribute((const void*)resolve_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, v)) != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)resolve_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+  if ((e = set_limit_ke<1>(v)) != hipSuccess) return e;
+  if ((e = set_limit_ke<2>(v)) != hipSuccess) return e;
+  if ((e = set_limit_ke<4>(v)) != hipSuccess) return e;
+  if ((e = set_limit_ke<8>(v)) != hipSuccess) return e;
+  return set_limit_ke<16>(v);
 }
 
 hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s) {
+  const int KE = pow2_at_least((p.k + NT - 1) / NT);
   switch (resolve_elems_per_thread(p.k, p.B)) {
-    case 1: return launch_e<1>(p, lds_bytes, s);
-    case 2: return launch_e<2>(p, lds_bytes, s);
-    case 4: return launch_e<4>(p, lds_bytes, s);
-    case 8: return launch_e<8>(p, lds_bytes, s);
-    default: return launch_e<16>(p, lds_bytes, s);
+    case 1: return launch_ke<1>(p, lds_bytes, s, KE);
+    case 2: return launch_ke<2>(p, lds_bytes, s, KE);
+    case 4: return launch_ke<4>(p, lds_bytes, s, KE);
+    case 8: return launch_ke<8>(p, lds_bytes, s, KE);
+    default: return launch_ke<16>(p, lds_bytes, s, KE);
   }
 }
 

@@ -60,6 +60,7 @@ typedef int32_t hs_status;
 /* hs_stats.error bits */
 #define HS_ERR_DUP 1u   /* a position (or block) selected twice */
 #define HS_ERR_RANGE 2u /* a position outside [0, ctx_len) */
+#define HS_ERR_STATE 4u /* internal: page table and slot map disagreed (never expected) */
 
 typedef struct {
   int32_t num_requests;    /* R: requests resolved together in one launch per layer */
