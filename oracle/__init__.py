@@ -11,6 +11,9 @@ from it; the only inputs both sides share come from ``synth``.
 * ``brute``        -- an independently written pure-Python model used to pin
                       ``Cache`` on exhaustive tiny traces.
 * ``attention``    -- float64 NumPy sparse decode attention.
+* ``policies``     -- offline replacement-policy comparator (topk, FIFO,
+                      Random, LRU, Belady) on the seeded traces; also a
+                      command-line analysis tool (``python -m oracle.policies``).
 """
 from __future__ import annotations
 
