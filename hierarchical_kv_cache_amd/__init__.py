@@ -25,7 +25,7 @@ LIB_PATH = _build.LIB
 HS_OK, HS_EINVAL, HS_ENOMEM, HS_EHIP, HS_ESTATE = 0, -1, -2, -3, -4
 HS_CFG_NEWEST_SLOT = 1
 HS_RECORD_PLAN, HS_SKIP_IO = 1, 2
-HS_ERR_DUP, HS_ERR_RANGE, HS_ERR_STATE = 1, 2, 4
+HS_ERR_DUP, HS_ERR_RANGE, HS_ERR_STATE, HS_ERR_RESIDENT = 1, 2, 4, 8
 
 
 class hs_config(ctypes.Structure):
@@ -44,11 +44,12 @@ class hs_config(ctypes.Structure):
 
 
 HS_STATS_DTYPE = np.dtype([("hits", np.uint32), ("misses", np.uint32), ("error", np.uint32),
-                           ("reserved", np.uint32)])
+                           ("resident", np.uint32)])
 
 # every symbol include/hisparse.h declares
 EXPORTS = (
-    "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_append", "hs_prefetch_shared",
+    "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_bind_resident", "hs_append",
+    "hs_prefetch_shared",
     "hs_wait_layer", "hs_sparse_attn", "hs_export_state", "hs_page_table", "hs_plan", "hs_reset_request",
     "hs_destroy", "hs_last_error", "hs_resolve_wgs", "hs_probe_host_read", "hs_probe_copy",
     "hs_probe_empty",
@@ -73,6 +74,7 @@ def _load():
         "hs_create": (i32, [cfgp, vp, vp, ctypes.POINTER(vp)]),
         "hs_host_pool": (vp, [vp, i32]),
         "hs_resolve": (i32, [vp, i32, vp, vp, vp, vp, vp, u32, vp]),
+        "hs_bind_resident": (i32, [vp, vp, i32, i32, vp, i64]),
         "hs_append": (i32, [vp, vp, vp, vp, vp]),
         "hs_prefetch_shared": (i32, [vp, i32, vp, vp]),
         "hs_wait_layer": (i32, [vp, i32, vp]),
@@ -124,6 +126,11 @@ def hs_host_pool(h: int, request: int) -> int:
 def hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, stream):
     _check(_lib.hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats or None, d_num_reqs or None,
                            flags, stream or None))
+
+
+def hs_bind_resident(h, d_block_table, pages_per_request, page_tokens, d_resident_kv, resident_rows):
+    _check(_lib.hs_bind_resident(h, d_block_table or None, pages_per_request, page_tokens, d_resident_kv or None,
+                                 resident_rows))
 
 
 def hs_append(h, d_new_kv, d_new_pos, compute, backup):

@@ -1,5 +1,6 @@
 // Sparse decode attention over the slots RESOLVE published ("HiSparse 深度解析"
-// (gentlecold.top) §5.4: attention reads the physical slots aligned with the
+// (gentlecold.top) §5.4 and §6.5: attention reads the physical rows -- hot slots,
+// or resident rows when a resident tier is bound -- aligned with the
 // top-k order).  Per request, H <= 16 query heads share one latent KV record
 // per token: the key is all 576 bf16 of the record, the value its first 512.
 //
@@ -109,12 +110,16 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
       const int f = tid + u * AT;
       const int row = f / CHUNKS, c = f - row * CHUNKS;
       const int tok = t0 + row;
-      // past the end: exact zeros; a slot outside [0, B]: NaN, so the output shows it
+      // past the end: exact zeros.  Slots 0..B are hot rows, B+1+row resident rows; any
+      // other value reads as NaN, so the output shows it
       if (tok >= t_end) {
         stage[u] = zero4;
       } else {
         const int sl = s_slot[tok - t_begin];
-        stage[u] = (sl >= 0 && sl <= p.B) ? *((const u32x4*)(hot_r + (size_t)sl * p.rec_bytes) + c) : nan4;
+        const int64_t rr = (int64_t)sl - (p.B + 1);
+        const uint8_t* src = (sl >= 0 && sl <= p.B) ? hot_r + (size_t)sl * p.rec_bytes
+                             : (rr >= 0 && rr < p.res_rows) ? p.res + (size_t)rr * p.rec_bytes : nullptr;
+        stage[u] = src ? *((const u32x4*)src + c) : nan4;
       }
     }
   };

@@ -129,6 +129,11 @@ struct hs_ctx {
   std::vector<hipEvent_t> ev_plan, ev_plan_free, ev_layer;  // per anchor, per anchor, per layer
   std::vector<char> plan_free_pending;
   int replay_wgs = 32;
+  // resident tier (hs_bind_resident); rtable null when none is bound
+  const int32_t* rtable = nullptr;
+  int64_t rt_stride = 0, res_rows = 0;
+  int page_shift = 0;
+  const uint8_t* res = nullptr;
 
   uint32_t* ctrl(int a) { return (uint32_t*)(ws + lay.ctrl) + size_t(a) * cfg.num_requests * 4; }
   int32_t* slot_pos(int a) {
@@ -321,7 +326,28 @@ hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int
   p.kb = h->cfg.top_k / h->cfg.block_tokens; p.bt_shift = ilog2(h->cfg.block_tokens);
   p.rec_bytes = h->cfg.record_bytes; p.G = h->G; p.hash_bits = h->hash_bits;
   p.flags = flags | ((h->cfg.flags & HS_CFG_NEWEST_SLOT) ? kHasNewest : 0u);
+  p.rtable = h->rtable; p.rt_stride = h->rt_stride; p.res_rows = h->res_rows; p.page_shift = h->page_shift;
   HS_HIP(launch_resolve(p, h->lds_bytes, s));
+  return HS_OK;
+}
+
+hs_status hs_bind_resident(hs_handle h, const int32_t* d_block_table, int32_t pages_per_request,
+                           int32_t page_tokens, const void* d_resident_kv, int64_t resident_rows) {
+  hs_status st;
+  if ((st = check_handle(h))) return st;
+  if (!d_block_table) {
+    h->rtable = nullptr; h->res = nullptr; h->rt_stride = 0; h->res_rows = 0; h->page_shift = 0;
+    return HS_OK;
+  }
+  if (page_tokens < 1 || page_tokens > (1 << 20) || !is_pow2(page_tokens))
+    return fail(HS_EINVAL, "page_tokens must be a power of two in [1, 2^20]");
+  if (pages_per_request < 1 || int64_t(pages_per_request) * page_tokens < h->cfg.max_positions)
+    return fail(HS_EINVAL, "pages_per_request * page_tokens must cover max_positions");
+  if (!d_resident_kv || (uintptr_t)d_resident_kv % 16) return fail(HS_EINVAL, "resident pool must be 16-byte aligned");
+  if (resident_rows < 1 || resident_rows > (int64_t(1) << 31) - 2 - h->cfg.buffer_slots)
+    return fail(HS_EINVAL, "resident_rows must be in [1, 2^31 - 2 - B]");
+  h->rtable = d_block_table; h->rt_stride = pages_per_request; h->page_shift = ilog2(page_tokens);
+  h->res = (const uint8_t*)d_resident_kv; h->res_rows = resident_rows;
   return HS_OK;
 }
 
@@ -394,6 +420,8 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
   p.q = (const uint16_t*)d_q; p.slots = d_slots; p.out = d_out; p.part = h->attn_part(layer);
   p.num_reqs = d_num_reqs; p.hot = h->hot;
   p.hot_req_stride = h->hot_req_stride(); p.hot_layer_off = h->hot_layer_off(layer);
+  p.res = h->res ? h->res + size_t(layer) * size_t(h->res_rows) * size_t(h->cfg.record_bytes) : nullptr;
+  p.res_rows = h->res ? h->res_rows : 0;
   p.R = h->cfg.num_requests; p.k = h->cfg.top_k; p.B = h->cfg.buffer_slots; p.heads = heads;
   p.value_dim = value_dim; p.S = h->lay.S;
   p.chunk = (int)align_up((size_t)((h->cfg.top_k + p.S - 1) / p.S), 64);

@@ -37,16 +37,16 @@ __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits) {
   L.sflag = o;   o = align_up(o + size_t(B), 16);
   L.wpos = o;    o = align_up(o + 4 * NWv * L.wcap, 16);
   L.widx = o;    o = align_up(o + 2 * NWv * L.wcap, 16);
-  L.scratch = o; o = align_up(o + 4 * size_t(4 * NWv + 8), 16);
+  L.scratch = o; o = align_up(o + 4 * size_t(5 * NWv + 8), 16);
   L.total = o;
   return L;
 }
 int resolve_elems_per_thread(int k, int B);
 
 // Per-anchor metadata in the caller's workspace.  ctrl per request (uint32 x 4):
-// [0..1] 64-bit count of resolve workgroups run (launches = count / G; the parity of
-// the launch count names the ping-pong half holding the current metadata),
-// [2] miss-plan count, [3] unused.
+// [0..1] 64-bit count of resolve workgroups that changed the metadata (every workgroup
+// of such a launch adds one, so count / G numbers those launches and its parity names
+// the ping-pong half holding the current metadata), [2] miss-plan count, [3] unused.
 struct ResolveParams {
   const int32_t* sel;        // [R][kb]
   const int32_t* ctx_len;    // [R]
@@ -65,6 +65,10 @@ struct ResolveParams {
   int64_t hot_req_stride;    // bytes per request in the hot buffer
   int64_t hot_layer_off;     // layer offset inside a request's hot buffer (bytes)
   int64_t max_positions;
+  const int32_t* rtable;     // [R][rt_stride] resident page of each logical page (-1 none), or null
+  int64_t rt_stride;         // logical pages per request
+  int64_t res_rows;          // rows of the resident pool (0 without a resident tier)
+  int32_t page_shift;        // log2 tokens per resident page
   int32_t R, B, Bpad, k, kb, bt_shift, rec_bytes, G, hash_bits;
   uint32_t flags;            // HS_RECORD_PLAN | HS_SKIP_IO | kHasNewest
 };
@@ -96,6 +100,8 @@ struct AttnParams {
   const int32_t* num_reqs;
   const uint8_t* hot;        // layer 0 base
   int64_t hot_req_stride, hot_layer_off;
+  const uint8_t* res;        // this layer's resident pool [res_rows][rec] (null without one)
+  int64_t res_rows;
   int32_t R, k, B, heads, value_dim, S, chunk, rec_bytes;
   float scale;
 };

@@ -15,14 +15,25 @@
 //              non-temporal loads, flattened over (miss, 16-byte chunk)
 //   5 publish  page table, slot map, slots aligned with the selection order
 //
+// Resident tier ("HiSparse 深度解析" §6.5; "HiSparse local KV offload
+// architecture" (docs.vllm.ai), "Hot lookup and LRU"): when the caller binds a
+// block table of resident pages, each selected position is looked up there
+// first.  A resident entry publishes B + 1 + its resident row and takes no part
+// in the LRU (its hash key is the complemented position, so no slot matches it
+// in stage 2, while duplicates are still caught).  When every entry is resident
+// the kernel returns right after the lookup: no hash, no LRU, no copy.
+//
 // MI355X layout of the work.  G workgroups serve one request.  Each of them
 // recomputes stages 1-3 from the current metadata (cheap, all in LDS) and
 // copies its 1/G share of the missed bytes, so that a single request keeps
 // enough loads in flight to fill the host link; only workgroup 0 writes the
 // new metadata.  The slot map and the LRU order are ping-ponged: a 64-bit
-// launch counter per request (each workgroup adds one) numbers the launch,
-// its parity names the half holding the current metadata, workgroup 0
-// writes the other half.  No workgroup waits on another.
+// counter per request numbers the launches that changed the metadata (each of
+// their workgroups adds one once it has read the metadata); its parity names
+// the half holding the current metadata, and workgroup 0 writes the other
+// half.  A launch that changes nothing (an error, or everything resident)
+// leaves the counter alone, so its half stays current.  No workgroup waits on
+// another.
 //
 // Latency shape (the all-hit call is bounded by launch and memory latency,
 // not bandwidth): every global read the kernel needs -- the selection, both
@@ -158,7 +169,8 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   int16_t* mrank = (int16_t*)(smem + Ly.mrank);      // [k] miss rank of a list entry
   uint8_t* sflag = (uint8_t*)(smem + Ly.sflag);      // [B] 0 evictable, 1 hit, 2 victim
   uint32_t* carry = (uint32_t*)(smem + Ly.scratch);  // 2 x 2 x NW scan carries
-  int* sh = (int*)(carry + 4 * NW);                  // [0] error bits [1] newest hits [2] half
+  uint32_t* rcnt = carry + 4 * NW;                   // [NW] resident entries per wave
+  int* sh = (int*)(rcnt + NW);                       // [0] error bits [1] newest hits [2] half
 
   const int tid = threadIdx.x;
   const int r = blockIdx.x % p.R;
@@ -176,13 +188,15 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   const int i0 = tid * EK;  // first selection entry of this thread
 
   // ---- every global read up front -------------------------------------------------------
-  // Launch counter: every launch adds G per request, so (count before / G) numbers this
-  // launch; its parity picks the ping-pong half that holds the current metadata.  The
-  // returned value is needed only after stage 1, so its latency hides behind the loads.
+  // Launch counter: every launch that changes the metadata adds G per request, one per
+  // workgroup after its reads, so count / G (a workgroup of this launch sees at most G-1
+  // of its siblings' increments) numbers the launches before this one; its parity picks
+  // the ping-pong half that holds the current metadata.  The value is needed only after
+  // stage 1, so its latency hides behind the loads.
+  uint64_t* counter = (uint64_t*)&p.ctrl[r * 4];
   uint64_t launches = 0;
   if (tid == 0)
-    launches = __hip_atomic_fetch_add((uint64_t*)&p.ctrl[r * 4], 1ull, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) / (uint64_t)p.G;
+    launches = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / (uint64_t)p.G;
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
   const int32_t* selr = p.sel + (size_t)r * p.kb;
@@ -191,6 +205,17 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
     raw[j] = (j < EK && i < p.k) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
+  }
+  // resident tier: the resident page of each own entry (-1 none)
+  const bool tiered = p.rtable != nullptr;
+  const int32_t* rtr = p.rtable + (tiered ? (size_t)r * p.rt_stride : 0);
+  int32_t rpg[KE];
+#pragma unroll
+  for (int j = 0; j < KE; ++j) {
+    const int i = i0 + j;
+    const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                     : (int64_t)raw[j];
+    rpg[j] = (tiered && j < EK && i < p.k && pos64 >= 0 && pos64 < ctx) ? rtr[pos64 >> p.page_shift] : -1;
   }
   // Fetch workgroups (all but workgroup 0 when G > 1) also read the selection entries of
   // their share of the list, spread over the waves: entry e of the share belongs to wave
@@ -225,7 +250,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   // Misses known early from the page table (kept the exact inverse of the slot map): a
   // selected position whose entry is -1 is not resident.  Their host loads start right
   // after stage 1 and land while stages 2-3 run; stage 3 names the slots they go to.
-  int32_t fpos[KE], fpt[KE];
+  int32_t fpos[KE], fpt[KE], fres[KE];
   const int32_t* ptr = p.page_table + (size_t)r * p.max_positions;
 #pragma unroll
   for (int q = 0; q < KE; ++q) {
@@ -234,11 +259,55 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     int64_t pos64 = -1;
     if (fetcher && e < f_n)
       pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
-    const bool ok = pos64 >= 0 && pos64 < ctx && pos64 != newest;
+    const bool ok = pos64 >= 0 && pos64 < ctx;
     fpos[q] = ok ? (int32_t)pos64 : -1;
     fpt[q] = ok ? ptr[pos64] : 0;
+    fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
+  }
+  // resident entries with a row inside the pool, counted per wave
+  uint32_t rbits = 0;
+  if (tiered) {
+    const int64_t pmask = ((int64_t)1 << p.page_shift) - 1;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KE; ++j) {
+      const int i = i0 + j;
+      const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                       : (int64_t)raw[j];
+      const bool res = rpg[j] >= 0 && (((int64_t)rpg[j] << p.page_shift) + (pos64 & pmask)) < p.res_rows;
+      rbits |= (uint32_t)res << j;
+      cnt += __popcll(__ballot(res));
+    }
+    if (lane == 0) rcnt[wid] = (uint32_t)cnt;
   }
   __syncthreads();
+
+  // ---- resident tier: a selection that is resident throughout returns here ---------------
+  int nres = 0;
+  if (tiered) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) nres += (int)rcnt[w];
+    if (nres == p.k) {
+      if (g == 0) {
+        const int64_t pmask = ((int64_t)1 << p.page_shift) - 1;
+#pragma unroll
+        for (int j = 0; j < KE; ++j) {
+          const int i = i0 + j;
+          if (j < EK && i < p.k) {
+            const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                             : (int64_t)raw[j];
+            p.out[(size_t)r * p.k + i] = p.B + 1 + (int32_t)(((int64_t)rpg[j] << p.page_shift) + (pos64 & pmask));
+          }
+        }
+        if (tid == 0 && p.stats) {
+          hs_stats st = {0u, 0u, 0u, (uint32_t)p.k};
+          p.stats[r] = st;
+        }
+        if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
+      }
+      return;
+    }
+  }
 
   // ---- stage 1: expand blocks, validate, hash the selected positions ----------------------
   // Insertion in two steps.  (a) Every entry stores its list index into its home bucket of
@@ -248,6 +317,8 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   // at most a quarter full) insert with compare-and-swap linear probing, which never
   // overwrites a bucket.  LDS atomics are serialised lane by lane, so step (a) keeps most
   // of the table build off them.
+  // Hash keys: the position, or its complement for an entry the resident tier serves, so
+  // that stage 2 never matches a slot to a resident entry.
   uint32_t err = 0;
   uint32_t pending = 0;
   uint32_t hh[KE];
@@ -266,15 +337,28 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       selslot[i] = -2;
       continue;
     }
-    pos[j] = (int32_t)pos64;
-    selp[i] = pos[j];
-    if (pos[j] == newest) {  // the newest token sits in slot B, outside the LRU
-      selslot[i] = p.B;
-      atomicAdd(&sh[1], 1);
-      continue;
+    if (rpg[j] >= 0) {  // resident page: served from the resident pool
+      const int64_t row = ((int64_t)rpg[j] << p.page_shift) + (pos64 & (((int64_t)1 << p.page_shift) - 1));
+      if ((rbits >> j) & 1u) {
+        selslot[i] = p.B + 1 + (int32_t)row;
+      } else {
+        err |= HS_ERR_RESIDENT;
+        selslot[i] = -2;
+      }
+      pos[j] = ~(int32_t)pos64;
+    } else {
+      pos[j] = (int32_t)pos64;
+      if (pos[j] == newest) {  // the newest token sits in slot B, outside the LRU
+        selp[i] = pos[j];
+        selslot[i] = p.B;
+        atomicAdd(&sh[1], 1);
+        pos[j] = -1;
+        continue;
+      }
+      selslot[i] = -1;
     }
-    selslot[i] = -1;
-    hh[j] = hash_pos(pos[j], p.hash_bits);
+    selp[i] = pos[j];
+    hh[j] = hash_pos((int32_t)pos64, p.hash_bits);
     htab[hh[j]] = i;
     pending |= 1u << j;
   }
@@ -322,7 +406,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   {
 #pragma unroll
     for (int q = 0; q < KE; ++q) {
-      const bool miss = fpos[q] >= 0 && fpt[q] < 0;
+      const bool miss = fpos[q] >= 0 && fpos[q] != newest && fres[q] < 0 && fpt[q] < 0;
       const uint64_t b = __ballot(miss);
       if (miss) {
         fmiss |= 1u << q;
@@ -366,15 +450,8 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   int16_t* lru_new = p.lru + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.Bpad;
   int32_t* sp_new = p.slot_pos + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.B;
 
-  if (err) {  // every workgroup of the request sees the same error: the state is carried over
+  if (err) {  // every workgroup of the request sees the same error; nothing changes
     if (g == 0) {
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        if (e0 + j < p.B) {
-          sp_new[e0 + j] = spo[j];
-          lru_new[e0 + j] = lro[j];
-        }
-      }
       for (int i = tid; i < p.k; i += NT) p.out[(size_t)r * p.k + i] = -1;
       if (tid == 0 && p.stats) {
         hs_stats st = {0u, 0u, err, 0u};
@@ -384,6 +461,8 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     }
     return;
   }
+  // this launch changes the metadata: the next one finds it in the other half
+  if (tid == 0) __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- stage 2: mark each slot hit (its position is selected) or evictable --------------
   uint32_t probing = 0;
@@ -541,7 +620,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     }
     if (tid == 0) {
       if (p.stats) {
-        hs_stats st = {(uint32_t)(p.k - m), (uint32_t)m, 0u, 0u};
+        hs_stats st = {(uint32_t)(p.k - m - nres), (uint32_t)m, 0u, (uint32_t)nres};
         p.stats[r] = st;
       }
       if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;

@@ -61,6 +61,7 @@ typedef int32_t hs_status;
 #define HS_ERR_DUP 1u   /* a position (or block) selected twice */
 #define HS_ERR_RANGE 2u /* a position outside [0, ctx_len) */
 #define HS_ERR_STATE 4u /* internal: page table and slot map disagreed (never expected) */
+#define HS_ERR_RESIDENT 8u /* a block-table entry names a row outside the bound resident pool */
 
 typedef struct {
   int32_t num_requests;    /* R: requests resolved together in one launch per layer */
@@ -80,11 +81,12 @@ typedef struct {
 
 /* Per-request result of one hs_resolve call (device memory, overwritten per call). */
 typedef struct {
-  uint32_t hits;   /* selected tokens already on the device (newest slot included) */
-  uint32_t misses; /* selected tokens fetched from host (record_bytes each) */
-  uint32_t error;  /* HS_ERR_* bits; when set, nothing of this request changed and its
-                      slots_out row is -1 */
-  uint32_t reserved;
+  uint32_t hits;     /* selected tokens found in the hot slots (newest slot included) */
+  uint32_t misses;   /* selected tokens fetched from host (record_bytes each) */
+  uint32_t error;    /* HS_ERR_* bits; when set, nothing of this request changed and its
+                        slots_out row is -1 */
+  uint32_t resident; /* selected tokens served by the resident tier (hs_bind_resident);
+                        hits + misses + resident = top_k */
 } hs_stats;
 
 /* Bytes of device workspace hs_create needs for cfg (0 when cfg is invalid). */
@@ -127,12 +129,38 @@ void* hs_host_pool(hs_handle h, int32_t request);
  * Replacement ([GC] §3.3): empty slots first; this call's hits rank newer than
  * this call's fetched entries; victims are the least recent slots not selected
  * now, ties by lower slot index; misses take victims in selection order.
+ * With a resident tier bound (hs_bind_resident) each position is looked up
+ * there first ([GC] §6.5): a resident entry gets B + 1 + its resident row and
+ * takes no part in the LRU (a slot holding that position counts as not
+ * selected); a call whose entries are all resident returns before the hash
+ * and LRU stages and changes nothing (duplicates are then not reported).
  * With HS_RECORD_PLAN the stream first waits until the previous plan of this
  * anchor has been replayed.
  */
 hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
                      int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs,
                      uint32_t flags, void* stream);
+
+/*
+ * Binds a resident tier in front of the hot slots ([GC] §6.5; [VD] "Hot lookup
+ * and LRU", "Performance invariants"): the caller's regular paged KV cache, of
+ * which some pages of each request are on the device.
+ *   d_block_table     device, caller-owned [R][pages_per_request] int32: the
+ *                     resident page of each logical page (page of position p =
+ *                     p / page_tokens), -1 when the page is not resident.  The
+ *                     caller may rewrite it between calls (stream-ordered).
+ *   pages_per_request pages_per_request * page_tokens >= max_positions
+ *   page_tokens       tokens per page, a power of two <= 2^20
+ *   d_resident_kv     device, caller-owned [L][resident_rows][record_bytes]; the
+ *                     record of position p of layer l is row
+ *                     table[r][p / page_tokens] * page_tokens + p % page_tokens
+ *   resident_rows     rows per layer, 1 .. 2^31 - 2 - B
+ * Afterwards hs_resolve consults the table and hs_sparse_attn reads slots
+ * above B from d_resident_kv.  d_block_table = NULL unbinds (other arguments
+ * ignored).  Takes effect for calls enqueued after it.
+ */
+hs_status hs_bind_resident(hs_handle h, const int32_t* d_block_table, int32_t pages_per_request,
+                           int32_t page_tokens, const void* d_resident_kv, int64_t resident_rows);
 
 /*
  * Write-through of one new token per request, for every layer ([GC] §3.4, §5.4;
@@ -164,13 +192,14 @@ hs_status hs_wait_layer(hs_handle h, int32_t layer, void* stream);
  * Sparse decode attention over the published slots ([GC] §5.4: attention reads
  * the slots aligned with the top-k order).  For each request: the key of entry
  * i is the first key_dim bf16 of the record in slot d_slots[r][i] of this
- * layer, its value the first value_dim of them; s = scale * q k^T, softmax over
- * the top_k entries, o = p v.
+ * layer (a slot B + 1 + row is row `row` of this layer's bound resident pool),
+ * its value the first value_dim of them; s = scale * q k^T, softmax over the
+ * top_k entries, o = p v.
  *   d_q     device [R][heads][key_dim] bf16, heads 1..16, key_dim = record_bytes/2 = 576
  *   d_slots device [R][top_k] int32 (the layer's, or its anchor's, d_slots_out)
  *   d_out   device [R][heads][value_dim] float32, value_dim = 512
  *   d_num_reqs as for hs_resolve (rows of skipped requests are not written)
- * Slots outside [0, B] make the request's output rows NaN.
+ * Slots outside [0, B] and outside the bound resident rows make the request's output rows NaN.
  */
 hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t heads,
                          int32_t value_dim, const int32_t* d_slots, float* d_out, float scale,

@@ -29,13 +29,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "_hso.so")
 _lib = None
 
-ERR_DUP, ERR_RANGE, ERR_CAPACITY = 1, 2, 4
+ERR_DUP, ERR_RANGE, ERR_CAPACITY, ERR_RESIDENT = 1, 2, 4, 8
 
 
 class OracleError(ValueError):
     def __init__(self, code: int):
         names = [n for b, n in ((ERR_DUP, "duplicate position"), (ERR_RANGE, "position out of range"),
-                                (ERR_CAPACITY, "selection larger than the buffer")) if code & b]
+                                (ERR_CAPACITY, "selection larger than the buffer"),
+                                (ERR_RESIDENT, "resident row outside the resident pool")) if code & b]
         super().__init__(", ".join(names) or "error %d" % code)
         self.code = code
 
@@ -63,6 +64,8 @@ def _load():
     lib.hso_destroy.restype = None
     lib.hso_resolve.argtypes = [vp, vp, i32, i64, vp, vp, vp, vp, vp]
     lib.hso_resolve.restype = i32
+    lib.hso_resolve_tiered.argtypes = [vp, vp, i32, i64, vp, i64, i32, i64, vp, vp, vp, vp, vp]
+    lib.hso_resolve_tiered.restype = i32
     lib.hso_append.argtypes = [vp, i64, vp, vp]
     lib.hso_append.restype = i32
     lib.hso_replay.argtypes = [vp, vp, i32, vp, vp, i32]
@@ -127,6 +130,25 @@ class Cache:
             raise OracleError(err)
         m = int(counts[1])
         return out, int(counts[0]), m, ppos[:m].copy(), pslot[:m].copy()
+
+    def resolve_tiered(self, sel, ctx_len: int, rtable, page_shift: int, res_rows: int, host):
+        """Resolve with the resident tier first (``hso_resolve_tiered``).  ``rtable`` is the
+        request's int32 block table (resident page per logical page, -1 none).
+        Returns (out, hits, misses, resident, plan_pos, plan_slot); raises OracleError."""
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        rt = np.ascontiguousarray(rtable, dtype=np.int32)
+        k = sel.size
+        out = np.empty(k, np.int32)
+        ppos = np.empty(k, np.int32)
+        pslot = np.empty(k, np.int32)
+        counts = np.zeros(3, np.int32)
+        err = self._lib.hso_resolve_tiered(self._h, sel.ctypes.data, k, ctx_len, rt.ctypes.data, rt.size,
+                                           page_shift, res_rows, _addr(host), out.ctypes.data,
+                                           ppos.ctypes.data, pslot.ctypes.data, counts.ctypes.data)
+        if err:
+            raise OracleError(err)
+        m = int(counts[1])
+        return out, int(counts[0]), m, int(counts[2]), ppos[:m].copy(), pslot[:m].copy()
 
     def append(self, pos: int, record: np.ndarray, host=None):
         rec = np.ascontiguousarray(record, dtype=np.uint8)

@@ -40,7 +40,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { HSO_ERR_DUP = 1, HSO_ERR_RANGE = 2, HSO_ERR_CAPACITY = 4, HSO_ERR_ALLOC = 8 };
+enum { HSO_ERR_DUP = 1, HSO_ERR_RANGE = 2, HSO_ERR_CAPACITY = 4, HSO_ERR_RESIDENT = 8 };
 
 typedef struct {
   int32_t B;
@@ -184,6 +184,79 @@ int32_t hso_resolve(hso_cache* c, const int32_t* sel, int32_t k, int64_t ctx_len
   counts[0] = n_hit;
   counts[1] = n_miss;
   return 0;
+}
+
+/*
+ * RESOLVE with a resident tier in front ("HiSparse 深度解析" (gentlecold.top)
+ * §6.5; "HiSparse local KV offload architecture" (docs.vllm.ai), "Hot lookup
+ * and LRU" and "Performance invariants"): each selected position is looked up
+ * first in the resident block table, then in the hot slots, and only then
+ * fetched from host.
+ *   rtable     : [n_pages] resident page of each logical page, -1 when the page
+ *                is not resident; the page of position p is p >> page_shift
+ *   res_rows   : rows of the resident pool; p's row is
+ *                rtable[page] * 2^page_shift + (p mod 2^page_shift)
+ *   out        : B + 1 + row for a resident entry, else as hso_resolve
+ *   counts     : [3] hot hits (newest slot included), misses, resident entries
+ * Reading of the pages: when every entry is resident the call returns right
+ * after the lookup (no duplicate check, nothing of the cache changes).
+ * Otherwise duplicates are checked over the whole list and the entries that
+ * are not resident go, in list order, through hso_resolve's steps; a slot
+ * holding a position served by the resident tier is not selected through the
+ * LRU, so it may be evicted.  Returns 0 or HSO_ERR_* bits; on error nothing
+ * changes.
+ */
+int32_t hso_resolve_tiered(hso_cache* c, const int32_t* sel, int32_t k, int64_t ctx_len,
+                           const int32_t* rtable, int64_t n_pages, int32_t page_shift, int64_t res_rows,
+                           const uint8_t* host, int32_t* out, int32_t* plan_pos, int32_t* plan_slot,
+                           int32_t* counts) {
+  const int32_t B = c->B;
+  int32_t err = 0, n_res = 0;
+  int32_t* rest = (int32_t*)calloc((size_t)(k > 0 ? k : 1), sizeof(int32_t));   /* non-resident list */
+  int32_t* where = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));  /* its list indices */
+  int32_t* rout = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+  if (!rest || !where || !rout) { free(rest); free(where); free(rout); return HSO_ERR_CAPACITY; }
+
+  /* 1. resident level */
+  int32_t n_rest = 0;
+  for (int32_t i = 0; i < k; ++i) {
+    const int64_t p = sel[i];
+    if (p < 0 || p >= ctx_len || p >= c->max_positions) { err |= HSO_ERR_RANGE; continue; }
+    const int64_t page = p >> page_shift;
+    const int32_t rp = page < n_pages ? rtable[page] : -1;
+    if (rp >= 0) {
+      const int64_t row = ((int64_t)rp << page_shift) + (p & (((int64_t)1 << page_shift) - 1));
+      if (row >= res_rows) { err |= HSO_ERR_RESIDENT; continue; }
+      out[i] = (int32_t)(B + 1 + row);
+      ++n_res;
+    } else {
+      where[n_rest] = i;
+      rest[n_rest++] = (int32_t)p;
+    }
+  }
+  if (!err && n_res == k) {  /* everything resident: return at once */
+    counts[0] = 0; counts[1] = 0; counts[2] = n_res;
+    free(rest); free(where); free(rout);
+    return 0;
+  }
+  /* 2. no position twice in the whole list */
+  for (int32_t i = 0; i < k; ++i) {
+    const int64_t p = sel[i];
+    if (p < 0 || p >= ctx_len || p >= c->max_positions) continue;
+    if (c->selected[p]) err |= HSO_ERR_DUP;
+    c->selected[p] = 1;
+  }
+  for (int32_t i = 0; i < k; ++i)
+    if (sel[i] >= 0 && sel[i] < c->max_positions) c->selected[sel[i]] = 0;
+  /* 3. the rest through the hot slots and the host */
+  int32_t c2[2] = {0, 0};
+  if (!err) err = hso_resolve(c, rest, n_rest, ctx_len, host, rout, plan_pos, plan_slot, c2);
+  if (!err) {
+    for (int32_t j = 0; j < n_rest; ++j) out[where[j]] = rout[j];
+    counts[0] = c2[0]; counts[1] = c2[1]; counts[2] = n_res;
+  }
+  free(rest); free(where); free(rout);
+  return err;
 }
 
 /* The new token at `pos`: its record goes to the reserved slot B and is

@@ -13,6 +13,7 @@ import torch
 import hierarchical_kv_cache_amd as hk
 import oracle
 import synth
+from synth.resident import ResidentSpec, resident_layout
 
 SCALE = 576 ** -0.5
 
@@ -25,7 +26,7 @@ class Pair:
     """One HiSparse handle plus the matching oracle caches for a workload."""
 
     def __init__(self, w: synth.Workload, steps: int | None = None, wgs: int = 0, all_hit=False,
-                 oracle_host_copy: bool | None = None, compare_hot=True):
+                 oracle_host_copy: bool | None = None, compare_hot=True, resident: ResidentSpec | None = None):
         self.w = w
         self.steps = w.steps if steps is None else steps
         self.lmax = w.max_positions(self.steps)
@@ -69,8 +70,35 @@ class Pair:
         self.d_stats = torch.zeros((w.R, 4), dtype=torch.int32, device=self.dev)
         self.t = 0
         self.newest = None
+        self.resident = resident
+        if resident is not None:
+            self._bind_resident(resident)
         # the oracle's C calls release the GIL: independent caches resolve in parallel
         self.pool = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+
+    def _bind_resident(self, spec: ResidentSpec):
+        """Resident tier: the pool holds, at each resident page's rows, the records of that
+        page's positions for every layer (copied from the prefill records)."""
+        w = self.w
+        P = spec.page_tokens
+        self.page_shift = P.bit_length() - 1
+        self.phys, self.masks, total = resident_layout(w, self.steps, spec)
+        self.res_rows = max(1, total) * P
+        pool = np.zeros((w.L, self.res_rows, self.rec), np.uint8)
+        for r in range(w.R):
+            pages = np.nonzero(self.phys[r] >= 0)[0]
+            src = (pages[:, None] * P + np.arange(P)).ravel()
+            dst = (self.phys[r][pages][:, None].astype(np.int64) * P + np.arange(P)).ravel()
+            for l in range(w.L):
+                pool[l, dst] = self.ohost[r][l][src]
+        self.res_pool = pool
+        self.d_res = torch.from_numpy(pool).to(self.dev)
+        self.n_pages = self.phys.shape[1]
+        self.d_table = torch.full((w.R, self.n_pages), -1, dtype=torch.int32, device=self.dev)
+        hk.hs_bind_resident(self.h, self.d_table.data_ptr(), self.n_pages, P, self.d_res.data_ptr(), self.res_rows)
+
+    def table(self, t):
+        return np.where(self.masks[t], self.phys, -1).astype(np.int32)
 
     # ---- one decode step ------------------------------------------------------------------
     def ctx_len(self):
@@ -93,6 +121,9 @@ class Pair:
                     self.caches[(r, l)].append(p, recs[r, l], self.ohost[r][l])
             self.newest = p
             self._keep = (d_new, d_pos)
+        if self.resident is not None:
+            tab = self.table(t)
+            self.d_table.copy_(torch.from_numpy(tab))
         d_nr = None
         if num_reqs is not None:
             d_nr = torch.tensor([num_reqs], dtype=torch.int32, device=self.dev)
@@ -108,7 +139,12 @@ class Pair:
 
             def one(r, l=l, ai=ai):
                 pos = expand(self.trace[t, ai, r], w.block_tokens)
-                res = self.caches[(r, l)].resolve(pos, ctx, self.ohost[r][l])
+                if self.resident is not None:
+                    o, hh, mm, rr, pp, ps = self.caches[(r, l)].resolve_tiered(
+                        pos, ctx, tab[r], self.page_shift, self.res_rows, self.ohost[r][l])
+                    res = (o, hh, mm, pp, ps, rr)
+                else:
+                    res = self.caches[(r, l)].resolve(pos, ctx, self.ohost[r][l]) + (0,)
                 for ls in range(l + 1, min(l + w.group, w.L)):
                     oracle.replay(res[3], res[4], self.ohost[r][ls], self.ohot_shared[(r, ls)], self.rec)
                 return res
@@ -116,8 +152,8 @@ class Pair:
             for r, res in zip(range(nr), self.pool.map(one, range(nr))):
                 results[(r, l)] = res
                 if check:
-                    assert stats[r, 0] == res[1] and stats[r, 1] == res[2] and stats[r, 2] == 0, \
-                        (t, r, l, stats[r], res[1], res[2])
+                    assert stats[r, 0] == res[1] and stats[r, 1] == res[2] and stats[r, 2] == 0 \
+                        and stats[r, 3] == res[5], (t, r, l, stats[r], res[1], res[2], res[5])
             if check:
                 got = self.d_out[ai].cpu().numpy()
                 for r in range(nr):
