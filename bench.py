@@ -216,6 +216,7 @@ def main():
         detail.update(measure_fetch(torch, hk, synth, w, dev, trace, lmax))
         detail.update(measure_fetch_heavy(torch, hk, synth, dev))
         detail.update(measure_all_hit(torch, hk, synth, dev))
+        detail.update(measure_resident(torch, hk, synth, w, dev, trace, lmax))
         detail["launch_latency_us"] = measure_empty(torch, hk)
         detail["hbm_copy_GBps"] = measure_hbm(torch, hk, dev)
         detail["link_ceiling_GBps"] = link["ceiling_GBps"]
@@ -306,12 +307,23 @@ def measure_link(torch, hk, dev):
     return {"dma_GBps": dma, "zero_copy_GBps": zc, "ceiling_GBps": max(dma, zc)}
 
 
-def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, hits_only=False):
-    """RESOLVE alone over `steps` steps of a trace on a fresh cache; per-launch µs per step."""
+def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, resident=None):
+    """RESOLVE alone over `steps` steps of a trace on a fresh cache; per-launch µs per step.
+    With `resident` (a ResidentSpec) a resident tier is bound and its block table follows
+    the spec's per-step layout (table rewrites are outside the timed launches)."""
     R, L, k, B = w.R, w.L, w.k, w.B
     cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, newest_slot=w.append))
     for r in range(R):
         synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    if resident is not None:
+        from synth.resident import resident_layout
+        P = resident.page_tokens
+        phys, masks, total = resident_layout(w, steps, resident, max_positions=lmax)
+        rows = max(1, total) * P
+        d_pool = torch.empty((L, rows, REC), dtype=torch.uint8, device=dev)  # never read by RESOLVE
+        d_tables = torch.from_numpy(np.where(masks, phys[None], -1).astype(np.int32)).to(dev)
+        d_table = torch.empty_like(d_tables[0])
+        hk.hs_bind_resident(cache.h, d_table.data_ptr(), phys.shape[1], P, d_pool.data_ptr(), rows)
     d_trace = torch.from_numpy(np.ascontiguousarray(trace[:steps])).to(dev)
     d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
     d_stats = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
@@ -327,6 +339,8 @@ def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, hits_o
            for _ in range(steps)]
     torch.cuda.synchronize()
     for t in range(steps):
+        if resident is not None:
+            d_table.copy_(d_tables[t])
         if w.append:
             hk.hs_append(cache.h, new_kv[t].data_ptr(), new_pos[t].data_ptr(), s.cuda_stream, side.cuda_stream)
         for l in range(L):
@@ -387,6 +401,32 @@ def measure_all_hit(torch, hk, synth, dev):
         # algorithmic HBM bytes of an all-hit launch: selection, slot map + LRU read and written, slots
         b = wl.R * (wl.k * 4 * 2 + wl.B * (4 + 2) * 2)
         out["all_hit_hbm_bound_us_%s" % name] = b / (HBM_PEAK_GBS * 1e9) * 1e6
+    return out
+
+
+def measure_resident(torch, hk, synth, w, dev, trace, lmax):
+    """Resident tier in front of the hot slots.  All resident (a short request that fits the
+    device pool): the kernel returns after the block-table lookup, at 1 and 32 requests.
+    Long workload with the last 16384 prefill tokens and 5 % of older pages resident:
+    steady-state µs per layer and the share of entries the resident tier serves."""
+    from synth.resident import ResidentSpec
+    out = {}
+    for name, wl in (("r1", synth.WORKLOADS["long"].scaled(append=False, force_newest=False, L=4,
+                                                           ctx=32768)),
+                     ("r32", synth.WORKLOADS["batched"].scaled(L=1))):
+        steps = 64
+        tr = np.stack([np.stack([synth.selection_trace(wl, r, l, steps) for r in range(wl.R)], axis=1)
+                       for l in range(wl.L)], axis=1)
+        us, st = run_resolve_only(torch, hk, synth, wl, dev, tr, wl.max_positions(steps), steps, 0,
+                                  resident=ResidentSpec(all_resident=True))
+        assert (st[..., 3] == wl.k).all() and st[..., 1].sum() == 0
+        out["all_resident_us_per_layer_%s" % name] = float(np.median(us[1:]))
+    steps = min(64, trace.shape[0])
+    us, st = run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, 0,
+                              resident=ResidentSpec(window_tokens=16384, old_frac=0.05))
+    out["long_resident_steady_us_per_layer"] = float(us[8:].mean())
+    out["long_resident_share"] = float(st[8:, ..., 3].sum() / (st[8:].shape[0] * w.L * w.R * w.k))
+    out["long_resident_miss_rate"] = float(st[8:, ..., 1].sum() / (st[8:].shape[0] * w.L * w.R * w.k))
     return out
 
 

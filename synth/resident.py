@@ -32,14 +32,15 @@ class ResidentSpec:
     all_resident: bool = False
 
 
-def resident_layout(w, steps: int, spec: ResidentSpec):
+def resident_layout(w, steps: int, spec: ResidentSpec, max_positions: int | None = None):
     """Returns (phys int32 [R][n_pages], masks bool [steps][R][n_pages], total_pages).
 
     phys[r][pg] is the physical page of logical page pg of request r (-1 when the page
-    is never resident); the block table of step t is where(masks[t], phys, -1).
+    is never resident); the block table of step t is where(masks[t], phys, -1).  The
+    table covers ``max_positions`` positions (default: the workload's over ``steps``).
     """
     P = spec.page_tokens
-    n_pages = -(-w.max_positions(steps) // P)
+    n_pages = -(-(max_positions or w.max_positions(steps)) // P)
     ctx_pages = w.ctx // P
     phys = np.full((w.R, n_pages), -1, np.int32)
     masks = np.zeros((steps, w.R, n_pages), bool)
