@@ -19,7 +19,7 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // LDS carve-up of the resolve kernel (shared by host sizing and device code).
 struct ResolveLds {
-  size_t htab, selp, selslot, victim, missidx, mrank, vmiss, sflag, wpos, widx, wcap, scratch, total;
+  size_t htab, selp, victim, missidx, mrank, sown, wpos, widx, wcap, scratch, total;
 };
 __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits) {
   ResolveLds L;
@@ -29,12 +29,10 @@ __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits) {
   L.wcap = 64 * ((size_t(k) + kResolveThreads - 1) / kResolveThreads);  // misses one wave can own
   L.htab = o;    o = align_up(o + 4 * H, 16);
   L.selp = o;    o = align_up(o + 4 * size_t(k), 16);
-  L.selslot = o; o = align_up(o + 4 * size_t(k), 16);
   L.victim = o;  o = align_up(o + 2 * size_t(k), 16);
   L.missidx = o; o = align_up(o + 2 * size_t(k), 16);
   L.mrank = o;   o = align_up(o + 2 * size_t(k), 16);
-  L.vmiss = o;   o = align_up(o + 2 * size_t(B), 16);
-  L.sflag = o;   o = align_up(o + size_t(B), 16);
+  L.sown = o;    o = align_up(o + 2 * size_t(B), 16);
   L.wpos = o;    o = align_up(o + 4 * NWv * L.wcap, 16);
   L.widx = o;    o = align_up(o + 2 * NWv * L.wcap, 16);
   L.scratch = o; o = align_up(o + 4 * size_t(5 * NWv + 8), 16);

@@ -3,9 +3,13 @@
 //
 // Stages ("HiSparse 深度解析" (gentlecold.top) §3.5; "推理系统基础设施手记（六）：
 // HiSparse" (naphjohn.github.io) §3):
-//   1 stage    selected positions -> LDS open-addressing hash (Knuth
-//              multiplicative hash, linear probing)
-//   2 mark     every slot's stored position probed in the hash: hit or evictable
+//   1 stage    selected positions classified; misses -> LDS open-addressing hash
+//              (Knuth multiplicative hash, linear probing) for duplicate detection
+//   2 mark     hit slots marked.  The pages probe every slot's stored position in
+//              the hash; here the page table, which the kernel keeps the exact
+//              inverse of the slot map, names each hit's slot directly, so the
+//              entry claims it in an LDS owner array (same hit set, no B-slot
+//              probe loop)
 //   3 scan     block-wide ranks (wave64 ballot + mbcnt, one LDS carry step):
 //              misses numbered in list order, evictable slots numbered in LRU
 //              order, the j-th evictable is the victim of the j-th miss; new LRU
@@ -161,16 +165,16 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
-  int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] expanded selection (the hash keys)
-  int32_t* selslot = (int32_t*)(smem + Ly.selslot);  // [k] slot of a hit or the newest, -1 miss
+  int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] position (hash key) of each entry
   int16_t* victim = (int16_t*)(smem + Ly.victim);    // [k] slot given to miss j
   int16_t* missidx = (int16_t*)(smem + Ly.missidx);  // [k] list index of miss j
-  int16_t* vmiss = (int16_t*)(smem + Ly.vmiss);      // [B] miss served by a victim slot
   int16_t* mrank = (int16_t*)(smem + Ly.mrank);      // [k] miss rank of a list entry
-  uint8_t* sflag = (uint8_t*)(smem + Ly.sflag);      // [B] 0 evictable, 1 hit, 2 victim
+  int16_t* sown = (int16_t*)(smem + Ly.sown);        // [B] -1 evictable, i >= 0 hit by entry i,
+                                                     //     -2-j victim of miss j
   uint32_t* carry = (uint32_t*)(smem + Ly.scratch);  // 2 x 2 x NW scan carries
   uint32_t* rcnt = carry + 4 * NW;                   // [NW] resident entries per wave
   int* sh = (int*)(rcnt + NW);                       // [0] error bits [1] newest hits [2] half
+                                                     // [3] slot map / page table disagreement
 
   const int tid = threadIdx.x;
   const int r = blockIdx.x % p.R;
@@ -200,22 +204,26 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
   const int32_t* selr = p.sel + (size_t)r * p.kb;
+  const int32_t* ptr = p.page_table + (size_t)r * p.max_positions;
   int32_t raw[KE];
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
     raw[j] = (j < EK && i < p.k) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
   }
-  // resident tier: the resident page of each own entry (-1 none)
+  // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
+  // map, so it names the slot of a hit) and, with a resident tier, its resident page.
   const bool tiered = p.rtable != nullptr;
   const int32_t* rtr = p.rtable + (tiered ? (size_t)r * p.rt_stride : 0);
-  int32_t rpg[KE];
+  int32_t ptv[KE], rpg[KE];
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
     const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
                                      : (int64_t)raw[j];
-    rpg[j] = (tiered && j < EK && i < p.k && pos64 >= 0 && pos64 < ctx) ? rtr[pos64 >> p.page_shift] : -1;
+    const bool ok = j < EK && i < p.k && pos64 >= 0 && pos64 < ctx;
+    ptv[j] = ok ? ptr[pos64] : -1;
+    rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
   // Fetch workgroups (all but workgroup 0 when G > 1) also read the selection entries of
   // their share of the list, spread over the waves: entry e of the share belongs to wave
@@ -237,21 +245,24 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   const bool bvec = (p.B % E) == 0;
   int32_t spa[E], spb[E];
   int16_t lra[E], lrb[E];
-  load_run32<E>(p.slot_pos + ((size_t)r * 2 + 0) * p.B, p.B, e0, bvec, spa, -1);
-  load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
+  if (g == 0) {  // only workgroup 0 publishes, and only it needs the slot map
+    load_run32<E>(p.slot_pos + ((size_t)r * 2 + 0) * p.B, p.B, e0, bvec, spa, -1);
+    load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
+  }
   load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, e0, bvec, lra, 0);
   load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, e0, bvec, lrb, 0);
   {
     u32x4* h4 = (u32x4*)htab;
     const u32x4 e4 = {~0u, ~0u, ~0u, ~0u};
     for (int h = tid; h < H / 4; h += NT) h4[h] = e4;
+    u32x4* s4 = (u32x4*)sown;  // B int16, padded to 16 bytes
+    for (int h = tid; h < (p.B + 7) / 8; h += NT) s4[h] = e4;
   }
-  if (tid == 0) { sh[0] = 0; sh[1] = 0; }
-  // Misses known early from the page table (kept the exact inverse of the slot map): a
-  // selected position whose entry is -1 is not resident.  Their host loads start right
-  // after stage 1 and land while stages 2-3 run; stage 3 names the slots they go to.
+  if (tid == 0) { sh[0] = 0; sh[1] = 0; sh[3] = 0; }
+  // Misses known early from the page table: a selected position whose entry is -1 (and
+  // that the resident tier does not serve) is not on the device.  Their host loads start
+  // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
   int32_t fpos[KE], fpt[KE], fres[KE];
-  const int32_t* ptr = p.page_table + (size_t)r * p.max_positions;
 #pragma unroll
   for (int q = 0; q < KE; ++q) {
     const int e = q * NT + lane * NW + wid;
@@ -309,75 +320,85 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     }
   }
 
-  // ---- stage 1: expand blocks, validate, hash the selected positions ----------------------
-  // Insertion in two steps.  (a) Every entry stores its list index into its home bucket of
-  // the empty table with a plain store; after a barrier an entry whose index reads back owns
-  // that bucket, and one that finds another entry of the same position there is a
-  // duplicate.  (b) The entries that lost their home bucket (a small fraction: the table is
-  // at most a quarter full) insert with compare-and-swap linear probing, which never
+  // ---- stages 1 and 2: classify each entry, mark the hit slots, hash the rest -------------
+  // An entry is served by the resident tier, by the newest slot, by the slot its page-table
+  // entry names (a hit: the entry claims that slot, which marks it), or is a miss.  Misses
+  // and resident entries go into the LDS hash, the resident ones under the complemented
+  // position, so duplicates are caught in every class: two entries of one position share
+  // their class, and a second claim of a slot or a second hash entry of a key reveals it.
+  //
+  // Hash insertion in two steps.  (a) Every entry stores its list index into its home
+  // bucket of the empty table with a plain store; after a barrier an entry whose index
+  // reads back owns that bucket, and one that finds another entry of the same key there is
+  // a duplicate.  (b) The entries that lost their home bucket (a small fraction: the table
+  // is at most a quarter full) insert with compare-and-swap linear probing, which never
   // overwrites a bucket.  LDS atomics are serialised lane by lane, so step (a) keeps most
-  // of the table build off them.
-  // Hash keys: the position, or its complement for an entry the resident tier serves, so
-  // that stage 2 never matches a slot to a resident entry.
+  // of the table build off them.  Slot claims use the same plain-store-and-read-back.
   uint32_t err = 0;
-  uint32_t pending = 0;
+  uint32_t pending = 0, hitb = 0;
   uint32_t hh[KE];
-  int32_t pos[KE];
+  int32_t key[KE], cls[KE];  // cls: published value (slot, B, B+1+row), -1 miss, -2 invalid
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
-    pos[j] = -1;
+    key[j] = -1;
     hh[j] = 0;
+    cls[j] = -2;
     if (j >= EK || i >= p.k) continue;
     const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
                                      : (int64_t)raw[j];
     if (pos64 < 0 || pos64 >= ctx) {
       err |= HS_ERR_RANGE;
-      selp[i] = -1;
-      selslot[i] = -2;
       continue;
     }
     if (rpg[j] >= 0) {  // resident page: served from the resident pool
       const int64_t row = ((int64_t)rpg[j] << p.page_shift) + (pos64 & (((int64_t)1 << p.page_shift) - 1));
-      if ((rbits >> j) & 1u) {
-        selslot[i] = p.B + 1 + (int32_t)row;
-      } else {
-        err |= HS_ERR_RESIDENT;
-        selslot[i] = -2;
-      }
-      pos[j] = ~(int32_t)pos64;
-    } else {
-      pos[j] = (int32_t)pos64;
-      if (pos[j] == newest) {  // the newest token sits in slot B, outside the LRU
-        selp[i] = pos[j];
-        selslot[i] = p.B;
-        atomicAdd(&sh[1], 1);
-        pos[j] = -1;
+      if ((rbits >> j) & 1u) cls[j] = p.B + 1 + (int32_t)row;
+      else err |= HS_ERR_RESIDENT;
+      key[j] = ~(int32_t)pos64;
+    } else if ((int32_t)pos64 == newest) {  // the newest token sits in slot B, outside the LRU
+      cls[j] = p.B;
+      atomicAdd(&sh[1], 1);
+      continue;
+    } else if (ptv[j] >= 0) {  // a hit: the slot holding the position
+      selp[i] = (int32_t)pos64;
+      if (ptv[j] >= p.B) {  // the page table never names a slot outside [0, B)
+        err |= HS_ERR_STATE;
         continue;
       }
-      selslot[i] = -1;
+      cls[j] = ptv[j];
+      sown[ptv[j]] = (int16_t)i;
+      hitb |= 1u << j;
+      continue;
+    } else {
+      cls[j] = -1;
+      key[j] = (int32_t)pos64;
     }
-    selp[i] = pos[j];
+    selp[i] = key[j];
     hh[j] = hash_pos((int32_t)pos64, p.hash_bits);
     htab[hh[j]] = i;
     pending |= 1u << j;
   }
-  __syncthreads();  // home-bucket stores and every key (selp) are visible
+  __syncthreads();  // home-bucket stores, slot claims and every key are visible
   {
     // branch-free read-back: every read issued before any result is used
-    int32_t own[KE], key[KE];
+    int32_t own[KE], kk[KE];
+    int16_t so[KE];
 #pragma unroll
     for (int j = 0; j < KE; ++j) own[j] = htab[hh[j]];
 #pragma unroll
-    for (int j = 0; j < KE; ++j) key[j] = selp[own[j] < 0 ? 0 : own[j]];
+    for (int j = 0; j < KE; ++j) so[j] = sown[((hitb >> j) & 1u) ? cls[j] : 0];
+#pragma unroll
+    for (int j = 0; j < KE; ++j) kk[j] = selp[own[j] < 0 ? 0 : own[j]];
 #pragma unroll
     for (int j = 0; j < KE; ++j) {
       const bool act = (pending >> j) & 1u;
       const bool mine = own[j] == i0 + j;
-      const bool dup = !mine && key[j] == pos[j];
+      const bool dup = !mine && kk[j] == key[j];
       if (act && dup) err |= HS_ERR_DUP;
       if (act && (mine || dup)) pending &= ~(1u << j);
       if (act && !mine && !dup) hh[j] = (hh[j] + 1) & hmask;
+      if (((hitb >> j) & 1u) && so[j] != (int16_t)(i0 + j)) err |= HS_ERR_DUP;
     }
   }
   // (no barrier: compare-and-swap only fills empty buckets, and every home bucket read
@@ -388,7 +409,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       const int32_t prev = atomicCAS(&htab[hh[j]], -1, i0 + j);
       if (prev == -1) {
         pending &= ~(1u << j);
-      } else if (selp[prev] == pos[j]) {
+      } else if (selp[prev] == key[j]) {
         err |= HS_ERR_DUP;
         pending &= ~(1u << j);
       } else {
@@ -401,7 +422,6 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   int16_t* widx = (int16_t*)(smem + Ly.widx) + wid * Ly.wcap;  // and list index
   const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
   const float invC = 1.0f / (float)C;
-  uint32_t fmiss = 0;
   int mw = 0;  // misses of this wave
   {
 #pragma unroll
@@ -409,7 +429,6 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       const bool miss = fpos[q] >= 0 && fpos[q] != newest && fres[q] < 0 && fpt[q] < 0;
       const uint64_t b = __ballot(miss);
       if (miss) {
-        fmiss |= 1u << q;
         const int at = mw + lanes_below(b);
         wpos[at] = fpos[q];
         widx[at] = (int16_t)(f_lo + q * NT + lane * NW + wid);
@@ -440,15 +459,10 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   __syncthreads();
   err = (uint32_t)sh[0] | (sh[1] > 1 ? HS_ERR_DUP : 0u);
   const bool h1 = sh[2] != 0;  // current metadata in half 1, new metadata goes to half 0
-  int32_t spo[E];
   int16_t lro[E];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    spo[j] = h1 ? spb[j] : spa[j];
-    lro[j] = h1 ? lrb[j] : lra[j];
-  }
+  for (int j = 0; j < E; ++j) lro[j] = h1 ? lrb[j] : lra[j];
   int16_t* lru_new = p.lru + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.Bpad;
-  int32_t* sp_new = p.slot_pos + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.B;
 
   if (err) {  // every workgroup of the request sees the same error; nothing changes
     if (g == 0) {
@@ -464,70 +478,18 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   // this launch changes the metadata: the next one finds it in the other half
   if (tid == 0) __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- stage 2: mark each slot hit (its position is selected) or evictable --------------
-  uint32_t probing = 0;
-  uint32_t hs2[E];
-#pragma unroll
-  for (int j = 0; j < E; ++j) {
-    hs2[j] = spo[j] >= 0 ? hash_pos(spo[j], p.hash_bits) : 0;
-    if (e0 + j < p.B && spo[j] >= 0) probing |= 1u << j;
-  }
-  uint32_t hitbits = 0;
-  while (probing) {
-    // branch-free probe step: all reads of the thread in flight together
-    int32_t ent[E], key[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) ent[j] = htab[hs2[j]];
-#pragma unroll
-    for (int j = 0; j < E; ++j) key[j] = selp[ent[j] < 0 ? 0 : ent[j]];
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const bool act = (probing >> j) & 1u;
-      const bool empty = ent[j] < 0;
-      const bool match = !empty && key[j] == spo[j];
-      if (act && match) {
-        selslot[ent[j]] = e0 + j;
-        hitbits |= 1u << j;
-      }
-      if (act && (empty || match)) probing &= ~(1u << j);
-      if (act && !empty && !match) hs2[j] = (hs2[j] + 1) & hmask;
-    }
-  }
-  if (e0 < p.B) {
-    bool stored = false;
-    if constexpr (E >= 4) {
-      if (bvec) {
-#pragma unroll
-        for (int v = 0; v < E / 4; ++v)  // four flag bytes per 32-bit LDS store
-          *(uint32_t*)(sflag + e0 + 4 * v) = ((hitbits >> (4 * v)) & 1u) | (((hitbits >> (4 * v + 1)) & 1u) << 8) |
-                                             (((hitbits >> (4 * v + 2)) & 1u) << 16) |
-                                             (((hitbits >> (4 * v + 3)) & 1u) << 24);
-        stored = true;
-      }
-    }
-    if (!stored) {
-#pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (e0 + j < p.B) sflag[e0 + j] = (hitbits >> j) & 1u;
-    }
-  }
-  __syncthreads();
-
   // ---- stage 3: misses in list order and evictables in LRU order, one scan -------------
   uint32_t mbits = 0, ebits = 0;
   {
-    int32_t ss[KE];
-    uint8_t sf[E];
+    int16_t sf[E];
 #pragma unroll
-    for (int j = 0; j < KE; ++j) ss[j] = selslot[min(i0 + j, p.k - 1)];
-#pragma unroll
-    for (int j = 0; j < E; ++j) sf[j] = sflag[lro[j]];
+    for (int j = 0; j < E; ++j) sf[j] = sown[lro[j]];
 #pragma unroll
     for (int j = 0; j < KE; ++j)
-      if (j < EK && i0 + j < p.k && ss[j] == -1) mbits |= 1u << j;
+      if (cls[j] == -1) mbits |= 1u << j;
 #pragma unroll
     for (int j = 0; j < E; ++j)
-      if (e0 + j < p.B && sf[j] == 0) ebits |= 1u << j;
+      if (e0 + j < p.B && sf[j] == -1) ebits |= 1u << j;
   }
   int rm, re, m, E_;
   block_ranks2<E>(mbits, ebits, carry, rm, re, m, E_);  // m misses, E_ evictable slots
@@ -542,8 +504,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       const int s = lro[j];
       if (re < m) {
         victim[re] = (int16_t)s;
-        vmiss[s] = (int16_t)re;
-        sflag[s] = 2;
+        sown[s] = (int16_t)(-2 - re);
       } else if (g == 0) {
         lru_new[re - m] = (int16_t)s;  // untouched evictables keep their old order
       }
@@ -554,14 +515,25 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
 
   // with several workgroups, workgroup 0 publishes while the others fetch
   if (g == 0) {
+    int32_t spo[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) spo[j] = h1 ? spb[j] : spa[j];
+    int32_t* sp_new = p.slot_pos + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.B;
     // filled victims, then hits, each by slot index, after the untouched evictables
-    uint32_t vb = 0, hb = 0;
+    int16_t fo[E];
+    int32_t hp[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) fo[j] = (e0 + j < p.B) ? sown[e0 + j] : (int16_t)-1;
+#pragma unroll
+    for (int j = 0; j < E; ++j) hp[j] = selp[fo[j] >= 0 ? fo[j] : 0];
+    uint32_t vb = 0, hb = 0, bad = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const uint8_t f = (e0 + j < p.B) ? sflag[e0 + j] : 0;
-      vb |= (uint32_t)(f == 2) << j;
-      hb |= (uint32_t)(f == 1) << j;
+      vb |= (uint32_t)(fo[j] <= -2) << j;
+      hb |= (uint32_t)(fo[j] >= 0) << j;
+      bad |= (uint32_t)(fo[j] >= 0 && hp[j] != spo[j]);  // a hit's slot must hold its position
     }
+    if (bad) atomicOr((unsigned*)&sh[3], HS_ERR_STATE);
     int rv, rh, tv, th;
     block_ranks2<E>(vb, hb, carry + 2 * NW, rv, rh, tv, th);
     int32_t* pt = p.page_table + (size_t)r * p.max_positions;
@@ -578,7 +550,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       if (s >= p.B) continue;
       if ((vb >> j) & 1u) {
         lru_new[E_ - m + rv++] = (int16_t)s;
-        const int jm = vmiss[s];
+        const int jm = -2 - fo[j];
         const int i = missidx[jm];
         const int32_t np = selp[i];
         if (spo[j] >= 0) pt[spo[j]] = -1;  // the evicted position is host-only again
@@ -611,16 +583,11 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
         if (e0 + j < p.B) sp_new[e0 + j] = spn[j];
     }
 #pragma unroll
-    for (int j = 0; j < KE; ++j) {
-      const int i = i0 + j;
-      if (j < EK && i < p.k) {
-        const int s = selslot[i];
-        if (s >= 0) outr[i] = s;
-      }
-    }
+    for (int j = 0; j < KE; ++j)
+      if (cls[j] >= 0) outr[i0 + j] = cls[j];
     if (tid == 0) {
       if (p.stats) {
-        hs_stats st = {(uint32_t)(p.k - m - nres), (uint32_t)m, 0u, (uint32_t)nres};
+        hs_stats st = {(uint32_t)(p.k - m - nres), (uint32_t)m, (uint32_t)sh[3], (uint32_t)nres};
         p.stats[r] = st;
       }
       if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;
@@ -630,14 +597,6 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
 
   // ---- stage 4, second part: the fetched records go to the slots stage 3 chose --------
   if (fetcher) {
-    // the page table and the hash must agree on every miss of this share
-    uint32_t bad = 0;
-#pragma unroll
-    for (int q = 0; q < KE; ++q) {
-      const int e = q * NT + lane * NW + wid;
-      if (e < f_n && fpos[q] >= 0) bad |= (uint32_t)(((fmiss >> q) & 1u) != (selslot[f_lo + e] == -1));
-    }
-    if (bad && p.stats) atomicOr(&p.stats[r].error, HS_ERR_STATE);
 #pragma unroll
     for (int u = 0; u < kEarly; ++u) {
       const int c = lane + 64 * u;
