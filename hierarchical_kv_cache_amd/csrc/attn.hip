@@ -21,6 +21,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AT = 256;                 // 4 waves
@@ -253,45 +254,59 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
 }
 
 // Merge of the S chunk partials of one (request, head): o = sum_s 2^(m_s - M) o_s /
-// sum_s 2^(m_s - M) l_s.  One workgroup of 128 threads per (request, head), 4 channels each.
-__global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams p) {
+// sum_s 2^(m_s - M) l_s.  One wave per (request, head, 128 channels), two channels per
+// lane.  Every lane issues its (m, l) pairs and the first kMergeBatch partial rows at once,
+// so a merge of up to kMergeBatch chunks costs one memory round trip.
+constexpr int kMergeBatch = 32;
+constexpr int kMergeQuarters = kAttnDv / 128;
+
+__global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
   __shared__ float fac[kAttnMaxChunks];
-  __shared__ float s_den;
-  const int r = blockIdx.x / p.heads, hh = blockIdx.x - r * p.heads;
+  const int rh = blockIdx.x / kMergeQuarters, qt = blockIdx.x - rh * kMergeQuarters;
+  const int r = rh / p.heads, hh = rh - r * p.heads;
   if (p.num_reqs && r >= *p.num_reqs) return;
+  const int lane = threadIdx.x;
   const float* pr = p.part + (size_t)r * p.S * kPartStride;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    float M = -INFINITY;
-    for (int q = tid; q < p.S; q += 64) M = fmaxf(M, pr[(size_t)q * kPartStride + 16 * kAttnDv + hh]);
+  const float* base = pr + hh * kAttnDv + qt * 128 + 2 * lane;
+  constexpr int NU = kAttnMaxChunks / 64;
+  float mv[NU], lv[NU];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
-    float den = 0.0f;
-    for (int q = tid; q < p.S; q += 64) {
-      const float* pq = pr + (size_t)q * kPartStride;
-      const float f = exp2f(pq[16 * kAttnDv + hh] - M);
-      fac[q] = f;
-      den += f * pq[16 * kAttnDv + 16 + hh];
-    }
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) den += __shfl_xor(den, d);
-    if (tid == 0) s_den = den;
+  for (int u = 0; u < NU; ++u) {
+    const int q = lane + 64 * u;
+    const float* pq = pr + (size_t)q * kPartStride + 16 * kAttnDv;
+    mv[u] = q < p.S ? pq[hh] : -INFINITY;
+    lv[u] = q < p.S ? pq[16 + hh] : 0.0f;
   }
+  f32x2 v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)
+    v[u] = u < p.S ? *(const f32x2*)(base + (size_t)u * kPartStride) : f32x2{0.0f, 0.0f};
+  float M = mv[0];
+#pragma unroll
+  for (int u = 1; u < NU; ++u) M = fmaxf(M, mv[u]);
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
+  float den = 0.0f;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const float f = exp2f(mv[u] - M);  // 0 for the chunks past S (m = -inf)
+    fac[lane + 64 * u] = f;
+    den += f * lv[u];
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) den += __shfl_xor(den, d);
   __syncthreads();
-  const int c = tid * 4;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const float* base = pr + hh * kAttnDv + c;
-  for (int q0 = 0; q0 < p.S; q0 += 16) {
-    f32x4 v[16];
+  f32x2 acc = {0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      v[u] = q0 + u < p.S ? *(const f32x4*)(base + (size_t)(q0 + u) * kPartStride) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int u = 0; u < kMergeBatch; ++u) acc += fac[u] * v[u];
+  for (int q0 = kMergeBatch; q0 < p.S; q0 += kMergeBatch) {  // more than kMergeBatch chunks
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (q0 + u < p.S) acc += fac[q0 + u] * v[u];
+    for (int u = 0; u < kMergeBatch; ++u)
+      v[u] = q0 + u < p.S ? *(const f32x2*)(base + (size_t)(q0 + u) * kPartStride) : f32x2{0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) acc += fac[q0 + u < kAttnMaxChunks ? q0 + u : 0] * v[u];
   }
-  const float inv = 1.0f / s_den;
-  *(f32x4*)(p.out + ((size_t)r * p.heads + hh) * p.value_dim + c) = acc * inv;
+  *(f32x2*)(p.out + ((size_t)r * p.heads + hh) * p.value_dim + qt * 128 + 2 * lane) = acc * (1.0f / den);
 }
 
 }  // namespace
@@ -301,7 +316,7 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(AT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(p.R * p.heads), dim3(128), 0, s, p);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(p.R * p.heads * kMergeQuarters), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
