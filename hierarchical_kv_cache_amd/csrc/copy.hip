@@ -55,8 +55,9 @@ __global__ void __launch_bounds__(kCopyThreads) backup_kernel(AppendParams p) {
     const int l = rest / C, c = rest - l * C;
     const u32x4* src =
         (const u32x4*)(p.hot + (((size_t)r * p.L + l) * (p.B + 1) + p.B) * p.rec_bytes) + c;
-    u32x4* dst = (u32x4*)(p.host_base[r] + ((size_t)l * p.max_positions + pos) * p.rec_bytes) + c;
-    __builtin_nontemporal_store(*src, dst);
+    // the pool table is shared with the readers (const); the write-through owns this row
+    uint8_t* row = const_cast<uint8_t*>(p.host_base[r]) + ((size_t)l * p.max_positions + pos) * p.rec_bytes;
+    store_host16(*src, row + 16 * (size_t)c);
   }
   __threadfence_system();
 }
@@ -87,8 +88,7 @@ __global__ void __launch_bounds__(kCopyThreads) replay_kernel(ReplayParams p) {
         const int f = f0 + u * stride;
         if (f < total) {
           split_index(f, C, invC, jj[u], cc[u]);
-          v[u] = __builtin_nontemporal_load(
-              (const u32x4*)(hbase + (size_t)ppos[jj[u]] * p.rec_bytes) + cc[u]);
+          v[u] = load_host16(hbase + (size_t)ppos[jj[u]] * p.rec_bytes + 16 * (size_t)cc[u]);
         }
       }
 #pragma unroll

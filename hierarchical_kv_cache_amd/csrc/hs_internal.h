@@ -17,6 +17,19 @@ constexpr uint32_t kHasNewest = 1u << 8;  // internal resolve flag: slot B holds
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// 16-byte non-temporal access to the pinned host pool through global (not flat)
+// addresses.  The pool's device addresses come from a table in memory, so the compiler
+// cannot prove their address space and would emit flat instructions, which also count
+// against the LDS wait counter: every barrier's wait for LDS would then wait for the PCIe
+// round trip as well.
+typedef uint32_t hs_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ hs_u32x4 load_host16(const uint8_t* p) {
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) hs_u32x4*)p);
+}
+__device__ __forceinline__ void store_host16(hs_u32x4 v, uint8_t* p) {
+  __builtin_nontemporal_store(v, (__attribute__((address_space(1))) hs_u32x4*)p);
+}
+
 // LDS carve-up of the resolve kernel (shared by host sizing and device code).
 struct ResolveLds {
   size_t htab, selp, victim, missidx, mrank, sown, wpos, widx, wcap, scratch, total;

@@ -450,7 +450,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       int cc = c - l * C;
       if (cc < 0) { --l; cc += C; }
       if (cc >= C) { ++l; cc -= C; }
-      early[u] = __builtin_nontemporal_load((const u32x4*)(hbase + (size_t)wpos[l] * (size_t)p.rec_bytes) + cc);
+      early[u] = load_host16(hbase + (size_t)wpos[l] * (size_t)p.rec_bytes + 16 * (size_t)cc);
     }
   }
 
@@ -623,7 +623,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
           if (x >= C) { ++l; x -= C; }
           ll[u] = l;
           cc[u] = x;
-          v[u] = __builtin_nontemporal_load((const u32x4*)(hbase + (size_t)wpos[l] * (size_t)p.rec_bytes) + x);
+          v[u] = load_host16(hbase + (size_t)wpos[l] * (size_t)p.rec_bytes + 16 * (size_t)x);
         }
       }
 #pragma unroll
