@@ -23,7 +23,7 @@ from . import _build
 LIB_PATH = _build.LIB
 
 HS_OK, HS_EINVAL, HS_ENOMEM, HS_EHIP, HS_ESTATE = 0, -1, -2, -3, -4
-HS_CFG_NEWEST_SLOT = 1
+HS_CFG_NEWEST_SLOT, HS_CFG_RECORD_FP8 = 1, 2
 HS_RECORD_PLAN, HS_SKIP_IO = 1, 2
 HS_ERR_DUP, HS_ERR_RANGE, HS_ERR_STATE, HS_ERR_RESIDENT = 1, 2, 4, 8
 
@@ -198,9 +198,10 @@ def hs_probe_empty(stream):
 # ---- convenience owner --------------------------------------------------------------------
 
 def make_config(R, L, max_positions, top_k, buffer_slots, record_bytes=1152, block_tokens=1, layer_group=1,
-                wgs_per_request=0, newest_slot=False) -> hs_config:
-    return hs_config(R, L, max_positions, record_bytes, top_k, block_tokens, buffer_slots, layer_group,
-                     wgs_per_request, HS_CFG_NEWEST_SLOT if newest_slot else 0)
+                wgs_per_request=0, newest_slot=False, fp8=False) -> hs_config:
+    flags = (HS_CFG_NEWEST_SLOT if newest_slot else 0) | (HS_CFG_RECORD_FP8 if fp8 else 0)
+    return hs_config(R, L, max_positions, 656 if fp8 else record_bytes, top_k, block_tokens, buffer_slots,
+                     layer_group, wgs_per_request, flags)
 
 
 class HiSparse:

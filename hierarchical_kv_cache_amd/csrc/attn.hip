@@ -33,6 +33,11 @@ constexpr int CHUNKS = kAttnDk * 2 / 16;  // 72 16-byte chunks per record
 constexpr int CT = kAttnDv / 4 / 16;    // 8 channel tiles of 16 per wave
 constexpr int GATHER = TT * CHUNKS / AT;  // 18 16-byte chunks per thread per tile
 constexpr int QS = kAttnDk * 2 + 16;       // LDS stride of a query row (padded off the bank period)
+// FP8 records (the fp8 latent-KV layout, 656 bytes): 512 E4M3 codes in 4 blocks of 128 with
+// a float32 scale each, then 64 bf16.  The gather turns them into the same bf16 rows.
+constexpr int F8_DATA = 32;                // 16-byte chunks of codes (16 values each)
+constexpr int F8_ITEMS = F8_DATA + 8;      // + 8 chunks of bf16 rope values
+constexpr int F8_GATHER = TT * F8_ITEMS / AT;  // 10 items per thread per tile
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   uint32_t u = __float_as_uint(x);
@@ -41,11 +46,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+template <bool FP8>
 __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char rows[TT * RS];
   __shared__ __attribute__((aligned(16))) unsigned char qs[16 * QS];  // q rows, zero past `heads`
-  __shared__ __attribute__((aligned(16))) uint16_t phi[2][16][32];  // [32-token block][head][k]
-  __shared__ __attribute__((aligned(16))) uint16_t plo[2][16][32];
+  // P (hi and lo bf16 parts) as P V operands: [wave][32-token block][head][k].  With FP8
+  // records each wave gets P times its channel block's per-token scale.
+  constexpr int PW = FP8 ? 4 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t phi[PW][2][16][32];
+  __shared__ __attribute__((aligned(16))) uint16_t plo[PW][2][16][32];
+  __shared__ float s_scale[FP8 ? TT : 1][4];  // FP8: the block scales of each token of the tile
   __shared__ float smax[4][16];
   __shared__ float ssum[4][16];
   __shared__ int s_slot[kAttnMaxChunk];
@@ -103,24 +113,38 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  // records of the tile starting at token t0: 18 16-byte loads per thread, all in flight
-  u32x4 stage[GATHER];
+  // records of the tile starting at token t0: 18 16-byte loads per thread (bf16 records) or
+  // 10 (FP8 records, each data chunk with its block's scale), all in flight
+  constexpr int NG = FP8 ? F8_GATHER : GATHER;
+  u32x4 stage[NG];
+  float sscale[FP8 ? NG : 1];
+  // the record of a published slot: 0..B hot rows, B+1+row resident rows, else none
+  auto record_of = [&](int tok) -> const uint8_t* {
+    const int sl = s_slot[tok - t_begin];
+    const int64_t rr = (int64_t)sl - (p.B + 1);
+    return (sl >= 0 && sl <= p.B) ? hot_r + (size_t)sl * p.rec_bytes
+           : (rr >= 0 && rr < p.res_rows) ? p.res + (size_t)rr * p.rec_bytes : nullptr;
+  };
   auto gather = [&](int t0) {
 #pragma unroll
-    for (int u = 0; u < GATHER; ++u) {
+    for (int u = 0; u < NG; ++u) {
       const int f = tid + u * AT;
-      const int row = f / CHUNKS, c = f - row * CHUNKS;
+      const int row = f / (FP8 ? F8_ITEMS : CHUNKS), c = f - row * (FP8 ? F8_ITEMS : CHUNKS);
       const int tok = t0 + row;
-      // past the end: exact zeros.  Slots 0..B are hot rows, B+1+row resident rows; any
-      // other value reads as NaN, so the output shows it
+      // past the end: exact zeros; no record (a slot outside the published range): NaN, so
+      // the output shows it
       if (tok >= t_end) {
         stage[u] = zero4;
+        if constexpr (FP8) sscale[u] = 0.0f;
       } else {
-        const int sl = s_slot[tok - t_begin];
-        const int64_t rr = (int64_t)sl - (p.B + 1);
-        const uint8_t* src = (sl >= 0 && sl <= p.B) ? hot_r + (size_t)sl * p.rec_bytes
-                             : (rr >= 0 && rr < p.res_rows) ? p.res + (size_t)rr * p.rec_bytes : nullptr;
-        stage[u] = src ? *((const u32x4*)src + c) : nan4;
+        const uint8_t* src = record_of(tok);
+        if constexpr (FP8) {
+          const int off = c < F8_DATA ? 16 * c : 528 + 16 * (c - F8_DATA);
+          stage[u] = src ? *(const u32x4*)(src + off) : nan4;
+          sscale[u] = (src && c < F8_DATA) ? *(const float*)(src + 512 + 4 * (c >> 3)) : __builtin_nanf("");
+        } else {
+          stage[u] = src ? *((const u32x4*)src + c) : nan4;
+        }
       }
     }
   };
@@ -137,10 +161,33 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     __syncthreads();  // the previous tile is no longer read
 #pragma unroll
-    for (int u = 0; u < GATHER; ++u) {
-      const int f = tid + u * AT;
-      const int row = f / CHUNKS, c = f - row * CHUNKS;
-      *(u32x4*)(rows + row * RS + c * 16) = stage[u];
+    for (int u = 0; u < NG; ++u) {
+      if constexpr (FP8) {
+        const int f = tid + u * AT;
+        const int row = f / F8_ITEMS, c = f - row * F8_ITEMS;
+        if (c < F8_DATA) {
+          // 16 codes -> 16 bf16, exactly (an E4M3 value has 4 significant bits); the block
+          // scale is applied to the fp32 sums below instead of rounding code * scale
+          uint32_t wv[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[u][q], false);
+            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[u][q], true);
+            wv[2 * q] = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xFFFF0000u);
+            wv[2 * q + 1] = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xFFFF0000u);
+          }
+          u32x4* d = (u32x4*)(rows + row * RS + c * 32);
+          d[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+          d[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+          if ((c & 7) == 0) s_scale[row][c >> 3] = sscale[u];
+        } else {
+          *(u32x4*)(rows + row * RS + 1024 + (c - F8_DATA) * 16) = stage[u];
+        }
+      } else {
+        const int f = tid + u * AT;
+        const int row = f / CHUNKS, c = f - row * CHUNKS;
+        *(u32x4*)(rows + row * RS + c * 16) = stage[u];
+      }
     }
     __syncthreads();
     if (t0 + TT < t_end) gather(t0 + TT);  // the next tile's loads fly during this tile's math
@@ -149,11 +196,28 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
     f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
     const unsigned char* krow = rows + (16 * w + col) * RS + qd * 16;
     const unsigned char* qrow = qs + col * QS + qd * 16;  // A operand: q[head = col][32 ks + 8 qd + j]
+    if constexpr (FP8) {
+      // one accumulator per 128-dim scale block (4 k-steps each) and one for the bf16 part
+      f32x4 sb[5];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8 qa = *(const bf16x8*)(qrow + ks * 64);
-      const bf16x8 kb = *(const bf16x8*)(krow + ks * 64);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, sacc, 0, 0, 0);
+      for (int b = 0; b < 5; ++b) sb[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 qa = *(const bf16x8*)(qrow + ks * 64);
+        const bf16x8 kb = *(const bf16x8*)(krow + ks * 64);
+        sb[ks < 16 ? ks >> 2 : 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, sb[ks < 16 ? ks >> 2 : 4], 0, 0, 0);
+      }
+      const float* scl = s_scale[16 * w + col];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc[i] = sb[0][i] * scl[0] + sb[1][i] * scl[1] + sb[2][i] * scl[2] + sb[3][i] * scl[3] + sb[4][i];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 qa = *(const bf16x8*)(qrow + ks * 64);
+        const bf16x8 kb = *(const bf16x8*)(krow + ks * 64);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, sacc, 0, 0, 0);
+      }
     }
     const bool valid = (t0 + 16 * w + col) < t_end;
     float sv[4], mx[4];
@@ -182,9 +246,20 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
       m_run[i] = mn;
       const float pv = exp2f(sv[i] - mn);
       l_lane[i] = l_lane[i] * alpha[i] + pv;
-      const uint16_t hi = f32_to_bf16_bits(pv);
-      phi[bk][hh][kk] = hi;
-      plo[bk][hh][kk] = f32_to_bf16_bits(pv - bf16_bits_to_f32(hi));
+      if constexpr (FP8) {
+        const float* scl = s_scale[tl];
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const float pw = pv * scl[w2];
+          const uint16_t hi = f32_to_bf16_bits(pw);
+          phi[w2][bk][hh][kk] = hi;
+          plo[w2][bk][hh][kk] = f32_to_bf16_bits(pw - bf16_bits_to_f32(hi));
+        }
+      } else {
+        const uint16_t hi = f32_to_bf16_bits(pv);
+        phi[0][bk][hh][kk] = hi;
+        plo[0][bk][hh][kk] = f32_to_bf16_bits(pv - bf16_bits_to_f32(hi));
+      }
     }
     __syncthreads();
 
@@ -195,8 +270,8 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
       for (int i = 0; i < 4; ++i) o[c][i] *= alpha[i];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const bf16x8 ahi = *(const bf16x8*)&phi[b][col][qd * 8];
-      const bf16x8 alo = *(const bf16x8*)&plo[b][col][qd * 8];
+      const bf16x8 ahi = *(const bf16x8*)&phi[FP8 ? w : 0][b][col][qd * 8];
+      const bf16x8 alo = *(const bf16x8*)&plo[FP8 ? w : 0][b][col][qd * 8];
       const unsigned char* vb = rows + (b * 32 + qd) * RS + (w * 128 + col) * 2;
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
@@ -313,7 +388,8 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   const int grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * p.S : p.R * p.S;
-  hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(AT), 0, s, p);
+  if (p.fp8) hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(AT), 0, s, p);
+  else hipLaunchKernelGGL(attn_kernel<false>, dim3(grid), dim3(AT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(p.R * p.heads * kMergeQuarters), dim3(64), 0, s, p);

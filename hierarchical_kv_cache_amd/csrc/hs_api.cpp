@@ -98,7 +98,9 @@ hs_status validate(const hs_config* c) {
     return fail(HS_EINVAL, "layer_group must be in [1, num_layers]");
   if (c->wgs_per_request < 0 || c->wgs_per_request > 256)
     return fail(HS_EINVAL, "wgs_per_request must be in [0, 256]");
-  if (c->flags & ~HS_CFG_NEWEST_SLOT) return fail(HS_EINVAL, "unknown config flags");
+  if (c->flags & ~(HS_CFG_NEWEST_SLOT | HS_CFG_RECORD_FP8)) return fail(HS_EINVAL, "unknown config flags");
+  if ((c->flags & HS_CFG_RECORD_FP8) && c->record_bytes != 656)
+    return fail(HS_EINVAL, "HS_CFG_RECORD_FP8 needs record_bytes = 656");
   // every flattened copy index stays below 2^24 (kernels divide it in float)
   if (int64_t(c->top_k) * (c->record_bytes / 16) >= (int64_t(1) << 24) ||
       int64_t(c->num_requests) * c->num_layers * (c->record_bytes / 16) >= (int64_t(1) << 24))
@@ -411,7 +413,9 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
                          void* stream) {
   hs_status st;
   if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
-  if (h->cfg.record_bytes != kAttnDk * 2) return fail(HS_EINVAL, "attention needs 576-element bf16 records");
+  const bool fp8 = (h->cfg.flags & HS_CFG_RECORD_FP8) != 0;
+  if (!fp8 && h->cfg.record_bytes != kAttnDk * 2)
+    return fail(HS_EINVAL, "attention needs 576-element bf16 records (or HS_CFG_RECORD_FP8)");
   if (heads < 1 || heads > kAttnMaxHeads) return fail(HS_EINVAL, "heads must be in [1, %d]", kAttnMaxHeads);
   if (value_dim != kAttnDv) return fail(HS_EINVAL, "value_dim must be %d", kAttnDv);
   if (!d_q || !d_slots || !d_out) return fail(HS_EINVAL, "null q, slots or output");
@@ -426,7 +430,7 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
   p.value_dim = value_dim; p.S = h->lay.S;
   p.chunk = (int)align_up((size_t)((h->cfg.top_k + p.S - 1) / p.S), 64);
   p.S = (h->cfg.top_k + p.chunk - 1) / p.chunk;  // no empty chunk
-  p.rec_bytes = h->cfg.record_bytes; p.scale = scale;
+  p.rec_bytes = h->cfg.record_bytes; p.scale = scale; p.fp8 = fp8 ? 1 : 0;
   HS_HIP(launch_attn(p, (hipStream_t)stream));
   return HS_OK;
 }

@@ -115,6 +115,7 @@ struct AttnParams {
   int64_t res_rows;
   int32_t R, k, B, heads, value_dim, S, chunk, rec_bytes;
   float scale;
+  int32_t fp8;               // records in the FP8 layout (HS_CFG_RECORD_FP8)
 };
 
 struct ExportParams {

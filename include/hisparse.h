@@ -51,6 +51,10 @@ typedef int32_t hs_status;
 
 /* hs_config.flags */
 #define HS_CFG_NEWEST_SLOT 1u /* slot B of every (request, layer) holds the newest token ([GC] §3.4, §5.2) */
+#define HS_CFG_RECORD_FP8 2u  /* records are fp8 latent KV ([GC] §5.5: fp8_e4m3 KV, FlashMLA-style layout):
+                                 record_bytes = 656 = 512 OCP E4M3 codes in 4 blocks of 128, a float32
+                                 scale per block, then 64 bf16 values; only hs_sparse_attn reads the
+                                 layout (RESOLVE moves records as opaque bytes) */
 
 /* hs_resolve flags ([GC] §5.5: compile-time switches of the pages' kernel) */
 #define HS_RECORD_PLAN 1u /* anchor layer: record the miss plan for its shared layers ([GC] §3.6, §5.5) */
@@ -195,7 +199,9 @@ hs_status hs_wait_layer(hs_handle h, int32_t layer, void* stream);
  * layer (a slot B + 1 + row is row `row` of this layer's bound resident pool),
  * its value the first value_dim of them; s = scale * q k^T, softmax over the
  * top_k entries, o = p v.
- *   d_q     device [R][heads][key_dim] bf16, heads 1..16, key_dim = record_bytes/2 = 576
+ *   d_q     device [R][heads][key_dim] bf16, heads 1..16, key_dim = 576 (with HS_CFG_RECORD_FP8 the
+ *           key is the 512 dequantised values (code * block scale, rounded to bf16) then the 64
+ *           bf16 values; otherwise the record's 576 bf16)
  *   d_slots device [R][top_k] int32 (the layer's, or its anchor's, d_slots_out)
  *   d_out   device [R][heads][value_dim] float32, value_dim = 512
  *   d_num_reqs as for hs_resolve (rows of skipped requests are not written)

@@ -28,6 +28,7 @@ _SO = os.path.join(_HERE, "_records.so")
 _lib = None
 
 RECORD_BYTES = 1152  # 576 bf16 per token: 512 value dims + 64 rope dims (scores use all 576)
+FP8_RECORD_BYTES = 656  # 512 e4m3 codes + 4 float32 block scales + 64 bf16 rope dims
 POISON = 0xFF        # byte of host positions not yet written (bf16 NaN pattern)
 RECORD_SEED = 0
 QUERY_SEED = 1
@@ -98,6 +99,8 @@ def _load():
     i64, u64, vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
     lib.synth_one.argtypes = [vp, u64, i64, i64, i64, i64]
     lib.synth_one.restype = None
+    lib.synth_one_fp8.argtypes = [vp, u64, i64, i64, i64]
+    lib.synth_one_fp8.restype = None
     lib.synth_fill_request.argtypes = [vp, i64, i64, i64, i64, i64, u64, ctypes.c_int, ctypes.c_int]
     lib.synth_fill_request.restype = ctypes.c_int
     lib.synth_records_at.argtypes = [vp, i64, i64, vp, i64, u64]
@@ -126,9 +129,13 @@ def _ptr(buf) -> int:
 
 
 def record(r: int, l: int, pos: int, rec_bytes: int = RECORD_BYTES, seed: int = RECORD_SEED):
-    """The bf16 KV record of (request r, layer l, position pos) as uint8 bytes."""
+    """The KV record of (request r, layer l, position pos) as uint8 bytes: bf16 values, or
+    the FP8 layout when rec_bytes is FP8_RECORD_BYTES."""
     out = np.empty(rec_bytes, np.uint8)
-    _load().synth_one(out.ctypes.data, seed, r, l, pos, rec_bytes // 2)
+    if rec_bytes == FP8_RECORD_BYTES:
+        _load().synth_one_fp8(out.ctypes.data, seed, r, l, pos)
+    else:
+        _load().synth_one(out.ctypes.data, seed, r, l, pos, rec_bytes // 2)
     return out
 
 

@@ -26,16 +26,18 @@ class Pair:
     """One HiSparse handle plus the matching oracle caches for a workload."""
 
     def __init__(self, w: synth.Workload, steps: int | None = None, wgs: int = 0, all_hit=False,
-                 oracle_host_copy: bool | None = None, compare_hot=True, resident: ResidentSpec | None = None):
+                 oracle_host_copy: bool | None = None, compare_hot=True, resident: ResidentSpec | None = None,
+                 fp8: bool = False):
         self.w = w
         self.steps = w.steps if steps is None else steps
         self.lmax = w.max_positions(self.steps)
         self.R, self.L, self.B, self.k, self.kb = w.R, w.L, w.B, w.k, w.kb
-        self.rec = synth.RECORD_BYTES
+        self.fp8 = fp8
+        self.rec = synth.FP8_RECORD_BYTES if fp8 else synth.RECORD_BYTES
         self.compare_hot = compare_hot
         cfg = hk.make_config(w.R, w.L, self.lmax, w.k, w.B, record_bytes=self.rec,
                              block_tokens=w.block_tokens, layer_group=w.group, wgs_per_request=wgs,
-                             newest_slot=w.append)
+                             newest_slot=w.append, fp8=fp8)
         self.gpu = hk.HiSparse(cfg)
         self.h = self.gpu.h
         self.dev = torch.device("cuda")
@@ -43,7 +45,7 @@ class Pair:
         self.side = torch.cuda.Stream()
         # host pools: the prefill records, written by the input generator
         for r in range(w.R):
-            synth.fill_request(self.gpu.host_pool_address(r), r, w.L, self.lmax, w.ctx)
+            synth.fill_request(self.gpu.host_pool_address(r), r, w.L, self.lmax, w.ctx, rec_bytes=self.rec)
         # the oracle reads the same input bytes; with write-through the GPU also writes the
         # pinned pool, so the oracle then keeps a pool of its own
         if oracle_host_copy is None:
@@ -52,7 +54,7 @@ class Pair:
             self.ohost = []
             for r in range(w.R):
                 a = np.empty((w.L, self.lmax, self.rec), np.uint8)
-                synth.fill_request(a, r, w.L, self.lmax, w.ctx)
+                synth.fill_request(a, r, w.L, self.lmax, w.ctx, rec_bytes=self.rec)
                 self.ohost.append(a)
         else:
             self.ohost = [self.gpu.host_pool(r) for r in range(w.R)]
@@ -111,7 +113,7 @@ class Pair:
         results = {}
         if w.append:
             p = w.ctx + t
-            recs = synth.records_at(w.R, w.L, [p] * w.R)
+            recs = synth.records_at(w.R, w.L, [p] * w.R, rec_bytes=self.rec)
             d_new = torch.from_numpy(recs).to(self.dev)
             d_pos = torch.full((w.R,), p, dtype=torch.int32, device=self.dev)
             hk.hs_append(self.h, d_new.data_ptr(), d_pos.data_ptr(), self.compute.cuda_stream,
@@ -216,9 +218,9 @@ class Pair:
                                          % (r, l, len(bad), bad[:5]))
                 # the bytes are the record of the position the slot holds (input generator)
                 for s in occ[:: max(1, occ.size // 16)]:
-                    assert np.array_equal(g[s], synth.record(r, l, int(st["slot_pos"][s]))), (r, l, s)
+                    assert np.array_equal(g[s], synth.record(r, l, int(st["slot_pos"][s]), self.rec)), (r, l, s)
                 if w.append and st["newest_pos"] >= 0:
-                    assert np.array_equal(g[w.B], synth.record(r, l, st["newest_pos"]))
+                    assert np.array_equal(g[w.B], synth.record(r, l, st["newest_pos"], self.rec))
 
     def close(self):
         torch.cuda.synchronize()
