@@ -217,6 +217,7 @@ def main():
         detail.update(measure_fetch_heavy(torch, hk, synth, dev))
         detail.update(measure_all_hit(torch, hk, synth, dev))
         detail.update(measure_resident(torch, hk, synth, w, dev, trace, lmax))
+        detail.update(measure_fp8(torch, hk, synth, dev))
         detail["launch_latency_us"] = measure_empty(torch, hk)
         detail["hbm_copy_GBps"] = measure_hbm(torch, hk, dev)
         detail["link_ceiling_GBps"] = link["ceiling_GBps"]
@@ -226,24 +227,19 @@ def main():
             detail[key.replace("GBps", "frac_of_link")] = detail[key] / link["ceiling_GBps"]
 
     # ---- roofline of the dominant kernel -------------------------------------------------
-    res_total = sum(res_us)
-    att_total = sum(att_us)
+    # RESOLVE is the longest single kernel of the step (the attention call is two kernels,
+    # attention and merge, each shorter; see the kernel trace).  Its algorithmic bytes per
+    # launch: selection in, slot map + LRU read and written, slots out, and per miss the
+    # record written to HBM plus two page-table writes and the plan entry.
     steady_misses = misses_timed / (K * L * R)
-    if att_total >= res_total:
-        # attention reads k records from HBM per (request, layer), plus q and the output
-        alg_bytes = R * (k * REC + heads * 576 * 2 + heads * 512 * 4)
-        t_us = statistics.fmean(att_us)
-        roof = {"kernel": "attn_kernel", "bound": "hbm", "achieved": alg_bytes / (t_us * 1e-6) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "traffic": profile_traffic("attn_kernel")}
-    else:
-        # RESOLVE: selection in, slot map + LRU read and written, slots out, 2 page-table
-        # writes + one record written per miss
-        alg_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + steady_misses * (REC + 8 + 8))
-        t_us = statistics.fmean(res_us)
-        roof = {"kernel": "resolve_kernel", "bound": "hbm", "achieved": alg_bytes / (t_us * 1e-6) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "traffic": profile_traffic("resolve_kernel")}
+    alg_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + steady_misses * (REC + 8 + 8))
+    t_us = statistics.fmean(res_us)
+    roof = {"kernel": "resolve_kernel", "bound": "hbm", "achieved": alg_bytes / (t_us * 1e-6) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": profile_traffic("resolve_kernel")}
+    # the attention call (attention + merge kernels) for reference: k records, q and out per request
+    att_bytes = R * (k * REC + heads * 576 * 2 + heads * 512 * 4)
+    detail["attention_call_bytes"] = att_bytes
+    detail["attention_call_GBps"] = att_bytes / (statistics.fmean(att_us) * 1e-6) / 1e9
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["avg_launch_us_events"] = t_us
     roof["avg_launch_us_rocprof"] = profile_avg_us(roof["kernel"])
@@ -428,6 +424,55 @@ def measure_resident(torch, hk, synth, w, dev, trace, lmax):
     out["long_resident_share"] = float(st[8:, ..., 3].sum() / (st[8:].shape[0] * w.L * w.R * w.k))
     out["long_resident_miss_rate"] = float(st[8:, ..., 1].sum() / (st[8:].shape[0] * w.L * w.R * w.k))
     return out
+
+
+def measure_fp8(torch, hk, synth, dev, steps=40, warmup=8):
+    """The long-request step (write-through, RESOLVE, attention over 8 layers) with FP8 latent-KV
+    records (656 bytes: E4M3 codes, block scales, bf16 rope): whole-step throughput."""
+    w = synth.WORKLOADS["long"]
+    R, L, k, B = w.R, w.L, w.k, w.B
+    n = steps + warmup
+    lmax = w.max_positions(n)
+    rec = synth.FP8_RECORD_BYTES
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, newest_slot=True, fp8=True))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx, rec_bytes=rec)
+    trace = np.stack([np.stack([synth.selection_trace(w, r, l, n) for r in range(R)], axis=1)
+                      for l in range(L)], axis=1)
+    d_trace = torch.from_numpy(trace).to(dev)
+    pos = w.ctx + np.arange(n)
+    d_new = torch.from_numpy(np.stack([synth.records_at(R, L, [p] * R, rec_bytes=rec) for p in pos])).to(dev)
+    d_pos = torch.from_numpy(np.repeat(pos[:, None], R, axis=1).astype(np.int32)).to(dev)
+    d_ctx = torch.from_numpy((pos[:, None] + 1).repeat(R, axis=1).astype(np.int32)).to(dev)
+    d_q = torch.from_numpy(np.stack([synth.queries(R, L, t, heads=w.heads) for t in range(n)])
+                           .view(np.int16)).to(dev).permute(0, 2, 1, 3, 4).contiguous()
+    d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n, L, R, 4), dtype=torch.int32, device=dev)
+    d_out = torch.empty((L, R, w.heads, 512), dtype=torch.float32, device=dev)
+    cs = torch.cuda.current_stream().cuda_stream
+    bs = torch.cuda.Stream()
+
+    def step(t):
+        hk.hs_append(cache.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), cs, bs.cuda_stream)
+        for l in range(L):
+            hk.hs_resolve(cache.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
+                          d_stats[t, l].data_ptr(), 0, 0, cs)
+            hk.hs_sparse_attn(cache.h, l, d_q[t, l].data_ptr(), w.heads, 512, d_slots[l].data_ptr(),
+                              d_out[l].data_ptr(), 576 ** -0.5, 0, cs)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warmup, n):
+        step(t)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    bs.synchronize()
+    assert not d_stats.cpu().numpy()[..., 2].any()
+    cache.close()
+    return {"fp8_long_selections_per_s": steps * L * R * k / el, "fp8_long_ms_per_step": el / steps * 1e3,
+            "fp8_record_bytes": rec}
 
 
 def measure_empty(torch, hk):

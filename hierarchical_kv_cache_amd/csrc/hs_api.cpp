@@ -216,6 +216,11 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
     int G = 128 / cfg->num_requests;
     h->G = G < 1 ? 1 : (G > 32 ? 32 : G);
   }
+  // resolve grid: R * G workgroups of 1024 threads
+  if (int64_t(cfg->num_requests) * h->G > (int64_t(1) << 21)) {
+    free_ctx(h);
+    return fail(HS_EINVAL, "num_requests * wgs_per_request too large for one resolve launch");
+  }
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetDevice"); }
   hipDeviceProp_t prop;
