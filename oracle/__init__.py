@@ -66,6 +66,8 @@ def _load():
     lib.hso_resolve.restype = i32
     lib.hso_resolve_tiered.argtypes = [vp, vp, i32, i64, vp, i64, i32, i64, vp, vp, vp, vp, vp]
     lib.hso_resolve_tiered.restype = i32
+    lib.hso_resolve_rows.argtypes = [vp, vp, i32, i32, i64, vp, i64, i32, i64, vp, vp, vp, vp, vp]
+    lib.hso_resolve_rows.restype = i32
     lib.hso_append.argtypes = [vp, i64, vp, vp]
     lib.hso_append.restype = i32
     lib.hso_replay.argtypes = [vp, vp, i32, vp, vp, i32]
@@ -149,6 +151,26 @@ class Cache:
             raise OracleError(err)
         m = int(counts[1])
         return out, int(counts[0]), m, int(counts[2]), ppos[:m].copy(), pslot[:m].copy()
+
+    def resolve_rows(self, sel, ctx_len: int, host, rtable=None, page_shift: int = 0, res_rows: int = 0):
+        """Resolve the verification rows ``sel`` [Q][k] of one speculative step together
+        (``hso_resolve_rows``).  Returns (out [Q][k], hits, misses, resident, plan_pos,
+        plan_slot, union_size); raises OracleError."""
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        Q, k = sel.shape
+        out = np.empty((Q, k), np.int32)
+        ppos = np.empty(Q * k, np.int32)
+        pslot = np.empty(Q * k, np.int32)
+        counts = np.zeros(4, np.int32)
+        rt = None if rtable is None else np.ascontiguousarray(rtable, dtype=np.int32)
+        err = self._lib.hso_resolve_rows(self._h, sel.ctypes.data, Q, k, ctx_len,
+                                         None if rt is None else rt.ctypes.data, 0 if rt is None else rt.size,
+                                         page_shift, res_rows, _addr(host), out.ctypes.data, ppos.ctypes.data,
+                                         pslot.ctypes.data, counts.ctypes.data)
+        if err:
+            raise OracleError(err)
+        m = int(counts[1])
+        return out, int(counts[0]), m, int(counts[2]), ppos[:m].copy(), pslot[:m].copy(), int(counts[3])
 
     def append(self, pos: int, record: np.ndarray, host=None):
         rec = np.ascontiguousarray(record, dtype=np.uint8)

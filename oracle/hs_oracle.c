@@ -259,6 +259,77 @@ int32_t hso_resolve_tiered(hso_cache* c, const int32_t* sel, int32_t k, int64_t 
   return err;
 }
 
+/*
+ * RESOLVE of several verification rows of one speculative decode step
+ * ("HiSparse 深度解析" (gentlecold.top) §6.5 comparison table; "HiSparse local
+ * KV offload architecture" (docs.vllm.ai), speculative decoding): one call
+ * resolves the union of the rows' selections, in first-reference order
+ * (row by row, then list order), so rows that select the same position share
+ * its slot and no row's miss evicts a slot another row reads.
+ *   sel      : [Q][k] positions, distinct within each row
+ *   out      : [Q][k] slot of each entry (rows sharing a position share it)
+ *   plan_pos, plan_slot : [Q*k] misses of the union in first-reference order
+ *   counts   : [4] hits, misses, resident entries (of the union), union size
+ *   rtable   : resident block table (NULL: no resident tier), as hso_resolve_tiered
+ * Returns 0 or HSO_ERR_* bits (a duplicate within a row is HSO_ERR_DUP); on
+ * error nothing changes.
+ */
+int32_t hso_resolve_rows(hso_cache* c, const int32_t* sel, int32_t Q, int32_t k, int64_t ctx_len,
+                         const int32_t* rtable, int64_t n_pages, int32_t page_shift, int64_t res_rows,
+                         const uint8_t* host, int32_t* out, int32_t* plan_pos, int32_t* plan_slot,
+                         int32_t* counts) {
+  const int64_t n = (int64_t)Q * k;
+  int32_t err = 0;
+  int32_t* uni = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));   /* the union */
+  int32_t* uidx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));  /* entry -> union index */
+  int32_t* uout = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  int32_t* where = (int32_t*)malloc(sizeof(int32_t) * (size_t)c->max_positions);   /* position -> union index */
+  if (!uni || !uidx || !uout || !where) {
+    free(uni); free(uidx); free(uout); free(where);
+    return HSO_ERR_CAPACITY;
+  }
+  /* 1. every position in the context, none twice within a row */
+  for (int32_t q = 0; q < Q; ++q) {
+    for (int32_t i = 0; i < k; ++i) {
+      const int64_t p = sel[(int64_t)q * k + i];
+      if (p < 0 || p >= ctx_len || p >= c->max_positions) { err |= HSO_ERR_RANGE; continue; }
+      if (c->selected[p]) err |= HSO_ERR_DUP;
+      c->selected[p] = 1;
+    }
+    for (int32_t i = 0; i < k; ++i) {
+      const int64_t p = sel[(int64_t)q * k + i];
+      if (p >= 0 && p < c->max_positions) c->selected[p] = 0;
+    }
+  }
+  int32_t nu = 0;
+  if (!err) {
+    /* 2. the union in first-reference order */
+    for (int64_t p = 0; p < c->max_positions; ++p) where[p] = -1;
+    for (int64_t f = 0; f < n; ++f) {
+      const int32_t p = sel[f];
+      if (where[p] < 0) { where[p] = nu; uni[nu++] = p; }
+      uidx[f] = where[p];
+    }
+    /* 3. one resolve of the union */
+    if (rtable) {
+      int32_t c3[3] = {0, 0, 0};
+      err = hso_resolve_tiered(c, uni, nu, ctx_len, rtable, n_pages, page_shift, res_rows, host, uout,
+                               plan_pos, plan_slot, c3);
+      if (!err) { counts[0] = c3[0]; counts[1] = c3[1]; counts[2] = c3[2]; }
+    } else {
+      int32_t c2[2] = {0, 0};
+      err = hso_resolve(c, uni, nu, ctx_len, host, uout, plan_pos, plan_slot, c2);
+      if (!err) { counts[0] = c2[0]; counts[1] = c2[1]; counts[2] = 0; }
+    }
+    if (!err) {
+      for (int64_t f = 0; f < n; ++f) out[f] = uout[uidx[f]];
+      counts[3] = nu;
+    }
+  }
+  free(uni); free(uidx); free(uout); free(where);
+  return err;
+}
+
 /* The new token at `pos`: its record goes to the reserved slot B and is
  * written through to the host pool; it becomes the newest position. */
 int32_t hso_append(hso_cache* c, int64_t pos, const uint8_t* record, uint8_t* host) {
