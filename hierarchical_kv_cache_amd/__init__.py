@@ -40,6 +40,7 @@ class hs_config(ctypes.Structure):
         ("layer_group", ctypes.c_int32),
         ("wgs_per_request", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("verify_rows", ctypes.c_int32),
     ]
 
 
@@ -48,7 +49,8 @@ HS_STATS_DTYPE = np.dtype([("hits", np.uint32), ("misses", np.uint32), ("error",
 
 # every symbol include/hisparse.h declares
 EXPORTS = (
-    "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_bind_resident", "hs_append",
+    "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_resolve_rows", "hs_bind_resident",
+    "hs_append",
     "hs_prefetch_shared",
     "hs_wait_layer", "hs_sparse_attn", "hs_export_state", "hs_page_table", "hs_plan", "hs_reset_request",
     "hs_destroy", "hs_last_error", "hs_resolve_wgs", "hs_probe_host_read", "hs_probe_copy",
@@ -74,6 +76,7 @@ def _load():
         "hs_create": (i32, [cfgp, vp, vp, ctypes.POINTER(vp)]),
         "hs_host_pool": (vp, [vp, i32]),
         "hs_resolve": (i32, [vp, i32, vp, vp, vp, vp, vp, u32, vp]),
+        "hs_resolve_rows": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, u32, vp]),
         "hs_bind_resident": (i32, [vp, vp, i32, i32, vp, i64]),
         "hs_append": (i32, [vp, vp, vp, vp, vp]),
         "hs_prefetch_shared": (i32, [vp, i32, vp, vp]),
@@ -126,6 +129,11 @@ def hs_host_pool(h: int, request: int) -> int:
 def hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, stream):
     _check(_lib.hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats or None, d_num_reqs or None,
                            flags, stream or None))
+
+
+def hs_resolve_rows(h, layer, rows, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, stream):
+    _check(_lib.hs_resolve_rows(h, layer, rows, d_sel, d_ctx_len, d_slots_out, d_stats or None, d_num_reqs or None,
+                                flags, stream or None))
 
 
 def hs_bind_resident(h, d_block_table, pages_per_request, page_tokens, d_resident_kv, resident_rows):
@@ -198,10 +206,10 @@ def hs_probe_empty(stream):
 # ---- convenience owner --------------------------------------------------------------------
 
 def make_config(R, L, max_positions, top_k, buffer_slots, record_bytes=1152, block_tokens=1, layer_group=1,
-                wgs_per_request=0, newest_slot=False, fp8=False) -> hs_config:
+                wgs_per_request=0, newest_slot=False, fp8=False, verify_rows=0) -> hs_config:
     flags = (HS_CFG_NEWEST_SLOT if newest_slot else 0) | (HS_CFG_RECORD_FP8 if fp8 else 0)
     return hs_config(R, L, max_positions, 656 if fp8 else record_bytes, top_k, block_tokens, buffer_slots,
-                     layer_group, wgs_per_request, flags)
+                     layer_group, wgs_per_request, flags, verify_rows)
 
 
 class HiSparse:

@@ -76,8 +76,8 @@ __global__ void __launch_bounds__(kCopyThreads) replay_kernel(ReplayParams p) {
   for (int r = 0; r < p.R; ++r) {
     const int m = (int)p.ctrl[r * 4 + 2];
     const int total = m * C;
-    const int32_t* ppos = p.plan + (size_t)r * 2 * p.k;
-    const int32_t* pslot = ppos + p.k;
+    const int32_t* ppos = p.plan + (size_t)r * 2 * p.plan_k;
+    const int32_t* pslot = ppos + p.plan_k;
     const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
     uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
     for (int f0 = t0; f0 < total; f0 += stride * U) {

@@ -45,8 +45,9 @@ struct Layout {
   int A = 0;        // anchor layers
   int Bpad = 0;
   int S = 1;        // attention chunks per request
+  int kmax = 0;     // longest list one resolve handles: top_k * max(1, verify_rows)
   size_t ctrl = 0, slot_pos = 0, lru = 0, plan = 0, page_table = 0, newest = 0, host_base = 0,
-         attn_part = 0, total = 0;
+         attn_part = 0, uni = 0, umap = 0, uout = 0, ucnt = 0, uerr = 0, total = 0;
 };
 
 int attn_chunks(const hs_config& c) {
@@ -66,16 +67,24 @@ Layout make_layout(const hs_config& c) {
   L.A = (c.num_layers + c.layer_group - 1) / c.layer_group;
   L.Bpad = (int)align_up(B, 8);
   L.S = attn_chunks(c);
+  L.kmax = c.top_k * (c.verify_rows > 1 ? c.verify_rows : 1);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   L.ctrl = take(size_t(L.A) * R * 4 * sizeof(uint32_t));
   L.slot_pos = take(size_t(L.A) * R * 2 * B * sizeof(int32_t));
   L.lru = take(size_t(L.A) * R * 2 * L.Bpad * sizeof(int16_t));
-  L.plan = take(size_t(L.A) * R * 2 * k * sizeof(int32_t));
+  L.plan = take(size_t(L.A) * R * 2 * L.kmax * sizeof(int32_t));
   L.page_table = take(size_t(L.A) * R * size_t(c.max_positions) * sizeof(int32_t));
   L.newest = take(R * sizeof(int32_t));
   L.host_base = take(R * sizeof(void*));
   L.attn_part = take(size_t(c.num_layers) * R * L.S * kPartStride * sizeof(float));
+  if (c.verify_rows > 1) {  // union scratch of hs_resolve_rows (one set per handle)
+    L.uni = take(R * L.kmax * sizeof(int32_t));
+    L.umap = take(R * L.kmax * sizeof(int32_t));
+    L.uout = take(R * L.kmax * sizeof(int32_t));
+    L.ucnt = take(R * sizeof(int32_t));
+    L.uerr = take(R * sizeof(uint32_t));
+  }
   L.total = o;
   return L;
 }
@@ -99,6 +108,13 @@ hs_status validate(const hs_config* c) {
   if (c->wgs_per_request < 0 || c->wgs_per_request > 256)
     return fail(HS_EINVAL, "wgs_per_request must be in [0, 256]");
   if (c->flags & ~(HS_CFG_NEWEST_SLOT | HS_CFG_RECORD_FP8)) return fail(HS_EINVAL, "unknown config flags");
+  if (c->verify_rows < 0 || c->verify_rows > 16) return fail(HS_EINVAL, "verify_rows must be in [0, 16]");
+  if (c->verify_rows > 1) {
+    if (int64_t(c->verify_rows) * c->top_k > kUnionMaxEntries)
+      return fail(HS_EINVAL, "verify_rows * top_k must be <= %d", kUnionMaxEntries);
+    if (c->buffer_slots < c->verify_rows * c->top_k)
+      return fail(HS_EINVAL, "buffer_slots must hold the selections of all verification rows (>= verify_rows * top_k)");
+  }
   if ((c->flags & HS_CFG_RECORD_FP8) && c->record_bytes != 656)
     return fail(HS_EINVAL, "HS_CFG_RECORD_FP8 needs record_bytes = 656");
   // every flattened copy index stays below 2^24 (kernels divide it in float)
@@ -123,6 +139,8 @@ struct hs_ctx {
   int G = 1;
   int hash_bits = 0;
   size_t lds_bytes = 0;
+  int spec_hash_bits = 0, union_hash_bits = 0;  // RESOLVE of a union, and the union kernel
+  size_t spec_lds_bytes = 0;
   int device = 0;
   uint8_t* hot = nullptr;
   uint8_t* ws = nullptr;
@@ -142,7 +160,7 @@ struct hs_ctx {
     return (int32_t*)(ws + lay.slot_pos) + size_t(a) * cfg.num_requests * 2 * cfg.buffer_slots;
   }
   int16_t* lru(int a) { return (int16_t*)(ws + lay.lru) + size_t(a) * cfg.num_requests * 2 * lay.Bpad; }
-  int32_t* plan(int a) { return (int32_t*)(ws + lay.plan) + size_t(a) * cfg.num_requests * 2 * cfg.top_k; }
+  int32_t* plan(int a) { return (int32_t*)(ws + lay.plan) + size_t(a) * cfg.num_requests * 2 * lay.kmax; }
   int32_t* page_table(int a) {
     return (int32_t*)(ws + lay.page_table) + size_t(a) * cfg.num_requests * size_t(cfg.max_positions);
   }
@@ -227,18 +245,37 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
   e = hipGetDeviceProperties(&prop, h->device);
   if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetDeviceProperties"); }
   // hash table of 4k entries (a quarter full), or 2k (half full) when LDS is short
-  h->lds_bytes = resolve_lds(cfg->top_k, cfg->buffer_slots, h->hash_bits).total;
-  if (h->lds_bytes > prop.sharedMemPerBlock) {
-    h->hash_bits -= 1;
-    h->lds_bytes = resolve_lds(cfg->top_k, cfg->buffer_slots, h->hash_bits).total;
-  }
-  if (h->lds_bytes > prop.sharedMemPerBlock) {
+  auto fit = [&](int k, int& bits, size_t& lds) {
+    bits = resolve_hash_bits(k);
+    lds = resolve_lds(k, cfg->buffer_slots, bits, h->G).total;
+    if (lds > prop.sharedMemPerBlock) {
+      bits -= 1;
+      lds = resolve_lds(k, cfg->buffer_slots, bits, h->G).total;
+    }
+    return lds <= prop.sharedMemPerBlock;
+  };
+  if (!fit(cfg->top_k, h->hash_bits, h->lds_bytes)) {
     size_t need = h->lds_bytes;
     free_ctx(h);
     return fail(HS_EINVAL, "resolve needs %zu bytes of LDS, device allows %zu", need, (size_t)prop.sharedMemPerBlock);
   }
+  if (cfg->verify_rows > 1) {
+    if (!fit(h->lay.kmax, h->spec_hash_bits, h->spec_lds_bytes)) {
+      size_t need = h->spec_lds_bytes;
+      free_ctx(h);
+      return fail(HS_EINVAL, "resolving %d verification rows needs %zu bytes of LDS, device allows %zu",
+                  cfg->verify_rows, need, (size_t)prop.sharedMemPerBlock);
+    }
+    h->union_hash_bits = ilog2(int64_t(2) * h->lay.kmax);  // at most half full
+    if (h->union_hash_bits < 6) h->union_hash_bits = 6;
+    if (union_lds_bytes(h->union_hash_bits) > prop.sharedMemPerBlock) {
+      free_ctx(h);
+      return fail(HS_EINVAL, "the union of %d rows needs too much LDS", cfg->verify_rows);
+    }
+  }
   // the limit is per kernel, not per handle: allow the device maximum once
   e = set_resolve_lds_limit(prop.sharedMemPerBlock);
+  if (e == hipSuccess) e = set_union_lds_limit(prop.sharedMemPerBlock);
   if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipFuncSetAttribute(resolve)"); }
 
   // pinned host pool: one allocation per request (the driver refuses single pins near 80 GiB)
@@ -334,7 +371,54 @@ hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int
   p.rec_bytes = h->cfg.record_bytes; p.G = h->G; p.hash_bits = h->hash_bits;
   p.flags = flags | ((h->cfg.flags & HS_CFG_NEWEST_SLOT) ? kHasNewest : 0u);
   p.rtable = h->rtable; p.rt_stride = h->rt_stride; p.res_rows = h->res_rows; p.page_shift = h->page_shift;
+  p.plan_k = h->lay.kmax;
   HS_HIP(launch_resolve(p, h->lds_bytes, s));
+  return HS_OK;
+}
+
+hs_status hs_resolve_rows(hs_handle h, int32_t layer, int32_t rows, const int32_t* d_sel, const int32_t* d_ctx_len,
+                          int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs, uint32_t flags,
+                          void* stream) {
+  hs_status st;
+  if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
+  if (h->cfg.verify_rows < 2) return fail(HS_ESTATE, "hs_resolve_rows needs verify_rows > 1 in the config");
+  if (rows < 1 || rows > h->cfg.verify_rows) return fail(HS_EINVAL, "rows must be in [1, %d]", h->cfg.verify_rows);
+  if (!h->is_anchor(layer))
+    return fail(HS_ESTATE, "layer %d shares its anchor's selection: use hs_prefetch_shared", layer);
+  if (!d_sel || !d_ctx_len || !d_slots_out) return fail(HS_EINVAL, "null selection, ctx_len or output");
+  if (flags & ~(HS_RECORD_PLAN | HS_SKIP_IO)) return fail(HS_EINVAL, "unknown resolve flags");
+  hipStream_t s = (hipStream_t)stream;
+  const int a = layer / h->cfg.layer_group;
+  const int R = h->cfg.num_requests, kmax = h->lay.kmax;
+  int32_t* uni = (int32_t*)(h->ws + h->lay.uni);
+  int32_t* umap = (int32_t*)(h->ws + h->lay.umap);
+  int32_t* uout = (int32_t*)(h->ws + h->lay.uout);
+  int32_t* ucnt = (int32_t*)(h->ws + h->lay.ucnt);
+  uint32_t* uerr = (uint32_t*)(h->ws + h->lay.uerr);
+  UnionParams u{};
+  u.sel = d_sel; u.ctx_len = d_ctx_len; u.num_reqs = d_num_reqs; u.uni = uni; u.map = umap; u.cnt = ucnt;
+  u.err = uerr; u.max_positions = h->cfg.max_positions; u.R = R; u.rows = rows; u.k = h->cfg.top_k;
+  u.kb = h->cfg.top_k / h->cfg.block_tokens; u.bt_shift = ilog2(h->cfg.block_tokens); u.kmax = kmax;
+  u.hash_bits = h->union_hash_bits;
+  HS_HIP(launch_union(u, s));
+  if ((flags & HS_RECORD_PLAN) && h->plan_free_pending[a]) HS_HIP(hipStreamWaitEvent(s, h->ev_plan_free[a], 0));
+  ResolveParams p{};
+  p.sel = uni; p.ctx_len = d_ctx_len; p.out = uout; p.stats = d_stats; p.num_reqs = d_num_reqs;
+  p.kvar = ucnt; p.kerr = uerr;
+  p.ctrl = h->ctrl(a); p.slot_pos = h->slot_pos(a); p.lru = h->lru(a); p.plan = h->plan(a);
+  p.page_table = h->page_table(a); p.newest = h->newest(); p.host_base = h->host_base(); p.hot = h->hot;
+  p.host_layer_off = h->host_layer_off(layer); p.hot_req_stride = h->hot_req_stride();
+  p.hot_layer_off = h->hot_layer_off(layer); p.max_positions = h->cfg.max_positions;
+  p.R = R; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad; p.k = kmax; p.kb = kmax; p.bt_shift = 0;
+  p.rec_bytes = h->cfg.record_bytes; p.G = h->G; p.hash_bits = h->spec_hash_bits;
+  p.flags = flags | ((h->cfg.flags & HS_CFG_NEWEST_SLOT) ? kHasNewest : 0u);
+  p.rtable = h->rtable; p.rt_stride = h->rt_stride; p.res_rows = h->res_rows; p.page_shift = h->page_shift;
+  p.plan_k = kmax;
+  HS_HIP(launch_resolve(p, h->spec_lds_bytes, s));
+  ScatterParams c{};
+  c.uout = uout; c.map = umap; c.err = uerr; c.num_reqs = d_num_reqs; c.out = d_slots_out; c.R = R;
+  c.n = rows * h->cfg.top_k; c.kmax = kmax;
+  HS_HIP(launch_scatter(c, s));
   return HS_OK;
 }
 
@@ -395,7 +479,7 @@ hs_status hs_prefetch_shared(hs_handle h, int32_t anchor_layer, void* compute, v
     ReplayParams p{};
     p.plan = h->plan(a); p.ctrl = h->ctrl(a); p.host_base = h->host_base(); p.hot = h->hot;
     p.host_layer_off = h->host_layer_off(l); p.hot_req_stride = h->hot_req_stride();
-    p.hot_layer_off = h->hot_layer_off(l); p.R = h->cfg.num_requests; p.k = h->cfg.top_k;
+    p.hot_layer_off = h->hot_layer_off(l); p.R = h->cfg.num_requests; p.plan_k = h->lay.kmax;
     p.rec_bytes = h->cfg.record_bytes;
     HS_HIP(launch_replay(p, h->replay_wgs, ps));
     HS_HIP(hipEventRecord(h->ev_layer[l], ps));

@@ -30,21 +30,27 @@ __device__ __forceinline__ void store_host16(hs_u32x4 v, uint8_t* p) {
   __builtin_nontemporal_store(v, (__attribute__((address_space(1))) hs_u32x4*)p);
 }
 
-// LDS carve-up of the resolve kernel (shared by host sizing and device code).
+// LDS carve-up of the resolve kernel (shared by host sizing and device code).  The hash
+// table is dead once stage 1 has checked for duplicates, so stage 3's per-miss arrays
+// (victim, missidx, mrank) reuse its bytes (H >= 2k entries of 4 bytes >= 3 arrays of 2k).
+// The per-wave early-fetch lists hold one fetch workgroup's share of the selection.
 struct ResolveLds {
   size_t htab, selp, victim, missidx, mrank, sown, wpos, widx, wcap, scratch, total;
 };
-__host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits) {
+__host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits, int G) {
   ResolveLds L;
-  size_t o = 0;
   const size_t H = size_t(1) << hash_bits;
   const int NWv = kResolveThreads / 64;
-  L.wcap = 64 * ((size_t(k) + kResolveThreads - 1) / kResolveThreads);  // misses one wave can own
-  L.htab = o;    o = align_up(o + 4 * H, 16);
+  const int nf = G > 1 ? G - 1 : 1;
+  const size_t share = (size_t(k) + nf - 1) / nf;  // the largest fetch share
+  L.wcap = 64 * ((share + kResolveThreads - 1) / kResolveThreads);  // misses one wave can own
+  L.htab = 0;
+  L.victim = 0;
+  L.missidx = align_up(L.victim + 2 * size_t(k), 16);
+  L.mrank = align_up(L.missidx + 2 * size_t(k), 16);
+  size_t o = align_up(L.mrank + 2 * size_t(k), 16);
+  if (o < 4 * H) o = 4 * H;
   L.selp = o;    o = align_up(o + 4 * size_t(k), 16);
-  L.victim = o;  o = align_up(o + 2 * size_t(k), 16);
-  L.missidx = o; o = align_up(o + 2 * size_t(k), 16);
-  L.mrank = o;   o = align_up(o + 2 * size_t(k), 16);
   L.sown = o;    o = align_up(o + 2 * size_t(B), 16);
   L.wpos = o;    o = align_up(o + 4 * NWv * L.wcap, 16);
   L.widx = o;    o = align_up(o + 2 * NWv * L.wcap, 16);
@@ -76,6 +82,9 @@ struct ResolveParams {
   int64_t hot_req_stride;    // bytes per request in the hot buffer
   int64_t hot_layer_off;     // layer offset inside a request's hot buffer (bytes)
   int64_t max_positions;
+  const int32_t* kvar;       // [R] entries of each request's list (null: k for every request)
+  const uint32_t* kerr;      // [R] error bits found before the launch (null: none)
+  int32_t plan_k;            // plan row length (entries per request in plan)
   const int32_t* rtable;     // [R][rt_stride] resident page of each logical page (-1 none), or null
   int64_t rt_stride;         // logical pages per request
   int64_t res_rows;          // rows of the resident pool (0 without a resident tier)
@@ -95,12 +104,34 @@ struct AppendParams {
 };
 
 struct ReplayParams {
-  const int32_t* plan;       // anchor's [R][2][k]
+  const int32_t* plan;       // anchor's [R][2][plan_k]
   const uint32_t* ctrl;      // anchor's [R][4]
   const uint8_t* const* host_base;
   uint8_t* hot;
   int64_t host_layer_off, hot_req_stride, hot_layer_off;
-  int32_t R, k, rec_bytes;
+  int32_t R, plan_k, rec_bytes;
+};
+
+// Union of the verification rows of one speculative step (first reference order).
+struct UnionParams {
+  const int32_t* sel;        // [R][rows][kb]
+  const int32_t* ctx_len;    // [R]
+  const int32_t* num_reqs;   // scalar or null
+  int32_t* uni;              // [R][kmax] union, first-reference order
+  int32_t* map;              // [R][kmax] union index of each entry (row-major)
+  int32_t* cnt;              // [R] union size (0 on error)
+  uint32_t* err;             // [R] error bits
+  int64_t max_positions;
+  int32_t R, rows, k, kb, bt_shift, kmax, hash_bits;
+};
+
+struct ScatterParams {
+  const int32_t* uout;       // [R][kmax] slot of each union entry
+  const int32_t* map;        // [R][kmax]
+  const uint32_t* err;       // [R]
+  const int32_t* num_reqs;
+  int32_t* out;              // [R][rows][k]
+  int32_t R, n, kmax;        // n = rows * k entries per request
 };
 
 struct AttnParams {
@@ -140,6 +171,11 @@ struct InitParams {
 };
 
 hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s);
+hipError_t launch_union(const UnionParams& p, hipStream_t s);
+hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
+size_t union_lds_bytes(int hash_bits);
+hipError_t set_union_lds_limit(size_t lds_bytes);
+constexpr int kUnionMaxEntries = 8192;  // rows * top_k of one speculative resolve
 hipError_t set_resolve_lds_limit(size_t lds_bytes);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_backup(const AppendParams& p, hipStream_t s);

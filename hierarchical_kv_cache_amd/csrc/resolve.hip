@@ -163,12 +163,12 @@ __device__ __forceinline__ void load_run16(const int16_t* __restrict__ src, int 
 template <int E, int KE>
 __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits);
+  const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits, p.G);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
   int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] position (hash key) of each entry
-  int16_t* victim = (int16_t*)(smem + Ly.victim);    // [k] slot given to miss j
-  int16_t* missidx = (int16_t*)(smem + Ly.missidx);  // [k] list index of miss j
-  int16_t* mrank = (int16_t*)(smem + Ly.mrank);      // [k] miss rank of a list entry
+  int16_t* victim = (int16_t*)(smem + Ly.victim);    // [k] slot given to miss j     (stage 3 on,
+  int16_t* missidx = (int16_t*)(smem + Ly.missidx);  // [k] list index of miss j   in the bytes
+  int16_t* mrank = (int16_t*)(smem + Ly.mrank);      // [k] miss rank of an entry  of the hash)
   int16_t* sown = (int16_t*)(smem + Ly.sown);        // [B] -1 evictable, i >= 0 hit by entry i,
                                                      //     -2-j victim of miss j
   uint32_t* carry = (uint32_t*)(smem + Ly.scratch);  // 2 x 2 x NW scan carries
@@ -190,6 +190,20 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   const int e0 = tid * E;  // first slot / LRU position of this thread
   const int EK = (p.k + NT - 1) / NT;
   const int i0 = tid * EK;  // first selection entry of this thread
+  // entries of this request's list (a speculative union is shorter than its k-entry row)
+  const int kr = p.kvar ? min(p.kvar[r], p.k) : p.k;
+  const uint32_t pre_err = p.kerr ? p.kerr[r] : 0u;
+  if (pre_err) {  // found before the launch (the union of verification rows): nothing changes
+    if (g == 0) {
+      for (int i = tid; i < p.k; i += NT) p.out[(size_t)r * p.k + i] = -1;
+      if (tid == 0 && p.stats) {
+        hs_stats st = {0u, 0u, pre_err, 0u};
+        p.stats[r] = st;
+      }
+      if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
+    }
+    return;
+  }
 
   // ---- every global read up front -------------------------------------------------------
   // Launch counter: every launch that changes the metadata adds G per request, one per
@@ -209,7 +223,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
-    raw[j] = (j < EK && i < p.k) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
+    raw[j] = (j < EK && i < kr) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
   }
   // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
   // map, so it names the slot of a hit) and, with a resident tier, its resident page.
@@ -221,7 +235,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     const int i = i0 + j;
     const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
                                      : (int64_t)raw[j];
-    const bool ok = j < EK && i < p.k && pos64 >= 0 && pos64 < ctx;
+    const bool ok = j < EK && i < kr && pos64 >= 0 && pos64 < ctx;
     ptv[j] = ok ? ptr[pos64] : -1;
     rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
@@ -232,8 +246,8 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   const bool fetcher = io && (p.G == 1 || g > 0);
   const int nf = p.G > 1 ? p.G - 1 : 1;
   const int gf = p.G > 1 ? g - 1 : 0;
-  const int f_lo = (int)((int64_t)p.k * gf / nf);
-  const int f_n = (int)((int64_t)p.k * (gf + 1) / nf) - f_lo;
+  const int f_lo = (int)((int64_t)kr * gf / nf);
+  const int f_n = (int)((int64_t)kr * (gf + 1) / nf) - f_lo;
   const int wid = tid >> 6, lane = tid & 63;
   int32_t fraw[KE];
 #pragma unroll
@@ -298,20 +312,20 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   if (tiered) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) nres += (int)rcnt[w];
-    if (nres == p.k) {
+    if (nres == kr) {
       if (g == 0) {
         const int64_t pmask = ((int64_t)1 << p.page_shift) - 1;
 #pragma unroll
         for (int j = 0; j < KE; ++j) {
           const int i = i0 + j;
-          if (j < EK && i < p.k) {
+          if (j < EK && i < kr) {
             const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
                                              : (int64_t)raw[j];
             p.out[(size_t)r * p.k + i] = p.B + 1 + (int32_t)(((int64_t)rpg[j] << p.page_shift) + (pos64 & pmask));
           }
         }
         if (tid == 0 && p.stats) {
-          hs_stats st = {0u, 0u, 0u, (uint32_t)p.k};
+          hs_stats st = {0u, 0u, 0u, (uint32_t)kr};
           p.stats[r] = st;
         }
         if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
@@ -344,7 +358,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     key[j] = -1;
     hh[j] = 0;
     cls[j] = -2;
-    if (j >= EK || i >= p.k) continue;
+    if (j >= EK || i >= kr) continue;
     const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
                                      : (int64_t)raw[j];
     if (pos64 < 0 || pos64 >= ctx) {
@@ -538,8 +552,8 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     block_ranks2<E>(vb, hb, carry + 2 * NW, rv, rh, tv, th);
     int32_t* pt = p.page_table + (size_t)r * p.max_positions;
     int32_t* outr = p.out + (size_t)r * p.k;
-    int32_t* plan_pos = p.plan + (size_t)r * 2 * p.k;
-    int32_t* plan_slot = plan_pos + p.k;
+    int32_t* plan_pos = p.plan + (size_t)r * 2 * p.plan_k;
+    int32_t* plan_slot = plan_pos + p.plan_k;
 
     // ---- stage 5: publish (every value is already on chip) ----
     int32_t spn[E];
@@ -587,7 +601,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       if (cls[j] >= 0) outr[i0 + j] = cls[j];
     if (tid == 0) {
       if (p.stats) {
-        hs_stats st = {(uint32_t)(p.k - m - nres), (uint32_t)m, (uint32_t)sh[3], (uint32_t)nres};
+        hs_stats st = {(uint32_t)(kr - m - nres), (uint32_t)m, (uint32_t)sh[3], (uint32_t)nres};
         p.stats[r] = st;
       }
       if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;
@@ -632,6 +646,120 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
           *((u32x4*)(dbase + (size_t)victim[mrank[widx[ll[u]]]] * (size_t)p.rec_bytes) + cc[u]) = v[u];
     }
   }
+}
+
+// Union of the verification rows of one speculative step ("HiSparse 深度解析" §6.5
+// comparison table; "HiSparse local KV offload architecture" (docs.vllm.ai),
+// speculative decoding): rows that select the same position share one slot, so the
+// rows are resolved as one list, their union in first-reference order (row by row,
+// list order within a row).  One workgroup per request:
+//   - every entry finds or inserts its position in an LDS hash (compare-and-swap
+//     linear probing; one bucket per distinct position);
+//   - row by row, each entry ORs its row's bit into its bucket's mask: a bit already
+//     set is a duplicate inside the row, a lower bit means an earlier row selected the
+//     position first;
+//   - the first references are ranked in list order (ballot + mbcnt scan); the rank is
+//     the position's index in the union, stored in the bucket for the other entries.
+constexpr int EU = kUnionMaxEntries / NT;  // entries per thread
+
+__global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int H = 1 << p.hash_bits;
+  const uint32_t hmask = (uint32_t)H - 1;
+  int32_t* key = (int32_t*)smem;          // [H] position, -1 empty
+  uint32_t* meta = (uint32_t*)(key + H);  // [H] row mask, then union index
+  uint32_t* carry = meta + H;             // scan carries
+  int* sh = (int*)(carry + 4 * NW);       // [0] error bits
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (p.num_reqs && r >= *p.num_reqs) return;
+  const int n = p.rows * p.k;
+  const int i0 = tid * EU;
+  const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
+  const int32_t* selr = p.sel + (size_t)r * p.rows * p.kb;
+  uint32_t err = 0;
+  int32_t pos[EU];
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
+    const int f = i0 + j;
+    pos[j] = -1;
+    if (f >= n) continue;
+    const int q = f / p.k, i = f - q * p.k;
+    const int32_t raw = selr[(size_t)q * p.kb + (p.bt_shift ? (i >> p.bt_shift) : i)];
+    const int64_t pos64 = p.bt_shift ? ((int64_t)raw << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)raw;
+    if (pos64 < 0 || pos64 >= ctx) err |= HS_ERR_RANGE;
+    else pos[j] = (int32_t)pos64;
+  }
+  {
+    u32x4* k4 = (u32x4*)key;
+    u32x4* m4 = (u32x4*)meta;
+    const u32x4 e4 = {~0u, ~0u, ~0u, ~0u};
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    for (int h = tid; h < H / 4; h += NT) { k4[h] = e4; m4[h] = z4; }
+  }
+  if (tid == 0) sh[0] = 0;
+  __syncthreads();
+  int32_t bkt[EU];
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
+    bkt[j] = -1;
+    if (pos[j] < 0) continue;
+    uint32_t h = hash_pos(pos[j], p.hash_bits);
+    for (int probe = 0; probe < H; ++probe) {  // the table is at most half full: this ends
+      const int32_t prev = atomicCAS(&key[h], -1, pos[j]);
+      if (prev == -1 || prev == pos[j]) {
+        bkt[j] = (int32_t)h;
+        break;
+      }
+      h = (h + 1) & hmask;
+    }
+  }
+  __syncthreads();
+  uint32_t first = 0;
+  for (int q = 0; q < p.rows; ++q) {
+#pragma unroll
+    for (int j = 0; j < EU; ++j) {
+      const int f = i0 + j;
+      if (bkt[j] < 0 || f / p.k != q) continue;
+      const uint32_t old = atomicOr(&meta[bkt[j]], 1u << q);
+      if (old & (1u << q)) err |= HS_ERR_DUP;
+      else if ((old & ((1u << q) - 1u)) == 0) first |= 1u << j;
+    }
+    __syncthreads();
+  }
+  if (err) atomicOr((unsigned*)&sh[0], err);
+  int ru, rz, nu, tz;
+  block_ranks2<EU>(first, 0u, carry, ru, rz, nu, tz);  // (its barrier also publishes sh[0])
+  int32_t* unir = p.uni + (size_t)r * p.kmax;
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
+    if ((first >> j) & 1u) {
+      meta[bkt[j]] = (uint32_t)ru;
+      unir[ru] = pos[j];
+      ++ru;
+    }
+  }
+  __syncthreads();
+  const uint32_t e = (uint32_t)sh[0];
+  int32_t* mapr = p.map + (size_t)r * p.kmax;
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
+    const int f = i0 + j;
+    if (f < n) mapr[f] = bkt[j] >= 0 ? (int32_t)meta[bkt[j]] : -1;
+  }
+  if (tid == 0) {
+    p.cnt[r] = e ? 0 : nu;
+    p.err[r] = e;
+  }
+}
+
+// Slots of the union back to every (row, entry): out[r][f] = union slot of entry f.
+__global__ void __launch_bounds__(256) scatter_kernel(ScatterParams p) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)p.R * p.n) return;
+  const int r = (int)(t / p.n), f = (int)(t - (int64_t)r * p.n);
+  if (p.num_reqs && r >= *p.num_reqs) return;
+  const int32_t u = p.map[(size_t)r * p.kmax + f];
+  p.out[t] = (p.err[r] || u < 0) ? -1 : p.uout[(size_t)r * p.kmax + u];
 }
 
 template <int E, int KE>
@@ -685,6 +813,23 @@ hipError_t set_resolve_lds_limit(size_t lds_bytes) {
   if ((e = set_limit_ke<4>(v)) != hipSuccess) return e;
   if ((e = set_limit_ke<8>(v)) != hipSuccess) return e;
   return set_limit_ke<16>(v);
+}
+
+size_t union_lds_bytes(int hash_bits) { return (size_t(8) << hash_bits) + 4 * (4 * NW + 8); }
+
+hipError_t set_union_lds_limit(size_t lds_bytes) {
+  return hipFuncSetAttribute((const void*)union_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+}
+
+hipError_t launch_union(const UnionParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(union_kernel, dim3(p.R), dim3(NT), union_lds_bytes(p.hash_bits), s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.R * p.n;
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s) {

@@ -81,6 +81,9 @@ typedef struct {
                               slot layout ([GC] §3.6 IndexCache / IndexShare) */
   int32_t wgs_per_request; /* workgroups per request in hs_resolve; 0 chooses */
   uint32_t flags;          /* HS_CFG_* */
+  int32_t verify_rows;     /* 0 or 1: no speculative decoding.  n > 1: hs_resolve_rows accepts up to n
+                              verification rows per call ([GC] §6.5, [VD]); needs
+                              n * top_k <= 8192 and buffer_slots >= n * top_k */
 } hs_config;
 
 /* Per-request result of one hs_resolve call (device memory, overwritten per call). */
@@ -144,6 +147,25 @@ void* hs_host_pool(hs_handle h, int32_t request);
 hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
                      int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs,
                      uint32_t flags, void* stream);
+
+/*
+ * RESOLVE of the verification rows of one speculative decode step ([GC] §6.5
+ * comparison table: one call resolves the union of all verification rows' top-k,
+ * rows selecting the same position share its slot, no row evicts a slot another
+ * row reads, misses are assigned in (row, entry) first-reference order; [VD]
+ * "Speculative decoding").  The union is resolved exactly as hs_resolve resolves
+ * one list; hits, misses and resident counts in d_stats are those of the union.
+ *   rows         1 .. cfg.verify_rows
+ *   d_sel        device [R][rows][top_k / block_tokens] int32, distinct within each row
+ *   d_slots_out  device [R][rows][top_k] int32, the slot of every (row, entry)
+ *   other arguments as hs_resolve.  A duplicate inside a row sets HS_ERR_DUP (nothing
+ *   changes); repeats across rows are the point and are not errors.
+ * Three kernel launches on `stream` (union, RESOLVE of the union, scatter); the union
+ * scratch is per handle, so calls on one handle must be ordered on one stream.
+ */
+hs_status hs_resolve_rows(hs_handle h, int32_t layer, int32_t rows, const int32_t* d_sel,
+                          const int32_t* d_ctx_len, int32_t* d_slots_out, hs_stats* d_stats,
+                          const int32_t* d_num_reqs, uint32_t flags, void* stream);
 
 /*
  * Binds a resident tier in front of the hot slots ([GC] §6.5; [VD] "Hot lookup
@@ -220,8 +242,8 @@ hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32
 /* Device address of an anchor layer's page table, int32 [R][max_positions], -1 = host only. */
 const int32_t* hs_page_table(hs_handle h, int32_t layer);
 
-/* Device address of an anchor layer's miss plan: int32 [R][2][top_k] (positions, then slots,
- * in miss order) and uint32 counts (stride 4 per request, count first). */
+/* Device address of an anchor layer's miss plan: int32 [R][2][P] (positions, then slots, in miss
+ * order), P = top_k * max(1, verify_rows), and uint32 counts (stride 4 per request, count first). */
 hs_status hs_plan(hs_handle h, int32_t layer, const int32_t** d_plan, const uint32_t** d_counts);
 
 /* Request release ([GC] §5.4): every layer of request r back to the admission state (all

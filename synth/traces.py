@@ -89,3 +89,39 @@ def trace_stats(trace: np.ndarray) -> dict:
     reuse = [np.intersect1d(trace[t], trace[t - 1]).size / trace.shape[1]
              for t in range(1, trace.shape[0])]
     return {"reuse": float(np.mean(reuse))}
+
+
+def verify_rows(w, r: int, l: int, steps: int, rows: int, keep: float = 0.9) -> np.ndarray:
+    """int32 [steps][rows][kb] selections of the verification rows of speculative steps.
+
+    Row 0 of step t is ``selection_trace``'s selection; row q > 0 keeps each entry of row
+    q-1 with probability ``keep`` (in order), then draws fresh entries as the trace model
+    does (uniform over the context with probability ``uniform_frac``, else recency-Zipf),
+    then is shuffled.  Generator: PCG64(SeedSequence([cfg_id, r, l, 0x5BEC])).
+    """
+    base = selection_trace(w, r, l, steps)
+    kb = base.shape[1]
+    bt = w.block_tokens
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.cfg_id, r, l, 0x5BEC])))
+    out = np.empty((steps, rows, kb), dtype=np.int32)
+    for t in range(steps):
+        n_units = (w.ctx + (t + 1 if w.append else 0)) // bt
+        out[t, 0] = base[t]
+        for q in range(1, rows):
+            prev = out[t, q - 1].astype(np.int64)
+            kept = prev[rng.random(kb) < keep]
+            member = set(kept.tolist())
+            fresh = []
+            while len(kept) + len(fresh) < kb:
+                if rng.random() < w.uniform_frac:
+                    c = int(rng.integers(0, n_units))
+                else:
+                    d = int(rng.zipf(w.zipf_a)) - 1
+                    if d >= n_units:
+                        continue
+                    c = n_units - 1 - d
+                if c not in member:
+                    member.add(c)
+                    fresh.append(c)
+            out[t, q] = rng.permutation(np.concatenate([kept, np.array(fresh, np.int64)]))
+    return out

@@ -27,7 +27,7 @@ class Pair:
 
     def __init__(self, w: synth.Workload, steps: int | None = None, wgs: int = 0, all_hit=False,
                  oracle_host_copy: bool | None = None, compare_hot=True, resident: ResidentSpec | None = None,
-                 fp8: bool = False):
+                 fp8: bool = False, rows: int = 1):
         self.w = w
         self.steps = w.steps if steps is None else steps
         self.lmax = w.max_positions(self.steps)
@@ -37,7 +37,7 @@ class Pair:
         self.compare_hot = compare_hot
         cfg = hk.make_config(w.R, w.L, self.lmax, w.k, w.B, record_bytes=self.rec,
                              block_tokens=w.block_tokens, layer_group=w.group, wgs_per_request=wgs,
-                             newest_slot=w.append, fp8=fp8)
+                             newest_slot=w.append, fp8=fp8, verify_rows=rows if rows > 1 else 0)
         self.gpu = hk.HiSparse(cfg)
         self.h = self.gpu.h
         self.dev = torch.device("cuda")
@@ -63,12 +63,20 @@ class Pair:
                        for r in range(w.R) for l in self.anchors}
         self.ohot_shared = {(r, l): np.zeros((w.B + 1, self.rec), np.uint8)
                             for r in range(w.R) for l in range(w.L) if l % w.group}
-        # selection traces, resident on the device: [steps][anchors][R][kb]
-        tr = np.stack([np.stack([synth.selection_trace(w, r, l, self.steps, all_hit=all_hit)
-                                 for r in range(w.R)], axis=1) for l in self.anchors], axis=1)
-        self.trace = tr  # numpy [steps][A][R][kb]
+        # selection traces, resident on the device: [steps][anchors][R][kb], or with
+        # speculative verification rows [steps][anchors][R][rows][kb]
+        self.rows = rows
+        if rows > 1:
+            from synth.traces import verify_rows
+            tr = np.stack([np.stack([verify_rows(w, r, l, self.steps, rows) for r in range(w.R)], axis=1)
+                           for l in self.anchors], axis=1)
+        else:
+            tr = np.stack([np.stack([synth.selection_trace(w, r, l, self.steps, all_hit=all_hit)
+                                     for r in range(w.R)], axis=1) for l in self.anchors], axis=1)
+        self.trace = tr
         self.d_trace = torch.from_numpy(tr).to(self.dev)
-        self.d_out = torch.empty((len(self.anchors), w.R, w.k), dtype=torch.int32, device=self.dev)
+        out_shape = (len(self.anchors), w.R, rows, w.k) if rows > 1 else (len(self.anchors), w.R, w.k)
+        self.d_out = torch.empty(out_shape, dtype=torch.int32, device=self.dev)
         self.d_stats = torch.zeros((w.R, 4), dtype=torch.int32, device=self.dev)
         self.t = 0
         self.newest = None
@@ -131,15 +139,30 @@ class Pair:
             d_nr = torch.tensor([num_reqs], dtype=torch.int32, device=self.dev)
         for ai, l in enumerate(self.anchors):
             d_sel = self.d_trace[t, ai]
-            hk.hs_resolve(self.h, l, d_sel.data_ptr(), d_ctx.data_ptr(), self.d_out[ai].data_ptr(),
-                          self.d_stats.data_ptr(), d_nr.data_ptr() if d_nr is not None else 0,
-                          flags | (hk.HS_RECORD_PLAN if w.group > 1 else 0), self.compute.cuda_stream)
+            fl = flags | (hk.HS_RECORD_PLAN if w.group > 1 else 0)
+            if self.rows > 1:
+                hk.hs_resolve_rows(self.h, l, self.rows, d_sel.data_ptr(), d_ctx.data_ptr(), self.d_out[ai].data_ptr(),
+                                   self.d_stats.data_ptr(), d_nr.data_ptr() if d_nr is not None else 0, fl,
+                                   self.compute.cuda_stream)
+            else:
+                hk.hs_resolve(self.h, l, d_sel.data_ptr(), d_ctx.data_ptr(), self.d_out[ai].data_ptr(),
+                              self.d_stats.data_ptr(), d_nr.data_ptr() if d_nr is not None else 0, fl,
+                              self.compute.cuda_stream)
             if w.group > 1:
                 hk.hs_prefetch_shared(self.h, l, self.compute.cuda_stream, self.side.cuda_stream)
             stats = self.d_stats.cpu().numpy().copy() if check else None
             nr = w.R if num_reqs is None else num_reqs
 
             def one(r, l=l, ai=ai):
+                if self.rows > 1:
+                    sel = np.stack([expand(row, w.block_tokens) for row in self.trace[t, ai, r]])
+                    rt = tab[r] if self.resident is not None else None
+                    o, hh, mm, rr, pp, ps, nu = self.caches[(r, l)].resolve_rows(
+                        sel, ctx, self.ohost[r][l], rt, getattr(self, "page_shift", 0), getattr(self, "res_rows", 0))
+                    res = (o, hh, mm, pp, ps, rr)
+                    for ls in range(l + 1, min(l + w.group, w.L)):
+                        oracle.replay(res[3], res[4], self.ohost[r][ls], self.ohot_shared[(r, ls)], self.rec)
+                    return res
                 pos = expand(self.trace[t, ai, r], w.block_tokens)
                 if self.resident is not None:
                     o, hh, mm, rr, pp, ps = self.caches[(r, l)].resolve_tiered(
