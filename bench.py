@@ -218,6 +218,7 @@ def main():
         detail.update(measure_all_hit(torch, hk, synth, dev))
         detail.update(measure_resident(torch, hk, synth, w, dev, trace, lmax))
         detail.update(measure_fp8(torch, hk, synth, dev))
+        detail.update(measure_rows(torch, hk, synth, dev))
         detail["launch_latency_us"] = measure_empty(torch, hk)
         detail["hbm_copy_GBps"] = measure_hbm(torch, hk, dev)
         detail["link_ceiling_GBps"] = link["ceiling_GBps"]
@@ -473,6 +474,48 @@ def measure_fp8(torch, hk, synth, dev, steps=40, warmup=8):
     cache.close()
     return {"fp8_long_selections_per_s": steps * L * R * k / el, "fp8_long_ms_per_step": el / steps * 1e3,
             "fp8_record_bytes": rec}
+
+
+def measure_rows(torch, hk, synth, dev, rows=4, steps=24):
+    """Speculative decoding with three draft tokens: each call resolves 4 verification rows of
+    k = 2048 (their union, first reference order) into B = 5 k slots, long-request shape
+    (1 request, 8 layers, write-through).  Median µs per call (union + RESOLVE + scatter)."""
+    from synth.traces import verify_rows
+    w = synth.WORKLOADS["long"].scaled(B=5 * 2048)
+    R, L, k, B = w.R, w.L, w.k, w.B
+    lmax = w.max_positions(steps)
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, newest_slot=True, verify_rows=rows))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    tr = np.stack([np.stack([verify_rows(w, r, l, steps, rows) for r in range(R)], axis=1) for l in range(L)], axis=1)
+    d_tr = torch.from_numpy(tr).to(dev)  # [steps][L][R][rows][k]
+    pos = w.ctx + np.arange(steps)
+    d_new = torch.from_numpy(np.stack([synth.records_at(R, L, [p] * R) for p in pos])).to(dev)
+    d_pos = torch.from_numpy(np.repeat(pos[:, None], R, axis=1).astype(np.int32)).to(dev)
+    d_ctx = torch.from_numpy((pos[:, None] + 1).repeat(R, axis=1).astype(np.int32)).to(dev)
+    d_out = torch.empty((R, rows, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    bs = torch.cuda.Stream()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+           for _ in range(steps)]
+    for t in range(steps):
+        hk.hs_append(cache.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), s.cuda_stream, bs.cuda_stream)
+        for l in range(L):
+            evs[t][l][0].record(s)
+            hk.hs_resolve_rows(cache.h, l, rows, d_tr[t, l].data_ptr(), d_ctx[t].data_ptr(), d_out.data_ptr(),
+                               d_stats[t, l].data_ptr(), 0, 0, s.cuda_stream)
+            evs[t][l][1].record(s)
+    torch.cuda.synchronize()
+    bs.synchronize()
+    us = np.array([[evs[t][l][0].elapsed_time(evs[t][l][1]) * 1e3 for l in range(L)] for t in range(steps)])
+    st = d_stats.cpu().numpy()
+    assert not st[..., 2].any()
+    union = (st[4:, ..., 0] + st[4:, ..., 1]).mean()
+    cache.close()
+    return {"spec4_resolve_rows_us_per_layer": float(np.median(us[4:])),
+            "spec4_union_entries": float(union),
+            "spec4_miss_rate_of_union": float(st[4:, ..., 1].sum() / max(1, (st[4:, ..., 0] + st[4:, ..., 1]).sum()))}
 
 
 def measure_empty(torch, hk):
