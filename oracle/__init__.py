@@ -68,6 +68,8 @@ def _load():
     lib.hso_resolve_tiered.restype = i32
     lib.hso_resolve_rows.argtypes = [vp, vp, i32, i32, i64, vp, i64, i32, i64, vp, vp, vp, vp, vp]
     lib.hso_resolve_rows.restype = i32
+    lib.hso_admit_short.argtypes = [vp, i64, vp]
+    lib.hso_admit_short.restype = i32
     lib.hso_append.argtypes = [vp, i64, vp, vp]
     lib.hso_append.restype = i32
     lib.hso_replay.argtypes = [vp, vp, i32, vp, vp, i32]
@@ -171,6 +173,13 @@ class Cache:
             raise OracleError(err)
         m = int(counts[1])
         return out, int(counts[0]), m, int(counts[2]), ppos[:m].copy(), pslot[:m].copy(), int(counts[3])
+
+    def admit_short(self, ctx_len: int, host):
+        """Admission of a short request (``hso_admit_short``): positions 0 .. ctx_len-1 in
+        slots 0 .. ctx_len-1, short-sequence fast path on while the context fits B."""
+        err = self._lib.hso_admit_short(self._h, ctx_len, _addr(host))
+        if err:
+            raise OracleError(err)
 
     def append(self, pos: int, record: np.ndarray, host=None):
         rec = np.ascontiguousarray(record, dtype=np.uint8)

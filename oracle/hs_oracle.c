@@ -47,6 +47,7 @@ typedef struct {
   int32_t rec_bytes;
   int64_t max_positions;
   int32_t newest_slot; /* 1: slot index B holds the newest token (outside the LRU) */
+  int32_t short_mode;  /* 1: admitted short: position p sits in slot p while the context fits B */
   int64_t step;        /* resolves completed */
   int64_t newest_pos;  /* -1: no newest token yet */
   int32_t* slot_pos;   /* [B]: position held by the slot, -1 when empty */
@@ -97,6 +98,46 @@ static void sort_evictable(int32_t* ev, int32_t n, const int64_t* stamp) {
 }
 
 /*
+ * Short-sequence fast path ("HiSparse 深度解析" (gentlecold.top) §5.4 and §5.5):
+ * while a request admitted short has at most B tokens, every token sits in the
+ * slot of its position, so a selection resolves to its own positions with no
+ * host IO and no change to the LRU (the pages' kernel returns at once; it does
+ * not check for duplicates).  Returns 1 when it applied (0 or an error in *err).
+ */
+static int short_fast(hso_cache* c, const int32_t* sel, int32_t k, int64_t ctx_len, int32_t* out,
+                      int32_t* counts, int32_t* err) {
+  if (!c->short_mode || ctx_len > c->B) return 0;
+  *err = 0;
+  for (int32_t i = 0; i < k; ++i)
+    if (sel[i] < 0 || sel[i] >= ctx_len) *err |= HSO_ERR_RANGE;
+  if (*err) return 1;
+  for (int32_t i = 0; i < k; ++i) out[i] = sel[i];
+  counts[0] = k;
+  counts[1] = 0;
+  return 1;
+}
+
+/*
+ * Admission of a short request (gentlecold.top §5.3, §5.4): its first ctx_len
+ * <= B tokens are staged into slots 0 .. ctx_len-1 in order (from host), the
+ * slot map and page table record them (stamps stay 0: never used), and the
+ * cache enters short mode.  Needs the admission state (every slot empty).
+ */
+int32_t hso_admit_short(hso_cache* c, int64_t ctx_len, const uint8_t* host) {
+  if (ctx_len < 0 || ctx_len > c->B || ctx_len > c->max_positions) return HSO_ERR_RANGE;
+  for (int32_t s = 0; s < c->B; ++s)
+    if (c->slot_pos[s] >= 0) return HSO_ERR_CAPACITY;
+  const size_t rec = (size_t)c->rec_bytes;
+  for (int64_t p = 0; p < ctx_len; ++p) {
+    c->slot_pos[p] = (int32_t)p;
+    c->page_table[p] = (int32_t)p;
+    memcpy(c->hot + (size_t)p * rec, host + (size_t)p * rec, rec);
+  }
+  c->short_mode = 1;
+  return 0;
+}
+
+/*
  * One RESOLVE of k selected positions (already expanded from blocks).
  *   host     : [max_positions][rec_bytes] records of this (request, layer)
  *   out      : [k] physical slot per selected entry, aligned with sel
@@ -111,6 +152,7 @@ int32_t hso_resolve(hso_cache* c, const int32_t* sel, int32_t k, int64_t ctx_len
   const int32_t B = c->B;
   const size_t rec = (size_t)c->rec_bytes;
   int32_t err = 0;
+  if (short_fast(c, sel, k, ctx_len, out, counts, &err)) return err;
 
   /* 1. validate: every position in the context, no position twice */
   for (int32_t i = 0; i < k; ++i) {
@@ -212,6 +254,13 @@ int32_t hso_resolve_tiered(hso_cache* c, const int32_t* sel, int32_t k, int64_t 
                            int32_t* counts) {
   const int32_t B = c->B;
   int32_t err = 0, n_res = 0;
+  {
+    int32_t c2[2];
+    if (short_fast(c, sel, k, ctx_len, out, c2, &err)) {
+      if (!err) { counts[0] = c2[0]; counts[1] = 0; counts[2] = 0; }
+      return err;
+    }
+  }
   int32_t* rest = (int32_t*)calloc((size_t)(k > 0 ? k : 1), sizeof(int32_t));   /* non-resident list */
   int32_t* where = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));  /* its list indices */
   int32_t* rout = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
@@ -335,6 +384,11 @@ int32_t hso_resolve_rows(hso_cache* c, const int32_t* sel, int32_t Q, int32_t k,
 int32_t hso_append(hso_cache* c, int64_t pos, const uint8_t* record, uint8_t* host) {
   if (!c->newest_slot || pos < 0 || pos >= c->max_positions) return HSO_ERR_RANGE;
   memcpy(c->hot + (size_t)c->B * (size_t)c->rec_bytes, record, (size_t)c->rec_bytes);
+  if (c->short_mode && pos < c->B) {  /* a short request keeps its tokens in order */
+    memcpy(c->hot + (size_t)pos * (size_t)c->rec_bytes, record, (size_t)c->rec_bytes);
+    c->slot_pos[pos] = (int32_t)pos;
+    c->page_table[pos] = (int32_t)pos;
+  }
   if (host) memcpy(host + (size_t)pos * (size_t)c->rec_bytes, record, (size_t)c->rec_bytes);
   c->newest_pos = pos;
   return 0;
