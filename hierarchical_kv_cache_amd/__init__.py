@@ -52,7 +52,8 @@ EXPORTS = (
     "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_resolve_rows", "hs_bind_resident",
     "hs_append",
     "hs_prefetch_shared",
-    "hs_wait_layer", "hs_sparse_attn", "hs_export_state", "hs_page_table", "hs_plan", "hs_reset_request",
+    "hs_wait_layer", "hs_sparse_attn", "hs_export_state", "hs_page_table", "hs_plan", "hs_admit_short",
+    "hs_reset_request",
     "hs_destroy", "hs_last_error", "hs_resolve_wgs", "hs_probe_host_read", "hs_probe_copy",
     "hs_probe_empty",
 )
@@ -85,6 +86,7 @@ def _load():
         "hs_export_state": (i32, [vp, i32, vp, vp, vp, vp]),
         "hs_page_table": (vp, [vp, i32]),
         "hs_plan": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp)]),
+        "hs_admit_short": (i32, [vp, i32, i32, vp]),
         "hs_reset_request": (i32, [vp, i32, vp]),
         "hs_destroy": (i32, [vp]),
         "hs_last_error": (ctypes.c_char_p, []),
@@ -173,6 +175,10 @@ def hs_plan(h, layer):
     plan, counts = ctypes.c_void_p(), ctypes.c_void_p()
     _check(_lib.hs_plan(h, layer, ctypes.byref(plan), ctypes.byref(counts)))
     return plan.value, counts.value
+
+
+def hs_admit_short(h, request, ctx_len, stream):
+    _check(_lib.hs_admit_short(h, request, ctx_len, stream or None))
 
 
 def hs_reset_request(h, request, stream):

@@ -34,8 +34,22 @@ __global__ void __launch_bounds__(kCopyThreads) append_kernel(AppendParams p) {
     const int l = rest / C, c = rest - l * C;
     const u32x4* src = (const u32x4*)(p.new_kv + ((size_t)r * p.L + l) * p.rec_bytes) + c;
     u32x4* dst = (u32x4*)(p.hot + (((size_t)r * p.L + l) * (p.B + 1) + p.B) * p.rec_bytes) + c;
-    *dst = *src;
-    if (rest == 0) p.newest[r] = pos;
+    const u32x4 v = *src;
+    *dst = v;
+    // a short request keeps its tokens in slot order while they fit ("HiSparse 深度解析" §5.4)
+    const bool in_order = p.ctrl[r * 4 + 3] != 0 && pos < p.B;
+    if (in_order) *((u32x4*)(p.hot + (((size_t)r * p.L + l) * (p.B + 1) + pos) * p.rec_bytes) + c) = v;
+    if (rest == 0) {
+      p.newest[r] = pos;
+      if (in_order) {
+        for (int a = 0; a < p.A; ++a) {  // every anchor's slot map and page table
+          const uint32_t* ca = p.ctrl + (size_t)a * p.R * 4;
+          const int cur = (int)((*(const uint64_t*)&ca[r * 4] / (uint64_t)p.G) & 1u);
+          p.slot_pos[((size_t)a * p.R + r) * 2 * p.B + (size_t)cur * p.B + pos] = pos;
+          p.page_table[((size_t)a * p.R + r) * (size_t)p.max_positions + pos] = pos;
+        }
+      }
+    }
   }
 }
 
@@ -125,6 +139,36 @@ __global__ void __launch_bounds__(kCopyThreads) init_kernel(InitParams p) {
   }
 }
 
+// Admission of a short request ("HiSparse 深度解析" (gentlecold.top) §5.3, §5.4): its first
+// ctx tokens of every layer are staged from host into slots 0 .. ctx-1 in order, every
+// anchor's slot map and page table record them, and the request is marked short.
+// Flattened over (layer, position, 16-byte chunk); the metadata by the first ctx threads.
+__global__ void __launch_bounds__(kCopyThreads) admit_kernel(AdmitParams p) {
+  const int r = p.request;
+  const int C = p.rec_bytes >> 4;
+  const int64_t total = (int64_t)p.L * p.ctx * C;
+  const int64_t nt = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t f = t0; f < total; f += nt) {
+    const int64_t lp = f / C;
+    const int c = (int)(f - lp * C);
+    const int l = (int)(lp / p.ctx), pos = (int)(lp - (int64_t)l * p.ctx);
+    const uint8_t* src = p.host_base[r] + ((size_t)l * p.max_positions + pos) * p.rec_bytes + 16 * (size_t)c;
+    uint8_t* dst = p.hot + (size_t)r * p.hot_req_stride + ((size_t)l * (p.B + 1) + pos) * p.rec_bytes + 16 * (size_t)c;
+    *(u32x4*)dst = load_host16(src);
+  }
+  for (int64_t s = t0; s < p.ctx; s += nt) {
+    for (int a = 0; a < p.A; ++a) {
+      const uint32_t* ca = p.ctrl + (size_t)a * p.R * 4;
+      const int cur = (int)((*(const uint64_t*)&ca[r * 4] / (uint64_t)p.G) & 1u);
+      p.slot_pos[((size_t)a * p.R + r) * 2 * p.B + (size_t)cur * p.B + s] = (int32_t)s;
+      p.page_table[((size_t)a * p.R + r) * (size_t)p.max_positions + s] = (int32_t)s;
+    }
+  }
+  if (t0 == 0)
+    for (int a = 0; a < p.A; ++a) p.ctrl[((size_t)a * p.R + r) * 4 + 3] = 1u;
+}
+
 __global__ void __launch_bounds__(kCopyThreads) export_kernel(ExportParams p) {
   const int r = blockIdx.y;
   const int cur = (int)((*(const uint64_t*)&p.ctrl[r * 4] / (uint64_t)p.G) & 1u);
@@ -193,6 +237,13 @@ hipError_t launch_init(const InitParams& p, hipStream_t s) {
   const int bx = grid_for((size_t)(p.max_positions > p.B ? p.max_positions : p.B), kCopyThreads * 8, 256);
   dim3 grid(bx, p.A, p.request >= 0 ? 1 : p.R);
   hipLaunchKernelGGL(init_kernel, grid, dim3(kCopyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_admit(const AdmitParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.L * p.ctx * (p.rec_bytes >> 4);
+  const int bx = grid_for((size_t)(n > p.ctx ? n : p.ctx), kCopyThreads * 4, 1024);
+  hipLaunchKernelGGL(admit_kernel, dim3(bx), dim3(kCopyThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -453,6 +453,8 @@ hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos,
   p.new_kv = (const uint8_t*)d_new_kv; p.new_pos = d_new_pos; p.newest = h->newest(); p.hot = h->hot;
   p.host_base = h->host_base(); p.max_positions = h->cfg.max_positions; p.R = h->cfg.num_requests;
   p.L = h->cfg.num_layers; p.B = h->cfg.buffer_slots; p.rec_bytes = h->cfg.record_bytes;
+  p.ctrl = h->ctrl(0); p.slot_pos = h->slot_pos(0); p.page_table = h->page_table(0); p.A = h->lay.A;
+  p.G = h->G; p.group = h->cfg.layer_group;
   // slot B may only be overwritten once the previous write-through has read it (and then every
   // later fetch of the previous newest position finds its bytes on the host)
   HS_HIP(hipStreamWaitEvent(cs, h->ev_backup_done, 0));
@@ -551,6 +553,21 @@ hs_status hs_plan(hs_handle h, int32_t layer, const int32_t** d_plan, const uint
   const int a = layer / h->cfg.layer_group;
   if (d_plan) *d_plan = h->plan(a);
   if (d_counts) *d_counts = h->ctrl(a) + 2;
+  return HS_OK;
+}
+
+hs_status hs_admit_short(hs_handle h, int32_t request, int32_t ctx_len, void* stream) {
+  hs_status st;
+  if ((st = check_handle(h))) return st;
+  if (request < 0 || request >= h->cfg.num_requests) return fail(HS_EINVAL, "request out of range");
+  if (ctx_len < 0 || ctx_len > h->cfg.buffer_slots || ctx_len > h->cfg.max_positions)
+    return fail(HS_EINVAL, "a short request holds at most buffer_slots (and max_positions) tokens");
+  AdmitParams p{};
+  p.host_base = h->host_base(); p.hot = h->hot; p.ctrl = h->ctrl(0); p.slot_pos = h->slot_pos(0);
+  p.page_table = h->page_table(0); p.max_positions = h->cfg.max_positions; p.hot_req_stride = h->hot_req_stride();
+  p.R = h->cfg.num_requests; p.L = h->cfg.num_layers; p.B = h->cfg.buffer_slots; p.A = h->lay.A; p.G = h->G;
+  p.rec_bytes = h->cfg.record_bytes; p.request = request; p.ctx = ctx_len;
+  HS_HIP(launch_admit(p, (hipStream_t)stream));
   return HS_OK;
 }
 

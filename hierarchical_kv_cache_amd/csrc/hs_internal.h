@@ -63,7 +63,8 @@ int resolve_elems_per_thread(int k, int B);
 // Per-anchor metadata in the caller's workspace.  ctrl per request (uint32 x 4):
 // [0..1] 64-bit count of resolve workgroups that changed the metadata (every workgroup
 // of such a launch adds one, so count / G numbers those launches and its parity names
-// the ping-pong half holding the current metadata), [2] miss-plan count, [3] unused.
+// the ping-pong half holding the current metadata), [2] miss-plan count, [3] 1 when the
+// request was admitted short (tokens in slot order while the context fits B).
 struct ResolveParams {
   const int32_t* sel;        // [R][kb]
   const int32_t* ctx_len;    // [R]
@@ -101,6 +102,22 @@ struct AppendParams {
   const uint8_t* const* host_base;
   int64_t max_positions;
   int32_t R, L, B, rec_bytes;
+  // short requests: their new tokens also go to the slot of their position
+  const uint32_t* ctrl;      // anchor 0's [R][4]; anchor a at + a * R * 4
+  int32_t* slot_pos;         // anchor 0's [R][2][B]; anchor a at + a * R * 2 * B
+  int32_t* page_table;       // anchor 0's [R][max_positions]
+  int32_t A, G, group;       // anchors, resolve workgroups per request, layers per anchor
+};
+
+// Admission of a short request: positions [0, ctx) of every layer staged into slots [0, ctx).
+struct AdmitParams {
+  const uint8_t* const* host_base;
+  uint8_t* hot;
+  uint32_t* ctrl;            // anchor 0's [R][4]
+  int32_t* slot_pos;         // anchor 0's [R][2][B]
+  int32_t* page_table;       // anchor 0's [R][max_positions]
+  int64_t max_positions, hot_req_stride;
+  int32_t R, L, B, A, G, rec_bytes, request, ctx;
 };
 
 struct ReplayParams {
@@ -183,6 +200,7 @@ hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_export(const ExportParams& p, hipStream_t s);
 hipError_t launch_init(const InitParams& p, hipStream_t s);
+hipError_t launch_admit(const AdmitParams& p, hipStream_t s);
 hipError_t launch_probe_host_read(const void* src, size_t bytes, void* sink, int wgs, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_probe_empty(hipStream_t s);

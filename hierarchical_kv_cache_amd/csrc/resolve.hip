@@ -175,6 +175,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   uint32_t* rcnt = carry + 4 * NW;                   // [NW] resident entries per wave
   int* sh = (int*)(rcnt + NW);                       // [0] error bits [1] newest hits [2] half
                                                      // [3] slot map / page table disagreement
+                                                     // [4] fast-path range error
 
   const int tid = threadIdx.x;
   const int r = blockIdx.x % p.R;
@@ -224,6 +225,44 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
     raw[j] = (j < EK && i < kr) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
+  }
+  // ---- short-sequence fast path ("HiSparse 深度解析" §5.4, §5.5): a request admitted short
+  // keeps its tokens in slot order while its context fits B, so every position is its own
+  // slot: no hash, no LRU, no host IO (only the range is checked)
+  if (p.ctrl[r * 4 + 3] != 0 && ctx <= p.B) {
+    uint32_t bad = 0;
+#pragma unroll
+    for (int j = 0; j < KE; ++j) {
+      const int i = i0 + j;
+      const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                       : (int64_t)raw[j];
+      if (j < EK && i < kr) bad |= (uint32_t)(pos64 < 0 || pos64 >= ctx);
+    }
+    // block-wide OR through a scratch word of the dynamic LDS (no static LDS in this kernel)
+    if (tid == 0) sh[4] = 0;
+    __syncthreads();
+    if (bad) atomicOr((unsigned*)&sh[4], 1u);
+    __syncthreads();
+    bad = (uint32_t)sh[4];
+    if (g == 0) {
+      int32_t* outr = p.out + (size_t)r * p.k;
+      if (bad) {
+        for (int i = tid; i < p.k; i += NT) outr[i] = -1;
+      } else {
+#pragma unroll
+        for (int j = 0; j < KE; ++j) {
+          const int i = i0 + j;
+          if (j < EK && i < kr)
+            outr[i] = p.bt_shift ? (int32_t)((raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))) : raw[j];
+        }
+      }
+      if (tid == 0 && p.stats) {
+        hs_stats st = {bad ? 0u : (uint32_t)kr, 0u, bad ? (uint32_t)HS_ERR_RANGE : 0u, 0u};
+        p.stats[r] = st;
+      }
+      if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
+    }
+    return;
   }
   // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
   // map, so it names the slot of a hit) and, with a resident tier, its resident page.
@@ -778,14 +817,22 @@ hipError_t launch_ke(const ResolveParams& p, size_t lds, hipStream_t s, int KE) 
   return hipErrorInvalidValue;
 }
 
+// Maximum dynamic LDS of a kernel: the device's per-block LDS less the kernel's static LDS.
+hipError_t set_dynamic_lds(const void* fn, int v) {
+  hipFuncAttributes a;
+  hipError_t e = hipFuncGetAttributes(&a, fn);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, v - (int)a.sharedSizeBytes);
+}
+
 template <int E>
 hipError_t set_limit_ke(int v) {
   hipError_t e = hipSuccess;
-  if constexpr (E >= 1) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
-  if constexpr (E >= 2) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
-  if constexpr (E >= 4) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
-  if constexpr (E >= 8) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
-  if constexpr (E >= 16) if (e == hipSuccess) e = hipFuncSetAttribute((const void*)resolve_kernel<E, 16>, hipFuncAttributeMaxDynamicSharedMemorySize, v);
+  if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1>, v);
+  if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 2>, v);
+  if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 4>, v);
+  if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 8>, v);
+  if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 16>, v);
   return e;
 }
 
@@ -818,7 +865,7 @@ hipError_t set_resolve_lds_limit(size_t lds_bytes) {
 size_t union_lds_bytes(int hash_bits) { return (size_t(8) << hash_bits) + 4 * (4 * NW + 8); }
 
 hipError_t set_union_lds_limit(size_t lds_bytes) {
-  return hipFuncSetAttribute((const void*)union_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+  return set_dynamic_lds((const void*)union_kernel, (int)lds_bytes);
 }
 
 hipError_t launch_union(const UnionParams& p, hipStream_t s) {

@@ -246,8 +246,24 @@ const int32_t* hs_page_table(hs_handle h, int32_t layer);
  * order), P = top_k * max(1, verify_rows), and uint32 counts (stride 4 per request, count first). */
 hs_status hs_plan(hs_handle h, int32_t layer, const int32_t** d_plan, const uint32_t** d_counts);
 
+/*
+ * Admission of a short request ([GC] §5.3, §5.4 and §5.5: a request whose tokens fit the device
+ * buffer keeps them there in order, and the swap-in kernel's fast path returns their slots
+ * directly, with no host IO).  Stages positions [0, ctx_len) of every layer of `request` from the
+ * host pool into slots [0, ctx_len) in order, records them in every anchor's slot map and page
+ * table (never used, so oldest first), and marks the request short:
+ *   - while its context length is <= B, hs_resolve / hs_resolve_rows return slot = position for
+ *     every entry and change no LRU state (positions are range-checked only);
+ *   - hs_append also writes a new token at position p < B into slot p (in order);
+ *   - once the context exceeds B (with the B slots full of positions 0 .. B-1) the normal path
+ *     takes over from that state.
+ * The request must be in the admission state (after hs_create or hs_reset_request) and grow
+ * only by hs_append.  ctx_len <= buffer_slots.  Asynchronous on `stream`.
+ */
+hs_status hs_admit_short(hs_handle h, int32_t request, int32_t ctx_len, void* stream);
+
 /* Request release ([GC] §5.4): every layer of request r back to the admission state (all
- * slots empty, all positions host-only, LRU in slot order, no newest token). */
+ * slots empty, all positions host-only, LRU in slot order, no newest token, not short). */
 hs_status hs_reset_request(hs_handle h, int32_t request, void* stream);
 
 /* Waits for the library's own events, frees the pinned pool and the handle. */
