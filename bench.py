@@ -219,6 +219,7 @@ def main():
         detail.update(measure_resident(torch, hk, synth, w, dev, trace, lmax))
         detail.update(measure_fp8(torch, hk, synth, dev))
         detail.update(measure_rows(torch, hk, synth, dev))
+        detail.update(measure_short(torch, hk, synth, dev))
         detail["launch_latency_us"] = measure_empty(torch, hk)
         detail["hbm_copy_GBps"] = measure_hbm(torch, hk, dev)
         detail["link_ceiling_GBps"] = link["ceiling_GBps"]
@@ -516,6 +517,39 @@ def measure_rows(torch, hk, synth, dev, rows=4, steps=24):
     return {"spec4_resolve_rows_us_per_layer": float(np.median(us[4:])),
             "spec4_union_entries": float(union),
             "spec4_miss_rate_of_union": float(st[4:, ..., 1].sum() / max(1, (st[4:, ..., 0] + st[4:, ..., 1]).sum()))}
+
+
+def measure_short(torch, hk, synth, dev, steps=64):
+    """Short-sequence fast path: a request admitted short (2048 tokens in slot order, B = 4096,
+    k = 2048) resolves each layer to its own positions with no hash, LRU or IO.  Median µs per
+    layer call, 1 request x 8 layers (events)."""
+    R, L, k, B, ctx = 1, 8, 2048, 4096, 3072
+    w = synth.WORKLOADS["long"].scaled(append=False, force_newest=False, ctx=ctx)
+    lmax = ctx
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, ctx)
+        hk.hs_admit_short(cache.h, r, ctx, 0)
+    tr = np.stack([np.stack([synth.selection_trace(w, r, l, steps) for r in range(R)], axis=1) for l in range(L)], axis=1)
+    d_tr = torch.from_numpy(tr).to(dev)
+    d_ctx = torch.full((R,), ctx, dtype=torch.int32, device=dev)
+    d_out = torch.empty((R, k), dtype=torch.int32, device=dev)
+    d_st = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+           for _ in range(steps)]
+    for t in range(steps):
+        for l in range(L):
+            evs[t][l][0].record(s)
+            hk.hs_resolve(cache.h, l, d_tr[t, l].data_ptr(), d_ctx.data_ptr(), d_out.data_ptr(), d_st[t, l].data_ptr(),
+                          0, 0, s.cuda_stream)
+            evs[t][l][1].record(s)
+    torch.cuda.synchronize()
+    st = d_st.cpu().numpy()
+    assert (st[..., 0] == k).all() and not st[..., 1:3].any()
+    us = np.array([[evs[t][l][0].elapsed_time(evs[t][l][1]) * 1e3 for l in range(L)] for t in range(steps)])
+    cache.close()
+    return {"short_fast_path_us_per_layer": float(np.median(us[2:]))}
 
 
 def measure_empty(torch, hk):
