@@ -44,9 +44,9 @@ __global__ void __launch_bounds__(kCopyThreads) append_kernel(AppendParams p) {
       if (in_order) {
         for (int a = 0; a < p.A; ++a) {  // every anchor's slot map and page table
           const uint32_t* ca = p.ctrl + (size_t)a * p.R * 4;
-          const int cur = (int)((*(const uint64_t*)&ca[r * 4] / (uint64_t)p.G) & 1u);
+          const int cur = (int)(launch_number(*(const uint64_t*)&ca[r * 4]) & 1u);
           p.slot_pos[((size_t)a * p.R + r) * 2 * p.B + (size_t)cur * p.B + pos] = pos;
-          p.page_table[((size_t)a * p.R + r) * (size_t)p.max_positions + pos] = pos;
+          p.page_table[((size_t)a * p.R + r) * (size_t)p.max_positions + pos] = pt_entry(pos, 0u);
         }
       }
     }
@@ -128,8 +128,8 @@ __global__ void __launch_bounds__(kCopyThreads) init_kernel(InitParams p) {
     p.lru[(ar * 2 + 0) * p.Bpad + s] = (int16_t)s;
     p.lru[(ar * 2 + 1) * p.Bpad + s] = (int16_t)s;
   }
-  int32_t* pt = p.page_table + ar * (size_t)p.max_positions;
-  for (int64_t q = t; q < p.max_positions; q += nt) pt[q] = -1;
+  uint64_t* pt = p.page_table + ar * (size_t)p.max_positions;
+  for (int64_t q = t; q < p.max_positions; q += nt) pt[q] = kPtHostOnly;
   if (t == 0) {
     p.ctrl[ar * 4 + 0] = 0;
     p.ctrl[ar * 4 + 1] = 0;
@@ -160,9 +160,9 @@ __global__ void __launch_bounds__(kCopyThreads) admit_kernel(AdmitParams p) {
   for (int64_t s = t0; s < p.ctx; s += nt) {
     for (int a = 0; a < p.A; ++a) {
       const uint32_t* ca = p.ctrl + (size_t)a * p.R * 4;
-      const int cur = (int)((*(const uint64_t*)&ca[r * 4] / (uint64_t)p.G) & 1u);
+      const int cur = (int)(launch_number(*(const uint64_t*)&ca[r * 4]) & 1u);
       p.slot_pos[((size_t)a * p.R + r) * 2 * p.B + (size_t)cur * p.B + s] = (int32_t)s;
-      p.page_table[((size_t)a * p.R + r) * (size_t)p.max_positions + s] = (int32_t)s;
+      p.page_table[((size_t)a * p.R + r) * (size_t)p.max_positions + s] = pt_entry((int32_t)s, 0u);
     }
   }
   if (t0 == 0)
@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(kCopyThreads) admit_kernel(AdmitParams p) {
 
 __global__ void __launch_bounds__(kCopyThreads) export_kernel(ExportParams p) {
   const int r = blockIdx.y;
-  const int cur = (int)((*(const uint64_t*)&p.ctrl[r * 4] / (uint64_t)p.G) & 1u);
+  const int cur = (int)(launch_number(*(const uint64_t*)&p.ctrl[r * 4]) & 1u);
   for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < p.B; s += gridDim.x * blockDim.x) {
     if (p.out_slot_pos) p.out_slot_pos[(size_t)r * p.B + s] = p.slot_pos[((size_t)r * 2 + cur) * p.B + s];
     if (p.out_lru) p.out_lru[(size_t)r * p.B + s] = p.lru[((size_t)r * 2 + cur) * p.Bpad + s];

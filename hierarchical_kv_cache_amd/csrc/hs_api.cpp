@@ -74,7 +74,7 @@ Layout make_layout(const hs_config& c) {
   L.slot_pos = take(size_t(L.A) * R * 2 * B * sizeof(int32_t));
   L.lru = take(size_t(L.A) * R * 2 * L.Bpad * sizeof(int16_t));
   L.plan = take(size_t(L.A) * R * 2 * L.kmax * sizeof(int32_t));
-  L.page_table = take(size_t(L.A) * R * size_t(c.max_positions) * sizeof(int32_t));
+  L.page_table = take(size_t(L.A) * R * size_t(c.max_positions) * sizeof(uint64_t));
   L.newest = take(R * sizeof(int32_t));
   L.host_base = take(R * sizeof(void*));
   L.attn_part = take(size_t(c.num_layers) * R * L.S * kPartStride * sizeof(float));
@@ -161,8 +161,8 @@ struct hs_ctx {
   }
   int16_t* lru(int a) { return (int16_t*)(ws + lay.lru) + size_t(a) * cfg.num_requests * 2 * lay.Bpad; }
   int32_t* plan(int a) { return (int32_t*)(ws + lay.plan) + size_t(a) * cfg.num_requests * 2 * lay.kmax; }
-  int32_t* page_table(int a) {
-    return (int32_t*)(ws + lay.page_table) + size_t(a) * cfg.num_requests * size_t(cfg.max_positions);
+  uint64_t* page_table(int a) {
+    return (uint64_t*)(ws + lay.page_table) + size_t(a) * cfg.num_requests * size_t(cfg.max_positions);
   }
   int32_t* newest() { return (int32_t*)(ws + lay.newest); }
   const uint8_t* const* host_base() { return (const uint8_t* const*)(ws + lay.host_base); }
@@ -454,7 +454,7 @@ hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos,
   p.host_base = h->host_base(); p.max_positions = h->cfg.max_positions; p.R = h->cfg.num_requests;
   p.L = h->cfg.num_layers; p.B = h->cfg.buffer_slots; p.rec_bytes = h->cfg.record_bytes;
   p.ctrl = h->ctrl(0); p.slot_pos = h->slot_pos(0); p.page_table = h->page_table(0); p.A = h->lay.A;
-  p.G = h->G; p.group = h->cfg.layer_group;
+  p.group = h->cfg.layer_group;
   // slot B may only be overwritten once the previous write-through has read it (and then every
   // later fetch of the previous newest position finds its bytes on the host)
   HS_HIP(hipStreamWaitEvent(cs, h->ev_backup_done, 0));
@@ -536,12 +536,12 @@ hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32
   p.ctrl = h->ctrl(a); p.slot_pos = h->slot_pos(a); p.lru = h->lru(a);
   p.newest = (h->cfg.flags & HS_CFG_NEWEST_SLOT) ? h->newest() : nullptr;
   p.out_slot_pos = d_slot_pos; p.out_lru = d_lru; p.out_newest = d_newest;
-  p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad; p.G = h->G;
+  p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad;
   HS_HIP(launch_export(p, (hipStream_t)stream));
   return HS_OK;
 }
 
-const int32_t* hs_page_table(hs_handle h, int32_t layer) {
+const uint64_t* hs_page_table(hs_handle h, int32_t layer) {
   if (!h || layer < 0 || layer >= h->cfg.num_layers || !h->is_anchor(layer)) return nullptr;
   return h->page_table(layer / h->cfg.layer_group);
 }
@@ -565,7 +565,7 @@ hs_status hs_admit_short(hs_handle h, int32_t request, int32_t ctx_len, void* st
   AdmitParams p{};
   p.host_base = h->host_base(); p.hot = h->hot; p.ctrl = h->ctrl(0); p.slot_pos = h->slot_pos(0);
   p.page_table = h->page_table(0); p.max_positions = h->cfg.max_positions; p.hot_req_stride = h->hot_req_stride();
-  p.R = h->cfg.num_requests; p.L = h->cfg.num_layers; p.B = h->cfg.buffer_slots; p.A = h->lay.A; p.G = h->G;
+  p.R = h->cfg.num_requests; p.L = h->cfg.num_layers; p.B = h->cfg.buffer_slots; p.A = h->lay.A;
   p.rec_bytes = h->cfg.record_bytes; p.request = request; p.ctx = ctx_len;
   HS_HIP(launch_admit(p, (hipStream_t)stream));
   return HS_OK;

@@ -17,6 +17,31 @@ constexpr uint32_t kHasNewest = 1u << 8;  // internal resolve flag: slot B holds
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Launch counter of an anchor (ctrl[0..1] per request, 64 bits).  The G workgroups of a
+// resolve launch that changes the metadata add 2^kLaunchShift to it in total: workgroup 0
+// adds 2^kLaunchShift - (G - 1), every other workgroup adds 1, each once it has read the
+// metadata.  A workgroup reads the counter before adding its own share, so it sees a strict
+// subset of its launch's additions (less than 2^kLaunchShift) and count >> kLaunchShift
+// numbers the earlier launches whatever G each launch used.
+constexpr int kLaunchShift = 16;
+__host__ __device__ inline uint64_t launch_number(uint64_t count) { return count >> kLaunchShift; }
+
+// Page-table entry (64 bits): the slot holding the position in the low half (-1: host only),
+// in the high half the generation of the launch that wrote it (launch number + 1; 0 for
+// admission and appends).  Workgroup 0 of a launch writes the entries of that launch's
+// misses while its sibling workgroups may still be reading the table; a reader that finds
+// an entry of its own launch's generation knows the entry was not there before the launch,
+// and treats the position as host only, exactly as a sibling that read earlier.
+constexpr uint64_t kPtHostOnly = ~0ull;
+__host__ __device__ inline uint64_t pt_entry(int32_t slot, uint32_t gen) {
+  return ((uint64_t)gen << 32) | (uint32_t)slot;
+}
+// The slot an entry names for a reader of launch generation `gen` (-1: host only).
+__host__ __device__ inline int32_t pt_slot_for(uint64_t e, uint32_t gen) {
+  const int32_t slot = (int32_t)(uint32_t)e;
+  return (slot >= 0 && (uint32_t)(e >> 32) != gen) ? slot : -1;
+}
+
 // 16-byte non-temporal access to the pinned host pool through global (not flat)
 // addresses.  The pool's device addresses come from a table in memory, so the compiler
 // cannot prove their address space and would emit flat instructions, which also count
@@ -61,10 +86,10 @@ __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits, i
 int resolve_elems_per_thread(int k, int B);
 
 // Per-anchor metadata in the caller's workspace.  ctrl per request (uint32 x 4):
-// [0..1] 64-bit count of resolve workgroups that changed the metadata (every workgroup
-// of such a launch adds one, so count / G numbers those launches and its parity names
-// the ping-pong half holding the current metadata), [2] miss-plan count, [3] 1 when the
-// request was admitted short (tokens in slot order while the context fits B).
+// [0..1] 64-bit launch counter (launch_number() of it numbers the launches that changed
+// the metadata; its parity names the ping-pong half holding the current slot map and LRU
+// order), [2] miss-plan count, [3] 1 when the request was admitted short (tokens in slot
+// order while the context fits B).
 struct ResolveParams {
   const int32_t* sel;        // [R][kb]
   const int32_t* ctx_len;    // [R]
@@ -75,7 +100,7 @@ struct ResolveParams {
   int32_t* slot_pos;         // [R][2][B]
   int16_t* lru;              // [R][2][Bpad]
   int32_t* plan;             // [R][2][k]
-  int32_t* page_table;       // [R][max_positions]
+  uint64_t* page_table;      // [R][max_positions] pt_entry values
   const int32_t* newest;     // [R]
   const uint8_t* const* host_base;  // [R] device-usable addresses of each request's host region
   uint8_t* hot;              // hot buffer base [R][L][B+1][rec]
@@ -105,8 +130,8 @@ struct AppendParams {
   // short requests: their new tokens also go to the slot of their position
   const uint32_t* ctrl;      // anchor 0's [R][4]; anchor a at + a * R * 4
   int32_t* slot_pos;         // anchor 0's [R][2][B]; anchor a at + a * R * 2 * B
-  int32_t* page_table;       // anchor 0's [R][max_positions]
-  int32_t A, G, group;       // anchors, resolve workgroups per request, layers per anchor
+  uint64_t* page_table;      // anchor 0's [R][max_positions]
+  int32_t A, group;          // anchors, layers per anchor
 };
 
 // Admission of a short request: positions [0, ctx) of every layer staged into slots [0, ctx).
@@ -115,9 +140,9 @@ struct AdmitParams {
   uint8_t* hot;
   uint32_t* ctrl;            // anchor 0's [R][4]
   int32_t* slot_pos;         // anchor 0's [R][2][B]
-  int32_t* page_table;       // anchor 0's [R][max_positions]
+  uint64_t* page_table;      // anchor 0's [R][max_positions]
   int64_t max_positions, hot_req_stride;
-  int32_t R, L, B, A, G, rec_bytes, request, ctx;
+  int32_t R, L, B, A, rec_bytes, request, ctx;
 };
 
 struct ReplayParams {
@@ -174,14 +199,14 @@ struct ExportParams {
   int32_t* out_slot_pos;
   int32_t* out_lru;
   int32_t* out_newest;
-  int32_t R, B, Bpad, G;
+  int32_t R, B, Bpad;
 };
 
 struct InitParams {
   uint32_t* ctrl;
   int32_t* slot_pos;
   int16_t* lru;
-  int32_t* page_table;
+  uint64_t* page_table;
   int32_t* newest;
   int64_t max_positions;
   int32_t R, B, Bpad, A, request;  // request < 0: all

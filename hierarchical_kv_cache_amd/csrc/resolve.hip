@@ -33,11 +33,14 @@
 // enough loads in flight to fill the host link; only workgroup 0 writes the
 // new metadata.  The slot map and the LRU order are ping-ponged: a 64-bit
 // counter per request numbers the launches that changed the metadata (each of
-// their workgroups adds one once it has read the metadata); its parity names
-// the half holding the current metadata, and workgroup 0 writes the other
-// half.  A launch that changes nothing (an error, or everything resident)
-// leaves the counter alone, so its half stays current.  No workgroup waits on
-// another.
+// their workgroups adds its share once it has read the metadata); its parity
+// names the half holding the current metadata, and workgroup 0 writes the other
+// half.  The page table is updated in place, each entry tagged with the
+// generation of the launch that wrote it, so a sibling that reads an entry
+// after workgroup 0 has written it still classifies the position as the miss
+// it was when the launch began.  A launch that changes nothing (an error, or
+// everything resident) leaves the counter alone, so its half stays current.
+// No workgroup waits on another.
 //
 // Latency shape (the all-hit call is bounded by launch and memory latency,
 // not bandwidth): every global read the kernel needs -- the selection, both
@@ -176,6 +179,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   int* sh = (int*)(rcnt + NW);                       // [0] error bits [1] newest hits [2] half
                                                      // [3] slot map / page table disagreement
                                                      // [4] fast-path range error
+                                                     // [5] page-table generation
 
   const int tid = threadIdx.x;
   const int r = blockIdx.x % p.R;
@@ -207,19 +211,19 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   }
 
   // ---- every global read up front -------------------------------------------------------
-  // Launch counter: every launch that changes the metadata adds G per request, one per
-  // workgroup after its reads, so count / G (a workgroup of this launch sees at most G-1
-  // of its siblings' increments) numbers the launches before this one; its parity picks
-  // the ping-pong half that holds the current metadata.  The value is needed only after
-  // stage 1, so its latency hides behind the loads.
+  // Launch counter (launch_number: the launches before this one that changed the
+  // metadata, whichever of this launch's siblings have already added their share).  Its
+  // parity picks the ping-pong half that holds the current slot map and LRU order, and
+  // number + 1 is the generation this launch writes into the page table.  The value is
+  // needed only after the entry loads, so its latency hides behind them.
   uint64_t* counter = (uint64_t*)&p.ctrl[r * 4];
   uint64_t launches = 0;
   if (tid == 0)
-    launches = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / (uint64_t)p.G;
+    launches = launch_number(__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
   const int32_t* selr = p.sel + (size_t)r * p.kb;
-  const int32_t* ptr = p.page_table + (size_t)r * p.max_positions;
+  const uint64_t* ptr = p.page_table + (size_t)r * p.max_positions;
   int32_t raw[KE];
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
@@ -268,14 +272,15 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   // map, so it names the slot of a hit) and, with a resident tier, its resident page.
   const bool tiered = p.rtable != nullptr;
   const int32_t* rtr = p.rtable + (tiered ? (size_t)r * p.rt_stride : 0);
-  int32_t ptv[KE], rpg[KE];
+  uint64_t ptv[KE];
+  int32_t rpg[KE];
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
     const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
                                      : (int64_t)raw[j];
     const bool ok = j < EK && i < kr && pos64 >= 0 && pos64 < ctx;
-    ptv[j] = ok ? ptr[pos64] : -1;
+    ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
     rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
   // Fetch workgroups (all but workgroup 0 when G > 1) also read the selection entries of
@@ -311,11 +316,16 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     u32x4* s4 = (u32x4*)sown;  // B int16, padded to 16 bytes
     for (int h = tid; h < (p.B + 7) / 8; h += NT) s4[h] = e4;
   }
-  if (tid == 0) { sh[0] = 0; sh[1] = 0; sh[3] = 0; }
+  if (tid == 0) {
+    sh[0] = 0; sh[1] = 0; sh[3] = 0;
+    sh[2] = (int)(launches & 1u);
+    sh[5] = (int)(uint32_t)(launches + 1);  // this launch's page-table generation
+  }
   // Misses known early from the page table: a selected position whose entry is -1 (and
   // that the resident tier does not serve) is not on the device.  Their host loads start
   // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
-  int32_t fpos[KE], fpt[KE], fres[KE];
+  int32_t fpos[KE], fres[KE];
+  uint64_t fpt[KE];
 #pragma unroll
   for (int q = 0; q < KE; ++q) {
     const int e = q * NT + lane * NW + wid;
@@ -325,7 +335,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
     const bool ok = pos64 >= 0 && pos64 < ctx;
     fpos[q] = ok ? (int32_t)pos64 : -1;
-    fpt[q] = ok ? ptr[pos64] : 0;
+    fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
     fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
   // resident entries with a row inside the pool, counted per wave
@@ -345,6 +355,12 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     if (lane == 0) rcnt[wid] = (uint32_t)cnt;
   }
   __syncthreads();
+  // Page-table entries written by this launch's workgroup 0 (a sibling that reads late can
+  // see them) name positions that were host only when the launch began.
+  const uint32_t gen = (uint32_t)sh[5];
+  int32_t pts[KE];
+#pragma unroll
+  for (int j = 0; j < KE; ++j) pts[j] = pt_slot_for(ptv[j], gen);
 
   // ---- resident tier: a selection that is resident throughout returns here ---------------
   int nres = 0;
@@ -413,14 +429,14 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       cls[j] = p.B;
       atomicAdd(&sh[1], 1);
       continue;
-    } else if (ptv[j] >= 0) {  // a hit: the slot holding the position
+    } else if (pts[j] >= 0) {  // a hit: the slot holding the position
       selp[i] = (int32_t)pos64;
-      if (ptv[j] >= p.B) {  // the page table never names a slot outside [0, B)
+      if (pts[j] >= p.B) {  // the page table never names a slot outside [0, B)
         err |= HS_ERR_STATE;
         continue;
       }
-      cls[j] = ptv[j];
-      sown[ptv[j]] = (int16_t)i;
+      cls[j] = pts[j];
+      sown[pts[j]] = (int16_t)i;
       hitb |= 1u << j;
       continue;
     } else {
@@ -479,7 +495,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   {
 #pragma unroll
     for (int q = 0; q < KE; ++q) {
-      const bool miss = fpos[q] >= 0 && fpos[q] != newest && fres[q] < 0 && fpt[q] < 0;
+      const bool miss = fpos[q] >= 0 && fpos[q] != newest && fres[q] < 0 && pt_slot_for(fpt[q], gen) < 0;
       const uint64_t b = __ballot(miss);
       if (miss) {
         const int at = mw + lanes_below(b);
@@ -508,7 +524,6 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   }
 
   if (err) atomicOr((unsigned*)&sh[0], err);
-  if (tid == 0) sh[2] = (int)(launches & 1u);
   __syncthreads();
   err = (uint32_t)sh[0] | (sh[1] > 1 ? HS_ERR_DUP : 0u);
   const bool h1 = sh[2] != 0;  // current metadata in half 1, new metadata goes to half 0
@@ -528,8 +543,11 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     }
     return;
   }
-  // this launch changes the metadata: the next one finds it in the other half
-  if (tid == 0) __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // this launch changes the metadata: the next one finds it in the other half (the shares
+  // of the G workgroups add up to one launch unit)
+  if (tid == 0)
+    __hip_atomic_fetch_add(counter, g == 0 ? (1ull << kLaunchShift) - (uint64_t)(p.G - 1) : 1ull,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- stage 3: misses in list order and evictables in LRU order, one scan -------------
   uint32_t mbits = 0, ebits = 0;
@@ -589,7 +607,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     if (bad) atomicOr((unsigned*)&sh[3], HS_ERR_STATE);
     int rv, rh, tv, th;
     block_ranks2<E>(vb, hb, carry + 2 * NW, rv, rh, tv, th);
-    int32_t* pt = p.page_table + (size_t)r * p.max_positions;
+    uint64_t* pt = p.page_table + (size_t)r * p.max_positions;
     int32_t* outr = p.out + (size_t)r * p.k;
     int32_t* plan_pos = p.plan + (size_t)r * 2 * p.plan_k;
     int32_t* plan_slot = plan_pos + p.plan_k;
@@ -606,8 +624,8 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
         const int jm = -2 - fo[j];
         const int i = missidx[jm];
         const int32_t np = selp[i];
-        if (spo[j] >= 0) pt[spo[j]] = -1;  // the evicted position is host-only again
-        pt[np] = s;
+        if (spo[j] >= 0) pt[spo[j]] = kPtHostOnly;  // the evicted position is host-only again
+        pt[np] = pt_entry(s, gen);
         spn[j] = np;
         outr[i] = s;
         if (record) {

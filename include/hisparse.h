@@ -239,8 +239,10 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
 hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32_t* d_lru,
                           int32_t* d_newest, void* stream);
 
-/* Device address of an anchor layer's page table, int32 [R][max_positions], -1 = host only. */
-const int32_t* hs_page_table(hs_handle h, int32_t layer);
+/* Device address of an anchor layer's page table, uint64 [R][max_positions]: the low 32 bits of
+ * an entry are the slot holding the position (int32, -1 = host only), the high 32 bits a
+ * generation tag the resolve kernel uses to order its own updates (bookkeeping only). */
+const uint64_t* hs_page_table(hs_handle h, int32_t layer);
 
 /* Device address of an anchor layer's miss plan: int32 [R][2][P] (positions, then slots, in miss
  * order), P = top_k * max(1, verify_rows), and uint32 counts (stride 4 per request, count first). */

@@ -208,10 +208,10 @@ class Pair:
             sp, lru, nw = sp.cpu().numpy(), lru.cpu().numpy(), nw.cpu().numpy()
             if page_table:
                 pt_addr = hk.hs_page_table(self.h, l)
-                pt = torch.empty((w.R, self.lmax), dtype=torch.int32, device=self.dev)
+                pt = torch.empty((w.R, self.lmax), dtype=torch.int64, device=self.dev)
                 torch.cuda.synchronize()
                 _copy_dev(pt_addr, pt)
-                pt = pt.cpu().numpy()
+                pt = page_table_slots(pt.cpu().numpy())
             for r in requests:
                 st = self.caches[(r, l)].export()
                 assert np.array_equal(sp[r], st["slot_pos"]), ("slot_pos", r, l)
@@ -249,6 +249,11 @@ class Pair:
         torch.cuda.synchronize()
         self.pool.shutdown()
         self.gpu.close()
+
+
+def page_table_slots(pt: np.ndarray) -> np.ndarray:
+    """Slots of 64-bit page-table entries (the low 32 bits, int32; -1 = host only)."""
+    return np.ascontiguousarray(pt).view(np.int32)[..., 0::2]
 
 
 def _copy_dev(addr, dst: torch.Tensor):
