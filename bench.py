@@ -80,7 +80,8 @@ def profile_avg_us(kernel: str, workload: str = "long"):
     with open(path) as f:
         for line in f:
             parts = line.split()
-            if parts and parts[0].split("<")[0] == kernel:
+            if parts and not line.startswith("#") and \
+                    (parts[0] == kernel if "<" in kernel else parts[0].split("<")[0] == kernel):
                 return float(parts[3])
     return None
 
@@ -135,54 +136,87 @@ def main():
     cs, bs = compute.cuda_stream, backup.cuda_stream
     input_s = time.time() - t_in
 
-    ev = {name: [[torch.cuda.Event(enable_timing=True) for _ in range(L)] for _ in range(K)]
-          for name in ("r0", "r1", "a1")}
-
-    def step(c, t, timed_idx=None):
+    def step(c, t, fused, ev_row=None):
+        """One decode step: write-through of the new token, then per layer RESOLVE and the
+        attention over the published slots (one fused call, or hs_resolve + hs_sparse_attn).
+        ev_row: events recorded on the launch stream around each layer's attention call."""
         hk.hs_append(c.h, d_new_kv[t].data_ptr(), d_new_pos[t].data_ptr(), cs, bs)
         for l in range(L):
-            if timed_idx is not None:
-                ev["r0"][timed_idx][l].record(compute)
-            hk.hs_resolve(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
-                          d_stats[t, l].data_ptr(), 0, 0, cs)
-            if timed_idx is not None:
-                ev["r1"][timed_idx][l].record(compute)
-            hk.hs_sparse_attn(c.h, l, d_q[t, l].data_ptr(), heads, 512, d_slots[l].data_ptr(),
-                              d_out[l].data_ptr(), scale, 0, cs)
-            if timed_idx is not None:
-                ev["a1"][timed_idx][l].record(compute)
+            if fused:
+                if ev_row is not None:
+                    ev_row[l][0].record(compute)
+                hk.hs_resolve_attn(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
+                                   d_stats[t, l].data_ptr(), 0, 0, d_q[t, l].data_ptr(), heads, 512,
+                                   d_out[l].data_ptr(), scale, cs)
+            else:
+                hk.hs_resolve(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
+                              d_stats[t, l].data_ptr(), 0, 0, cs)
+                if ev_row is not None:
+                    ev_row[l][0].record(compute)
+                hk.hs_sparse_attn(c.h, l, d_q[t, l].data_ptr(), heads, 512, d_slots[l].data_ptr(),
+                                  d_out[l].data_ptr(), scale, 0, cs)
+            if ev_row is not None:
+                ev_row[l][1].record(compute)
 
-    # pass 1 (the reported value): W warmup steps, then K timed steps, nothing between kernels
-    for t in range(W):
-        step(cache, t)
-    sync_barrier(torch)
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(cache, W + i)
-    sync_barrier(torch)
-    elapsed = time.perf_counter() - t0
-    backup.synchronize()
+    def fresh_cache():
+        c = hk.HiSparse(cfg)
+        for r in range(R):
+            synth.fill_request(c.host_pool_address(r), r, L, lmax, w.ctx)
+        return c
+
+    def value_pass(c, fused):
+        """W warmup steps, then K timed steps with nothing between kernels."""
+        for t in range(W):
+            step(c, t, fused)
+        sync_barrier(torch)
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(c, W + i, fused)
+        sync_barrier(torch)
+        dt = time.perf_counter() - t0
+        backup.synchronize()
+        return dt
+
+    def timing_pass(c, fused):
+        """The same steps from the same empty start: the RESOLVE (or fused) kernel of every
+        timed layer stamped by its own start and end; events around each attention call
+        (for the fused call: around the whole call, kernel and merge)."""
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)] for _ in range(K)]
+        for t in range(W):
+            step(c, t, fused)
+        hk.hs_timing_start(c.h, K * L)
+        for i in range(K):
+            step(c, W + i, fused, ev_row=ev[i])
+        sync_barrier(torch)
+        backup.synchronize()
+        kern = hk.hs_timing_read(c.h, K * L)
+        assert kern.size == K * L
+        call = [ev[i][l][0].elapsed_time(ev[i][l][1]) * 1e3 for i in range(K) for l in range(L)]
+        return [float(x) for x in kern], call
+
+    # pass 1 (the reported value): the fused path
+    fused = hk.hs_resolve_attn_wgs(cache.h) > 0
+    elapsed = value_pass(cache, True)
     stats = d_stats.cpu().numpy()
-
-    # pass 2 (per-kernel durations): the same steps from the same empty start on a second
-    # cache, with HIP events recorded on the launch stream around every kernel (events
-    # between kernels add about a quarter to the step time, so they stay out of pass 1)
+    out_fused = d_out.clone()
     cache.close()
-    cache = hk.HiSparse(cfg)
-    for r in range(R):
-        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
-    d_stats2 = d_stats
-    d_stats = torch.zeros_like(d_stats2)
-    for t in range(W):
-        step(cache, t)
-    for i in range(K):
-        step(cache, W + i, timed_idx=i)
-    sync_barrier(torch)
-    backup.synchronize()
-    assert np.array_equal(d_stats.cpu().numpy(), stats), "the two passes resolved differently"
+    # pass 2: kernel durations of the fused path
+    cache = fresh_cache()
+    d_stats.zero_()
+    kern_us, call_us = timing_pass(cache, True)
+    assert np.array_equal(d_stats.cpu().numpy(), stats), "the passes resolved differently"
+    cache.close()
+    # passes 3 and 4: the same steps through hs_resolve + hs_sparse_attn
+    cache = fresh_cache()
+    d_stats.zero_()
+    elapsed_sep = value_pass(cache, False)
+    assert np.array_equal(d_stats.cpu().numpy(), stats), "the separate calls resolved differently"
+    att_dev = float((d_out - out_fused).abs().max() / out_fused.abs().max())
+    cache.close()
+    cache = fresh_cache()
+    d_stats.zero_()
+    res_us, att_us = timing_pass(cache, False)
 
-    res_us = [ev["r0"][i][l].elapsed_time(ev["r1"][i][l]) * 1e3 for i in range(K) for l in range(L)]
-    att_us = [ev["r1"][i][l].elapsed_time(ev["a1"][i][l]) * 1e3 for i in range(K) for l in range(L)]
     errors = int(stats[..., 2].any())
     misses_timed = int(stats[W:, :, :, 1].sum())
     hits_timed = int(stats[W:, :, :, 0].sum())
@@ -191,9 +225,18 @@ def main():
     miss_rate = misses_timed / max(1, misses_timed + hits_timed)
 
     detail = {
-        "resolve_us_per_layer_mean": statistics.fmean(res_us),
-        "resolve_us_per_layer_median": statistics.median(res_us),
-        "attention_us_per_layer_mean": statistics.fmean(att_us),
+        "path": "hs_resolve_attn (fused RESOLVE + attention kernel, then merge)" if fused
+                else "hs_resolve_attn (two calls: no fused kernel for this configuration)",
+        "fused_kernel_us_per_layer_mean": statistics.fmean(kern_us),
+        "fused_kernel_us_per_layer_median": statistics.median(kern_us),
+        "fused_call_us_per_layer_mean": statistics.fmean(call_us),
+        "fused_wgs_per_request": hk.hs_resolve_attn_wgs(cache.h),
+        "separate_selections_per_s": selections / elapsed_sep,
+        "separate_ms_per_step": elapsed_sep / K * 1e3,
+        "separate_resolve_kernel_us_per_layer_mean": statistics.fmean(res_us),
+        "separate_resolve_kernel_us_per_layer_median": statistics.median(res_us),
+        "separate_attention_call_us_per_layer_mean": statistics.fmean(att_us),
+        "fused_vs_separate_attention_max_rel_diff": att_dev,
         "miss_rate": miss_rate,
         "misses_per_layer_step": misses_timed / (K * L * R),
         "cold_step_misses": int(stats[0, :, :, 1].sum()),
@@ -201,7 +244,6 @@ def main():
         "resolve_wgs_per_request": cache.wgs,
         "input_setup_s": round(input_s, 2),
     }
-
     # ---- secondary measurements --------------------------------------------------------
     link = {}
     if args.quick:
@@ -229,23 +271,27 @@ def main():
             detail[key.replace("GBps", "frac_of_link")] = detail[key] / link["ceiling_GBps"]
 
     # ---- roofline of the dominant kernel -------------------------------------------------
-    # RESOLVE is the longest single kernel of the step (the attention call is two kernels,
-    # attention and merge, each shorter; see the kernel trace).  Its algorithmic bytes per
-    # launch: selection in, slot map + LRU read and written, slots out, and per miss the
-    # record written to HBM plus two page-table writes and the plan entry.
+    # The fused RESOLVE + attention kernel is the longest kernel of the step (the merge and the
+    # write-through kernels are short; see the kernel trace).  Its algorithmic bytes per
+    # launch, per request: the selection in and the slots out; the slot map and LRU order read
+    # and written; per miss the record written to HBM and two page-table entries; the k
+    # selected records read once (hot slots from HBM, misses from the host pool); the queries
+    # in and the output out.  The split into chunk partials is not counted.
     steady_misses = misses_timed / (K * L * R)
-    alg_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + steady_misses * (REC + 8 + 8))
-    t_us = statistics.fmean(res_us)
-    roof = {"kernel": "resolve_kernel", "bound": "hbm", "achieved": alg_bytes / (t_us * 1e-6) / 1e9,
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": profile_traffic("resolve_kernel")}
-    # the attention call (attention + merge kernels) for reference: k records, q and out per request
-    att_bytes = R * (k * REC + heads * 576 * 2 + heads * 512 * 4)
-    detail["attention_call_bytes"] = att_bytes
-    detail["attention_call_GBps"] = att_bytes / (statistics.fmean(att_us) * 1e-6) / 1e9
+    alg_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + steady_misses * (REC + 8 + 8)
+                     + k * REC + heads * 576 * 2 + heads * 512 * 4)
+    t_us = statistics.fmean(kern_us)
+    kname = "resolve_kernel<4,2,true>"
+    roof = {"kernel": kname, "bound": "hbm", "achieved": alg_bytes / (t_us * 1e-6) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": profile_traffic("resolve_attn_kernel")}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["avg_launch_us_events"] = t_us
-    roof["avg_launch_us_rocprof"] = profile_avg_us(roof["kernel"])
+    roof["avg_launch_us_kernel_events"] = t_us
+    roof["avg_launch_us_rocprof"] = profile_avg_us(kname)
     roof["algorithmic_bytes_per_launch"] = alg_bytes
+    # the separate path's RESOLVE kernel for reference (metadata and misses only)
+    sep_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + steady_misses * (REC + 8 + 8))
+    detail["separate_resolve_alg_bytes"] = sep_bytes
+    detail["separate_resolve_GBps"] = sep_bytes / (statistics.fmean(res_us) * 1e-6) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -52,10 +52,10 @@ EXPORTS = (
     "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_resolve_rows", "hs_bind_resident",
     "hs_append",
     "hs_prefetch_shared",
-    "hs_wait_layer", "hs_sparse_attn", "hs_export_state", "hs_page_table", "hs_plan", "hs_admit_short",
+    "hs_wait_layer", "hs_sparse_attn", "hs_resolve_attn", "hs_resolve_attn_wgs", "hs_export_state", "hs_page_table", "hs_plan", "hs_admit_short",
     "hs_reset_request",
     "hs_destroy", "hs_last_error", "hs_resolve_wgs", "hs_probe_host_read", "hs_probe_copy",
-    "hs_probe_empty",
+    "hs_probe_empty", "hs_timing_start", "hs_timing_read",
 )
 
 
@@ -83,6 +83,8 @@ def _load():
         "hs_prefetch_shared": (i32, [vp, i32, vp, vp]),
         "hs_wait_layer": (i32, [vp, i32, vp]),
         "hs_sparse_attn": (i32, [vp, i32, vp, i32, i32, vp, vp, ctypes.c_float, vp, vp]),
+        "hs_resolve_attn": (i32, [vp, i32, vp, vp, vp, vp, vp, u32, vp, i32, i32, vp, ctypes.c_float, vp]),
+        "hs_resolve_attn_wgs": (i32, [vp]),
         "hs_export_state": (i32, [vp, i32, vp, vp, vp, vp]),
         "hs_page_table": (vp, [vp, i32]),
         "hs_plan": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp)]),
@@ -94,6 +96,8 @@ def _load():
         "hs_probe_host_read": (i32, [vp, sz, vp, i32, vp]),
         "hs_probe_copy": (i32, [vp, vp, sz, vp]),
         "hs_probe_empty": (i32, [vp]),
+        "hs_timing_start": (i32, [vp, i32]),
+        "hs_timing_read": (i32, [vp, vp, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -160,6 +164,16 @@ def hs_sparse_attn(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num
                                stream or None))
 
 
+def hs_resolve_attn(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, d_q, heads, value_dim,
+                    d_out, scale, stream):
+    _check(_lib.hs_resolve_attn(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats or None, d_num_reqs or None,
+                                flags, d_q, heads, value_dim, d_out, scale, stream or None))
+
+
+def hs_resolve_attn_wgs(h) -> int:
+    return _lib.hs_resolve_attn_wgs(h)
+
+
 def hs_export_state(h, layer, d_slot_pos, d_lru, d_newest, stream):
     _check(_lib.hs_export_state(h, layer, d_slot_pos or None, d_lru or None, d_newest or None, stream or None))
 
@@ -207,6 +221,19 @@ def hs_probe_copy(d_src, d_dst, nbytes, stream):
 
 def hs_probe_empty(stream):
     _check(_lib.hs_probe_empty(stream or None))
+
+
+def hs_timing_start(h, n):
+    _check(_lib.hs_timing_start(h, n))
+
+
+def hs_timing_read(h, n) -> np.ndarray:
+    """Durations (µs) of the timed RESOLVE launches, in launch order."""
+    out = np.zeros(max(0, n), np.float32)
+    m = _lib.hs_timing_read(h, out.ctypes.data, n)
+    if m < 0:
+        raise HsError(m, _lib.hs_last_error().decode())
+    return out[:m]
 
 
 # ---- convenience owner --------------------------------------------------------------------

@@ -26,8 +26,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AT = 256;                 // 4 waves
 constexpr int TT = 64;                  // tokens per tile
-constexpr int RS = 1184;                // LDS row stride: 1152 + 32 bytes keeps quarter-waves on
-                                        // disjoint banks in the P V operand reads
+constexpr int RS = kTileStride;         // LDS row stride (1168 bytes): conflict-free QK^T and P V
+                                        // operand reads
 constexpr int KSTEPS = kAttnDk / 32;    // 18
 constexpr int CHUNKS = kAttnDk * 2 / 16;  // 72 16-byte chunks per record
 constexpr int CT = kAttnDv / 4 / 16;    // 8 channel tiles of 16 per wave
@@ -224,9 +224,7 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sv[i] = valid ? sacc[i] * sl2 : -INFINITY;
-      mx[i] = sv[i];
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], d));
+      mx[i] = row16_max(sv[i]);
     }
     if (col == 0)
 #pragma unroll
@@ -287,10 +285,7 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
   // per-head sums: over the 16 token columns of a quarter-wave, then over waves
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float v = l_lane[i];
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d);
-    l_lane[i] = v;
+    l_lane[i] = row16_sum(l_lane[i]);
   }
   __syncthreads();
   if (col == 0)
@@ -392,6 +387,10 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   else hipLaunchKernelGGL(attn_kernel<false>, dim3(grid), dim3(AT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
+  return launch_attn_merge(p, s);
+}
+
+hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s) {
   hipLaunchKernelGGL(attn_merge_kernel, dim3(p.R * p.heads * kMergeQuarters), dim3(64), 0, s, p);
   return hipGetLastError();
 }

@@ -45,6 +45,7 @@ struct Layout {
   int A = 0;        // anchor layers
   int Bpad = 0;
   int S = 1;        // attention chunks per request
+  int Spart = 1;    // partial records per (layer, request): max(S, fused chunks)
   int kmax = 0;     // longest list one resolve handles: top_k * max(1, verify_rows)
   size_t ctrl = 0, slot_pos = 0, lru = 0, plan = 0, page_table = 0, newest = 0, host_base = 0,
          attn_part = 0, uni = 0, umap = 0, uout = 0, ucnt = 0, uerr = 0, total = 0;
@@ -61,12 +62,26 @@ int attn_chunks(const hs_config& c) {
   return S;
 }
 
+// Fused RESOLVE + attention (hs_resolve_attn): one fetch workgroup per 64 selected entries
+// plus workgroup 0, all of them resident at once (one workgroup per CU, 256 CUs), bf16
+// records of 576 values.  Returns the chunk count S, or 0 when the configuration does not
+// take the fused kernel (whether LDS suffices is checked per device in hs_create).
+int fused_chunks(const hs_config& c) {
+  if ((c.flags & HS_CFG_RECORD_FP8) || c.record_bytes != kAttnDk * 2) return 0;
+  if (!fused_supported(c.top_k, c.buffer_slots)) return 0;
+  const int S = (c.top_k + kTileRows - 1) / kTileRows;
+  if (int64_t(c.num_requests) * (S + 1) > 256) return 0;
+  return S;
+}
+
 Layout make_layout(const hs_config& c) {
   Layout L;
   const size_t R = c.num_requests, B = c.buffer_slots, k = c.top_k;
   L.A = (c.num_layers + c.layer_group - 1) / c.layer_group;
   L.Bpad = (int)align_up(B, 8);
   L.S = attn_chunks(c);
+  const int Sf = fused_chunks(c);
+  L.Spart = L.S > Sf ? L.S : Sf;
   L.kmax = c.top_k * (c.verify_rows > 1 ? c.verify_rows : 1);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
@@ -77,7 +92,7 @@ Layout make_layout(const hs_config& c) {
   L.page_table = take(size_t(L.A) * R * size_t(c.max_positions) * sizeof(uint64_t));
   L.newest = take(R * sizeof(int32_t));
   L.host_base = take(R * sizeof(void*));
-  L.attn_part = take(size_t(c.num_layers) * R * L.S * kPartStride * sizeof(float));
+  L.attn_part = take(size_t(c.num_layers) * R * L.Spart * kPartStride * sizeof(float));
   if (c.verify_rows > 1) {  // union scratch of hs_resolve_rows (one set per handle)
     L.uni = take(R * L.kmax * sizeof(int32_t));
     L.umap = take(R * L.kmax * sizeof(int32_t));
@@ -141,6 +156,12 @@ struct hs_ctx {
   size_t lds_bytes = 0;
   int spec_hash_bits = 0, union_hash_bits = 0;  // RESOLVE of a union, and the union kernel
   size_t spec_lds_bytes = 0;
+  int att_G = 0, att_hash_bits = 0;  // fused RESOLVE + attention; att_G 0: not available
+  size_t att_lds = 0;
+  // measurement aid: kernel-timed RESOLVE launches (hs_timing_start / hs_timing_read)
+  std::vector<KernelTiming> tm;
+  size_t tm_next = 0;
+  const KernelTiming* next_timing() { return tm_next < tm.size() ? &tm[tm_next++] : nullptr; }
   int device = 0;
   uint8_t* hot = nullptr;
   uint8_t* ws = nullptr;
@@ -167,7 +188,7 @@ struct hs_ctx {
   int32_t* newest() { return (int32_t*)(ws + lay.newest); }
   const uint8_t* const* host_base() { return (const uint8_t* const*)(ws + lay.host_base); }
   float* attn_part(int l) {
-    return (float*)(ws + lay.attn_part) + size_t(l) * cfg.num_requests * lay.S * kPartStride;
+    return (float*)(ws + lay.attn_part) + size_t(l) * cfg.num_requests * lay.Spart * kPartStride;
   }
   int64_t host_layer_off(int l) const { return int64_t(l) * cfg.max_positions * cfg.record_bytes; }
   int64_t hot_req_stride() const { return int64_t(cfg.num_layers) * (cfg.buffer_slots + 1) * cfg.record_bytes; }
@@ -185,9 +206,19 @@ void destroy_events(hs_ctx* h) {
   for (auto e : h->ev_layer) if (e) (void)hipEventDestroy(e);
 }
 
+void free_timing(hs_ctx* h) {
+  for (auto& t : h->tm) {
+    if (t.start) (void)hipEventDestroy(t.start);
+    if (t.stop) (void)hipEventDestroy(t.stop);
+  }
+  h->tm.clear();
+  h->tm_next = 0;
+}
+
 void free_ctx(hs_ctx* h) {
   if (!h) return;
   destroy_events(h);
+  free_timing(h);
   for (void* p : h->pool) if (p) (void)hipHostFree(p);
   delete h;
 }
@@ -200,6 +231,25 @@ hs_status check_handle(hs_ctx* h) {
 hs_status check_layer(hs_ctx* h, int32_t layer) {
   if (layer < 0 || layer >= h->cfg.num_layers) return fail(HS_EINVAL, "layer %d out of range", layer);
   return HS_OK;
+}
+
+// The RESOLVE launch of one anchor layer (the fused call overrides G and the hash size).
+ResolveParams resolve_params(hs_ctx* h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
+                             int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs, uint32_t flags) {
+  const int a = layer / h->cfg.layer_group;
+  ResolveParams p{};
+  p.sel = d_sel; p.ctx_len = d_ctx_len; p.out = d_slots_out; p.stats = d_stats; p.num_reqs = d_num_reqs;
+  p.ctrl = h->ctrl(a); p.slot_pos = h->slot_pos(a); p.lru = h->lru(a); p.plan = h->plan(a);
+  p.page_table = h->page_table(a); p.newest = h->newest(); p.host_base = h->host_base(); p.hot = h->hot;
+  p.host_layer_off = h->host_layer_off(layer); p.hot_req_stride = h->hot_req_stride();
+  p.hot_layer_off = h->hot_layer_off(layer); p.max_positions = h->cfg.max_positions;
+  p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad; p.k = h->cfg.top_k;
+  p.kb = h->cfg.top_k / h->cfg.block_tokens; p.bt_shift = ilog2(h->cfg.block_tokens);
+  p.rec_bytes = h->cfg.record_bytes; p.G = h->G; p.hash_bits = h->hash_bits;
+  p.flags = flags | ((h->cfg.flags & HS_CFG_NEWEST_SLOT) ? kHasNewest : 0u);
+  p.rtable = h->rtable; p.rt_stride = h->rt_stride; p.res_rows = h->res_rows; p.page_shift = h->page_shift;
+  p.plan_k = h->lay.kmax;
+  return p;
 }
 
 }  // namespace
@@ -271,6 +321,21 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
     if (union_lds_bytes(h->union_hash_bits) > prop.sharedMemPerBlock) {
       free_ctx(h);
       return fail(HS_EINVAL, "the union of %d rows needs too much LDS", cfg->verify_rows);
+    }
+  }
+  // fused RESOLVE + attention: G = chunks + 1, when its LDS fits (a half-full hash if need be)
+  if (const int Sf = fused_chunks(*cfg)) {
+    const int G = Sf + 1;
+    int bits = resolve_hash_bits(cfg->top_k);
+    size_t lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G).total;
+    if (lds > prop.sharedMemPerBlock) {
+      bits -= 1;
+      lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G).total;
+    }
+    if (lds <= prop.sharedMemPerBlock) {
+      h->att_G = G;
+      h->att_hash_bits = bits;
+      h->att_lds = lds;
     }
   }
   // the limit is per kernel, not per handle: allow the device maximum once
@@ -345,6 +410,8 @@ void* hs_host_pool(hs_handle h, int32_t request) {
 
 int32_t hs_resolve_wgs(hs_handle h) { return h ? h->G : 0; }
 
+int32_t hs_resolve_attn_wgs(hs_handle h) { return h ? h->att_G : 0; }
+
 hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
                      int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs, uint32_t flags,
                      void* stream) {
@@ -360,19 +427,45 @@ hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int
     // the previous plan of this anchor must be replayed before it is overwritten
     HS_HIP(hipStreamWaitEvent(s, h->ev_plan_free[a], 0));
   }
-  ResolveParams p{};
-  p.sel = d_sel; p.ctx_len = d_ctx_len; p.out = d_slots_out; p.stats = d_stats; p.num_reqs = d_num_reqs;
-  p.ctrl = h->ctrl(a); p.slot_pos = h->slot_pos(a); p.lru = h->lru(a); p.plan = h->plan(a);
-  p.page_table = h->page_table(a); p.newest = h->newest(); p.host_base = h->host_base(); p.hot = h->hot;
-  p.host_layer_off = h->host_layer_off(layer); p.hot_req_stride = h->hot_req_stride();
-  p.hot_layer_off = h->hot_layer_off(layer); p.max_positions = h->cfg.max_positions;
-  p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad; p.k = h->cfg.top_k;
-  p.kb = h->cfg.top_k / h->cfg.block_tokens; p.bt_shift = ilog2(h->cfg.block_tokens);
-  p.rec_bytes = h->cfg.record_bytes; p.G = h->G; p.hash_bits = h->hash_bits;
-  p.flags = flags | ((h->cfg.flags & HS_CFG_NEWEST_SLOT) ? kHasNewest : 0u);
-  p.rtable = h->rtable; p.rt_stride = h->rt_stride; p.res_rows = h->res_rows; p.page_shift = h->page_shift;
-  p.plan_k = h->lay.kmax;
-  HS_HIP(launch_resolve(p, h->lds_bytes, s));
+  ResolveParams p = resolve_params(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags);
+  HS_HIP(launch_resolve(p, h->lds_bytes, s, h->next_timing()));
+  return HS_OK;
+}
+
+hs_status hs_resolve_attn(hs_handle h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
+                          int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs, uint32_t flags,
+                          const void* d_q, int32_t heads, int32_t value_dim, float* d_out, float scale,
+                          void* stream) {
+  hs_status st;
+  if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
+  if (flags & HS_SKIP_IO) return fail(HS_EINVAL, "hs_resolve_attn reads the records: HS_SKIP_IO is not allowed");
+  if (!h->att_G) {  // no fused kernel for this configuration: the same two calls in sequence
+    if ((st = hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, stream))) return st;
+    return hs_sparse_attn(h, layer, d_q, heads, value_dim, d_slots_out, d_out, scale, d_num_reqs, stream);
+  }
+  if (!h->is_anchor(layer))
+    return fail(HS_ESTATE, "layer %d shares its anchor's selection: use hs_prefetch_shared", layer);
+  if (!d_sel || !d_ctx_len || !d_slots_out) return fail(HS_EINVAL, "null selection, ctx_len or output");
+  if (flags & ~(HS_RECORD_PLAN | HS_SKIP_IO)) return fail(HS_EINVAL, "unknown resolve flags");
+  if (heads < 1 || heads > kAttnMaxHeads) return fail(HS_EINVAL, "heads must be in [1, %d]", kAttnMaxHeads);
+  if (value_dim != kAttnDv) return fail(HS_EINVAL, "value_dim must be %d", kAttnDv);
+  if (!d_q || !d_out) return fail(HS_EINVAL, "null q or output");
+  if ((uintptr_t)d_q % 16) return fail(HS_EINVAL, "q must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int a = layer / h->cfg.layer_group;
+  if ((flags & HS_RECORD_PLAN) && h->plan_free_pending[a]) HS_HIP(hipStreamWaitEvent(s, h->ev_plan_free[a], 0));
+  ResolveParams p = resolve_params(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags);
+  p.G = h->att_G; p.hash_bits = h->att_hash_bits;
+  p.q = (const uint16_t*)d_q; p.part = h->attn_part(layer); p.att_out = d_out;
+  p.att_res = h->res ? h->res + size_t(layer) * size_t(h->res_rows) * size_t(h->cfg.record_bytes) : nullptr;
+  p.heads = heads; p.att_scale = scale;
+  HS_HIP(launch_resolve_attn(p, h->att_lds, s, h->next_timing()));
+  if (h->att_G > 2) {  // the chunk partials of every (request, head) merged into the output
+    AttnParams m{};
+    m.out = d_out; m.part = h->attn_part(layer); m.num_reqs = d_num_reqs; m.R = h->cfg.num_requests;
+    m.heads = heads; m.value_dim = value_dim; m.S = h->att_G - 1; m.k = h->cfg.top_k;
+    HS_HIP(launch_attn_merge(m, s));
+  }
   return HS_OK;
 }
 
@@ -606,6 +699,36 @@ hs_status hs_probe_copy(const void* d_src, void* d_dst, size_t bytes, void* stre
   if (!d_src || !d_dst || bytes % 16) return fail(HS_EINVAL, "bad probe arguments");
   HS_HIP(launch_probe_copy(d_src, d_dst, bytes, (hipStream_t)stream));
   return HS_OK;
+}
+
+hs_status hs_timing_start(hs_handle h, int32_t n) {
+  hs_status st;
+  if ((st = check_handle(h))) return st;
+  if (n < 0 || n > (1 << 20)) return fail(HS_EINVAL, "n must be in [0, 2^20]");
+  free_timing(h);
+  h->tm.resize(n);
+  for (auto& t : h->tm) {
+    hipError_t e = hipEventCreate(&t.start);
+    if (e == hipSuccess) e = hipEventCreate(&t.stop);
+    if (e != hipSuccess) {
+      free_timing(h);
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  return HS_OK;
+}
+
+int32_t hs_timing_read(hs_handle h, float* us_out, int32_t n) {
+  if (!h || !us_out || n < 0) return fail(HS_EINVAL, "bad timing read arguments");
+  const size_t m = h->tm_next < size_t(n) ? h->tm_next : size_t(n);
+  for (size_t i = 0; i < m; ++i) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(h->tm[i].stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, h->tm[i].start, h->tm[i].stop);
+    if (e != hipSuccess) return hip_fail(e, "hs_timing_read");
+    us_out[i] = ms * 1e3f;
+  }
+  return (int32_t)m;
 }
 
 hs_status hs_probe_empty(void* stream) {

@@ -42,6 +42,27 @@ __host__ __device__ inline int32_t pt_slot_for(uint64_t e, uint32_t gen) {
   return (slot >= 0 && (uint32_t)(e >> 32) != gen) ? slot : -1;
 }
 
+// Max and sum over the 16 lanes of each DPP row of a wave (lanes 16q .. 16q+15), every lane
+// getting the result: lane ^ 1, lane ^ 2 (quad permutations), then the half-row and row
+// mirrors (lane i with 7 - i, then with 15 - i) combine quads and half-rows.  DPP moves
+// operands between lanes inside the ALU, without the LDS round trip of a shuffle.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  return v + dpp_mov<0x140>(v);
+}
+
 // 16-byte non-temporal access to the pinned host pool through global (not flat)
 // addresses.  The pool's device addresses come from a table in memory, so the compiler
 // cannot prove their address space and would emit flat instructions, which also count
@@ -85,6 +106,29 @@ __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits, i
 }
 int resolve_elems_per_thread(int k, int B);
 
+// Fused RESOLVE + attention (one tile of <= 64 selected records per fetch workgroup): the
+// resolve carve-up, then the record tile, the query rows, and per tile row the miss's list
+// index and the record's address.  The
+// attention scratch (scores' maxima and sums, P) reuses the start of the resolve region once
+// stage 3 is done with it.
+constexpr int kTileRows = 64;        // records per fetch workgroup
+constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (292 words): the 16 rows
+                                     // of a QK^T operand read fall on 16 distinct 4-bank groups, and
+                                     // the quarter-waves of a P V operand read on disjoint banks
+constexpr int kQStride = 1168;       // LDS stride of a query row (16-byte aligned, off the bank period)
+struct FusedLds {
+  size_t tile, qs, arow, asrc, total;
+};
+__host__ __device__ inline FusedLds fused_lds(int k, int B, int hash_bits, int G) {
+  FusedLds F;
+  F.tile = align_up(resolve_lds(k, B, hash_bits, G).total, 16);
+  F.qs = F.tile + size_t(kTileRows) * kTileStride;
+  F.arow = F.qs + 16 * size_t(kQStride);
+  F.asrc = F.arow + 4 * size_t(kTileRows);
+  F.total = align_up(F.asrc + 8 * size_t(kTileRows), 16);
+  return F;
+}
+
 // Per-anchor metadata in the caller's workspace.  ctrl per request (uint32 x 4):
 // [0..1] 64-bit launch counter (launch_number() of it numbers the launches that changed
 // the metadata; its parity names the ping-pong half holding the current slot map and LRU
@@ -117,6 +161,14 @@ struct ResolveParams {
   int32_t page_shift;        // log2 tokens per resident page
   int32_t R, B, Bpad, k, kb, bt_shift, rec_bytes, G, hash_bits;
   uint32_t flags;            // HS_RECORD_PLAN | HS_SKIP_IO | kHasNewest
+  // fused attention (resolve_kernel<.., true>): G - 1 fetch workgroups per request, each
+  // attends over its share of the selection (<= 64 entries)
+  const uint16_t* q;         // [R][heads][576] bf16
+  float* part;               // [R][G-1][kPartStride] chunk partials (G > 2)
+  float* att_out;            // [R][heads][512] (written directly when G == 2)
+  const uint8_t* att_res;    // this layer's resident pool [res_rows][rec] (null without one)
+  int32_t heads;
+  float att_scale;
 };
 
 struct AppendParams {
@@ -212,7 +264,16 @@ struct InitParams {
   int32_t R, B, Bpad, A, request;  // request < 0: all
 };
 
-hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s);
+// Optional kernel timing of one launch: events stamped by the kernel's own start and end
+// (hipExtLaunchKernel), for the measurement aid hs_timing_start / hs_timing_read.
+struct KernelTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s, const KernelTiming* tm = nullptr);
+// the fused variant; false when no instantiation covers (k, B) (top_k <= 4096, B <= 8192)
+bool fused_supported(int k, int B);
+hipError_t launch_resolve_attn(const ResolveParams& p, size_t lds_bytes, hipStream_t s,
+                               const KernelTiming* tm = nullptr);
 hipError_t launch_union(const UnionParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 size_t union_lds_bytes(int hash_bits);
@@ -223,6 +284,7 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_backup(const AppendParams& p, hipStream_t s);
 hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s);  // the S chunk partials -> out
 hipError_t launch_export(const ExportParams& p, hipStream_t s);
 hipError_t launch_init(const InitParams& p, hipStream_t s);
 hipError_t launch_admit(const AdmitParams& p, hipStream_t s);

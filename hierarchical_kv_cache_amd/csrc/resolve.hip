@@ -50,6 +50,8 @@
 // as vectors; hash insertion uses plain LDS stores and a read-back instead
 // of atomics (which the LDS serialises lane by lane); all probes of a thread
 // are in flight together; two two-field rank scans order everything.
+#include <hip/hip_ext.h>
+
 #include "hs_internal.h"
 
 namespace hs {
@@ -71,6 +73,13 @@ __device__ __forceinline__ uint32_t hash_pos(int32_t pos, int bits) {
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// This wave's vector-memory operations complete (vmcnt 0).
+__device__ __forceinline__ void vm_wait() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Exclusive block-wide ranks for two flag sets at once.  Thread t owns elements
@@ -161,11 +170,172 @@ __device__ __forceinline__ void load_run16(const int16_t* __restrict__ src, int 
   for (int j = 0; j < E; ++j) out[j] = (base + j < n) ? src[base + j] : fill;
 }
 
+// The fused path's record tile: 64 rows of 72 16-byte chunks.  Thread t holds chunks t,
+// t + NT, ... (row f / 72, chunk f % 72) in registers from their loads until the tile is
+// written to LDS after stage 3, so the loads fly while stages 1-3 run.  (Loads straight
+// into LDS made the stages' LDS waits wait for them as well.)  Non-temporal: every record
+// is read once per launch.
+constexpr int kRowChunks = kAttnDk / 8;               // 16-byte chunks per 1152-byte record
+constexpr int kTileChunks = kTileRows * kRowChunks;   // 4608
+constexpr int kTU = (kTileChunks + NT - 1) / NT;      // chunks per thread
+constexpr int kQChunks = 16 * kRowChunks;             // query rows of 16 heads
+constexpr int kQU = (kQChunks + NT - 1) / NT;
+
+// row addresses in LDS (asrc[row]) -> this thread's chunks of the tile
+__device__ __forceinline__ void tile_load(u32x4 (&tv)[kTU], const uint64_t* asrc) {
+#pragma unroll
+  for (int u = 0; u < kTU; ++u) {
+    const int f = threadIdx.x + u * NT;
+    if (f < kTileChunks) {
+      const int row = f / kRowChunks, c = f - row * kRowChunks;
+      tv[u] = load_host16((const uint8_t*)asrc[row] + 16 * c);
+    }
+  }
+}
+__device__ __forceinline__ void tile_store(const u32x4 (&tv)[kTU], unsigned char* tile) {
+#pragma unroll
+  for (int u = 0; u < kTU; ++u) {
+    const int f = threadIdx.x + u * NT;
+    if (f < kTileChunks) {
+      const int row = f / kRowChunks, c = f - row * kRowChunks;
+      *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
+    }
+  }
+}
+// the query rows of request r (rows past `heads`: zeros)
+__device__ __forceinline__ void q_load(u32x4 (&qv)[kQU], const uint16_t* q, int r, int heads) {
+#pragma unroll
+  for (int u = 0; u < kQU; ++u) {
+    const int f = threadIdx.x + u * NT;
+    const int h = f / kRowChunks, c = f - h * kRowChunks;
+    qv[u] = (f < kQChunks && h < heads) ? load_host16((const uint8_t*)(q + ((size_t)r * heads + h) * kAttnDk) + 16 * c)
+                                        : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+__device__ __forceinline__ void q_store(const u32x4 (&qv)[kQU], unsigned char* qs) {
+#pragma unroll
+  for (int u = 0; u < kQU; ++u) {
+    const int f = threadIdx.x + u * NT;
+    const int h = f / kRowChunks, c = f - h * kRowChunks;
+    if (f < kQChunks) *(u32x4*)(qs + (size_t)h * kQStride + 16 * c) = qv[u];
+  }
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (finite inputs)
+  return (uint16_t)(u >> 16);
+}
+
+// Attention of the 16 query heads over one tile of n_tok records held in LDS (sparse decode
+// attention, "HiSparse 深度解析" (gentlecold.top) §5.4: the records of the published slots;
+// key = the record's 576 bf16, value = its first 512).  Waves 0-3 compute the 16 x 16 score
+// blocks of tokens 16w .. 16w+15 on v_mfma_f32_16x16x32_bf16 (18 k-steps), every head's
+// maximum and sum over the tile follow, and all 16 waves accumulate P V for 32 output
+// channels each.  P is split into bf16 hi + lo parts so the fp32 probabilities survive the
+// bf16 operand.  Writes the chunk's partial (unnormalised o, max and sum in log2 units) for
+// the merge, or the normalised output when the request has one chunk.
+__device__ __forceinline__ void attend_tile(const unsigned char* tile, const unsigned char* qs,
+                                            unsigned char* scratch, int n_tok, float sl2, float* part,
+                                            float* out, int heads) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, qd = lane >> 4;
+  float* smax = (float*)scratch;                 // [4][16]
+  float* ssum = smax + 64;                       // [4][16]
+  uint16_t* phi = (uint16_t*)(ssum + 64);        // [2 token blocks][16 heads][32]
+  uint16_t* plo = phi + 2 * 16 * 32;
+  constexpr int KSTEPS = kAttnDk / 32;
+  float sv[4];
+  if (w < 4) {
+    // lane: s[head = 4 qd + i][token = 16 w + col]; two accumulators halve the dependent
+    // MFMA chain
+    f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+    const unsigned char* krow = tile + (16 * w + col) * kTileStride + qd * 16;
+    const unsigned char* qrow = qs + col * kQStride + qd * 16;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks += 2) {
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64), *(const bf16x8*)(krow + ks * 64),
+                                                   sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64 + 64),
+                                                   *(const bf16x8*)(krow + ks * 64 + 64), sb, 0, 0, 0);
+    }
+    const bool valid = 16 * w + col < n_tok;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = valid ? (sa[i] + sb[i]) * sl2 : -INFINITY;
+      const float mx = row16_max(sv[i]);
+      if (col == 0) smax[w * 16 + qd * 4 + i] = mx;
+    }
+  }
+  __syncthreads();
+  if (w < 4) {
+    const int tl = 16 * w + col;
+    const int bk = tl >> 5, t32 = tl & 31;
+    const int kk = (t32 & 3) * 8 + (t32 >> 2);  // P V operands pair k index 8 qd + j with token 4 j + qd
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = qd * 4 + i;
+      const float m = fmaxf(fmaxf(smax[hh], smax[16 + hh]), fmaxf(smax[32 + hh], smax[48 + hh]));
+      const float pv = exp2f(sv[i] - m);
+      const float l = row16_sum(pv);
+      if (col == 0) ssum[w * 16 + hh] = l;
+      const uint16_t hi = f32_to_bf16_rne(pv);
+      phi[(bk * 16 + hh) * 32 + kk] = hi;
+      plo[(bk * 16 + hh) * 32 + kk] = f32_to_bf16_rne(pv - __uint_as_float((uint32_t)hi << 16));
+    }
+  }
+  __syncthreads();
+  // o[head][channel] = p v over the tile; wave w owns channels 32 w .. 32 w + 31
+  f32x4 o[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const bf16x8 ahi = *(const bf16x8*)&phi[(b * 16 + col) * 32 + qd * 8];
+    const bf16x8 alo = *(const bf16x8*)&plo[(b * 16 + col) * 32 + qd * 8];
+    const unsigned char* vb = tile + (b * 32 + qd) * kTileStride + (32 * w + col) * 2;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 vv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vv[j] = *(const __bf16*)(vb + 4 * j * kTileStride + c * 32);
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, vv, o[c], 0, 0, 0);
+      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vv, o[c], 0, 0, 0);
+    }
+  }
+  // o[c][i]: head 4 qd + i, channel 32 w + 16 c + col
+  if (out) {  // one chunk: normalise and write the output rows of the heads asked for
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = qd * 4 + i;
+      if (hh >= heads) continue;
+      const float inv = 1.0f / (ssum[hh] + ssum[16 + hh] + ssum[32 + hh] + ssum[48 + hh]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) out[hh * kAttnDv + 32 * w + 16 * c + col] = o[c][i] * inv;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) part[(qd * 4 + i) * kAttnDv + 32 * w + 16 * c + col] = o[c][i];
+  if (tid < 16) {
+    part[16 * kAttnDv + tid] = fmaxf(fmaxf(smax[tid], smax[16 + tid]), fmaxf(smax[32 + tid], smax[48 + tid]));
+    part[16 * kAttnDv + 16 + tid] = ssum[tid] + ssum[16 + tid] + ssum[32 + tid] + ssum[48 + tid];
+  }
+}
+
+// Outcome of the resolve part of a workgroup: nothing more to do, or (fused attention) a
+// record tile to attend over, or an error that makes the request's attention output NaN.
+constexpr int kDone = 0, kTile = 1, kError = 2;
+
 // E: slots (and LRU positions) per thread, KE: selection entries per thread (both powers
-// of two, KE <= E, EK = ceil(k / NT) <= KE).
-template <int E, int KE>
-__global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// of two, KE <= E, EK = ceil(k / NT) <= KE).  ATT: fused attention -- every fetch workgroup
+// also loads its share of the selected records (<= 64) into an LDS tile, straight from the
+// hot slots, the resident pool or (misses) the host pool, and the misses go from the tile to
+// their victim slots.
+template <int E, int KE, bool ATT>
+__device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned char* smem) {
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits, p.G);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
   int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] position (hash key) of each entry
@@ -188,7 +358,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   if (p.num_reqs && r >= *p.num_reqs) {
     // a padded request: untouched, and an empty plan so a replay copies nothing
     if (record && g == 0 && tid == 0) p.ctrl[r * 4 + 2] = 0;
-    return;
+    return kDone;
   }
   const int H = 1 << p.hash_bits;
   const uint32_t hmask = (uint32_t)H - 1;
@@ -207,7 +377,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
     }
-    return;
+    return kDone;
   }
 
   // ---- every global read up front -------------------------------------------------------
@@ -229,6 +399,51 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
     raw[j] = (j < EK && i < kr) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
+  }
+  // Fetch workgroups (all but workgroup 0 when G > 1) also read the selection entries of
+  // their share of the list, spread over the waves: entry e of the share belongs to wave
+  // e % NW, lane (e / NW) % 64, slot e / NT.
+  const bool io = !(p.flags & HS_SKIP_IO);
+  const bool fetcher = io && (p.G == 1 || g > 0);
+  const int nf = p.G > 1 ? p.G - 1 : 1;
+  const int gf = p.G > 1 ? g - 1 : 0;
+  // (32-bit: k * G < 2^23)
+  const int f_lo = kr * gf / nf;
+  const int f_n = kr * (gf + 1) / nf - f_lo;
+  const int wid = tid >> 6, lane = tid & 63;
+  // (loaded here by the fused variant, whose short path needs them; later otherwise, which
+  // keeps them out of the registers live across the entry loads)
+  int32_t fraw[KE];
+  auto load_share = [&]() {
+#pragma unroll
+    for (int q = 0; q < KE; ++q) {
+      const int e = q * NT + lane * NW + wid;
+      const int i = f_lo + e;
+      fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
+    }
+  };
+  if constexpr (ATT) load_share();
+  const uint8_t* hbase = nullptr;  // this (request, layer)'s host records
+  uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+  unsigned char* tile = smem;
+  unsigned char* qs = smem;
+  uint64_t* asrc = nullptr;  // fused: record address of each tile row
+  int32_t* arow = nullptr;   // fused: list index of the miss in each tile row, -1 otherwise
+  const uint8_t* filler = nullptr;
+  u32x4 qv[kQU], tv[kTU];
+  if constexpr (ATT) {
+    const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G);
+    tile = smem + F.tile;
+    qs = smem + F.qs;
+    arow = (int32_t*)(smem + F.arow);
+    asrc = (uint64_t*)(smem + F.asrc);
+    // a row without a record (past the share, or an entry in error) is loaded from the first
+    // query row: any finite bytes do, its score is masked and only its value row must be finite
+    filler = (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);
+    if (g > 0) {
+      hbase = p.host_base[r] + p.host_layer_off;
+      q_load(qv, p.q, r, p.heads);  // the query rows, in LDS once the entry loads are in
+    }
   }
   // ---- short-sequence fast path ("HiSparse 深度解析" §5.4, §5.5): a request admitted short
   // keeps its tokens in slot order while its context fits B, so every position is its own
@@ -266,7 +481,28 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
     }
-    return;
+    if constexpr (ATT) {
+      if (g > 0) {
+        if (bad) return kError;
+        // slot = position: the share's records straight from the hot slots
+        q_store(qv, qs);
+        if (lane < kTileRows / NW) {
+          const uint8_t* src = filler;
+          if (fraw[0] >= 0) {
+            const int e = lane * NW + wid, i = f_lo + e;
+            const int64_t pos64 = p.bt_shift ? ((int64_t)fraw[0] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                             : (int64_t)fraw[0];
+            src = dbase + (size_t)pos64 * p.rec_bytes;
+          }
+          asrc[lane * NW + wid] = (uint64_t)src;
+        }
+        __syncthreads();
+        tile_load(tv, asrc);
+        tile_store(tv, tile);
+        return kTile;
+      }
+    }
+    return kDone;
   }
   // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
   // map, so it names the slot of a hit) and, with a resident tier, its resident page.
@@ -283,23 +519,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
     ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
     rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
-  // Fetch workgroups (all but workgroup 0 when G > 1) also read the selection entries of
-  // their share of the list, spread over the waves: entry e of the share belongs to wave
-  // e % NW, lane (e / NW) % 64, slot e / NT.
-  const bool io = !(p.flags & HS_SKIP_IO);
-  const bool fetcher = io && (p.G == 1 || g > 0);
-  const int nf = p.G > 1 ? p.G - 1 : 1;
-  const int gf = p.G > 1 ? g - 1 : 0;
-  const int f_lo = (int)((int64_t)kr * gf / nf);
-  const int f_n = (int)((int64_t)kr * (gf + 1) / nf) - f_lo;
-  const int wid = tid >> 6, lane = tid & 63;
-  int32_t fraw[KE];
-#pragma unroll
-  for (int q = 0; q < KE; ++q) {
-    const int e = q * NT + lane * NW + wid;
-    const int i = f_lo + e;
-    fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
-  }
+  if constexpr (!ATT) load_share();
   const bool bvec = (p.B % E) == 0;
   int32_t spa[E], spb[E];
   int16_t lra[E], lrb[E];
@@ -361,6 +581,44 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   int32_t pts[KE];
 #pragma unroll
   for (int j = 0; j < KE; ++j) pts[j] = pt_slot_for(ptv[j], gen);
+  if constexpr (ATT) {
+    // Every load of the entry phase has landed (all of them are needed by now or soon), so
+    // the only loads in flight from here on are the tile's, and no wait the compiler places
+    // for an earlier load can hold up on them.  In every workgroup: the compiler merges the
+    // paths of workgroup 0 and the fetch workgroups.
+    vm_wait();
+    if (g > 0) {
+      q_store(qv, qs);
+      // The record of each share entry, classified as stage 1 will classify it: resident
+      // row, newest slot, hit slot, or (a miss) the host record.  The loads fly while
+      // stages 1-3 run.
+      if (lane < kTileRows / NW) {
+        const uint8_t* src = filler;
+        int32_t mi = -1;
+        if (fpos[0] >= 0) {
+          const int32_t pos = fpos[0];
+          if (fres[0] >= 0) {
+            const int64_t row = ((int64_t)fres[0] << p.page_shift) + (pos & (((int64_t)1 << p.page_shift) - 1));
+            if (row < p.res_rows) src = p.att_res + (size_t)row * p.rec_bytes;
+          } else if (pos == newest) {
+            src = dbase + (size_t)p.B * p.rec_bytes;
+          } else {
+            const int32_t sl = pt_slot_for(fpt[0], gen);
+            if (sl < 0) {
+              src = hbase + (size_t)pos * p.rec_bytes;
+              mi = f_lo + lane * NW + wid;
+            } else if (sl < p.B) {
+              src = dbase + (size_t)sl * p.rec_bytes;
+            }
+          }
+        }
+        asrc[lane * NW + wid] = (uint64_t)src;
+        arow[lane * NW + wid] = mi;
+      }
+      __syncthreads();
+      tile_load(tv, asrc);
+    }
+  }
 
   // ---- resident tier: a selection that is resident throughout returns here ---------------
   int nres = 0;
@@ -385,7 +643,11 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
         }
         if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
       }
-      return;
+      if (ATT && g > 0) {
+        tile_store(tv, tile);
+        return kTile;
+      }
+      return kDone;
     }
   }
 
@@ -492,7 +754,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
   const float invC = 1.0f / (float)C;
   int mw = 0;  // misses of this wave
-  {
+  if constexpr (!ATT) {
 #pragma unroll
     for (int q = 0; q < KE; ++q) {
       const bool miss = fpos[q] >= 0 && fpos[q] != newest && fres[q] < 0 && pt_slot_for(fpt[q], gen) < 0;
@@ -507,14 +769,15 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
-  uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+  if constexpr (!ATT) {
+    if (fetcher) hbase = p.host_base[r] + p.host_layer_off;
+  }
   const int wtotal = mw * C;  // 16-byte chunks of this wave's misses
   u32x4 early[kEarly];
 #pragma unroll
   for (int u = 0; u < kEarly; ++u) {
     const int c = lane + 64 * u;
-    if (c < wtotal) {
+    if (!ATT && c < wtotal) {
       int l = (int)((float)c * invC);
       int cc = c - l * C;
       if (cc < 0) { --l; cc += C; }
@@ -541,7 +804,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
     }
-    return;
+    return (ATT && g > 0) ? kError : kDone;
   }
   // this launch changes the metadata: the next one finds it in the other half (the shares
   // of the G workgroups add up to one launch unit)
@@ -663,7 +926,23 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       }
       if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;
     }
-    if (p.G > 1) return;
+    if (p.G > 1) return kDone;
+  }
+
+  if constexpr (ATT) {
+    // ---- stage 4 (fused): the tile goes to LDS, its missed records to their victim slots ----
+#pragma unroll
+    for (int u = 0; u < kTU; ++u) {
+      const int f = tid + u * NT;
+      if (f < kTileChunks) {
+        const int row = f / kRowChunks, c = f - row * kRowChunks;
+        *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
+        const int a = arow[row];
+        if (a >= 0) *((u32x4*)(dbase + (size_t)victim[mrank[a]] * (size_t)p.rec_bytes) + c) = tv[u];
+      }
+    }
+    __syncthreads();  // the tile is complete, the resolve region free for the attention scratch
+    return kTile;
   }
 
   // ---- stage 4, second part: the fetched records go to the slots stage 3 chose --------
@@ -702,6 +981,32 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
         if (c0 + 64 * u < wtotal)
           *((u32x4*)(dbase + (size_t)victim[mrank[widx[ll[u]]]] * (size_t)p.rec_bytes) + cc[u]) = v[u];
     }
+  }
+  return kDone;
+}
+
+template <int E, int KE, bool ATT>
+__global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int outcome = resolve_body<E, KE, ATT>(p, smem);
+  if constexpr (ATT) {
+    if (outcome == kDone) return;
+    // fetch workgroup g >= 1 attends over its share (chunk g - 1) of the selection
+    const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
+    const int S = p.G - 1;
+    const int f_lo = p.k * (g - 1) / S;
+    const int n_tok = p.k * g / S - f_lo;
+    const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G);
+    float* part = p.part + ((size_t)r * S + (g - 1)) * kPartStride;
+    float* out = S == 1 ? p.att_out + (size_t)r * p.heads * kAttnDv : nullptr;
+    __syncthreads();  // the tile and the query rows are in LDS
+    if (outcome == kError) {  // the request's output is NaN, as for unresolved slots
+      const float nan = __builtin_nanf("");
+      if (out) for (int f = threadIdx.x; f < p.heads * kAttnDv; f += NT) out[f] = nan;
+      else for (int f = threadIdx.x; f < kPartStride; f += NT) part[f] = nan;
+      return;
+    }
+    attend_tile(smem + F.tile, smem + F.qs, smem, n_tok, p.att_scale * 1.4426950408889634f, part, out, p.heads);
   }
 }
 
@@ -819,20 +1124,33 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterParams p) {
   p.out[t] = (p.err[r] || u < 0) ? -1 : p.uout[(size_t)r * p.kmax + u];
 }
 
-template <int E, int KE>
-hipError_t launch_e(const ResolveParams& p, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((resolve_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), lds, s, p);
+template <int E, int KE, bool ATT>
+hipError_t launch_e(const ResolveParams& p, size_t lds, hipStream_t s, const KernelTiming* tm) {
+  if (tm && tm->start) {
+    hipExtLaunchKernelGGL((resolve_kernel<E, KE, ATT>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, tm->start,
+                          tm->stop, 0u, p);
+  } else {
+    hipLaunchKernelGGL((resolve_kernel<E, KE, ATT>), dim3(p.R * p.G), dim3(NT), lds, s, p);
+  }
   return hipGetLastError();
 }
 
-template <int E>
-hipError_t launch_ke(const ResolveParams& p, size_t lds, hipStream_t s, int KE) {
-  if constexpr (E >= 1) if (KE <= 1) return launch_e<E, 1>(p, lds, s);
-  if constexpr (E >= 2) if (KE <= 2) return launch_e<E, 2>(p, lds, s);
-  if constexpr (E >= 4) if (KE <= 4) return launch_e<E, 4>(p, lds, s);
-  if constexpr (E >= 8) if (KE <= 8) return launch_e<E, 8>(p, lds, s);
-  if constexpr (E >= 16) return launch_e<E, 16>(p, lds, s);
-  return hipErrorInvalidValue;
+// The fused variant exists for KE <= 4 and E <= 8 (top_k <= 4096, B <= 8192): larger lists
+// leave no LDS for the record tile.
+constexpr int kFusedMaxE = 8, kFusedMaxKE = 4;
+
+template <int E, bool ATT>
+hipError_t launch_ke(const ResolveParams& p, size_t lds, hipStream_t s, int KE, const KernelTiming* tm) {
+  if constexpr (ATT && E > kFusedMaxE) {
+    return hipErrorInvalidValue;
+  } else {
+    if constexpr (E >= 1) if (KE <= 1) return launch_e<E, 1, ATT>(p, lds, s, tm);
+    if constexpr (E >= 2) if (KE <= 2) return launch_e<E, 2, ATT>(p, lds, s, tm);
+    if constexpr (E >= 4) if (KE <= 4) return launch_e<E, 4, ATT>(p, lds, s, tm);
+    if constexpr (!ATT && E >= 8) if (KE <= 8) return launch_e<E, 8, ATT>(p, lds, s, tm);
+    if constexpr (!ATT && E >= 16) return launch_e<E, 16, ATT>(p, lds, s, tm);
+    return hipErrorInvalidValue;
+  }
 }
 
 // Maximum dynamic LDS of a kernel: the device's per-block LDS less the kernel's static LDS.
@@ -846,11 +1164,16 @@ hipError_t set_dynamic_lds(const void* fn, int v) {
 template <int E>
 hipError_t set_limit_ke(int v) {
   hipError_t e = hipSuccess;
-  if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1>, v);
-  if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 2>, v);
-  if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 4>, v);
-  if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 8>, v);
-  if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 16>, v);
+  if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1, false>, v);
+  if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 2, false>, v);
+  if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 4, false>, v);
+  if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 8, false>, v);
+  if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 16, false>, v);
+  if constexpr (E <= kFusedMaxE) {
+    if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1, true>, v);
+    if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 2, true>, v);
+    if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 4, true>, v);
+  }
   return e;
 }
 
@@ -897,14 +1220,29 @@ hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s) {
+hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s, const KernelTiming* tm) {
   const int KE = pow2_at_least((p.k + NT - 1) / NT);
   switch (resolve_elems_per_thread(p.k, p.B)) {
-    case 1: return launch_ke<1>(p, lds_bytes, s, KE);
-    case 2: return launch_ke<2>(p, lds_bytes, s, KE);
-    case 4: return launch_ke<4>(p, lds_bytes, s, KE);
-    case 8: return launch_ke<8>(p, lds_bytes, s, KE);
-    default: return launch_ke<16>(p, lds_bytes, s, KE);
+    case 1: return launch_ke<1, false>(p, lds_bytes, s, KE, tm);
+    case 2: return launch_ke<2, false>(p, lds_bytes, s, KE, tm);
+    case 4: return launch_ke<4, false>(p, lds_bytes, s, KE, tm);
+    case 8: return launch_ke<8, false>(p, lds_bytes, s, KE, tm);
+    default: return launch_ke<16, false>(p, lds_bytes, s, KE, tm);
+  }
+}
+
+bool fused_supported(int k, int B) {
+  return resolve_elems_per_thread(k, B) <= kFusedMaxE && pow2_at_least((k + NT - 1) / NT) <= kFusedMaxKE;
+}
+
+hipError_t launch_resolve_attn(const ResolveParams& p, size_t lds_bytes, hipStream_t s, const KernelTiming* tm) {
+  const int KE = pow2_at_least((p.k + NT - 1) / NT);
+  switch (resolve_elems_per_thread(p.k, p.B)) {
+    case 1: return launch_ke<1, true>(p, lds_bytes, s, KE, tm);
+    case 2: return launch_ke<2, true>(p, lds_bytes, s, KE, tm);
+    case 4: return launch_ke<4, true>(p, lds_bytes, s, KE, tm);
+    case 8: return launch_ke<8, true>(p, lds_bytes, s, KE, tm);
+    default: return hipErrorInvalidValue;
   }
 }
 

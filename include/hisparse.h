@@ -233,6 +233,28 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
                          int32_t value_dim, const int32_t* d_slots, float* d_out, float scale,
                          const int32_t* d_num_reqs, void* stream);
 
+/*
+ * RESOLVE of one anchor layer and the sparse attention over its published slots, in one
+ * kernel where the configuration allows ([GC] §3.5 for the resolve, §5.4 for the attention
+ * that reads the slots aligned with the top-k order).  Results are those of
+ *   hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, stream);
+ *   hs_sparse_attn(h, layer, d_q, heads, value_dim, d_slots_out, d_out, scale, d_num_reqs, stream);
+ * with the same arguments: the same slots, counts, metadata and hot bytes bit for bit, the
+ * same attention up to the order of the fp32 sums.  The fused kernel gives every 64
+ * selected entries of a request a workgroup that loads their records (hot slot, resident
+ * row or, for a miss, the host record) into LDS while the resolve stages run, stores the
+ * misses into their victim slots and attends over the records it holds; a merge kernel then
+ * combines the chunks of each (request, head).  It applies to bf16 records of 576 values
+ * (record_bytes 1152), top_k <= 4096, buffer_slots <= 8192 and num_requests *
+ * (ceil(top_k / 64) + 1) <= 256 (hs_resolve_attn_wgs > 0); otherwise this call makes the
+ * two calls above.  HS_SKIP_IO is not allowed (the attention reads the records).  Errors as
+ * for the two calls; a request with error bits gets NaN output rows.
+ */
+hs_status hs_resolve_attn(hs_handle h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
+                          int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs, uint32_t flags,
+                          const void* d_q, int32_t heads, int32_t value_dim, float* d_out, float scale,
+                          void* stream);
+
 /* Copies the current metadata of an anchor layer into caller buffers (device):
  * d_slot_pos [R][B] position held by each slot (-1 empty), d_lru [R][B] slots
  * from least to most recent, d_newest [R] newest position (-1 none).  Any may be NULL. */
@@ -277,6 +299,9 @@ const char* hs_last_error(void);
 /* Workgroups per request hs_resolve launches for this handle. */
 int32_t hs_resolve_wgs(hs_handle h);
 
+/* Workgroups per request of the fused kernel of hs_resolve_attn (0: the call makes two). */
+int32_t hs_resolve_attn_wgs(hs_handle h);
+
 /* ---- measurement aids (no part of the cache) ---------------------------------------------- */
 
 /* Streams `bytes` of pinned host memory through the GPU with 16-byte non-temporal loads from
@@ -287,6 +312,15 @@ hs_status hs_probe_host_read(const void* host_src, size_t bytes, void* d_sink, i
 hs_status hs_probe_copy(const void* d_src, void* d_dst, size_t bytes, void* stream);
 /* An empty kernel (launch-latency probe). */
 hs_status hs_probe_empty(void* stream);
+
+/* Kernel durations of the next n RESOLVE launches of h (hs_resolve's kernel, or the fused
+ * kernel of hs_resolve_attn; not the merge), stamped by the kernels' own start and end
+ * (hipExtLaunchKernel events), so no event between launches adds to them.  hs_timing_start
+ * creates n event pairs (dropping earlier ones); launches beyond n are not timed. */
+hs_status hs_timing_start(hs_handle h, int32_t n);
+/* Waits for the timed launches and writes the first min(n, launched) durations in
+ * microseconds, in launch order, to host memory us_out; returns that count (< 0: error). */
+int32_t hs_timing_read(hs_handle h, float* us_out, int32_t n);
 
 #ifdef __cplusplus
 }

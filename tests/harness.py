@@ -27,7 +27,7 @@ class Pair:
 
     def __init__(self, w: synth.Workload, steps: int | None = None, wgs: int = 0, all_hit=False,
                  oracle_host_copy: bool | None = None, compare_hot=True, resident: ResidentSpec | None = None,
-                 fp8: bool = False, rows: int = 1):
+                 fp8: bool = False, rows: int = 1, fused_heads: int = 0):
         self.w = w
         self.steps = w.steps if steps is None else steps
         self.lmax = w.max_positions(self.steps)
@@ -66,6 +66,12 @@ class Pair:
         # selection traces, resident on the device: [steps][anchors][R][kb], or with
         # speculative verification rows [steps][anchors][R][rows][kb]
         self.rows = rows
+        # fused RESOLVE + attention (hs_resolve_attn) with this many query heads; 0: hs_resolve
+        self.fused_heads = fused_heads
+        self.worst_attn = 0.0
+        if fused_heads:
+            self.d_att = torch.empty((len(self.anchors_of(w)), w.R, fused_heads, 512), dtype=torch.float32,
+                                     device=self.dev)
         if rows > 1:
             from synth.traces import verify_rows
             tr = np.stack([np.stack([verify_rows(w, r, l, self.steps, rows) for r in range(w.R)], axis=1)
@@ -107,6 +113,10 @@ class Pair:
         self.d_table = torch.full((w.R, self.n_pages), -1, dtype=torch.int32, device=self.dev)
         hk.hs_bind_resident(self.h, self.d_table.data_ptr(), self.n_pages, P, self.d_res.data_ptr(), self.res_rows)
 
+    @staticmethod
+    def anchors_of(w):
+        return [l for l in range(w.L) if l % w.group == 0]
+
     def table(self, t):
         return np.where(self.masks[t], self.phys, -1).astype(np.int32)
 
@@ -137,6 +147,9 @@ class Pair:
         d_nr = None
         if num_reqs is not None:
             d_nr = torch.tensor([num_reqs], dtype=torch.int32, device=self.dev)
+        if self.fused_heads:
+            q = synth.queries(w.R, w.L, t, heads=self.fused_heads)
+            d_q = torch.from_numpy(q.view(np.int16)).to(self.dev)
         for ai, l in enumerate(self.anchors):
             d_sel = self.d_trace[t, ai]
             fl = flags | (hk.HS_RECORD_PLAN if w.group > 1 else 0)
@@ -144,6 +157,13 @@ class Pair:
                 hk.hs_resolve_rows(self.h, l, self.rows, d_sel.data_ptr(), d_ctx.data_ptr(), self.d_out[ai].data_ptr(),
                                    self.d_stats.data_ptr(), d_nr.data_ptr() if d_nr is not None else 0, fl,
                                    self.compute.cuda_stream)
+            elif self.fused_heads:
+                dq = d_q[:, l].contiguous()
+                hk.hs_resolve_attn(self.h, l, d_sel.data_ptr(), d_ctx.data_ptr(), self.d_out[ai].data_ptr(),
+                                   self.d_stats.data_ptr(), d_nr.data_ptr() if d_nr is not None else 0, fl,
+                                   dq.data_ptr(), self.fused_heads, 512, self.d_att[ai].data_ptr(), SCALE,
+                                   self.compute.cuda_stream)
+                self._keep_q = dq
             else:
                 hk.hs_resolve(self.h, l, d_sel.data_ptr(), d_ctx.data_ptr(), self.d_out[ai].data_ptr(),
                               self.d_stats.data_ptr(), d_nr.data_ptr() if d_nr is not None else 0, fl,
@@ -188,10 +208,26 @@ class Pair:
                         raise AssertionError("slots differ at step %d r %d l %d: %d entries, first %s"
                                              % (t, r, l, bad.size, [(int(i), int(got[r][i]), int(exp[i]))
                                                                       for i in bad[:5]]))
+                if self.fused_heads:
+                    self._check_attention(t, ai, l, q, nr)
         for l in range(w.L):
             hk.hs_wait_layer(self.h, l, self.compute.cuda_stream)
         self.t += 1
         return results
+
+    def _check_attention(self, t, ai, l, q, nr):
+        """Fused attention output against float64 attention over the records of the selected
+        positions (every selected entry's slot holds its position's bytes)."""
+        w = self.w
+        att = self.d_att[ai].cpu().numpy()
+        for r in range(nr):
+            pos = expand(self.trace[t, ai, r], w.block_tokens)
+            rows = np.ascontiguousarray(self.ohost[r][l][pos.astype(np.int64)]).view(np.uint16)
+            K = oracle.attention.bf16_to_f64(rows)
+            ref = oracle.attention.sparse_decode_attention_rows(q[r, l], K, SCALE)
+            err = np.abs(att[r] - ref).max() / np.abs(ref).max()
+            self.worst_attn = max(self.worst_attn, err)
+            assert err <= 2e-3, ("attention", t, r, l, err)
 
     # ---- state comparison ---------------------------------------------------------------
     def check_state(self, layers=None, hot=True, page_table=True, requests=None):

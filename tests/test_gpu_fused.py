@@ -1,0 +1,227 @@
+"""hs_resolve_attn: RESOLVE and the sparse attention over the published slots in one kernel.
+
+Every step: slots, counts and (at the end) the slot map, LRU order, page table and hot
+bytes bit for bit against the oracle, as for hs_resolve; the attention output within
+2e-3 * max|o_ref| of float64 attention over the records of the selected positions.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu]
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import hierarchical_kv_cache_amd as hk  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from harness import Pair, SCALE  # noqa: E402
+from synth.resident import ResidentSpec  # noqa: E402
+
+W = synth.WORKLOADS
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def run(p: Pair, steps=None, expect_fused=True):
+    assert (hk.hs_resolve_attn_wgs(p.h) > 0) == expect_fused, hk.hs_resolve_attn_wgs(p.h)
+    for _ in range(p.steps if steps is None else steps):
+        p.step_gpu_and_oracle()
+    p.check_state()
+    log("  worst attention rel err %.2e" % p.worst_attn)
+
+
+@pytest.mark.parametrize("B", [64, 128, 256])
+def test_tiny_one_chunk(B):
+    """k = 64: one fetch workgroup per request writes the output itself (no merge)."""
+    w = W["tiny"].scaled(R=3, B=B)
+    log("tiny R=3 B=%d" % B)
+    p = Pair(w, fused_heads=16)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) == 2
+        run(p)
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("k,heads", [(100, 5), (1000, 16), (130, 1)])
+def test_ragged_chunks(k, heads):
+    """Shares of 50, 62-63 and 43-44 entries; fewer than 16 heads."""
+    w = W["tiny"].scaled(k=k, B=max(128, k + 40), R=3, forced_last=min(16, k), steps=6)
+    log("ragged k=%d heads=%d" % (k, heads))
+    p = Pair(w, fused_heads=heads)
+    try:
+        run(p)
+    finally:
+        p.close()
+
+
+def test_long_with_write_through():
+    """The long-request shape (k 2048, B 4096, 33 workgroups), newest slot via write-through."""
+    w = W["long"].scaled(L=2, steps=6)
+    log("long L=2 steps=6")
+    p = Pair(w, fused_heads=16)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) == 33
+        run(p)
+    finally:
+        p.close()
+
+
+def test_batched_four_requests():
+    w = W["batched"].scaled(R=4, L=2, steps=4, B=4096)
+    log("batched R=4 L=2 B=4096")
+    p = Pair(w, fused_heads=16)
+    try:
+        run(p)
+    finally:
+        p.close()
+
+
+def test_capacity_blocks():
+    w = W["capacity"].scaled(R=2, L=2, ctx=262144, steps=4)
+    log("capacity blocks R=2 L=2 ctx=262144")
+    p = Pair(w, fused_heads=16)
+    try:
+        run(p)
+    finally:
+        p.close()
+
+
+def test_resident_tier():
+    """Resident rows read from the resident pool, hot rows and misses in one tile."""
+    w = W["long"].scaled(L=2, ctx=65536, steps=5)
+    log("long with a resident window")
+    p = Pair(w, fused_heads=16, resident=ResidentSpec(page_tokens=64, window_tokens=16384, old_frac=0.1,
+                                                      spill_every=1, churn=0.05))
+    try:
+        run(p)
+    finally:
+        p.close()
+
+
+def test_shared_layers_anchor_fused():
+    """Anchors through the fused call (with the miss plan), shared layers through the replay and
+    hs_sparse_attn on the anchor's slots."""
+    w = W["shared"].scaled(R=2, L=4, ctx=16384, steps=3)
+    log("shared R=2 L=4")
+    p = Pair(w, fused_heads=16)
+    try:
+        run(p)
+        p.check_hot()
+    finally:
+        p.close()
+
+
+def test_padded_requests_untouched():
+    w = W["tiny"].scaled(R=4, steps=4)
+    p = Pair(w, fused_heads=16)
+    try:
+        sentinel = torch.full_like(p.d_att, 7.0)
+        p.d_att.copy_(sentinel)
+        for _ in range(3):
+            p.step_gpu_and_oracle(num_reqs=3)
+        torch.cuda.synchronize()
+        assert torch.equal(p.d_att[:, 3], sentinel[:, 3])
+        p.check_state(requests=range(3))
+    finally:
+        p.close()
+
+
+def test_errors_give_nan_rows_and_leave_state():
+    """A duplicate in one request: its error bits, its output rows NaN, nothing of it changes;
+    the other requests resolve and attend as usual."""
+    R, k, B, lmax, ctx = 3, 256, 512, 8192, 6000
+    cfg = hk.make_config(R, 1, lmax, k, B)
+    c = hk.HiSparse(cfg)
+    try:
+        assert hk.hs_resolve_attn_wgs(c.h) == 5
+        for r in range(R):
+            synth.fill_request(c.host_pool_address(r), r, 1, lmax, lmax)
+        caches = [oracle.Cache(B, lmax, 1152) for _ in range(R)]
+        dev = torch.device("cuda")
+        out = torch.empty((R, k), dtype=torch.int32, device=dev)
+        st = torch.zeros((R, 4), dtype=torch.int32, device=dev)
+        att = torch.empty((R, 16, 512), dtype=torch.float32, device=dev)
+        d_ctx = torch.full((R,), ctx, dtype=torch.int32, device=dev)
+        rng = np.random.default_rng(3)
+        for t in range(4):
+            sels = [rng.choice(ctx, k, replace=False).astype(np.int32) for _ in range(R)]
+            bad = t % 2 == 1
+            if bad:
+                sels[1][200] = sels[1][7]
+            q = synth.queries(R, 1, t)
+            d_q = torch.from_numpy(q[:, 0].copy().view(np.int16)).to(dev)
+            d_sel = torch.from_numpy(np.stack(sels)).to(dev)
+            hk.hs_resolve_attn(c.h, 0, d_sel.data_ptr(), d_ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0,
+                               d_q.data_ptr(), 16, 512, att.data_ptr(), SCALE, 0)
+            torch.cuda.synchronize()
+            got, s, o = out.cpu().numpy(), st.cpu().numpy(), att.cpu().numpy()
+            for r in range(R):
+                if bad and r == 1:
+                    with pytest.raises(oracle.OracleError) as e:
+                        caches[r].resolve(sels[r], ctx, c.host_pool(r)[0])
+                    assert s[r, 2] == e.value.code == hk.HS_ERR_DUP
+                    assert (got[r] == -1).all() and np.isnan(o[r]).all()
+                    continue
+                ref = caches[r].resolve(sels[r], ctx, c.host_pool(r)[0])[0]
+                assert s[r, 2] == 0 and np.array_equal(got[r], ref), (t, r)
+                o_ref = oracle.attention.sparse_decode_attention(q[r, 0], caches[r].hot, ref, SCALE)
+                assert np.abs(o[r] - o_ref).max() <= 2e-3 * np.abs(o_ref).max(), (t, r)
+    finally:
+        c.close()
+
+
+def test_short_requests_cross_into_the_normal_path():
+    """Short requests (slot = position) through the fused call, growing by write-through
+    appends past B."""
+    w = W["tiny"].scaled(R=2, ctx=200, B=256, k=64, forced_last=16, steps=80, append=True)
+    p = Pair(w, fused_heads=16)
+    try:
+        for r in range(w.R):
+            hk.hs_admit_short(p.h, r, w.ctx, p.compute.cuda_stream)
+            for l in p.anchors:
+                p.caches[(r, l)].admit_short(w.ctx, p.ohost[r][l])
+        run(p)
+    finally:
+        p.close()
+
+
+def test_configuration_without_the_fused_kernel():
+    """32 requests x (2048 / 64 + 1) workgroups exceed one wave of workgroups: the call makes
+    hs_resolve and hs_sparse_attn, with the same results."""
+    w = W["batched"].scaled(L=1, steps=2, B=4096)
+    log("batched R=32: two calls")
+    p = Pair(w, fused_heads=16)
+    try:
+        run(p, expect_fused=False)
+    finally:
+        p.close()
+
+
+def test_fused_matches_separate_calls():
+    """The same trace through hs_resolve + hs_sparse_attn on one handle and hs_resolve_attn on
+    another: identical slots every step, attention within the tolerance of each other."""
+    w = W["long"].scaled(L=1, steps=4, ctx=32768)
+    a = Pair(w, fused_heads=16)
+    b = Pair(w)
+    try:
+        q_all = [synth.queries(w.R, w.L, t) for t in range(w.steps)]
+        out_b = torch.empty((w.R, 16, 512), dtype=torch.float32, device="cuda")
+        for t in range(w.steps):
+            a.step_gpu_and_oracle()
+            b.step_gpu_and_oracle()
+            d_q = torch.from_numpy(q_all[t][:, 0].copy().view(np.int16)).to("cuda")
+            hk.hs_sparse_attn(b.h, 0, d_q.data_ptr(), 16, 512, b.d_out[0].data_ptr(), out_b.data_ptr(), SCALE, 0,
+                              b.compute.cuda_stream)
+            torch.cuda.synchronize()
+            assert torch.equal(a.d_out, b.d_out)
+            oa, ob = a.d_att[0].cpu().numpy(), out_b.cpu().numpy()
+            assert np.abs(oa - ob).max() <= 2e-3 * np.abs(ob).max()
+    finally:
+        a.close()
+        b.close()

@@ -28,8 +28,8 @@ def test_library_exports_every_declared_symbol():
 def test_workspace_sizing_and_validation_without_gpu():
     cfg = hk.make_config(R=32, L=16, max_positions=32768, top_k=2048, buffer_slots=4096)
     n = hk.hs_workspace_bytes(cfg)
-    # page tables dominate: 32 * 16 * 32768 int32
-    assert n >= 32 * 16 * 32768 * 4
+    # page tables dominate: 32 * 16 * 32768 entries of 8 bytes (slot, generation)
+    assert n >= 32 * 16 * 32768 * 8
     bad = hk.make_config(R=1, L=1, max_positions=4096, top_k=128, buffer_slots=64)  # B < k
     try:
         hk.hs_workspace_bytes(bad)
