@@ -21,7 +21,7 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts
 
 import hierarchical_kv_cache_amd as hk  # noqa: E402
 import synth  # noqa: E402
-from harness import Pair  # noqa: E402
+from harness import Pair, SCALE  # noqa: E402
 
 W = synth.WORKLOADS
 
@@ -31,7 +31,8 @@ def log(msg):
 
 
 def replay_with_published_page_table(p: Pair, t0: int):
-    """Runs steps 0..t0 (checked against the oracle), then re-runs step t0 as described above."""
+    """Runs steps 0..t0 (checked against the oracle), then re-runs step t0 as described above
+    (through hs_resolve_attn when the pair drives the fused call)."""
     w = p.w
     for _ in range(t0):
         p.step_gpu_and_oracle()
@@ -55,13 +56,28 @@ def replay_with_published_page_table(p: Pair, t0: int):
     out2 = torch.full_like(p.d_out, -7)
     stats2 = torch.full_like(p.d_stats, -7)
     d_ctx = torch.full((w.R,), p.w.ctx, dtype=torch.int32, device=p.dev)
+    if p.fused_heads:
+        att1 = p.d_att.clone()
+        q = synth.queries(w.R, w.L, t0, heads=p.fused_heads)
+        d_q = torch.from_numpy(q.view(np.int16)).to(p.dev)
+        att2 = torch.full_like(p.d_att, -7.0)
     for ai, l in enumerate(p.anchors):
-        hk.hs_resolve(p.h, l, p.d_trace[t0, ai].data_ptr(), d_ctx.data_ptr(), out2[ai].data_ptr(),
-                      stats2.data_ptr(), 0, hk.HS_RECORD_PLAN if w.group > 1 else 0, p.compute.cuda_stream)
+        fl = hk.HS_RECORD_PLAN if w.group > 1 else 0
+        if p.fused_heads:
+            dq = d_q[:, l].contiguous()
+            hk.hs_resolve_attn(p.h, l, p.d_trace[t0, ai].data_ptr(), d_ctx.data_ptr(), out2[ai].data_ptr(),
+                               stats2.data_ptr(), 0, fl, dq.data_ptr(), p.fused_heads, 512, att2[ai].data_ptr(),
+                               SCALE, p.compute.cuda_stream)
+            torch.cuda.synchronize()
+        else:
+            hk.hs_resolve(p.h, l, p.d_trace[t0, ai].data_ptr(), d_ctx.data_ptr(), out2[ai].data_ptr(),
+                          stats2.data_ptr(), 0, fl, p.compute.cuda_stream)
         if ai == len(p.anchors) - 1:
             assert torch.equal(stats2, stats1), (stats2.cpu().numpy(), stats1.cpu().numpy())
     torch.cuda.synchronize()
     assert torch.equal(out2, out1)
+    if p.fused_heads:  # the same records in the same order: the same attention, bit for bit
+        assert torch.equal(att2, att1)
     assert int(stats1[:, 2].abs().sum()) == 0
     assert torch.equal(ws, ws1), "workspace differs from the first run"
     assert torch.equal(hot, hot1), "hot buffer differs from the first run"
@@ -98,5 +114,19 @@ def test_capacity_blocks_published_page_table():
     p = Pair(w)
     try:
         assert replay_with_published_page_table(p, 2) > 0
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("t0", [0, 5])
+def test_fused_published_page_table(t0):
+    """The fused kernel: its fetch workgroups pick every record's source (hot slot or host)
+    from the page table at entry, so a late read must classify as an early one did."""
+    w = W["long"].scaled(L=2, ctx=32768, steps=6, append=False, force_newest=False)
+    log("fused long-shape R=1 L=2 t0=%d" % t0)
+    p = Pair(w, fused_heads=16)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) > 0
+        assert replay_with_published_page_table(p, t0) > 0
     finally:
         p.close()
