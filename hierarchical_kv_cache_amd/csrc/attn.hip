@@ -330,13 +330,11 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
 constexpr int kMergeBatch = 32;
 constexpr int kMergeQuarters = kAttnDv / 128;
 
-__global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
-  __shared__ float fac[kAttnMaxChunks];
-  const int rh = blockIdx.x / kMergeQuarters, qt = blockIdx.x - rh * kMergeQuarters;
-  const int r = rh / p.heads, hh = rh - r * p.heads;
-  if (p.num_reqs && r >= *p.num_reqs) return;
-  const int lane = threadIdx.x;
-  const float* pr = p.part + (size_t)r * p.S * kPartStride;
+// One wave: channels 128 qt .. 128 qt + 127 of head hh, from the S partials of one request
+// (pr); `fac` is this wave's LDS scratch of kAttnMaxChunks floats.  Every wave of the
+// workgroup calls it (it holds a workgroup barrier).
+__device__ __forceinline__ void merge_quarter(const float* pr, int S, int hh, int qt, int lane, float* fac,
+                                              float* orow) {
   const float* base = pr + hh * kAttnDv + qt * 128 + 2 * lane;
   constexpr int NU = kAttnMaxChunks / 64;
   float mv[NU], lv[NU];
@@ -344,13 +342,13 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
   for (int u = 0; u < NU; ++u) {
     const int q = lane + 64 * u;
     const float* pq = pr + (size_t)q * kPartStride + 16 * kAttnDv;
-    mv[u] = q < p.S ? pq[hh] : -INFINITY;
-    lv[u] = q < p.S ? pq[16 + hh] : 0.0f;
+    mv[u] = q < S ? pq[hh] : -INFINITY;
+    lv[u] = q < S ? pq[16 + hh] : 0.0f;
   }
   f32x2 v[kMergeBatch];
 #pragma unroll
   for (int u = 0; u < kMergeBatch; ++u)
-    v[u] = u < p.S ? *(const f32x2*)(base + (size_t)u * kPartStride) : f32x2{0.0f, 0.0f};
+    v[u] = u < S ? *(const f32x2*)(base + (size_t)u * kPartStride) : f32x2{0.0f, 0.0f};
   float M = mv[0];
 #pragma unroll
   for (int u = 1; u < NU; ++u) M = fmaxf(M, mv[u]);
@@ -369,14 +367,88 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
   f32x2 acc = {0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < kMergeBatch; ++u) acc += fac[u] * v[u];
-  for (int q0 = kMergeBatch; q0 < p.S; q0 += kMergeBatch) {  // more than kMergeBatch chunks
+  for (int q0 = kMergeBatch; q0 < S; q0 += kMergeBatch) {  // more than kMergeBatch chunks
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-      v[u] = q0 + u < p.S ? *(const f32x2*)(base + (size_t)(q0 + u) * kPartStride) : f32x2{0.0f, 0.0f};
+      v[u] = q0 + u < S ? *(const f32x2*)(base + (size_t)(q0 + u) * kPartStride) : f32x2{0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) acc += fac[q0 + u < kAttnMaxChunks ? q0 + u : 0] * v[u];
   }
-  *(f32x2*)(p.out + ((size_t)r * p.heads + hh) * p.value_dim + qt * 128 + 2 * lane) = acc * (1.0f / den);
+  *(f32x2*)(orow + qt * 128 + 2 * lane) = acc * (1.0f / den);
+}
+
+__global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
+  __shared__ float fac[kAttnMaxChunks];
+  const int rh = blockIdx.x / kMergeQuarters, qt = blockIdx.x - rh * kMergeQuarters;
+  const int r = rh / p.heads, hh = rh - r * p.heads;
+  if (p.num_reqs && r >= *p.num_reqs) return;
+  merge_quarter(p.part + (size_t)r * p.S * kPartStride, p.S, hh, qt, threadIdx.x, fac,
+                p.out + ((size_t)r * p.heads + hh) * p.value_dim);
+}
+
+// The fused call's second kernel.  Workgroups [0, merge_blocks): one per (request, head),
+// four waves for the four 128-channel quarters: the chunk merge, or NaN rows when workgroup
+// 0 of the fused kernel reported an error for the request (with one chunk the fetch
+// workgroup wrote the output itself).  The other workgroups stride over every request's
+// misses: the page-table updates (the evicted position host only, the new position in its
+// victim slot, tagged with the launch's generation) and the 16-byte chunks of the missed
+// records from the staging area into their victim slots.  No two misses share a slot or a
+// position, and evicted positions are not selected, so the writes are independent.
+constexpr int kFinishThreads = 256;
+constexpr int kFinishUnroll = 4;
+
+__global__ void __launch_bounds__(kFinishThreads) attn_finish_kernel(FinishParams p) {
+  __shared__ float fac[kFinishThreads / 64][kAttnMaxChunks];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (b < p.merge_blocks) {
+    const int r = b / p.heads, hh = b - r * p.heads;
+    if (p.num_reqs && r >= *p.num_reqs) return;
+    float* orow = p.out + ((size_t)r * p.heads + hh) * p.value_dim;
+    if (p.hdr[r * 4] != 0) {
+      for (int c = tid; c < p.value_dim; c += kFinishThreads) orow[c] = __builtin_nanf("");
+      return;
+    }
+    if (p.S == 1) return;
+    merge_quarter(p.part + (size_t)r * p.S * kPartStride, p.S, hh, tid >> 6, tid & 63, fac[tid >> 6], orow);
+    return;
+  }
+  const int C = p.rec_bytes >> 4;
+  const int nthreads = (gridDim.x - p.merge_blocks) * kFinishThreads;
+  const int t0 = (b - p.merge_blocks) * kFinishThreads + tid;
+  for (int r = 0; r < p.R; ++r) {
+    if (p.num_reqs && r >= *p.num_reqs) break;
+    const uint32_t* h = p.hdr + (size_t)r * 4;
+    if (h[0] != 0) continue;
+    const int m = (int)h[1];
+    const uint32_t gen = h[2];
+    const int32_t* ml = p.mlist + (size_t)r * p.k * 4;
+    uint64_t* pt = p.page_table + (size_t)r * p.max_positions;
+    for (int j = t0; j < m; j += nthreads) {
+      const int32_t old = ml[4 * j + 2];
+      if (old >= 0) pt[old] = kPtHostOnly;
+      pt[ml[4 * j + 3]] = pt_entry(ml[4 * j + 1], gen);
+    }
+    const uint8_t* st = p.stage + (size_t)r * p.k * p.rec_bytes;
+    uint8_t* dst = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+    const int total = m * C;
+    for (int f0 = t0; f0 < total; f0 += nthreads * kFinishUnroll) {
+      u32x4 v[kFinishUnroll];
+      int slot[kFinishUnroll], cc[kFinishUnroll];
+#pragma unroll
+      for (int u = 0; u < kFinishUnroll; ++u) {
+        const int f = f0 + u * nthreads;
+        if (f < total) {
+          const int j = f / C;
+          cc[u] = f - j * C;
+          slot[u] = ml[4 * j + 1];
+          v[u] = *((const u32x4*)(st + (size_t)ml[4 * j] * p.rec_bytes) + cc[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kFinishUnroll; ++u)
+        if (f0 + u * nthreads < total) *((u32x4*)(dst + (size_t)slot[u] * p.rec_bytes) + cc[u]) = v[u];
+    }
+  }
 }
 
 }  // namespace
@@ -392,6 +464,12 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
 
 hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s) {
   hipLaunchKernelGGL(attn_merge_kernel, dim3(p.R * p.heads * kMergeQuarters), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_finish(const FinishParams& p, hipStream_t s) {
+  constexpr int kCopyBlocks = 128;  // 32K threads: a cold step's 2048 misses in ~5 strides
+  hipLaunchKernelGGL(attn_finish_kernel, dim3(p.merge_blocks + kCopyBlocks), dim3(kFinishThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ struct Layout {
   int Spart = 1;    // partial records per (layer, request): max(S, fused chunks)
   int kmax = 0;     // longest list one resolve handles: top_k * max(1, verify_rows)
   size_t ctrl = 0, slot_pos = 0, lru = 0, plan = 0, page_table = 0, newest = 0, host_base = 0,
-         attn_part = 0, uni = 0, umap = 0, uout = 0, ucnt = 0, uerr = 0, total = 0;
+         attn_part = 0, uni = 0, umap = 0, uout = 0, ucnt = 0, uerr = 0, att_hdr = 0, att_mlist = 0,
+         att_stage = 0, total = 0;
 };
 
 int attn_chunks(const hs_config& c) {
@@ -93,6 +94,11 @@ Layout make_layout(const hs_config& c) {
   L.newest = take(R * sizeof(int32_t));
   L.host_base = take(R * sizeof(void*));
   L.attn_part = take(size_t(c.num_layers) * R * L.Spart * kPartStride * sizeof(float));
+  if (Sf) {  // the fused call's report, miss list and staging area (one set per handle)
+    L.att_hdr = take(R * 4 * sizeof(uint32_t));
+    L.att_mlist = take(R * k * 4 * sizeof(int32_t));
+    L.att_stage = take(R * k * size_t(c.record_bytes));
+  }
   if (c.verify_rows > 1) {  // union scratch of hs_resolve_rows (one set per handle)
     L.uni = take(R * L.kmax * sizeof(int32_t));
     L.umap = take(R * L.kmax * sizeof(int32_t));
@@ -459,13 +465,17 @@ hs_status hs_resolve_attn(hs_handle h, int32_t layer, const int32_t* d_sel, cons
   p.q = (const uint16_t*)d_q; p.part = h->attn_part(layer); p.att_out = d_out;
   p.att_res = h->res ? h->res + size_t(layer) * size_t(h->res_rows) * size_t(h->cfg.record_bytes) : nullptr;
   p.heads = heads; p.att_scale = scale;
+  p.att_hdr = (uint32_t*)(h->ws + h->lay.att_hdr); p.att_mlist = (int32_t*)(h->ws + h->lay.att_mlist);
+  p.att_stage = h->ws + h->lay.att_stage;
   HS_HIP(launch_resolve_attn(p, h->att_lds, s, h->next_timing()));
-  if (h->att_G > 2) {  // the chunk partials of every (request, head) merged into the output
-    AttnParams m{};
-    m.out = d_out; m.part = h->attn_part(layer); m.num_reqs = d_num_reqs; m.R = h->cfg.num_requests;
-    m.heads = heads; m.value_dim = value_dim; m.S = h->att_G - 1; m.k = h->cfg.top_k;
-    HS_HIP(launch_attn_merge(m, s));
-  }
+  // the chunk merge (or NaN rows), the staged misses into their slots, the page-table updates
+  FinishParams f{};
+  f.out = d_out; f.part = h->attn_part(layer); f.num_reqs = d_num_reqs; f.hdr = p.att_hdr; f.mlist = p.att_mlist;
+  f.stage = p.att_stage; f.hot = h->hot; f.hot_req_stride = h->hot_req_stride(); f.hot_layer_off = h->hot_layer_off(layer);
+  f.page_table = h->page_table(a); f.max_positions = h->cfg.max_positions; f.R = h->cfg.num_requests;
+  f.heads = heads; f.value_dim = value_dim; f.S = h->att_G - 1; f.k = h->cfg.top_k;
+  f.rec_bytes = h->cfg.record_bytes; f.merge_blocks = h->cfg.num_requests * heads;
+  HS_HIP(launch_attn_finish(f, s));
   return HS_OK;
 }
 

@@ -106,26 +106,29 @@ __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits, i
 }
 int resolve_elems_per_thread(int k, int B);
 
-// Fused RESOLVE + attention (one tile of <= 64 selected records per fetch workgroup): the
-// resolve carve-up, then the record tile, the query rows, and per tile row the miss's list
-// index and the record's address.  The
-// attention scratch (scores' maxima and sums, P) reuses the start of the resolve region once
-// stage 3 is done with it.
+// Fused RESOLVE + attention.  Workgroup 0 uses the resolve carve-up; each fetch workgroup
+// (one tile of <= 64 selected records) the record tile, the query rows, per tile row the
+// miss's list index and the record's address, and the attention scratch (scores' maxima and
+// sums, P).  The dynamic LDS of the launch is the larger of the two.
 constexpr int kTileRows = 64;        // records per fetch workgroup
 constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (292 words): the 16 rows
                                      // of a QK^T operand read fall on 16 distinct 4-bank groups, and
                                      // the quarter-waves of a P V operand read on disjoint banks
 constexpr int kQStride = 1168;       // LDS stride of a query row (16-byte aligned, off the bank period)
+constexpr int kAttnScratch = 2 * 4 * 16 * 4 + 2 * 2 * 16 * 32 * 2;  // maxima, sums, P hi and lo
 struct FusedLds {
-  size_t tile, qs, arow, asrc, total;
+  size_t tile, qs, arow, asrc, scratch, total;
 };
 __host__ __device__ inline FusedLds fused_lds(int k, int B, int hash_bits, int G) {
   FusedLds F;
-  F.tile = align_up(resolve_lds(k, B, hash_bits, G).total, 16);
+  F.tile = 0;
   F.qs = F.tile + size_t(kTileRows) * kTileStride;
   F.arow = F.qs + 16 * size_t(kQStride);
   F.asrc = F.arow + 4 * size_t(kTileRows);
-  F.total = align_up(F.asrc + 8 * size_t(kTileRows), 16);
+  F.scratch = F.asrc + 8 * size_t(kTileRows);
+  const size_t fetch = align_up(F.scratch + kAttnScratch, 16);
+  const size_t resolve = resolve_lds(k, B, hash_bits, G).total;
+  F.total = fetch > resolve ? fetch : resolve;
   return F;
 }
 
@@ -167,8 +170,27 @@ struct ResolveParams {
   float* part;               // [R][G-1][kPartStride] chunk partials (G > 2)
   float* att_out;            // [R][heads][512] (written directly when G == 2)
   const uint8_t* att_res;    // this layer's resident pool [res_rows][rec] (null without one)
+  uint32_t* att_hdr;         // [R][4] workgroup 0's report: error bits, misses, page-table generation
+  int32_t* att_mlist;        // [R][k][4] per miss: list index, victim slot, evicted position, position
+  uint8_t* att_stage;        // [R][k][rec] missed records by list index
   int32_t heads;
   float att_scale;
+};
+
+// The finish kernel of the fused call: chunk merge (or NaN rows on error), the missed records
+// from the staging area into their victim slots, the page-table updates of the misses.
+struct FinishParams {
+  float* out;                // [R][heads][value_dim]
+  const float* part;         // [R][S][kPartStride]
+  const int32_t* num_reqs;
+  const uint32_t* hdr;       // [R][4]
+  const int32_t* mlist;      // [R][k][4]
+  const uint8_t* stage;      // [R][k][rec]
+  uint8_t* hot;
+  int64_t hot_req_stride, hot_layer_off;
+  uint64_t* page_table;      // the anchor's [R][max_positions]
+  int64_t max_positions;
+  int32_t R, heads, value_dim, S, k, rec_bytes, merge_blocks;
 };
 
 struct AppendParams {
@@ -285,6 +307,7 @@ hipError_t launch_backup(const AppendParams& p, hipStream_t s);
 hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s);  // the S chunk partials -> out
+hipError_t launch_attn_finish(const FinishParams& p, hipStream_t s);
 hipError_t launch_export(const ExportParams& p, hipStream_t s);
 hipError_t launch_init(const InitParams& p, hipStream_t s);
 hipError_t launch_admit(const AdmitParams& p, hipStream_t s);

@@ -325,17 +325,15 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
   }
 }
 
-// Outcome of the resolve part of a workgroup: nothing more to do, or (fused attention) a
-// record tile to attend over, or an error that makes the request's attention output NaN.
-constexpr int kDone = 0, kTile = 1, kError = 2;
-
 // E: slots (and LRU positions) per thread, KE: selection entries per thread (both powers
-// of two, KE <= E, EK = ceil(k / NT) <= KE).  ATT: fused attention -- every fetch workgroup
-// also loads its share of the selected records (<= 64) into an LDS tile, straight from the
-// hot slots, the resident pool or (misses) the host pool, and the misses go from the tile to
-// their victim slots.
+// of two, KE <= E, EK = ceil(k / NT) <= KE).  ATT: workgroup 0 of the fused kernel (its
+// other workgroups run fetch_attend instead).  It resolves as usual but leaves the page
+// table alone: it writes the list of its misses (list index, victim slot, evicted position,
+// new position) and a per-request header, and the finish kernel that follows applies the
+// page-table updates and copies the missed records, which the fetch workgroups staged, into
+// their victim slots.  So the page table does not change while the fused kernel runs.
 template <int E, int KE, bool ATT>
-__device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned char* smem) {
+__device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned char* smem) {
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits, p.G);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
   int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] position (hash key) of each entry
@@ -358,7 +356,7 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
   if (p.num_reqs && r >= *p.num_reqs) {
     // a padded request: untouched, and an empty plan so a replay copies nothing
     if (record && g == 0 && tid == 0) p.ctrl[r * 4 + 2] = 0;
-    return kDone;
+    return;
   }
   const int H = 1 << p.hash_bits;
   const uint32_t hmask = (uint32_t)H - 1;
@@ -377,7 +375,7 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
     }
-    return kDone;
+    return;
   }
 
   // ---- every global read up front -------------------------------------------------------
@@ -404,47 +402,18 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
   // their share of the list, spread over the waves: entry e of the share belongs to wave
   // e % NW, lane (e / NW) % 64, slot e / NT.
   const bool io = !(p.flags & HS_SKIP_IO);
-  const bool fetcher = io && (p.G == 1 || g > 0);
+  const bool fetcher = !ATT && io && (p.G == 1 || g > 0);  // (the fused kernel's fetch workgroups
+                                                           // do not run this function)
   const int nf = p.G > 1 ? p.G - 1 : 1;
   const int gf = p.G > 1 ? g - 1 : 0;
   // (32-bit: k * G < 2^23)
   const int f_lo = kr * gf / nf;
   const int f_n = kr * (gf + 1) / nf - f_lo;
   const int wid = tid >> 6, lane = tid & 63;
-  // (loaded here by the fused variant, whose short path needs them; later otherwise, which
-  // keeps them out of the registers live across the entry loads)
-  int32_t fraw[KE];
-  auto load_share = [&]() {
-#pragma unroll
-    for (int q = 0; q < KE; ++q) {
-      const int e = q * NT + lane * NW + wid;
-      const int i = f_lo + e;
-      fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
-    }
-  };
-  if constexpr (ATT) load_share();
   const uint8_t* hbase = nullptr;  // this (request, layer)'s host records
   uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
-  unsigned char* tile = smem;
-  unsigned char* qs = smem;
-  uint64_t* asrc = nullptr;  // fused: record address of each tile row
-  int32_t* arow = nullptr;   // fused: list index of the miss in each tile row, -1 otherwise
-  const uint8_t* filler = nullptr;
-  u32x4 qv[kQU], tv[kTU];
-  if constexpr (ATT) {
-    const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G);
-    tile = smem + F.tile;
-    qs = smem + F.qs;
-    arow = (int32_t*)(smem + F.arow);
-    asrc = (uint64_t*)(smem + F.asrc);
-    // a row without a record (past the share, or an entry in error) is loaded from the first
-    // query row: any finite bytes do, its score is masked and only its value row must be finite
-    filler = (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);
-    if (g > 0) {
-      hbase = p.host_base[r] + p.host_layer_off;
-      q_load(qv, p.q, r, p.heads);  // the query rows, in LDS once the entry loads are in
-    }
-  }
+  // fused: workgroup 0's report to the finish kernel
+  uint32_t* hdr = ATT ? p.att_hdr + (size_t)r * 4 : nullptr;
   // ---- short-sequence fast path ("HiSparse 深度解析" §5.4, §5.5): a request admitted short
   // keeps its tokens in slot order while its context fits B, so every position is its own
   // slot: no hash, no LRU, no host IO (only the range is checked)
@@ -480,29 +449,9 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
         p.stats[r] = st;
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
+      if (ATT && tid == 0) { hdr[0] = bad ? (uint32_t)HS_ERR_RANGE : 0u; hdr[1] = 0u; }
     }
-    if constexpr (ATT) {
-      if (g > 0) {
-        if (bad) return kError;
-        // slot = position: the share's records straight from the hot slots
-        q_store(qv, qs);
-        if (lane < kTileRows / NW) {
-          const uint8_t* src = filler;
-          if (fraw[0] >= 0) {
-            const int e = lane * NW + wid, i = f_lo + e;
-            const int64_t pos64 = p.bt_shift ? ((int64_t)fraw[0] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
-                                             : (int64_t)fraw[0];
-            src = dbase + (size_t)pos64 * p.rec_bytes;
-          }
-          asrc[lane * NW + wid] = (uint64_t)src;
-        }
-        __syncthreads();
-        tile_load(tv, asrc);
-        tile_store(tv, tile);
-        return kTile;
-      }
-    }
-    return kDone;
+    return;
   }
   // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
   // map, so it names the slot of a hit) and, with a resident tier, its resident page.
@@ -519,7 +468,13 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
     ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
     rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
-  if constexpr (!ATT) load_share();
+  int32_t fraw[KE];
+#pragma unroll
+  for (int q = 0; q < KE; ++q) {
+    const int e = q * NT + lane * NW + wid;
+    const int i = f_lo + e;
+    fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
+  }
   const bool bvec = (p.B % E) == 0;
   int32_t spa[E], spb[E];
   int16_t lra[E], lrb[E];
@@ -581,45 +536,6 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
   int32_t pts[KE];
 #pragma unroll
   for (int j = 0; j < KE; ++j) pts[j] = pt_slot_for(ptv[j], gen);
-  if constexpr (ATT) {
-    // Every load of the entry phase has landed (all of them are needed by now or soon), so
-    // the only loads in flight from here on are the tile's, and no wait the compiler places
-    // for an earlier load can hold up on them.  In every workgroup: the compiler merges the
-    // paths of workgroup 0 and the fetch workgroups.
-    vm_wait();
-    if (g > 0) {
-      q_store(qv, qs);
-      // The record of each share entry, classified as stage 1 will classify it: resident
-      // row, newest slot, hit slot, or (a miss) the host record.  The loads fly while
-      // stages 1-3 run.
-      if (lane < kTileRows / NW) {
-        const uint8_t* src = filler;
-        int32_t mi = -1;
-        if (fpos[0] >= 0) {
-          const int32_t pos = fpos[0];
-          if (fres[0] >= 0) {
-            const int64_t row = ((int64_t)fres[0] << p.page_shift) + (pos & (((int64_t)1 << p.page_shift) - 1));
-            if (row < p.res_rows) src = p.att_res + (size_t)row * p.rec_bytes;
-          } else if (pos == newest) {
-            src = dbase + (size_t)p.B * p.rec_bytes;
-          } else {
-            const int32_t sl = pt_slot_for(fpt[0], gen);
-            if (sl < 0) {
-              src = hbase + (size_t)pos * p.rec_bytes;
-              mi = f_lo + lane * NW + wid;
-            } else if (sl < p.B) {
-              src = dbase + (size_t)sl * p.rec_bytes;
-            }
-          }
-        }
-        asrc[lane * NW + wid] = (uint64_t)src;
-        arow[lane * NW + wid] = mi;
-      }
-      __syncthreads();
-      tile_load(tv, asrc);
-    }
-  }
-
   // ---- resident tier: a selection that is resident throughout returns here ---------------
   int nres = 0;
   if (tiered) {
@@ -642,12 +558,9 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
           p.stats[r] = st;
         }
         if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
+        if (ATT && tid == 0) { hdr[0] = 0u; hdr[1] = 0u; }
       }
-      if (ATT && g > 0) {
-        tile_store(tv, tile);
-        return kTile;
-      }
-      return kDone;
+      return;
     }
   }
 
@@ -754,7 +667,7 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
   const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
   const float invC = 1.0f / (float)C;
   int mw = 0;  // misses of this wave
-  if constexpr (!ATT) {
+  {
 #pragma unroll
     for (int q = 0; q < KE; ++q) {
       const bool miss = fpos[q] >= 0 && fpos[q] != newest && fres[q] < 0 && pt_slot_for(fpt[q], gen) < 0;
@@ -769,15 +682,13 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if constexpr (!ATT) {
-    if (fetcher) hbase = p.host_base[r] + p.host_layer_off;
-  }
+  if (fetcher) hbase = p.host_base[r] + p.host_layer_off;
   const int wtotal = mw * C;  // 16-byte chunks of this wave's misses
   u32x4 early[kEarly];
 #pragma unroll
   for (int u = 0; u < kEarly; ++u) {
     const int c = lane + 64 * u;
-    if (!ATT && c < wtotal) {
+    if (c < wtotal) {
       int l = (int)((float)c * invC);
       int cc = c - l * C;
       if (cc < 0) { --l; cc += C; }
@@ -803,13 +714,16 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
         p.stats[r] = st;
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
+      if (ATT && tid == 0) { hdr[0] = err; hdr[1] = 0u; }
     }
-    return (ATT && g > 0) ? kError : kDone;
+    return;
   }
   // this launch changes the metadata: the next one finds it in the other half (the shares
   // of the G workgroups add up to one launch unit)
+  // (the fused kernel's other workgroups do not resolve: workgroup 0 adds the whole unit)
   if (tid == 0)
-    __hip_atomic_fetch_add(counter, g == 0 ? (1ull << kLaunchShift) - (uint64_t)(p.G - 1) : 1ull,
+    __hip_atomic_fetch_add(counter,
+                           g == 0 ? (1ull << kLaunchShift) - (ATT ? 0ull : (uint64_t)(p.G - 1)) : 1ull,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- stage 3: misses in list order and evictables in LRU order, one scan -------------
@@ -887,8 +801,13 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
         const int jm = -2 - fo[j];
         const int i = missidx[jm];
         const int32_t np = selp[i];
-        if (spo[j] >= 0) pt[spo[j]] = kPtHostOnly;  // the evicted position is host-only again
-        pt[np] = pt_entry(s, gen);
+        if constexpr (ATT) {  // the finish kernel applies it
+          const u32x4 e = {(uint32_t)i, (uint32_t)s, (uint32_t)spo[j], (uint32_t)np};
+          *(u32x4*)(p.att_mlist + ((size_t)r * p.k + jm) * 4) = e;
+        } else {
+          if (spo[j] >= 0) pt[spo[j]] = kPtHostOnly;  // the evicted position is host-only again
+          pt[np] = pt_entry(s, gen);
+        }
         spn[j] = np;
         outr[i] = s;
         if (record) {
@@ -925,24 +844,9 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
         p.stats[r] = st;
       }
       if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;
+      if (ATT) { hdr[0] = 0u; hdr[1] = (uint32_t)m; hdr[2] = gen; }
     }
-    if (p.G > 1) return kDone;
-  }
-
-  if constexpr (ATT) {
-    // ---- stage 4 (fused): the tile goes to LDS, its missed records to their victim slots ----
-#pragma unroll
-    for (int u = 0; u < kTU; ++u) {
-      const int f = tid + u * NT;
-      if (f < kTileChunks) {
-        const int row = f / kRowChunks, c = f - row * kRowChunks;
-        *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
-        const int a = arow[row];
-        if (a >= 0) *((u32x4*)(dbase + (size_t)victim[mrank[a]] * (size_t)p.rec_bytes) + c) = tv[u];
-      }
-    }
-    __syncthreads();  // the tile is complete, the resolve region free for the attention scratch
-    return kTile;
+    if (p.G > 1) return;
   }
 
   // ---- stage 4, second part: the fetched records go to the slots stage 3 chose --------
@@ -982,32 +886,99 @@ __device__ __forceinline__ int resolve_body(const ResolveParams& p, unsigned cha
           *((u32x4*)(dbase + (size_t)victim[mrank[widx[ll[u]]]] * (size_t)p.rec_bytes) + cc[u]) = v[u];
     }
   }
-  return kDone;
+}
+
+// A fetch workgroup g >= 1 of the fused kernel: attention over its share (chunk g - 1, at
+// most 64 entries) of the selection.  It does not resolve.  Each share entry's record is
+// where the page table (stable while the fused kernel runs: workgroup 0 leaves its updates
+// to the finish kernel) and the resident tier put it: a resident row, the newest slot, the
+// hot slot of a hit, or for a miss the host record.  The records are loaded into registers
+// (5 x 16 bytes per thread), then written to the LDS tile, the missed ones also to the
+// staging area (by list index) from which the finish kernel copies them into their victim
+// slots, so host bytes cross the link once.  Entries in error (out of range, resident rows
+// outside the pool) load a finite filler row; workgroup 0 reports the error and the finish
+// kernel makes the request's output NaN.
+__device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned char* smem) {
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
+  if (p.num_reqs && r >= *p.num_reqs) return;
+  const int S = p.G - 1;
+  const int f_lo = p.k * (g - 1) / S;  // (32-bit: k * G < 2^23)
+  const int f_n = p.k * g / S - f_lo;
+  const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G);
+  unsigned char* tile = smem + F.tile;
+  unsigned char* qs = smem + F.qs;
+  int32_t* arow = (int32_t*)(smem + F.arow);   // list index of the miss in each row, -1 otherwise
+  uint64_t* asrc = (uint64_t*)(smem + F.asrc);  // record address of each row
+  const uint8_t* filler = (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);
+  const uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+  u32x4 qv[kQU];
+  q_load(qv, p.q, r, p.heads);
+  // share entry e = lane * NW + wid: lanes 0..3 of every wave, all 64 rows of the tile
+  const int e = lane * NW + wid;
+  const uint8_t* src = filler;
+  int32_t mi = -1;
+  if (lane < kTileRows / NW && e < f_n) {
+    const int i = f_lo + e;
+    const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
+    const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
+    const bool short_path = p.ctrl[r * 4 + 3] != 0 && ctx <= p.B;  // slot = position
+    const int32_t raw = p.sel[(size_t)r * p.kb + (p.bt_shift ? (i >> p.bt_shift) : i)];
+    const int64_t pos64 = p.bt_shift ? ((int64_t)raw << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)raw;
+    if (pos64 >= 0 && pos64 < ctx) {
+      if (short_path) {
+        src = dbase + (size_t)pos64 * p.rec_bytes;
+      } else {
+        const int32_t sl = (int32_t)(uint32_t)p.page_table[(size_t)r * p.max_positions + pos64];
+        const int32_t rp = p.rtable ? p.rtable[(size_t)r * p.rt_stride + (pos64 >> p.page_shift)] : -1;
+        if (rp >= 0) {
+          const int64_t row = ((int64_t)rp << p.page_shift) + (pos64 & (((int64_t)1 << p.page_shift) - 1));
+          if (row < p.res_rows) src = p.att_res + (size_t)row * p.rec_bytes;
+        } else if ((int32_t)pos64 == newest) {
+          src = dbase + (size_t)p.B * p.rec_bytes;
+        } else if (sl >= 0) {
+          if (sl < p.B) src = dbase + (size_t)sl * p.rec_bytes;
+        } else {
+          src = p.host_base[r] + p.host_layer_off + (size_t)pos64 * p.rec_bytes;
+          mi = i;
+        }
+      }
+    }
+  }
+  if (lane < kTileRows / NW) {
+    asrc[e] = (uint64_t)src;
+    arow[e] = mi;
+  }
+  q_store(qv, qs);
+  __syncthreads();
+  u32x4 tv[kTU];
+  tile_load(tv, asrc);
+#pragma unroll
+  for (int u = 0; u < kTU; ++u) {
+    const int f = tid + u * NT;
+    if (f < kTileChunks) {
+      const int row = f / kRowChunks, c = f - row * kRowChunks;
+      *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
+      const int a = arow[row];
+      if (a >= 0) *((u32x4*)(p.att_stage + ((size_t)r * p.k + a) * (size_t)p.rec_bytes) + c) = tv[u];
+    }
+  }
+  __syncthreads();
+  float* part = p.part + ((size_t)r * S + (g - 1)) * kPartStride;
+  float* out = S == 1 ? p.att_out + (size_t)r * p.heads * kAttnDv : nullptr;
+  attend_tile(tile, qs, smem + F.scratch, f_n, p.att_scale * 1.4426950408889634f, part, out, p.heads);
 }
 
 template <int E, int KE, bool ATT>
 __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int outcome = resolve_body<E, KE, ATT>(p, smem);
   if constexpr (ATT) {
-    if (outcome == kDone) return;
-    // fetch workgroup g >= 1 attends over its share (chunk g - 1) of the selection
-    const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
-    const int S = p.G - 1;
-    const int f_lo = p.k * (g - 1) / S;
-    const int n_tok = p.k * g / S - f_lo;
-    const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G);
-    float* part = p.part + ((size_t)r * S + (g - 1)) * kPartStride;
-    float* out = S == 1 ? p.att_out + (size_t)r * p.heads * kAttnDv : nullptr;
-    __syncthreads();  // the tile and the query rows are in LDS
-    if (outcome == kError) {  // the request's output is NaN, as for unresolved slots
-      const float nan = __builtin_nanf("");
-      if (out) for (int f = threadIdx.x; f < p.heads * kAttnDv; f += NT) out[f] = nan;
-      else for (int f = threadIdx.x; f < kPartStride; f += NT) part[f] = nan;
+    if ((int)(blockIdx.x / p.R) > 0) {
+      fetch_attend(p, smem);
       return;
     }
-    attend_tile(smem + F.tile, smem + F.qs, smem, n_tok, p.att_scale * 1.4426950408889634f, part, out, p.heads);
   }
+  resolve_body<E, KE, ATT>(p, smem);
 }
 
 // Union of the verification rows of one speculative step ("HiSparse 深度解析" §6.5

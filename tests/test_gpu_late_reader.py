@@ -8,6 +8,10 @@ metadata is restored to its state before the launch except for the page table, w
 what the launch wrote, the hot buffer is restored (so the victim slots hold the evicted
 records again), and the same launch is run again.  Both runs must agree byte for byte: slots,
 counts, the whole workspace and the hot buffer.
+
+(The fused call, hs_resolve_attn, does not write the page table while its resolve kernel
+runs: its second kernel applies the updates, so no workgroup of the fused kernel can meet
+an entry of its own launch.)
 """
 import numpy as np
 import pytest
@@ -117,16 +121,3 @@ def test_capacity_blocks_published_page_table():
     finally:
         p.close()
 
-
-@pytest.mark.parametrize("t0", [0, 5])
-def test_fused_published_page_table(t0):
-    """The fused kernel: its fetch workgroups pick every record's source (hot slot or host)
-    from the page table at entry, so a late read must classify as an early one did."""
-    w = W["long"].scaled(L=2, ctx=32768, steps=6, append=False, force_newest=False)
-    log("fused long-shape R=1 L=2 t0=%d" % t0)
-    p = Pair(w, fused_heads=16)
-    try:
-        assert hk.hs_resolve_attn_wgs(p.h) > 0
-        assert replay_with_published_page_table(p, t0) > 0
-    finally:
-        p.close()
