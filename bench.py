@@ -260,12 +260,13 @@ def main():
         detail.update(measure_fp8(torch, hk, synth, dev))
         detail.update(measure_rows(torch, hk, synth, dev))
         detail.update(measure_short(torch, hk, synth, dev))
+        detail.update(measure_batched(torch, hk, synth, dev))
         detail["launch_latency_us"] = measure_empty(torch, hk)
         detail["hbm_copy_GBps"] = measure_hbm(torch, hk, dev)
         detail["link_ceiling_GBps"] = link["ceiling_GBps"]
         detail["link_dma_h2d_GBps"] = link["dma_GBps"]
         detail["link_zero_copy_GBps"] = link["zero_copy_GBps"]
-        for key in ("batched_cold_fetch_GBps", "long_cold_fetch_GBps"):
+        for key in ("batched_cold_fetch_GBps", "long_cold_fetch_GBps", "batched_steady_link_GBps"):
             detail[key.replace("GBps", "frac_of_link")] = detail[key] / link["ceiling_GBps"]
 
     # ---- roofline of the dominant kernel -------------------------------------------------
@@ -595,6 +596,56 @@ def measure_short(torch, hk, synth, dev, steps=64):
     us = np.array([[evs[t][l][0].elapsed_time(evs[t][l][1]) * 1e3 for l in range(L)] for t in range(steps)])
     cache.close()
     return {"short_fast_path_us_per_layer": float(np.median(us[2:]))}
+
+
+def measure_batched(torch, hk, synth, dev, layers=4, steps=16, warmup=4):
+    """The batched decode step: 32 requests, ctx 32768, k 2048, B 4096, every layer through
+    hs_resolve_attn (at 32 requests the call makes hs_resolve + hs_sparse_attn: 32 x 33
+    workgroups would not fit one wave of workgroups).  Four of the sixteen layers (the host
+    pool of all sixteen is 19.3 GB; every layer is independent and costs the same).  Steady
+    state after the cold step: selections/s, and the miss bytes per second over the host link,
+    which bounds this step."""
+    w = synth.WORKLOADS["batched"].scaled(L=layers, B=4096)
+    R, L, k, B = w.R, w.L, w.k, w.B
+    n = warmup + steps
+    lmax = w.max_positions(n)
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    tr = np.stack([np.stack([synth.selection_trace(w, r, l, n) for r in range(R)], axis=1) for l in range(L)],
+                  axis=1)
+    d_tr = torch.from_numpy(tr).to(dev)
+    d_q = torch.from_numpy(np.stack([synth.queries(R, L, t) for t in range(n)]).view(np.int16)).to(dev)
+    d_q = d_q.permute(0, 2, 1, 3, 4).contiguous()  # [steps][L][R][16][576]
+    d_ctx = torch.full((R,), w.ctx, dtype=torch.int32, device=dev)
+    d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n, L, R, 4), dtype=torch.int32, device=dev)
+    d_out = torch.empty((L, R, 16, 512), dtype=torch.float32, device=dev)
+    cs = torch.cuda.current_stream().cuda_stream
+
+    def step(t):
+        for l in range(L):
+            hk.hs_resolve_attn(cache.h, l, d_tr[t, l].data_ptr(), d_ctx.data_ptr(), d_slots[l].data_ptr(),
+                               d_stats[t, l].data_ptr(), 0, 0, d_q[t, l].data_ptr(), 16, 512, d_out[l].data_ptr(),
+                               576 ** -0.5, cs)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warmup, n):
+        step(t)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    st = d_stats.cpu().numpy()
+    assert st[..., 2].sum() == 0
+    miss_bytes = float(st[warmup:, :, :, 1].sum()) * REC
+    cache.close()
+    return {"batched_step_ms_4_layers": el / steps * 1e3,
+            "batched_us_per_layer": el / (steps * L) * 1e6,
+            "batched_selections_per_s": steps * L * R * k / el,
+            "batched_miss_rate": float(st[warmup:, ..., 1].sum() / (steps * L * R * k)),
+            "batched_steady_link_GBps": miss_bytes / el / 1e9}
 
 
 def measure_empty(torch, hk):
