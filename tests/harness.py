@@ -222,8 +222,9 @@ class Pair:
         att = self.d_att[ai].cpu().numpy()
         for r in range(nr):
             pos = expand(self.trace[t, ai, r], w.block_tokens)
-            rows = np.ascontiguousarray(self.ohost[r][l][pos.astype(np.int64)]).view(np.uint16)
-            K = oracle.attention.bf16_to_f64(rows)
+            recs = np.ascontiguousarray(self.ohost[r][l][pos.astype(np.int64)])
+            K = oracle.attention.fp8_records_to_f64(recs) if self.fp8 else \
+                oracle.attention.bf16_to_f64(recs.view(np.uint16))
             ref = oracle.attention.sparse_decode_attention_rows(q[r, l], K, SCALE)
             err = np.abs(att[r] - ref).max() / np.abs(ref).max()
             self.worst_attn = max(self.worst_attn, err)

@@ -191,6 +191,17 @@ def test_short_requests_cross_into_the_normal_path():
         p.close()
 
 
+def test_fp8_records_take_the_two_calls():
+    """FP8 latent-KV records: no fused kernel (it reads bf16 tiles), the call makes
+    hs_resolve + hs_sparse_attn with the FP8 attention kernel."""
+    w = W["long"].scaled(L=2, steps=4, ctx=32768)
+    p = Pair(w, fused_heads=16, fp8=True)
+    try:
+        run(p, expect_fused=False)
+    finally:
+        p.close()
+
+
 def test_configuration_without_the_fused_kernel():
     """32 requests x (2048 / 64 + 1) workgroups exceed one wave of workgroups: the call makes
     hs_resolve and hs_sparse_attn, with the same results."""
