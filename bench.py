@@ -261,12 +261,17 @@ def main():
         detail.update(measure_rows(torch, hk, synth, dev))
         detail.update(measure_short(torch, hk, synth, dev))
         detail.update(measure_batched(torch, hk, synth, dev))
+        detail.update(measure_capacity(torch, hk, synth, dev))
+        detail.update(measure_replay(torch, hk, synth, dev))
         detail["launch_latency_us"] = measure_empty(torch, hk)
         detail["hbm_copy_GBps"] = measure_hbm(torch, hk, dev)
         detail["link_ceiling_GBps"] = link["ceiling_GBps"]
         detail["link_dma_h2d_GBps"] = link["dma_GBps"]
         detail["link_zero_copy_GBps"] = link["zero_copy_GBps"]
-        for key in ("batched_cold_fetch_GBps", "long_cold_fetch_GBps", "batched_steady_link_GBps"):
+        detail["link_random_records_GBps"] = link["random_records_GBps"]
+        for key in ("batched_cold_fetch_GBps", "long_cold_fetch_GBps", "batched_steady_link_GBps",
+                    "capacity_cold_fetch_GBps", "capacity_steady_fetch_GBps", "replay_cold_GBps",
+                    "replay_steady_GBps", "replay_cold_kernels_GBps", "replay_steady_kernels_GBps"):
             detail[key.replace("GBps", "frac_of_link")] = detail[key] / link["ceiling_GBps"]
 
     # ---- roofline of the dominant kernel -------------------------------------------------
@@ -346,8 +351,23 @@ def measure_link(torch, hk, dev):
     e1.record(s)
     torch.cuda.synchronize()
     zc = 3 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # scattered 1152-byte records: 65536 distinct records at random places in the same buffer
+    nrec = 65536
+    idx = np.random.Generator(np.random.PCG64(7)).choice(n // REC, size=nrec, replace=False).astype(np.int32)
+    d_idx = torch.from_numpy(idx).to(dev)
+    d_rec = torch.empty((nrec, REC), dtype=torch.uint8, device=dev)
+    hk.hs_probe_host_records(src.data_ptr(), n // REC, REC, d_idx.data_ptr(), nrec, d_rec.data_ptr(), 1024,
+                             s.cuda_stream)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(3):
+        hk.hs_probe_host_records(src.data_ptr(), n // REC, REC, d_idx.data_ptr(), nrec, d_rec.data_ptr(), 1024,
+                                 s.cuda_stream)
+    e1.record(s)
+    torch.cuda.synchronize()
+    rec = 3 * nrec * REC / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
-    return {"dma_GBps": dma, "zero_copy_GBps": zc, "ceiling_GBps": max(dma, zc)}
+    return {"dma_GBps": dma, "zero_copy_GBps": zc, "ceiling_GBps": max(dma, zc), "random_records_GBps": rec}
 
 
 def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, resident=None):
@@ -355,7 +375,7 @@ def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, reside
     With `resident` (a ResidentSpec) a resident tier is bound and its block table follows
     the spec's per-step layout (table rewrites are outside the timed launches)."""
     R, L, k, B = w.R, w.L, w.k, w.B
-    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, newest_slot=w.append))
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, block_tokens=w.block_tokens, newest_slot=w.append))
     for r in range(R):
         synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
     if resident is not None:
@@ -428,6 +448,68 @@ def measure_fetch_heavy(torch, hk, synth, dev):
             "batched_cold_resolve_skip_io_us": float(us_skip[0, 0]),
             "batched_cold_fetch_GBps": b / (us_io[0, 0] * 1e-6) / 1e9,
             "batched_cold_io_added_us": float(us_io[0, 0] - us_skip[0, 0])}
+
+
+def measure_capacity(torch, hk, synth, dev, steps=24):
+    """Block selections (32 blocks of 64 tokens, 4 requests, 1,048,576-token context, B = 4096),
+    one layer: the cold launch (every token misses) and the steady state, miss bytes over the
+    whole RESOLVE kernel."""
+    wl = synth.WORKLOADS["capacity"].scaled(L=1)
+    tr = np.stack([np.stack([synth.selection_trace(wl, r, 0, steps) for r in range(wl.R)], axis=1)], axis=1)
+    us, st = run_resolve_only(torch, hk, synth, wl, dev, tr, wl.max_positions(steps), steps, 0)
+    miss_bytes = st[:, 0, :, 1].sum(axis=1) * REC  # [steps]
+    return {"capacity_cold_launch_bytes": float(miss_bytes[0]),
+            "capacity_cold_resolve_us": float(us[0, 0]),
+            "capacity_cold_fetch_GBps": float(miss_bytes[0] / (us[0, 0] * 1e-6) / 1e9),
+            "capacity_steady_resolve_us": float(np.median(us[2:, 0])),
+            "capacity_steady_miss_rate": float(st[2:, 0, :, 1].sum() / (st[2:, 0, :, :2].sum())),
+            "capacity_steady_fetch_GBps": float(miss_bytes[2:].sum() / (us[2:, 0].sum() * 1e-6) / 1e9)}
+
+
+def measure_replay(torch, hk, synth, dev, steps=12):
+    """Shared-layer replay: 16 requests, one anchor and its three shared layers, 131072-token
+    context, k = 2048, B = 4096.  Each step resolves the anchor with the miss plan recorded,
+    then times hs_prefetch_shared (three copy-only replay launches on the prefetch stream)
+    with events on that stream, and each replay kernel by its own start and end: plan bytes
+    (3 x misses x 1152) per second of the call and of the three kernels, cold and steady."""
+    wl = synth.WORKLOADS["shared"].scaled(L=4)
+    R, k, B = wl.R, wl.k, wl.B
+    lmax = wl.max_positions(steps)
+    cache = hk.HiSparse(hk.make_config(R, wl.L, lmax, k, B, layer_group=wl.group))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, wl.L, lmax, wl.ctx)
+    tr = np.stack([synth.selection_trace(wl, r, 0, steps) for r in range(R)], axis=1)  # [steps][R][k]
+    d_tr = torch.from_numpy(tr).to(dev)
+    d_ctx = torch.full((R,), wl.ctx, dtype=torch.int32, device=dev)
+    d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((steps, R, 4), dtype=torch.int32, device=dev)
+    cs = torch.cuda.current_stream()
+    ps = torch.cuda.Stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    hk.hs_timing_start(cache.h, steps * 4)  # per step: the anchor's RESOLVE, then three replays
+    for t in range(steps):
+        hk.hs_resolve(cache.h, 0, d_tr[t].data_ptr(), d_ctx.data_ptr(), d_slots.data_ptr(), d_stats[t].data_ptr(),
+                      0, hk.HS_RECORD_PLAN, cs.cuda_stream)
+        torch.cuda.synchronize()
+        ev[t][0].record(ps)
+        hk.hs_prefetch_shared(cache.h, 0, cs.cuda_stream, ps.cuda_stream)
+        ev[t][1].record(ps)
+        torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    kern = hk.hs_timing_read(cache.h, steps * 4).astype(np.float64).reshape(steps, 4)[:, 1:].sum(axis=1)
+    st = d_stats.cpu().numpy()
+    cache.close()
+    assert not st[..., 2].any()
+    plan_bytes = 3 * st[:, :, 1].sum(axis=1) * REC  # [steps]
+    return {"replay_cold_bytes": float(plan_bytes[0]),
+            "replay_cold_us": float(us[0]),
+            "replay_cold_GBps": float(plan_bytes[0] / (us[0] * 1e-6) / 1e9),
+            "replay_cold_kernels_GBps": float(plan_bytes[0] / (kern[0] * 1e-6) / 1e9),
+            "replay_steady_us": float(np.median(us[2:])),
+            "replay_steady_bytes": float(plan_bytes[2:].mean()),
+            "replay_steady_GBps": float(plan_bytes[2:].sum() / (us[2:].sum() * 1e-6) / 1e9),
+            "replay_steady_kernel_us": float(np.median(kern[2:]) / 3),
+            "replay_steady_kernels_GBps": float(plan_bytes[2:].sum() / (kern[2:].sum() * 1e-6) / 1e9)}
 
 
 def measure_all_hit(torch, hk, synth, dev):
@@ -650,13 +732,11 @@ def measure_batched(torch, hk, synth, dev, layers=4, steps=16, warmup=4):
 
 def measure_empty(torch, hk):
     s = torch.cuda.current_stream()
-    for _ in range(100):
-        hk.hs_probe_empty(s.cuda_stream)
+    hk.hs_probe_empty(100, s.cuda_stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
-    for _ in range(2000):
-        hk.hs_probe_empty(s.cuda_stream)
+    hk.hs_probe_empty(2000, s.cuda_stream)
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / 2000
@@ -679,10 +759,13 @@ def measure_hbm(torch, hk, dev):
 
 
 def cpu_baseline(synth, w, trace, n_steps, W, K, budget_s):
-    """The oracle as it stands, on this host's cores: one thread per layer cache, the same
-    trace; untimed through the warmup steps, then timed over the first timed steps that
-    fit the budget.  Same step: append + write-through, resolve, float64 attention."""
+    """The oracle as it stands, on this host's cores, over the same trace: one thread per layer
+    cache, then one thread for all of them.  Each leg starts from empty caches, runs the
+    warmup steps untimed and times the first timed steps that fit its budget.  Same step:
+    append + write-through, resolve, float64 attention."""
     from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
 
     import oracle
 
@@ -691,37 +774,61 @@ def cpu_baseline(synth, w, trace, n_steps, W, K, budget_s):
     host = [np.empty((L, lmax, REC), np.uint8) for _ in range(R)]
     for r in range(R):
         synth.fill_request(host[r], r, L, lmax, w.ctx)
-    caches = {(r, l): oracle.Cache(B, lmax, REC, newest_slot=True) for r in range(R) for l in range(L)}
+
+    def leg(threads, budget):
+        caches = {(r, l): oracle.Cache(B, lmax, REC, newest_slot=True) for r in range(R) for l in range(L)}
+        pool = ThreadPoolExecutor(max_workers=threads)
+
+        def layer_step(args):
+            t, r, l, q = args
+            p = w.ctx + t
+            c = caches[(r, l)]
+            c.append(p, synth.record(r, l, p), host[r][l])
+            out, _, _, _, _ = c.resolve(trace[t, l, r], p + 1, host[r][l])
+            oracle.attention.sparse_decode_attention(q[r, l], c.hot, out, 576 ** -0.5)
+            return out.size
+
+        def run_step(t):
+            q = synth.queries(R, L, t, heads=w.heads)
+            return sum(pool.map(layer_step, [(t, r, l, q) for r in range(R) for l in range(L)]))
+
+        for t in range(W):
+            run_step(t)
+        done, sel = 0, 0
+        t0 = time.perf_counter()
+        while done < K and time.perf_counter() - t0 < budget:
+            sel += run_step(W + done)
+            done += 1
+        el = time.perf_counter() - t0
+        pool.shutdown()
+        for c in caches.values():
+            c.close()
+        return sel / el, done
+
+    # one BLAS thread per caller, so that the pool's size is the number of threads used
+    # (numpy's BLAS would otherwise start its own threads inside every pool thread)
     threads = min(L * R, os.cpu_count() or 1)
-    pool = ThreadPoolExecutor(max_workers=threads)
-
-    def layer_step(args):
-        t, r, l, q = args
-        p = w.ctx + t
-        c = caches[(r, l)]
-        c.append(p, synth.record(r, l, p), host[r][l])
-        out, _, _, _, _ = c.resolve(trace[t, l, r], p + 1, host[r][l])
-        oracle.attention.sparse_decode_attention(q[r, l], c.hot, out, 576 ** -0.5)
-        return out.size
-
-    def run_step(t):
-        q = synth.queries(R, L, t, heads=w.heads)
-        return sum(pool.map(layer_step, [(t, r, l, q) for r in range(R) for l in range(L)]))
-
-    for t in range(W):
-        run_step(t)
-    done, sel = 0, 0
-    t0 = time.perf_counter()
-    while done < K and time.perf_counter() - t0 < budget_s:
-        sel += run_step(W + done)
-        done += 1
-    el = time.perf_counter() - t0
-    pool.shutdown()
-    for c in caches.values():
-        c.close()
-    return {"value": sel / el, "unit": "selections/s", "cores": threads, "kind": "oracle",
+    with threadpool_limits(limits=1):
+        value, done = leg(threads, budget_s)
+        value1, done1 = leg(1, budget_s / 2)
+    return {"value": value, "unit": "selections/s", "cores": threads, "kind": "oracle",
             "sample": "%d of the %d timed decode steps (after the same %d warmup steps), all %d layers; "
-                      "append + resolve + float64 attention per layer" % (done, K, W, L)}
+                      "append + resolve + float64 attention per layer" % (done, K, W, L),
+            "single_thread_value": value1,
+            "single_thread_sample": "the first %d timed steps, same start, one thread" % done1,
+            "host_cpu": host_cpu(), "nproc": os.cpu_count()}
+
+
+def host_cpu():
+    """Model name of this host's processor (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -55,7 +55,7 @@ EXPORTS = (
     "hs_wait_layer", "hs_sparse_attn", "hs_resolve_attn", "hs_resolve_attn_wgs", "hs_export_state", "hs_page_table", "hs_plan", "hs_admit_short",
     "hs_reset_request",
     "hs_destroy", "hs_last_error", "hs_resolve_wgs", "hs_probe_host_read", "hs_probe_copy",
-    "hs_probe_empty", "hs_timing_start", "hs_timing_read",
+    "hs_probe_host_records", "hs_probe_empty", "hs_timing_start", "hs_timing_read",
 )
 
 
@@ -95,7 +95,8 @@ def _load():
         "hs_resolve_wgs": (i32, [vp]),
         "hs_probe_host_read": (i32, [vp, sz, vp, i32, vp]),
         "hs_probe_copy": (i32, [vp, vp, sz, vp]),
-        "hs_probe_empty": (i32, [vp]),
+        "hs_probe_host_records": (i32, [vp, i64, i32, vp, i32, vp, i32, vp]),
+        "hs_probe_empty": (i32, [i32, vp]),
         "hs_timing_start": (i32, [vp, i32]),
         "hs_timing_read": (i32, [vp, vp, i32]),
     }
@@ -219,8 +220,13 @@ def hs_probe_copy(d_src, d_dst, nbytes, stream):
     _check(_lib.hs_probe_copy(d_src, d_dst, nbytes, stream or None))
 
 
-def hs_probe_empty(stream):
-    _check(_lib.hs_probe_empty(stream or None))
+def hs_probe_host_records(host_src, src_records, rec_bytes, d_index, n, d_dst, wgs, stream):
+    _check(_lib.hs_probe_host_records(host_src, src_records, rec_bytes, d_index, n, d_dst, wgs,
+                                      stream or None))
+
+
+def hs_probe_empty(n, stream):
+    _check(_lib.hs_probe_empty(n, stream or None))
 
 
 def hs_timing_start(h, n):

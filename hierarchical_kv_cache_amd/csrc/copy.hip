@@ -1,6 +1,8 @@
 // Byte-moving kernels around RESOLVE: write-through of the newest token,
 // copy-only replay of an anchor's miss plan, metadata init/export, and the
 // link/latency probes used for measurement.
+#include <hip/hip_ext.h>
+
 #include "hs_internal.h"
 
 namespace hs {
@@ -78,27 +80,103 @@ __global__ void __launch_bounds__(kCopyThreads) backup_kernel(AppendParams p) {
 
 // Copy-only replay of an anchor's miss plan into one shared layer
 // (gentlecold.top §3.6 and §5.6): the same (position, slot) pairs, this
-// layer's own records.  A small fixed number of workgroups strides over the
-// flattened (request, miss, 16-byte chunk) space so the copy leaves most of
-// the GPU to the compute stream.
+// layer's own records.  A small fixed number of workgroups does it, so the
+// copy leaves most of the GPU to the compute stream.  Up to kReplayFlatR
+// requests, every workgroup builds the prefix of the per-request miss counts
+// in LDS and the grid strides over the flattened (request, miss, 16-byte
+// chunk) space, so the launch stays balanced however the misses fall over
+// the requests.  Beyond that, ceil(grid / R) workgroups take each request's
+// own chunk space (a workgroup takes every grid-th request when R > grid).
+constexpr int kReplayFlatR = 1024;
+constexpr int kReplayU = 8;  // loads in flight per thread
+static_assert(4 * kCopyThreads >= kReplayFlatR, "each thread sums four requests' counts");
+
+__device__ __forceinline__ void replay_flat(const ReplayParams& p, int* pre, int* scan) {
+  const int t = threadIdx.x;
+  const int C = p.rec_bytes >> 4;
+  // pre[r] = misses of requests before r, pre[R] = all (R <= 4 * kCopyThreads)
+  int mv[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * t + i;
+    mv[i] = r < p.R ? (int)p.ctrl[r * 4 + 2] : 0;
+    sum += mv[i];
+  }
+  scan[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < kCopyThreads; off <<= 1) {
+    const int add = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  int run = scan[t] - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * t + i;
+    if (r < p.R) pre[r] = run;
+    run += mv[i];
+  }
+  if (t == kCopyThreads - 1) pre[p.R] = scan[t];
+  __syncthreads();
+  const int64_t total = (int64_t)pre[p.R] * C;
+  const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
+  for (int64_t f0 = (int64_t)blockIdx.x * kCopyThreads + t; f0 < total; f0 += stride * kReplayU) {
+    u32x4 v[kReplayU];
+    int rr[kReplayU], jj[kReplayU], cc[kReplayU];
+#pragma unroll
+    for (int u = 0; u < kReplayU; ++u) {
+      const int64_t f = f0 + u * stride;
+      if (f < total) {
+        const int j = (int)(f / C);
+        cc[u] = (int)(f - (int64_t)j * C);
+        int lo = 0, hi = p.R - 1;  // the request r with pre[r] <= j < pre[r + 1]
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        rr[u] = lo;
+        jj[u] = j - pre[lo];
+        const int32_t* ppos = p.plan + (size_t)lo * 2 * p.plan_k;
+        v[u] = load_host16(p.host_base[lo] + p.host_layer_off + (size_t)ppos[jj[u]] * p.rec_bytes +
+                           16 * (size_t)cc[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kReplayU; ++u)
+      if (f0 + u * stride < total) {
+        const int32_t* pslot = p.plan + (size_t)rr[u] * 2 * p.plan_k + p.plan_k;
+        uint8_t* dbase = p.hot + (size_t)rr[u] * p.hot_req_stride + p.hot_layer_off;
+        *((u32x4*)(dbase + (size_t)pslot[jj[u]] * p.rec_bytes) + cc[u]) = v[u];
+      }
+  }
+}
+
 __global__ void __launch_bounds__(kCopyThreads) replay_kernel(ReplayParams p) {
+  __shared__ int pre[kReplayFlatR + 1];
+  __shared__ int scan[kCopyThreads];
+  if (p.R <= kReplayFlatR) {
+    replay_flat(p, pre, scan);
+    return;
+  }
   const int C = p.rec_bytes >> 4;
   const float invC = 1.0f / (float)C;
-  const int stride = gridDim.x * blockDim.x;
-  const int t0 = blockIdx.x * blockDim.x + threadIdx.x;
-  constexpr int U = 4;
-  for (int r = 0; r < p.R; ++r) {
+  const int P = ((int)gridDim.x + p.R - 1) / p.R;  // workgroups per request
+  const int stride = P * (int)blockDim.x;
+  for (int pair = blockIdx.x; pair < p.R * P; pair += gridDim.x) {
+    const int r = pair / P;
+    const int t0 = (pair - r * P) * (int)blockDim.x + (int)threadIdx.x;
     const int m = (int)p.ctrl[r * 4 + 2];
     const int total = m * C;
     const int32_t* ppos = p.plan + (size_t)r * 2 * p.plan_k;
     const int32_t* pslot = ppos + p.plan_k;
     const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
     uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
-    for (int f0 = t0; f0 < total; f0 += stride * U) {
-      u32x4 v[U];
-      int jj[U], cc[U];
+    for (int f0 = t0; f0 < total; f0 += stride * kReplayU) {
+      u32x4 v[kReplayU];
+      int jj[kReplayU], cc[kReplayU];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < kReplayU; ++u) {
         const int f = f0 + u * stride;
         if (f < total) {
           split_index(f, C, invC, jj[u], cc[u]);
@@ -106,7 +184,7 @@ __global__ void __launch_bounds__(kCopyThreads) replay_kernel(ReplayParams p) {
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < kReplayU; ++u)
         if (f0 + u * stride < total)
           *((u32x4*)(dbase + (size_t)pslot[jj[u]] * p.rec_bytes) + cc[u]) = v[u];
     }
@@ -205,6 +283,26 @@ __global__ void __launch_bounds__(kCopyThreads) probe_copy_kernel(const u32x4* _
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Gathers n records at random indices of a pinned host array into a dense
+// device array, flattened over (record, 16-byte chunk): the link rate a fetch of
+// scattered 1152-byte records can reach.  Indices outside [0, src_records) are
+// skipped.
+__global__ void __launch_bounds__(kCopyThreads) probe_host_records_kernel(const unsigned char* __restrict__ src,
+                                                                          const int32_t* __restrict__ index,
+                                                                          int n, int C, int64_t src_records,
+                                                                          unsigned char* __restrict__ dst) {
+  const int total = n * C;
+  const float invC = 1.0f / (float)C;
+  for (int f = blockIdx.x * blockDim.x + threadIdx.x; f < total; f += gridDim.x * blockDim.x) {
+    int j, c;
+    split_index(f, C, invC, j, c);
+    const int32_t i = index[j];
+    if (i < 0 || (int64_t)i >= src_records) continue;
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(src + (size_t)i * C * 16) + c);
+    *((u32x4*)(dst + (size_t)j * C * 16) + c) = v;
+  }
+}
+
 __global__ void probe_empty_kernel() {}
 
 int grid_for(size_t work, int per_block, int cap) {
@@ -228,8 +326,12 @@ hipError_t launch_backup(const AppendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s) {
-  hipLaunchKernelGGL(replay_kernel, dim3(wgs), dim3(kCopyThreads), 0, s, p);
+hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s, const KernelTiming* tm) {
+  if (tm && tm->start) {
+    hipExtLaunchKernelGGL(replay_kernel, dim3(wgs), dim3(kCopyThreads), 0, s, tm->start, tm->stop, 0u, p);
+  } else {
+    hipLaunchKernelGGL(replay_kernel, dim3(wgs), dim3(kCopyThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -265,8 +367,15 @@ hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_probe_empty(hipStream_t s) {
-  hipLaunchKernelGGL(probe_empty_kernel, dim3(1), dim3(64), 0, s);
+hipError_t launch_probe_host_records(const void* src, const int32_t* index, int n, int rec_bytes,
+                                     int64_t src_records, void* dst, int wgs, hipStream_t s) {
+  hipLaunchKernelGGL(probe_host_records_kernel, dim3(wgs), dim3(kCopyThreads), 0, s, (const unsigned char*)src,
+                     index, n, rec_bytes >> 4, src_records, (unsigned char*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_empty(int n, hipStream_t s) {
+  for (int i = 0; i < n; ++i) hipLaunchKernelGGL(probe_empty_kernel, dim3(1), dim3(64), 0, s);
   return hipGetLastError();
 }
 

@@ -586,7 +586,7 @@ hs_status hs_prefetch_shared(hs_handle h, int32_t anchor_layer, void* compute, v
     p.host_layer_off = h->host_layer_off(l); p.hot_req_stride = h->hot_req_stride();
     p.hot_layer_off = h->hot_layer_off(l); p.R = h->cfg.num_requests; p.plan_k = h->lay.kmax;
     p.rec_bytes = h->cfg.record_bytes;
-    HS_HIP(launch_replay(p, h->replay_wgs, ps));
+    HS_HIP(launch_replay(p, h->replay_wgs, ps, h->next_timing()));
     HS_HIP(hipEventRecord(h->ev_layer[l], ps));
   }
   HS_HIP(hipEventRecord(h->ev_plan_free[a], ps));
@@ -711,6 +711,16 @@ hs_status hs_probe_copy(const void* d_src, void* d_dst, size_t bytes, void* stre
   return HS_OK;
 }
 
+hs_status hs_probe_host_records(const void* host_src, int64_t src_records, int32_t rec_bytes,
+                                const int32_t* d_index, int32_t n, void* d_dst, int32_t wgs, void* stream) {
+  if (!host_src || !d_index || !d_dst || wgs < 1 || n < 0 || src_records < 0 || rec_bytes < 16 ||
+      rec_bytes % 16 || rec_bytes > 16384 || (int64_t)n * (rec_bytes / 16) > (1ll << 30))
+    return fail(HS_EINVAL, "bad probe arguments");
+  if (n == 0) return HS_OK;
+  HS_HIP(launch_probe_host_records(host_src, d_index, n, rec_bytes, src_records, d_dst, wgs, (hipStream_t)stream));
+  return HS_OK;
+}
+
 hs_status hs_timing_start(hs_handle h, int32_t n) {
   hs_status st;
   if ((st = check_handle(h))) return st;
@@ -741,8 +751,9 @@ int32_t hs_timing_read(hs_handle h, float* us_out, int32_t n) {
   return (int32_t)m;
 }
 
-hs_status hs_probe_empty(void* stream) {
-  HS_HIP(launch_probe_empty((hipStream_t)stream));
+hs_status hs_probe_empty(int32_t n, void* stream) {
+  if (n < 0 || n > (1 << 20)) return fail(HS_EINVAL, "n must be in [0, 2^20]");
+  HS_HIP(launch_probe_empty(n, (hipStream_t)stream));
   return HS_OK;
 }
 

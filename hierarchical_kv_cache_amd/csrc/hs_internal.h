@@ -304,7 +304,7 @@ constexpr int kUnionMaxEntries = 8192;  // rows * top_k of one speculative resol
 hipError_t set_resolve_lds_limit(size_t lds_bytes);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_backup(const AppendParams& p, hipStream_t s);
-hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s);
+hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s, const KernelTiming* tm = nullptr);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s);  // the S chunk partials -> out
 hipError_t launch_attn_finish(const FinishParams& p, hipStream_t s);
@@ -313,7 +313,9 @@ hipError_t launch_init(const InitParams& p, hipStream_t s);
 hipError_t launch_admit(const AdmitParams& p, hipStream_t s);
 hipError_t launch_probe_host_read(const void* src, size_t bytes, void* sink, int wgs, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
-hipError_t launch_probe_empty(hipStream_t s);
+hipError_t launch_probe_host_records(const void* src, const int32_t* index, int n, int rec_bytes,
+                                     int64_t src_records, void* dst, int wgs, hipStream_t s);
+hipError_t launch_probe_empty(int n, hipStream_t s);
 
 // attention partial record: [16][512] output accumulators, then [16] max, [16] sum
 constexpr int kAttnMaxHeads = 16;

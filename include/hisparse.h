@@ -308,15 +308,26 @@ int32_t hs_resolve_attn_wgs(hs_handle h);
  * `wgs` workgroups (a zero-copy link probe).  d_sink: device, >= 16 KiB. */
 hs_status hs_probe_host_read(const void* host_src, size_t bytes, void* d_sink, int32_t wgs,
                              void* stream);
+/* Gathers the n records d_index[0..n) (device int32, record numbers) of a pinned host array of
+ * src_records records of rec_bytes each (a multiple of 16, at most 16384) into the dense device
+ * array d_dst [n][rec_bytes], with 16-byte non-temporal loads from `wgs` workgroups: the link
+ * rate of scattered record reads.  Indices outside [0, src_records) are skipped (their d_dst
+ * rows are left as they were).  HS_EINVAL for null pointers, bad sizes or n * rec_bytes / 16
+ * above 2^30. */
+hs_status hs_probe_host_records(const void* host_src, int64_t src_records, int32_t rec_bytes,
+                                const int32_t* d_index, int32_t n, void* d_dst, int32_t wgs, void* stream);
 /* Plain device-to-device copy kernel (16-byte vectors), for counter calibration. */
 hs_status hs_probe_copy(const void* d_src, void* d_dst, size_t bytes, void* stream);
-/* An empty kernel (launch-latency probe). */
-hs_status hs_probe_empty(void* stream);
+/* n empty kernels back to back on one stream, launched from this call (the launch-latency
+ * probe, free of the caller's per-call cost).  HS_EINVAL unless 0 <= n <= 2^20. */
+hs_status hs_probe_empty(int32_t n, void* stream);
 
-/* Kernel durations of the next n RESOLVE launches of h (hs_resolve's kernel, or the fused
- * kernel of hs_resolve_attn; not the merge), stamped by the kernels' own start and end
- * (hipExtLaunchKernel events), so no event between launches adds to them.  hs_timing_start
- * creates n event pairs (dropping earlier ones); launches beyond n are not timed. */
+/* Kernel durations of the next n RESOLVE and replay launches of h, in call order
+ * (hs_resolve's kernel, the fused kernel of hs_resolve_attn (not its finish kernel), and each
+ * shared layer's replay kernel of hs_prefetch_shared), stamped by the kernels' own start and
+ * end (hipExtLaunchKernel events), so no event between launches adds to them.
+ * hs_timing_start creates n event pairs (dropping earlier ones); launches beyond n are not
+ * timed. */
 hs_status hs_timing_start(hs_handle h, int32_t n);
 /* Waits for the timed launches and writes the first min(n, launched) durations in
  * microseconds, in launch order, to host memory us_out; returns that count (< 0: error). */

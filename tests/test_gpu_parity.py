@@ -142,6 +142,24 @@ def test_shared_index_prefetch_scaled():
     p.close()
 
 
+@pytest.mark.parametrize("R", [1, 3, 40, 1100])
+def test_shared_replay_request_counts(R):
+    """The replay kernel over one, a few and many requests: up to 1024 requests the launch
+    strides over all requests' misses at once; 1100 requests take the per-request split
+    (each workgroup takes every grid-th request)."""
+    w = W["shared"].scaled(R=R, L=4, ctx=8192, k=256, B=512) if R <= 40 else \
+        W["shared"].scaled(R=R, L=4, ctx=512, k=64, B=128)
+    log("shared replay R=%d" % R)
+    p = Pair(w, steps=5)
+    try:
+        for _ in range(5):
+            p.step_gpu_and_oracle()
+        p.check_state()
+        p.check_hot(layers=range(w.L))
+    finally:
+        p.close()
+
+
 def test_capacity_blocks_scaled():
     """Block-id selections (32 blocks of 64 tokens), recency-Zipf trace, on 2 x 2 caches with
     a 64K context; blocks are expanded in the kernel."""
