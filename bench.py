@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing")
     ap.add_argument("--quick", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--measure", choices=sorted(SECONDARY), default=None,
+                    help="run only this secondary measurement (and the 64 MiB copy that calibrates "
+                         "the HBM-traffic counters) and print its figures as one JSON line")
     return ap.parse_args()
 
 
@@ -104,6 +107,10 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.measure:
+        calibration_copy(torch, hk, dev)
+        print(json.dumps(SECONDARY[args.measure](torch, hk, synth, dev)))
+        return
     w = synth.WORKLOADS["long"]
     W, K = args.warmup, args.steps
     n_steps = W + K
@@ -245,12 +252,7 @@ def main():
     # ---- secondary measurements --------------------------------------------------------
     link = {}
     if args.quick:
-        # one plain copy of known size: the calibration kernel of the HBM-traffic counters
-        a = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        hk.hs_probe_copy(a.data_ptr(), b.data_ptr(), a.numel(), cs)
-        torch.cuda.synchronize()
-        del a, b
+        calibration_copy(torch, hk, dev)
     else:
         link = measure_link(torch, hk, dev)
         detail.update(measure_fetch(torch, hk, synth, w, dev, trace, lmax))
@@ -324,6 +326,15 @@ def main():
         "detail": detail,
     }
     print(json.dumps(line))
+
+
+def calibration_copy(torch, hk, dev):
+    """One plain copy of known size (64 MiB): the calibration kernel of the HBM-traffic counters."""
+    a = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    hk.hs_probe_copy(a.data_ptr(), b.data_ptr(), a.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def measure_link(torch, hk, dev):
@@ -830,6 +841,15 @@ def host_cpu():
         pass
     return None
 
+
+# secondary measurements that --measure can run on their own (name -> f(torch, hk, synth, dev))
+SECONDARY = {
+    "replay": measure_replay,
+    "capacity": measure_capacity,
+    "batched": measure_batched,
+    "fetch_heavy": measure_fetch_heavy,
+    "all_hit": measure_all_hit,
+}
 
 if __name__ == "__main__":
     main()
