@@ -389,16 +389,31 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
 // The fused call's second kernel.  Workgroups [0, merge_blocks): one per (request, head),
 // four waves for the four 128-channel quarters: the chunk merge, or NaN rows when workgroup
 // 0 of the fused kernel reported an error for the request (with one chunk the fetch
-// workgroup wrote the output itself).  The other workgroups stride over every request's
-// misses: the page-table updates (the evicted position host only, the new position in its
-// victim slot, tagged with the launch's generation) and the 16-byte chunks of the missed
-// records from the staging area into their victim slots.  No two misses share a slot or a
-// position, and evicted positions are not selected, so the writes are independent.
+// workgroup wrote the output itself).  The other workgroups take the misses of every request
+// whose resolve succeeded: each builds the prefix of their miss counts in LDS (the fused
+// kernel runs at most kFinishThreads requests), then the grid strides over all requests'
+// misses at once for the page-table updates (the evicted position host only, the new
+// position in its victim slot, tagged with the launch's generation), and over their 16-byte
+// chunks to copy the missed records from the staging area into their victim slots.  No two
+// misses share a slot or a position, and evicted positions are not selected, so the writes
+// are independent.
 constexpr int kFinishThreads = 256;
 constexpr int kFinishUnroll = 4;
+constexpr int kFinishCopyBlocks = 256;
+
+// the request r with pre[r] <= j < pre[r + 1] (pre non-decreasing, pre[R] > j)
+__device__ __forceinline__ int request_of(const int* pre, int R, int j) {
+  int lo = 0, hi = R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 __global__ void __launch_bounds__(kFinishThreads) attn_finish_kernel(FinishParams p) {
   __shared__ float fac[kFinishThreads / 64][kAttnMaxChunks];
+  __shared__ int pre[kFinishThreads + 1];
   const int b = blockIdx.x, tid = threadIdx.x;
   if (b < p.merge_blocks) {
     const int r = b / p.heads, hh = b - r * p.heads;
@@ -412,42 +427,56 @@ __global__ void __launch_bounds__(kFinishThreads) attn_finish_kernel(FinishParam
     merge_quarter(p.part + (size_t)r * p.S * kPartStride, p.S, hh, tid >> 6, tid & 63, fac[tid >> 6], orow);
     return;
   }
+  // pre[r] = misses of the applying requests before r (p.R <= kFinishThreads)
+  const int nr = p.num_reqs ? min(*p.num_reqs, p.R) : p.R;
+  const int mine = (tid < nr && p.hdr[tid * 4] == 0) ? (int)p.hdr[tid * 4 + 1] : 0;
+  pre[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kFinishThreads; off <<= 1) {
+    const int add = tid >= off ? pre[tid - off] : 0;
+    __syncthreads();
+    pre[tid] += add;
+    __syncthreads();
+  }
+  const int incl = pre[tid];
+  __syncthreads();
+  pre[tid] = incl - mine;
+  if (tid == kFinishThreads - 1) pre[kFinishThreads] = incl;
+  __syncthreads();
+  const int M = pre[kFinishThreads];
   const int C = p.rec_bytes >> 4;
   const int nthreads = (gridDim.x - p.merge_blocks) * kFinishThreads;
   const int t0 = (b - p.merge_blocks) * kFinishThreads + tid;
-  for (int r = 0; r < p.R; ++r) {
-    if (p.num_reqs && r >= *p.num_reqs) break;
-    const uint32_t* h = p.hdr + (size_t)r * 4;
-    if (h[0] != 0) continue;
-    const int m = (int)h[1];
-    const uint32_t gen = h[2];
-    const int32_t* ml = p.mlist + (size_t)r * p.k * 4;
+  for (int j = t0; j < M; j += nthreads) {
+    const int r = request_of(pre, p.R, j);
+    const int32_t* ml = p.mlist + ((size_t)r * p.k + (j - pre[r])) * 4;
     uint64_t* pt = p.page_table + (size_t)r * p.max_positions;
-    for (int j = t0; j < m; j += nthreads) {
-      const int32_t old = ml[4 * j + 2];
-      if (old >= 0) pt[old] = kPtHostOnly;
-      pt[ml[4 * j + 3]] = pt_entry(ml[4 * j + 1], gen);
-    }
-    const uint8_t* st = p.stage + (size_t)r * p.k * p.rec_bytes;
-    uint8_t* dst = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
-    const int total = m * C;
-    for (int f0 = t0; f0 < total; f0 += nthreads * kFinishUnroll) {
-      u32x4 v[kFinishUnroll];
-      int slot[kFinishUnroll], cc[kFinishUnroll];
+    const int32_t old = ml[2];
+    if (old >= 0) pt[old] = kPtHostOnly;
+    pt[ml[3]] = pt_entry(ml[1], p.hdr[r * 4 + 2]);
+  }
+  const int total = M * C;  // M <= 256 * 4096
+  for (int f0 = t0; f0 < total; f0 += nthreads * kFinishUnroll) {
+    u32x4 v[kFinishUnroll];
+    int slot[kFinishUnroll], cc[kFinishUnroll], rr[kFinishUnroll];
 #pragma unroll
-      for (int u = 0; u < kFinishUnroll; ++u) {
-        const int f = f0 + u * nthreads;
-        if (f < total) {
-          const int j = f / C;
-          cc[u] = f - j * C;
-          slot[u] = ml[4 * j + 1];
-          v[u] = *((const u32x4*)(st + (size_t)ml[4 * j] * p.rec_bytes) + cc[u]);
-        }
+    for (int u = 0; u < kFinishUnroll; ++u) {
+      const int f = f0 + u * nthreads;
+      if (f < total) {
+        const int j = f / C;
+        cc[u] = f - j * C;
+        const int r = request_of(pre, p.R, j);
+        rr[u] = r;
+        const int32_t* ml = p.mlist + ((size_t)r * p.k + (j - pre[r])) * 4;
+        slot[u] = ml[1];
+        v[u] = *((const u32x4*)(p.stage + ((size_t)r * p.k + ml[0]) * p.rec_bytes) + cc[u]);
       }
-#pragma unroll
-      for (int u = 0; u < kFinishUnroll; ++u)
-        if (f0 + u * nthreads < total) *((u32x4*)(dst + (size_t)slot[u] * p.rec_bytes) + cc[u]) = v[u];
     }
+#pragma unroll
+    for (int u = 0; u < kFinishUnroll; ++u)
+      if (f0 + u * nthreads < total)
+        *((u32x4*)(p.hot + (size_t)rr[u] * p.hot_req_stride + p.hot_layer_off + (size_t)slot[u] * p.rec_bytes) +
+          cc[u]) = v[u];
   }
 }
 
@@ -468,8 +497,8 @@ hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s) {
 }
 
 hipError_t launch_attn_finish(const FinishParams& p, hipStream_t s) {
-  constexpr int kCopyBlocks = 128;  // 32K threads: a cold step's 2048 misses in ~5 strides
-  hipLaunchKernelGGL(attn_finish_kernel, dim3(p.merge_blocks + kCopyBlocks), dim3(kFinishThreads), 0, s, p);
+  if (p.R > kFinishThreads) return hipErrorInvalidValue;  // one prefix entry per request
+  hipLaunchKernelGGL(attn_finish_kernel, dim3(p.merge_blocks + kFinishCopyBlocks), dim3(kFinishThreads), 0, s, p);
   return hipGetLastError();
 }
 

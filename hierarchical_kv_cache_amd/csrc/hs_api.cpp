@@ -63,16 +63,22 @@ int attn_chunks(const hs_config& c) {
   return S;
 }
 
-// Fused RESOLVE + attention (hs_resolve_attn): one fetch workgroup per 64 selected entries
-// plus workgroup 0, all of them resident at once (one workgroup per CU, 256 CUs), bf16
-// records of 576 values.  Returns the chunk count S, or 0 when the configuration does not
-// take the fused kernel (whether LDS suffices is checked per device in hs_create).
-int fused_chunks(const hs_config& c) {
+// Fused RESOLVE + attention (hs_resolve_attn): per request workgroup 0 and S fetch
+// workgroups, all of them resident at once (one workgroup per CU, 256 CUs), bf16 records of
+// 576 values.  A fetch workgroup attends T tiles of 64 entries: the smallest T for which
+// R (S + 1) <= 256 with S = ceil(k / 64 T).  Returns S (and T), or 0 when the configuration
+// does not take the fused kernel (whether LDS suffices is checked per device in hs_create).
+int fused_chunks(const hs_config& c, int* tiles = nullptr) {
   if ((c.flags & HS_CFG_RECORD_FP8) || c.record_bytes != kAttnDk * 2) return 0;
   if (!fused_supported(c.top_k, c.buffer_slots)) return 0;
-  const int S = (c.top_k + kTileRows - 1) / kTileRows;
-  if (int64_t(c.num_requests) * (S + 1) > 256) return 0;
-  return S;
+  for (int T = 1; T <= kFusedMaxTiles; ++T) {
+    const int S = (c.top_k + kTileRows * T - 1) / (kTileRows * T);
+    if (int64_t(c.num_requests) * (S + 1) <= 256) {
+      if (tiles) *tiles = T;
+      return S;
+    }
+  }
+  return 0;
 }
 
 Layout make_layout(const hs_config& c) {
@@ -162,7 +168,7 @@ struct hs_ctx {
   size_t lds_bytes = 0;
   int spec_hash_bits = 0, union_hash_bits = 0;  // RESOLVE of a union, and the union kernel
   size_t spec_lds_bytes = 0;
-  int att_G = 0, att_hash_bits = 0;  // fused RESOLVE + attention; att_G 0: not available
+  int att_G = 0, att_T = 1, att_hash_bits = 0;  // fused RESOLVE + attention; att_G 0: not available
   size_t att_lds = 0;
   // measurement aid: kernel-timed RESOLVE launches (hs_timing_start / hs_timing_read)
   std::vector<KernelTiming> tm;
@@ -330,16 +336,18 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
     }
   }
   // fused RESOLVE + attention: G = chunks + 1, when its LDS fits (a half-full hash if need be)
-  if (const int Sf = fused_chunks(*cfg)) {
+  int T = 1;
+  if (const int Sf = fused_chunks(*cfg, &T)) {
     const int G = Sf + 1;
     int bits = resolve_hash_bits(cfg->top_k);
-    size_t lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G).total;
+    size_t lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G, T).total;
     if (lds > prop.sharedMemPerBlock) {
       bits -= 1;
-      lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G).total;
+      lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G, T).total;
     }
     if (lds <= prop.sharedMemPerBlock) {
       h->att_G = G;
+      h->att_T = T;
       h->att_hash_bits = bits;
       h->att_lds = lds;
     }
@@ -464,7 +472,7 @@ hs_status hs_resolve_attn(hs_handle h, int32_t layer, const int32_t* d_sel, cons
   p.G = h->att_G; p.hash_bits = h->att_hash_bits;
   p.q = (const uint16_t*)d_q; p.part = h->attn_part(layer); p.att_out = d_out;
   p.att_res = h->res ? h->res + size_t(layer) * size_t(h->res_rows) * size_t(h->cfg.record_bytes) : nullptr;
-  p.heads = heads; p.att_scale = scale;
+  p.heads = heads; p.att_tiles = h->att_T; p.att_scale = scale;
   p.att_hdr = (uint32_t*)(h->ws + h->lay.att_hdr); p.att_mlist = (int32_t*)(h->ws + h->lay.att_mlist);
   p.att_stage = h->ws + h->lay.att_stage;
   HS_HIP(launch_resolve_attn(p, h->att_lds, s, h->next_timing()));

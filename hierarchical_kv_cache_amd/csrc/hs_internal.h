@@ -107,10 +107,12 @@ __host__ __device__ inline ResolveLds resolve_lds(int k, int B, int hash_bits, i
 int resolve_elems_per_thread(int k, int B);
 
 // Fused RESOLVE + attention.  Workgroup 0 uses the resolve carve-up; each fetch workgroup
-// (one tile of <= 64 selected records) the record tile, the query rows, per tile row the
-// miss's list index and the record's address, and the attention scratch (scores' maxima and
-// sums, P).  The dynamic LDS of the launch is the larger of the two.
-constexpr int kTileRows = 64;        // records per fetch workgroup
+// (a share of <= 64 T selected records, attended one 64-row tile at a time) the record tile,
+// the query rows, per share entry the record's address and the miss's list index, and the
+// attention scratch (scores' maxima and sums, P).  The dynamic LDS of the launch is the
+// larger of the two.
+constexpr int kTileRows = 64;        // records per tile
+constexpr int kFusedMaxTiles = 16;   // tiles per fetch workgroup (share entries <= 1024 threads)
 constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (292 words): the 16 rows
                                      // of a QK^T operand read fall on 16 distinct 4-bank groups, and
                                      // the quarter-waves of a P V operand read on disjoint banks
@@ -119,13 +121,13 @@ constexpr int kAttnScratch = 2 * 4 * 16 * 4 + 2 * 2 * 16 * 32 * 2;  // maxima, s
 struct FusedLds {
   size_t tile, qs, arow, asrc, scratch, total;
 };
-__host__ __device__ inline FusedLds fused_lds(int k, int B, int hash_bits, int G) {
+__host__ __device__ inline FusedLds fused_lds(int k, int B, int hash_bits, int G, int T) {
   FusedLds F;
   F.tile = 0;
   F.qs = F.tile + size_t(kTileRows) * kTileStride;
-  F.arow = F.qs + 16 * size_t(kQStride);
-  F.asrc = F.arow + 4 * size_t(kTileRows);
-  F.scratch = F.asrc + 8 * size_t(kTileRows);
+  F.asrc = F.qs + 16 * size_t(kQStride);
+  F.arow = F.asrc + 8 * size_t(kTileRows) * T;
+  F.scratch = F.arow + 4 * size_t(kTileRows) * T;
   const size_t fetch = align_up(F.scratch + kAttnScratch, 16);
   const size_t resolve = resolve_lds(k, B, hash_bits, G).total;
   F.total = fetch > resolve ? fetch : resolve;
@@ -165,7 +167,7 @@ struct ResolveParams {
   int32_t R, B, Bpad, k, kb, bt_shift, rec_bytes, G, hash_bits;
   uint32_t flags;            // HS_RECORD_PLAN | HS_SKIP_IO | kHasNewest
   // fused attention (resolve_kernel<.., true>): G - 1 fetch workgroups per request, each
-  // attends over its share of the selection (<= 64 entries)
+  // attends over its share of the selection (<= 64 att_tiles entries, a tile at a time)
   const uint16_t* q;         // [R][heads][576] bf16
   float* part;               // [R][G-1][kPartStride] chunk partials (G > 2)
   float* att_out;            // [R][heads][512] (written directly when G == 2)
@@ -173,7 +175,7 @@ struct ResolveParams {
   uint32_t* att_hdr;         // [R][4] workgroup 0's report: error bits, misses, page-table generation
   int32_t* att_mlist;        // [R][k][4] per miss: list index, victim slot, evicted position, position
   uint8_t* att_stage;        // [R][k][rec] missed records by list index
-  int32_t heads;
+  int32_t heads, att_tiles;
   float att_scale;
 };
 

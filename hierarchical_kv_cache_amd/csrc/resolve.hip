@@ -230,17 +230,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
+// Running attention of one fetch workgroup over its tiles (online softmax).  Lane (wave w,
+// quarter qd, column col) holds, for heads 4 qd + i, the running maximum m and sum l of the
+// scores (log2 units) and the unnormalised output o of channels 32 w + 16 c + col.
+struct AttnAcc {
+  float m[4], l[4];
+  f32x4 o[2];
+};
+
+__device__ __forceinline__ void acc_init(AttnAcc& a) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a.m[i] = -INFINITY;
+    a.l[i] = 0.0f;
+  }
+  a.o[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  a.o[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
 // Attention of the 16 query heads over one tile of n_tok records held in LDS (sparse decode
 // attention, "HiSparse 深度解析" (gentlecold.top) §5.4: the records of the published slots;
-// key = the record's 576 bf16, value = its first 512).  Waves 0-3 compute the 16 x 16 score
-// blocks of tokens 16w .. 16w+15 on v_mfma_f32_16x16x32_bf16 (18 k-steps), every head's
-// maximum and sum over the tile follow, and all 16 waves accumulate P V for 32 output
-// channels each.  P is split into bf16 hi + lo parts so the fp32 probabilities survive the
-// bf16 operand.  Writes the chunk's partial (unnormalised o, max and sum in log2 units) for
-// the merge, or the normalised output when the request has one chunk.
+// key = the record's 576 bf16, value = its first 512), folded into the running state.  Waves
+// 0-3 compute the 16 x 16 score blocks of tokens 16w .. 16w+15 on v_mfma_f32_16x16x32_bf16
+// (18 k-steps); each head's new maximum is the larger of the running one and the tile's, the
+// probabilities are taken against it, and every wave rescales its running sum and output by
+// 2^(old max - new max) before all 16 waves accumulate P V for 32 output channels each.  P is
+// split into bf16 hi + lo parts so the fp32 probabilities survive the bf16 operand.
 __device__ __forceinline__ void attend_tile(const unsigned char* tile, const unsigned char* qs,
-                                            unsigned char* scratch, int n_tok, float sl2, float* part,
-                                            float* out, int heads) {
+                                            unsigned char* scratch, int n_tok, float sl2, AttnAcc& acc) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, qd = lane >> 4;
   float* smax = (float*)scratch;                 // [4][16]
   float* ssum = smax + 64;                       // [4][16]
@@ -270,6 +287,14 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
     }
   }
   __syncthreads();
+  float mnew[4], alpha[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = qd * 4 + i;
+    const float mt = fmaxf(fmaxf(smax[hh], smax[16 + hh]), fmaxf(smax[32 + hh], smax[48 + hh]));
+    mnew[i] = fmaxf(acc.m[i], mt);     // finite: every tile has a valid row
+    alpha[i] = exp2f(acc.m[i] - mnew[i]);  // 0 on the first tile
+  }
   if (w < 4) {
     const int tl = 16 * w + col;
     const int bk = tl >> 5, t32 = tl & 31;
@@ -277,8 +302,7 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = qd * 4 + i;
-      const float m = fmaxf(fmaxf(smax[hh], smax[16 + hh]), fmaxf(smax[32 + hh], smax[48 + hh]));
-      const float pv = exp2f(sv[i] - m);
+      const float pv = exp2f(sv[i] - mnew[i]);
       const float l = row16_sum(pv);
       if (col == 0) ssum[w * 16 + hh] = l;
       const uint16_t hi = f32_to_bf16_rne(pv);
@@ -287,8 +311,15 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
     }
   }
   __syncthreads();
-  // o[head][channel] = p v over the tile; wave w owns channels 32 w .. 32 w + 31
-  f32x4 o[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = qd * 4 + i;
+    acc.l[i] = acc.l[i] * alpha[i] + (ssum[hh] + ssum[16 + hh] + ssum[32 + hh] + ssum[48 + hh]);
+    acc.m[i] = mnew[i];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc.o[c][i] *= alpha[i];
+  }
+  // o[head][channel] += p v over the tile; wave w owns channels 32 w .. 32 w + 31
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const bf16x8 ahi = *(const bf16x8*)&phi[(b * 16 + col) * 32 + qd * 8];
@@ -299,29 +330,38 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
       bf16x8 vv;
 #pragma unroll
       for (int j = 0; j < 8; ++j) vv[j] = *(const __bf16*)(vb + 4 * j * kTileStride + c * 32);
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, vv, o[c], 0, 0, 0);
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vv, o[c], 0, 0, 0);
+      acc.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, vv, acc.o[c], 0, 0, 0);
+      acc.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vv, acc.o[c], 0, 0, 0);
     }
   }
+}
+
+// The share's result: its partial (unnormalised o, maximum and sum in log2 units) for the
+// merge, or the normalised output rows of the heads asked for when the request has one share.
+__device__ __forceinline__ void attend_write(const AttnAcc& acc, float* part, float* out, int heads) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, qd = lane >> 4;
   // o[c][i]: head 4 qd + i, channel 32 w + 16 c + col
-  if (out) {  // one chunk: normalise and write the output rows of the heads asked for
+  if (out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = qd * 4 + i;
       if (hh >= heads) continue;
-      const float inv = 1.0f / (ssum[hh] + ssum[16 + hh] + ssum[32 + hh] + ssum[48 + hh]);
+      const float inv = 1.0f / acc.l[i];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) out[hh * kAttnDv + 32 * w + 16 * c + col] = o[c][i] * inv;
+      for (int c = 0; c < 2; ++c) out[hh * kAttnDv + 32 * w + 16 * c + col] = acc.o[c][i] * inv;
     }
     return;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) part[(qd * 4 + i) * kAttnDv + 32 * w + 16 * c + col] = o[c][i];
-  if (tid < 16) {
-    part[16 * kAttnDv + tid] = fmaxf(fmaxf(smax[tid], smax[16 + tid]), fmaxf(smax[32 + tid], smax[48 + tid]));
-    part[16 * kAttnDv + 16 + tid] = ssum[tid] + ssum[16 + tid] + ssum[32 + tid] + ssum[48 + tid];
+    for (int c = 0; c < 2; ++c) part[(qd * 4 + i) * kAttnDv + 32 * w + 16 * c + col] = acc.o[c][i];
+  if (w == 0 && col == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      part[16 * kAttnDv + qd * 4 + i] = acc.m[i];
+      part[16 * kAttnDv + 16 + qd * 4 + i] = acc.l[i];
+    }
   }
 }
 
@@ -889,84 +929,95 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
 }
 
 // A fetch workgroup g >= 1 of the fused kernel: attention over its share (chunk g - 1, at
-// most 64 entries) of the selection.  It does not resolve.  Each share entry's record is
-// where the page table (stable while the fused kernel runs: workgroup 0 leaves its updates
-// to the finish kernel) and the resident tier put it: a resident row, the newest slot, the
-// hot slot of a hit, or for a miss the host record.  The records are loaded into registers
-// (5 x 16 bytes per thread), then written to the LDS tile, the missed ones also to the
-// staging area (by list index) from which the finish kernel copies them into their victim
-// slots, so host bytes cross the link once.  Entries in error (out of range, resident rows
-// outside the pool) load a finite filler row; workgroup 0 reports the error and the finish
-// kernel makes the request's output NaN.
+// most 64 att_tiles entries) of the selection, one 64-row tile at a time.  It does not
+// resolve.  Each share entry's record is where the page table (stable while the fused kernel
+// runs: workgroup 0 leaves its updates to the finish kernel) and the resident tier put it: a
+// resident row, the newest slot, the hot slot of a hit, or for a miss the host record.  All
+// share entries' record addresses are found first, in one pass.  A tile's records are loaded
+// into registers (5 x 16 bytes per thread) and written to the LDS tile, the missed ones also
+// to the staging area (by list index) from which the finish kernel copies them into their
+// victim slots, so host bytes cross the link once; the next tile's loads are issued before
+// the current tile is attended, so they fly meanwhile.  Entries in error (out of range,
+// resident rows outside the pool) load a finite filler row; workgroup 0 reports the error
+// and the finish kernel makes the request's output NaN.
 __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned char* smem) {
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
   if (p.num_reqs && r >= *p.num_reqs) return;
   const int S = p.G - 1;
   const int f_lo = p.k * (g - 1) / S;  // (32-bit: k * G < 2^23)
-  const int f_n = p.k * g / S - f_lo;
-  const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G);
+  const int f_n = p.k * g / S - f_lo;  // <= 64 att_tiles
+  const int nt = (f_n + kTileRows - 1) / kTileRows;
+  const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G, p.att_tiles);
   unsigned char* tile = smem + F.tile;
   unsigned char* qs = smem + F.qs;
-  int32_t* arow = (int32_t*)(smem + F.arow);   // list index of the miss in each row, -1 otherwise
-  uint64_t* asrc = (uint64_t*)(smem + F.asrc);  // record address of each row
+  int32_t* arow = (int32_t*)(smem + F.arow);   // list index of the miss of each share entry, -1 otherwise
+  uint64_t* asrc = (uint64_t*)(smem + F.asrc);  // record address of each share entry
   const uint8_t* filler = (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);
   const uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   u32x4 qv[kQU];
   q_load(qv, p.q, r, p.heads);
-  // share entry e = lane * NW + wid: lanes 0..3 of every wave, all 64 rows of the tile
+  // share entry e = lane * NW + wid: the first tile's 64 rows on lanes 0..3 of every wave
   const int e = lane * NW + wid;
-  const uint8_t* src = filler;
-  int32_t mi = -1;
-  if (lane < kTileRows / NW && e < f_n) {
-    const int i = f_lo + e;
-    const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
-    const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
-    const bool short_path = p.ctrl[r * 4 + 3] != 0 && ctx <= p.B;  // slot = position
-    const int32_t raw = p.sel[(size_t)r * p.kb + (p.bt_shift ? (i >> p.bt_shift) : i)];
-    const int64_t pos64 = p.bt_shift ? ((int64_t)raw << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)raw;
-    if (pos64 >= 0 && pos64 < ctx) {
-      if (short_path) {
-        src = dbase + (size_t)pos64 * p.rec_bytes;
-      } else {
-        const int32_t sl = (int32_t)(uint32_t)p.page_table[(size_t)r * p.max_positions + pos64];
-        const int32_t rp = p.rtable ? p.rtable[(size_t)r * p.rt_stride + (pos64 >> p.page_shift)] : -1;
-        if (rp >= 0) {
-          const int64_t row = ((int64_t)rp << p.page_shift) + (pos64 & (((int64_t)1 << p.page_shift) - 1));
-          if (row < p.res_rows) src = p.att_res + (size_t)row * p.rec_bytes;
-        } else if ((int32_t)pos64 == newest) {
-          src = dbase + (size_t)p.B * p.rec_bytes;
-        } else if (sl >= 0) {
-          if (sl < p.B) src = dbase + (size_t)sl * p.rec_bytes;
+  if (e < nt * kTileRows) {
+    const uint8_t* src = filler;
+    int32_t mi = -1;
+    if (e < f_n) {
+      const int i = f_lo + e;
+      const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
+      const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
+      const bool short_path = p.ctrl[r * 4 + 3] != 0 && ctx <= p.B;  // slot = position
+      const int32_t raw = p.sel[(size_t)r * p.kb + (p.bt_shift ? (i >> p.bt_shift) : i)];
+      const int64_t pos64 = p.bt_shift ? ((int64_t)raw << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)raw;
+      if (pos64 >= 0 && pos64 < ctx) {
+        if (short_path) {
+          src = dbase + (size_t)pos64 * p.rec_bytes;
         } else {
-          src = p.host_base[r] + p.host_layer_off + (size_t)pos64 * p.rec_bytes;
-          mi = i;
+          const int32_t sl = (int32_t)(uint32_t)p.page_table[(size_t)r * p.max_positions + pos64];
+          const int32_t rp = p.rtable ? p.rtable[(size_t)r * p.rt_stride + (pos64 >> p.page_shift)] : -1;
+          if (rp >= 0) {
+            const int64_t row = ((int64_t)rp << p.page_shift) + (pos64 & (((int64_t)1 << p.page_shift) - 1));
+            if (row < p.res_rows) src = p.att_res + (size_t)row * p.rec_bytes;
+          } else if ((int32_t)pos64 == newest) {
+            src = dbase + (size_t)p.B * p.rec_bytes;
+          } else if (sl >= 0) {
+            if (sl < p.B) src = dbase + (size_t)sl * p.rec_bytes;
+          } else {
+            src = p.host_base[r] + p.host_layer_off + (size_t)pos64 * p.rec_bytes;
+            mi = i;
+          }
         }
       }
     }
-  }
-  if (lane < kTileRows / NW) {
     asrc[e] = (uint64_t)src;
     arow[e] = mi;
   }
   q_store(qv, qs);
   __syncthreads();
+  const float sl2 = p.att_scale * 1.4426950408889634f;
   u32x4 tv[kTU];
   tile_load(tv, asrc);
+  AttnAcc acc;
+  acc_init(acc);
+  for (int t = 0; t < nt; ++t) {
+    if (t > 0) __syncthreads();  // the previous tile's readers are done with the tile and P
 #pragma unroll
-  for (int u = 0; u < kTU; ++u) {
-    const int f = tid + u * NT;
-    if (f < kTileChunks) {
-      const int row = f / kRowChunks, c = f - row * kRowChunks;
-      *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
-      const int a = arow[row];
-      if (a >= 0) *((u32x4*)(p.att_stage + ((size_t)r * p.k + a) * (size_t)p.rec_bytes) + c) = tv[u];
+    for (int u = 0; u < kTU; ++u) {
+      const int f = tid + u * NT;
+      if (f < kTileChunks) {
+        const int row = f / kRowChunks, c = f - row * kRowChunks;
+        *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
+        const int a = arow[t * kTileRows + row];
+        if (a >= 0) *((u32x4*)(p.att_stage + ((size_t)r * p.k + a) * (size_t)p.rec_bytes) + c) = tv[u];
+      }
     }
+    if (t + 1 < nt) tile_load(tv, asrc + (t + 1) * kTileRows);
+    __syncthreads();
+    attend_tile(tile, qs, smem + F.scratch, min(kTileRows, f_n - t * kTileRows), sl2, acc);
   }
-  __syncthreads();
   float* part = p.part + ((size_t)r * S + (g - 1)) * kPartStride;
   float* out = S == 1 ? p.att_out + (size_t)r * p.heads * kAttnDv : nullptr;
-  attend_tile(tile, qs, smem + F.scratch, f_n, p.att_scale * 1.4426950408889634f, part, out, p.heads);
+  attend_write(acc, part, out, p.heads);
 }
 
 template <int E, int KE, bool ATT>

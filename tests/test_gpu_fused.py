@@ -203,13 +203,32 @@ def test_fp8_records_take_the_two_calls():
 
 
 def test_configuration_without_the_fused_kernel():
-    """32 requests x (2048 / 64 + 1) workgroups exceed one wave of workgroups: the call makes
-    hs_resolve and hs_sparse_attn, with the same results."""
-    w = W["batched"].scaled(L=1, steps=2, B=4096)
-    log("batched R=32: two calls")
+    """130 requests x 2 workgroups exceed one wave of workgroups even with one fetch
+    workgroup per request: the call makes hs_resolve and hs_sparse_attn, with the same
+    results."""
+    w = W["tiny"].scaled(R=130, steps=3)
+    log("tiny R=130: two calls")
     p = Pair(w, fused_heads=16)
     try:
         run(p, expect_fused=False)
+    finally:
+        p.close()
+
+
+@pytest.mark.parametrize("R,k,tiles", [(32, 2048, 5), (8, 2048, 2), (16, 1000, 2), (40, 2048, 7)])
+def test_fetch_workgroups_over_several_tiles(R, k, tiles):
+    """Fetch workgroups that attend several 64-row tiles with a running maximum, sum and
+    output: the batched shape (32 requests, 7 shares of 292-293 entries, the last tile of a
+    share partly filled), shares of exactly two tiles, a ragged second tile (125-entry
+    shares) and 40 requests (5 shares of 409-410 entries)."""
+    w = W["batched"].scaled(R=R, L=1, k=k, B=4096, steps=3)
+    S = -(-k // (64 * tiles))
+    assert R * (S + 1) <= 256 and (tiles == 1 or R * (-(-k // (64 * (tiles - 1))) + 1) > 256)
+    log("batched R=%d k=%d: %d fetch workgroups of %d tiles per request" % (R, k, S, tiles))
+    p = Pair(w, fused_heads=16)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) == S + 1
+        run(p)
     finally:
         p.close()
 
