@@ -693,8 +693,8 @@ def measure_short(torch, hk, synth, dev, steps=64):
 
 def measure_batched(torch, hk, synth, dev, layers=4, steps=16, warmup=4):
     """The batched decode step: 32 requests, ctx 32768, k 2048, B 4096, every layer through
-    hs_resolve_attn (at 32 requests the call makes hs_resolve + hs_sparse_attn: 32 x 33
-    workgroups would not fit one wave of workgroups).  Four of the sixteen layers (the host
+    hs_resolve_attn (the fused kernel: per request one resolving workgroup and 7 fetch
+    workgroups of 5 tiles each, then the finish kernel).  Four of the sixteen layers (the host
     pool of all sixteen is 19.3 GB; every layer is independent and costs the same).  Steady
     state after the cold step: selections/s, and the miss bytes per second over the host link,
     which bounds this step."""
@@ -733,8 +733,10 @@ def measure_batched(torch, hk, synth, dev, layers=4, steps=16, warmup=4):
     st = d_stats.cpu().numpy()
     assert st[..., 2].sum() == 0
     miss_bytes = float(st[warmup:, :, :, 1].sum()) * REC
+    wgs = hk.hs_resolve_attn_wgs(cache.h)
     cache.close()
-    return {"batched_step_ms_4_layers": el / steps * 1e3,
+    return {"batched_fused_wgs_per_request": wgs,
+            "batched_step_ms_4_layers": el / steps * 1e3,
             "batched_us_per_layer": el / (steps * L) * 1e6,
             "batched_selections_per_s": steps * L * R * k / el,
             "batched_miss_rate": float(st[warmup:, ..., 1].sum() / (steps * L * R * k)),

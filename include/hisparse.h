@@ -240,15 +240,18 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
  *   hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, stream);
  *   hs_sparse_attn(h, layer, d_q, heads, value_dim, d_slots_out, d_out, scale, d_num_reqs, stream);
  * with the same arguments: the same slots, counts, metadata and hot bytes bit for bit, the
- * same attention up to the order of the fp32 sums.  The fused kernel gives every 64
- * selected entries of a request a workgroup that loads their records (hot slot, resident
- * row or, for a miss, the host record) into LDS while the resolve stages run, stores the
- * misses into their victim slots and attends over the records it holds; a merge kernel then
- * combines the chunks of each (request, head).  It applies to bf16 records of 576 values
- * (record_bytes 1152), top_k <= 4096, buffer_slots <= 8192 and num_requests *
- * (ceil(top_k / 64) + 1) <= 256 (hs_resolve_attn_wgs > 0); otherwise this call makes the
- * two calls above.  HS_SKIP_IO is not allowed (the attention reads the records).  Errors as
- * for the two calls; a request with error bits gets NaN output rows.
+ * same attention up to the order of the fp32 sums.  In the fused kernel one workgroup per
+ * request resolves, and S more each take a share of <= 64 T selected entries: they load
+ * the share's records (hot slot, resident row or, for a miss, the host record) 64 at a time
+ * into LDS while the resolve runs, stage the misses, and attend over the tiles with a
+ * running maximum and sum.  A second kernel merges the shares of each (request, head),
+ * applies the page-table updates and copies the staged misses into their victim slots.  T is
+ * the smallest value in [1, 16] with num_requests * (S + 1) <= 256, S = ceil(top_k / 64 T),
+ * so that all workgroups run at once.  It applies to bf16 records of 576 values
+ * (record_bytes 1152), top_k <= 4096, buffer_slots <= 8192 and such a T (so at most 128
+ * requests; hs_resolve_attn_wgs > 0); otherwise this call makes the two calls above.
+ * HS_SKIP_IO is not allowed (the attention reads the records).  Errors as for the two calls;
+ * a request with error bits gets NaN output rows.
  */
 hs_status hs_resolve_attn(hs_handle h, int32_t layer, const int32_t* d_sel, const int32_t* d_ctx_len,
                           int32_t* d_slots_out, hs_stats* d_stats, const int32_t* d_num_reqs, uint32_t flags,
@@ -299,7 +302,8 @@ const char* hs_last_error(void);
 /* Workgroups per request hs_resolve launches for this handle. */
 int32_t hs_resolve_wgs(hs_handle h);
 
-/* Workgroups per request of the fused kernel of hs_resolve_attn (0: the call makes two). */
+/* Workgroups per request of the fused kernel of hs_resolve_attn, S + 1 (0: the call makes
+ * two). */
 int32_t hs_resolve_attn_wgs(hs_handle h);
 
 /* ---- measurement aids (no part of the cache) ---------------------------------------------- */
