@@ -851,6 +851,7 @@ SECONDARY = {
     "batched": measure_batched,
     "fetch_heavy": measure_fetch_heavy,
     "all_hit": measure_all_hit,
+    "rows": measure_rows,
 }
 
 if __name__ == "__main__":

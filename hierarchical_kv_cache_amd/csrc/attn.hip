@@ -14,6 +14,8 @@
 // bf16 operand.  A second small kernel merges the per-chunk partials (max,
 // sum, unnormalised output) of each (request, head).  With R >= 8 all chunks
 // of a request run on one XCD.
+#include <algorithm>
+
 #include "hs_internal.h"
 
 namespace hs {
@@ -399,7 +401,7 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(AttnParams p) {
 // are independent.
 constexpr int kFinishThreads = 256;
 constexpr int kFinishUnroll = 4;
-constexpr int kFinishCopyBlocks = 256;
+constexpr int kFinishMaxCopyBlocks = 1024;
 
 // the request r with pre[r] <= j < pre[r + 1] (pre non-decreasing, pre[R] > j)
 __device__ __forceinline__ int request_of(const int* pre, int R, int j) {
@@ -498,7 +500,11 @@ hipError_t launch_attn_merge(const AttnParams& p, hipStream_t s) {
 
 hipError_t launch_attn_finish(const FinishParams& p, hipStream_t s) {
   if (p.R > kFinishThreads) return hipErrorInvalidValue;  // one prefix entry per request
-  hipLaunchKernelGGL(attn_finish_kernel, dim3(p.merge_blocks + kFinishCopyBlocks), dim3(kFinishThreads), 0, s, p);
+  // enough copy workgroups for every selected entry's chunks in one stride (all misses)
+  const int64_t chunks = (int64_t)p.R * p.k * (p.rec_bytes >> 4);
+  const int64_t per_block = (int64_t)kFinishThreads * kFinishUnroll;
+  const int copy = (int)std::min<int64_t>(kFinishMaxCopyBlocks, (chunks + per_block - 1) / per_block);
+  hipLaunchKernelGGL(attn_finish_kernel, dim3(p.merge_blocks + copy), dim3(kFinishThreads), 0, s, p);
   return hipGetLastError();
 }
 
