@@ -327,8 +327,9 @@ hs_status hs_probe_copy(const void* d_src, void* d_dst, size_t bytes, void* stre
 hs_status hs_probe_empty(int32_t n, void* stream);
 
 /* Kernel durations of the next n RESOLVE and replay launches of h, in call order
- * (hs_resolve's kernel, the fused kernel of hs_resolve_attn (not its finish kernel), and each
- * shared layer's replay kernel of hs_prefetch_shared), stamped by the kernels' own start and
+ * (hs_resolve's kernel, the fused kernel of hs_resolve_attn (not its finish kernel), the
+ * RESOLVE kernel of hs_resolve_rows (not its union and scatter kernels), and each shared
+ * layer's replay kernel of hs_prefetch_shared), stamped by the kernels' own start and
  * end (hipExtLaunchKernel events), so no event between launches adds to them.
  * hs_timing_start creates n event pairs (dropping earlier ones); launches beyond n are not
  * timed. */
