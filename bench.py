@@ -302,6 +302,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(synth, w, trace, n_steps, W, K, args.cpu_seconds)
+        if not args.quick:
+            detail["configs"] = cpu_baseline_configs(torch, hk, synth, dev)
+            for row in detail["configs"]:
+                if "link_ceiling_GBps" in detail:
+                    row["gpu_miss_frac_of_link"] = row["gpu_miss_GBps"] / detail["link_ceiling_GBps"]
 
     cache.close()
     line = {
@@ -381,14 +386,17 @@ def measure_link(torch, hk, dev):
     return {"dma_GBps": dma, "zero_copy_GBps": zc, "ceiling_GBps": max(dma, zc), "random_records_GBps": rec}
 
 
-def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, resident=None):
+def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, resident=None, cache=None):
     """RESOLVE alone over `steps` steps of a trace on a fresh cache; per-launch µs per step.
     With `resident` (a ResidentSpec) a resident tier is bound and its block table follows
-    the spec's per-step layout (table rewrites are outside the timed launches)."""
+    the spec's per-step layout (table rewrites are outside the timed launches).  `cache`: a
+    fresh, filled handle to use (and leave open) instead of a new one."""
     R, L, k, B = w.R, w.L, w.k, w.B
-    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, block_tokens=w.block_tokens, newest_slot=w.append))
-    for r in range(R):
-        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    own = cache is None
+    if own:
+        cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, block_tokens=w.block_tokens, newest_slot=w.append))
+        for r in range(R):
+            synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
     if resident is not None:
         from synth.resident import resident_layout
         P = resident.page_tokens
@@ -422,7 +430,8 @@ def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, reside
     torch.cuda.synchronize()
     us = hk.hs_timing_read(cache.h, steps * L).astype(np.float64).reshape(steps, L)
     st = d_stats.cpu().numpy()
-    cache.close()
+    if own:
+        cache.close()
     return us, st
 
 
@@ -830,6 +839,86 @@ def cpu_baseline(synth, w, trace, n_steps, W, K, budget_s):
             "single_thread_value": value1,
             "single_thread_sample": "the first %d timed steps, same start, one thread" % done1,
             "host_cpu": host_cpu(), "nproc": os.cpu_count()}
+
+
+def cpu_baseline_configs(torch, hk, synth, dev, budget_s=3.0):
+    """Each workload side by side: GPU RESOLVE (hs_resolve, every launch stamped by its own
+    start and end) and the oracle on this host's cores, the same seeded trace from the same
+    empty start, steady-state steps (the cold step and the next excluded).  The oracle reads
+    the records from the library's pinned pool (filled by the same generator; nothing writes
+    it here) and runs one thread per (request, layer) cache; it times the steady steps that
+    fit its budget.  Long runs without the appended token here (RESOLVE only; the decode step
+    with write-through and attention is the headline).  The shared-index workload's row is its
+    anchor layer (the replay is measured on its own).  Selections/s count every selected
+    token; miss GB/s are missed record bytes over the same time."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    W = synth.WORKLOADS
+    cases = [("tiny", W["tiny"], 32),
+             ("long (no append)", W["long"].scaled(append=False, force_newest=False), 24),
+             ("batched B=2048", W["batched"].scaled(L=2, B=2048), 16),
+             ("batched B=4096", W["batched"].scaled(L=2, B=4096), 16),
+             ("batched B=8192", W["batched"].scaled(L=2, B=8192), 16),
+             ("shared (anchor)", W["shared"].scaled(L=1, group=1), 16),
+             ("capacity (blocks)", W["capacity"].scaled(L=1), 24)]
+    link = None
+    out = []
+    threads_max = min(16, os.cpu_count() or 1)
+    for name, w, steps in cases:
+        R, L, k, B = w.R, w.L, w.k, w.B
+        lmax = w.max_positions(steps)
+        trace = np.stack([np.stack([synth.selection_trace(w, r, l, steps) for r in range(R)], axis=1)
+                          for l in range(L)], axis=1)  # [steps][L][R][kb]
+        cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, block_tokens=w.block_tokens))
+        for r in range(R):
+            synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+        # GPU; then the oracle reads the same pool (RESOLVE does not write it)
+        us, st = run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, 0, cache=cache)
+        gpu_t = float(us[2:].sum()) * 1e-6
+        gpu_sel = (steps - 2) * L * R * k / gpu_t
+        gpu_miss = float(st[2:, :, :, 1].sum()) * REC / gpu_t / 1e9
+        # oracle
+        caches = {(r, l): oracle.Cache(B, lmax, REC) for r in range(R) for l in range(L)}
+        base = {r: cache.host_pool_address(r) for r in range(R)}
+        threads = min(R * L, threads_max)
+        pool = ThreadPoolExecutor(max_workers=threads)
+
+        def one(args):
+            t, r, l = args
+            sel = trace[t, l, r]
+            if w.block_tokens > 1:
+                sel = oracle.expand_blocks(sel, w.block_tokens)
+            _, _, m, _, _ = caches[(r, l)].resolve(sel, w.ctx, base[r] + l * lmax * REC)
+            return m
+
+        def step(t):
+            return sum(pool.map(one, [(t, r, l) for r in range(R) for l in range(L)]))
+
+        step(0)
+        step(1)
+        done, misses = 0, 0
+        t0 = time.perf_counter()
+        while 2 + done < steps and time.perf_counter() - t0 < budget_s:
+            misses += step(2 + done)
+            done += 1
+        el = time.perf_counter() - t0
+        pool.shutdown()
+        exp = int(st[2:2 + done, :, :, 1].sum())
+        assert misses == exp, (name, misses, exp)  # the same trace, the same misses
+        for c in caches.values():
+            c.close()
+        cache.close()
+        row = {"workload": name, "requests": R, "layers": L, "top_k": k, "buffer_slots": B,
+               "miss_rate": float(st[2:, :, :, 1].sum() / ((steps - 2) * L * R * k)),
+               "gpu_selections_per_s": gpu_sel, "gpu_miss_GBps": gpu_miss,
+               "gpu_resolve_us_per_launch": float(us[2:].mean()),
+               "oracle_selections_per_s": done * L * R * k / el if done else None,
+               "oracle_miss_GBps": misses * REC / el / 1e9 if done else None,
+               "oracle_threads": threads, "oracle_steps": done}
+        out.append(row)
+    return out
 
 
 def host_cpu():
