@@ -132,14 +132,16 @@ def test_padded_requests_untouched():
         p.close()
 
 
-def test_errors_give_nan_rows_and_leave_state():
+@pytest.mark.parametrize("R,wgs", [(3, 5), (60, 3)])
+def test_errors_give_nan_rows_and_leave_state(R, wgs):
     """A duplicate in one request: its error bits, its output rows NaN, nothing of it changes;
-    the other requests resolve and attend as usual."""
-    R, k, B, lmax, ctx = 3, 256, 512, 8192, 6000
+    the other requests resolve and attend as usual.  With 60 requests the fetch workgroups
+    attend two tiles each."""
+    k, B, lmax, ctx = 256, 512, 8192, 6000
     cfg = hk.make_config(R, 1, lmax, k, B)
     c = hk.HiSparse(cfg)
     try:
-        assert hk.hs_resolve_attn_wgs(c.h) == 5
+        assert hk.hs_resolve_attn_wgs(c.h) == wgs
         for r in range(R):
             synth.fill_request(c.host_pool_address(r), r, 1, lmax, lmax)
         caches = [oracle.Cache(B, lmax, 1152) for _ in range(R)]
@@ -300,5 +302,58 @@ def test_graph_capture_replays_match_oracle():
                     assert np.abs(o[l, r] - o_ref).max() <= 2e-3 * np.abs(o_ref).max(), (t, l, r)
             p.t += 1
         p.check_state()
+    finally:
+        p.close()
+
+
+def test_several_tiles_with_resident_tier():
+    """Eight requests (two tiles per fetch workgroup): resident rows, hot rows and misses
+    across tile boundaries."""
+    w = W["long"].scaled(R=8, L=1, ctx=65536, steps=4, append=False, force_newest=False)
+    log("long R=8 with a resident window: 17 workgroups of 2 tiles")
+    p = Pair(w, fused_heads=16, resident=ResidentSpec(page_tokens=64, window_tokens=16384, old_frac=0.1,
+                                                      spill_every=1, churn=0.05))
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) == 17
+        run(p)
+    finally:
+        p.close()
+
+
+def test_several_tiles_capacity_blocks():
+    w = W["capacity"].scaled(R=8, L=1, ctx=262144, steps=4)
+    log("capacity blocks R=8: 17 workgroups of 2 tiles")
+    p = Pair(w, fused_heads=16)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) == 17
+        run(p)
+    finally:
+        p.close()
+
+
+def test_several_tiles_shared_layers():
+    w = W["shared"].scaled(R=8, L=4, ctx=16384, steps=3)
+    log("shared R=8 L=4: anchors with 17 workgroups of 2 tiles")
+    p = Pair(w, fused_heads=16)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) == 17
+        run(p)
+        p.check_hot()
+    finally:
+        p.close()
+
+
+def test_several_tiles_padded_requests_untouched():
+    w = W["batched"].scaled(R=32, L=1, steps=3, B=4096)
+    p = Pair(w, fused_heads=16)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) == 8
+        sentinel = torch.full_like(p.d_att, 7.0)
+        p.d_att.copy_(sentinel)
+        for _ in range(3):
+            p.step_gpu_and_oracle(num_reqs=21)
+        torch.cuda.synchronize()
+        assert torch.equal(p.d_att[:, 21:], sentinel[:, 21:])
+        p.check_state(requests=range(21))
     finally:
         p.close()
