@@ -265,8 +265,11 @@ def main():
         detail.update(measure_batched(torch, hk, synth, dev))
         detail.update(measure_capacity(torch, hk, synth, dev))
         detail.update(measure_replay(torch, hk, synth, dev))
+        detail.update(measure_attention(torch, hk, synth, dev))
         detail["launch_latency_us"] = measure_empty(torch, hk)
-        detail["hbm_copy_GBps"] = measure_hbm(torch, hk, dev)
+        detail.update(measure_hbm(torch, hk, dev))
+        detail["attention_r32_frac_of_scattered_read"] = (detail["attention_r32_GBps"]
+                                                          / detail["hbm_scattered_records_read_GBps"])
         detail["link_ceiling_GBps"] = link["ceiling_GBps"]
         detail["link_dma_h2d_GBps"] = link["dma_GBps"]
         detail["link_zero_copy_GBps"] = link["zero_copy_GBps"]
@@ -752,6 +755,42 @@ def measure_batched(torch, hk, synth, dev, layers=4, steps=16, warmup=4):
             "batched_steady_link_GBps": miss_bytes / el / 1e9}
 
 
+def measure_attention(torch, hk, synth, dev, steps=12, warmup=2):
+    """The attention consumer alone (hs_sparse_attn: attention kernel, then the chunk merge) at
+    the batched shape: 32 requests, k 2048, B 4096, 16 heads, one layer.  Each step resolves
+    (untimed), then the attention call runs between events on the launch stream.  Bytes per
+    call: the k records of every request, the queries and the outputs."""
+    w = synth.WORKLOADS["batched"].scaled(L=1, B=4096)
+    R, L, k, B = w.R, w.L, w.k, w.B
+    n = warmup + steps
+    lmax = w.max_positions(n)
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    tr = np.stack([synth.selection_trace(w, r, 0, n) for r in range(R)], axis=1)  # [n][R][k]
+    d_tr = torch.from_numpy(tr).to(dev)
+    d_q = torch.from_numpy(np.stack([synth.queries(R, L, t)[:, 0] for t in range(n)]).view(np.int16)).to(dev)
+    d_ctx = torch.full((R,), w.ctx, dtype=torch.int32, device=dev)
+    d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
+    d_out = torch.empty((R, 16, 512), dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for t in range(n):
+        hk.hs_resolve(cache.h, 0, d_tr[t].data_ptr(), d_ctx.data_ptr(), d_slots.data_ptr(), 0, 0, 0, s.cuda_stream)
+        ev[t][0].record(s)
+        hk.hs_sparse_attn(cache.h, 0, d_q[t].data_ptr(), 16, 512, d_slots.data_ptr(), d_out.data_ptr(),
+                          576 ** -0.5, 0, s.cuda_stream)
+        ev[t][1].record(s)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev[warmup:]])
+    cache.close()
+    nbytes = R * (k * REC + 16 * 576 * 2 + 16 * 512 * 4)
+    t_us = float(np.median(us))
+    return {"attention_r32_call_us": t_us, "attention_r32_bytes": nbytes,
+            "attention_r32_GBps": nbytes / (t_us * 1e-6) / 1e9,
+            "attention_r32_frac_of_hbm_peak": nbytes / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 def measure_empty(torch, hk):
     s = torch.cuda.current_stream()
     hk.hs_probe_empty(100, s.cuda_stream)
@@ -765,19 +804,37 @@ def measure_empty(torch, hk):
 
 
 def measure_hbm(torch, hk, dev):
+    """HBM rates: a 1 GiB copy (bytes read + written), a streaming read of it (256 workgroups
+    of 16-byte loads, 8 per thread in flight), and 65536 scattered 1152-byte records gathered
+    from it into a dense buffer (the access pattern of the attention's hot-slot reads; bytes
+    read)."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
     b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
     s = torch.cuda.current_stream()
-    hk.hs_probe_copy(a.data_ptr(), b.data_ptr(), n, s.cuda_stream)
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(5):
-        hk.hs_probe_copy(a.data_ptr(), b.data_ptr(), n, s.cuda_stream)
-    e1.record(s)
-    torch.cuda.synchronize()
-    return 5 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    copy = 2 * n / timed(lambda: hk.hs_probe_copy(a.data_ptr(), b.data_ptr(), n, s.cuda_stream)) / 1e9
+    sink = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    read = n / timed(lambda: hk.hs_probe_host_read(a.data_ptr(), n, sink.data_ptr(), 256, s.cuda_stream)) / 1e9
+    nrec = 65536
+    idx = np.random.Generator(np.random.PCG64(7)).choice(n // REC, size=nrec, replace=False).astype(np.int32)
+    d_idx = torch.from_numpy(idx).to(dev)
+    gather = nrec * REC / timed(lambda: hk.hs_probe_host_records(a.data_ptr(), n // REC, REC, d_idx.data_ptr(), nrec,
+                                                                 b.data_ptr(), 4096, s.cuda_stream)) / 1e9
+    del a, b
+    return {"hbm_copy_GBps": copy, "hbm_stream_read_GBps": read, "hbm_scattered_records_read_GBps": gather}
 
 
 def cpu_baseline(synth, w, trace, n_steps, W, K, budget_s):
@@ -941,6 +998,7 @@ SECONDARY = {
     "fetch_heavy": measure_fetch_heavy,
     "all_hit": measure_all_hit,
     "rows": measure_rows,
+    "attention": measure_attention,
 }
 
 if __name__ == "__main__":

@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libhisparse.so")
 SOURCES = ["csrc/resolve.hip", "csrc/copy.hip", "csrc/attn.hip", "csrc/hs_api.cpp"]
-HEADERS = ["csrc/hs_internal.h", "../include/hisparse.h"]
+HEADERS = ["csrc/hs_internal.h", "csrc/hs_attend.h", "../include/hisparse.h"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

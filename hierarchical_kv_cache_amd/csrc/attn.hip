@@ -5,18 +5,24 @@
 // per token: the key is all 576 bf16 of the record, the value its first 512.
 //
 // Work split (split-k over the top-k entries): workgroup (r, s) owns a chunk
-// of request r's entries and walks it in tiles of 64 tokens.  A tile's
-// records are gathered from HBM into LDS; each of the 4 waves computes the
-// 16 x 16 score block of 16 tokens with v_mfma_f32_16x16x32_bf16 (18 k-steps
-// over the 576 key dims), the block keeps a running max / sum per head, and
-// each wave then accumulates P V for its 128 output channels, again on MFMA.
+// of request r's entries and walks it in tiles of 64 tokens, keeping a running
+// max / sum per head.  A second small kernel merges the per-chunk partials
+// (max, sum, unnormalised output) of each (request, head).  With R >= 8 all
+// chunks of a request run on one XCD.
+//   - bf16 records (attn_tiles_kernel): 1024-thread workgroups on the tile
+//     functions the fused kernel uses.  The chunk's record addresses are found
+//     in one pass, each tile is gathered into registers (5 16-byte loads per
+//     thread) while the previous tile is attended, 4 waves compute the scores
+//     on v_mfma_f32_16x16x32_bf16 and all 16 accumulate P V, 32 channels each.
+//   - FP8 records (attn_kernel): 4 waves; a tile's E4M3 codes are turned into
+//     bf16 in LDS, the scores keep one MFMA accumulator per 128-dim scale block,
+//     and P is scaled per block for P V.
 // P is split into bf16 hi + lo parts so the fp32 probabilities survive the
-// bf16 operand.  A second small kernel merges the per-chunk partials (max,
-// sum, unnormalised output) of each (request, head).  With R >= 8 all chunks
-// of a request run on one XCD.
+// bf16 operand.
 #include <algorithm>
 
 #include "hs_internal.h"
+#include "hs_attend.h"
 
 namespace hs {
 namespace {
@@ -33,7 +39,6 @@ constexpr int RS = kTileStride;         // LDS row stride (1168 bytes): conflict
 constexpr int KSTEPS = kAttnDk / 32;    // 18
 constexpr int CHUNKS = kAttnDk * 2 / 16;  // 72 16-byte chunks per record
 constexpr int CT = kAttnDv / 4 / 16;    // 8 channel tiles of 16 per wave
-constexpr int GATHER = TT * CHUNKS / AT;  // 18 16-byte chunks per thread per tile
 constexpr int QS = kAttnDk * 2 + 16;       // LDS stride of a query row (padded off the bank period)
 // FP8 records (the fp8 latent-KV layout, 656 bytes): 512 E4M3 codes in 4 blocks of 128 with
 // a float32 scale each, then 64 bf16.  The gather turns them into the same bf16 rows.
@@ -48,16 +53,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-template <bool FP8>
+// FP8 records.
 __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char rows[TT * RS];
   __shared__ __attribute__((aligned(16))) unsigned char qs[16 * QS];  // q rows, zero past `heads`
-  // P (hi and lo bf16 parts) as P V operands: [wave][32-token block][head][k].  With FP8
-  // records each wave gets P times its channel block's per-token scale.
-  constexpr int PW = FP8 ? 4 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t phi[PW][2][16][32];
-  __shared__ __attribute__((aligned(16))) uint16_t plo[PW][2][16][32];
-  __shared__ float s_scale[FP8 ? TT : 1][4];  // FP8: the block scales of each token of the tile
+  // P (hi and lo bf16 parts) as P V operands: [wave][32-token block][head][k]; each wave gets
+  // P times its channel block's per-token scale.
+  __shared__ __attribute__((aligned(16))) uint16_t phi[4][2][16][32];
+  __shared__ __attribute__((aligned(16))) uint16_t plo[4][2][16][32];
+  __shared__ float s_scale[TT][4];  // the block scales of each token of the tile
   __shared__ float smax[4][16];
   __shared__ float ssum[4][16];
   __shared__ int s_slot[kAttnMaxChunk];
@@ -115,11 +119,11 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  // records of the tile starting at token t0: 18 16-byte loads per thread (bf16 records) or
-  // 10 (FP8 records, each data chunk with its block's scale), all in flight
-  constexpr int NG = FP8 ? F8_GATHER : GATHER;
+  // records of the tile starting at token t0: 10 16-byte loads per thread (each data chunk
+  // with its block's scale), all in flight
+  constexpr int NG = F8_GATHER;
   u32x4 stage[NG];
-  float sscale[FP8 ? NG : 1];
+  float sscale[NG];
   // the record of a published slot: 0..B hot rows, B+1+row resident rows, else none
   auto record_of = [&](int tok) -> const uint8_t* {
     const int sl = s_slot[tok - t_begin];
@@ -131,22 +135,18 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
       const int f = tid + u * AT;
-      const int row = f / (FP8 ? F8_ITEMS : CHUNKS), c = f - row * (FP8 ? F8_ITEMS : CHUNKS);
+      const int row = f / F8_ITEMS, c = f - row * F8_ITEMS;
       const int tok = t0 + row;
       // past the end: exact zeros; no record (a slot outside the published range): NaN, so
       // the output shows it
       if (tok >= t_end) {
         stage[u] = zero4;
-        if constexpr (FP8) sscale[u] = 0.0f;
+        sscale[u] = 0.0f;
       } else {
         const uint8_t* src = record_of(tok);
-        if constexpr (FP8) {
-          const int off = c < F8_DATA ? 16 * c : 528 + 16 * (c - F8_DATA);
-          stage[u] = src ? *(const u32x4*)(src + off) : nan4;
-          sscale[u] = (src && c < F8_DATA) ? *(const float*)(src + 512 + 4 * (c >> 3)) : __builtin_nanf("");
-        } else {
-          stage[u] = src ? *((const u32x4*)src + c) : nan4;
-        }
+        const int off = c < F8_DATA ? 16 * c : 528 + 16 * (c - F8_DATA);
+        stage[u] = src ? *(const u32x4*)(src + off) : nan4;
+        sscale[u] = (src && c < F8_DATA) ? *(const float*)(src + 512 + 4 * (c >> 3)) : __builtin_nanf("");
       }
     }
   };
@@ -164,31 +164,25 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
     __syncthreads();  // the previous tile is no longer read
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      if constexpr (FP8) {
-        const int f = tid + u * AT;
-        const int row = f / F8_ITEMS, c = f - row * F8_ITEMS;
-        if (c < F8_DATA) {
-          // 16 codes -> 16 bf16, exactly (an E4M3 value has 4 significant bits); the block
-          // scale is applied to the fp32 sums below instead of rounding code * scale
-          uint32_t wv[8];
+      const int f = tid + u * AT;
+      const int row = f / F8_ITEMS, c = f - row * F8_ITEMS;
+      if (c < F8_DATA) {
+        // 16 codes -> 16 bf16, exactly (an E4M3 value has 4 significant bits); the block
+        // scale is applied to the fp32 sums below instead of rounding code * scale
+        uint32_t wv[8];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[u][q], false);
-            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[u][q], true);
-            wv[2 * q] = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xFFFF0000u);
-            wv[2 * q + 1] = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xFFFF0000u);
-          }
-          u32x4* d = (u32x4*)(rows + row * RS + c * 32);
-          d[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
-          d[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
-          if ((c & 7) == 0) s_scale[row][c >> 3] = sscale[u];
-        } else {
-          *(u32x4*)(rows + row * RS + 1024 + (c - F8_DATA) * 16) = stage[u];
+        for (int q = 0; q < 4; ++q) {
+          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[u][q], false);
+          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)stage[u][q], true);
+          wv[2 * q] = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xFFFF0000u);
+          wv[2 * q + 1] = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xFFFF0000u);
         }
+        u32x4* d = (u32x4*)(rows + row * RS + c * 32);
+        d[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        d[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+        if ((c & 7) == 0) s_scale[row][c >> 3] = sscale[u];
       } else {
-        const int f = tid + u * AT;
-        const int row = f / CHUNKS, c = f - row * CHUNKS;
-        *(u32x4*)(rows + row * RS + c * 16) = stage[u];
+        *(u32x4*)(rows + row * RS + 1024 + (c - F8_DATA) * 16) = stage[u];
       }
     }
     __syncthreads();
@@ -198,7 +192,7 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
     f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
     const unsigned char* krow = rows + (16 * w + col) * RS + qd * 16;
     const unsigned char* qrow = qs + col * QS + qd * 16;  // A operand: q[head = col][32 ks + 8 qd + j]
-    if constexpr (FP8) {
+    {
       // one accumulator per 128-dim scale block (4 k-steps each) and one for the bf16 part
       f32x4 sb[5];
 #pragma unroll
@@ -213,13 +207,6 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sacc[i] = sb[0][i] * scl[0] + sb[1][i] * scl[1] + sb[2][i] * scl[2] + sb[3][i] * scl[3] + sb[4][i];
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8 qa = *(const bf16x8*)(qrow + ks * 64);
-        const bf16x8 kb = *(const bf16x8*)(krow + ks * 64);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, sacc, 0, 0, 0);
-      }
     }
     const bool valid = (t0 + 16 * w + col) < t_end;
     float sv[4], mx[4];
@@ -246,19 +233,13 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
       m_run[i] = mn;
       const float pv = exp2f(sv[i] - mn);
       l_lane[i] = l_lane[i] * alpha[i] + pv;
-      if constexpr (FP8) {
-        const float* scl = s_scale[tl];
+      const float* scl = s_scale[tl];
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const float pw = pv * scl[w2];
-          const uint16_t hi = f32_to_bf16_bits(pw);
-          phi[w2][bk][hh][kk] = hi;
-          plo[w2][bk][hh][kk] = f32_to_bf16_bits(pw - bf16_bits_to_f32(hi));
-        }
-      } else {
-        const uint16_t hi = f32_to_bf16_bits(pv);
-        phi[0][bk][hh][kk] = hi;
-        plo[0][bk][hh][kk] = f32_to_bf16_bits(pv - bf16_bits_to_f32(hi));
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float pw = pv * scl[w2];
+        const uint16_t hi = f32_to_bf16_bits(pw);
+        phi[w2][bk][hh][kk] = hi;
+        plo[w2][bk][hh][kk] = f32_to_bf16_bits(pw - bf16_bits_to_f32(hi));
       }
     }
     __syncthreads();
@@ -270,8 +251,8 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
       for (int i = 0; i < 4; ++i) o[c][i] *= alpha[i];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const bf16x8 ahi = *(const bf16x8*)&phi[FP8 ? w : 0][b][col][qd * 8];
-      const bf16x8 alo = *(const bf16x8*)&plo[FP8 ? w : 0][b][col][qd * 8];
+      const bf16x8 ahi = *(const bf16x8*)&phi[w][b][col][qd * 8];
+      const bf16x8 alo = *(const bf16x8*)&plo[w][b][col][qd * 8];
       const unsigned char* vb = rows + (b * 32 + qd) * RS + (w * 128 + col) * 2;
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
@@ -323,6 +304,73 @@ __global__ void __launch_bounds__(AT, 1) attn_kernel(AttnParams p) {
       part[16 * kAttnDv + 16 + hh] = ssum[0][hh] + ssum[1][hh] + ssum[2][hh] + ssum[3][hh];
     }
   }
+}
+
+// bf16 records: workgroup (r, s) over chunk s of request r (<= kAttnMaxChunk entries, so at
+// most 16 tiles).  A slot that names no record (outside [0, B] and the resident rows) makes
+// the chunk's result NaN, so the request's output shows it.
+__global__ void __launch_bounds__(kAT) attn_tiles_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char tile[kTileRows * kTileStride];
+  __shared__ __attribute__((aligned(16))) unsigned char qs[16 * kQStride];
+  __shared__ __attribute__((aligned(16))) unsigned char scratch[kAttnScratch];
+  __shared__ uint64_t asrc[kAttnMaxChunk];  // record address of each chunk entry
+  int r, s;
+  if (p.R >= 8) {  // chunks of one request on one XCD (workgroups go round-robin over 8 XCDs)
+    const int x = blockIdx.x & 7, loc = blockIdx.x >> 3;
+    r = (loc / p.S) * 8 + x;
+    s = loc % p.S;
+    if (r >= p.R) return;
+  } else {
+    r = blockIdx.x / p.S;
+    s = blockIdx.x % p.S;
+  }
+  if (p.num_reqs && r >= *p.num_reqs) return;
+  const int tid = threadIdx.x;
+  const int t_begin = s * p.chunk;
+  const int n = min(p.k, t_begin + p.chunk) - t_begin;
+  const int nt = (n + kTileRows - 1) / kTileRows;
+  const uint8_t* hot_r = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
+  const uint8_t* filler = (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);  // finite rows
+  u32x4 qv[kQU];
+  q_load(qv, p.q, r, p.heads);
+  int bad = 0;
+  if (tid < nt * kTileRows) {
+    const uint8_t* src = filler;
+    if (tid < n) {
+      const int sl = p.slots[(size_t)r * p.k + t_begin + tid];
+      const int64_t rr = (int64_t)sl - (p.B + 1);
+      if (sl >= 0 && sl <= p.B) src = hot_r + (size_t)sl * p.rec_bytes;
+      else if (rr >= 0 && rr < p.res_rows) src = p.res + (size_t)rr * p.rec_bytes;
+      else bad = 1;
+    }
+    asrc[tid] = (uint64_t)src;
+  }
+  q_store(qv, qs);
+  bad = __syncthreads_or(bad);
+  const float sl2 = p.scale * 1.4426950408889634f;  // scores kept in log2 units
+  u32x4 tv[kTU];
+  tile_load(tv, asrc);
+  AttnAcc acc;
+  acc_init(acc);
+  for (int t = 0; t < nt; ++t) {
+    if (t > 0) __syncthreads();  // the previous tile's readers are done with the tile and P
+    tile_store(tv, tile);
+    if (t + 1 < nt) tile_load(tv, asrc + (t + 1) * kTileRows);  // flies during this tile's math
+    __syncthreads();
+    attend_tile(tile, qs, scratch, min(kTileRows, n - t * kTileRows), sl2, acc);
+  }
+  if (bad) {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc.m[i] = nan;
+      acc.l[i] = nan;
+      acc.o[0][i] = nan;
+      acc.o[1][i] = nan;
+    }
+  }
+  attend_write(acc, p.part + ((size_t)r * p.S + s) * kPartStride,
+               p.S == 1 ? p.out + (size_t)r * p.heads * kAttnDv : nullptr, p.heads);
 }
 
 // Merge of the S chunk partials of one (request, head): o = sum_s 2^(m_s - M) o_s /
@@ -486,8 +534,8 @@ __global__ void __launch_bounds__(kFinishThreads) attn_finish_kernel(FinishParam
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   const int grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * p.S : p.R * p.S;
-  if (p.fp8) hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(AT), 0, s, p);
-  else hipLaunchKernelGGL(attn_kernel<false>, dim3(grid), dim3(AT), 0, s, p);
+  if (p.fp8) hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(AT), 0, s, p);
+  else hipLaunchKernelGGL(attn_tiles_kernel, dim3(grid), dim3(kAT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   return launch_attn_merge(p, s);

@@ -1,0 +1,214 @@
+// Device functions of the record tile and the attention over it, shared by the fused
+// RESOLVE + attention kernel (resolve.hip) and the attention kernel (attn.hip): a 64-row tile
+// of 1152-byte bf16 records gathered into registers and written to LDS, the 16 query rows,
+// and the attention of 16 heads over one tile folded into a running maximum, sum and output
+// (online softmax), on 1024-thread workgroups.
+#pragma once
+
+#include "hs_internal.h"
+
+namespace hs {
+namespace {
+
+constexpr int kAT = kResolveThreads;  // threads of a tile workgroup (16 waves)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The record tile: 64 rows of 72 16-byte chunks.  Thread t holds chunks t, t + kAT, ...
+// (row f / 72, chunk f % 72) in registers from their loads until the tile is written to LDS,
+// so the loads fly meanwhile (in the fused kernel while workgroup 0 runs stages 1-3; in both
+// kernels during the previous tile's attention).  Loads straight into LDS made the fused
+// kernel's LDS waits wait for them as well.  Non-temporal: every record is read once per
+// launch.
+constexpr int kRowChunks = kAttnDk / 8;               // 16-byte chunks per 1152-byte record
+constexpr int kTileChunks = kTileRows * kRowChunks;   // 4608
+constexpr int kTU = (kTileChunks + kAT - 1) / kAT;      // chunks per thread
+constexpr int kQChunks = 16 * kRowChunks;             // query rows of 16 heads
+constexpr int kQU = (kQChunks + kAT - 1) / kAT;
+
+// row addresses in LDS (asrc[row]) -> this thread's chunks of the tile
+__device__ __forceinline__ void tile_load(u32x4 (&tv)[kTU], const uint64_t* asrc) {
+#pragma unroll
+  for (int u = 0; u < kTU; ++u) {
+    const int f = threadIdx.x + u * kAT;
+    if (f < kTileChunks) {
+      const int row = f / kRowChunks, c = f - row * kRowChunks;
+      tv[u] = load_host16((const uint8_t*)asrc[row] + 16 * c);
+    }
+  }
+}
+__device__ __forceinline__ void tile_store(const u32x4 (&tv)[kTU], unsigned char* tile) {
+#pragma unroll
+  for (int u = 0; u < kTU; ++u) {
+    const int f = threadIdx.x + u * kAT;
+    if (f < kTileChunks) {
+      const int row = f / kRowChunks, c = f - row * kRowChunks;
+      *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
+    }
+  }
+}
+// the query rows of request r (rows past `heads`: zeros)
+__device__ __forceinline__ void q_load(u32x4 (&qv)[kQU], const uint16_t* q, int r, int heads) {
+#pragma unroll
+  for (int u = 0; u < kQU; ++u) {
+    const int f = threadIdx.x + u * kAT;
+    const int h = f / kRowChunks, c = f - h * kRowChunks;
+    qv[u] = (f < kQChunks && h < heads) ? load_host16((const uint8_t*)(q + ((size_t)r * heads + h) * kAttnDk) + 16 * c)
+                                        : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+__device__ __forceinline__ void q_store(const u32x4 (&qv)[kQU], unsigned char* qs) {
+#pragma unroll
+  for (int u = 0; u < kQU; ++u) {
+    const int f = threadIdx.x + u * kAT;
+    const int h = f / kRowChunks, c = f - h * kRowChunks;
+    if (f < kQChunks) *(u32x4*)(qs + (size_t)h * kQStride + 16 * c) = qv[u];
+  }
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (finite inputs)
+  return (uint16_t)(u >> 16);
+}
+
+// Running attention of one fetch workgroup over its tiles (online softmax).  Lane (wave w,
+// quarter qd, column col) holds, for heads 4 qd + i, the running maximum m and sum l of the
+// scores (log2 units) and the unnormalised output o of channels 32 w + 16 c + col.
+struct AttnAcc {
+  float m[4], l[4];
+  f32x4 o[2];
+};
+
+__device__ __forceinline__ void acc_init(AttnAcc& a) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a.m[i] = -INFINITY;
+    a.l[i] = 0.0f;
+  }
+  a.o[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  a.o[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// Attention of the 16 query heads over one tile of n_tok records held in LDS (sparse decode
+// attention, "HiSparse 深度解析" (gentlecold.top) §5.4: the records of the published slots;
+// key = the record's 576 bf16, value = its first 512), folded into the running state.  Waves
+// 0-3 compute the 16 x 16 score blocks of tokens 16w .. 16w+15 on v_mfma_f32_16x16x32_bf16
+// (18 k-steps); each head's new maximum is the larger of the running one and the tile's, the
+// probabilities are taken against it, and every wave rescales its running sum and output by
+// 2^(old max - new max) before all 16 waves accumulate P V for 32 output channels each.  P is
+// split into bf16 hi + lo parts so the fp32 probabilities survive the bf16 operand.
+__device__ __forceinline__ void attend_tile(const unsigned char* tile, const unsigned char* qs,
+                                            unsigned char* scratch, int n_tok, float sl2, AttnAcc& acc) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, qd = lane >> 4;
+  float* smax = (float*)scratch;                 // [4][16]
+  float* ssum = smax + 64;                       // [4][16]
+  uint16_t* phi = (uint16_t*)(ssum + 64);        // [2 token blocks][16 heads][32]
+  uint16_t* plo = phi + 2 * 16 * 32;
+  constexpr int KSTEPS = kAttnDk / 32;
+  float sv[4];
+  if (w < 4) {
+    // lane: s[head = 4 qd + i][token = 16 w + col]; two accumulators halve the dependent
+    // MFMA chain
+    f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+    const unsigned char* krow = tile + (16 * w + col) * kTileStride + qd * 16;
+    const unsigned char* qrow = qs + col * kQStride + qd * 16;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ks += 2) {
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64), *(const bf16x8*)(krow + ks * 64),
+                                                   sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64 + 64),
+                                                   *(const bf16x8*)(krow + ks * 64 + 64), sb, 0, 0, 0);
+    }
+    const bool valid = 16 * w + col < n_tok;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = valid ? (sa[i] + sb[i]) * sl2 : -INFINITY;
+      const float mx = row16_max(sv[i]);
+      if (col == 0) smax[w * 16 + qd * 4 + i] = mx;
+    }
+  }
+  __syncthreads();
+  float mnew[4], alpha[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = qd * 4 + i;
+    const float mt = fmaxf(fmaxf(smax[hh], smax[16 + hh]), fmaxf(smax[32 + hh], smax[48 + hh]));
+    mnew[i] = fmaxf(acc.m[i], mt);     // finite: every tile has a valid row
+    alpha[i] = exp2f(acc.m[i] - mnew[i]);  // 0 on the first tile
+  }
+  if (w < 4) {
+    const int tl = 16 * w + col;
+    const int bk = tl >> 5, t32 = tl & 31;
+    const int kk = (t32 & 3) * 8 + (t32 >> 2);  // P V operands pair k index 8 qd + j with token 4 j + qd
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = qd * 4 + i;
+      const float pv = exp2f(sv[i] - mnew[i]);
+      const float l = row16_sum(pv);
+      if (col == 0) ssum[w * 16 + hh] = l;
+      const uint16_t hi = f32_to_bf16_rne(pv);
+      phi[(bk * 16 + hh) * 32 + kk] = hi;
+      plo[(bk * 16 + hh) * 32 + kk] = f32_to_bf16_rne(pv - __uint_as_float((uint32_t)hi << 16));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = qd * 4 + i;
+    acc.l[i] = acc.l[i] * alpha[i] + (ssum[hh] + ssum[16 + hh] + ssum[32 + hh] + ssum[48 + hh]);
+    acc.m[i] = mnew[i];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc.o[c][i] *= alpha[i];
+  }
+  // o[head][channel] += p v over the tile; wave w owns channels 32 w .. 32 w + 31
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const bf16x8 ahi = *(const bf16x8*)&phi[(b * 16 + col) * 32 + qd * 8];
+    const bf16x8 alo = *(const bf16x8*)&plo[(b * 16 + col) * 32 + qd * 8];
+    const unsigned char* vb = tile + (b * 32 + qd) * kTileStride + (32 * w + col) * 2;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 vv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vv[j] = *(const __bf16*)(vb + 4 * j * kTileStride + c * 32);
+      acc.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, vv, acc.o[c], 0, 0, 0);
+      acc.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vv, acc.o[c], 0, 0, 0);
+    }
+  }
+}
+
+// The share's result: its partial (unnormalised o, maximum and sum in log2 units) for the
+// merge, or the normalised output rows of the heads asked for when the request has one share.
+__device__ __forceinline__ void attend_write(const AttnAcc& acc, float* part, float* out, int heads) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, qd = lane >> 4;
+  // o[c][i]: head 4 qd + i, channel 32 w + 16 c + col
+  if (out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = qd * 4 + i;
+      if (hh >= heads) continue;
+      const float inv = 1.0f / acc.l[i];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) out[hh * kAttnDv + 32 * w + 16 * c + col] = acc.o[c][i] * inv;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) part[(qd * 4 + i) * kAttnDv + 32 * w + 16 * c + col] = acc.o[c][i];
+  if (w == 0 && col == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      part[16 * kAttnDv + qd * 4 + i] = acc.m[i];
+      part[16 * kAttnDv + 16 + qd * 4 + i] = acc.l[i];
+    }
+  }
+}
+
+}  // namespace
+}  // namespace hs
