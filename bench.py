@@ -266,6 +266,7 @@ def main():
         detail.update(measure_capacity(torch, hk, synth, dev))
         detail.update(measure_replay(torch, hk, synth, dev))
         detail.update(measure_attention(torch, hk, synth, dev))
+        detail.update(measure_shared_step(torch, hk, synth, dev))
         detail["launch_latency_us"] = measure_empty(torch, hk)
         detail.update(measure_hbm(torch, hk, dev))
         detail["attention_r32_frac_of_scattered_read"] = (detail["attention_r32_GBps"]
@@ -755,6 +756,80 @@ def measure_batched(torch, hk, synth, dev, layers=4, steps=16, warmup=4):
             "batched_steady_link_GBps": miss_bytes / el / 1e9}
 
 
+def measure_shared_step(torch, hk, synth, dev, steps=12, warmup=4):
+    """A decode step of the shared-index workload, one anchor group: 16 requests, the anchor
+    and its three shared layers, ctx 131072, k 2048, B 4096, 16 heads.  Per step the anchor
+    goes through hs_resolve_attn with its miss plan recorded; hs_prefetch_shared replays the
+    plan into the three shared layers on the prefetch stream; each shared layer's attention
+    (hs_sparse_attn over the anchor's slots) waits for its own layer's replay only.
+    Selections/s count the k selected tokens of every request in all four layers.  The anchor's
+    fused kernel and the replay kernels are stamped by their own start and end."""
+    w = synth.WORKLOADS["shared"].scaled(L=4)
+    R, L, k, B = w.R, w.L, w.k, w.B
+    n = warmup + steps
+    lmax = w.max_positions(n)
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, layer_group=w.group))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    tr = np.stack([synth.selection_trace(w, r, 0, n) for r in range(R)], axis=1)  # [n][R][k]
+    d_tr = torch.from_numpy(tr).to(dev)
+    d_q = torch.from_numpy(np.stack([synth.queries(R, L, t) for t in range(n)]).view(np.int16)).to(dev)
+    d_q = d_q.permute(0, 2, 1, 3, 4).contiguous()  # [n][L][R][16][576]
+    d_ctx = torch.full((R,), w.ctx, dtype=torch.int32, device=dev)
+    d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n, R, 4), dtype=torch.int32, device=dev)
+    d_out = torch.empty((L, R, 16, 512), dtype=torch.float32, device=dev)
+    cs = torch.cuda.current_stream()
+    ps = torch.cuda.Stream()
+    scale = 576 ** -0.5
+
+    def step(t):
+        hk.hs_resolve_attn(cache.h, 0, d_tr[t].data_ptr(), d_ctx.data_ptr(), d_slots.data_ptr(),
+                           d_stats[t].data_ptr(), 0, hk.HS_RECORD_PLAN, d_q[t, 0].data_ptr(), 16, 512,
+                           d_out[0].data_ptr(), scale, cs.cuda_stream)
+        hk.hs_prefetch_shared(cache.h, 0, cs.cuda_stream, ps.cuda_stream)
+        for l in range(1, L):
+            hk.hs_wait_layer(cache.h, l, cs.cuda_stream)
+            hk.hs_sparse_attn(cache.h, l, d_q[t, l].data_ptr(), 16, 512, d_slots.data_ptr(), d_out[l].data_ptr(),
+                              scale, 0, cs.cuda_stream)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warmup, n):
+        step(t)
+    torch.cuda.synchronize()
+    ps.synchronize()
+    el = time.perf_counter() - t0
+    # the same steps again from an empty start, with the kernels stamped (fused, then 3 replays)
+    wgs = hk.hs_resolve_attn_wgs(cache.h)
+    st = d_stats.cpu().numpy()
+    cache.close()
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, layer_group=w.group))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    hk.hs_timing_start(cache.h, steps * 4)
+    for t in range(warmup, n):
+        step(t)
+    torch.cuda.synchronize()
+    ps.synchronize()
+    us = hk.hs_timing_read(cache.h, steps * 4).astype(np.float64).reshape(steps, 4)
+    cache.close()
+    assert not st[..., 2].any()
+    plan_bytes = 3 * st[warmup:, :, 1].sum(axis=1) * REC
+    return {"shared_step_us": el / steps * 1e6,
+            "shared_selections_per_s": steps * L * R * k / el,
+            "shared_fused_wgs_per_request": wgs,
+            "shared_anchor_fused_kernel_us": float(np.median(us[:, 0])),
+            "shared_replay_kernels_us_per_step": float(np.median(us[:, 1:].sum(axis=1))),
+            "shared_replay_GBps": float(plan_bytes.sum() / (us[:, 1:].sum() * 1e-6) / 1e9),
+            "shared_miss_rate": float(st[warmup:, :, 1].sum() / (steps * R * k))}
+
+
 def measure_attention(torch, hk, synth, dev, steps=12, warmup=2):
     """The attention consumer alone (hs_sparse_attn: attention kernel, then the chunk merge) at
     the batched shape: 32 requests, k 2048, B 4096, 16 heads, one layer.  Each step resolves
@@ -999,6 +1074,7 @@ SECONDARY = {
     "all_hit": measure_all_hit,
     "rows": measure_rows,
     "attention": measure_attention,
+    "shared_step": measure_shared_step,
 }
 
 if __name__ == "__main__":
