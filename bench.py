@@ -582,7 +582,9 @@ def measure_resident(torch, hk, synth, w, dev, trace, lmax):
 
 def measure_fp8(torch, hk, synth, dev, steps=40, warmup=8):
     """The long-request step (write-through, RESOLVE, attention over 8 layers) with FP8 latent-KV
-    records (656 bytes: E4M3 codes, block scales, bf16 rope): whole-step throughput."""
+    records (656 bytes: E4M3 codes, block scales, bf16 rope): whole-step throughput through
+    hs_resolve_attn (the fused kernel over FP8 tiles), and through hs_resolve + hs_sparse_attn
+    from the same empty start."""
     w = synth.WORKLOADS["long"]
     R, L, k, B = w.R, w.L, w.k, w.B
     n = steps + warmup
@@ -606,26 +608,45 @@ def measure_fp8(torch, hk, synth, dev, steps=40, warmup=8):
     cs = torch.cuda.current_stream().cuda_stream
     bs = torch.cuda.Stream()
 
-    def step(t):
-        hk.hs_append(cache.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), cs, bs.cuda_stream)
+    def step(c, t, fused):
+        hk.hs_append(c.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), cs, bs.cuda_stream)
         for l in range(L):
-            hk.hs_resolve(cache.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
-                          d_stats[t, l].data_ptr(), 0, 0, cs)
-            hk.hs_sparse_attn(cache.h, l, d_q[t, l].data_ptr(), w.heads, 512, d_slots[l].data_ptr(),
-                              d_out[l].data_ptr(), 576 ** -0.5, 0, cs)
+            if fused:
+                hk.hs_resolve_attn(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
+                                   d_stats[t, l].data_ptr(), 0, 0, d_q[t, l].data_ptr(), w.heads, 512,
+                                   d_out[l].data_ptr(), 576 ** -0.5, cs)
+            else:
+                hk.hs_resolve(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
+                              d_stats[t, l].data_ptr(), 0, 0, cs)
+                hk.hs_sparse_attn(c.h, l, d_q[t, l].data_ptr(), w.heads, 512, d_slots[l].data_ptr(),
+                                  d_out[l].data_ptr(), 576 ** -0.5, 0, cs)
 
-    for t in range(warmup):
-        step(t)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(warmup, n):
-        step(t)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    bs.synchronize()
-    assert not d_stats.cpu().numpy()[..., 2].any()
+    def run(c, fused):
+        for t in range(warmup):
+            step(c, t, fused)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(warmup, n):
+            step(c, t, fused)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        bs.synchronize()
+        return el
+
+    fused = hk.hs_resolve_attn_wgs(cache.h) > 0
+    el = run(cache, True)
+    st = d_stats.cpu().numpy()
+    cache.close()
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B, newest_slot=True, fp8=True))
+    for r in range(R):
+        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx, rec_bytes=rec)
+    d_stats.zero_()
+    el_sep = run(cache, False)
+    assert np.array_equal(d_stats.cpu().numpy(), st) and not st[..., 2].any()
     cache.close()
     return {"fp8_long_selections_per_s": steps * L * R * k / el, "fp8_long_ms_per_step": el / steps * 1e3,
+            "fp8_long_fused": fused,
+            "fp8_long_separate_selections_per_s": steps * L * R * k / el_sep,
             "fp8_record_bytes": rec}
 
 
@@ -1075,6 +1096,7 @@ SECONDARY = {
     "rows": measure_rows,
     "attention": measure_attention,
     "shared_step": measure_shared_step,
+    "fp8": measure_fp8,
 }
 
 if __name__ == "__main__":

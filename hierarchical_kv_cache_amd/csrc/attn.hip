@@ -357,7 +357,7 @@ __global__ void __launch_bounds__(kAT) attn_tiles_kernel(AttnParams p) {
     tile_store(tv, tile);
     if (t + 1 < nt) tile_load(tv, asrc + (t + 1) * kTileRows);  // flies during this tile's math
     __syncthreads();
-    attend_tile(tile, qs, scratch, min(kTileRows, n - t * kTileRows), sl2, acc);
+    attend_tile<false>(tile, qs, scratch, min(kTileRows, n - t * kTileRows), sl2, acc);
   }
   if (bad) {
     const float nan = __builtin_nanf("");

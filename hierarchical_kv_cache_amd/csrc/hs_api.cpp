@@ -48,7 +48,7 @@ struct Layout {
   int Spart = 1;    // partial records per (layer, request): max(S, fused chunks)
   int kmax = 0;     // longest list one resolve handles: top_k * max(1, verify_rows)
   size_t ctrl = 0, slot_pos = 0, lru = 0, plan = 0, page_table = 0, newest = 0, host_base = 0,
-         attn_part = 0, uni = 0, umap = 0, uout = 0, ucnt = 0, uerr = 0, att_hdr = 0, att_mlist = 0,
+         attn_part = 0, uni = 0, umap = 0, uout = 0, ucnt = 0, uerr = 0, att_zero = 0, att_hdr = 0, att_mlist = 0,
          att_stage = 0, total = 0;
 };
 
@@ -65,11 +65,12 @@ int attn_chunks(const hs_config& c) {
 
 // Fused RESOLVE + attention (hs_resolve_attn): per request workgroup 0 and S fetch
 // workgroups, all of them resident at once (one workgroup per CU, 256 CUs), bf16 records of
-// 576 values.  A fetch workgroup attends T tiles of 64 entries: the smallest T for which
-// R (S + 1) <= 256 with S = ceil(k / 64 T).  Returns S (and T), or 0 when the configuration
-// does not take the fused kernel (whether LDS suffices is checked per device in hs_create).
+// 576 values or FP8 records.  A fetch workgroup attends T tiles of 64 entries: the smallest T
+// for which R (S + 1) <= 256 with S = ceil(k / 64 T).  Returns S (and T), or 0 when the
+// configuration does not take the fused kernel (whether LDS suffices is checked per device in
+// hs_create).
 int fused_chunks(const hs_config& c, int* tiles = nullptr) {
-  if ((c.flags & HS_CFG_RECORD_FP8) || c.record_bytes != kAttnDk * 2) return 0;
+  if (!(c.flags & HS_CFG_RECORD_FP8) && c.record_bytes != kAttnDk * 2) return 0;
   if (!fused_supported(c.top_k, c.buffer_slots)) return 0;
   for (int T = 1; T <= kFusedMaxTiles; ++T) {
     const int S = (c.top_k + kTileRows * T - 1) / (kTileRows * T);
@@ -101,6 +102,7 @@ Layout make_layout(const hs_config& c) {
   L.host_base = take(R * sizeof(void*));
   L.attn_part = take(size_t(c.num_layers) * R * L.Spart * kPartStride * sizeof(float));
   if (Sf) {  // the fused call's report, miss list and staging area (one set per handle)
+    L.att_zero = take(size_t(c.record_bytes));
     L.att_hdr = take(R * 4 * sizeof(uint32_t));
     L.att_mlist = take(R * k * 4 * sizeof(int32_t));
     L.att_stage = take(R * k * size_t(c.record_bytes));
@@ -340,10 +342,11 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
   if (const int Sf = fused_chunks(*cfg, &T)) {
     const int G = Sf + 1;
     int bits = resolve_hash_bits(cfg->top_k);
-    size_t lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G, T).total;
+    const bool f8 = (cfg->flags & HS_CFG_RECORD_FP8) != 0;
+    size_t lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G, T, f8).total;
     if (lds > prop.sharedMemPerBlock) {
       bits -= 1;
-      lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G, T).total;
+      lds = fused_lds(cfg->top_k, cfg->buffer_slots, bits, G, T, f8).total;
     }
     if (lds <= prop.sharedMemPerBlock) {
       h->att_G = G;
@@ -472,7 +475,7 @@ hs_status hs_resolve_attn(hs_handle h, int32_t layer, const int32_t* d_sel, cons
   p.G = h->att_G; p.hash_bits = h->att_hash_bits;
   p.q = (const uint16_t*)d_q; p.part = h->attn_part(layer); p.att_out = d_out;
   p.att_res = h->res ? h->res + size_t(layer) * size_t(h->res_rows) * size_t(h->cfg.record_bytes) : nullptr;
-  p.heads = heads; p.att_tiles = h->att_T; p.att_scale = scale;
+  p.heads = heads; p.att_tiles = h->att_T; p.att_scale = scale; p.att_zero = h->ws + h->lay.att_zero;
   p.att_hdr = (uint32_t*)(h->ws + h->lay.att_hdr); p.att_mlist = (int32_t*)(h->ws + h->lay.att_mlist);
   p.att_stage = h->ws + h->lay.att_stage;
   HS_HIP(launch_resolve_attn(p, h->att_lds, s, h->next_timing()));

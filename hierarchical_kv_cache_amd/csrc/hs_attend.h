@@ -68,6 +68,52 @@ __device__ __forceinline__ void q_store(const u32x4 (&qv)[kQU], unsigned char* q
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// FP8 records (656 bytes: 32 16-byte chunks of E4M3 codes, one chunk of the 4 float32 block
+// scales, 8 chunks of bf16 values) in the same 64-row tile: the codes become bf16 exactly (an
+// E4M3 value has 4 significant bits) in the first 1024 bytes of the row, the bf16 values follow,
+// and the scales go to a [64][4] array apart; the scores and P V apply them in fp32.
+constexpr int kF8RowChunks = kF8RecordBytes / 16;         // 41
+constexpr int kF8TileChunks = kTileRows * kF8RowChunks;   // 2624
+constexpr int kTU8 = (kF8TileChunks + kAT - 1) / kAT;     // chunks per thread
+
+__device__ __forceinline__ void tile_load8(u32x4 (&tv)[kTU8], const uint64_t* asrc) {
+#pragma unroll
+  for (int u = 0; u < kTU8; ++u) {
+    const int f = threadIdx.x + u * kAT;
+    if (f < kF8TileChunks) {
+      const int row = f / kF8RowChunks, c = f - row * kF8RowChunks;
+      tv[u] = load_host16((const uint8_t*)asrc[row] + 16 * c);
+    }
+  }
+}
+__device__ __forceinline__ void tile_store8(const u32x4 (&tv)[kTU8], unsigned char* tile, float* scales) {
+#pragma unroll
+  for (int u = 0; u < kTU8; ++u) {
+    const int f = threadIdx.x + u * kAT;
+    if (f < kF8TileChunks) {
+      const int row = f / kF8RowChunks, c = f - row * kF8RowChunks;
+      if (c < 32) {
+        uint32_t wv[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)tv[u][q], false);
+          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)tv[u][q], true);
+          wv[2 * q] = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xFFFF0000u);
+          wv[2 * q + 1] = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xFFFF0000u);
+        }
+        u32x4* d = (u32x4*)(tile + (size_t)row * kTileStride + 32 * c);
+        d[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        d[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+      } else if (c == 32) {
+        *(u32x4*)(scales + 4 * row) = tv[u];
+      } else {
+        *(u32x4*)(tile + (size_t)row * kTileStride + 1024 + 16 * (c - 33)) = tv[u];
+      }
+    }
+  }
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
@@ -93,40 +139,68 @@ __device__ __forceinline__ void acc_init(AttnAcc& a) {
   a.o[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// The [64][4] block scales of an FP8 tile in the attention scratch.
+__device__ __forceinline__ float* tile_scales8(unsigned char* scratch) {
+  return (float*)(scratch + 2 * 4 * 16 * 4 + 4 * 2 * 2 * 16 * 32 * 2);
+}
+
 // Attention of the 16 query heads over one tile of n_tok records held in LDS (sparse decode
 // attention, "HiSparse 深度解析" (gentlecold.top) §5.4: the records of the published slots;
-// key = the record's 576 bf16, value = its first 512), folded into the running state.  Waves
+// key = the record's 576 values, value = its first 512), folded into the running state.  Waves
 // 0-3 compute the 16 x 16 score blocks of tokens 16w .. 16w+15 on v_mfma_f32_16x16x32_bf16
 // (18 k-steps); each head's new maximum is the larger of the running one and the tile's, the
 // probabilities are taken against it, and every wave rescales its running sum and output by
 // 2^(old max - new max) before all 16 waves accumulate P V for 32 output channels each.  P is
 // split into bf16 hi + lo parts so the fp32 probabilities survive the bf16 operand.
+// F8: FP8 records (tile_store8).  The scores keep one accumulator per 128-dim scale block (4
+// k-steps each) and one for the bf16 part, and apply the token's scales to the fp32 sums; wave
+// w's 32 channels lie in scale block w / 4, so it takes P times that block's per-token scale
+// (the sums keep the unscaled P).
+template <bool F8>
 __device__ __forceinline__ void attend_tile(const unsigned char* tile, const unsigned char* qs,
                                             unsigned char* scratch, int n_tok, float sl2, AttnAcc& acc) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, qd = lane >> 4;
+  constexpr int NB = F8 ? 4 : 1;                 // P variants (one per scale block)
   float* smax = (float*)scratch;                 // [4][16]
   float* ssum = smax + 64;                       // [4][16]
-  uint16_t* phi = (uint16_t*)(ssum + 64);        // [2 token blocks][16 heads][32]
-  uint16_t* plo = phi + 2 * 16 * 32;
+  uint16_t* phi = (uint16_t*)(ssum + 64);        // [NB][2 token blocks][16 heads][32]
+  uint16_t* plo = phi + NB * 2 * 16 * 32;
+  const float* scl8 = F8 ? tile_scales8(scratch) : nullptr;  // [64][4]
   constexpr int KSTEPS = kAttnDk / 32;
   float sv[4];
   if (w < 4) {
-    // lane: s[head = 4 qd + i][token = 16 w + col]; two accumulators halve the dependent
-    // MFMA chain
-    f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
     const unsigned char* krow = tile + (16 * w + col) * kTileStride + qd * 16;
     const unsigned char* qrow = qs + col * kQStride + qd * 16;
+    float s[4];
+    if constexpr (F8) {
+      f32x4 sb[5];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ks += 2) {
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64), *(const bf16x8*)(krow + ks * 64),
-                                                   sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64 + 64),
-                                                   *(const bf16x8*)(krow + ks * 64 + 64), sb, 0, 0, 0);
+      for (int b = 0; b < 5; ++b) sb[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        sb[ks < 16 ? ks >> 2 : 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *(const bf16x8*)(qrow + ks * 64), *(const bf16x8*)(krow + ks * 64), sb[ks < 16 ? ks >> 2 : 4], 0, 0, 0);
+      const float* sc = scl8 + 4 * (16 * w + col);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = sb[0][i] * sc[0] + sb[1][i] * sc[1] + sb[2][i] * sc[2] + sb[3][i] * sc[3] + sb[4][i];
+    } else {
+      // lane: s[head = 4 qd + i][token = 16 w + col]; two accumulators halve the dependent
+      // MFMA chain
+      f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ks += 2) {
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64), *(const bf16x8*)(krow + ks * 64),
+                                                     sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64 + 64),
+                                                     *(const bf16x8*)(krow + ks * 64 + 64), sb, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = sa[i] + sb[i];
     }
     const bool valid = 16 * w + col < n_tok;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = valid ? (sa[i] + sb[i]) * sl2 : -INFINITY;
+      sv[i] = valid ? s[i] * sl2 : -INFINITY;
       const float mx = row16_max(sv[i]);
       if (col == 0) smax[w * 16 + qd * 4 + i] = mx;
     }
@@ -150,9 +224,14 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
       const float pv = exp2f(sv[i] - mnew[i]);
       const float l = row16_sum(pv);
       if (col == 0) ssum[w * 16 + hh] = l;
-      const uint16_t hi = f32_to_bf16_rne(pv);
-      phi[(bk * 16 + hh) * 32 + kk] = hi;
-      plo[(bk * 16 + hh) * 32 + kk] = f32_to_bf16_rne(pv - __uint_as_float((uint32_t)hi << 16));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        // a masked row (p = 0) takes no scale: a filler's scale must not turn 0 into NaN
+        const float pw = F8 ? (pv != 0.0f ? pv * scl8[4 * tl + b] : 0.0f) : pv;
+        const uint16_t hi = f32_to_bf16_rne(pw);
+        phi[((b * 2 + bk) * 16 + hh) * 32 + kk] = hi;
+        plo[((b * 2 + bk) * 16 + hh) * 32 + kk] = f32_to_bf16_rne(pw - __uint_as_float((uint32_t)hi << 16));
+      }
     }
   }
   __syncthreads();
@@ -167,8 +246,9 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
   // o[head][channel] += p v over the tile; wave w owns channels 32 w .. 32 w + 31
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const bf16x8 ahi = *(const bf16x8*)&phi[(b * 16 + col) * 32 + qd * 8];
-    const bf16x8 alo = *(const bf16x8*)&plo[(b * 16 + col) * 32 + qd * 8];
+    const int pb = F8 ? (w >> 2) * 2 + b : b;  // wave w's channels lie in scale block w / 4
+    const bf16x8 ahi = *(const bf16x8*)&phi[(pb * 16 + col) * 32 + qd * 8];
+    const bf16x8 alo = *(const bf16x8*)&plo[(pb * 16 + col) * 32 + qd * 8];
     const unsigned char* vb = tile + (b * 32 + qd) * kTileStride + (32 * w + col) * 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {

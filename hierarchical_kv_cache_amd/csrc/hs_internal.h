@@ -118,17 +118,20 @@ constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (29
                                      // the quarter-waves of a P V operand read on disjoint banks
 constexpr int kQStride = 1168;       // LDS stride of a query row (16-byte aligned, off the bank period)
 constexpr int kAttnScratch = 2 * 4 * 16 * 4 + 2 * 2 * 16 * 32 * 2;  // maxima, sums, P hi and lo
+// FP8 records: P hi and lo per 128-channel scale block, and the tile's block scales
+constexpr int kAttnScratch8 = 2 * 4 * 16 * 4 + 4 * 2 * 2 * 16 * 32 * 2 + kTileRows * 4 * 4;
+constexpr int kF8RecordBytes = 656;  // 512 E4M3 codes, 4 float32 block scales, 64 bf16
 struct FusedLds {
   size_t tile, qs, arow, asrc, scratch, total;
 };
-__host__ __device__ inline FusedLds fused_lds(int k, int B, int hash_bits, int G, int T) {
+__host__ __device__ inline FusedLds fused_lds(int k, int B, int hash_bits, int G, int T, bool f8 = false) {
   FusedLds F;
   F.tile = 0;
   F.qs = F.tile + size_t(kTileRows) * kTileStride;
   F.asrc = F.qs + 16 * size_t(kQStride);
   F.arow = F.asrc + 8 * size_t(kTileRows) * T;
   F.scratch = F.arow + 4 * size_t(kTileRows) * T;
-  const size_t fetch = align_up(F.scratch + kAttnScratch, 16);
+  const size_t fetch = align_up(F.scratch + (f8 ? kAttnScratch8 : kAttnScratch), 16);
   const size_t resolve = resolve_lds(k, B, hash_bits, G).total;
   F.total = fetch > resolve ? fetch : resolve;
   return F;
@@ -177,6 +180,7 @@ struct ResolveParams {
   uint8_t* att_stage;        // [R][k][rec] missed records by list index
   int32_t heads, att_tiles;
   float att_scale;
+  const uint8_t* att_zero;   // a zero record: the finite filler row of FP8 tiles
 };
 
 // The finish kernel of the fused call: chunk merge (or NaN rows on error), the missed records

@@ -745,7 +745,9 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
 // victim slots, so host bytes cross the link once; the next tile's loads are issued before
 // the current tile is attended, so they fly meanwhile.  Entries in error (out of range,
 // resident rows outside the pool) load a finite filler row; workgroup 0 reports the error
-// and the finish kernel makes the request's output NaN.
+// and the finish kernel makes the request's output NaN.  F8: FP8 records (tile_load8 /
+// tile_store8; the staged misses are the raw 656-byte records; the filler is a zero record).
+template <bool F8>
 __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned char* smem) {
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
@@ -754,12 +756,12 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
   const int f_lo = p.k * (g - 1) / S;  // (32-bit: k * G < 2^23)
   const int f_n = p.k * g / S - f_lo;  // <= 64 att_tiles
   const int nt = (f_n + kTileRows - 1) / kTileRows;
-  const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G, p.att_tiles);
+  const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G, p.att_tiles, F8);
   unsigned char* tile = smem + F.tile;
   unsigned char* qs = smem + F.qs;
   int32_t* arow = (int32_t*)(smem + F.arow);   // list index of the miss of each share entry, -1 otherwise
   uint64_t* asrc = (uint64_t*)(smem + F.asrc);  // record address of each share entry
-  const uint8_t* filler = (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);
+  const uint8_t* filler = F8 ? p.att_zero : (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);
   const uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   u32x4 qv[kQU];
   q_load(qv, p.q, r, p.heads);
@@ -801,25 +803,34 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
   q_store(qv, qs);
   __syncthreads();
   const float sl2 = p.att_scale * 1.4426950408889634f;
-  u32x4 tv[kTU];
-  tile_load(tv, asrc);
+  constexpr int TU = F8 ? kTU8 : kTU;
+  constexpr int RC = F8 ? kF8RowChunks : kRowChunks;
+  constexpr int TC = F8 ? kF8TileChunks : kTileChunks;
+  u32x4 tv[TU];
+  if constexpr (F8) tile_load8(tv, asrc);
+  else tile_load(tv, asrc);
   AttnAcc acc;
   acc_init(acc);
   for (int t = 0; t < nt; ++t) {
     if (t > 0) __syncthreads();  // the previous tile's readers are done with the tile and P
+    // the missed records, as loaded, to the staging area
 #pragma unroll
-    for (int u = 0; u < kTU; ++u) {
+    for (int u = 0; u < TU; ++u) {
       const int f = tid + u * NT;
-      if (f < kTileChunks) {
-        const int row = f / kRowChunks, c = f - row * kRowChunks;
-        *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
+      if (f < TC) {
+        const int row = f / RC, c = f - row * RC;
         const int a = arow[t * kTileRows + row];
         if (a >= 0) *((u32x4*)(p.att_stage + ((size_t)r * p.k + a) * (size_t)p.rec_bytes) + c) = tv[u];
       }
     }
-    if (t + 1 < nt) tile_load(tv, asrc + (t + 1) * kTileRows);
+    if constexpr (F8) tile_store8(tv, tile, tile_scales8(smem + F.scratch));
+    else tile_store(tv, tile);
+    if (t + 1 < nt) {
+      if constexpr (F8) tile_load8(tv, asrc + (t + 1) * kTileRows);
+      else tile_load(tv, asrc + (t + 1) * kTileRows);
+    }
     __syncthreads();
-    attend_tile(tile, qs, smem + F.scratch, min(kTileRows, f_n - t * kTileRows), sl2, acc);
+    attend_tile<F8>(tile, qs, smem + F.scratch, min(kTileRows, f_n - t * kTileRows), sl2, acc);
   }
   float* part = p.part + ((size_t)r * S + (g - 1)) * kPartStride;
   float* out = S == 1 ? p.att_out + (size_t)r * p.heads * kAttnDv : nullptr;
@@ -831,11 +842,23 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   if constexpr (ATT) {
     if ((int)(blockIdx.x / p.R) > 0) {
-      fetch_attend(p, smem);
+      fetch_attend<false>(p, smem);
       return;
     }
   }
   resolve_body<E, KE, ATT>(p, smem);
+}
+
+// The fused kernel over FP8 records: workgroup 0 as in resolve_kernel<E, KE, true>, the fetch
+// workgroups on FP8 tiles.
+template <int E, int KE>
+__global__ void __launch_bounds__(NT) resolve_f8_kernel(ResolveParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if ((int)(blockIdx.x / p.R) > 0) {
+    fetch_attend<true>(p, smem);
+    return;
+  }
+  resolve_body<E, KE, true>(p, smem);
 }
 
 // Union of the verification rows of one speculative step ("HiSparse 深度解析" §6.5
@@ -954,6 +977,18 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterParams p) {
 
 template <int E, int KE, bool ATT>
 hipError_t launch_e(const ResolveParams& p, size_t lds, hipStream_t s, const KernelTiming* tm) {
+  // the fused kernel over FP8 records is a kernel of its own
+  if constexpr (ATT) {
+    if (p.rec_bytes == kF8RecordBytes) {
+      if (tm && tm->start) {
+        hipExtLaunchKernelGGL((resolve_f8_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, tm->start,
+                              tm->stop, 0u, p);
+      } else {
+        hipLaunchKernelGGL((resolve_f8_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), lds, s, p);
+      }
+      return hipGetLastError();
+    }
+  }
   if (tm && tm->start) {
     hipExtLaunchKernelGGL((resolve_kernel<E, KE, ATT>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, tm->start,
                           tm->stop, 0u, p);
@@ -1001,6 +1036,9 @@ hipError_t set_limit_ke(int v) {
     if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1, true>, v);
     if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 2, true>, v);
     if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 4, true>, v);
+    if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_f8_kernel<E, 1>, v);
+    if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_f8_kernel<E, 2>, v);
+    if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_f8_kernel<E, 4>, v);
   }
   return e;
 }

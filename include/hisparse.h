@@ -248,8 +248,10 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
  * applies the page-table updates and copies the staged misses into their victim slots.  T is
  * the smallest value in [1, 16] with num_requests * (S + 1) <= 256, S = ceil(top_k / 64 T),
  * so that all workgroups run at once.  It applies to bf16 records of 576 values
- * (record_bytes 1152), top_k <= 4096, buffer_slots <= 8192 and such a T (so at most 128
- * requests; hs_resolve_attn_wgs > 0); otherwise this call makes the two calls above.
+ * (record_bytes 1152) and to FP8 records (HS_CFG_RECORD_FP8: the codes are turned into bf16
+ * in the tile exactly, the block scales applied in fp32, the misses staged as raw records),
+ * with top_k <= 4096, buffer_slots <= 8192 and such a T (so at most 128 requests;
+ * hs_resolve_attn_wgs > 0); otherwise this call makes the two calls above.
  * HS_SKIP_IO is not allowed (the attention reads the records).  Errors as for the two calls;
  * a request with error bits gets NaN output rows.
  */

@@ -193,13 +193,51 @@ def test_short_requests_cross_into_the_normal_path():
         p.close()
 
 
-def test_fp8_records_take_the_two_calls():
-    """FP8 latent-KV records: no fused kernel (it reads bf16 tiles), the call makes
-    hs_resolve + hs_sparse_attn with the FP8 attention kernel."""
+def test_fp8_records_long():
+    """FP8 latent-KV records (656 bytes) through the fused kernel: the codes are turned into
+    bf16 in the tile, the scores and P V apply the block scales; the misses staged and copied
+    as raw records."""
     w = W["long"].scaled(L=2, steps=4, ctx=32768)
+    log("fp8 long L=2")
     p = Pair(w, fused_heads=16, fp8=True)
     try:
-        run(p, expect_fused=False)
+        assert hk.hs_resolve_attn_wgs(p.h) == 33
+        run(p)
+    finally:
+        p.close()
+
+
+def test_fp8_records_several_tiles():
+    w = W["batched"].scaled(R=32, L=1, steps=3, B=4096)
+    log("fp8 batched R=32: 8 workgroups of 5 tiles")
+    p = Pair(w, fused_heads=16, fp8=True)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) == 8
+        run(p)
+    finally:
+        p.close()
+
+
+def test_fp8_records_resident_tier_and_ragged():
+    """FP8 records from the resident pool and the hot slots, eight requests (two tiles per
+    fetch workgroup), k = 1000 (ragged shares)."""
+    w = W["long"].scaled(R=8, L=1, ctx=65536, k=1000, steps=4, append=False, force_newest=False)
+    log("fp8 R=8 k=1000 with a resident window")
+    p = Pair(w, fused_heads=16, fp8=True, resident=ResidentSpec(page_tokens=64, window_tokens=16384,
+                                                                old_frac=0.1, spill_every=1, churn=0.05))
+    try:
+        run(p)
+    finally:
+        p.close()
+
+
+def test_fp8_records_shared_layers():
+    w = W["shared"].scaled(R=2, L=4, ctx=16384, steps=3)
+    log("fp8 shared R=2 L=4")
+    p = Pair(w, fused_heads=16, fp8=True)
+    try:
+        run(p)
+        p.check_hot()
     finally:
         p.close()
 
