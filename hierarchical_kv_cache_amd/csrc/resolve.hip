@@ -143,32 +143,45 @@ __device__ __forceinline__ void load_run32(const int32_t* __restrict__ src, int 
   for (int j = 0; j < E; ++j) out[j] = (base + j < n) ? src[base + j] : fill;
 }
 
-// The same for int16 elements (8 per 16-byte load, 4 per 8-byte load).
+// The same for int16 elements (8 per 16-byte load, 4 per 8-byte load), kept as the packed
+// 32-bit words they arrive in (element j in half j & 1 of word j / 2) and unpacked where they
+// are used (run16_at), so nothing waits for the loads here.
+template <int E>
+struct Run16 {
+  uint32_t w[E >= 2 ? E / 2 : 1];
+};
 template <int E>
 __device__ __forceinline__ void load_run16(const int16_t* __restrict__ src, int n, int base, bool vec,
-                                           int16_t (&out)[E], int16_t fill) {
+                                           Run16<E>& out, int16_t fill) {
   if constexpr (E >= 4) {
     if (vec && base + E <= n) {
       if constexpr (E == 4) {
         const u32x2 x = *(const u32x2*)(src + base);
-        out[0] = (int16_t)(x[0] & 0xFFFFu); out[1] = (int16_t)(x[0] >> 16);
-        out[2] = (int16_t)(x[1] & 0xFFFFu); out[3] = (int16_t)(x[1] >> 16);
+        out.w[0] = x[0];
+        out.w[1] = x[1];
       } else {
 #pragma unroll
         for (int v = 0; v < E / 8; ++v) {
           const u32x4 x = *((const u32x4*)(src + base) + v);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            out[8 * v + 2 * q] = (int16_t)(x[q] & 0xFFFFu);
-            out[8 * v + 2 * q + 1] = (int16_t)(x[q] >> 16);
-          }
+          for (int q = 0; q < 4; ++q) out.w[4 * v + q] = x[q];
         }
       }
       return;
     }
   }
 #pragma unroll
-  for (int j = 0; j < E; ++j) out[j] = (base + j < n) ? src[base + j] : fill;
+  for (int j = 0; j < E; ++j) {
+    const uint32_t v = (uint16_t)((base + j < n) ? src[base + j] : fill);
+    if (E == 1) out.w[0] = v;
+    else if (j & 1) out.w[j >> 1] |= v << 16;
+    else out.w[j >> 1] = v;
+  }
+}
+template <int E>
+__device__ __forceinline__ int16_t run16_at(const Run16<E>& a, int j) {
+  if constexpr (E == 1) return (int16_t)a.w[0];
+  else return (int16_t)(a.w[j >> 1] >> (16 * (j & 1)));
 }
 
 // E: slots (and LRU positions) per thread, KE: selection entries per thread (both powers
@@ -225,15 +238,20 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   }
 
   // ---- every global read up front -------------------------------------------------------
+  // All loads that do not depend on another load are issued before any branch that could
+  // make the compiler wait: the launch counter, the request's scalars, the selection (this
+  // workgroup's and its fetch share), and both halves of the slot map and LRU order.  Then
+  // the page-table entries of the selected positions (which need the selection): two memory
+  // round trips in all before the LDS work.
   // Launch counter (launch_number: the launches before this one that changed the
   // metadata, whichever of this launch's siblings have already added their share).  Its
   // parity picks the ping-pong half that holds the current slot map and LRU order, and
-  // number + 1 is the generation this launch writes into the page table.  The value is
-  // needed only after the entry loads, so its latency hides behind them.
+  // number + 1 is the generation this launch writes into the page table.  Every lane reads
+  // it (one broadcast load per wave): a load in a branch that also used the value would
+  // wait for it there.
   uint64_t* counter = (uint64_t*)&p.ctrl[r * 4];
-  uint64_t launches = 0;
-  if (tid == 0)
-    launches = launch_number(__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const uint64_t counter_raw = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t short_req = p.ctrl[r * 4 + 3];
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
   const int32_t* selr = p.sel + (size_t)r * p.kb;
@@ -256,6 +274,54 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   const int f_lo = kr * gf / nf;
   const int f_n = kr * (gf + 1) / nf - f_lo;
   const int wid = tid >> 6, lane = tid & 63;
+  int32_t fraw[KE];
+#pragma unroll
+  for (int q = 0; q < KE; ++q) {
+    const int e = q * NT + lane * NW + wid;
+    const int i = f_lo + e;
+    fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
+  }
+  const bool bvec = (p.B % E) == 0;
+  int32_t spa[E], spb[E];
+  Run16<E> lra, lrb;
+  if (g == 0) {  // only workgroup 0 publishes, and only it needs the slot map
+    load_run32<E>(p.slot_pos + ((size_t)r * 2 + 0) * p.B, p.B, e0, bvec, spa, -1);
+    load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
+  }
+  load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, e0, bvec, lra, 0);
+  load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, e0, bvec, lrb, 0);
+  // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
+  // map, so it names the slot of a hit) and, with a resident tier, its resident page.
+  const bool tiered = p.rtable != nullptr;
+  const int32_t* rtr = p.rtable + (tiered ? (size_t)r * p.rt_stride : 0);
+  uint64_t ptv[KE];
+  int32_t rpg[KE];
+#pragma unroll
+  for (int j = 0; j < KE; ++j) {
+    const int i = i0 + j;
+    const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                     : (int64_t)raw[j];
+    const bool ok = j < EK && i < kr && pos64 >= 0 && pos64 < ctx;
+    ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
+    rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
+  }
+  // Misses known early from the page table: a selected position whose entry is -1 (and
+  // that the resident tier does not serve) is not on the device.  Their host loads start
+  // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
+  int32_t fpos[KE], fres[KE];
+  uint64_t fpt[KE];
+#pragma unroll
+  for (int q = 0; q < KE; ++q) {
+    const int e = q * NT + lane * NW + wid;
+    const int i = f_lo + e;
+    int64_t pos64 = -1;
+    if (fetcher && e < f_n)
+      pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
+    const bool ok = pos64 >= 0 && pos64 < ctx;
+    fpos[q] = ok ? (int32_t)pos64 : -1;
+    fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
+    fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
+  }
   const uint8_t* hbase = nullptr;  // this (request, layer)'s host records
   uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   // fused: workgroup 0's report to the finish kernel
@@ -263,7 +329,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   // ---- short-sequence fast path ("HiSparse 深度解析" §5.4, §5.5): a request admitted short
   // keeps its tokens in slot order while its context fits B, so every position is its own
   // slot: no hash, no LRU, no host IO (only the range is checked)
-  if (p.ctrl[r * 4 + 3] != 0 && ctx <= p.B) {
+  if (short_req != 0 && ctx <= p.B) {
     uint32_t bad = 0;
 #pragma unroll
     for (int j = 0; j < KE; ++j) {
@@ -299,37 +365,6 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     }
     return;
   }
-  // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
-  // map, so it names the slot of a hit) and, with a resident tier, its resident page.
-  const bool tiered = p.rtable != nullptr;
-  const int32_t* rtr = p.rtable + (tiered ? (size_t)r * p.rt_stride : 0);
-  uint64_t ptv[KE];
-  int32_t rpg[KE];
-#pragma unroll
-  for (int j = 0; j < KE; ++j) {
-    const int i = i0 + j;
-    const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
-                                     : (int64_t)raw[j];
-    const bool ok = j < EK && i < kr && pos64 >= 0 && pos64 < ctx;
-    ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
-    rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
-  }
-  int32_t fraw[KE];
-#pragma unroll
-  for (int q = 0; q < KE; ++q) {
-    const int e = q * NT + lane * NW + wid;
-    const int i = f_lo + e;
-    fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
-  }
-  const bool bvec = (p.B % E) == 0;
-  int32_t spa[E], spb[E];
-  int16_t lra[E], lrb[E];
-  if (g == 0) {  // only workgroup 0 publishes, and only it needs the slot map
-    load_run32<E>(p.slot_pos + ((size_t)r * 2 + 0) * p.B, p.B, e0, bvec, spa, -1);
-    load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
-  }
-  load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, e0, bvec, lra, 0);
-  load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, e0, bvec, lrb, 0);
   {
     u32x4* h4 = (u32x4*)htab;
     const u32x4 e4 = {~0u, ~0u, ~0u, ~0u};
@@ -338,26 +373,10 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     for (int h = tid; h < (p.B + 7) / 8; h += NT) s4[h] = e4;
   }
   if (tid == 0) {
+    const uint64_t launches = launch_number(counter_raw);
     sh[0] = 0; sh[1] = 0; sh[3] = 0;
     sh[2] = (int)(launches & 1u);
     sh[5] = (int)(uint32_t)(launches + 1);  // this launch's page-table generation
-  }
-  // Misses known early from the page table: a selected position whose entry is -1 (and
-  // that the resident tier does not serve) is not on the device.  Their host loads start
-  // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
-  int32_t fpos[KE], fres[KE];
-  uint64_t fpt[KE];
-#pragma unroll
-  for (int q = 0; q < KE; ++q) {
-    const int e = q * NT + lane * NW + wid;
-    const int i = f_lo + e;
-    int64_t pos64 = -1;
-    if (fetcher && e < f_n)
-      pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
-    const bool ok = pos64 >= 0 && pos64 < ctx;
-    fpos[q] = ok ? (int32_t)pos64 : -1;
-    fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
-    fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
   // resident entries with a row inside the pool, counted per wave
   uint32_t rbits = 0;
@@ -549,7 +568,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   const bool h1 = sh[2] != 0;  // current metadata in half 1, new metadata goes to half 0
   int16_t lro[E];
 #pragma unroll
-  for (int j = 0; j < E; ++j) lro[j] = h1 ? lrb[j] : lra[j];
+  for (int j = 0; j < E; ++j) lro[j] = h1 ? run16_at(lrb, j) : run16_at(lra, j);
   int16_t* lru_new = p.lru + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.Bpad;
 
   if (err) {  // every workgroup of the request sees the same error; nothing changes
