@@ -322,7 +322,8 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
     fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
-  const uint8_t* hbase = nullptr;  // this (request, layer)'s host records
+  // this (request, layer)'s host records (the pointer table is read at entry with the rest)
+  const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
   uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   // fused: workgroup 0's report to the finish kernel
   uint32_t* hdr = ATT ? p.att_hdr + (size_t)r * 4 : nullptr;
@@ -547,7 +548,6 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (fetcher) hbase = p.host_base[r] + p.host_layer_off;
   const int wtotal = mw * C;  // 16-byte chunks of this wave's misses
   u32x4 early[kEarly];
 #pragma unroll
@@ -781,6 +781,12 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
   int32_t* arow = (int32_t*)(smem + F.arow);   // list index of the miss of each share entry, -1 otherwise
   uint64_t* asrc = (uint64_t*)(smem + F.asrc);  // record address of each share entry
   const uint8_t* filler = F8 ? p.att_zero : (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);
+  // the request's scalars, read before the branches below so that they share the selection's
+  // round trip and only the page-table entries come after it
+  const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
+  const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
+  const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
+  const uint32_t short_req = p.ctrl[r * 4 + 3];
   const uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   u32x4 qv[kQU];
   q_load(qv, p.q, r, p.heads);
@@ -791,9 +797,7 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
     int32_t mi = -1;
     if (e < f_n) {
       const int i = f_lo + e;
-      const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
-      const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
-      const bool short_path = p.ctrl[r * 4 + 3] != 0 && ctx <= p.B;  // slot = position
+      const bool short_path = short_req != 0 && ctx <= p.B;  // slot = position
       const int32_t raw = p.sel[(size_t)r * p.kb + (p.bt_shift ? (i >> p.bt_shift) : i)];
       const int64_t pos64 = p.bt_shift ? ((int64_t)raw << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)raw;
       if (pos64 >= 0 && pos64 < ctx) {
@@ -810,7 +814,7 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
           } else if (sl >= 0) {
             if (sl < p.B) src = dbase + (size_t)sl * p.rec_bytes;
           } else {
-            src = p.host_base[r] + p.host_layer_off + (size_t)pos64 * p.rec_bytes;
+            src = hbase + (size_t)pos64 * p.rec_bytes;
             mi = i;
           }
         }
