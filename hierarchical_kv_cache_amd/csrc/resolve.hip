@@ -43,9 +43,10 @@
 // No workgroup waits on another.
 //
 // Latency shape (the all-hit call is bounded by launch and memory latency,
-// not bandwidth): every global read the kernel needs -- the selection, both
-// halves of the slot map and LRU order, the launch counter -- is issued at entry, so
-// the kernel pays about one memory round trip before its LDS work.  Threads
+// not bandwidth): every global read that depends on no other -- the selection, both
+// halves of the slot map and LRU order, the launch counter, the request's scalars -- is
+// issued at entry before any branch, then the page-table entries of the selected
+// positions, so the kernel pays two memory round trips before its LDS work.  Threads
 // own contiguous runs of slots / LRU positions / selection entries, loaded
 // as vectors; hash insertion uses plain LDS stores and a read-back instead
 // of atomics (which the LDS serialises lane by lane); all probes of a thread
