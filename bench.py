@@ -1097,6 +1097,7 @@ SECONDARY = {
     "attention": measure_attention,
     "shared_step": measure_shared_step,
     "fp8": measure_fp8,
+    "short": measure_short,
 }
 
 if __name__ == "__main__":

@@ -247,11 +247,13 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   // Launch counter (launch_number: the launches before this one that changed the
   // metadata, whichever of this launch's siblings have already added their share).  Its
   // parity picks the ping-pong half that holds the current slot map and LRU order, and
-  // number + 1 is the generation this launch writes into the page table.  Every lane reads
-  // it (one broadcast load per wave): a load in a branch that also used the value would
-  // wait for it there.
+  // number + 1 is the generation this launch writes into the page table.  Thread 0 reads it
+  // (an agent-scope load; one per wave made the all-hit call slower) and the value is used
+  // only where sh[2] and sh[5] are set, so nothing waits for it before the other loads are
+  // issued.
   uint64_t* counter = (uint64_t*)&p.ctrl[r * 4];
-  const uint64_t counter_raw = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t counter_raw = 0;
+  if (tid == 0) counter_raw = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t short_req = p.ctrl[r * 4 + 3];
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
@@ -291,38 +293,6 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   }
   load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, e0, bvec, lra, 0);
   load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, e0, bvec, lrb, 0);
-  // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
-  // map, so it names the slot of a hit) and, with a resident tier, its resident page.
-  const bool tiered = p.rtable != nullptr;
-  const int32_t* rtr = p.rtable + (tiered ? (size_t)r * p.rt_stride : 0);
-  uint64_t ptv[KE];
-  int32_t rpg[KE];
-#pragma unroll
-  for (int j = 0; j < KE; ++j) {
-    const int i = i0 + j;
-    const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
-                                     : (int64_t)raw[j];
-    const bool ok = j < EK && i < kr && pos64 >= 0 && pos64 < ctx;
-    ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
-    rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
-  }
-  // Misses known early from the page table: a selected position whose entry is -1 (and
-  // that the resident tier does not serve) is not on the device.  Their host loads start
-  // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
-  int32_t fpos[KE], fres[KE];
-  uint64_t fpt[KE];
-#pragma unroll
-  for (int q = 0; q < KE; ++q) {
-    const int e = q * NT + lane * NW + wid;
-    const int i = f_lo + e;
-    int64_t pos64 = -1;
-    if (fetcher && e < f_n)
-      pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
-    const bool ok = pos64 >= 0 && pos64 < ctx;
-    fpos[q] = ok ? (int32_t)pos64 : -1;
-    fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
-    fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
-  }
   // this (request, layer)'s host records (the pointer table is read at entry with the rest)
   const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
   uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
@@ -366,6 +336,39 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
       if (ATT && tid == 0) { hdr[0] = bad ? (uint32_t)HS_ERR_RANGE : 0u; hdr[1] = 0u; }
     }
     return;
+  }
+  // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
+  // map, so it names the slot of a hit) and, with a resident tier, its resident page: the
+  // second round trip (after the short-path test, which needs only the first).
+  const bool tiered = p.rtable != nullptr;
+  const int32_t* rtr = p.rtable + (tiered ? (size_t)r * p.rt_stride : 0);
+  uint64_t ptv[KE];
+  int32_t rpg[KE];
+#pragma unroll
+  for (int j = 0; j < KE; ++j) {
+    const int i = i0 + j;
+    const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                     : (int64_t)raw[j];
+    const bool ok = j < EK && i < kr && pos64 >= 0 && pos64 < ctx;
+    ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
+    rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
+  }
+  // Misses known early from the page table: a selected position whose entry is -1 (and
+  // that the resident tier does not serve) is not on the device.  Their host loads start
+  // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
+  int32_t fpos[KE], fres[KE];
+  uint64_t fpt[KE];
+#pragma unroll
+  for (int q = 0; q < KE; ++q) {
+    const int e = q * NT + lane * NW + wid;
+    const int i = f_lo + e;
+    int64_t pos64 = -1;
+    if (fetcher && e < f_n)
+      pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
+    const bool ok = pos64 >= 0 && pos64 < ctx;
+    fpos[q] = ok ? (int32_t)pos64 : -1;
+    fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
+    fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
   }
   {
     u32x4* h4 = (u32x4*)htab;
