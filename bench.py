@@ -48,6 +48,15 @@ def parse():
     return ap.parse_args()
 
 
+def addr(t, *idx):
+    """Device address of t[idx] computed from the strides, without building the view (a
+    torch view costs microseconds of host time per call, more than the launch it feeds)."""
+    off = 0
+    for i, st in zip(idx, t.stride()):
+        off += i * st
+    return t.data_ptr() + off * t.element_size()
+
+
 def sync_barrier(torch):
     torch.cuda.synchronize()
 
@@ -141,6 +150,15 @@ def main():
     compute = torch.cuda.current_stream()
     backup = torch.cuda.Stream()
     cs, bs = compute.cuda_stream, backup.cuda_stream
+    # every step's buffer addresses, computed once (as a serving loop holds them)
+    a_sel = [[addr(d_trace, t, l) for l in range(L)] for t in range(n_steps)]
+    a_q = [[addr(d_q, t, l) for l in range(L)] for t in range(n_steps)]
+    a_stats = [[addr(d_stats, t, l) for l in range(L)] for t in range(n_steps)]
+    a_ctx = [addr(d_ctx, t) for t in range(n_steps)]
+    a_kv = [addr(d_new_kv, t) for t in range(n_steps)]
+    a_pos = [addr(d_new_pos, t) for t in range(n_steps)]
+    a_slots = [addr(d_slots, l) for l in range(L)]
+    a_out = [addr(d_out, l) for l in range(L)]
     input_s = time.time() - t_in
 
     def step(c, t, fused, ev_row=None):
@@ -148,19 +166,18 @@ def main():
         attention over the published slots (one fused call, or hs_resolve + hs_sparse_attn).
         ev_row: events recorded on the launch stream around each layer's attention call
         (separate calls only)."""
-        hk.hs_append(c.h, d_new_kv[t].data_ptr(), d_new_pos[t].data_ptr(), cs, bs)
+        h = c.h
+        hk.hs_append(h, a_kv[t], a_pos[t], cs, bs)
+        sel, q, stats, ctx = a_sel[t], a_q[t], a_stats[t], a_ctx[t]
         for l in range(L):
             if fused:
-                hk.hs_resolve_attn(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
-                                   d_stats[t, l].data_ptr(), 0, 0, d_q[t, l].data_ptr(), heads, 512,
-                                   d_out[l].data_ptr(), scale, cs)
+                hk.hs_resolve_attn(h, l, sel[l], ctx, a_slots[l], stats[l], 0, 0, q[l], heads, 512,
+                                   a_out[l], scale, cs)
             else:
-                hk.hs_resolve(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
-                              d_stats[t, l].data_ptr(), 0, 0, cs)
+                hk.hs_resolve(h, l, sel[l], ctx, a_slots[l], stats[l], 0, 0, cs)
                 if ev_row is not None:
                     ev_row[l][0].record(compute)
-                hk.hs_sparse_attn(c.h, l, d_q[t, l].data_ptr(), heads, 512, d_slots[l].data_ptr(),
-                                  d_out[l].data_ptr(), scale, 0, cs)
+                hk.hs_sparse_attn(h, l, q[l], heads, 512, a_slots[l], a_out[l], scale, 0, cs)
             if ev_row is not None:
                 ev_row[l][1].record(compute)
 
@@ -171,17 +188,20 @@ def main():
         return c
 
     def value_pass(c, fused):
-        """W warmup steps, then K timed steps with nothing between kernels."""
+        """W warmup steps, then K timed steps with nothing between kernels.  Returns the
+        elapsed time and the host's enqueue time of the K steps (well below the elapsed time:
+        the GPU, not the host, sets the pace)."""
         for t in range(W):
             step(c, t, fused)
         sync_barrier(torch)
         t0 = time.perf_counter()
         for i in range(K):
             step(c, W + i, fused)
+        t_enq = time.perf_counter() - t0
         sync_barrier(torch)
         dt = time.perf_counter() - t0
         backup.synchronize()
-        return dt
+        return dt, t_enq
 
     def timing_pass(c, fused):
         """The same steps from the same empty start: the RESOLVE (or fused) kernel of every
@@ -202,7 +222,7 @@ def main():
 
     # pass 1 (the reported value): the fused path
     fused = hk.hs_resolve_attn_wgs(cache.h) > 0
-    elapsed = value_pass(cache, True)
+    elapsed, enqueue = value_pass(cache, True)
     stats = d_stats.cpu().numpy()
     out_fused = d_out.clone()
     cache.close()
@@ -215,7 +235,7 @@ def main():
     # passes 3 and 4: the same steps through hs_resolve + hs_sparse_attn
     cache = fresh_cache()
     d_stats.zero_()
-    elapsed_sep = value_pass(cache, False)
+    elapsed_sep, enqueue_sep = value_pass(cache, False)
     assert np.array_equal(d_stats.cpu().numpy(), stats), "the separate calls resolved differently"
     att_dev = float((d_out - out_fused).abs().max() / out_fused.abs().max())
     cache.close()
@@ -233,11 +253,13 @@ def main():
     detail = {
         "path": "hs_resolve_attn (fused RESOLVE + attention kernel, then merge)" if fused
                 else "hs_resolve_attn (two calls: no fused kernel for this configuration)",
+        "host_enqueue_us_per_step": enqueue / K * 1e6,
         "fused_kernel_us_per_layer_mean": statistics.fmean(kern_us),
         "fused_kernel_us_per_layer_median": statistics.median(kern_us),
         "fused_wgs_per_request": hk.hs_resolve_attn_wgs(cache.h),
         "separate_selections_per_s": selections / elapsed_sep,
         "separate_ms_per_step": elapsed_sep / K * 1e3,
+        "separate_host_enqueue_us_per_step": enqueue_sep / K * 1e6,
         "separate_resolve_kernel_us_per_layer_mean": statistics.fmean(res_us),
         "separate_resolve_kernel_us_per_layer_median": statistics.median(res_us),
         "separate_attention_call_us_per_layer_mean": statistics.fmean(att_us),

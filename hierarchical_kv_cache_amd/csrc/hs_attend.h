@@ -144,66 +144,89 @@ __device__ __forceinline__ float* tile_scales8(unsigned char* scratch) {
   return (float*)(scratch + 2 * 4 * 16 * 4 + 4 * 2 * 2 * 16 * 32 * 2);
 }
 
+// V operand of v_mfma_f32_16x16x32_bf16 by two transposed LDS reads (ds_read_b64_tr_b16).
+// Within each 16-lane group the instruction hands output lane L, element j, element L % 4 of
+// the 8 bytes that lane 4 j + L / 4 addressed.  So lane s of group g addresses row
+// row0 + 8 g + s / 4 (second read: 4 rows further) at channel c0 + 4 (s % 4), and lane L ends
+// up with channel c0 + L of rows row0 + 8 g + 0..7: the operand's k index is the token's
+// place in its 32-token block.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 v_operand(const unsigned char* tile, int row0, int c0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const unsigned char* a = tile + (row0 + 8 * g + (s >> 2)) * kTileStride + 2 * (c0 + 4 * (s & 3));
+  typedef s16x4 __attribute__((address_space(3))) * lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a + 4 * kTileStride));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Attention of the 16 query heads over one tile of n_tok records held in LDS (sparse decode
 // attention, "HiSparse 深度解析" (gentlecold.top) §5.4: the records of the published slots;
-// key = the record's 576 values, value = its first 512), folded into the running state.  Waves
-// 0-3 compute the 16 x 16 score blocks of tokens 16w .. 16w+15 on v_mfma_f32_16x16x32_bf16
-// (18 k-steps); each head's new maximum is the larger of the running one and the tile's, the
-// probabilities are taken against it, and every wave rescales its running sum and output by
-// 2^(old max - new max) before all 16 waves accumulate P V for 32 output channels each.  P is
-// split into bf16 hi + lo parts so the fp32 probabilities survive the bf16 operand.
-// F8: FP8 records (tile_store8).  The scores keep one accumulator per 128-dim scale block (4
-// k-steps each) and one for the bf16 part, and apply the token's scales to the fp32 sums; wave
-// w's 32 channels lie in scale block w / 4, so it takes P times that block's per-token scale
-// (the sums keep the unscaled P).
+// key = the record's 576 values, value = its first 512), folded into the running state, on
+// v_mfma_f32_16x16x32_bf16 with all 16 waves busy in every phase:
+//   1. scores: wave w computes the 16 heads x 16 tokens block of tokens 16 (w % 4) .. + 15 over
+//      key range w / 4 (its 4 k-steps of 32 channels, 128 (w / 4) .. + 127, and for w / 4 < 2
+//      the rope k-step 16 + w / 4), all its operand reads issued at once, into LDS;
+//   2. wave w then takes head 4 qd + w / 4 (lane quarter qd) of its 16 tokens: the four
+//      partial sums added in key-range order, scaled and masked, and the block maximum;
+//   3. each head's new maximum is the larger of the running one and the tile's; the wave's
+//      probabilities against it, their block sum, and P split into bf16 hi + lo parts (so the
+//      fp32 probabilities survive the bf16 operand) in the operand layout of step 4;
+//   4. every wave rescales its running sum and output by 2^(old max - new max) and
+//      accumulates P V for 32 output channels, the V operands read transposed (v_operand).
+// F8: FP8 records (tile_store8).  Key range kp is scale block kp: its partial takes the token's
+// block scale on the fp32 sum before the rope part is added; wave w's 32 output channels lie
+// in scale block w / 4, so it takes P times that block's per-token scale (the sums keep the
+// unscaled P).
 template <bool F8>
 __device__ __forceinline__ void attend_tile(const unsigned char* tile, const unsigned char* qs,
                                             unsigned char* scratch, int n_tok, float sl2, AttnAcc& acc) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, qd = lane >> 4;
-  constexpr int NB = F8 ? 4 : 1;                 // P variants (one per scale block)
-  float* smax = (float*)scratch;                 // [4][16]
-  float* ssum = smax + 64;                       // [4][16]
-  uint16_t* phi = (uint16_t*)(ssum + 64);        // [NB][2 token blocks][16 heads][32]
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, qd = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tb = w & 3, kp = w >> 2;  // token block and key range of step 1; head 4 qd + kp in 2-3
+  constexpr int NB = F8 ? 4 : 1;      // P variants (one per scale block)
+  float* smax = (float*)scratch;      // [4 token blocks][16 heads]
+  float* ssum = smax + 64;            // [4][16]
+  float* spart = ssum + 64;           // step 1 -> 2: [4 key ranges][4 token blocks][16 heads][16 tokens]
+  uint16_t* phi = (uint16_t*)spart;   // step 3 -> 4 (the partials are dead): [NB][2 token blocks][16 heads][32]
   uint16_t* plo = phi + NB * 2 * 16 * 32;
   const float* scl8 = F8 ? tile_scales8(scratch) : nullptr;  // [64][4]
-  constexpr int KSTEPS = kAttnDk / 32;
-  float sv[4];
-  if (w < 4) {
-    const unsigned char* krow = tile + (16 * w + col) * kTileStride + qd * 16;
+  const int tl = 16 * tb + col;       // this lane's token in steps 2-3
+  {
+    // lane: partial s[head = 4 qd + i][token = 16 tb + col]
+    const unsigned char* krow = tile + tl * kTileStride + qd * 16;
     const unsigned char* qrow = qs + col * kQStride + qd * 16;
-    float s[4];
-    if constexpr (F8) {
-      f32x4 sb[5];
+    bf16x8 qa[4], ka[4];
 #pragma unroll
-      for (int b = 0; b < 5; ++b) sb[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        sb[ks < 16 ? ks >> 2 : 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            *(const bf16x8*)(qrow + ks * 64), *(const bf16x8*)(krow + ks * 64), sb[ks < 16 ? ks >> 2 : 4], 0, 0, 0);
-      const float* sc = scl8 + 4 * (16 * w + col);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = sb[0][i] * sc[0] + sb[1][i] * sc[1] + sb[2][i] * sc[2] + sb[3][i] * sc[3] + sb[4][i];
-    } else {
-      // lane: s[head = 4 qd + i][token = 16 w + col]; two accumulators halve the dependent
-      // MFMA chain
-      f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ks += 2) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64), *(const bf16x8*)(krow + ks * 64),
-                                                     sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(qrow + ks * 64 + 64),
-                                                     *(const bf16x8*)(krow + ks * 64 + 64), sb, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = sa[i] + sb[i];
+    for (int j = 0; j < 4; ++j) {
+      qa[j] = *(const bf16x8*)(qrow + (4 * kp + j) * 64);
+      ka[j] = *(const bf16x8*)(krow + (4 * kp + j) * 64);
     }
-    const bool valid = 16 * w + col < n_tok;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = valid ? s[i] * sl2 : -INFINITY;
-      const float mx = row16_max(sv[i]);
-      if (col == 0) smax[w * 16 + qd * 4 + i] = mx;
+    f32x4 sr = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (kp < 2) {
+      const bf16x8 qr = *(const bf16x8*)(qrow + (16 + kp) * 64);
+      const bf16x8 kr = *(const bf16x8*)(krow + (16 + kp) * 64);
+      sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qr, kr, sr, 0, 0, 0);
     }
+    f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], ka[j], sa, 0, 0, 0);
+    const float sc = F8 ? scl8[4 * tl + kp] : 1.0f;
+    float* sp = spart + (kp * 4 + tb) * 256 + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sp[(4 * qd + i) * 16] = F8 ? sa[i] * sc + sr[i] : sa[i] + sr[i];
+  }
+  __syncthreads();
+  const int hk = 4 * qd + kp;
+  float sv;
+  {
+    const float* sp = spart + tb * 256 + hk * 16 + col;
+    const float s = sp[0] + sp[1024] + sp[2048] + sp[3072];
+    sv = tl < n_tok ? s * sl2 : -INFINITY;
+    const float mx = row16_max(sv);
+    if (col == 0) smax[tb * 16 + hk] = mx;
   }
   __syncthreads();
   float mnew[4], alpha[4];
@@ -211,27 +234,22 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
   for (int i = 0; i < 4; ++i) {
     const int hh = qd * 4 + i;
     const float mt = fmaxf(fmaxf(smax[hh], smax[16 + hh]), fmaxf(smax[32 + hh], smax[48 + hh]));
-    mnew[i] = fmaxf(acc.m[i], mt);     // finite: every tile has a valid row
+    mnew[i] = fmaxf(acc.m[i], mt);         // finite: every tile has a valid row
     alpha[i] = exp2f(acc.m[i] - mnew[i]);  // 0 on the first tile
   }
-  if (w < 4) {
-    const int tl = 16 * w + col;
-    const int bk = tl >> 5, t32 = tl & 31;
-    const int kk = (t32 & 3) * 8 + (t32 >> 2);  // P V operands pair k index 8 qd + j with token 4 j + qd
+  {
+    const float mk = kp == 0 ? mnew[0] : kp == 1 ? mnew[1] : kp == 2 ? mnew[2] : mnew[3];
+    const float pv = exp2f(sv - mk);
+    const float l = row16_sum(pv);
+    if (col == 0) ssum[tb * 16 + hk] = l;
+    const int bk = tl >> 5, kk = tl & 31;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = qd * 4 + i;
-      const float pv = exp2f(sv[i] - mnew[i]);
-      const float l = row16_sum(pv);
-      if (col == 0) ssum[w * 16 + hh] = l;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        // a masked row (p = 0) takes no scale: a filler's scale must not turn 0 into NaN
-        const float pw = F8 ? (pv != 0.0f ? pv * scl8[4 * tl + b] : 0.0f) : pv;
-        const uint16_t hi = f32_to_bf16_rne(pw);
-        phi[((b * 2 + bk) * 16 + hh) * 32 + kk] = hi;
-        plo[((b * 2 + bk) * 16 + hh) * 32 + kk] = f32_to_bf16_rne(pw - __uint_as_float((uint32_t)hi << 16));
-      }
+    for (int b = 0; b < NB; ++b) {
+      // a masked row (p = 0) takes no scale: a filler's scale must not turn 0 into NaN
+      const float pw = F8 ? (pv != 0.0f ? pv * scl8[4 * tl + b] : 0.0f) : pv;
+      const uint16_t hi = f32_to_bf16_rne(pw);
+      phi[((b * 2 + bk) * 16 + hk) * 32 + kk] = hi;
+      plo[((b * 2 + bk) * 16 + hk) * 32 + kk] = f32_to_bf16_rne(pw - __uint_as_float((uint32_t)hi << 16));
     }
   }
   __syncthreads();
@@ -249,12 +267,9 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
     const int pb = F8 ? (w >> 2) * 2 + b : b;  // wave w's channels lie in scale block w / 4
     const bf16x8 ahi = *(const bf16x8*)&phi[(pb * 16 + col) * 32 + qd * 8];
     const bf16x8 alo = *(const bf16x8*)&plo[(pb * 16 + col) * 32 + qd * 8];
-    const unsigned char* vb = tile + (b * 32 + qd) * kTileStride + (32 * w + col) * 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      bf16x8 vv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vv[j] = *(const __bf16*)(vb + 4 * j * kTileStride + c * 32);
+      const bf16x8 vv = v_operand(tile, 32 * b, 32 * w + 16 * c, lane);
       acc.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, vv, acc.o[c], 0, 0, 0);
       acc.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, vv, acc.o[c], 0, 0, 0);
     }

@@ -113,13 +113,18 @@ int resolve_elems_per_thread(int k, int B);
 // larger of the two.
 constexpr int kTileRows = 64;        // records per tile
 constexpr int kFusedMaxTiles = 16;   // tiles per fetch workgroup (share entries <= 1024 threads)
-constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (292 words): the 16 rows
-                                     // of a QK^T operand read fall on 16 distinct 4-bank groups, and
-                                     // the quarter-waves of a P V operand read on disjoint banks
+constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (292 words, 8-byte
+                                     // aligned for the transposed V reads): consecutive rows start
+                                     // 36 banks apart modulo 64, so the 16 rows of a QK^T operand
+                                     // read, and the 4 rows of a 16-lane group of a V read, spread
 constexpr int kQStride = 1168;       // LDS stride of a query row (16-byte aligned, off the bank period)
-constexpr int kAttnScratch = 2 * 4 * 16 * 4 + 2 * 2 * 16 * 32 * 2;  // maxima, sums, P hi and lo
-// FP8 records: P hi and lo per 128-channel scale block, and the tile's block scales
+// maxima and sums, then the partial scores (4 key ranges x 4 token blocks x 16 x 16 fp32),
+// whose space P hi and lo reuse
+constexpr int kAttnScratch = 2 * 4 * 16 * 4 + 4 * 4 * 16 * 16 * 4;
+// FP8 records: the same (P hi and lo per 128-channel scale block fill the partials' space
+// exactly), and the tile's block scales
 constexpr int kAttnScratch8 = 2 * 4 * 16 * 4 + 4 * 2 * 2 * 16 * 32 * 2 + kTileRows * 4 * 4;
+static_assert(4 * 2 * 2 * 16 * 32 * 2 == 4 * 4 * 16 * 16 * 4, "FP8 P fills the partial scores' space");
 constexpr int kF8RecordBytes = 656;  // 512 E4M3 codes, 4 float32 block scales, 64 bf16
 struct FusedLds {
   size_t tile, qs, arow, asrc, scratch, total;
