@@ -161,13 +161,14 @@ def main():
     a_out = [addr(d_out, l) for l in range(L)]
     input_s = time.time() - t_in
 
-    def step(c, t, fused, ev_row=None):
+    def step(c, t, fused, ev_row=None, backup_stream=False):
         """One decode step: write-through of the new token, then per layer RESOLVE and the
         attention over the published slots (one fused call, or hs_resolve + hs_sparse_attn).
-        ev_row: events recorded on the launch stream around each layer's attention call
-        (separate calls only)."""
+        The write-through is one kernel on the compute stream (backup_stream: the backup
+        stream with its event pair).  ev_row: events recorded on the launch stream around
+        each layer's attention call (separate calls only)."""
         h = c.h
-        hk.hs_append(h, a_kv[t], a_pos[t], cs, bs)
+        hk.hs_append(h, a_kv[t], a_pos[t], cs, bs if backup_stream else cs)
         sel, q, stats, ctx = a_sel[t], a_q[t], a_stats[t], a_ctx[t]
         for l in range(L):
             if fused:
@@ -187,16 +188,16 @@ def main():
             synth.fill_request(c.host_pool_address(r), r, L, lmax, w.ctx)
         return c
 
-    def value_pass(c, fused):
+    def value_pass(c, fused, backup_stream=False):
         """W warmup steps, then K timed steps with nothing between kernels.  Returns the
         elapsed time and the host's enqueue time of the K steps (well below the elapsed time:
         the GPU, not the host, sets the pace)."""
         for t in range(W):
-            step(c, t, fused)
+            step(c, t, fused, backup_stream=backup_stream)
         sync_barrier(torch)
         t0 = time.perf_counter()
         for i in range(K):
-            step(c, W + i, fused)
+            step(c, W + i, fused, backup_stream=backup_stream)
         t_enq = time.perf_counter() - t0
         sync_barrier(torch)
         dt = time.perf_counter() - t0
@@ -226,6 +227,13 @@ def main():
     stats = d_stats.cpu().numpy()
     out_fused = d_out.clone()
     cache.close()
+    # pass 1b: the same with the write-through on the backup stream (the pages' layout)
+    cache = fresh_cache()
+    d_stats.zero_()
+    elapsed_bs, _ = value_pass(cache, True, backup_stream=True)
+    assert np.array_equal(d_stats.cpu().numpy(), stats), "the backup-stream pass resolved differently"
+    assert torch.equal(d_out, out_fused), "the backup-stream pass attended differently"
+    cache.close()
     # pass 2: kernel durations of the fused path
     cache = fresh_cache()
     d_stats.zero_()
@@ -254,6 +262,8 @@ def main():
         "path": "hs_resolve_attn (fused RESOLVE + attention kernel, then merge)" if fused
                 else "hs_resolve_attn (two calls: no fused kernel for this configuration)",
         "host_enqueue_us_per_step": enqueue / K * 1e6,
+        "write_through_backup_stream_ms_per_step": elapsed_bs / K * 1e3,
+        "write_through_backup_stream_selections_per_s": selections / elapsed_bs,
         "fused_kernel_us_per_layer_mean": statistics.fmean(kern_us),
         "fused_kernel_us_per_layer_median": statistics.median(kern_us),
         "fused_wgs_per_request": hk.hs_resolve_attn_wgs(cache.h),
@@ -436,7 +446,6 @@ def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, reside
     d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
     d_stats = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
     ctx = torch.from_numpy((w.ctx + 1 + np.arange(steps))[:, None].repeat(R, 1).astype(np.int32)).to(dev) \
         if w.append else torch.full((steps, R), w.ctx, dtype=torch.int32, device=dev)
     if w.append:
@@ -449,7 +458,7 @@ def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, reside
         if resident is not None:
             d_table.copy_(d_tables[t])
         if w.append:
-            hk.hs_append(cache.h, new_kv[t].data_ptr(), new_pos[t].data_ptr(), s.cuda_stream, side.cuda_stream)
+            hk.hs_append(cache.h, new_kv[t].data_ptr(), new_pos[t].data_ptr(), s.cuda_stream, s.cuda_stream)
         for l in range(L):
             hk.hs_resolve(cache.h, l, d_trace[t, l].data_ptr(), ctx[t].data_ptr(), d_slots.data_ptr(),
                           d_stats[t, l].data_ptr(), 0, flags, s.cuda_stream)
@@ -628,10 +637,9 @@ def measure_fp8(torch, hk, synth, dev, steps=40, warmup=8):
     d_stats = torch.zeros((n, L, R, 4), dtype=torch.int32, device=dev)
     d_out = torch.empty((L, R, w.heads, 512), dtype=torch.float32, device=dev)
     cs = torch.cuda.current_stream().cuda_stream
-    bs = torch.cuda.Stream()
 
     def step(c, t, fused):
-        hk.hs_append(c.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), cs, bs.cuda_stream)
+        hk.hs_append(c.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), cs, cs)
         for l in range(L):
             if fused:
                 hk.hs_resolve_attn(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
@@ -652,7 +660,6 @@ def measure_fp8(torch, hk, synth, dev, steps=40, warmup=8):
             step(c, t, fused)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        bs.synchronize()
         return el
 
     fused = hk.hs_resolve_attn_wgs(cache.h) > 0
@@ -692,18 +699,16 @@ def measure_rows(torch, hk, synth, dev, rows=4, steps=24):
     d_out = torch.empty((R, rows, k), dtype=torch.int32, device=dev)
     d_stats = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream()
-    bs = torch.cuda.Stream()
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
            for _ in range(steps)]
     for t in range(steps):
-        hk.hs_append(cache.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), s.cuda_stream, bs.cuda_stream)
+        hk.hs_append(cache.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), s.cuda_stream, s.cuda_stream)
         for l in range(L):
             evs[t][l][0].record(s)
             hk.hs_resolve_rows(cache.h, l, rows, d_tr[t, l].data_ptr(), d_ctx[t].data_ptr(), d_out.data_ptr(),
                                d_stats[t, l].data_ptr(), 0, 0, s.cuda_stream)
             evs[t][l][1].record(s)
     torch.cuda.synchronize()
-    bs.synchronize()
     us = np.array([[evs[t][l][0].elapsed_time(evs[t][l][1]) * 1e3 for l in range(L)] for t in range(steps)])
     st = d_stats.cpu().numpy()
     assert not st[..., 2].any()

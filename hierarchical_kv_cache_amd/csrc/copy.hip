@@ -23,6 +23,10 @@ __device__ __forceinline__ void split_index(int f, int C, float invC, int& j, in
 // New token -> slot B of every (request, layer); the newest position is set
 // ("HiSparse 深度解析" (gentlecold.top) §3.4: written into the GPU's reserved
 // slot first).  Flattened over (request, layer, 16-byte chunk).
+// WT: the write-through in the same pass (each 16-byte chunk also stored into the host pool at
+// the new position, then the system-scope fence of backup_kernel), for callers that order it on
+// their own stream instead of a backup stream.
+template <bool WT>
 __global__ void __launch_bounds__(kCopyThreads) append_kernel(AppendParams p) {
   const int C = p.rec_bytes >> 4;
   const int per_req = p.L * C;
@@ -38,6 +42,10 @@ __global__ void __launch_bounds__(kCopyThreads) append_kernel(AppendParams p) {
     u32x4* dst = (u32x4*)(p.hot + (((size_t)r * p.L + l) * (p.B + 1) + p.B) * p.rec_bytes) + c;
     const u32x4 v = *src;
     *dst = v;
+    if constexpr (WT) {
+      uint8_t* row = const_cast<uint8_t*>(p.host_base[r]) + ((size_t)l * p.max_positions + pos) * p.rec_bytes;
+      store_host16(v, row + 16 * (size_t)c);
+    }
     // a short request keeps its tokens in slot order while they fit ("HiSparse 深度解析" §5.4)
     const bool in_order = p.ctrl[r * 4 + 3] != 0 && pos < p.B;
     if (in_order) *((u32x4*)(p.hot + (((size_t)r * p.L + l) * (p.B + 1) + pos) * p.rec_bytes) + c) = v;
@@ -53,6 +61,7 @@ __global__ void __launch_bounds__(kCopyThreads) append_kernel(AppendParams p) {
       }
     }
   }
+  if constexpr (WT) __threadfence_system();
 }
 
 // Slot B -> host pool at the newest position (write-through on the backup
@@ -314,9 +323,12 @@ int grid_for(size_t work, int per_block, int cap) {
 
 }  // namespace
 
-hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+hipError_t launch_append(const AppendParams& p, hipStream_t s, bool write_through) {
   const size_t work = (size_t)p.R * p.L * (p.rec_bytes >> 4);
-  hipLaunchKernelGGL(append_kernel, dim3(grid_for(work, kCopyThreads, 1024)), dim3(kCopyThreads), 0, s, p);
+  if (write_through)
+    hipLaunchKernelGGL(append_kernel<true>, dim3(grid_for(work, kCopyThreads, 1024)), dim3(kCopyThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, dim3(grid_for(work, kCopyThreads, 1024)), dim3(kCopyThreads), 0, s, p);
   return hipGetLastError();
 }
 

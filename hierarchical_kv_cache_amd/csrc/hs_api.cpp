@@ -181,6 +181,7 @@ struct hs_ctx {
   uint8_t* ws = nullptr;
   std::vector<void*> pool;  // per request pinned region
   hipEvent_t ev_appended = nullptr, ev_backup_done = nullptr;
+  bool backup_pending = false;  // a backup-stream write-through may still read slot B
   std::vector<hipEvent_t> ev_plan, ev_plan_free, ev_layer;  // per anchor, per anchor, per layer
   std::vector<char> plan_free_pending;
   int replay_wgs = 32;
@@ -561,7 +562,6 @@ hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos,
   if ((st = check_handle(h))) return st;
   if (!(h->cfg.flags & HS_CFG_NEWEST_SLOT)) return fail(HS_ESTATE, "hs_append needs HS_CFG_NEWEST_SLOT");
   if (!d_new_kv || !d_new_pos) return fail(HS_EINVAL, "null new record or position");
-  if (compute == backup) return fail(HS_EINVAL, "write-through needs a backup stream distinct from compute");
   hipStream_t cs = (hipStream_t)compute, bs = (hipStream_t)backup;
   AppendParams p{};
   p.new_kv = (const uint8_t*)d_new_kv; p.new_pos = d_new_pos; p.newest = h->newest(); p.hot = h->hot;
@@ -569,14 +569,24 @@ hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos,
   p.L = h->cfg.num_layers; p.B = h->cfg.buffer_slots; p.rec_bytes = h->cfg.record_bytes;
   p.ctrl = h->ctrl(0); p.slot_pos = h->slot_pos(0); p.page_table = h->page_table(0); p.A = h->lay.A;
   p.group = h->cfg.layer_group;
-  // slot B may only be overwritten once the previous write-through has read it (and then every
-  // later fetch of the previous newest position finds its bytes on the host)
+  // Slot B may only be overwritten once the previous write-through has read it (and then every
+  // later fetch of the previous newest position finds its bytes on the host).
+  if (!backup || backup == compute) {
+    // One kernel on `compute` writes slot B and the host pool, ordered with the caller's later
+    // work by the stream itself.  A cross-stream event pair costs more GPU time per step than
+    // writing a few records to the host, so this is the mode for small appends.
+    if (h->backup_pending) HS_HIP(hipStreamWaitEvent(cs, h->ev_backup_done, 0));
+    h->backup_pending = false;
+    HS_HIP(launch_append(p, cs, true));
+    return HS_OK;
+  }
   HS_HIP(hipStreamWaitEvent(cs, h->ev_backup_done, 0));
-  HS_HIP(launch_append(p, cs));
+  HS_HIP(launch_append(p, cs, false));
   HS_HIP(hipEventRecord(h->ev_appended, cs));
   HS_HIP(hipStreamWaitEvent(bs, h->ev_appended, 0));
   HS_HIP(launch_backup(p, bs));
   HS_HIP(hipEventRecord(h->ev_backup_done, bs));
+  h->backup_pending = true;
   return HS_OK;
 }
 

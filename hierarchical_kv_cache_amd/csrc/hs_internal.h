@@ -313,7 +313,7 @@ size_t union_lds_bytes(int hash_bits);
 hipError_t set_union_lds_limit(size_t lds_bytes);
 constexpr int kUnionMaxEntries = 8192;  // rows * top_k of one speculative resolve
 hipError_t set_resolve_lds_limit(size_t lds_bytes);
-hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_append(const AppendParams& p, hipStream_t s, bool write_through);
 hipError_t launch_backup(const AppendParams& p, hipStream_t s);
 hipError_t launch_replay(const ReplayParams& p, int wgs, hipStream_t s, const KernelTiming* tm = nullptr);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);

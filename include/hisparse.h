@@ -193,11 +193,17 @@ hs_status hs_bind_resident(hs_handle h, const int32_t* d_block_table, int32_t pa
  * [KJ] §7.1).  Needs HS_CFG_NEWEST_SLOT.
  *   d_new_kv   device [R][L][record_bytes]: the new token's records
  *   d_new_pos  device [R] int32: its position (< max_positions)
- * On `compute`: waits for the previous write-through to finish reading slot B,
+ * Two streams (backup non-null and distinct from compute), the pages' layout:
+ * on `compute` waits for the previous write-through to finish reading slot B,
  * copies d_new_kv into slot B of every layer and makes d_new_pos the newest
- * position.  On `backup`: waits for that copy, then writes slot B to the host
+ * position; on `backup` waits for that copy, then writes slot B to the host
  * pool at d_new_pos.  A later hs_append on `compute` waits for this backup,
  * so any later resolve that fetches that position reads the written bytes.
+ * One stream (backup null or equal to compute): a single kernel on `compute`
+ * does both copies, so the stream orders it with every later call; it first
+ * waits for a two-stream write-through that may still be reading slot B.  On
+ * MI355X the cross-stream event pair costs about 18 us of GPU time per step,
+ * more than writing R x L records to the host, so small appends take this mode.
  */
 hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos, void* compute,
                     void* backup);

@@ -27,8 +27,11 @@ class Pair:
 
     def __init__(self, w: synth.Workload, steps: int | None = None, wgs: int = 0, all_hit=False,
                  oracle_host_copy: bool | None = None, compare_hot=True, resident: ResidentSpec | None = None,
-                 fp8: bool = False, rows: int = 1, fused_heads: int = 0):
+                 fp8: bool = False, rows: int = 1, fused_heads: int = 0, append_streams: str = "two"):
         self.w = w
+        # hs_append's write-through: "two" (backup stream and events) or "one" (one kernel on
+        # the compute stream); may be changed between steps
+        self.append_streams = append_streams
         self.steps = w.steps if steps is None else steps
         self.lmax = w.max_positions(self.steps)
         self.R, self.L, self.B, self.k, self.kb = w.R, w.L, w.B, w.k, w.kb
@@ -134,8 +137,8 @@ class Pair:
             recs = synth.records_at(w.R, w.L, [p] * w.R, rec_bytes=self.rec)
             d_new = torch.from_numpy(recs).to(self.dev)
             d_pos = torch.full((w.R,), p, dtype=torch.int32, device=self.dev)
-            hk.hs_append(self.h, d_new.data_ptr(), d_pos.data_ptr(), self.compute.cuda_stream,
-                         self.side.cuda_stream)
+            backup = self.side.cuda_stream if self.append_streams == "two" else self.compute.cuda_stream
+            hk.hs_append(self.h, d_new.data_ptr(), d_pos.data_ptr(), self.compute.cuda_stream, backup)
             for r in range(w.R):
                 for l in self.anchors:
                     self.caches[(r, l)].append(p, recs[r, l], self.ohost[r][l])

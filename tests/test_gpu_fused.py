@@ -178,11 +178,12 @@ def test_errors_give_nan_rows_and_leave_state(R, wgs):
         c.close()
 
 
-def test_short_requests_cross_into_the_normal_path():
+@pytest.mark.parametrize("streams", ["two", "one"])
+def test_short_requests_cross_into_the_normal_path(streams):
     """Short requests (slot = position) through the fused call, growing by write-through
-    appends past B."""
+    appends past B (on a backup stream, or in the append kernel on the compute stream)."""
     w = W["tiny"].scaled(R=2, ctx=200, B=256, k=64, forced_last=16, steps=80, append=True)
-    p = Pair(w, fused_heads=16)
+    p = Pair(w, fused_heads=16, append_streams=streams)
     try:
         for r in range(w.R):
             hk.hs_admit_short(p.h, r, w.ctx, p.compute.cuda_stream)

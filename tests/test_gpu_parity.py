@@ -86,16 +86,37 @@ def test_tiny_every_step(B, wgs):
     p.close()
 
 
-def test_long_with_write_through_scaled():
+@pytest.mark.parametrize("streams", ["two", "one"])
+def test_long_with_write_through_scaled(streams):
     """Long-request shape (k 2048, B 4096, one token appended and written through per step,
-    always selected) on 2 layers and a 16K context, state checked every step."""
+    always selected) on 2 layers and a 16K context, state checked every step; the
+    write-through on a backup stream or in the append kernel on the compute stream."""
     w = W["long"].scaled(L=2, ctx=16384, steps=12)
-    log("long scaled")
-    p = Pair(w)
+    log("long scaled, write-through on %s stream(s)" % streams)
+    p = Pair(w, append_streams=streams)
     for _ in range(w.steps):
         p.step_gpu_and_oracle()
         p.check_state()
     # the appended tokens are on the host, in the pinned pool the GPU wrote
+    for t in range(w.steps):
+        pos = w.ctx + t
+        for l in range(w.L):
+            assert np.array_equal(p.gpu.host_pool(0)[l, pos], synth.record(0, l, pos))
+    p.close()
+
+
+def test_write_through_modes_alternating():
+    """Write-through alternating between the backup stream and the one-kernel mode every step
+    (a one-stream append must wait for a backup that may still read slot B): state checked
+    every step, every appended record in the host pool at the end."""
+    w = W["long"].scaled(L=2, ctx=8192, steps=10)
+    log("write-through modes alternating")
+    p = Pair(w)
+    for t in range(w.steps):
+        p.append_streams = "one" if t % 2 else "two"
+        p.step_gpu_and_oracle()
+        p.check_state()
+    torch.cuda.synchronize()
     for t in range(w.steps):
         pos = w.ctx + t
         for l in range(w.L):
