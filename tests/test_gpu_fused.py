@@ -345,6 +345,68 @@ def test_graph_capture_replays_match_oracle():
         p.close()
 
 
+def test_graph_capture_with_write_through_on_the_compute_stream():
+    """hs_append without a backup stream (one kernel, no event) and hs_resolve_attn of every
+    layer captured once in a HIP graph that reads fixed input buffers, replayed for 6 decode
+    steps with eager input copies and unrelated eager work between replays; every replay
+    agrees with the oracle, and the written-through records reach the host pool."""
+    w = W["long"].scaled(R=2, L=2, ctx=16384, steps=6)
+    steps = w.steps
+    p = Pair(w, steps=steps)
+    try:
+        assert hk.hs_resolve_attn_wgs(p.h) > 0
+        dev = torch.device("cuda")
+        s = torch.cuda.Stream()
+        sel_buf = torch.empty_like(p.d_trace[0])
+        q_all = np.stack([synth.queries(w.R, w.L, t) for t in range(steps)])  # [t][R][L][16][576]
+        d_q_all = torch.from_numpy(q_all.view(np.int16)).to(dev).permute(0, 2, 1, 3, 4).contiguous()
+        q_buf = torch.empty_like(d_q_all[0])
+        recs_all = [synth.records_at(w.R, w.L, [w.ctx + t] * w.R) for t in range(steps)]
+        new_buf = torch.empty((w.R, w.L, synth.RECORD_BYTES), dtype=torch.uint8, device=dev)
+        pos_buf = torch.empty((w.R,), dtype=torch.int32, device=dev)
+        ctx = torch.empty((w.R,), dtype=torch.int32, device=dev)
+        out = torch.empty((w.L, w.R, 16, 512), dtype=torch.float32, device=dev)
+        stats = torch.zeros((w.L, w.R, 4), dtype=torch.int32, device=dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            hk.hs_append(p.h, new_buf.data_ptr(), pos_buf.data_ptr(), s.cuda_stream, 0)
+            for ai, l in enumerate(p.anchors):
+                hk.hs_resolve_attn(p.h, l, sel_buf[ai].data_ptr(), ctx.data_ptr(), p.d_out[ai].data_ptr(),
+                                   stats[ai].data_ptr(), 0, 0, q_buf[l].data_ptr(), 16, 512, out[l].data_ptr(),
+                                   SCALE, s.cuda_stream)
+        torch.cuda.synchronize()
+        for t in range(steps):
+            pos = w.ctx + t
+            sel_buf.copy_(p.d_trace[t])
+            q_buf.copy_(d_q_all[t])
+            new_buf.copy_(torch.from_numpy(recs_all[t]))
+            pos_buf.fill_(pos)
+            ctx.fill_(pos + 1)
+            noise = torch.randn(4096, device=dev).sum()  # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.isfinite(noise)
+            got, st, o = p.d_out.cpu().numpy(), stats.cpu().numpy(), out.cpu().numpy()
+            for ai, l in enumerate(p.anchors):
+                for r in range(w.R):
+                    p.caches[(r, l)].append(pos, recs_all[t][r, l], p.ohost[r][l])
+                    ref, hits, misses, _, _ = p.caches[(r, l)].resolve(p.trace[t, ai, r], pos + 1, p.ohost[r][l])
+                    assert np.array_equal(got[ai, r], ref), (t, l, r)
+                    assert tuple(st[ai, r, :3]) == (hits, misses, 0), (t, l, r)
+                    o_ref = oracle.attention.sparse_decode_attention(q_all[t, r, l], p.caches[(r, l)].hot, ref, SCALE)
+                    assert np.abs(o[l, r] - o_ref).max() <= 2e-3 * np.abs(o_ref).max(), (t, l, r)
+            p.t += 1
+            p.newest = pos
+        p.check_state()
+        for t in range(steps):
+            for r in range(w.R):
+                for l in range(w.L):
+                    assert np.array_equal(p.gpu.host_pool(r)[l, w.ctx + t], recs_all[t][r, l]), (t, r, l)
+    finally:
+        p.close()
+
+
 def test_several_tiles_with_resident_tier():
     """Eight requests (two tiles per fetch workgroup): resident rows, hot rows and misses
     across tile boundaries."""
