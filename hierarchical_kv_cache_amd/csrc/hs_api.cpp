@@ -101,8 +101,8 @@ Layout make_layout(const hs_config& c) {
   L.newest = take(R * sizeof(int32_t));
   L.host_base = take(R * sizeof(void*));
   L.attn_part = take(size_t(c.num_layers) * R * L.Spart * kPartStride * sizeof(float));
+  L.att_zero = take(size_t(c.record_bytes));  // a zero record: filler rows of FP8 tiles
   if (Sf) {  // the fused call's report, miss list and staging area (one set per handle)
-    L.att_zero = take(size_t(c.record_bytes));
     L.att_hdr = take(R * 4 * sizeof(uint32_t));
     L.att_mlist = take(R * k * 4 * sizeof(int32_t));
     L.att_stage = take(R * k * size_t(c.record_bytes));
@@ -646,6 +646,7 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
   p.chunk = (int)align_up((size_t)((h->cfg.top_k + p.S - 1) / p.S), 64);
   p.S = (h->cfg.top_k + p.chunk - 1) / p.chunk;  // no empty chunk
   p.rec_bytes = h->cfg.record_bytes; p.scale = scale; p.fp8 = fp8 ? 1 : 0;
+  p.zero = h->ws + h->lay.att_zero;
   HS_HIP(launch_attn(p, (hipStream_t)stream));
   return HS_OK;
 }

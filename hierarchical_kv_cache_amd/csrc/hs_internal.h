@@ -274,6 +274,7 @@ struct AttnParams {
   int32_t R, k, B, heads, value_dim, S, chunk, rec_bytes;
   float scale;
   int32_t fp8;               // records in the FP8 layout (HS_CFG_RECORD_FP8)
+  const uint8_t* zero;       // a zero record (the FP8 tiles' filler)
 };
 
 struct ExportParams {
