@@ -48,9 +48,9 @@ def test_tiny_one_chunk(B):
         p.close()
 
 
-@pytest.mark.parametrize("k,heads", [(100, 5), (1000, 16), (130, 1)])
+@pytest.mark.parametrize("k,heads", [(100, 5), (1000, 16), (130, 1), (65, 3)])
 def test_ragged_chunks(k, heads):
-    """Shares of 50, 62-63 and 43-44 entries; fewer than 16 heads."""
+    """Shares of 50, 62-63, 43-44 and 32-33 entries; fewer than 16 heads."""
     w = W["tiny"].scaled(k=k, B=max(128, k + 40), R=3, forced_last=min(16, k), steps=6)
     log("ragged k=%d heads=%d" % (k, heads))
     p = Pair(w, fused_heads=heads)

@@ -318,7 +318,8 @@ def _attn_check(p, step, layers, heads=16):
         slots = p.d_out[ai].cpu().numpy()
         for r in range(w.R):
             hot = p.caches[(r, l)].hot if l == a else p.ohot_shared[(r, l)]
-            ref = oracle.attention.sparse_decode_attention(q[r, l], hot, slots[r], SCALE)
+            att = oracle.attention.sparse_decode_attention_fp8 if p.fp8 else oracle.attention.sparse_decode_attention
+            ref = att(q[r, l], hot, slots[r], SCALE)
             err = np.abs(o[r] - ref).max() / np.abs(ref).max()
             worst = max(worst, err)
             assert err <= 2e-3, (r, l, err)
@@ -345,11 +346,13 @@ def test_attention_single_request_and_shared_layers():
     p.close()
 
 
-@pytest.mark.parametrize("k,heads", [(64, 16), (100, 5), (1000, 16)])
-def test_attention_ragged(k, heads):
-    """Entry counts that leave a ragged last tile, and fewer than 16 heads."""
+@pytest.mark.parametrize("k,heads,fp8", [(64, 16, False), (100, 5, False), (1000, 16, False), (65, 3, False),
+                                        (65, 3, True), (1000, 16, True)])
+def test_attention_ragged(k, heads, fp8):
+    """Entry counts that leave a ragged last tile (k = 65: a chunk with one entry), and fewer
+    than 16 heads; bf16 and FP8 records."""
     w = W["tiny"].scaled(k=k, B=max(128, k + 40), R=3, forced_last=min(16, k))
-    p = Pair(w, steps=3)
+    p = Pair(w, steps=3, fp8=fp8)
     for t in range(3):
         p.step_gpu_and_oracle()
         _attn_check(p, t, [0], heads=heads)
