@@ -285,11 +285,17 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
   }
   const bool bvec = (p.B % E) == 0;
-  int32_t spa[E], spb[E];
+  // Both halves of the slot map are read here, before the launch counter says which one is
+  // current, so they share the first round trip.  With 8 or more slots per thread they
+  // would hold too many registers until the publish, which then reads the current half.
+  constexpr bool kEarlySlotMap = E < 8;
+  int32_t spa[kEarlySlotMap ? E : 1], spb[kEarlySlotMap ? E : 1];
   Run16<E> lra, lrb;
-  if (g == 0) {  // only workgroup 0 publishes, and only it needs the slot map
-    load_run32<E>(p.slot_pos + ((size_t)r * 2 + 0) * p.B, p.B, e0, bvec, spa, -1);
-    load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
+  if constexpr (kEarlySlotMap) {
+    if (g == 0) {  // only workgroup 0 publishes, and only it needs the slot map
+      load_run32<E>(p.slot_pos + ((size_t)r * 2 + 0) * p.B, p.B, e0, bvec, spa, -1);
+      load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
+    }
   }
   load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, e0, bvec, lra, 0);
   load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, e0, bvec, lrb, 0);
@@ -634,7 +640,8 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   if (g == 0) {
     int32_t spo[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) spo[j] = h1 ? spb[j] : spa[j];
+    for (int j = 0; j < E; ++j) spo[j] = kEarlySlotMap ? (h1 ? spb[j] : spa[j]) : -1;
+    if constexpr (!kEarlySlotMap) load_run32<E>(p.slot_pos + ((size_t)r * 2 + (h1 ? 1 : 0)) * p.B, p.B, e0, bvec, spo, -1);
     int32_t* sp_new = p.slot_pos + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.B;
     // filled victims, then hits, each by slot index, after the untouched evictables
     int16_t fo[E];
