@@ -141,7 +141,7 @@ __device__ __forceinline__ void acc_init(AttnAcc& a) {
 
 // The [64][4] block scales of an FP8 tile in the attention scratch.
 __device__ __forceinline__ float* tile_scales8(unsigned char* scratch) {
-  return (float*)(scratch + 2 * 4 * 16 * 4 + 4 * 2 * 2 * 16 * 32 * 2);
+  return (float*)(scratch + kAttnScratch);
 }
 
 // V operand of v_mfma_f32_16x16x32_bf16 by two transposed LDS reads (ds_read_b64_tr_b16).
@@ -189,9 +189,9 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
   constexpr int NB = F8 ? 4 : 1;      // P variants (one per scale block)
   float* smax = (float*)scratch;      // [4 token blocks][16 heads]
   float* ssum = smax + 64;            // [4][16]
-  float* spart = ssum + 64;           // step 1 -> 2: [4 key ranges][4 token blocks][16 heads][16 tokens]
-  uint16_t* phi = (uint16_t*)spart;   // step 3 -> 4 (the partials are dead): [NB][2 token blocks][16 heads][32]
-  uint16_t* plo = phi + NB * 2 * 16 * 32;
+  float* spart = ssum + 64;           // step 1 -> 2: [4 key ranges][4 token blocks][16 heads][kSpartRow]
+  uint16_t* phi = (uint16_t*)spart;   // step 3 -> 4 (the partials are dead): [NB][2 token blocks][16 heads][kPRow]
+  uint16_t* plo = phi + NB * 2 * 16 * kPRow;
   const float* scl8 = F8 ? tile_scales8(scratch) : nullptr;  // [64][4]
   const int tl = 16 * tb + col;       // this lane's token in steps 2-3
   {
@@ -214,16 +214,17 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
 #pragma unroll
     for (int j = 0; j < 4; ++j) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], ka[j], sa, 0, 0, 0);
     const float sc = F8 ? scl8[4 * tl + kp] : 1.0f;
-    float* sp = spart + (kp * 4 + tb) * 256 + col;
+    float* sp = spart + (kp * 4 + tb) * 16 * kSpartRow + col;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sp[(4 * qd + i) * 16] = F8 ? sa[i] * sc + sr[i] : sa[i] + sr[i];
+    for (int i = 0; i < 4; ++i) sp[(4 * qd + i) * kSpartRow] = F8 ? sa[i] * sc + sr[i] : sa[i] + sr[i];
   }
   __syncthreads();
   const int hk = 4 * qd + kp;
   float sv;
   {
-    const float* sp = spart + tb * 256 + hk * 16 + col;
-    const float s = sp[0] + sp[1024] + sp[2048] + sp[3072];
+    constexpr int KR = 4 * 16 * kSpartRow;  // one key range's partials
+    const float* sp = spart + (tb * 16 + hk) * kSpartRow + col;
+    const float s = sp[0] + sp[KR] + sp[2 * KR] + sp[3 * KR];
     sv = tl < n_tok ? s * sl2 : -INFINITY;
     const float mx = row16_max(sv);
     if (col == 0) smax[tb * 16 + hk] = mx;
@@ -248,8 +249,8 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
       // a masked row (p = 0) takes no scale: a filler's scale must not turn 0 into NaN
       const float pw = F8 ? (pv != 0.0f ? pv * scl8[4 * tl + b] : 0.0f) : pv;
       const uint16_t hi = f32_to_bf16_rne(pw);
-      phi[((b * 2 + bk) * 16 + hk) * 32 + kk] = hi;
-      plo[((b * 2 + bk) * 16 + hk) * 32 + kk] = f32_to_bf16_rne(pw - __uint_as_float((uint32_t)hi << 16));
+      phi[((b * 2 + bk) * 16 + hk) * kPRow + kk] = hi;
+      plo[((b * 2 + bk) * 16 + hk) * kPRow + kk] = f32_to_bf16_rne(pw - __uint_as_float((uint32_t)hi << 16));
     }
   }
   __syncthreads();
@@ -265,8 +266,8 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int pb = F8 ? (w >> 2) * 2 + b : b;  // wave w's channels lie in scale block w / 4
-    const bf16x8 ahi = *(const bf16x8*)&phi[(pb * 16 + col) * 32 + qd * 8];
-    const bf16x8 alo = *(const bf16x8*)&plo[(pb * 16 + col) * 32 + qd * 8];
+    const bf16x8 ahi = *(const bf16x8*)&phi[(pb * 16 + col) * kPRow + qd * 8];
+    const bf16x8 alo = *(const bf16x8*)&plo[(pb * 16 + col) * kPRow + qd * 8];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const bf16x8 vv = v_operand(tile, 32 * b, 32 * w + 16 * c, lane);

@@ -118,13 +118,16 @@ constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (29
                                      // 36 banks apart modulo 64, so the 16 rows of a QK^T operand
                                      // read, and the 4 rows of a 16-lane group of a V read, spread
 constexpr int kQStride = 1168;       // LDS stride of a query row (16-byte aligned, off the bank period)
-// maxima and sums, then the partial scores (4 key ranges x 4 token blocks x 16 x 16 fp32),
-// whose space P hi and lo reuse
-constexpr int kAttnScratch = 2 * 4 * 16 * 4 + 4 * 4 * 16 * 16 * 4;
+// maxima and sums, then the partial scores (4 key ranges x 4 token blocks x 16 heads, rows of
+// 16 tokens padded to kSpartRow fp32), whose space P hi and lo reuse (rows of 32 tokens padded
+// to kPRow bf16): the padding puts the four lane quarters of an access on distinct banks
+constexpr int kSpartRow = 20, kPRow = 40;
+constexpr int kAttnSpart = 4 * 4 * 16 * kSpartRow * 4;
+constexpr int kAttnScratch = 2 * 4 * 16 * 4 + kAttnSpart;
 // FP8 records: the same (P hi and lo per 128-channel scale block fill the partials' space
 // exactly), and the tile's block scales
-constexpr int kAttnScratch8 = 2 * 4 * 16 * 4 + 4 * 2 * 2 * 16 * 32 * 2 + kTileRows * 4 * 4;
-static_assert(4 * 2 * 2 * 16 * 32 * 2 == 4 * 4 * 16 * 16 * 4, "FP8 P fills the partial scores' space");
+constexpr int kAttnScratch8 = kAttnScratch + kTileRows * 4 * 4;
+static_assert(4 * 2 * 2 * 16 * kPRow * 2 == kAttnSpart, "FP8 P fills the partial scores' space");
 constexpr int kF8RecordBytes = 656;  // 512 E4M3 codes, 4 float32 block scales, 64 bf16
 struct FusedLds {
   size_t tile, qs, arow, asrc, scratch, total;
