@@ -146,18 +146,28 @@ __device__ __forceinline__ float* tile_scales8(unsigned char* scratch) {
 
 // V operand of v_mfma_f32_16x16x32_bf16 by two transposed LDS reads (ds_read_b64_tr_b16).
 // Within each 16-lane group the instruction hands output lane L, element j, element L % 4 of
-// the 8 bytes that lane 4 j + L / 4 addressed.  So lane s of group g addresses row
-// row0 + 8 g + s / 4 (second read: 4 rows further) at channel c0 + 4 (s % 4), and lane L ends
-// up with channel c0 + L of rows row0 + 8 g + 0..7: the operand's k index is the token's
-// place in its 32-token block.
+// the 8 bytes that lane 4 j + L / 4 addressed.  So lane s of group g addresses token row
+// v_row(g, s / 4) (second read: v_row(g, 4 + s / 4)) at channel c0 + 4 (s % 4), and lane L ends
+// up with channel c0 + L of rows v_row(g, 0..7): k index 8 g + j is token v_row(g, j) of the
+// 32-token block.  v_row gives each group's read the rows 2 a + p (one parity p, a step of 2),
+// whose 32-byte pieces start on distinct 8-bank blocks at the 1168-byte row stride, also for
+// the two groups an access serves together.
+__device__ __forceinline__ int v_row(int g, int j) {
+  return 2 * (4 * (g & 1) + (j & 3)) + 16 * (j >> 2) + (g >> 1);
+}
+// its inverse: the k index of token t (0..31) of a block
+__device__ __forceinline__ int v_k(int t) {
+  const int a = t >> 1;
+  return 8 * (((t & 1) << 1) | ((a >> 2) & 1)) + (((a >> 3) << 2) | (a & 3));
+}
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ bf16x8 v_operand(const unsigned char* tile, int row0, int c0, int lane) {
   const int g = lane >> 4, s = lane & 15;
-  const unsigned char* a = tile + (row0 + 8 * g + (s >> 2)) * kTileStride + 2 * (c0 + 4 * (s & 3));
+  const unsigned char* a = tile + (row0 + v_row(g, s >> 2)) * kTileStride + 2 * (c0 + 4 * (s & 3));
   typedef s16x4 __attribute__((address_space(3))) * lds_s16x4;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a + 4 * kTileStride));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a + 16 * kTileStride));
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -243,7 +253,7 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
     const float pv = exp2f(sv - mk);
     const float l = row16_sum(pv);
     if (col == 0) ssum[tb * 16 + hk] = l;
-    const int bk = tl >> 5, kk = tl & 31;
+    const int bk = tl >> 5, kk = v_k(tl & 31);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       // a masked row (p = 0) takes no scale: a filler's scale must not turn 0 into NaN
