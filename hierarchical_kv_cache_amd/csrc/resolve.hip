@@ -900,11 +900,12 @@ __global__ void __launch_bounds__(NT) resolve_f8_kernel(ResolveParams p) {
 // speculative decoding): rows that select the same position share one slot, so the
 // rows are resolved as one list, their union in first-reference order (row by row,
 // list order within a row).  One workgroup per request:
-//   - every entry finds or inserts its position in an LDS hash (compare-and-swap
-//     linear probing; one bucket per distinct position);
-//   - row by row, each entry ORs its row's bit into its bucket's mask: a bit already
-//     set is a duplicate inside the row, a lower bit means an earlier row selected the
-//     position first;
+//   - every entry finds or inserts its position in an LDS hash (one bucket per distinct
+//     position: a plain store into the home bucket, then compare-and-swap linear probing
+//     for the entries whose home bucket holds another position);
+//   - each entry ORs its row's bit into its bucket's mask: a bit already set is a
+//     duplicate inside the row; once every row's bits are in, an entry whose mask has no
+//     lower bit is its position's first reference;
 //   - the first references are ranked in list order (ballot + mbcnt scan); the rank is
 //     the position's index in the union, stored in the bucket for the other entries.
 constexpr int EU = kUnionMaxEntries / NT;  // entries per thread
@@ -945,13 +946,29 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
   }
   if (tid == 0) sh[0] = 0;
   __syncthreads();
+  // Insertion in two steps, as in RESOLVE's hash: every entry stores its position into its
+  // home bucket with a plain store; after a barrier an entry that reads its own position back
+  // has its bucket (entries of one position share it), and the others probe from the next
+  // bucket with compare-and-swap, which only fills empty buckets.  LDS atomics serialise lane
+  // by lane, so this keeps most of the table build off them.
   int32_t bkt[EU];
+  uint32_t hh[EU];
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
+    hh[j] = pos[j] >= 0 ? hash_pos(pos[j], p.hash_bits) : 0u;
+    if (pos[j] >= 0) key[hh[j]] = pos[j];
+  }
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
     bkt[j] = -1;
     if (pos[j] < 0) continue;
-    uint32_t h = hash_pos(pos[j], p.hash_bits);
-    for (int probe = 0; probe < H; ++probe) {  // the table is at most half full: this ends
+    if (key[hh[j]] == pos[j]) {
+      bkt[j] = (int32_t)hh[j];
+      continue;
+    }
+    uint32_t h = (hh[j] + 1) & hmask;
+    for (int probe = 1; probe < H; ++probe) {  // the table is at most half full: this ends
       const int32_t prev = atomicCAS(&key[h], -1, pos[j]);
       if (prev == -1 || prev == pos[j]) {
         bkt[j] = (int32_t)h;
@@ -960,18 +977,27 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
       h = (h + 1) & hmask;
     }
   }
+  // Each entry ORs its row's bit into its bucket's mask (one pass: the old mask already shows
+  // a duplicate inside the row); after the barrier an entry is its position's first reference
+  // when no earlier row's bit is set.  A duplicate is never the first reference.
+  uint32_t dupb = 0;
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
+    if (bkt[j] < 0) continue;
+    const int q = (i0 + j) / p.k;
+    const uint32_t old = atomicOr(&meta[bkt[j]], 1u << q);
+    if (old & (1u << q)) {
+      err |= HS_ERR_DUP;
+      dupb |= 1u << j;
+    }
+  }
   __syncthreads();
   uint32_t first = 0;
-  for (int q = 0; q < p.rows; ++q) {
 #pragma unroll
-    for (int j = 0; j < EU; ++j) {
-      const int f = i0 + j;
-      if (bkt[j] < 0 || f / p.k != q) continue;
-      const uint32_t old = atomicOr(&meta[bkt[j]], 1u << q);
-      if (old & (1u << q)) err |= HS_ERR_DUP;
-      else if ((old & ((1u << q) - 1u)) == 0) first |= 1u << j;
-    }
-    __syncthreads();
+  for (int j = 0; j < EU; ++j) {
+    if (bkt[j] < 0 || ((dupb >> j) & 1u)) continue;
+    const int q = (i0 + j) / p.k;
+    if ((meta[bkt[j]] & ((1u << q) - 1u)) == 0) first |= 1u << j;
   }
   if (err) atomicOr((unsigned*)&sh[0], err);
   int ru, rz, nu, tz;
