@@ -277,13 +277,19 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   const int f_lo = kr * gf / nf;
   const int f_n = kr * (gf + 1) / nf - f_lo;
   const int wid = tid >> 6, lane = tid & 63;
+  // With 8 or more list entries per thread these share arrays would stay live through
+  // stages 1-2 beside the stage arrays: then they are read just before the fetch stage.
+  constexpr bool kEarlyShare = KE < 8;
   int32_t fraw[KE];
+  auto share_sel = [&]() {
 #pragma unroll
-  for (int q = 0; q < KE; ++q) {
-    const int e = q * NT + lane * NW + wid;
-    const int i = f_lo + e;
-    fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
-  }
+    for (int q = 0; q < KE; ++q) {
+      const int e = q * NT + lane * NW + wid;
+      const int i = f_lo + e;
+      fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
+    }
+  };
+  if constexpr (kEarlyShare) share_sel();
   const bool bvec = (p.B % E) == 0;
   // Both halves of the slot map are read here, before the launch counter says which one is
   // current, so they share the first round trip.  With 8 or more slots per thread they
@@ -364,18 +370,21 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
   int32_t fpos[KE], fres[KE];
   uint64_t fpt[KE];
+  auto share_pt = [&]() {
 #pragma unroll
-  for (int q = 0; q < KE; ++q) {
-    const int e = q * NT + lane * NW + wid;
-    const int i = f_lo + e;
-    int64_t pos64 = -1;
-    if (fetcher && e < f_n)
-      pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
-    const bool ok = pos64 >= 0 && pos64 < ctx;
-    fpos[q] = ok ? (int32_t)pos64 : -1;
-    fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
-    fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
-  }
+    for (int q = 0; q < KE; ++q) {
+      const int e = q * NT + lane * NW + wid;
+      const int i = f_lo + e;
+      int64_t pos64 = -1;
+      if (fetcher && e < f_n)
+        pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
+      const bool ok = pos64 >= 0 && pos64 < ctx;
+      fpos[q] = ok ? (int32_t)pos64 : -1;
+      fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
+      fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
+    }
+  };
+  if constexpr (kEarlyShare) share_pt();
   {
     u32x4* h4 = (u32x4*)htab;
     const u32x4 e4 = {~0u, ~0u, ~0u, ~0u};
@@ -538,6 +547,10 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     }
   }
   // ---- stage 4, first part: per-wave lists of the page-table misses, host loads issued ----
+  if constexpr (!kEarlyShare) {
+    share_sel();
+    share_pt();
+  }
   int32_t* wpos = (int32_t*)(smem + Ly.wpos) + wid * Ly.wcap;  // this wave's misses: position
   int16_t* widx = (int16_t*)(smem + Ly.widx) + wid * Ly.wcap;  // and list index
   const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
