@@ -54,3 +54,25 @@ def test_committed_profiles_name_existing_sources():
             if line.startswith("source_files:"):
                 for src in line.split(":", 1)[1].split():
                     assert os.path.exists(os.path.join(ROOT, src)), (n, src)
+
+
+def test_precomputed_addresses_match_the_views():
+    """bench.addr(t, i, ...) is the address of the view t[i, ...], for every buffer shape and
+    index the timed loop uses (contiguous and permuted-then-contiguous tensors, leading
+    indices only)."""
+    import torch
+    steps, L, R, k = 5, 3, 2, 7
+    tensors = [
+        torch.zeros((steps, L, R, k), dtype=torch.int32),          # selections
+        torch.zeros((steps, L, R, 4), dtype=torch.int32),          # stats
+        torch.zeros((steps, R), dtype=torch.int32),                # context lengths
+        torch.zeros((steps, R, L, 9), dtype=torch.uint8),          # new records
+        torch.zeros((steps, R, L, 3, 5), dtype=torch.int16).permute(0, 2, 1, 3, 4).contiguous(),  # queries
+        torch.zeros((L, R, 3, 6), dtype=torch.float32),            # outputs
+    ]
+    for t in tensors:
+        for i in range(t.shape[0]):
+            assert bench.addr(t, i) == t[i].data_ptr()
+            if t.dim() > 2:
+                for j in range(t.shape[1]):
+                    assert bench.addr(t, i, j) == t[i, j].data_ptr()
