@@ -88,29 +88,79 @@ __device__ __forceinline__ void tile_load8(u32x4 (&tv)[kTU8], const uint64_t* as
     }
   }
 }
+// chunk c of FP8 record `row` into the tile (codes as bf16, scales apart, bf16 values after)
+__device__ __forceinline__ void store8_chunk(const u32x4& v, unsigned char* tile, float* scales, int row, int c) {
+  if (c < 32) {
+    uint32_t wv[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], false);
+      const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], true);
+      wv[2 * q] = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xFFFF0000u);
+      wv[2 * q + 1] = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xFFFF0000u);
+    }
+    u32x4* d = (u32x4*)(tile + (size_t)row * kTileStride + 32 * c);
+    d[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    d[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+  } else if (c == 32) {
+    *(u32x4*)(scales + 4 * row) = v;
+  } else {
+    *(u32x4*)(tile + (size_t)row * kTileStride + 1024 + 16 * (c - 33)) = v;
+  }
+}
 __device__ __forceinline__ void tile_store8(const u32x4 (&tv)[kTU8], unsigned char* tile, float* scales) {
 #pragma unroll
   for (int u = 0; u < kTU8; ++u) {
     const int f = threadIdx.x + u * kAT;
     if (f < kF8TileChunks) {
       const int row = f / kF8RowChunks, c = f - row * kF8RowChunks;
-      if (c < 32) {
-        uint32_t wv[8];
+      store8_chunk(tv[u], tile, scales, row, c);
+    }
+  }
+}
+
+// A wave's own rows of a tile, for callers whose lanes l0 .. l0 + 3 of wave w resolved the
+// tile's rows 16 i + w (i = 0..3): each lane holds the record address of its row (rsrc),
+// the wave reads those four into scalar registers, and lane l takes chunks q = l + 64 u of
+// the four rows (row i = q / RC).  No workgroup barrier stands between a wave's address
+// lookups and its loads.  RC: 16-byte chunks per record.
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+template <typename T>
+__device__ __forceinline__ T pick4(const T (&x)[4], int i) {
+  return i == 0 ? x[0] : i == 1 ? x[1] : i == 2 ? x[2] : x[3];
+}
+template <int RC, int U>
+__device__ __forceinline__ void wave_rows_load(u32x4 (&tv)[U], uint64_t rsrc, int l0) {
+  static_assert(4 * RC <= 64 * U, "a wave's four rows fit its lanes' chunks");
+  const int lane = threadIdx.x & 63;
+  uint64_t b[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)tv[u][q], false);
-          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)tv[u][q], true);
-          wv[2 * q] = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xFFFF0000u);
-          wv[2 * q + 1] = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xFFFF0000u);
-        }
-        u32x4* d = (u32x4*)(tile + (size_t)row * kTileStride + 32 * c);
-        d[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
-        d[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
-      } else if (c == 32) {
-        *(u32x4*)(scales + 4 * row) = tv[u];
-      } else {
-        *(u32x4*)(tile + (size_t)row * kTileStride + 1024 + 16 * (c - 33)) = tv[u];
-      }
+  for (int i = 0; i < 4; ++i) b[i] = readlane64(rsrc, l0 + i);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = lane + 64 * u;
+    if (q < 4 * RC) {
+      const int i = q / RC, c = q - i * RC;
+      tv[u] = load_host16((const uint8_t*)pick4(b, i) + 16 * c);
+    }
+  }
+}
+// the wave's loaded chunks into the LDS tile (F8: FP8 records, as tile_store8)
+template <int RC, int U, bool F8>
+__device__ __forceinline__ void wave_rows_store(const u32x4 (&tv)[U], unsigned char* tile, float* scales) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = lane + 64 * u;
+    if (q < 4 * RC) {
+      const int i = q / RC, c = q - i * RC;
+      const int row = 16 * i + w;
+      if constexpr (F8) store8_chunk(tv[u], tile, scales, row, c);
+      else *(u32x4*)(tile + (size_t)row * kTileStride + 16 * c) = tv[u];
     }
   }
 }

@@ -108,9 +108,9 @@ int resolve_elems_per_thread(int k, int B);
 
 // Fused RESOLVE + attention.  Workgroup 0 uses the resolve carve-up; each fetch workgroup
 // (a share of <= 64 T selected records, attended one 64-row tile at a time) the record tile,
-// the query rows, per share entry the record's address and the miss's list index, and the
-// attention scratch (scores' maxima and sums, P).  The dynamic LDS of the launch is the
-// larger of the two.
+// the query rows and the attention scratch (scores' maxima and sums, partial scores, P); each
+// share entry's record address and miss index stay in the register of the lane that resolved
+// it.  The dynamic LDS of the launch is the larger of the two.
 constexpr int kTileRows = 64;        // records per tile
 constexpr int kFusedMaxTiles = 16;   // tiles per fetch workgroup (share entries <= 1024 threads)
 constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (292 words, 8-byte
@@ -130,15 +130,14 @@ constexpr int kAttnScratch8 = kAttnScratch + kTileRows * 4 * 4;
 static_assert(4 * 2 * 2 * 16 * kPRow * 2 == kAttnSpart, "FP8 P fills the partial scores' space");
 constexpr int kF8RecordBytes = 656;  // 512 E4M3 codes, 4 float32 block scales, 64 bf16
 struct FusedLds {
-  size_t tile, qs, arow, asrc, scratch, total;
+  size_t tile, qs, scratch, total;
 };
 __host__ __device__ inline FusedLds fused_lds(int k, int B, int hash_bits, int G, int T, bool f8 = false) {
   FusedLds F;
   F.tile = 0;
   F.qs = F.tile + size_t(kTileRows) * kTileStride;
-  F.asrc = F.qs + 16 * size_t(kQStride);
-  F.arow = F.asrc + 8 * size_t(kTileRows) * T;
-  F.scratch = F.arow + 4 * size_t(kTileRows) * T;
+  F.scratch = F.qs + 16 * size_t(kQStride);
+  (void)T;  // the tiles of a share no longer add LDS
   const size_t fetch = align_up(F.scratch + (f8 ? kAttnScratch8 : kAttnScratch), 16);
   const size_t resolve = resolve_lds(k, B, hash_bits, G).total;
   F.total = fetch > resolve ? fetch : resolve;

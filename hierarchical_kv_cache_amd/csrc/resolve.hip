@@ -802,8 +802,6 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
   const FusedLds F = fused_lds(p.k, p.B, p.hash_bits, p.G, p.att_tiles, F8);
   unsigned char* tile = smem + F.tile;
   unsigned char* qs = smem + F.qs;
-  int32_t* arow = (int32_t*)(smem + F.arow);   // list index of the miss of each share entry, -1 otherwise
-  uint64_t* asrc = (uint64_t*)(smem + F.asrc);  // record address of each share entry
   const uint8_t* filler = F8 ? p.att_zero : (const uint8_t*)(p.q + (size_t)r * p.heads * kAttnDk);
   // the request's scalars, read before the branches below so that they share the selection's
   // round trip and only the page-table entries come after it
@@ -814,8 +812,11 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
   const uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   u32x4 qv[kQU];
   q_load(qv, p.q, r, p.heads);
-  // share entry e = lane * NW + wid: the first tile's 64 rows on lanes 0..3 of every wave
+  // share entry e = lane * NW + wid: tile t's rows 16 i + wid (i = 0..3) on lanes 4 t + i of
+  // wave wid, so each wave loads the rows its own lanes resolved (wave_rows_load)
   const int e = lane * NW + wid;
+  uint64_t my_src = (uint64_t)filler;  // this lane's row: record address, and the list index of a miss
+  int32_t my_mi = -1;
   if (e < nt * kTileRows) {
     const uint8_t* src = filler;
     int32_t mi = -1;
@@ -844,38 +845,34 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
         }
       }
     }
-    asrc[e] = (uint64_t)src;
-    arow[e] = mi;
+    my_src = (uint64_t)src;
+    my_mi = mi;
   }
-  q_store(qv, qs);
-  __syncthreads();
+  q_store(qv, qs);  // read after the barrier that precedes the first tile's attention
   const float sl2 = p.att_scale * 1.4426950408889634f;
   constexpr int TU = F8 ? kTU8 : kTU;
   constexpr int RC = F8 ? kF8RowChunks : kRowChunks;
-  constexpr int TC = F8 ? kF8TileChunks : kTileChunks;
   u32x4 tv[TU];
-  if constexpr (F8) tile_load8(tv, asrc);
-  else tile_load(tv, asrc);
+  wave_rows_load<RC, TU>(tv, my_src, 0);
   AttnAcc acc;
   acc_init(acc);
   for (int t = 0; t < nt; ++t) {
     if (t > 0) __syncthreads();  // the previous tile's readers are done with the tile and P
     // the missed records, as loaded, to the staging area
+    int32_t mi4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mi4[i] = __builtin_amdgcn_readlane(my_mi, 4 * t + i);
 #pragma unroll
     for (int u = 0; u < TU; ++u) {
-      const int f = tid + u * NT;
-      if (f < TC) {
-        const int row = f / RC, c = f - row * RC;
-        const int a = arow[t * kTileRows + row];
+      const int q = lane + 64 * u;
+      if (q < 4 * RC) {
+        const int i = q / RC, c = q - i * RC;
+        const int a = pick4(mi4, i);
         if (a >= 0) *((u32x4*)(p.att_stage + ((size_t)r * p.k + a) * (size_t)p.rec_bytes) + c) = tv[u];
       }
     }
-    if constexpr (F8) tile_store8(tv, tile, tile_scales8(smem + F.scratch));
-    else tile_store(tv, tile);
-    if (t + 1 < nt) {
-      if constexpr (F8) tile_load8(tv, asrc + (t + 1) * kTileRows);
-      else tile_load(tv, asrc + (t + 1) * kTileRows);
-    }
+    wave_rows_store<RC, TU, F8>(tv, tile, tile_scales8(smem + F.scratch));
+    if (t + 1 < nt) wave_rows_load<RC, TU>(tv, my_src, 4 * (t + 1));
     __syncthreads();
     attend_tile<F8>(tile, qs, smem + F.scratch, min(kTileRows, f_n - t * kTileRows), sl2, acc);
   }
