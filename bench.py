@@ -102,7 +102,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each (request, layer) "
+        print("bench.py measures one GPU: the library has no multi-GPU path (each (request, layer) "
               "cache is independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
