@@ -145,7 +145,7 @@ def main():
                            .view(np.int16)).to(dev)  # [steps][R][L][H][576]
     d_q = d_q.permute(0, 2, 1, 3, 4).contiguous()   # [steps][L][R][H][576]
     d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
-    d_stats = torch.zeros((n_steps, L, R, 4), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n_steps, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     d_out = torch.empty((L, R, heads, 512), dtype=torch.float32, device=dev)
     compute = torch.cuda.current_stream()
     backup = torch.cuda.Stream()
@@ -168,7 +168,7 @@ def main():
         stream with its event pair).  ev_row: events recorded on the launch stream around
         each layer's attention call (separate calls only)."""
         h = c.h
-        hk.hs_append(h, a_kv[t], a_pos[t], cs, bs if backup_stream else cs)
+        hk.hs_writeback(h, a_kv[t], a_pos[t], cs, bs if backup_stream else cs)
         sel, q, stats, ctx = a_sel[t], a_q[t], a_stats[t], a_ctx[t]
         for l in range(L):
             if fused:
@@ -444,7 +444,7 @@ def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, reside
         hk.hs_bind_resident(cache.h, d_table.data_ptr(), phys.shape[1], P, d_pool.data_ptr(), rows)
     d_trace = torch.from_numpy(np.ascontiguousarray(trace[:steps])).to(dev)
     d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
-    d_stats = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((steps, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream()
     ctx = torch.from_numpy((w.ctx + 1 + np.arange(steps))[:, None].repeat(R, 1).astype(np.int32)).to(dev) \
         if w.append else torch.full((steps, R), w.ctx, dtype=torch.int32, device=dev)
@@ -458,7 +458,7 @@ def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, reside
         if resident is not None:
             d_table.copy_(d_tables[t])
         if w.append:
-            hk.hs_append(cache.h, new_kv[t].data_ptr(), new_pos[t].data_ptr(), s.cuda_stream, s.cuda_stream)
+            hk.hs_writeback(cache.h, new_kv[t].data_ptr(), new_pos[t].data_ptr(), s.cuda_stream, s.cuda_stream)
         for l in range(L):
             hk.hs_resolve(cache.h, l, d_trace[t, l].data_ptr(), ctx[t].data_ptr(), d_slots.data_ptr(),
                           d_stats[t, l].data_ptr(), 0, flags, s.cuda_stream)
@@ -537,7 +537,7 @@ def measure_replay(torch, hk, synth, dev, steps=12):
     d_tr = torch.from_numpy(tr).to(dev)
     d_ctx = torch.full((R,), wl.ctx, dtype=torch.int32, device=dev)
     d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
-    d_stats = torch.zeros((steps, R, 4), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((steps, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     cs = torch.cuda.current_stream()
     ps = torch.cuda.Stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -634,12 +634,12 @@ def measure_fp8(torch, hk, synth, dev, steps=40, warmup=8):
     d_q = torch.from_numpy(np.stack([synth.queries(R, L, t, heads=w.heads) for t in range(n)])
                            .view(np.int16)).to(dev).permute(0, 2, 1, 3, 4).contiguous()
     d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
-    d_stats = torch.zeros((n, L, R, 4), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     d_out = torch.empty((L, R, w.heads, 512), dtype=torch.float32, device=dev)
     cs = torch.cuda.current_stream().cuda_stream
 
     def step(c, t, fused):
-        hk.hs_append(c.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), cs, cs)
+        hk.hs_writeback(c.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), cs, cs)
         for l in range(L):
             if fused:
                 hk.hs_resolve_attn(c.h, l, d_trace[t, l].data_ptr(), d_ctx[t].data_ptr(), d_slots[l].data_ptr(),
@@ -697,12 +697,12 @@ def measure_rows(torch, hk, synth, dev, rows=4, steps=24):
     d_pos = torch.from_numpy(np.repeat(pos[:, None], R, axis=1).astype(np.int32)).to(dev)
     d_ctx = torch.from_numpy((pos[:, None] + 1).repeat(R, axis=1).astype(np.int32)).to(dev)
     d_out = torch.empty((R, rows, k), dtype=torch.int32, device=dev)
-    d_stats = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((steps, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream()
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
            for _ in range(steps)]
     for t in range(steps):
-        hk.hs_append(cache.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), s.cuda_stream, s.cuda_stream)
+        hk.hs_writeback(cache.h, d_new[t].data_ptr(), d_pos[t].data_ptr(), s.cuda_stream, s.cuda_stream)
         for l in range(L):
             evs[t][l][0].record(s)
             hk.hs_resolve_rows(cache.h, l, rows, d_tr[t, l].data_ptr(), d_ctx[t].data_ptr(), d_out.data_ptr(),
@@ -734,7 +734,7 @@ def measure_short(torch, hk, synth, dev, steps=64):
     d_tr = torch.from_numpy(tr).to(dev)
     d_ctx = torch.full((R,), ctx, dtype=torch.int32, device=dev)
     d_out = torch.empty((R, k), dtype=torch.int32, device=dev)
-    d_st = torch.zeros((steps, L, R, 4), dtype=torch.int32, device=dev)
+    d_st = torch.zeros((steps, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream()
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
            for _ in range(steps)]
@@ -773,7 +773,7 @@ def measure_batched(torch, hk, synth, dev, layers=4, steps=16, warmup=4):
     d_q = d_q.permute(0, 2, 1, 3, 4).contiguous()  # [steps][L][R][16][576]
     d_ctx = torch.full((R,), w.ctx, dtype=torch.int32, device=dev)
     d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
-    d_stats = torch.zeros((n, L, R, 4), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     d_out = torch.empty((L, R, 16, 512), dtype=torch.float32, device=dev)
     cs = torch.cuda.current_stream().cuda_stream
 
@@ -825,7 +825,7 @@ def measure_shared_step(torch, hk, synth, dev, steps=12, warmup=4):
     d_q = d_q.permute(0, 2, 1, 3, 4).contiguous()  # [n][L][R][16][576]
     d_ctx = torch.full((R,), w.ctx, dtype=torch.int32, device=dev)
     d_slots = torch.empty((R, k), dtype=torch.int32, device=dev)
-    d_stats = torch.zeros((n, R, 4), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     d_out = torch.empty((L, R, 16, 512), dtype=torch.float32, device=dev)
     cs = torch.cuda.current_stream()
     ps = torch.cuda.Stream()

@@ -45,12 +45,16 @@ class hs_config(ctypes.Structure):
 
 
 HS_STATS_DTYPE = np.dtype([("hits", np.uint32), ("misses", np.uint32), ("error", np.uint32),
-                           ("resident", np.uint32)])
+                           ("resident", np.uint32), ("bytes_fetched", np.uint64)])
+# hs_stats in int32 words (24 bytes): hits, misses, error, resident, then bytes_fetched as two
+# words (low, high)
+HS_STATS_WORDS = 6
+assert HS_STATS_DTYPE.itemsize == 4 * HS_STATS_WORDS
 
 # every symbol include/hisparse.h declares
 EXPORTS = (
     "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_resolve_rows", "hs_bind_resident",
-    "hs_append",
+    "hs_writeback",
     "hs_prefetch_shared",
     "hs_wait_layer", "hs_sparse_attn", "hs_resolve_attn", "hs_resolve_attn_wgs", "hs_export_state", "hs_page_table", "hs_plan", "hs_admit_short",
     "hs_reset_request",
@@ -79,13 +83,13 @@ def _load():
         "hs_resolve": (i32, [vp, i32, vp, vp, vp, vp, vp, u32, vp]),
         "hs_resolve_rows": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, u32, vp]),
         "hs_bind_resident": (i32, [vp, vp, i32, i32, vp, i64]),
-        "hs_append": (i32, [vp, vp, vp, vp, vp]),
+        "hs_writeback": (i32, [vp, vp, vp, vp, vp]),
         "hs_prefetch_shared": (i32, [vp, i32, vp, vp]),
         "hs_wait_layer": (i32, [vp, i32, vp]),
         "hs_sparse_attn": (i32, [vp, i32, vp, i32, i32, vp, vp, ctypes.c_float, vp, vp]),
         "hs_resolve_attn": (i32, [vp, i32, vp, vp, vp, vp, vp, u32, vp, i32, i32, vp, ctypes.c_float, vp]),
         "hs_resolve_attn_wgs": (i32, [vp]),
-        "hs_export_state": (i32, [vp, i32, vp, vp, vp, vp]),
+        "hs_export_state": (i32, [vp, i32, vp, vp, vp, vp, vp]),
         "hs_page_table": (vp, [vp, i32]),
         "hs_plan": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp)]),
         "hs_admit_short": (i32, [vp, i32, i32, vp]),
@@ -148,8 +152,8 @@ def hs_bind_resident(h, d_block_table, pages_per_request, page_tokens, d_residen
                                  resident_rows))
 
 
-def hs_append(h, d_new_kv, d_new_pos, compute, backup):
-    _check(_lib.hs_append(h, d_new_kv, d_new_pos, compute or None, backup or None))
+def hs_writeback(h, d_new_kv, d_new_pos, compute, backup):
+    _check(_lib.hs_writeback(h, d_new_kv, d_new_pos, compute or None, backup or None))
 
 
 def hs_prefetch_shared(h, anchor_layer, compute, prefetch):
@@ -175,8 +179,9 @@ def hs_resolve_attn_wgs(h) -> int:
     return _lib.hs_resolve_attn_wgs(h)
 
 
-def hs_export_state(h, layer, d_slot_pos, d_lru, d_newest, stream):
-    _check(_lib.hs_export_state(h, layer, d_slot_pos or None, d_lru or None, d_newest or None, stream or None))
+def hs_export_state(h, layer, d_slot_pos, d_lru, d_page_table, d_newest, stream):
+    _check(_lib.hs_export_state(h, layer, d_slot_pos or None, d_lru or None, d_page_table or None, d_newest or None,
+                                stream or None))
 
 
 def hs_page_table(h, layer) -> int:

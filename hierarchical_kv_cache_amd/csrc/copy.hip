@@ -263,6 +263,14 @@ __global__ void __launch_bounds__(kCopyThreads) export_kernel(ExportParams p) {
     if (p.out_slot_pos) p.out_slot_pos[(size_t)r * p.B + s] = p.slot_pos[((size_t)r * 2 + cur) * p.B + s];
     if (p.out_lru) p.out_lru[(size_t)r * p.B + s] = p.lru[((size_t)r * 2 + cur) * p.Bpad + s];
   }
+  // the page table's slots (the low half of each entry; the generation tag is bookkeeping)
+  if (p.out_page_table) {
+    const uint64_t* pt = p.page_table + (size_t)r * p.max_positions;
+    int32_t* o = p.out_page_table + (size_t)r * p.max_positions;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < p.max_positions;
+         q += (int64_t)gridDim.x * blockDim.x)
+      o[q] = (int32_t)(uint32_t)pt[q];
+  }
   if (p.out_newest && blockIdx.x == 0 && threadIdx.x == 0) p.out_newest[r] = p.newest ? p.newest[r] : -1;
 }
 

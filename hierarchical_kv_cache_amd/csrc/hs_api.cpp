@@ -557,10 +557,10 @@ hs_status hs_bind_resident(hs_handle h, const int32_t* d_block_table, int32_t pa
   return HS_OK;
 }
 
-hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos, void* compute, void* backup) {
+hs_status hs_writeback(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos, void* compute, void* backup) {
   hs_status st;
   if ((st = check_handle(h))) return st;
-  if (!(h->cfg.flags & HS_CFG_NEWEST_SLOT)) return fail(HS_ESTATE, "hs_append needs HS_CFG_NEWEST_SLOT");
+  if (!(h->cfg.flags & HS_CFG_NEWEST_SLOT)) return fail(HS_ESTATE, "hs_writeback needs HS_CFG_NEWEST_SLOT");
   if (!d_new_kv || !d_new_pos) return fail(HS_EINVAL, "null new record or position");
   hipStream_t cs = (hipStream_t)compute, bs = (hipStream_t)backup;
   AppendParams p{};
@@ -651,8 +651,8 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
   return HS_OK;
 }
 
-hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32_t* d_lru, int32_t* d_newest,
-                          void* stream) {
+hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32_t* d_lru, int32_t* d_page_table,
+                          int32_t* d_newest, void* stream) {
   hs_status st;
   if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
   if (!h->is_anchor(layer)) return fail(HS_ESTATE, "layer %d has no metadata of its own", layer);
@@ -660,7 +660,8 @@ hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32
   ExportParams p{};
   p.ctrl = h->ctrl(a); p.slot_pos = h->slot_pos(a); p.lru = h->lru(a);
   p.newest = (h->cfg.flags & HS_CFG_NEWEST_SLOT) ? h->newest() : nullptr;
-  p.out_slot_pos = d_slot_pos; p.out_lru = d_lru; p.out_newest = d_newest;
+  p.page_table = h->page_table(a); p.max_positions = h->cfg.max_positions;
+  p.out_slot_pos = d_slot_pos; p.out_lru = d_lru; p.out_page_table = d_page_table; p.out_newest = d_newest;
   p.R = h->cfg.num_requests; p.B = h->cfg.buffer_slots; p.Bpad = h->lay.Bpad;
   HS_HIP(launch_export(p, (hipStream_t)stream));
   return HS_OK;

@@ -284,9 +284,12 @@ struct ExportParams {
   const int32_t* slot_pos;
   const int16_t* lru;
   const int32_t* newest;
+  const uint64_t* page_table;  // [R][max_positions]
   int32_t* out_slot_pos;
   int32_t* out_lru;
+  int32_t* out_page_table;
   int32_t* out_newest;
+  int64_t max_positions;
   int32_t R, B, Bpad;
 };
 

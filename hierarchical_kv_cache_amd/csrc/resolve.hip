@@ -230,7 +230,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     if (g == 0) {
       for (int i = tid; i < p.k; i += NT) p.out[(size_t)r * p.k + i] = -1;
       if (tid == 0 && p.stats) {
-        hs_stats st = {0u, 0u, pre_err, 0u};
+        hs_stats st = {0u, 0u, pre_err, 0u, 0ull};
         p.stats[r] = st;
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
@@ -341,7 +341,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
         }
       }
       if (tid == 0 && p.stats) {
-        hs_stats st = {bad ? 0u : (uint32_t)kr, 0u, bad ? (uint32_t)HS_ERR_RANGE : 0u, 0u};
+        hs_stats st = {bad ? 0u : (uint32_t)kr, 0u, bad ? (uint32_t)HS_ERR_RANGE : 0u, 0u, 0ull};
         p.stats[r] = st;
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
@@ -439,7 +439,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
           }
         }
         if (tid == 0 && p.stats) {
-          hs_stats st = {0u, 0u, 0u, (uint32_t)kr};
+          hs_stats st = {0u, 0u, 0u, (uint32_t)kr, 0ull};
           p.stats[r] = st;
         }
         if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
@@ -598,7 +598,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     if (g == 0) {
       for (int i = tid; i < p.k; i += NT) p.out[(size_t)r * p.k + i] = -1;
       if (tid == 0 && p.stats) {
-        hs_stats st = {0u, 0u, err, 0u};
+        hs_stats st = {0u, 0u, err, 0u, 0ull};
         p.stats[r] = st;
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
@@ -729,7 +729,8 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
       if (cls[j] >= 0) outr[i0 + j] = cls[j];
     if (tid == 0) {
       if (p.stats) {
-        hs_stats st = {(uint32_t)(kr - m - nres), (uint32_t)m, (uint32_t)sh[3], (uint32_t)nres};
+        hs_stats st = {(uint32_t)(kr - m - nres), (uint32_t)m, (uint32_t)sh[3], (uint32_t)nres,
+                        io ? (uint64_t)m * (uint64_t)p.rec_bytes : 0ull};
         p.stats[r] = st;
       }
       if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;

@@ -86,17 +86,28 @@ typedef struct {
                               n * top_k <= 8192 and buffer_slots >= n * top_k */
 } hs_config;
 
-/* Per-request result of one hs_resolve call (device memory, overwritten per call). */
+/* Per-request result of one hs_resolve call (device memory, overwritten per call; 24 bytes,
+ * 8-byte aligned).  The counts are the pages' hit / miss statistics of the resolve ([GC] §3.3,
+ * §3.5: every selected position is a hit or a miss; [GC] §6.5 adds the resident level). */
 typedef struct {
-  uint32_t hits;     /* selected tokens found in the hot slots (newest slot included) */
-  uint32_t misses;   /* selected tokens fetched from host (record_bytes each) */
-  uint32_t error;    /* HS_ERR_* bits; when set, nothing of this request changed and its
-                        slots_out row is -1 */
-  uint32_t resident; /* selected tokens served by the resident tier (hs_bind_resident);
-                        hits + misses + resident = top_k */
+  uint32_t hits;          /* selected tokens found in the hot slots (newest slot included) */
+  uint32_t misses;        /* selected tokens fetched from host (record_bytes each) */
+  uint32_t error;         /* HS_ERR_* bits; when set, nothing of this request changed and its
+                             slots_out row is -1 */
+  uint32_t resident;      /* selected tokens served by the resident tier (hs_bind_resident);
+                             hits + misses + resident = top_k */
+  uint64_t bytes_fetched; /* record bytes this call copied from the host pool into the hot
+                             slots: misses * record_bytes (0 with HS_SKIP_IO, which moves none) */
 } hs_stats;
 
-/* Bytes of device workspace hs_create needs for cfg (0 when cfg is invalid). */
+/*
+ * Bytes of device workspace hs_create needs for cfg (0 when cfg is invalid; hs_last_error says
+ * why).  The workspace holds what the pages keep resident on the GPU beside the hot buffer
+ * ([GC] §3.2: the page table and the LRU metadata of every (request, layer); §5.3: admission
+ * reserves each request's slots and metadata before it is scheduled): per anchor layer the slot
+ * map and LRU order (two halves each), the page table, the miss plan ([GC] §3.6), and the
+ * attention partials and staging of the fused call.  Deterministic in cfg; no allocation.
+ */
 size_t hs_workspace_bytes(const hs_config* cfg);
 
 /*
@@ -190,14 +201,16 @@ hs_status hs_bind_resident(hs_handle h, const int32_t* d_block_table, int32_t pa
 
 /*
  * Write-through of one new token per request, for every layer ([GC] §3.4, §5.4;
- * [KJ] §7.1).  Needs HS_CFG_NEWEST_SLOT.
+ * [KJ] §7.1): the new token's KV goes into the reserved newest slot, so the newest position is
+ * always on the device, and a backup copy goes to the host pool, ordered by events so that a
+ * later fetch of that position reads complete bytes.  Needs HS_CFG_NEWEST_SLOT.
  *   d_new_kv   device [R][L][record_bytes]: the new token's records
  *   d_new_pos  device [R] int32: its position (< max_positions)
  * Two streams (backup non-null and distinct from compute), the pages' layout:
  * on `compute` waits for the previous write-through to finish reading slot B,
  * copies d_new_kv into slot B of every layer and makes d_new_pos the newest
  * position; on `backup` waits for that copy, then writes slot B to the host
- * pool at d_new_pos.  A later hs_append on `compute` waits for this backup,
+ * pool at d_new_pos.  A later hs_writeback on `compute` waits for this backup,
  * so any later resolve that fetches that position reads the written bytes.
  * One stream (backup null or equal to compute): a single kernel on `compute`
  * does both copies, so the stream orders it with every later call; it first
@@ -205,8 +218,8 @@ hs_status hs_bind_resident(hs_handle h, const int32_t* d_block_table, int32_t pa
  * MI355X the cross-stream event pair costs about 18 us of GPU time per step,
  * more than writing R x L records to the host, so small appends take this mode.
  */
-hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos, void* compute,
-                    void* backup);
+hs_status hs_writeback(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos, void* compute,
+                       void* backup);
 
 /*
  * Exact layer-wise prefetch ([GC] §3.6, §5.6): `prefetch` waits for the
@@ -217,7 +230,14 @@ hs_status hs_append(hs_handle h, const void* d_new_kv, const int32_t* d_new_pos,
  */
 hs_status hs_prefetch_shared(hs_handle h, int32_t anchor_layer, void* compute, void* prefetch);
 
-/* `stream` waits until the prefetch of shared layer `layer` is done. */
+/*
+ * `stream` waits until the prefetch of shared layer `layer` is done ([GC] §5.6: a shared-index
+ * layer waits for its own prefetch event, then reuses the anchor's slot table; [GC] §3.6).
+ * The wait is on the event that hs_prefetch_shared recorded for this layer, so a shared layer
+ * never waits for the replay of a later one.  An anchor layer (or a layer of a group that has
+ * not been prefetched) returns HS_OK with nothing enqueued: an anchor's records are in place
+ * when its own resolve ends on the caller's stream.  HS_EINVAL for a bad handle or layer.
+ */
 hs_status hs_wait_layer(hs_handle h, int32_t layer, void* stream);
 
 /*
@@ -266,11 +286,20 @@ hs_status hs_resolve_attn(hs_handle h, int32_t layer, const int32_t* d_sel, cons
                           const void* d_q, int32_t heads, int32_t value_dim, float* d_out, float scale,
                           void* stream);
 
-/* Copies the current metadata of an anchor layer into caller buffers (device):
- * d_slot_pos [R][B] position held by each slot (-1 empty), d_lru [R][B] slots
- * from least to most recent, d_newest [R] newest position (-1 none).  Any may be NULL. */
+/*
+ * Copies the current metadata of an anchor layer into caller buffers (device), the state the
+ * pages keep resident on the GPU ([GC] §3.2: the page table maps each logical position to a
+ * slot or to the host-only sentinel; the LRU metadata orders the slots):
+ *   d_slot_pos   [R][B] int32 position held by each slot (-1 empty)
+ *   d_lru        [R][B] int32 slots from least to most recent
+ *   d_page_table [R][max_positions] int32 slot holding each position (-1: host only; the
+ *                newest token's slot B is not entered, [GC] §3.4)
+ *   d_newest     [R] int32 newest position (-1 none)
+ * Any may be NULL.  Asynchronous on `stream`; HS_ESTATE for a shared layer (it has no
+ * metadata of its own).
+ */
 hs_status hs_export_state(hs_handle h, int32_t layer, int32_t* d_slot_pos, int32_t* d_lru,
-                          int32_t* d_newest, void* stream);
+                          int32_t* d_page_table, int32_t* d_newest, void* stream);
 
 /* Device address of an anchor layer's page table, uint64 [R][max_positions]: the low 32 bits of
  * an entry are the slot holding the position (int32, -1 = host only), the high 32 bits a
@@ -289,11 +318,11 @@ hs_status hs_plan(hs_handle h, int32_t layer, const int32_t** d_plan, const uint
  * table (never used, so oldest first), and marks the request short:
  *   - while its context length is <= B, hs_resolve / hs_resolve_rows return slot = position for
  *     every entry and change no LRU state (positions are range-checked only);
- *   - hs_append also writes a new token at position p < B into slot p (in order);
+ *   - hs_writeback also writes a new token at position p < B into slot p (in order);
  *   - once the context exceeds B (with the B slots full of positions 0 .. B-1) the normal path
  *     takes over from that state.
  * The request must be in the admission state (after hs_create or hs_reset_request) and grow
- * only by hs_append.  ctx_len <= buffer_slots.  Asynchronous on `stream`.
+ * only by hs_writeback.  ctx_len <= buffer_slots.  Asynchronous on `stream`.
  */
 hs_status hs_admit_short(hs_handle h, int32_t request, int32_t ctx_len, void* stream);
 
@@ -301,7 +330,14 @@ hs_status hs_admit_short(hs_handle h, int32_t request, int32_t ctx_len, void* st
  * slots empty, all positions host-only, LRU in slot order, no newest token, not short). */
 hs_status hs_reset_request(hs_handle h, int32_t request, void* stream);
 
-/* Waits for the library's own events, frees the pinned pool and the handle. */
+/*
+ * Teardown of the cache, after the pages' release order ([GC] §5.4: a finishing request first
+ * waits for the pending backup, then its host and device slots are released): waits for the
+ * library's own work still in flight (a backup-stream write-through into the host pool, shared-
+ * layer replays reading it), then frees the pinned pool, the events and the handle.  The hot
+ * buffer and the workspace are the caller's and stay allocated.  NULL is a no-op.  On a HIP
+ * error while waiting the handle is still freed and HS_EHIP is returned.
+ */
 hs_status hs_destroy(hs_handle h);
 
 /* Message of the last failing call on this thread ("" if none). */

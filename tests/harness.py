@@ -29,7 +29,7 @@ class Pair:
                  oracle_host_copy: bool | None = None, compare_hot=True, resident: ResidentSpec | None = None,
                  fp8: bool = False, rows: int = 1, fused_heads: int = 0, append_streams: str = "two"):
         self.w = w
-        # hs_append's write-through: "two" (backup stream and events) or "one" (one kernel on
+        # hs_writeback's write-through: "two" (backup stream and events) or "one" (one kernel on
         # the compute stream); may be changed between steps
         self.append_streams = append_streams
         self.steps = w.steps if steps is None else steps
@@ -86,7 +86,7 @@ class Pair:
         self.d_trace = torch.from_numpy(tr).to(self.dev)
         out_shape = (len(self.anchors), w.R, rows, w.k) if rows > 1 else (len(self.anchors), w.R, w.k)
         self.d_out = torch.empty(out_shape, dtype=torch.int32, device=self.dev)
-        self.d_stats = torch.zeros((w.R, 4), dtype=torch.int32, device=self.dev)
+        self.d_stats = torch.zeros((w.R, hk.HS_STATS_WORDS), dtype=torch.int32, device=self.dev)
         self.t = 0
         self.newest = None
         self.resident = resident
@@ -138,7 +138,7 @@ class Pair:
             d_new = torch.from_numpy(recs).to(self.dev)
             d_pos = torch.full((w.R,), p, dtype=torch.int32, device=self.dev)
             backup = self.side.cuda_stream if self.append_streams == "two" else self.compute.cuda_stream
-            hk.hs_append(self.h, d_new.data_ptr(), d_pos.data_ptr(), self.compute.cuda_stream, backup)
+            hk.hs_writeback(self.h, d_new.data_ptr(), d_pos.data_ptr(), self.compute.cuda_stream, backup)
             for r in range(w.R):
                 for l in self.anchors:
                     self.caches[(r, l)].append(p, recs[r, l], self.ohost[r][l])
@@ -202,6 +202,9 @@ class Pair:
                 if check:
                     assert stats[r, 0] == res[1] and stats[r, 1] == res[2] and stats[r, 2] == 0 \
                         and stats[r, 3] == res[5], (t, r, l, stats[r], res[1], res[2], res[5])
+                    fetched = int(stats[r, 4].astype(np.uint32)) | (int(stats[r, 5].astype(np.uint32)) << 32)
+                    want = 0 if flags & hk.HS_SKIP_IO else res[2] * self.rec
+                    assert fetched == want, ("bytes_fetched", t, r, l, fetched, want)
             if check:
                 got = self.d_out[ai].cpu().numpy()
                 for r in range(nr):
@@ -243,15 +246,19 @@ class Pair:
             sp = torch.empty((w.R, w.B), dtype=torch.int32, device=self.dev)
             lru = torch.empty((w.R, w.B), dtype=torch.int32, device=self.dev)
             nw = torch.empty((w.R,), dtype=torch.int32, device=self.dev)
-            hk.hs_export_state(self.h, l, sp.data_ptr(), lru.data_ptr(), nw.data_ptr(), self.compute.cuda_stream)
+            ptx = torch.empty((w.R, self.lmax), dtype=torch.int32, device=self.dev) if page_table else None
+            hk.hs_export_state(self.h, l, sp.data_ptr(), lru.data_ptr(), ptx.data_ptr() if page_table else 0,
+                               nw.data_ptr(), self.compute.cuda_stream)
             torch.cuda.synchronize()
             sp, lru, nw = sp.cpu().numpy(), lru.cpu().numpy(), nw.cpu().numpy()
             if page_table:
+                # the exported slots, and the raw 64-bit table's low halves, are the same
+                pt = ptx.cpu().numpy()
                 pt_addr = hk.hs_page_table(self.h, l)
-                pt = torch.empty((w.R, self.lmax), dtype=torch.int64, device=self.dev)
+                raw = torch.empty((w.R, self.lmax), dtype=torch.int64, device=self.dev)
                 torch.cuda.synchronize()
-                _copy_dev(pt_addr, pt)
-                pt = page_table_slots(pt.cpu().numpy())
+                _copy_dev(pt_addr, raw)
+                assert np.array_equal(page_table_slots(raw.cpu().numpy()), pt), ("page table export", l)
             for r in requests:
                 st = self.caches[(r, l)].export()
                 assert np.array_equal(sp[r], st["slot_pos"]), ("slot_pos", r, l)

@@ -64,7 +64,7 @@ def test_precomputed_addresses_match_the_views():
     steps, L, R, k = 5, 3, 2, 7
     tensors = [
         torch.zeros((steps, L, R, k), dtype=torch.int32),          # selections
-        torch.zeros((steps, L, R, 4), dtype=torch.int32),          # stats
+        torch.zeros((steps, L, R, 6), dtype=torch.int32),            # stats
         torch.zeros((steps, R), dtype=torch.int32),                # context lengths
         torch.zeros((steps, R, L, 9), dtype=torch.uint8),          # new records
         torch.zeros((steps, R, L, 3, 5), dtype=torch.int16).permute(0, 2, 1, 3, 4).contiguous(),  # queries

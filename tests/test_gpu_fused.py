@@ -147,7 +147,7 @@ def test_errors_give_nan_rows_and_leave_state(R, wgs):
         caches = [oracle.Cache(B, lmax, 1152) for _ in range(R)]
         dev = torch.device("cuda")
         out = torch.empty((R, k), dtype=torch.int32, device=dev)
-        st = torch.zeros((R, 4), dtype=torch.int32, device=dev)
+        st = torch.zeros((R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
         att = torch.empty((R, 16, 512), dtype=torch.float32, device=dev)
         d_ctx = torch.full((R,), ctx, dtype=torch.int32, device=dev)
         rng = np.random.default_rng(3)
@@ -318,7 +318,7 @@ def test_graph_capture_replays_match_oracle():
         q_buf = torch.empty_like(d_q_all[0])
         ctx = torch.full((w.R,), w.ctx, dtype=torch.int32, device=dev)
         out = torch.empty((w.L, w.R, 16, 512), dtype=torch.float32, device=dev)
-        stats = torch.zeros((w.L, w.R, 4), dtype=torch.int32, device=dev)
+        stats = torch.zeros((w.L, w.R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             for ai, l in enumerate(p.anchors):
@@ -349,7 +349,7 @@ def test_graph_capture_replays_match_oracle():
 
 
 def test_graph_capture_with_write_through_on_the_compute_stream():
-    """hs_append without a backup stream (one kernel, no event) and hs_resolve_attn of every
+    """hs_writeback without a backup stream (one kernel, no event) and hs_resolve_attn of every
     layer captured once in a HIP graph that reads fixed input buffers, replayed for 6 decode
     steps with eager input copies and unrelated eager work between replays; every replay
     agrees with the oracle, and the written-through records reach the host pool."""
@@ -369,10 +369,10 @@ def test_graph_capture_with_write_through_on_the_compute_stream():
         pos_buf = torch.empty((w.R,), dtype=torch.int32, device=dev)
         ctx = torch.empty((w.R,), dtype=torch.int32, device=dev)
         out = torch.empty((w.L, w.R, 16, 512), dtype=torch.float32, device=dev)
-        stats = torch.zeros((w.L, w.R, 4), dtype=torch.int32, device=dev)
+        stats = torch.zeros((w.L, w.R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            hk.hs_append(p.h, new_buf.data_ptr(), pos_buf.data_ptr(), s.cuda_stream, 0)
+            hk.hs_writeback(p.h, new_buf.data_ptr(), pos_buf.data_ptr(), s.cuda_stream, 0)
             for ai, l in enumerate(p.anchors):
                 hk.hs_resolve_attn(p.h, l, sel_buf[ai].data_ptr(), ctx.data_ptr(), p.d_out[ai].data_ptr(),
                                    stats[ai].data_ptr(), 0, 0, q_buf[l].data_ptr(), 16, 512, out[l].data_ptr(),

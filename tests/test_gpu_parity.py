@@ -38,7 +38,7 @@ def test_example_a_through_the_c_abi(golden):
     synth.fill_request(c.host_pool_address(0), 0, 1, 64, newest)
     dev = torch.device("cuda")
     out = torch.empty((1, 4), dtype=torch.int32, device=dev)
-    st = torch.zeros((1, 4), dtype=torch.int32, device=dev)
+    st = torch.zeros((1, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     side = torch.cuda.Stream()
 
     def resolve(sel, ctx):
@@ -52,13 +52,13 @@ def test_example_a_through_the_c_abi(golden):
     resolve(toks[4:], newest)
     rec = torch.from_numpy(synth.records_at(1, 1, [newest])).to(dev)
     pos = torch.tensor([newest], dtype=torch.int32, device=dev)
-    hk.hs_append(c.h, rec.data_ptr(), pos.data_ptr(), 0, side.cuda_stream)
+    hk.hs_writeback(c.h, rec.data_ptr(), pos.data_ptr(), 0, side.cuda_stream)
     slots, stats = resolve([int(x) for x in g["selection"]], newest + 1)
     assert slots == [int(x) for x in g["expect_slots"]]
     assert stats[:3] == [int(g["expect_hits"][0]), int(g["expect_misses"][0]), 0]
     lru = torch.empty((1, B), dtype=torch.int32, device=dev)
     sp = torch.empty((1, B), dtype=torch.int32, device=dev)
-    hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0)
+    hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0, 0)
     torch.cuda.synchronize()
     assert lru.cpu().numpy()[0].tolist() == [int(x) for x in g["expect_lru"]]
     assert sp.cpu().numpy()[0].tolist() == [25, 11, 12, 13, 14, 15, 16, 17]
@@ -207,13 +207,13 @@ def test_bad_selections_set_error_and_change_nothing():
     dev = torch.device("cuda")
     c = _single()
     out = torch.empty((2, 8), dtype=torch.int32, device=dev)
-    st = torch.zeros((2, 4), dtype=torch.int32, device=dev)
+    st = torch.zeros((2, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     ctx = torch.tensor([200, 200], dtype=torch.int32, device=dev)
     good = torch.tensor([list(range(8)), list(range(50, 58))], dtype=torch.int32, device=dev)
     hk.hs_resolve(c.h, 0, good.data_ptr(), ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0, 0)
     sp0 = torch.empty((2, 16), dtype=torch.int32, device=dev)
     lru0 = torch.empty((2, 16), dtype=torch.int32, device=dev)
-    hk.hs_export_state(c.h, 0, sp0.data_ptr(), lru0.data_ptr(), 0, 0)
+    hk.hs_export_state(c.h, 0, sp0.data_ptr(), lru0.data_ptr(), 0, 0, 0)
     bad = torch.tensor([[1, 2, 3, 4, 5, 6, 7, 3], [50, 51, 52, 53, 54, 55, 56, 250]], dtype=torch.int32,
                        device=dev)
     hk.hs_resolve(c.h, 0, bad.data_ptr(), ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0, 0)
@@ -223,7 +223,7 @@ def test_bad_selections_set_error_and_change_nothing():
     assert (out.cpu().numpy() == -1).all()
     sp1 = torch.empty_like(sp0)
     lru1 = torch.empty_like(lru0)
-    hk.hs_export_state(c.h, 0, sp1.data_ptr(), lru1.data_ptr(), 0, 0)
+    hk.hs_export_state(c.h, 0, sp1.data_ptr(), lru1.data_ptr(), 0, 0, 0)
     torch.cuda.synchronize()
     assert torch.equal(sp0, sp1) and torch.equal(lru0, lru1)
     # the oracle agrees on the error bits
@@ -248,7 +248,7 @@ def test_padded_requests_are_untouched():
     p.check_state(requests=[0, 1])
     # request 2 still has its state after step 1 only
     sp = torch.empty((3, w.B), dtype=torch.int32, device="cuda")
-    hk.hs_export_state(p.h, 0, sp.data_ptr(), 0, 0, 0)
+    hk.hs_export_state(p.h, 0, sp.data_ptr(), 0, 0, 0, 0)
     torch.cuda.synchronize()
     oc = oracle.Cache(w.B, p.lmax, 1152)
     oc.resolve(p.trace[0, 0, 2], w.ctx, p.ohost[2][0])
@@ -281,7 +281,7 @@ def test_reset_request_returns_to_admission_state():
     hk.hs_reset_request(p.h, 1, 0)
     sp = torch.empty((2, w.B), dtype=torch.int32, device="cuda")
     lru = torch.empty((2, w.B), dtype=torch.int32, device="cuda")
-    hk.hs_export_state(p.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0)
+    hk.hs_export_state(p.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0, 0)
     torch.cuda.synchronize()
     assert (sp.cpu().numpy()[1] == -1).all()
     assert lru.cpu().numpy()[1].tolist() == list(range(w.B))
@@ -371,7 +371,7 @@ def test_duplicates_in_many_patterns_then_valid_steps():
     caches = [oracle.Cache(B, lmax, 1152, newest_slot=True) for _ in range(R)]
     dev = torch.device("cuda")
     out = torch.empty((R, k), dtype=torch.int32, device=dev)
-    st = torch.zeros((R, 4), dtype=torch.int32, device=dev)
+    st = torch.zeros((R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     side = torch.cuda.Stream()
     rng = np.random.default_rng(5)
     ctx = 6000
@@ -382,7 +382,7 @@ def test_duplicates_in_many_patterns_then_valid_steps():
             recs = synth.records_at(R, 1, [newest] * R)
             d_new = torch.from_numpy(recs).to(dev)
             d_pos = torch.full((R,), newest, dtype=torch.int32, device=dev)
-            hk.hs_append(c.h, d_new.data_ptr(), d_pos.data_ptr(), 0, side.cuda_stream)
+            hk.hs_writeback(c.h, d_new.data_ptr(), d_pos.data_ptr(), 0, side.cuda_stream)
             for r in range(R):
                 caches[r].append(newest, recs[r, 0], None)
         d_sel = torch.from_numpy(np.stack(sels).astype(np.int32)).to(dev)
@@ -398,7 +398,7 @@ def test_duplicates_in_many_patterns_then_valid_steps():
                 assert (got[r] == -1).all()
         sp = torch.empty((R, B), dtype=torch.int32, device=dev)
         lru = torch.empty((R, B), dtype=torch.int32, device=dev)
-        hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0)
+        hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), 0, 0, 0)
         torch.cuda.synchronize()
         for r in range(R):
             ex = caches[r].export()
@@ -462,7 +462,7 @@ def test_graph_capture_replays_match_oracle():
     q_buf = torch.empty_like(d_q_all[0])
     ctx = torch.full((w.R,), w.ctx, dtype=torch.int32, device=dev)
     out = torch.empty((w.L, w.R, 16, 512), dtype=torch.float32, device=dev)
-    stats = torch.zeros((w.L, w.R, 4), dtype=torch.int32, device=dev)
+    stats = torch.zeros((w.L, w.R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for ai, l in enumerate(p.anchors):

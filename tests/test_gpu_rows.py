@@ -108,7 +108,7 @@ def test_duplicate_inside_a_row_is_an_error_repeats_across_rows_are_not():
     rng = np.random.default_rng(1)
     dev = torch.device("cuda")
     out = torch.empty((R, 3, k), dtype=torch.int32, device=dev)
-    st = torch.zeros((R, 4), dtype=torch.int32, device=dev)
+    st = torch.zeros((R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     ctx = torch.full((R,), lmax, dtype=torch.int32, device=dev)
     for step in range(6):
         sel = np.stack([np.stack([rng.choice(lmax, k, replace=False) for _ in range(3)]) for _ in range(R)]).astype(np.int32)

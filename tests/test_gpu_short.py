@@ -30,7 +30,7 @@ def export(c, R, B):
     sp = torch.empty((R, B), dtype=torch.int32, device="cuda")
     lru = torch.empty((R, B), dtype=torch.int32, device="cuda")
     nw = torch.empty((R,), dtype=torch.int32, device="cuda")
-    hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), nw.data_ptr(), 0)
+    hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), 0, nw.data_ptr(), 0)
     torch.cuda.synchronize()
     return sp.cpu().numpy(), lru.cpu().numpy(), nw.cpu().numpy()
 
@@ -59,7 +59,7 @@ def test_short_requests_cross_into_the_normal_path(rows):
     side = torch.cuda.Stream()
     shape = (R, rows, k) if rows > 1 else (R, k)
     out = torch.empty(shape, dtype=torch.int32, device=dev)
-    st = torch.zeros((R, 4), dtype=torch.int32, device=dev)
+    st = torch.zeros((R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     ctx = list(ctx0)
     fast = slow = 0
     for t in range(steps):
@@ -67,7 +67,7 @@ def test_short_requests_cross_into_the_normal_path(rows):
         recs = synth.records_at(R, L, pos)  # [R][L][rec]: request r's record at pos[r]
         d_new = torch.from_numpy(recs).to(dev)
         d_pos = torch.from_numpy(pos).to(dev)
-        hk.hs_append(c.h, d_new.data_ptr(), d_pos.data_ptr(), torch.cuda.current_stream().cuda_stream,
+        hk.hs_writeback(c.h, d_new.data_ptr(), d_pos.data_ptr(), torch.cuda.current_stream().cuda_stream,
                      side.cuda_stream)
         for r in range(R):
             caches[r].append(int(pos[r]), recs[r, 0], ohost[r][0])
@@ -123,7 +123,7 @@ def test_fast_path_range_error_and_reset():
     dev = torch.device("cuda")
     sel = np.stack([np.arange(k), np.arange(k) + 90]).astype(np.int32)  # request 1 reaches 105 >= 100
     out = torch.empty((R, k), dtype=torch.int32, device=dev)
-    st = torch.zeros((R, 4), dtype=torch.int32, device=dev)
+    st = torch.zeros((R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
     ctx = torch.full((R,), 100, dtype=torch.int32, device=dev)
     hk.hs_resolve(c.h, 0, torch.from_numpy(sel).to(dev).data_ptr(), ctx.data_ptr(), out.data_ptr(), st.data_ptr(),
                   0, 0, 0)

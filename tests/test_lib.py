@@ -56,3 +56,49 @@ def test_capacity_closed_form():
     assert round(100 * w.B / w.ctx, 1) == 3.1 and w.ctx // w.B == 32
     assert w.hot_bytes() == w.R * w.L * (w.B + 1) * 1152
     assert synth.WORKLOADS["capacity"].host_bytes() == 4 * 4 * 1048576 * 1152
+
+
+# The per-layer boundary the hot path is specified by: create, resolve, write-through of the
+# new token, shared-layer prefetch, the layer wait, the attention consumer, state export,
+# teardown.
+CONTRACT = ("hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_writeback",
+            "hs_prefetch_shared", "hs_wait_layer", "hs_sparse_attn", "hs_export_state", "hs_destroy",
+            "hs_last_error")
+
+
+def declarations():
+    """(name, the comment block right above the declaration) for every function declared."""
+    text = open(os.path.join(ROOT, "include", "hisparse.h")).read()
+    out = []
+    for m in re.finditer(r"(/\*(?:(?!\*/).)*\*/)\s*\n(?:[a-z_0-9 ]+\*?\s*)(hs_[a-z_0-9]+)\s*\(", text, flags=re.S):
+        out.append((m.group(2), m.group(1)))
+    return out
+
+
+def test_contract_names_are_exported():
+    lib = ctypes.CDLL(hk.LIB_PATH)
+    for name in CONTRACT:
+        assert name in hk.EXPORTS and hasattr(lib, name), name
+    assert not hasattr(lib, "hs_append"), "the write-through entry has one name, hs_writeback"
+
+
+def test_stats_layout():
+    """hs_stats: hits, misses, error, resident (uint32), then bytes_fetched (uint64)."""
+    assert hk.HS_STATS_DTYPE.itemsize == 24
+    assert hk.HS_STATS_DTYPE.fields["bytes_fetched"][1] == 16
+
+
+def test_every_cache_declaration_cites_its_passage():
+    """Each declaration of the cache's calls (not the measurement aids after the marker) has a
+    comment above it that names a page section ([GC] / [VD] / [NJ] / [KJ] and a §)."""
+    text = open(os.path.join(ROOT, "include", "hisparse.h")).read()
+    cut = text.index("measurement aids")
+    seen = set()
+    for name, comment in declarations():
+        pos = text.index(name + "(")
+        if pos > cut or name in ("hs_last_error", "hs_resolve_wgs", "hs_resolve_attn_wgs", "hs_host_pool",
+                                 "hs_page_table", "hs_plan"):
+            continue
+        seen.add(name)
+        assert re.search(r"\[(GC|VD|NJ|KJ)\]", comment), (name, "no page cited")
+    assert {"hs_wait_layer", "hs_export_state", "hs_destroy", "hs_workspace_bytes", "hs_writeback"} <= seen
