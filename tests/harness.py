@@ -89,6 +89,12 @@ class Pair:
         self.d_stats = torch.zeros((w.R, hk.HS_STATS_WORDS), dtype=torch.int32, device=self.dev)
         self.t = 0
         self.newest = None
+        # occupied LRU slots of each anchor cache, and how many misses so far took a slot that
+        # held a position (an eviction): empty slots are taken first, so a step with m misses
+        # and e empty slots evicts max(0, m - e) occupied ones (counted from the oracle's misses)
+        self.occupied = {}
+        self.evicted = 0
+        self.evicted_at = {}
         self.resident = resident
         if resident is not None:
             self._bind_resident(resident)
@@ -199,6 +205,13 @@ class Pair:
 
             for r, res in zip(range(nr), self.pool.map(one, range(nr))):
                 results[(r, l)] = res
+                if self.resident is None:
+                    occ = self.occupied.get((r, l), 0)
+                    ev = max(0, int(res[2]) - (w.B - occ))
+                    self.evicted += ev
+                    if ev:
+                        self.evicted_at[t] = self.evicted_at.get(t, 0) + ev
+                    self.occupied[(r, l)] = min(w.B, occ + int(res[2]))
                 if check:
                     assert stats[r, 0] == res[1] and stats[r, 1] == res[2] and stats[r, 2] == 0 \
                         and stats[r, 3] == res[5], (t, r, l, stats[r], res[1], res[2], res[5])

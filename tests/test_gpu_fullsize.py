@@ -44,14 +44,17 @@ def published_slots_hold_their_records(p, results, samples=64, seed=0):
             assert np.array_equal(rows[n], synth.record(r, l, int(pos[i]))), (r, l, i)
 
 
-def run(w, steps, sample_hot, label):
+def run(w, steps, sample_hot, label, min_evicting_steps=0):
     t0 = time.time()
     p = Pair(w, steps=steps)
     log("%s: set-up %.1f s (host pool %.1f GB)" % (label, time.time() - t0, w.host_bytes(steps) / 1e9))
     res = None
     for _ in range(steps):
         res = p.step_gpu_and_oracle()
-    log("%s: %d steps %.1f s" % (label, steps, time.time() - t0))
+    log("%s: %d steps %.1f s; occupied slots evicted %d in %d steps" % (label, steps, time.time() - t0,
+                                                                     p.evicted, len(p.evicted_at)))
+    # past the buffer-fill point: misses beyond the empty slots evict slots holding positions
+    assert len(p.evicted_at) >= min_evicting_steps, (p.evicted, sorted(p.evicted_at))
     p.check_state(hot=False)
     published_slots_hold_their_records(p, res)
     p.check_hot(*sample_hot)
@@ -59,15 +62,23 @@ def run(w, steps, sample_hot, label):
     p.close()
 
 
+# steps per buffer size: all 128 at B = 4096; at 2048 (= k) the buffer is full after the first
+# step, at 8192 after about 28
+BATCHED_STEPS = {2048: 16, 4096: 128, 8192: 40}
+BATCHED_EVICTING = {2048: 14, 4096: 110, 8192: 8}
+
+
 @pytest.mark.parametrize("B", synth.BATCHED_B_SWEEP)
 def test_batched_full(B):
-    """32 requests x 16 layers, ctx 32768, k 2048, B in {2048, 4096, 8192}; 6 steps."""
-    run(W["batched"].scaled(B=B), 6, (range(16)[::5], [0, 17, 31]), "batched B=%d" % B)
+    """32 requests x 16 layers, ctx 32768, k 2048, B in {2048, 4096, 8192}: all 128 steps at
+    B = 4096, and past the buffer-fill point at 2048 and 8192."""
+    run(W["batched"].scaled(B=B), BATCHED_STEPS[B], (range(16)[::5], [0, 17, 31]), "batched B=%d" % B,
+        min_evicting_steps=BATCHED_EVICTING[B])
 
 
 def test_capacity_full():
     """4 x 4, ctx 1048576 (19.3 GB pinned), 32 blocks of 64 tokens, all 64 steps."""
-    run(W["capacity"], 64, (range(4), range(4)), "capacity")
+    run(W["capacity"], 64, (range(4), range(4)), "capacity", min_evicting_steps=40)
 
 
 def test_long_full_all_steps():
