@@ -1,19 +1,18 @@
 """Benchmark of the per-layer RESOLVE hot path on one MI355X.
 
-Workload: the long-request configuration -- 1 request x 8 layers, 131072-token
-context, 1152-byte bf16 records, k = 2048, B = 4096, one token appended and
-written through per step.  One step is one decode step of the whole path:
-write-through of the new token, then for each layer RESOLVE (stage, mark,
-scan, fetch, publish) and the sparse-attention consumer over the published
-slots.  Inputs (selection traces, new records, queries) are resident in HBM
-before the timed region starts.
+Workload (the headline): the batched decode step -- 32 requests x 16 layers,
+32768-token contexts, 1152-byte bf16 records, k = 2048, B = 4096.  Per layer one
+launch for all 32 requests resolves the selections (stage, mark, scan, fetch,
+publish) and runs the sparse decode attention (16 heads) over the published
+slots (hs_resolve_attn).  One step is all 16 layers.  Inputs (selection traces,
+queries) are resident in HBM before the timed region starts.
 
 Prints one JSON line.  `value` is resolved selections per second over the K
-timed steps.  Also reported: per-kernel durations from HIP events on the
-launch stream, miss-fetch GB/s against the measured host-link ceiling, the
-all-hit RESOLVE latency per layer (k = 2048, B = 4096) against the launch and
-HBM bounds, a roofline entry for the dominant kernel, and the CPU oracle on
-this host's cores.
+timed steps.  Also reported: the miss-fetch GB/s against the measured host-link
+ceiling, the all-hit RESOLVE latency per layer (k = 2048, B = 4096) against the
+launch bound, a roofline entry for the dominant kernel (against the host link,
+which binds it here, and against HBM), the CPU oracle on this host's cores over
+the same trace, and (without --quick) the other workloads and probes.
 """
 from __future__ import annotations
 
@@ -30,14 +29,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+# the host link of an MI355X: PCIe 5.0 x16, 64 GB/s per direction (published)
+HOST_LINK_PEAK_GBS = 64.0
 REC = 1152
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=120)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing")
@@ -55,6 +55,11 @@ def addr(t, *idx):
     for i, st in zip(idx, t.stride()):
         off += i * st
     return t.data_ptr() + off * t.element_size()
+
+
+def progress(msg):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
 def sync_barrier(torch):
@@ -98,11 +103,18 @@ def profile_avg_us(kernel: str, workload: str = "long"):
     return None
 
 
+def fill_pools(synth, cache, w, lmax):
+    """The prefill records of every request into the library's pinned pool (the generator's C
+    code runs several threads per request)."""
+    for r in range(w.R):
+        synth.fill_request(cache.host_pool_address(r), r, w.L, lmax, w.ctx)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path (each (request, layer) "
+        print("bench.py measures one GPU: libhisparse has no multi-GPU path (each (request, layer) "
               "cache is independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
@@ -120,231 +132,83 @@ def main():
         calibration_copy(torch, hk, dev)
         print(json.dumps(SECONDARY[args.measure](torch, hk, synth, dev)))
         return
-    w = synth.WORKLOADS["long"]
-    W, K = args.warmup, args.steps
-    n_steps = W + K
+    t_start = time.time()
+    # the host link's ceiling first (the headline's miss-fetch fraction is taken against it)
+    link = measure_link(torch, hk, dev)
+    progress("link ceiling %.1f GB/s" % link["ceiling_GBps"])
+    w = synth.WORKLOADS["batched"].scaled(B=4096)
+    head = batched_decode(torch, hk, synth, dev, w, args.warmup, args.steps, args)
     R, L, k, B = w.R, w.L, w.k, w.B
-    lmax = w.max_positions(n_steps)
-    heads, scale = w.heads, 576 ** -0.5
+    K, W = args.steps, args.warmup
+    detail = head["detail"]
+    detail["link_ceiling_GBps"] = link["ceiling_GBps"]
+    detail["link_dma_h2d_GBps"] = link["dma_GBps"]
+    detail["link_zero_copy_GBps"] = link["zero_copy_GBps"]
+    detail["link_random_records_GBps"] = link["random_records_GBps"]
+    # the all-hit RESOLVE latency per layer at k 2048, B 4096 (part of the metric)
+    detail.update(measure_all_hit(torch, hk, synth, dev))
+    progress("all-hit RESOLVE %.2f / %.2f us per layer (1 / 32 requests)"
+             % (detail["all_hit_us_per_layer_r1"], detail["all_hit_us_per_layer_r32"]))
 
-    # ---- inputs (host generation, then resident in HBM) ------------------------------
-    # the step's kernels run on `compute` (torch's current stream); write-through on `backup`
-    t_in = time.time()
-    cfg = hk.make_config(R, L, lmax, k, B, newest_slot=True)
-    cache = hk.HiSparse(cfg)
-    for r in range(R):
-        synth.fill_request(cache.host_pool_address(r), r, L, lmax, w.ctx)
-    trace = np.stack([np.stack([synth.selection_trace(w, r, l, n_steps) for r in range(R)], axis=1)
-                      for l in range(L)], axis=1)  # [steps][L][R][k]
-    d_trace = torch.from_numpy(trace).to(dev)
-    new_pos = w.ctx + np.arange(n_steps)
-    d_new_kv = torch.from_numpy(np.stack([synth.records_at(R, L, [p] * R) for p in new_pos])).to(dev)
-    d_new_pos = torch.from_numpy(np.repeat(new_pos[:, None], R, axis=1).astype(np.int32)).to(dev)
-    d_ctx = torch.from_numpy((new_pos[:, None] + 1).repeat(R, axis=1).astype(np.int32)).to(dev)
-    d_q = torch.from_numpy(np.stack([synth.queries(R, L, t, heads=heads) for t in range(n_steps)])
-                           .view(np.int16)).to(dev)  # [steps][R][L][H][576]
-    d_q = d_q.permute(0, 2, 1, 3, 4).contiguous()   # [steps][L][R][H][576]
-    d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
-    d_stats = torch.zeros((n_steps, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
-    d_out = torch.empty((L, R, heads, 512), dtype=torch.float32, device=dev)
-    compute = torch.cuda.current_stream()
-    backup = torch.cuda.Stream()
-    cs, bs = compute.cuda_stream, backup.cuda_stream
-    # every step's buffer addresses, computed once (as a serving loop holds them)
-    a_sel = [[addr(d_trace, t, l) for l in range(L)] for t in range(n_steps)]
-    a_q = [[addr(d_q, t, l) for l in range(L)] for t in range(n_steps)]
-    a_stats = [[addr(d_stats, t, l) for l in range(L)] for t in range(n_steps)]
-    a_ctx = [addr(d_ctx, t) for t in range(n_steps)]
-    a_kv = [addr(d_new_kv, t) for t in range(n_steps)]
-    a_pos = [addr(d_new_pos, t) for t in range(n_steps)]
-    a_slots = [addr(d_slots, l) for l in range(L)]
-    a_out = [addr(d_out, l) for l in range(L)]
-    input_s = time.time() - t_in
-
-    def step(c, t, fused, ev_row=None, backup_stream=False):
-        """One decode step: write-through of the new token, then per layer RESOLVE and the
-        attention over the published slots (one fused call, or hs_resolve + hs_sparse_attn).
-        The write-through is one kernel on the compute stream (backup_stream: the backup
-        stream with its event pair).  ev_row: events recorded on the launch stream around
-        each layer's attention call (separate calls only)."""
-        h = c.h
-        hk.hs_writeback(h, a_kv[t], a_pos[t], cs, bs if backup_stream else cs)
-        sel, q, stats, ctx = a_sel[t], a_q[t], a_stats[t], a_ctx[t]
-        for l in range(L):
-            if fused:
-                hk.hs_resolve_attn(h, l, sel[l], ctx, a_slots[l], stats[l], 0, 0, q[l], heads, 512,
-                                   a_out[l], scale, cs)
-            else:
-                hk.hs_resolve(h, l, sel[l], ctx, a_slots[l], stats[l], 0, 0, cs)
-                if ev_row is not None:
-                    ev_row[l][0].record(compute)
-                hk.hs_sparse_attn(h, l, q[l], heads, 512, a_slots[l], a_out[l], scale, 0, cs)
-            if ev_row is not None:
-                ev_row[l][1].record(compute)
-
-    def fresh_cache():
-        c = hk.HiSparse(cfg)
-        for r in range(R):
-            synth.fill_request(c.host_pool_address(r), r, L, lmax, w.ctx)
-        return c
-
-    def value_pass(c, fused, backup_stream=False):
-        """W warmup steps, then K timed steps with nothing between kernels.  Returns the
-        elapsed time and the host's enqueue time of the K steps (well below the elapsed time:
-        the GPU, not the host, sets the pace)."""
-        for t in range(W):
-            step(c, t, fused, backup_stream=backup_stream)
-        sync_barrier(torch)
-        t0 = time.perf_counter()
-        for i in range(K):
-            step(c, W + i, fused, backup_stream=backup_stream)
-        t_enq = time.perf_counter() - t0
-        sync_barrier(torch)
-        dt = time.perf_counter() - t0
-        backup.synchronize()
-        return dt, t_enq
-
-    def timing_pass(c, fused):
-        """The same steps from the same empty start: the RESOLVE (or fused) kernel of every
-        timed layer stamped by its own start and end; for the separate calls also events
-        around each attention call (attention and merge kernels)."""
-        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)] for _ in range(K)]
-        for t in range(W):
-            step(c, t, fused)
-        hk.hs_timing_start(c.h, K * L)
-        for i in range(K):
-            step(c, W + i, fused, ev_row=None if fused else ev[i])
-        sync_barrier(torch)
-        backup.synchronize()
-        kern = hk.hs_timing_read(c.h, K * L)
-        assert kern.size == K * L
-        call = [] if fused else [ev[i][l][0].elapsed_time(ev[i][l][1]) * 1e3 for i in range(K) for l in range(L)]
-        return [float(x) for x in kern], call
-
-    # pass 1 (the reported value): the fused path
-    fused = hk.hs_resolve_attn_wgs(cache.h) > 0
-    elapsed, enqueue = value_pass(cache, True)
-    stats = d_stats.cpu().numpy()
-    out_fused = d_out.clone()
-    cache.close()
-    # pass 1b: the same with the write-through on the backup stream (the pages' layout)
-    cache = fresh_cache()
-    d_stats.zero_()
-    elapsed_bs, _ = value_pass(cache, True, backup_stream=True)
-    assert np.array_equal(d_stats.cpu().numpy(), stats), "the backup-stream pass resolved differently"
-    assert torch.equal(d_out, out_fused), "the backup-stream pass attended differently"
-    cache.close()
-    # pass 2: kernel durations of the fused path
-    cache = fresh_cache()
-    d_stats.zero_()
-    kern_us, _ = timing_pass(cache, True)
-    assert np.array_equal(d_stats.cpu().numpy(), stats), "the passes resolved differently"
-    cache.close()
-    # passes 3 and 4: the same steps through hs_resolve + hs_sparse_attn
-    cache = fresh_cache()
-    d_stats.zero_()
-    elapsed_sep, enqueue_sep = value_pass(cache, False)
-    assert np.array_equal(d_stats.cpu().numpy(), stats), "the separate calls resolved differently"
-    att_dev = float((d_out - out_fused).abs().max() / out_fused.abs().max())
-    cache.close()
-    cache = fresh_cache()
-    d_stats.zero_()
-    res_us, att_us = timing_pass(cache, False)
-
-    errors = int(stats[..., 2].any())
-    misses_timed = int(stats[W:, :, :, 1].sum())
-    hits_timed = int(stats[W:, :, :, 0].sum())
-    selections = K * L * R * k
-    value = selections / elapsed
-    miss_rate = misses_timed / max(1, misses_timed + hits_timed)
-
-    detail = {
-        "path": "hs_resolve_attn (fused RESOLVE + attention kernel, then merge)" if fused
-                else "hs_resolve_attn (two calls: no fused kernel for this configuration)",
-        "host_enqueue_us_per_step": enqueue / K * 1e6,
-        "write_through_backup_stream_ms_per_step": elapsed_bs / K * 1e3,
-        "write_through_backup_stream_selections_per_s": selections / elapsed_bs,
-        "fused_kernel_us_per_layer_mean": statistics.fmean(kern_us),
-        "fused_kernel_us_per_layer_median": statistics.median(kern_us),
-        "fused_wgs_per_request": hk.hs_resolve_attn_wgs(cache.h),
-        "separate_selections_per_s": selections / elapsed_sep,
-        "separate_ms_per_step": elapsed_sep / K * 1e3,
-        "separate_host_enqueue_us_per_step": enqueue_sep / K * 1e6,
-        "separate_resolve_kernel_us_per_layer_mean": statistics.fmean(res_us),
-        "separate_resolve_kernel_us_per_layer_median": statistics.median(res_us),
-        "separate_attention_call_us_per_layer_mean": statistics.fmean(att_us),
-        "fused_vs_separate_attention_max_rel_diff": att_dev,
-        "miss_rate": miss_rate,
-        "misses_per_layer_step": misses_timed / (K * L * R),
-        "cold_step_misses": int(stats[0, :, :, 1].sum()),
-        "errors": errors,
-        "resolve_wgs_per_request": cache.wgs,
-        "input_setup_s": round(input_s, 2),
-    }
     # ---- secondary measurements --------------------------------------------------------
-    link = {}
     if args.quick:
         calibration_copy(torch, hk, dev)
     else:
-        link = measure_link(torch, hk, dev)
-        detail.update(measure_fetch(torch, hk, synth, w, dev, trace, lmax))
-        detail.update(measure_fetch_heavy(torch, hk, synth, dev))
-        detail.update(measure_all_hit(torch, hk, synth, dev))
-        detail.update(measure_resident(torch, hk, synth, w, dev, trace, lmax))
-        detail.update(measure_fp8(torch, hk, synth, dev))
-        detail.update(measure_rows(torch, hk, synth, dev))
-        detail.update(measure_short(torch, hk, synth, dev))
-        detail.update(measure_batched(torch, hk, synth, dev))
-        detail.update(measure_capacity(torch, hk, synth, dev))
-        detail.update(measure_replay(torch, hk, synth, dev))
-        detail.update(measure_attention(torch, hk, synth, dev))
-        detail.update(measure_shared_step(torch, hk, synth, dev))
+        detail["long_decode"] = measure_long_decode(torch, hk, synth, dev)
+        progress("long decode %.1f M selections/s" % (detail["long_decode"]["selections_per_s"] / 1e6))
+        for fn in (measure_fetch, measure_fetch_heavy, measure_resident, measure_fp8, measure_rows, measure_short,
+                   measure_capacity, measure_replay, measure_attention, measure_shared_step):
+            detail.update(fn(torch, hk, synth, dev))
+            progress(fn.__name__ + " done")
         detail["launch_latency_us"] = measure_empty(torch, hk)
         detail.update(measure_hbm(torch, hk, dev))
         detail["attention_r32_frac_of_scattered_read"] = (detail["attention_r32_GBps"]
                                                           / detail["hbm_scattered_records_read_GBps"])
-        detail["link_ceiling_GBps"] = link["ceiling_GBps"]
-        detail["link_dma_h2d_GBps"] = link["dma_GBps"]
-        detail["link_zero_copy_GBps"] = link["zero_copy_GBps"]
-        detail["link_random_records_GBps"] = link["random_records_GBps"]
-        for key in ("batched_cold_fetch_GBps", "long_cold_fetch_GBps", "batched_steady_link_GBps",
-                    "capacity_cold_fetch_GBps", "capacity_steady_fetch_GBps", "replay_cold_GBps",
-                    "replay_steady_GBps", "replay_cold_kernels_GBps", "replay_steady_kernels_GBps"):
+        for key in ("batched_cold_fetch_GBps", "long_cold_fetch_GBps", "capacity_cold_fetch_GBps",
+                    "capacity_steady_fetch_GBps", "replay_cold_GBps", "replay_steady_GBps",
+                    "replay_cold_kernels_GBps", "replay_steady_kernels_GBps"):
             detail[key.replace("GBps", "frac_of_link")] = detail[key] / link["ceiling_GBps"]
 
     # ---- roofline of the dominant kernel -------------------------------------------------
-    # The fused RESOLVE + attention kernel is the longest kernel of the step (the merge and the
-    # write-through kernels are short; see the kernel trace).  Its algorithmic bytes per
-    # launch, per request: the selection in and the slots out; the slot map and LRU order read
-    # and written; per miss the record written to HBM and two page-table entries; the k
-    # selected records read once (hot slots from HBM, misses from the host pool); the queries
-    # in and the output out.  The split into chunk partials is not counted.
-    steady_misses = misses_timed / (K * L * R)
-    alg_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + steady_misses * (REC + 8 + 8)
-                     + k * REC + heads * 576 * 2 + heads * 512 * 4)
+    # The fused RESOLVE + attention kernel is the longest kernel of the step (the finish
+    # kernel is short; see the kernel trace).  Per launch it moves, for each of the R requests:
+    # over the host link the m missed records (m x 1152 bytes); in HBM the selection in and the
+    # slots out, the slot map and LRU order read and written, the k - m hit records read, the m
+    # missed records and their two page-table entries written, the queries in and the output
+    # out.  The staging of the misses and the chunk partials are implementation choices and
+    # are not counted.  At 32 requests the link carries the binding share.
+    kern_us = head["kern_us"]
     t_us = statistics.fmean(kern_us)
+    m_req = head["misses_timed"] / (K * L * R)  # misses per (request, layer) launch share
+    link_bytes = R * m_req * REC
+    hbm_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + (k - m_req) * REC + m_req * (REC + 8 + 8)
+                     + w.heads * 576 * 2 + w.heads * 512 * 4)
+    link_gbs = link_bytes / (t_us * 1e-6) / 1e9
+    hbm_gbs = hbm_bytes / (t_us * 1e-6) / 1e9
     kname = "resolve_kernel<4,2,true>"
-    roof = {"kernel": kname, "bound": "hbm", "achieved": alg_bytes / (t_us * 1e-6) / 1e9,
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": profile_traffic("resolve_attn_kernel")}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["avg_launch_us_kernel_events"] = t_us
-    roof["avg_launch_us_rocprof"] = profile_avg_us(kname)
-    roof["algorithmic_bytes_per_launch"] = alg_bytes
-    # the separate path's RESOLVE kernel for reference (metadata and misses only)
-    sep_bytes = R * (k * 4 + B * 4 * 2 + B * 2 * 2 + k * 4 + steady_misses * (REC + 8 + 8))
-    detail["separate_resolve_alg_bytes"] = sep_bytes
-    detail["separate_resolve_GBps"] = sep_bytes / (statistics.fmean(res_us) * 1e-6) / 1e9
+    hbm = {"achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hbm_gbs / HBM_PEAK_GBS,
+           "algorithmic_bytes_per_launch": hbm_bytes, "traffic": profile_traffic("resolve_attn_kernel", "batched")}
+    roof = {"kernel": kname, "bound": "link", "achieved": link_gbs, "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+            "frac": link_gbs / HOST_LINK_PEAK_GBS, "traffic": hbm["traffic"],
+            "algorithmic_bytes_per_launch": link_bytes,
+            "frac_of_measured_link_ceiling": link_gbs / link["ceiling_GBps"],
+            "measured_link_ceiling_GBps": link["ceiling_GBps"],
+            "avg_launch_us_kernel_events": t_us, "avg_launch_us_rocprof": profile_avg_us(kname, "batched"),
+            "hbm": hbm}
+    if hbm["frac"] > roof["frac"]:  # (not at this shape: reported for completeness)
+        roof["bound"] = "hbm"
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(synth, w, trace, n_steps, W, K, args.cpu_seconds)
+        cpu = cpu_baseline_batched(synth, w, head, W, K, args.cpu_seconds)
+        progress("oracle %.2f M selections/s on %d threads" % (cpu["value"] / 1e6, cpu["cores"]))
         if not args.quick:
             detail["configs"] = cpu_baseline_configs(torch, hk, synth, dev)
             for row in detail["configs"]:
-                if "link_ceiling_GBps" in detail:
-                    row["gpu_miss_frac_of_link"] = row["gpu_miss_GBps"] / detail["link_ceiling_GBps"]
+                row["gpu_miss_frac_of_link"] = row["gpu_miss_GBps"] / link["ceiling_GBps"]
+    head["cache"].close()
 
-    cache.close()
+    value = head["value"]
     line = {
         "metric": "resolved selections/s",
         "value": value,
@@ -352,21 +216,312 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": elapsed / K * 1e3,
+        "ms_per_step": head["elapsed"] / K * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int32 index + bf16 records (fp32 attention accumulate)",
-        "data": "synthetic (seeded selection traces; counter-based N(0,1) bf16 records)",
-        "config": {"workload": "long request: 1 req x 8 layers, ctx 131072, k 2048, B 4096, "
-                               "write-through + sparse attention (16 heads)",
+        "data": "synthetic (seeded selection traces; counter-based N(0,1) bf16 records and queries)",
+        "config": {"workload": "batched decode: 32 requests x 16 layers, ctx 32768, k 2048, B 4096; per layer one "
+                               "launch for all requests of RESOLVE + sparse decode attention (16 heads) over "
+                               "the published slots",
                    "requests": R, "layers": L, "ctx": w.ctx, "top_k": k, "buffer_slots": B,
-                   "record_bytes": REC, "parallelism": "single GPU"},
+                   "record_bytes": REC, "heads": w.heads, "parallelism": "single GPU"},
+        "metric_parts": {
+            "resolved_selections_per_s": value,
+            "miss_fetch_GBps_fused_kernel": link_gbs,
+            "miss_fetch_frac_of_link_ceiling": link_gbs / link["ceiling_GBps"],
+            "miss_fetch_GBps_whole_step": detail["steady_link_GBps"],
+            "link_ceiling_GBps": link["ceiling_GBps"],
+            "all_hit_resolve_us_per_layer_r1": detail["all_hit_us_per_layer_r1"],
+            "all_hit_resolve_us_per_layer_r32": detail["all_hit_us_per_layer_r32"],
+            "launch_latency_bound_us": detail.get("launch_latency_us"),
+        },
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": detail,
+        "bench_wall_s": round(time.time() - t_start, 1),
     }
     print(json.dumps(line))
+
+
+def batched_decode(torch, hk, synth, dev, w, W, K, args):
+    """The headline: the batched decode step (32 requests x 16 layers, ctx 32768, k 2048,
+    B 4096, 16 heads).  A step resolves every layer for all requests in one launch and attends
+    over the published slots (hs_resolve_attn: the fused kernel, then the finish kernel).
+    Inputs (selection traces, queries) are resident in HBM and every step's buffer addresses
+    are computed before the timed region.  W warmup steps, then K timed steps with nothing
+    between kernels.  Further passes from the same empty start (hs_reset_request): every fused
+    kernel stamped by its own start and end, and the separate calls (hs_resolve +
+    hs_sparse_attn), which must resolve identically."""
+    R, L, k, B, heads = w.R, w.L, w.k, w.B, w.heads
+    n = W + K
+    lmax = w.max_positions(n)
+    scale = 576 ** -0.5
+    t_in = time.time()
+    cache = hk.HiSparse(hk.make_config(R, L, lmax, k, B))
+    fill_pools(synth, cache, w, lmax)
+    t_fill = time.time() - t_in
+    progress("batched: host pool %.1f GB filled in %.1f s" % (w.host_bytes(n) / 1e9, t_fill))
+    trace = np.stack([np.stack([synth.selection_trace(w, r, l, n) for r in range(R)], axis=1)
+                      for l in range(L)], axis=1)  # [n][L][R][k]
+    d_trace = torch.from_numpy(trace).to(dev)
+    d_q = torch.empty((n, L, R, heads, 576), dtype=torch.int16, device=dev)
+    for t in range(n):  # [R][L][H][576] per step, stored [L][R][H][576]
+        d_q[t].copy_(torch.from_numpy(synth.queries(R, L, t, heads=heads).view(np.int16)).permute(1, 0, 2, 3))
+    d_ctx = torch.full((R,), w.ctx, dtype=torch.int32, device=dev)
+    d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
+    d_out = torch.empty((L, R, heads, 512), dtype=torch.float32, device=dev)
+    compute = torch.cuda.current_stream()
+    cs = compute.cuda_stream
+    a_sel = [[addr(d_trace, t, l) for l in range(L)] for t in range(n)]
+    a_q = [[addr(d_q, t, l) for l in range(L)] for t in range(n)]
+    a_stats = [[addr(d_stats, t, l) for l in range(L)] for t in range(n)]
+    a_slots = [addr(d_slots, l) for l in range(L)]
+    a_out = [addr(d_out, l) for l in range(L)]
+    a_ctx = d_ctx.data_ptr()
+    torch.cuda.synchronize()
+    input_s = time.time() - t_in
+    progress("batched: inputs resident in HBM after %.1f s" % input_s)
+    h = cache.h
+
+    def step(t, fused=True):
+        sel, q, st = a_sel[t], a_q[t], a_stats[t]
+        for l in range(L):
+            if fused:
+                hk.hs_resolve_attn(h, l, sel[l], a_ctx, a_slots[l], st[l], 0, 0, q[l], heads, 512, a_out[l],
+                                   scale, cs)
+            else:
+                hk.hs_resolve(h, l, sel[l], a_ctx, a_slots[l], st[l], 0, 0, cs)
+                hk.hs_sparse_attn(h, l, q[l], heads, 512, a_slots[l], a_out[l], scale, 0, cs)
+
+    def reset():
+        for r in range(R):
+            hk.hs_reset_request(h, r, cs)
+        d_stats.zero_()
+        torch.cuda.synchronize()
+
+    def value_pass(fused=True):
+        for t in range(W):
+            step(t, fused)
+        sync_barrier(torch)
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(W + i, fused)
+        t_enq = time.perf_counter() - t0
+        sync_barrier(torch)
+        return time.perf_counter() - t0, t_enq
+
+    fused = hk.hs_resolve_attn_wgs(h) > 0
+    elapsed, enqueue = value_pass()
+    progress("batched: %.1f M selections/s, %.3f ms per step" % (K * L * R * k / elapsed / 1e6, elapsed / K * 1e3))
+    stats = d_stats.cpu().numpy()
+    out_fused = d_out.clone()
+    # kernel durations of the fused kernel, the same steps from the same empty start
+    reset()
+    for t in range(W):
+        step(t)
+    hk.hs_timing_start(h, K * L)
+    for i in range(K):
+        step(W + i)
+    sync_barrier(torch)
+    kern_us = [float(x) for x in hk.hs_timing_read(h, K * L)]
+    assert len(kern_us) == K * L
+    assert np.array_equal(d_stats.cpu().numpy(), stats), "the timing pass resolved differently"
+    assert torch.equal(d_out, out_fused), "the timing pass attended differently"
+    # the separate calls (hs_resolve + hs_sparse_attn), the same steps
+    reset()
+    elapsed_sep, _ = value_pass(fused=False)
+    assert np.array_equal(d_stats.cpu().numpy(), stats), "the separate calls resolved differently"
+    att_dev = float((d_out - out_fused).abs().max() / out_fused.abs().max())
+    assert not stats[..., 2].any(), "error bits set"
+    misses_timed = int(stats[W:, :, :, 1].sum())
+    hits_timed = int(stats[W:, :, :, 0].sum())
+    fetched = stats[W:, :, :, 4].astype(np.uint32).astype(np.int64) + \
+        (stats[W:, :, :, 5].astype(np.uint32).astype(np.int64) << 32)
+    assert int(fetched.sum()) == misses_timed * REC, "bytes_fetched disagrees with misses"
+    selections = K * L * R * k
+    # occupied slots evicted in the timed steps (empty slots are taken first)
+    occ = np.minimum(B, np.cumsum(stats[:, :, :, 1], axis=0))
+    before = np.concatenate([np.zeros_like(occ[:1]), occ[:-1]])
+    evicted = np.maximum(0, stats[:, :, :, 1] - (B - before))
+    detail = {
+        "path": "hs_resolve_attn (fused RESOLVE + attention kernel, then the finish kernel)" if fused
+                else "hs_resolve_attn (two calls: no fused kernel for this configuration)",
+        "fused_wgs_per_request": hk.hs_resolve_attn_wgs(h),
+        "host_enqueue_us_per_step": enqueue / K * 1e6,
+        "fused_kernel_us_per_layer_mean": statistics.fmean(kern_us),
+        "fused_kernel_us_per_layer_median": statistics.median(kern_us),
+        "fused_kernel_us_p90": float(np.percentile(kern_us, 90)),
+        "separate_selections_per_s": selections / elapsed_sep,
+        "separate_ms_per_step": elapsed_sep / K * 1e3,
+        "fused_vs_separate_attention_max_rel_diff": att_dev,
+        "miss_rate": misses_timed / max(1, misses_timed + hits_timed),
+        "misses_per_launch": misses_timed / (K * L),
+        "steady_link_GBps": misses_timed * REC / elapsed / 1e9,
+        "occupied_slots_evicted_timed": int(evicted[W:].sum()),
+        "first_step_evicting": int(np.argmax(evicted.sum(axis=(1, 2)) > 0)) + 1,
+        "cold_step_misses": int(stats[0, :, :, 1].sum()),
+        "host_pool_GB": w.host_bytes(n) / 1e9,
+        "host_pool_fill_s": round(t_fill, 1),
+        "input_setup_s": round(input_s, 1),
+    }
+    return {"value": selections / elapsed, "elapsed": elapsed, "kern_us": kern_us, "stats": stats,
+            "trace": trace, "misses_timed": misses_timed, "detail": detail, "cache": cache, "lmax": lmax}
+
+
+def measure_long_decode(torch, hk, synth, dev, W=8, K=64):
+    """The long-request decode step (1 request x 8 layers, ctx 131072, k 2048, B 4096): the
+    write-through of the new token, then per layer hs_resolve_attn.  The write-through as one
+    kernel on the compute stream, and on a backup stream with its event pair (the pages'
+    layout); fused kernels stamped by their own start and end; the separate calls."""
+    w = synth.WORKLOADS["long"]
+    R, L, k, B = w.R, w.L, w.k, w.B
+    n = W + K
+    lmax = w.max_positions(n)
+    heads, scale = w.heads, 576 ** -0.5
+    cfg = hk.make_config(R, L, lmax, k, B, newest_slot=True)
+    trace = np.stack([np.stack([synth.selection_trace(w, r, l, n) for r in range(R)], axis=1)
+                      for l in range(L)], axis=1)  # [n][L][R][k]
+    d_trace = torch.from_numpy(trace).to(dev)
+    new_pos = w.ctx + np.arange(n)
+    d_new_kv = torch.from_numpy(np.stack([synth.records_at(R, L, [p] * R) for p in new_pos])).to(dev)
+    d_new_pos = torch.from_numpy(np.repeat(new_pos[:, None], R, axis=1).astype(np.int32)).to(dev)
+    d_ctx = torch.from_numpy((new_pos[:, None] + 1).repeat(R, axis=1).astype(np.int32)).to(dev)
+    d_q = torch.from_numpy(np.stack([synth.queries(R, L, t, heads=heads) for t in range(n)])
+                           .view(np.int16)).to(dev).permute(0, 2, 1, 3, 4).contiguous()
+    d_slots = torch.empty((L, R, k), dtype=torch.int32, device=dev)
+    d_stats = torch.zeros((n, L, R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
+    d_out = torch.empty((L, R, heads, 512), dtype=torch.float32, device=dev)
+    compute = torch.cuda.current_stream()
+    backup = torch.cuda.Stream()
+    cs, bs = compute.cuda_stream, backup.cuda_stream
+    a_sel = [[addr(d_trace, t, l) for l in range(L)] for t in range(n)]
+    a_q = [[addr(d_q, t, l) for l in range(L)] for t in range(n)]
+    a_stats = [[addr(d_stats, t, l) for l in range(L)] for t in range(n)]
+    a_ctx = [addr(d_ctx, t) for t in range(n)]
+    a_kv = [addr(d_new_kv, t) for t in range(n)]
+    a_pos = [addr(d_new_pos, t) for t in range(n)]
+    a_slots = [addr(d_slots, l) for l in range(L)]
+    a_out = [addr(d_out, l) for l in range(L)]
+
+    def fresh():
+        c = hk.HiSparse(cfg)
+        for r in range(R):
+            synth.fill_request(c.host_pool_address(r), r, L, lmax, w.ctx)
+        return c
+
+    def step(c, t, fused=True, backup_stream=False):
+        hk.hs_writeback(c.h, a_kv[t], a_pos[t], cs, bs if backup_stream else cs)
+        for l in range(L):
+            if fused:
+                hk.hs_resolve_attn(c.h, l, a_sel[t][l], a_ctx[t], a_slots[l], a_stats[t][l], 0, 0, a_q[t][l], heads,
+                                   512, a_out[l], scale, cs)
+            else:
+                hk.hs_resolve(c.h, l, a_sel[t][l], a_ctx[t], a_slots[l], a_stats[t][l], 0, 0, cs)
+                hk.hs_sparse_attn(c.h, l, a_q[t][l], heads, 512, a_slots[l], a_out[l], scale, 0, cs)
+
+    def run(fused=True, backup_stream=False, timed=False):
+        c = fresh()
+        d_stats.zero_()
+        for t in range(W):
+            step(c, t, fused, backup_stream)
+        sync_barrier(torch)
+        if timed:
+            hk.hs_timing_start(c.h, K * L)
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(c, W + i, fused, backup_stream)
+        sync_barrier(torch)
+        el = time.perf_counter() - t0
+        backup.synchronize()
+        kern = [float(x) for x in hk.hs_timing_read(c.h, K * L)] if timed else None
+        c.close()
+        return el, kern, d_stats.cpu().numpy()
+
+    el, _, st = run()
+    out_fused = d_out.clone()
+    el_bs, _, st_bs = run(backup_stream=True)
+    assert np.array_equal(st, st_bs) and torch.equal(d_out, out_fused), "backup-stream pass differs"
+    _, kern, st_t = run(timed=True)
+    assert np.array_equal(st, st_t)
+    el_sep, _, st_sep = run(fused=False)
+    assert np.array_equal(st, st_sep)
+    sel = K * L * R * k
+    m = int(st[W:, ..., 1].sum())
+    return {"workload": "long request: 1 req x 8 layers, ctx 131072, k 2048, B 4096, write-through + sparse "
+                        "attention (16 heads)",
+            "selections_per_s": sel / el, "ms_per_step": el / K * 1e3,
+            "write_through_backup_stream_selections_per_s": sel / el_bs,
+            "write_through_backup_stream_ms_per_step": el_bs / K * 1e3,
+            "fused_kernel_us_per_layer_mean": statistics.fmean(kern),
+            "fused_kernel_us_per_layer_median": statistics.median(kern),
+            "separate_selections_per_s": sel / el_sep,
+            "miss_rate": m / (K * L * R * k), "misses_per_layer_step": m / (K * L * R),
+            "steps": K, "warmup": W}
+
+
+def cpu_baseline_batched(synth, w, head, W, K, budget_s):
+    """The oracle as it stands, on this host's cores, over the headline's trace: one oracle
+    cache per (request, layer), the same empty start, the W warmup steps resolved untimed
+    (RESOLVE only: they only build the state), then the timed steps that fit the budget, each
+    a RESOLVE and a float64 attention over the selected records per (request, layer).  The
+    oracle reads the records from the library's pinned pool (RESOLVE never writes it).  Its
+    miss counts must equal the GPU's for every (step, layer, request) it ran.  One thread per
+    cache up to the host's cores (at most 16), then one thread."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    R, L, k, B = w.R, w.L, w.k, w.B
+    trace, stats, cache, lmax = head["trace"], head["stats"], head["cache"], head["lmax"]
+    pools = [cache.host_pool(r) for r in range(R)]
+
+    def leg(threads, budget):
+        caches = {(r, l): oracle.Cache(B, lmax, REC) for r in range(R) for l in range(L)}
+        pool = ThreadPoolExecutor(max_workers=threads)
+
+        def layer_step(args):
+            t, r, l, q, attend = args
+            c = caches[(r, l)]
+            out, _, m, _, _ = c.resolve(trace[t, l, r], w.ctx, pools[r][l])
+            if attend:
+                oracle.attention.sparse_decode_attention(q[r, l], c.hot, out, 576 ** -0.5)
+            return m
+
+        def run_step(t, attend):
+            q = synth.queries(R, L, t, heads=w.heads) if attend else None
+            jobs = [(t, r, l, q, attend) for l in range(L) for r in range(R)]
+            return np.array(list(pool.map(layer_step, jobs))).reshape(L, R)
+
+        for t in range(W):
+            run_step(t, False)
+        done = 0
+        t0 = time.perf_counter()
+        while done < K and time.perf_counter() - t0 < budget:
+            m = run_step(W + done, True)
+            assert np.array_equal(m, stats[W + done, :, :, 1]), "oracle and GPU misses differ"
+            done += 1
+        el = time.perf_counter() - t0
+        pool.shutdown()
+        for c in caches.values():
+            c.close()
+        return done * L * R * k / el, done
+
+    threads = min(L * R, os.cpu_count() or 1, 16)
+    with threadpool_limits(limits=1):
+        value, done = leg(threads, budget_s)
+        value1, done1 = leg(1, budget_s / 2)
+    return {"value": value, "unit": "selections/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of the %d timed decode steps (after the same %d warmup steps, resolved untimed), all "
+                      "%d layers x %d requests; RESOLVE + float64 attention per (request, layer); misses "
+                      "checked equal to the GPU's" % (done, K, W, L, R),
+            "single_thread_value": value1,
+            "single_thread_sample": "the first %d timed steps, same start, one thread" % done1,
+            "host_cpu": host_cpu(), "nproc": os.cpu_count()}
 
 
 def calibration_copy(torch, hk, dev):
@@ -470,13 +625,23 @@ def run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, flags, reside
     return us, st
 
 
-def measure_fetch(torch, hk, synth, w, dev, trace, lmax):
+def long_trace(synth, steps):
+    """The long request's workload (one token appended per step), its trace [steps][L][R][k]
+    and its pool size in positions."""
+    w = synth.WORKLOADS["long"]
+    trace = np.stack([np.stack([synth.selection_trace(w, r, l, steps) for r in range(w.R)], axis=1)
+                      for l in range(w.L)], axis=1)
+    return w, trace, w.max_positions(steps)
+
+
+def measure_fetch(torch, hk, synth, dev):
     """IO cost inside RESOLVE on identical metadata states (the same trace from the same empty
     start, run once normally and once with SKIP_IO), for the long workload.  The cold step's
     fetch rate is its miss bytes over the whole RESOLVE kernel (a lower bound on the link rate
     reached: the metadata stages count as transfer time); the difference to the SKIP_IO
     kernel only says how much of the kernel the IO adds, since the fetch overlaps stages 1-3."""
-    steps = min(64, trace.shape[0])
+    steps = 64
+    w, trace, lmax = long_trace(synth, steps)
     us_io, st = run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, 0)
     us_skip, st2 = run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, hk.HS_SKIP_IO)
     assert np.array_equal(st, st2)
@@ -585,7 +750,7 @@ def measure_all_hit(torch, hk, synth, dev):
     return out
 
 
-def measure_resident(torch, hk, synth, w, dev, trace, lmax):
+def measure_resident(torch, hk, synth, dev):
     """Resident tier in front of the hot slots.  All resident (a short request that fits the
     device pool): the kernel returns after the block-table lookup, at 1 and 32 requests.
     Long workload with the last 16384 prefill tokens and 5 % of older pages resident:
@@ -602,7 +767,8 @@ def measure_resident(torch, hk, synth, w, dev, trace, lmax):
                                   resident=ResidentSpec(all_resident=True))
         assert (st[..., 3] == wl.k).all() and st[..., 1].sum() == 0
         out["all_resident_us_per_layer_%s" % name] = float(np.median(us[1:]))
-    steps = min(64, trace.shape[0])
+    steps = 64
+    w, trace, lmax = long_trace(synth, steps)
     us, st = run_resolve_only(torch, hk, synth, w, dev, trace, lmax, steps, 0,
                               resident=ResidentSpec(window_tokens=16384, old_frac=0.05))
     out["long_resident_steady_us_per_layer"] = float(us[8:].mean())
@@ -960,67 +1126,6 @@ def measure_hbm(torch, hk, dev):
     return {"hbm_copy_GBps": copy, "hbm_stream_read_GBps": read, "hbm_scattered_records_read_GBps": gather}
 
 
-def cpu_baseline(synth, w, trace, n_steps, W, K, budget_s):
-    """The oracle as it stands, on this host's cores, over the same trace: one thread per layer
-    cache, then one thread for all of them.  Each leg starts from empty caches, runs the
-    warmup steps untimed and times the first timed steps that fit its budget.  Same step:
-    append + write-through, resolve, float64 attention."""
-    from concurrent.futures import ThreadPoolExecutor
-
-    from threadpoolctl import threadpool_limits
-
-    import oracle
-
-    R, L, k, B = w.R, w.L, w.k, w.B
-    lmax = w.max_positions(n_steps)
-    host = [np.empty((L, lmax, REC), np.uint8) for _ in range(R)]
-    for r in range(R):
-        synth.fill_request(host[r], r, L, lmax, w.ctx)
-
-    def leg(threads, budget):
-        caches = {(r, l): oracle.Cache(B, lmax, REC, newest_slot=True) for r in range(R) for l in range(L)}
-        pool = ThreadPoolExecutor(max_workers=threads)
-
-        def layer_step(args):
-            t, r, l, q = args
-            p = w.ctx + t
-            c = caches[(r, l)]
-            c.append(p, synth.record(r, l, p), host[r][l])
-            out, _, _, _, _ = c.resolve(trace[t, l, r], p + 1, host[r][l])
-            oracle.attention.sparse_decode_attention(q[r, l], c.hot, out, 576 ** -0.5)
-            return out.size
-
-        def run_step(t):
-            q = synth.queries(R, L, t, heads=w.heads)
-            return sum(pool.map(layer_step, [(t, r, l, q) for r in range(R) for l in range(L)]))
-
-        for t in range(W):
-            run_step(t)
-        done, sel = 0, 0
-        t0 = time.perf_counter()
-        while done < K and time.perf_counter() - t0 < budget:
-            sel += run_step(W + done)
-            done += 1
-        el = time.perf_counter() - t0
-        pool.shutdown()
-        for c in caches.values():
-            c.close()
-        return sel / el, done
-
-    # one BLAS thread per caller, so that the pool's size is the number of threads used
-    # (numpy's BLAS would otherwise start its own threads inside every pool thread)
-    threads = min(L * R, os.cpu_count() or 1)
-    with threadpool_limits(limits=1):
-        value, done = leg(threads, budget_s)
-        value1, done1 = leg(1, budget_s / 2)
-    return {"value": value, "unit": "selections/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of the %d timed decode steps (after the same %d warmup steps), all %d layers; "
-                      "append + resolve + float64 attention per layer" % (done, K, W, L),
-            "single_thread_value": value1,
-            "single_thread_sample": "the first %d timed steps, same start, one thread" % done1,
-            "host_cpu": host_cpu(), "nproc": os.cpu_count()}
-
-
 def cpu_baseline_configs(torch, hk, synth, dev, budget_s=3.0):
     """Each workload side by side: GPU RESOLVE (hs_resolve, every launch stamped by its own
     start and end) and the oracle on this host's cores, the same seeded trace from the same
@@ -1118,6 +1223,7 @@ SECONDARY = {
     "replay": measure_replay,
     "capacity": measure_capacity,
     "batched": measure_batched,
+    "long_decode": measure_long_decode,
     "fetch_heavy": measure_fetch_heavy,
     "all_hit": measure_all_hit,
     "rows": measure_rows,
