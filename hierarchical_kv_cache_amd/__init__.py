@@ -56,7 +56,7 @@ EXPORTS = (
     "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_resolve_rows", "hs_bind_resident",
     "hs_writeback",
     "hs_prefetch_shared",
-    "hs_wait_layer", "hs_sparse_attn", "hs_resolve_attn", "hs_resolve_attn_wgs", "hs_export_state", "hs_page_table", "hs_plan", "hs_admit_short",
+    "hs_wait_layer", "hs_sparse_attn", "hs_sparse_attn_static", "hs_resolve_attn", "hs_resolve_attn_wgs", "hs_export_state", "hs_page_table", "hs_plan", "hs_admit_short",
     "hs_reset_request",
     "hs_destroy", "hs_last_error", "hs_resolve_wgs", "hs_probe_host_read", "hs_probe_copy",
     "hs_probe_host_records", "hs_probe_empty", "hs_timing_start", "hs_timing_read",
@@ -87,6 +87,7 @@ def _load():
         "hs_prefetch_shared": (i32, [vp, i32, vp, vp]),
         "hs_wait_layer": (i32, [vp, i32, vp]),
         "hs_sparse_attn": (i32, [vp, i32, vp, i32, i32, vp, vp, ctypes.c_float, vp, vp]),
+        "hs_sparse_attn_static": (i32, [vp, i32, vp, i32, i32, vp, vp, ctypes.c_float, vp, vp]),
         "hs_resolve_attn": (i32, [vp, i32, vp, vp, vp, vp, vp, u32, vp, i32, i32, vp, ctypes.c_float, vp]),
         "hs_resolve_attn_wgs": (i32, [vp]),
         "hs_export_state": (i32, [vp, i32, vp, vp, vp, vp, vp]),
@@ -167,6 +168,11 @@ def hs_wait_layer(h, layer, stream):
 def hs_sparse_attn(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num_reqs, stream):
     _check(_lib.hs_sparse_attn(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num_reqs or None,
                                stream or None))
+
+
+def hs_sparse_attn_static(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num_reqs, stream):
+    _check(_lib.hs_sparse_attn_static(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num_reqs or None,
+                                      stream or None))
 
 
 def hs_resolve_attn(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, d_q, heads, value_dim,

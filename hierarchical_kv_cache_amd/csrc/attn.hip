@@ -16,6 +16,7 @@
 // all 16 waves on v_mfma_f32_16x16x32_bf16 (scores split by key range, P V by
 // 32 output channels per wave).
 #include <algorithm>
+#include <mutex>
 
 #include "hs_internal.h"
 #include "hs_attend.h"
@@ -32,7 +33,7 @@ template <bool F8>
 __global__ void __launch_bounds__(kAT) attn_tiles_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char tile[kTileRows * kTileStride];
   __shared__ __attribute__((aligned(16))) unsigned char qs[16 * kQStride];
-  __shared__ __attribute__((aligned(16))) unsigned char scratch[F8 ? kAttnScratch8 : kAttnScratch];
+  __shared__ __attribute__((aligned(16))) unsigned char att_lds[F8 ? kAttnScratch8 : kAttnScratch];
   __shared__ uint64_t asrc[kAttnMaxChunk];  // record address of each chunk entry
   int r, s;
   if (p.R >= 8) {  // chunks of one request on one XCD (workgroups go round-robin over 8 XCDs)
@@ -75,14 +76,14 @@ __global__ void __launch_bounds__(kAT) attn_tiles_kernel(AttnParams p) {
   acc_init(acc);
   for (int t = 0; t < nt; ++t) {
     if (t > 0) __syncthreads();  // the previous tile's readers are done with the tile and P
-    if constexpr (F8) tile_store8(tv, tile, tile_scales8(scratch));
+    if constexpr (F8) tile_store8(tv, tile, tile_scales8(att_lds));
     else tile_store(tv, tile);
     if (t + 1 < nt) {  // flies during this tile's math
       if constexpr (F8) tile_load8(tv, asrc + (t + 1) * kTileRows);
       else tile_load(tv, asrc + (t + 1) * kTileRows);
     }
     __syncthreads();
-    attend_tile<F8>(tile, qs, scratch, min(kTileRows, n - t * kTileRows), sl2, acc);
+    attend_tile<F8>(tile, qs, att_lds, min(kTileRows, n - t * kTileRows), sl2, acc);
   }
   if (bad) {
     const float nan = __builtin_nanf("");
@@ -256,6 +257,37 @@ __global__ void __launch_bounds__(kFinishThreads) attn_finish_kernel(FinishParam
 }
 
 }  // namespace
+
+// ---- allocation-free attention (hs_sparse_attn_static) ------------------------------------
+// The chunk partials of hs_sparse_attn_static live in this file-scope device array instead of
+// the handle's workspace: kStaticAttnPartials partial records (16.8 MB), one copy per GPU,
+// held until the process ends.  Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address): attn_scratch_init takes each device's address
+// of it once, with that device current, and the launches use that address.
+static __device__ __align__(256) float scratch[(size_t)kStaticAttnPartials * kPartStride];
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+float* g_scratch_ptr[kScratchMaxDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t attn_scratch_init(int device) {
+  if (device < 0 || device >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[device] = (float*)ptr;
+  return hipSuccess;
+}
+
+float* attn_scratch(int device) {
+  if (device < 0 || device >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   const int grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * p.S : p.R * p.S;

@@ -306,6 +306,9 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
   }
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetDevice"); }
+  // this device's address of the allocation-free attention's partials (once per device)
+  e = attn_scratch_init(h->device);
+  if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetSymbolAddress(attention scratch)"); }
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, h->device);
   if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetDeviceProperties"); }
@@ -623,9 +626,14 @@ hs_status hs_wait_layer(hs_handle h, int32_t layer, void* stream) {
   return HS_OK;
 }
 
-hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t heads, int32_t value_dim,
-                         const int32_t* d_slots, float* d_out, float scale, const int32_t* d_num_reqs,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The attention launch of one layer (hs_sparse_attn and hs_sparse_attn_static), after the
+// argument checks; partials in the handle's workspace.
+hs_status attn_params(hs_ctx* h, int32_t layer, const void* d_q, int32_t heads, int32_t value_dim,
+                      const int32_t* d_slots, float* d_out, float scale, const int32_t* d_num_reqs, AttnParams* out) {
   hs_status st;
   if ((st = check_handle(h)) || (st = check_layer(h, layer))) return st;
   const bool fp8 = (h->cfg.flags & HS_CFG_RECORD_FP8) != 0;
@@ -647,6 +655,40 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
   p.S = (h->cfg.top_k + p.chunk - 1) / p.chunk;  // no empty chunk
   p.rec_bytes = h->cfg.record_bytes; p.scale = scale; p.fp8 = fp8 ? 1 : 0;
   p.zero = h->ws + h->lay.att_zero;
+  *out = p;
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t heads, int32_t value_dim,
+                         const int32_t* d_slots, float* d_out, float scale, const int32_t* d_num_reqs,
+                         void* stream) {
+  AttnParams p;
+  const hs_status st = attn_params(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num_reqs, &p);
+  if (st) return st;
+  HS_HIP(launch_attn(p, (hipStream_t)stream));
+  return HS_OK;
+}
+
+hs_status hs_sparse_attn_static(hs_handle h, int32_t layer, const void* d_q, int32_t heads, int32_t value_dim,
+                                const int32_t* d_slots, float* d_out, float scale, const int32_t* d_num_reqs,
+                                void* stream) {
+  AttnParams p;
+  const hs_status st = attn_params(h, layer, d_q, heads, value_dim, d_slots, d_out, scale, d_num_reqs, &p);
+  if (st) return st;
+  // the partials go to the file-scope device array (the S chunks of every request)
+  if (p.S > 1 && int64_t(p.R) * p.S > kStaticAttnPartials)  // (one chunk: the output is written directly)
+    return fail(HS_EINVAL, "hs_sparse_attn_static: %d requests x %d chunks need %lld partial records, the "
+                "static scratch holds %d", p.R, p.S, (long long)p.R * p.S, kStaticAttnPartials);
+  int dev = -1;
+  HS_HIP(hipGetDevice(&dev));
+  if (dev != h->device) return fail(HS_ESTATE, "hs_sparse_attn_static: device %d is current, the handle's is %d", dev,
+                                    h->device);
+  p.part = attn_scratch(h->device);
+  if (!p.part) return fail(HS_ESTATE, "hs_sparse_attn_static: no scratch address for device %d", h->device);
   HS_HIP(launch_attn(p, (hipStream_t)stream));
   return HS_OK;
 }

@@ -341,5 +341,9 @@ constexpr int kAttnDv = 512;
 constexpr int kPartStride = kAttnMaxHeads * kAttnDv + 2 * kAttnMaxHeads;
 constexpr int kAttnMaxChunks = 256;  // top_k <= 16384 in chunks of >= 64 entries
 constexpr int kAttnMaxChunk = 1024;  // entries per chunk (their slots are staged in LDS)
+// allocation-free attention: partial records in a file-scope device array of attn.hip
+constexpr int kStaticAttnPartials = 512;
+hipError_t attn_scratch_init(int device);  // with `device` current; once per device
+float* attn_scratch(int device);           // that device's address of the array (null before init)
 
 }  // namespace hs

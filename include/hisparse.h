@@ -260,6 +260,22 @@ hs_status hs_sparse_attn(hs_handle h, int32_t layer, const void* d_q, int32_t he
                          const int32_t* d_num_reqs, void* stream);
 
 /*
+ * hs_sparse_attn for callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the same arguments, the same
+ * kernels and the same output bit for bit, but the per-chunk attention partials go to a
+ * file-scope device array of the library (held on each GPU until the process ends) instead of
+ * the handle's workspace.  The call allocates nothing.  Limit: num_requests x chunks per
+ * request <= 512 partial records (16.8 MB) when a request has more than one chunk (chunks per
+ * request: min(ceil(256 / R), ceil(k / 64)), at least ceil(k / 1024)); otherwise HS_EINVAL.
+ * HS_ESTATE unless the handle's device is current.  Every call on one GPU shares that array: calls that overlap on one GPU (different
+ * streams, not ordered) race; calls ordered on one stream do not (each call's partials are
+ * written before its merge reads them, so nothing needs clearing).
+ */
+hs_status hs_sparse_attn_static(hs_handle h, int32_t layer, const void* d_q, int32_t heads,
+                                int32_t value_dim, const int32_t* d_slots, float* d_out, float scale,
+                                const int32_t* d_num_reqs, void* stream);
+
+/*
  * RESOLVE of one anchor layer and the sparse attention over its published slots, in one
  * kernel where the configuration allows ([GC] §3.5 for the resolve, §5.4 for the attention
  * that reads the slots aligned with the top-k order).  Results are those of
