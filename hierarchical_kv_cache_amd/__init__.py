@@ -70,6 +70,13 @@ class HsError(RuntimeError):
 
 
 def _load():
+    # torch ships a HIP runtime of its own: when torch is installed it is loaded first, so that
+    # the library's libamdhip64 dependency resolves to that same runtime (two runtimes in one
+    # process do not see each other's devices, streams or allocations)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError("libhisparse.so is not built: run hierarchical_kv_cache_amd._build.build() "
                           "(or __graft_entry__.build())")
