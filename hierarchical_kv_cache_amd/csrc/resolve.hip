@@ -154,12 +154,15 @@ struct Run16 {
 template <int E>
 __device__ __forceinline__ void load_run16(const int16_t* __restrict__ src, int n, int base, bool vec,
                                            Run16<E>& out, int16_t fill) {
-  if constexpr (E >= 4) {
+  if constexpr (E >= 4 && E % 4 == 0) {
     if (vec && base + E <= n) {
-      if constexpr (E == 4) {
-        const u32x2 x = *(const u32x2*)(src + base);
-        out.w[0] = x[0];
-        out.w[1] = x[1];
+      if constexpr (E % 8 != 0) {  // E = 4, 12: the run starts 8-byte aligned (8-byte loads)
+#pragma unroll
+        for (int v = 0; v < E / 4; ++v) {
+          const u32x2 x = *((const u32x2*)(src + base) + v);
+          out.w[2 * v] = x[0];
+          out.w[2 * v + 1] = x[1];
+        }
       } else {
 #pragma unroll
         for (int v = 0; v < E / 8; ++v) {
@@ -221,10 +224,11 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   const int H = 1 << p.hash_bits;
   const uint32_t hmask = (uint32_t)H - 1;
   const int e0 = tid * E;  // first slot / LRU position of this thread
-  const int EK = (p.k + NT - 1) / NT;
-  const int i0 = tid * EK;  // first selection entry of this thread
-  // entries of this request's list (a speculative union is shorter than its k-entry row)
+  // entries of this request's list (a speculative union is shorter than its k-entry row), spread
+  // over all threads: EK = ceil(kr / NT) <= KE consecutive entries per thread
   const int kr = p.kvar ? min(p.kvar[r], p.k) : p.k;
+  const int EK = (kr + NT - 1) / NT;
+  const int i0 = tid * EK;  // first selection entry of this thread
   const uint32_t pre_err = p.kerr ? p.kerr[r] : 0u;
   if (pre_err) {  // found before the launch (the union of verification rows): nothing changes
     if (g == 0) {
@@ -265,32 +269,31 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     const int i = i0 + j;
     raw[j] = (j < EK && i < kr) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
   }
-  // Fetch workgroups (all but workgroup 0 when G > 1) also read the selection entries of
+  // Fetch-only workgroups (g > 0 of a launch with several) also read the selection entries of
   // their share of the list, spread over the waves: entry e of the share belongs to wave
-  // e % NW, lane (e / NW) % 64, slot e / NT.
+  // e % NW, lane (e / NW) % 64, slot e / NT.  Slot 0 is read at entry with everything else;
+  // a share longer than NT entries (a long speculative union over few workgroups) reads its
+  // further slots at the fetch stage.  A one-workgroup launch (G = 1) takes its misses from
+  // its own classified entries instead.
   const bool io = !(p.flags & HS_SKIP_IO);
   const bool fetcher = !ATT && io && (p.G == 1 || g > 0);  // (the fused kernel's fetch workgroups
                                                            // do not run this function)
+  const bool share_fetch = fetcher && g > 0;
   const int nf = p.G > 1 ? p.G - 1 : 1;
   const int gf = p.G > 1 ? g - 1 : 0;
   // (32-bit: k * G < 2^23)
   const int f_lo = kr * gf / nf;
   const int f_n = kr * (gf + 1) / nf - f_lo;
   const int wid = tid >> 6, lane = tid & 63;
-  // With 8 or more list entries per thread these share arrays would stay live through
-  // stages 1-2 beside the stage arrays: then they are read just before the fetch stage.
-  constexpr bool kEarlyShare = KE < 8;
-  int32_t fraw[KE];
-  auto share_sel = [&]() {
-#pragma unroll
-    for (int q = 0; q < KE; ++q) {
-      const int e = q * NT + lane * NW + wid;
-      const int i = f_lo + e;
-      fraw[q] = (fetcher && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
-    }
+  auto share_raw = [&](int q) -> int32_t {
+    const int e = q * NT + lane * NW + wid;
+    const int i = f_lo + e;
+    return (share_fetch && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
   };
-  if constexpr (kEarlyShare) share_sel();
-  const bool bvec = (p.B % E) == 0;
+  const int32_t fraw0 = share_raw(0);
+  // vector loads and stores of a thread's run: every half of the slot map starts 16-byte aligned
+  // when B is a multiple of 4 (the LRU halves are padded to 8 entries)
+  const bool bvec = (p.B % 4) == 0;
   // Both halves of the slot map are read here, before the launch counter says which one is
   // current, so they share the first round trip.  With 8 or more slots per thread they
   // would hold too many registers until the publish, which then reads the current half.
@@ -368,23 +371,25 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   // Misses known early from the page table: a selected position whose entry is -1 (and
   // that the resident tier does not serve) is not on the device.  Their host loads start
   // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
-  int32_t fpos[KE], fres[KE];
-  uint64_t fpt[KE];
-  auto share_pt = [&]() {
-#pragma unroll
-    for (int q = 0; q < KE; ++q) {
-      const int e = q * NT + lane * NW + wid;
-      const int i = f_lo + e;
-      int64_t pos64 = -1;
-      if (fetcher && e < f_n)
-        pos64 = p.bt_shift ? ((int64_t)fraw[q] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fraw[q];
-      const bool ok = pos64 >= 0 && pos64 < ctx;
-      fpos[q] = ok ? (int32_t)pos64 : -1;
-      fpt[q] = ok ? ptr[pos64] : kPtHostOnly;
-      fres[q] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
-    }
+  // a share entry's position, page-table entry and resident page (slot q, its raw selection)
+  struct ShareEntry {
+    int32_t pos, res;
+    uint64_t pt;
   };
-  if constexpr (kEarlyShare) share_pt();
+  auto share_entry = [&](int q, int32_t fr) -> ShareEntry {
+    const int e = q * NT + lane * NW + wid;
+    const int i = f_lo + e;
+    int64_t pos64 = -1;
+    if (share_fetch && e < f_n)
+      pos64 = p.bt_shift ? ((int64_t)fr << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)fr;
+    const bool ok = pos64 >= 0 && pos64 < ctx;
+    ShareEntry se;
+    se.pos = ok ? (int32_t)pos64 : -1;
+    se.pt = ok ? ptr[pos64] : kPtHostOnly;
+    se.res = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
+    return se;
+  };
+  const ShareEntry f0 = share_entry(0, fraw0);
   {
     u32x4* h4 = (u32x4*)htab;
     const u32x4 e4 = {~0u, ~0u, ~0u, ~0u};
@@ -547,36 +552,43 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     }
   }
   // ---- stage 4, first part: per-wave lists of the page-table misses, host loads issued ----
-  if constexpr (!kEarlyShare) {
-    share_sel();
-    share_pt();
-  }
   int32_t* wpos = (int32_t*)(smem + Ly.wpos) + wid * Ly.wcap;  // this wave's misses: position
   int16_t* widx = (int16_t*)(smem + Ly.widx) + wid * Ly.wcap;  // and list index
   const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
   const float invC = 1.0f / (float)C;
   int mw = 0;  // misses of this wave
-  {
-#pragma unroll
-    for (int q = 0; q < KE; ++q) {
-      const bool miss = fpos[q] >= 0 && fpos[q] != newest && fres[q] < 0 && pt_slot_for(fpt[q], gen) < 0;
-      const uint64_t b = __ballot(miss);
-      if (miss) {
-        const int at = mw + lanes_below(b);
-        wpos[at] = fpos[q];
-        widx[at] = (int16_t)(f_lo + q * NT + lane * NW + wid);
-      }
-      mw += __popcll(b);
+  auto append = [&](bool miss, int32_t pos, int i) {
+    const uint64_t b = __ballot(miss);
+    if (miss) {
+      const int at = mw + lanes_below(b);
+      wpos[at] = pos;
+      widx[at] = (int16_t)i;
     }
+    mw += __popcll(b);
+  };
+  auto share_miss = [&](const ShareEntry& se) {
+    return se.pos >= 0 && se.pos != newest && se.res < 0 && pt_slot_for(se.pt, gen) < 0;
+  };
+  if (share_fetch) {
+    append(share_miss(f0), f0.pos, f_lo + lane * NW + wid);
+    for (int q = 1; q * NT < f_n; ++q) {  // (the same bound in every wave)
+      const ShareEntry se = share_entry(q, share_raw(q));
+      append(share_miss(se), se.pos, f_lo + q * NT + lane * NW + wid);
+    }
+  } else if (fetcher) {  // one workgroup per request: its own entries' misses
+#pragma unroll
+    for (int j = 0; j < KE; ++j) append(j < EK && i0 + j < kr && cls[j] == -1, key[j], i0 + j);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int wtotal = mw * C;  // 16-byte chunks of this wave's misses
+  // Only a fetch-only workgroup (g > 0) loads early: with one workgroup per request, workgroup 0
+  // loads its misses after the publish, so these registers are not held through it.
   u32x4 early[kEarly];
 #pragma unroll
   for (int u = 0; u < kEarly; ++u) {
     const int c = lane + 64 * u;
-    if (c < wtotal) {
+    if (g > 0 && c < wtotal) {
       int l = (int)((float)c * invC);
       int cc = c - l * C;
       if (cc < 0) { --l; cc += C; }
@@ -614,15 +626,20 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
                            g == 0 ? (1ull << kLaunchShift) - (ATT ? 0ull : (uint64_t)(p.G - 1)) : 1ull,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- stage 3: misses in list order and evictables in LRU order, one scan -------------
+  // the entries served without a fetch (hit slot, newest slot, resident row) are published now,
+  // and the misses flagged, so the per-entry classes are not held through stage 3 and publish
   uint32_t mbits = 0, ebits = 0;
+#pragma unroll
+  for (int j = 0; j < KE; ++j) {
+    if (cls[j] == -1) mbits |= 1u << j;
+    if (g == 0 && cls[j] >= 0) p.out[(size_t)r * p.k + i0 + j] = cls[j];
+  }
+
+  // ---- stage 3: misses in list order and evictables in LRU order, one scan -------------
   {
     int16_t sf[E];
 #pragma unroll
     for (int j = 0; j < E; ++j) sf[j] = sown[lro[j]];
-#pragma unroll
-    for (int j = 0; j < KE; ++j)
-      if (cls[j] == -1) mbits |= 1u << j;
 #pragma unroll
     for (int j = 0; j < E; ++j)
       if (e0 + j < p.B && sf[j] == -1) ebits |= 1u << j;
@@ -649,112 +666,11 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   }
   __syncthreads();
 
-  // with several workgroups, workgroup 0 publishes while the others fetch
-  if (g == 0) {
-    int32_t spo[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) spo[j] = kEarlySlotMap ? (h1 ? spb[j] : spa[j]) : -1;
-    if constexpr (!kEarlySlotMap) load_run32<E>(p.slot_pos + ((size_t)r * 2 + (h1 ? 1 : 0)) * p.B, p.B, e0, bvec, spo, -1);
-    int32_t* sp_new = p.slot_pos + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.B;
-    // filled victims, then hits, each by slot index, after the untouched evictables
-    int16_t fo[E];
-    int32_t hp[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) fo[j] = (e0 + j < p.B) ? sown[e0 + j] : (int16_t)-1;
-#pragma unroll
-    for (int j = 0; j < E; ++j) hp[j] = selp[fo[j] >= 0 ? fo[j] : 0];
-    uint32_t vb = 0, hb = 0, bad = 0;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      vb |= (uint32_t)(fo[j] <= -2) << j;
-      hb |= (uint32_t)(fo[j] >= 0) << j;
-      bad |= (uint32_t)(fo[j] >= 0 && hp[j] != spo[j]);  // a hit's slot must hold its position
-    }
-    if (bad) atomicOr((unsigned*)&sh[3], HS_ERR_STATE);
-    int rv, rh, tv, th;
-    block_ranks2<E>(vb, hb, carry + 2 * NW, rv, rh, tv, th);
-    uint64_t* pt = p.page_table + (size_t)r * p.max_positions;
-    int32_t* outr = p.out + (size_t)r * p.k;
-    int32_t* plan_pos = p.plan + (size_t)r * 2 * p.plan_k;
-    int32_t* plan_slot = plan_pos + p.plan_k;
-
-    // ---- stage 5: publish (every value is already on chip) ----
-    int32_t spn[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int s = e0 + j;
-      spn[j] = spo[j];
-      if (s >= p.B) continue;
-      if ((vb >> j) & 1u) {
-        lru_new[E_ - m + rv++] = (int16_t)s;
-        const int jm = -2 - fo[j];
-        const int i = missidx[jm];
-        const int32_t np = selp[i];
-        if constexpr (ATT) {  // the finish kernel applies it
-          const u32x4 e = {(uint32_t)i, (uint32_t)s, (uint32_t)spo[j], (uint32_t)np};
-          *(u32x4*)(p.att_mlist + ((size_t)r * p.k + jm) * 4) = e;
-        } else {
-          if (spo[j] >= 0) pt[spo[j]] = kPtHostOnly;  // the evicted position is host-only again
-          pt[np] = pt_entry(s, gen);
-        }
-        spn[j] = np;
-        outr[i] = s;
-        if (record) {
-          plan_pos[jm] = np;
-          plan_slot[jm] = s;
-        }
-      } else if ((hb >> j) & 1u) {
-        lru_new[E_ + rh++] = (int16_t)s;
-      }
-    }
-    bool stored = false;
-    if constexpr (E % 4 == 0) {
-      if (bvec && e0 + E <= p.B) {
-#pragma unroll
-        for (int v = 0; v < E / 4; ++v) {
-          const u32x4 x = {(uint32_t)spn[4 * v], (uint32_t)spn[4 * v + 1], (uint32_t)spn[4 * v + 2],
-                           (uint32_t)spn[4 * v + 3]};
-          *((u32x4*)(sp_new + e0) + v) = x;
-        }
-        stored = true;
-      }
-    }
-    if (!stored) {
-#pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (e0 + j < p.B) sp_new[e0 + j] = spn[j];
-    }
-#pragma unroll
-    for (int j = 0; j < KE; ++j)
-      if (cls[j] >= 0) outr[i0 + j] = cls[j];
-    if (tid == 0) {
-      if (p.stats) {
-        hs_stats st = {(uint32_t)(kr - m - nres), (uint32_t)m, (uint32_t)sh[3], (uint32_t)nres,
-                        io ? (uint64_t)m * (uint64_t)p.rec_bytes : 0ull};
-        p.stats[r] = st;
-      }
-      if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;
-      if (ATT) { hdr[0] = 0u; hdr[1] = (uint32_t)m; hdr[2] = gen; }
-    }
-    if (p.G > 1) return;
-  }
-
-  // ---- stage 4, second part: the fetched records go to the slots stage 3 chose --------
-  if (fetcher) {
-#pragma unroll
-    for (int u = 0; u < kEarly; ++u) {
-      const int c = lane + 64 * u;
-      if (c < wtotal) {
-        int l = (int)((float)c * invC);
-        int cc = c - l * C;
-        if (cc < 0) { --l; cc += C; }
-        if (cc >= C) { ++l; cc -= C; }
-        const int slot = victim[mrank[widx[l]]];
-        *((u32x4*)(dbase + (size_t)slot * (size_t)p.rec_bytes) + cc) = early[u];
-      }
-    }
-    // a wave with more than kEarly chunks per lane (miss-heavy steps) continues here
-    for (int c0 = lane + 64 * kEarly; c0 < wtotal; c0 += 64 * kUnroll) {
+  // this wave's missed chunks from c_first on (stride 64 per lane): host loads, then stores
+  // into the victim slots stage 3 chose (a wave with more than kEarly chunks per lane, or
+  // workgroup 0 of a one-workgroup launch, which loads none early)
+  auto late_fetch = [&](int c_first) {
+    for (int c0 = c_first; c0 < wtotal; c0 += 64 * kUnroll) {
       u32x4 v[kUnroll];
       int ll[kUnroll], cc[kUnroll];
 #pragma unroll
@@ -775,6 +691,109 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
         if (c0 + 64 * u < wtotal)
           *((u32x4*)(dbase + (size_t)victim[mrank[widx[ll[u]]]] * (size_t)p.rec_bytes) + cc[u]) = v[u];
     }
+  };
+
+  // with several workgroups, workgroup 0 publishes while the others fetch
+  if (g == 0) {
+    int32_t spo[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) spo[j] = kEarlySlotMap ? (h1 ? spb[j] : spa[j]) : -1;
+    if constexpr (!kEarlySlotMap) load_run32<E>(p.slot_pos + ((size_t)r * 2 + (h1 ? 1 : 0)) * p.B, p.B, e0, bvec, spo, -1);
+    int32_t* sp_new = p.slot_pos + ((size_t)r * 2 + (h1 ? 0 : 1)) * p.B;
+    // filled victims, then hits, each by slot index, after the untouched evictables (the owner
+    // of each slot is read from the LDS owner array here and again in the publish loop, so no
+    // per-slot array is held across the rank scan beside the slot map)
+    uint32_t vb = 0, hb = 0, bad = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int16_t fo = (e0 + j < p.B) ? sown[e0 + j] : (int16_t)-1;
+      const int32_t hp = selp[fo >= 0 ? fo : 0];
+      vb |= (uint32_t)(fo <= -2) << j;
+      hb |= (uint32_t)(fo >= 0) << j;
+      bad |= (uint32_t)(fo >= 0 && hp != spo[j]);  // a hit's slot must hold its position
+    }
+    if (bad) atomicOr((unsigned*)&sh[3], HS_ERR_STATE);
+    int rv, rh, tv, th;
+    block_ranks2<E>(vb, hb, carry + 2 * NW, rv, rh, tv, th);
+    uint64_t* pt = p.page_table + (size_t)r * p.max_positions;
+    int32_t* outr = p.out + (size_t)r * p.k;
+    int32_t* plan_pos = p.plan + (size_t)r * 2 * p.plan_k;
+    int32_t* plan_slot = plan_pos + p.plan_k;
+
+    // ---- stage 5: publish (every value is already on chip); spo becomes the new slot map ----
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int s = e0 + j;
+      if (s >= p.B) continue;
+      if ((vb >> j) & 1u) {
+        lru_new[E_ - m + rv++] = (int16_t)s;
+        const int jm = -2 - sown[s];
+        const int i = missidx[jm];
+        const int32_t np = selp[i];
+        if constexpr (ATT) {  // the finish kernel applies it
+          const u32x4 e = {(uint32_t)i, (uint32_t)s, (uint32_t)spo[j], (uint32_t)np};
+          *(u32x4*)(p.att_mlist + ((size_t)r * p.k + jm) * 4) = e;
+        } else {
+          if (spo[j] >= 0) pt[spo[j]] = kPtHostOnly;  // the evicted position is host-only again
+          pt[np] = pt_entry(s, gen);
+        }
+        spo[j] = np;
+        outr[i] = s;
+        if (record) {
+          plan_pos[jm] = np;
+          plan_slot[jm] = s;
+        }
+      } else if ((hb >> j) & 1u) {
+        lru_new[E_ + rh++] = (int16_t)s;
+      }
+    }
+    bool stored = false;
+    if constexpr (E % 4 == 0) {
+      if (bvec && e0 + E <= p.B) {
+#pragma unroll
+        for (int v = 0; v < E / 4; ++v) {
+          const u32x4 x = {(uint32_t)spo[4 * v], (uint32_t)spo[4 * v + 1], (uint32_t)spo[4 * v + 2],
+                           (uint32_t)spo[4 * v + 3]};
+          *((u32x4*)(sp_new + e0) + v) = x;
+        }
+        stored = true;
+      }
+    }
+    if (!stored) {
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (e0 + j < p.B) sp_new[e0 + j] = spo[j];
+    }
+    if (tid == 0) {
+      if (p.stats) {
+        hs_stats st = {(uint32_t)(kr - m - nres), (uint32_t)m, (uint32_t)sh[3], (uint32_t)nres,
+                        io ? (uint64_t)m * (uint64_t)p.rec_bytes : 0ull};
+        p.stats[r] = st;
+      }
+      if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;
+      if (ATT) { hdr[0] = 0u; hdr[1] = (uint32_t)m; hdr[2] = gen; }
+    }
+    if (p.G > 1 || !fetcher) return;
+    late_fetch(lane);  // one workgroup per request: workgroup 0 copies every miss itself
+    return;
+  }
+
+  // ---- stage 4, second part (fetch-only workgroups): the early chunks go to the slots stage 3
+  // chose, then the rest of this wave's misses
+  if (fetcher) {
+#pragma unroll
+    for (int u = 0; u < kEarly; ++u) {
+      const int c = lane + 64 * u;
+      if (c < wtotal) {
+        int l = (int)((float)c * invC);
+        int cc = c - l * C;
+        if (cc < 0) { --l; cc += C; }
+        if (cc >= C) { ++l; cc -= C; }
+        const int slot = victim[mrank[widx[l]]];
+        *((u32x4*)(dbase + (size_t)slot * (size_t)p.rec_bytes) + cc) = early[u];
+      }
+    }
+    late_fetch(lane + 64 * kEarly);
   }
 }
 
@@ -1119,6 +1138,10 @@ hipError_t set_limit_ke(int v) {
 int resolve_elems_per_thread(int k, int B) {
   const int n = (k > B ? k : B);
   const int e = (n + NT - 1) / NT;
+  // 12 slots per thread for 8192 < B <= 12288 (with at most 8 list entries per thread): the
+  // power of two 16 would leave a quarter or more of the threads without slots and every
+  // thread's slot arrays a third larger
+  if (e > 8 && e <= 12 && k <= 8 * NT) return 12;
   int E = 1;
   while (E < e) E <<= 1;
   return E;
@@ -1137,6 +1160,7 @@ hipError_t set_resolve_lds_limit(size_t lds_bytes) {
   if ((e = set_limit_ke<2>(v)) != hipSuccess) return e;
   if ((e = set_limit_ke<4>(v)) != hipSuccess) return e;
   if ((e = set_limit_ke<8>(v)) != hipSuccess) return e;
+  if ((e = set_limit_ke<12>(v)) != hipSuccess) return e;
   return set_limit_ke<16>(v);
 }
 
@@ -1164,6 +1188,7 @@ hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t 
     case 2: return launch_ke<2, false>(p, lds_bytes, s, KE, tm);
     case 4: return launch_ke<4, false>(p, lds_bytes, s, KE, tm);
     case 8: return launch_ke<8, false>(p, lds_bytes, s, KE, tm);
+    case 12: return launch_ke<12, false>(p, lds_bytes, s, KE, tm);
     default: return launch_ke<16, false>(p, lds_bytes, s, KE, tm);
   }
 }
