@@ -555,7 +555,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   int32_t* wpos = (int32_t*)(smem + Ly.wpos) + wid * Ly.wcap;  // this wave's misses: position
   int16_t* widx = (int16_t*)(smem + Ly.widx) + wid * Ly.wcap;  // and list index
   const int C = p.rec_bytes >> 4;  // 16-byte chunks per record
-  const float invC = 1.0f / (float)C;
+  const float invC = __builtin_amdgcn_rcpf((float)C);  // (the +-1 corrections below absorb its error)
   int mw = 0;  // misses of this wave
   auto append = [&](bool miss, int32_t pos, int i) {
     const uint64_t b = __ballot(miss);
@@ -583,10 +583,14 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int wtotal = mw * C;  // 16-byte chunks of this wave's misses
   // Only a fetch-only workgroup (g > 0) loads early: with one workgroup per request, workgroup 0
-  // loads its misses after the publish, so these registers are not held through it.
-  u32x4 early[kEarly];
+  // loads its misses after the publish, so these registers are not held through it.  With 12
+  // or more slots, or 8 list entries, per thread the registers would not last through stage 3
+  // (the compiler then waits for each load and spills its value), so those layouts load none
+  // early.
+  constexpr int kEarlyN = (E >= 12 || KE >= 8) ? 0 : kEarly;
+  u32x4 early[kEarlyN > 0 ? kEarlyN : 1];
 #pragma unroll
-  for (int u = 0; u < kEarly; ++u) {
+  for (int u = 0; u < kEarlyN; ++u) {
     const int c = lane + 64 * u;
     if (g > 0 && c < wtotal) {
       int l = (int)((float)c * invC);
@@ -782,7 +786,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   // chose, then the rest of this wave's misses
   if (fetcher) {
 #pragma unroll
-    for (int u = 0; u < kEarly; ++u) {
+    for (int u = 0; u < kEarlyN; ++u) {
       const int c = lane + 64 * u;
       if (c < wtotal) {
         int l = (int)((float)c * invC);
@@ -793,7 +797,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
         *((u32x4*)(dbase + (size_t)slot * (size_t)p.rec_bytes) + cc) = early[u];
       }
     }
-    late_fetch(lane + 64 * kEarly);
+    late_fetch(lane + 64 * kEarlyN);
   }
 }
 
