@@ -23,9 +23,9 @@ from . import _build
 LIB_PATH = _build.LIB
 
 HS_OK, HS_EINVAL, HS_ENOMEM, HS_EHIP, HS_ESTATE = 0, -1, -2, -3, -4
-HS_CFG_NEWEST_SLOT, HS_CFG_RECORD_FP8 = 1, 2
+HS_CFG_NEWEST_SLOT, HS_CFG_RECORD_FP8, HS_CFG_HOT_ON_DEMAND = 1, 2, 4
 HS_RECORD_PLAN, HS_SKIP_IO = 1, 2
-HS_ERR_DUP, HS_ERR_RANGE, HS_ERR_STATE, HS_ERR_RESIDENT = 1, 2, 4, 8
+HS_ERR_DUP, HS_ERR_RANGE, HS_ERR_STATE, HS_ERR_RESIDENT, HS_ERR_CAPACITY = 1, 2, 4, 8, 16
 
 
 class hs_config(ctypes.Structure):
@@ -53,7 +53,8 @@ assert HS_STATS_DTYPE.itemsize == 4 * HS_STATS_WORDS
 
 # every symbol include/hisparse.h declares
 EXPORTS = (
-    "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_resolve", "hs_resolve_rows", "hs_bind_resident",
+    "hs_workspace_bytes", "hs_create", "hs_host_pool", "hs_hot_buffer", "hs_grow_request", "hs_hot_backed_bytes",
+    "hs_resolve", "hs_resolve_rows", "hs_bind_resident",
     "hs_writeback",
     "hs_prefetch_shared",
     "hs_wait_layer", "hs_sparse_attn", "hs_sparse_attn_static", "hs_resolve_attn", "hs_resolve_attn_wgs", "hs_export_state", "hs_page_table", "hs_plan", "hs_admit_short",
@@ -87,6 +88,9 @@ def _load():
         "hs_workspace_bytes": (sz, [cfgp]),
         "hs_create": (i32, [cfgp, vp, vp, ctypes.POINTER(vp)]),
         "hs_host_pool": (vp, [vp, i32]),
+        "hs_hot_buffer": (vp, [vp]),
+        "hs_grow_request": (i32, [vp, i32, i32, vp]),
+        "hs_hot_backed_bytes": (i64, [vp]),
         "hs_resolve": (i32, [vp, i32, vp, vp, vp, vp, vp, u32, vp]),
         "hs_resolve_rows": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, u32, vp]),
         "hs_bind_resident": (i32, [vp, vp, i32, i32, vp, i64]),
@@ -143,6 +147,18 @@ def hs_create(cfg: hs_config, d_hot: int, d_workspace: int) -> int:
 
 def hs_host_pool(h: int, request: int) -> int:
     return _lib.hs_host_pool(h, request) or 0
+
+
+def hs_hot_buffer(h) -> int:
+    return _lib.hs_hot_buffer(h) or 0
+
+
+def hs_grow_request(h, request, slots, stream):
+    _check(_lib.hs_grow_request(h, request, slots, stream or None))
+
+
+def hs_hot_backed_bytes(h) -> int:
+    return _lib.hs_hot_backed_bytes(h)
 
 
 def hs_resolve(h, layer, d_sel, d_ctx_len, d_slots_out, d_stats, d_num_reqs, flags, stream):
@@ -263,8 +279,9 @@ def hs_timing_read(h, n) -> np.ndarray:
 # ---- convenience owner --------------------------------------------------------------------
 
 def make_config(R, L, max_positions, top_k, buffer_slots, record_bytes=1152, block_tokens=1, layer_group=1,
-                wgs_per_request=0, newest_slot=False, fp8=False, verify_rows=0) -> hs_config:
-    flags = (HS_CFG_NEWEST_SLOT if newest_slot else 0) | (HS_CFG_RECORD_FP8 if fp8 else 0)
+                wgs_per_request=0, newest_slot=False, fp8=False, verify_rows=0, hot_on_demand=False) -> hs_config:
+    flags = (HS_CFG_NEWEST_SLOT if newest_slot else 0) | (HS_CFG_RECORD_FP8 if fp8 else 0) | \
+        (HS_CFG_HOT_ON_DEMAND if hot_on_demand else 0)
     return hs_config(R, L, max_positions, 656 if fp8 else record_bytes, top_k, block_tokens, buffer_slots,
                      layer_group, wgs_per_request, flags, verify_rows)
 
@@ -279,9 +296,13 @@ class HiSparse:
         self.rec = cfg.record_bytes
         self.max_positions = cfg.max_positions
         ws_bytes = hs_workspace_bytes(cfg)
-        self.hot = torch.empty((self.R, self.L, self.B + 1, self.rec), dtype=torch.uint8, device=device)
+        # with HS_CFG_HOT_ON_DEMAND the library reserves the hot buffer (hot_address; no tensor)
+        on_demand = bool(cfg.flags & HS_CFG_HOT_ON_DEMAND)
+        self.hot = None if on_demand else \
+            torch.empty((self.R, self.L, self.B + 1, self.rec), dtype=torch.uint8, device=device)
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
-        self.h = hs_create(cfg, self.hot.data_ptr(), self.workspace.data_ptr())
+        self.h = hs_create(cfg, 0 if on_demand else self.hot.data_ptr(), self.workspace.data_ptr())
+        self.hot_address = hs_hot_buffer(self.h)
 
     def host_pool(self, request: int) -> np.ndarray:
         """numpy view [L][max_positions][record_bytes] of request's pinned region."""

@@ -55,12 +55,14 @@ __global__ void __launch_bounds__(kAT) attn_tiles_kernel(AttnParams p) {
   u32x4 qv[kQU];
   q_load(qv, p.q, r, p.heads);
   int bad = 0;
+  // the newest slot and the backed LRU slots (all of them, unless the hot buffer is on demand)
+  const int capr = p.cap ? p.cap[r] : p.B;
   if (tid < nt * kTileRows) {
     const uint8_t* src = filler;
     if (tid < n) {
       const int sl = p.slots[(size_t)r * p.k + t_begin + tid];
       const int64_t rr = (int64_t)sl - (p.B + 1);
-      if (sl >= 0 && sl <= p.B) src = hot_r + (size_t)sl * p.rec_bytes;
+      if (sl >= 0 && (sl < capr || sl == p.B)) src = hot_r + (size_t)sl * p.rec_bytes;
       else if (rr >= 0 && rr < p.res_rows) src = p.res + (size_t)rr * p.rec_bytes;
       else bad = 1;
     }

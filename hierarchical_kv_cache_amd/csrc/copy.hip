@@ -47,7 +47,8 @@ __global__ void __launch_bounds__(kCopyThreads) append_kernel(AppendParams p) {
       store_host16(v, row + 16 * (size_t)c);
     }
     // a short request keeps its tokens in slot order while they fit ("HiSparse 深度解析" §5.4)
-    const bool in_order = p.ctrl[r * 4 + 3] != 0 && pos < p.B;
+    // (on an on-demand hot buffer, only into a backed slot: the caller grows the request first)
+    const bool in_order = p.ctrl[r * 4 + 3] != 0 && pos < p.B && (!p.cap || pos < p.cap[r]);
     if (in_order) *((u32x4*)(p.hot + (((size_t)r * p.L + l) * (p.B + 1) + pos) * p.rec_bytes) + c) = v;
     if (rest == 0) {
       p.newest[r] = pos;
@@ -322,6 +323,8 @@ __global__ void __launch_bounds__(kCopyThreads) probe_host_records_kernel(const 
 
 __global__ void probe_empty_kernel() {}
 
+__global__ void set_capacity_kernel(int32_t* cap, int r, int slots) { cap[r] = slots; }
+
 int grid_for(size_t work, int per_block, int cap) {
   size_t b = (work + per_block - 1) / per_block;
   if (b < 1) b = 1;
@@ -391,6 +394,11 @@ hipError_t launch_probe_host_records(const void* src, const int32_t* index, int 
                                      int64_t src_records, void* dst, int wgs, hipStream_t s) {
   hipLaunchKernelGGL(probe_host_records_kernel, dim3(wgs), dim3(kCopyThreads), 0, s, (const unsigned char*)src,
                      index, n, rec_bytes >> 4, src_records, (unsigned char*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_capacity(int32_t* cap, int r, int slots, hipStream_t s) {
+  hipLaunchKernelGGL(set_capacity_kernel, dim3(1), dim3(1), 0, s, cap, r, slots);
   return hipGetLastError();
 }
 

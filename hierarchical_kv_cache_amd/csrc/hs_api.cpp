@@ -49,7 +49,7 @@ struct Layout {
   int kmax = 0;     // longest list one resolve handles: top_k * max(1, verify_rows)
   size_t ctrl = 0, slot_pos = 0, lru = 0, plan = 0, page_table = 0, newest = 0, host_base = 0,
          attn_part = 0, uni = 0, umap = 0, uout = 0, ucnt = 0, uerr = 0, att_zero = 0, att_hdr = 0, att_mlist = 0,
-         att_stage = 0, total = 0;
+         att_stage = 0, cap = 0, total = 0;
 };
 
 int attn_chunks(const hs_config& c) {
@@ -102,6 +102,7 @@ Layout make_layout(const hs_config& c) {
   L.host_base = take(R * sizeof(void*));
   L.attn_part = take(size_t(c.num_layers) * R * L.Spart * kPartStride * sizeof(float));
   L.att_zero = take(size_t(c.record_bytes));  // a zero record: filler rows of FP8 tiles
+  L.cap = take(R * sizeof(int32_t));           // backed slots per request (on-demand hot buffer)
   if (Sf) {  // the fused call's report, miss list and staging area (one set per handle)
     L.att_hdr = take(R * 4 * sizeof(uint32_t));
     L.att_mlist = take(R * k * 4 * sizeof(int32_t));
@@ -136,7 +137,8 @@ hs_status validate(const hs_config* c) {
     return fail(HS_EINVAL, "layer_group must be in [1, num_layers]");
   if (c->wgs_per_request < 0 || c->wgs_per_request > 256)
     return fail(HS_EINVAL, "wgs_per_request must be in [0, 256]");
-  if (c->flags & ~(HS_CFG_NEWEST_SLOT | HS_CFG_RECORD_FP8)) return fail(HS_EINVAL, "unknown config flags");
+  if (c->flags & ~(HS_CFG_NEWEST_SLOT | HS_CFG_RECORD_FP8 | HS_CFG_HOT_ON_DEMAND))
+    return fail(HS_EINVAL, "unknown config flags");
   if (c->verify_rows < 0 || c->verify_rows > 16) return fail(HS_EINVAL, "verify_rows must be in [0, 16]");
   if (c->verify_rows > 1) {
     if (int64_t(c->verify_rows) * c->top_k > kUnionMaxEntries)
@@ -190,6 +192,14 @@ struct hs_ctx {
   int64_t rt_stride = 0, res_rows = 0;
   int page_shift = 0;
   const uint8_t* res = nullptr;
+  // on-demand hot buffer (HS_CFG_HOT_ON_DEMAND): the reserved range, its mapped kHotChunk chunks,
+  // and each request's capacity as the host granted it
+  bool on_demand = false;
+  size_t hot_va_bytes = 0;
+  std::vector<hipMemGenericAllocationHandle_t> chunks;
+  int64_t mapped_chunks = 0;
+  std::vector<int32_t> cap_host;
+  int32_t* cap_dev() { return on_demand ? (int32_t*)(ws + lay.cap) : nullptr; }
 
   uint32_t* ctrl(int a) { return (uint32_t*)(ws + lay.ctrl) + size_t(a) * cfg.num_requests * 4; }
   int32_t* slot_pos(int a) {
@@ -235,7 +245,49 @@ void free_ctx(hs_ctx* h) {
   destroy_events(h);
   free_timing(h);
   for (void* p : h->pool) if (p) (void)hipHostFree(p);
+  if (h->on_demand && h->hot) {
+    // no kernel may still use the range: the device finishes its work first
+    (void)hipDeviceSynchronize();
+    for (size_t c = 0; c < h->chunks.size(); ++c) {
+      if (!h->chunks[c]) continue;
+      (void)hipMemUnmap(h->hot + c * kHotChunk, kHotChunk);
+      (void)hipMemRelease(h->chunks[c]);
+    }
+    (void)hipMemAddressFree(h->hot, h->hot_va_bytes);
+  }
   delete h;
+}
+
+// Backs the chunks of the on-demand hot buffer that overlap bytes [lo, hi) with device memory.
+hs_status map_hot_range(hs_ctx* h, size_t lo, size_t hi) {
+  if (hi <= lo) return HS_OK;
+  hipMemAllocationProp prop = {};
+  prop.type = hipMemAllocationTypePinned;
+  prop.location.type = hipMemLocationTypeDevice;
+  prop.location.id = h->device;
+  hipMemAccessDesc acc = {};
+  acc.location = prop.location;
+  acc.flags = hipMemAccessFlagsProtReadWrite;
+  for (size_t c = lo / kHotChunk; c <= (hi - 1) / kHotChunk; ++c) {
+    if (h->chunks[c]) continue;
+    hipMemGenericAllocationHandle_t hnd;
+    hipError_t e = hipMemCreate(&hnd, kHotChunk, &prop, 0);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(HS_ENOMEM, "backing the hot buffer: %s", hipGetErrorString(e));
+    }
+    void* at = h->hot + c * kHotChunk;
+    e = hipMemMap(at, kHotChunk, 0, hnd, 0);
+    if (e == hipSuccess) e = hipMemSetAccess(at, kHotChunk, &acc, 1);
+    if (e != hipSuccess) {
+      (void)hipMemUnmap(at, kHotChunk);
+      (void)hipMemRelease(hnd);
+      return hip_fail(e, "mapping the hot buffer");
+    }
+    h->chunks[c] = hnd;
+    ++h->mapped_chunks;
+  }
+  return HS_OK;
 }
 
 hs_status check_handle(hs_ctx* h) {
@@ -264,6 +316,7 @@ ResolveParams resolve_params(hs_ctx* h, int32_t layer, const int32_t* d_sel, con
   p.flags = flags | ((h->cfg.flags & HS_CFG_NEWEST_SLOT) ? kHasNewest : 0u);
   p.rtable = h->rtable; p.rt_stride = h->rt_stride; p.res_rows = h->res_rows; p.page_shift = h->page_shift;
   p.plan_k = h->lay.kmax;
+  p.cap = h->cap_dev();
   return p;
 }
 
@@ -281,7 +334,9 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
   *out = nullptr;
   hs_status st = validate(cfg);
   if (st != HS_OK) return st;
-  if (!d_hot || !d_workspace) return fail(HS_EINVAL, "null hot buffer or workspace");
+  const bool on_demand = (cfg->flags & HS_CFG_HOT_ON_DEMAND) != 0;
+  if (on_demand && d_hot) return fail(HS_EINVAL, "HS_CFG_HOT_ON_DEMAND: the library reserves the hot buffer (d_hot = NULL)");
+  if ((!d_hot && !on_demand) || !d_workspace) return fail(HS_EINVAL, "null hot buffer or workspace");
   if ((uintptr_t)d_hot % 16 || (uintptr_t)d_workspace % 256)
     return fail(HS_EINVAL, "hot buffer must be 16-byte and workspace 256-byte aligned");
 
@@ -309,6 +364,34 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
   // this device's address of the allocation-free attention's partials (once per device)
   e = attn_scratch_init(h->device);
   if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetSymbolAddress(attention scratch)"); }
+  if (on_demand) {  // the hot buffer's address range, backed later by hs_grow_request
+    int vmm = 0;
+    e = hipDeviceGetAttribute(&vmm, hipDeviceAttributeVirtualMemoryManagementSupported, h->device);
+    if (e != hipSuccess || !vmm) {
+      free_ctx(h);
+      return fail(HS_EINVAL, "HS_CFG_HOT_ON_DEMAND: the device has no virtual memory management");
+    }
+    hipMemAllocationProp prop = {};
+    prop.type = hipMemAllocationTypePinned;
+    prop.location.type = hipMemLocationTypeDevice;
+    prop.location.id = h->device;
+    size_t gran = 0;
+    e = hipMemGetAllocationGranularity(&gran, &prop, hipMemAllocationGranularityMinimum);
+    if (e != hipSuccess || gran == 0 || kHotChunk % gran) {
+      free_ctx(h);
+      return fail(HS_EINVAL, "HS_CFG_HOT_ON_DEMAND: allocation granularity %zu does not divide %zu", gran, kHotChunk);
+    }
+    const size_t bytes = size_t(cfg->num_requests) * cfg->num_layers * (size_t(cfg->buffer_slots) + 1) *
+                         size_t(cfg->record_bytes);
+    h->hot_va_bytes = align_up(bytes, kHotChunk);
+    void* va = nullptr;
+    e = hipMemAddressReserve(&va, h->hot_va_bytes, kHotChunk, nullptr, 0);
+    if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipMemAddressReserve(hot buffer)"); }
+    h->on_demand = true;
+    h->hot = (uint8_t*)va;
+    h->chunks.assign(h->hot_va_bytes / kHotChunk, hipMemGenericAllocationHandle_t{});
+    h->cap_host.assign(cfg->num_requests, 0);
+  }
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, h->device);
   if (e != hipSuccess) { free_ctx(h); return hip_fail(e, "hipGetDeviceProperties"); }
@@ -429,6 +512,35 @@ void* hs_host_pool(hs_handle h, int32_t request) {
   return h->pool[request];
 }
 
+void* hs_hot_buffer(hs_handle h) { return h ? (void*)h->hot : nullptr; }
+
+int64_t hs_hot_backed_bytes(hs_handle h) {
+  if (!h) return -1;
+  if (!h->on_demand) return int64_t(h->cfg.num_requests) * h->hot_req_stride();
+  return h->mapped_chunks * int64_t(kHotChunk);
+}
+
+hs_status hs_grow_request(hs_handle h, int32_t request, int32_t slots, void* stream) {
+  hs_status st;
+  if ((st = check_handle(h))) return st;
+  if (request < 0 || request >= h->cfg.num_requests) return fail(HS_EINVAL, "request out of range");
+  if (slots < 0 || slots > h->cfg.buffer_slots) return fail(HS_EINVAL, "slots must be in [0, buffer_slots]");
+  if (!h->on_demand) return HS_OK;  // a caller-owned hot buffer is backed throughout
+  // every layer's slots [0, slots) and its newest slot B
+  const size_t rec = h->cfg.record_bytes;
+  for (int l = 0; l < h->cfg.num_layers; ++l) {
+    const size_t base = size_t(request) * h->hot_req_stride() + h->hot_layer_off(l);
+    if ((st = map_hot_range(h, base, base + size_t(slots) * rec))) return st;
+    const size_t nb = base + size_t(h->cfg.buffer_slots) * rec;
+    if ((st = map_hot_range(h, nb, nb + rec))) return st;
+  }
+  if (slots > h->cap_host[request]) {
+    h->cap_host[request] = slots;
+    HS_HIP(launch_set_capacity(h->cap_dev(), request, slots, (hipStream_t)stream));
+  }
+  return HS_OK;
+}
+
 int32_t hs_resolve_wgs(hs_handle h) { return h ? h->G : 0; }
 
 int32_t hs_resolve_attn_wgs(hs_handle h) { return h ? h->att_G : 0; }
@@ -532,6 +644,7 @@ hs_status hs_resolve_rows(hs_handle h, int32_t layer, int32_t rows, const int32_
   p.flags = flags | ((h->cfg.flags & HS_CFG_NEWEST_SLOT) ? kHasNewest : 0u);
   p.rtable = h->rtable; p.rt_stride = h->rt_stride; p.res_rows = h->res_rows; p.page_shift = h->page_shift;
   p.plan_k = kmax;
+  p.cap = h->cap_dev();
   HS_HIP(launch_resolve(p, h->spec_lds_bytes, s, h->next_timing()));
   ScatterParams c{};
   c.uout = uout; c.map = umap; c.err = uerr; c.num_reqs = d_num_reqs; c.out = d_slots_out; c.R = R;
@@ -571,7 +684,7 @@ hs_status hs_writeback(hs_handle h, const void* d_new_kv, const int32_t* d_new_p
   p.host_base = h->host_base(); p.max_positions = h->cfg.max_positions; p.R = h->cfg.num_requests;
   p.L = h->cfg.num_layers; p.B = h->cfg.buffer_slots; p.rec_bytes = h->cfg.record_bytes;
   p.ctrl = h->ctrl(0); p.slot_pos = h->slot_pos(0); p.page_table = h->page_table(0); p.A = h->lay.A;
-  p.group = h->cfg.layer_group;
+  p.group = h->cfg.layer_group; p.cap = h->cap_dev();
   // Slot B may only be overwritten once the previous write-through has read it (and then every
   // later fetch of the previous newest position finds its bytes on the host).
   if (!backup || backup == compute) {
@@ -655,6 +768,7 @@ hs_status attn_params(hs_ctx* h, int32_t layer, const void* d_q, int32_t heads, 
   p.S = (h->cfg.top_k + p.chunk - 1) / p.chunk;  // no empty chunk
   p.rec_bytes = h->cfg.record_bytes; p.scale = scale; p.fp8 = fp8 ? 1 : 0;
   p.zero = h->ws + h->lay.att_zero;
+  p.cap = h->cap_dev();
   *out = p;
   return HS_OK;
 }
@@ -730,6 +844,9 @@ hs_status hs_admit_short(hs_handle h, int32_t request, int32_t ctx_len, void* st
   if (request < 0 || request >= h->cfg.num_requests) return fail(HS_EINVAL, "request out of range");
   if (ctx_len < 0 || ctx_len > h->cfg.buffer_slots || ctx_len > h->cfg.max_positions)
     return fail(HS_EINVAL, "a short request holds at most buffer_slots (and max_positions) tokens");
+  if (h->on_demand && ctx_len > h->cap_host[request])
+    return fail(HS_EINVAL, "request %d has %d backed slots: hs_grow_request before admitting %d tokens", request,
+                h->cap_host[request], ctx_len);
   AdmitParams p{};
   p.host_base = h->host_base(); p.hot = h->hot; p.ctrl = h->ctrl(0); p.slot_pos = h->slot_pos(0);
   p.page_table = h->page_table(0); p.max_positions = h->cfg.max_positions; p.hot_req_stride = h->hot_req_stride();

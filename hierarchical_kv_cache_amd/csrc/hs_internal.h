@@ -188,6 +188,8 @@ struct ResolveParams {
   int32_t heads, att_tiles;
   float att_scale;
   const uint8_t* att_zero;   // a zero record: the finite filler row of FP8 tiles
+  const int32_t* cap;        // [R] LRU slots backed by device memory (on-demand hot buffer), or
+                             // null: every slot is backed
 };
 
 // The finish kernel of the fused call: chunk merge (or NaN rows on error), the missed records
@@ -219,6 +221,7 @@ struct AppendParams {
   int32_t* slot_pos;         // anchor 0's [R][2][B]; anchor a at + a * R * 2 * B
   uint64_t* page_table;      // anchor 0's [R][max_positions]
   int32_t A, group;          // anchors, layers per anchor
+  const int32_t* cap;        // [R] backed LRU slots (on-demand hot buffer) or null (all)
 };
 
 // Admission of a short request: positions [0, ctx) of every layer staged into slots [0, ctx).
@@ -277,6 +280,7 @@ struct AttnParams {
   float scale;
   int32_t fp8;               // records in the FP8 layout (HS_CFG_RECORD_FP8)
   const uint8_t* zero;       // a zero record (the FP8 tiles' filler)
+  const int32_t* cap;        // [R] backed LRU slots (on-demand hot buffer) or null (all)
 };
 
 struct ExportParams {
@@ -333,6 +337,9 @@ hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream
 hipError_t launch_probe_host_records(const void* src, const int32_t* index, int n, int rec_bytes,
                                      int64_t src_records, void* dst, int wgs, hipStream_t s);
 hipError_t launch_probe_empty(int n, hipStream_t s);
+// cap[r] = slots, ordered on s (the on-demand hot buffer's capacity of request r)
+hipError_t launch_set_capacity(int32_t* cap, int r, int slots, hipStream_t s);
+constexpr size_t kHotChunk = size_t(1) << 16;  // mapping unit of the on-demand hot buffer
 
 // attention partial record: [16][512] output accumulators, then [16] max, [16] sum
 constexpr int kAttnMaxHeads = 16;

@@ -261,6 +261,8 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   const uint32_t short_req = p.ctrl[r * 4 + 3];
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
+  // LRU slots backed by device memory (an on-demand hot buffer grows with the request)
+  const int32_t capr = p.cap ? p.cap[r] : p.B;
   const int32_t* selr = p.sel + (size_t)r * p.kb;
   const uint64_t* ptr = p.page_table + (size_t)r * p.max_positions;
   int32_t raw[KE];
@@ -328,7 +330,9 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     // block-wide OR through a scratch word of the dynamic LDS (no static LDS in this kernel)
     if (tid == 0) sh[4] = 0;
     __syncthreads();
-    if (bad) atomicOr((unsigned*)&sh[4], 1u);
+    if (bad) atomicOr((unsigned*)&sh[4], HS_ERR_RANGE);
+    // slot = position needs every position of the context backed
+    if (tid == 0 && ctx > capr) atomicOr((unsigned*)&sh[4], HS_ERR_CAPACITY);
     __syncthreads();
     bad = (uint32_t)sh[4];
     if (g == 0) {
@@ -344,11 +348,11 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
         }
       }
       if (tid == 0 && p.stats) {
-        hs_stats st = {bad ? 0u : (uint32_t)kr, 0u, bad ? (uint32_t)HS_ERR_RANGE : 0u, 0u, 0ull};
+        hs_stats st = {bad ? 0u : (uint32_t)kr, 0u, bad, 0u, 0ull};
         p.stats[r] = st;
       }
       if (tid == 0 && record) p.ctrl[r * 4 + 2] = 0;
-      if (ATT && tid == 0) { hdr[0] = bad ? (uint32_t)HS_ERR_RANGE : 0u; hdr[1] = 0u; }
+      if (ATT && tid == 0) { hdr[0] = bad; hdr[1] = 0u; }
     }
     return;
   }
@@ -601,6 +605,9 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     }
   }
 
+  // the normal path may fill any of the B slots: all of them must be backed (every workgroup
+  // of the request sees the same capacity, so all of them return below and nothing changes)
+  if (tid == 0 && capr < p.B) err |= HS_ERR_CAPACITY;
   if (err) atomicOr((unsigned*)&sh[0], err);
   __syncthreads();
   err = (uint32_t)sh[0] | (sh[1] > 1 ? HS_ERR_DUP : 0u);
@@ -833,6 +840,7 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
   const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
   const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
   const uint32_t short_req = p.ctrl[r * 4 + 3];
+  const int32_t capr = p.cap ? p.cap[r] : p.B;
   const uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   u32x4 qv[kQU];
   q_load(qv, p.q, r, p.heads);
@@ -851,7 +859,8 @@ __device__ __forceinline__ void fetch_attend(const ResolveParams& p, unsigned ch
       const int64_t pos64 = p.bt_shift ? ((int64_t)raw << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)raw;
       if (pos64 >= 0 && pos64 < ctx) {
         if (short_path) {
-          src = dbase + (size_t)pos64 * p.rec_bytes;
+          // (a position outside the backed slots keeps the filler: workgroup 0 reports it)
+          if (pos64 < capr) src = dbase + (size_t)pos64 * p.rec_bytes;
         } else {
           const int32_t sl = (int32_t)(uint32_t)p.page_table[(size_t)r * p.max_positions + pos64];
           const int32_t rp = p.rtable ? p.rtable[(size_t)r * p.rt_stride + (pos64 >> p.page_shift)] : -1;

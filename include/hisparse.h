@@ -51,6 +51,9 @@ typedef int32_t hs_status;
 
 /* hs_config.flags */
 #define HS_CFG_NEWEST_SLOT 1u /* slot B of every (request, layer) holds the newest token ([GC] §3.4, §5.2) */
+#define HS_CFG_HOT_ON_DEMAND 4u /* the library reserves the hot buffer's address range and backs it with
+                                   device memory as requests grow (hs_grow_request; [GC] §5.4
+                                   _grow_device_buffers): hs_create takes d_hot = NULL */
 #define HS_CFG_RECORD_FP8 2u  /* records are fp8 latent KV ([GC] §5.5: fp8_e4m3 KV, FlashMLA-style layout):
                                  record_bytes = 656 = 512 OCP E4M3 codes in 4 blocks of 128, a float32
                                  scale per block, then 64 bf16 values; only hs_sparse_attn reads the
@@ -66,6 +69,9 @@ typedef int32_t hs_status;
 #define HS_ERR_RANGE 2u /* a position outside [0, ctx_len) */
 #define HS_ERR_STATE 4u /* internal: page table and slot map disagreed (never expected) */
 #define HS_ERR_RESIDENT 8u /* a block-table entry names a row outside the bound resident pool */
+#define HS_ERR_CAPACITY 16u /* HS_CFG_HOT_ON_DEMAND: the request needs hot slots that are not backed yet
+                               (a short request longer than its grown capacity, or the normal path
+                               before all B slots are backed); nothing changes */
 
 typedef struct {
   int32_t num_requests;    /* R: requests resolved together in one launch per layer */
@@ -113,7 +119,9 @@ size_t hs_workspace_bytes(const hs_config* cfg);
 /*
  * Creates a cache.
  *   d_hot       device, caller-owned, [R][L][B+1][record_bytes]: the hot buffers
- *               ([GC] §3.2; slot B is the reserved newest slot, [GC] §5.2).
+ *               ([GC] §3.2; slot B is the reserved newest slot, [GC] §5.2).  NULL with
+ *               HS_CFG_HOT_ON_DEMAND: the library reserves that address range and backs it on
+ *               demand (hs_grow_request); no request has device slots until it is grown.
  *   d_workspace device, caller-owned, hs_workspace_bytes(cfg) bytes, 256-byte
  *               aligned: metadata (slot map, LRU order, page table, miss plans,
  *               attention partials).  hs_create initialises it synchronously:
@@ -128,6 +136,31 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
 /* Host address of request r's pool region [L][max_positions][record_bytes]; NULL if r is out of
  * range.  Valid until hs_destroy. */
 void* hs_host_pool(hs_handle h, int32_t request);
+
+/* Device address of the hot buffer [R][L][B+1][record_bytes] (the caller's d_hot, or the range
+ * the library reserved with HS_CFG_HOT_ON_DEMAND); NULL for a bad handle. */
+void* hs_hot_buffer(hs_handle h);
+
+/*
+ * On-demand growth of a request's device buffer ([GC] §5.4: the device buffer grows as needed --
+ * _grow_device_buffers -- so a short request does not hold all B slots from the start; §5.3:
+ * only a request longer than B gets the full B).  With HS_CFG_HOT_ON_DEMAND, backs slots
+ * [0, slots) and the newest slot B of every layer of `request` with device memory (64 KiB
+ * chunks of the reserved range, mapped now, on the host), then, ordered on `stream`, raises
+ * the request's capacity to `slots` for the kernels.  Capacity only grows (hs_reset_request
+ * keeps it; hs_destroy releases everything).  The caller grows a short request before its
+ * context outgrows the capacity (hs_admit_short needs ctx_len <= capacity; a hs_writeback of
+ * a position >= capacity writes only slot B and the host pool), and grows it to B before its
+ * context exceeds B; kernels that would need unbacked slots report HS_ERR_CAPACITY instead.
+ *   slots  0 .. B (0: the newest slot only)
+ * HS_ENOMEM when device memory runs out (chunks mapped so far stay); without
+ * HS_CFG_HOT_ON_DEMAND every slot is backed already and the call does nothing.
+ */
+hs_status hs_grow_request(hs_handle h, int32_t request, int32_t slots, void* stream);
+
+/* Bytes of device memory behind the hot buffer: all of it for a caller-owned buffer, the mapped
+ * chunks with HS_CFG_HOT_ON_DEMAND.  (-1 for a bad handle.) */
+int64_t hs_hot_backed_bytes(hs_handle h);
 
 /*
  * RESOLVE of one layer for all requests ([GC] §3.5, [NJ] §3, [KJ] §7.1):
@@ -338,7 +371,8 @@ hs_status hs_plan(hs_handle h, int32_t layer, const int32_t** d_plan, const uint
  *   - once the context exceeds B (with the B slots full of positions 0 .. B-1) the normal path
  *     takes over from that state.
  * The request must be in the admission state (after hs_create or hs_reset_request) and grow
- * only by hs_writeback.  ctx_len <= buffer_slots.  Asynchronous on `stream`.
+ * only by hs_writeback.  ctx_len <= buffer_slots (with HS_CFG_HOT_ON_DEMAND, <= the capacity
+ * hs_grow_request gave the request).  Asynchronous on `stream`.
  */
 hs_status hs_admit_short(hs_handle h, int32_t request, int32_t ctx_len, void* stream);
 
@@ -351,8 +385,9 @@ hs_status hs_reset_request(hs_handle h, int32_t request, void* stream);
  * waits for the pending backup, then its host and device slots are released): waits for the
  * library's own work still in flight (a backup-stream write-through into the host pool, shared-
  * layer replays reading it), then frees the pinned pool, the events and the handle.  The hot
- * buffer and the workspace are the caller's and stay allocated.  NULL is a no-op.  On a HIP
- * error while waiting the handle is still freed and HS_EHIP is returned.
+ * buffer and the workspace are the caller's and stay allocated (with HS_CFG_HOT_ON_DEMAND the
+ * device first finishes all its work, then the reserved range is unmapped and released).  NULL
+ * is a no-op.  On a HIP error while waiting the handle is still freed and HS_EHIP is returned.
  */
 hs_status hs_destroy(hs_handle h);
 

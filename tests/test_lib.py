@@ -97,7 +97,8 @@ def test_every_cache_declaration_cites_its_passage():
     for name, comment in declarations():
         pos = text.index(name + "(")
         if pos > cut or name in ("hs_last_error", "hs_resolve_wgs", "hs_resolve_attn_wgs", "hs_host_pool",
-                                 "hs_page_table", "hs_plan", "hs_sparse_attn_static"):
+                                 "hs_page_table", "hs_plan", "hs_sparse_attn_static", "hs_hot_buffer",
+                                 "hs_hot_backed_bytes"):
             continue
         seen.add(name)
         assert re.search(r"\[(GC|VD|NJ|KJ)\]", comment), (name, "no page cited")
