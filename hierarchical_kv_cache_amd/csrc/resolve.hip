@@ -586,17 +586,15 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int wtotal = mw * C;  // 16-byte chunks of this wave's misses
-  // Only a fetch-only workgroup (g > 0) loads early: with one workgroup per request, workgroup 0
-  // loads its misses after the publish, so these registers are not held through it.  With 12
-  // or more slots, or 8 list entries, per thread the registers would not last through stage 3
-  // (the compiler then waits for each load and spills its value), so those layouts load none
-  // early.
+  // With 12 or more slots, or 8 list entries, per thread these registers would not last through
+  // stage 3 (the compiler then waits for each load and spills its value), so those layouts load
+  // none early.
   constexpr int kEarlyN = (E >= 12 || KE >= 8) ? 0 : kEarly;
   u32x4 early[kEarlyN > 0 ? kEarlyN : 1];
 #pragma unroll
   for (int u = 0; u < kEarlyN; ++u) {
     const int c = lane + 64 * u;
-    if (g > 0 && c < wtotal) {
+    if (c < wtotal) {
       int l = (int)((float)c * invC);
       int cc = c - l * C;
       if (cc < 0) { --l; cc += C; }
@@ -637,13 +635,15 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
                            g == 0 ? (1ull << kLaunchShift) - (ATT ? 0ull : (uint64_t)(p.G - 1)) : 1ull,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // the entries served without a fetch (hit slot, newest slot, resident row) are published now,
-  // and the misses flagged, so the per-entry classes are not held through stage 3 and publish
+  // The entries served without a fetch (hit slot, newest slot, resident row) are published at
+  // the end of the publish stage; in the large layouts (8 list entries or 12 slots per thread)
+  // already here, so that the per-entry classes are not held through stage 3 and publish.
+  constexpr bool kEarlyHitOut = KE >= 8 || E >= 12;
   uint32_t mbits = 0, ebits = 0;
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
     if (cls[j] == -1) mbits |= 1u << j;
-    if (g == 0 && cls[j] >= 0) p.out[(size_t)r * p.k + i0 + j] = cls[j];
+    if (kEarlyHitOut && g == 0 && cls[j] >= 0) p.out[(size_t)r * p.k + i0 + j] = cls[j];
   }
 
   // ---- stage 3: misses in list order and evictables in LRU order, one scan -------------
@@ -678,8 +678,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   __syncthreads();
 
   // this wave's missed chunks from c_first on (stride 64 per lane): host loads, then stores
-  // into the victim slots stage 3 chose (a wave with more than kEarly chunks per lane, or
-  // workgroup 0 of a one-workgroup launch, which loads none early)
+  // into the victim slots stage 3 chose (a wave with more than kEarlyN chunks per lane)
   auto late_fetch = [&](int c_first) {
     for (int c0 = c_first; c0 < wtotal; c0 += 64 * kUnroll) {
       u32x4 v[kUnroll];
@@ -775,6 +774,11 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
       for (int j = 0; j < E; ++j)
         if (e0 + j < p.B) sp_new[e0 + j] = spo[j];
     }
+    if constexpr (!kEarlyHitOut) {
+#pragma unroll
+      for (int j = 0; j < KE; ++j)
+        if (cls[j] >= 0) outr[i0 + j] = cls[j];
+    }
     if (tid == 0) {
       if (p.stats) {
         hs_stats st = {(uint32_t)(kr - m - nres), (uint32_t)m, (uint32_t)sh[3], (uint32_t)nres,
@@ -784,13 +788,11 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
       if (record) p.ctrl[r * 4 + 2] = (uint32_t)m;
       if (ATT) { hdr[0] = 0u; hdr[1] = (uint32_t)m; hdr[2] = gen; }
     }
-    if (p.G > 1 || !fetcher) return;
-    late_fetch(lane);  // one workgroup per request: workgroup 0 copies every miss itself
-    return;
+    if (p.G > 1) return;
   }
 
-  // ---- stage 4, second part (fetch-only workgroups): the early chunks go to the slots stage 3
-  // chose, then the rest of this wave's misses
+  // ---- stage 4, second part: the early chunks go to the slots stage 3 chose, then the rest
+  // of this wave's misses
   if (fetcher) {
 #pragma unroll
     for (int u = 0; u < kEarlyN; ++u) {
