@@ -677,32 +677,6 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   }
   __syncthreads();
 
-  // this wave's missed chunks from c_first on (stride 64 per lane): host loads, then stores
-  // into the victim slots stage 3 chose (a wave with more than kEarlyN chunks per lane)
-  auto late_fetch = [&](int c_first) {
-    for (int c0 = c_first; c0 < wtotal; c0 += 64 * kUnroll) {
-      u32x4 v[kUnroll];
-      int ll[kUnroll], cc[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + 64 * u;
-        if (c < wtotal) {
-          int l = (int)((float)c * invC);
-          int x = c - l * C;
-          if (x < 0) { --l; x += C; }
-          if (x >= C) { ++l; x -= C; }
-          ll[u] = l;
-          cc[u] = x;
-          v[u] = load_host16(hbase + (size_t)wpos[l] * (size_t)p.rec_bytes + 16 * (size_t)x);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        if (c0 + 64 * u < wtotal)
-          *((u32x4*)(dbase + (size_t)victim[mrank[widx[ll[u]]]] * (size_t)p.rec_bytes) + cc[u]) = v[u];
-    }
-  };
-
   // with several workgroups, workgroup 0 publishes while the others fetch
   if (g == 0) {
     int32_t spo[E];
@@ -806,7 +780,28 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
         *((u32x4*)(dbase + (size_t)slot * (size_t)p.rec_bytes) + cc) = early[u];
       }
     }
-    late_fetch(lane + 64 * kEarlyN);
+    // a wave with more than kEarlyN chunks per lane (miss-heavy steps) continues here
+    for (int c0 = lane + 64 * kEarlyN; c0 < wtotal; c0 += 64 * kUnroll) {
+      u32x4 v[kUnroll];
+      int ll[kUnroll], cc[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < wtotal) {
+          int l = (int)((float)c * invC);
+          int x = c - l * C;
+          if (x < 0) { --l; x += C; }
+          if (x >= C) { ++l; x -= C; }
+          ll[u] = l;
+          cc[u] = x;
+          v[u] = load_host16(hbase + (size_t)wpos[l] * (size_t)p.rec_bytes + 16 * (size_t)x);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (c0 + 64 * u < wtotal)
+          *((u32x4*)(dbase + (size_t)victim[mrank[widx[ll[u]]]] * (size_t)p.rec_bytes) + cc[u]) = v[u];
+    }
   }
 }
 
