@@ -129,6 +129,9 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
   return ((uint64_t)hi << 32) | lo;
 }
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 template <typename T>
 __device__ __forceinline__ T pick4(const T (&x)[4], int i) {
   return i == 0 ? x[0] : i == 1 ? x[1] : i == 2 ? x[2] : x[3];
@@ -191,7 +194,7 @@ __device__ __forceinline__ void acc_init(AttnAcc& a) {
 
 // The [64][4] block scales of an FP8 tile in the attention scratch.
 __device__ __forceinline__ float* tile_scales8(unsigned char* scratch) {
-  return (float*)(scratch + kAttnScratch);
+  return (float*)(scratch + kAttnScales8Off);
 }
 
 // V operand of v_mfma_f32_16x16x32_bf16 by two transposed LDS reads (ds_read_b64_tr_b16).
@@ -225,16 +228,16 @@ __device__ __forceinline__ bf16x8 v_operand(const unsigned char* tile, int row0,
 // Attention of the 16 query heads over one tile of n_tok records held in LDS (sparse decode
 // attention, "HiSparse 深度解析" (gentlecold.top) §5.4: the records of the published slots;
 // key = the record's 576 values, value = its first 512), folded into the running state, on
-// v_mfma_f32_16x16x32_bf16 with all 16 waves busy in every phase:
+// v_mfma_f32_16x16x32_bf16 with all 16 waves busy in every step:
 //   1. scores: wave w computes the 16 heads x 16 tokens block of tokens 16 (w % 4) .. + 15 over
 //      key range w / 4 (its 4 k-steps of 32 channels, 128 (w / 4) .. + 127, and for w / 4 < 2
 //      the rope k-step 16 + w / 4), all its operand reads issued at once, into LDS;
-//   2. wave w then takes head 4 qd + w / 4 (lane quarter qd) of its 16 tokens: the four
-//      partial sums added in key-range order, scaled and masked, and the block maximum;
-//   3. each head's new maximum is the larger of the running one and the tile's; the wave's
-//      probabilities against it, their block sum, and P split into bf16 hi + lo parts (so the
-//      fp32 probabilities survive the bf16 operand) in the operand layout of step 4;
-//   4. every wave rescales its running sum and output by 2^(old max - new max) and
+//   2. wave w then takes head w over the 64 tokens (lane = token): the four partial sums added
+//      in key-range order, scaled and masked; the tile maximum (16-token blocks, then across
+//      them) and the new running maximum, the larger of the two; the probabilities against it,
+//      their sum (16-token block sums added in block order), and P split into bf16 hi + lo parts
+//      (so the fp32 probabilities survive the bf16 operand) in the operand layout of step 3;
+//   3. every wave rescales its running sum and output by 2^(old max - new max) and
 //      accumulates P V for 32 output channels, the V operands read transposed (v_operand).
 // F8: FP8 records (tile_store8).  Key range kp is scale block kp: its partial takes the token's
 // block scale on the fp32 sum before the rope part is added; wave w's 32 output channels lie
@@ -245,17 +248,17 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
                                             unsigned char* scratch, int n_tok, float sl2, AttnAcc& acc) {
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, qd = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tb = w & 3, kp = w >> 2;  // token block and key range of step 1; head 4 qd + kp in 2-3
   constexpr int NB = F8 ? 4 : 1;      // P variants (one per scale block)
-  float* smax = (float*)scratch;      // [4 token blocks][16 heads]
-  float* ssum = smax + 64;            // [4][16]
-  float* spart = ssum + 64;           // step 1 -> 2: [4 key ranges][4 token blocks][16 heads][kSpartRow]
-  uint16_t* phi = (uint16_t*)spart;   // step 3 -> 4 (the partials are dead): [NB][2 token blocks][16 heads][kPRow]
+  float* smax = (float*)scratch;      // [16 heads]: the new running maximum
+  float* ssum = smax + 16;            // [16 heads]: the tile's probability sum
+  float* spart = ssum + 16;           // step 1 -> 2: [4 key ranges][4 token blocks (kSpartTB)][16 heads][kSpartRow]
+  uint16_t* phi = (uint16_t*)(scratch + kAttnPOff);  // step 2 -> 3: [NB][2 token blocks][16 heads][kPRow]
   uint16_t* plo = phi + NB * 2 * 16 * kPRow;
   const float* scl8 = F8 ? tile_scales8(scratch) : nullptr;  // [64][4]
-  const int tl = 16 * tb + col;       // this lane's token in steps 2-3
   {
     // lane: partial s[head = 4 qd + i][token = 16 tb + col]
+    const int tb = w & 3, kp = w >> 2;  // token block and key range
+    const int tl = 16 * tb + col;
     const unsigned char* krow = tile + tl * kTileStride + qd * 16;
     const unsigned char* qrow = qs + col * kQStride + qd * 16;
     bf16x8 qa[4], ka[4];
@@ -274,53 +277,49 @@ __device__ __forceinline__ void attend_tile(const unsigned char* tile, const uns
 #pragma unroll
     for (int j = 0; j < 4; ++j) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], ka[j], sa, 0, 0, 0);
     const float sc = F8 ? scl8[4 * tl + kp] : 1.0f;
-    float* sp = spart + (kp * 4 + tb) * 16 * kSpartRow + col;
+    float* sp = spart + (kp * 4 + tb) * kSpartTB + col;
 #pragma unroll
     for (int i = 0; i < 4; ++i) sp[(4 * qd + i) * kSpartRow] = F8 ? sa[i] * sc + sr[i] : sa[i] + sr[i];
   }
   __syncthreads();
-  const int hk = 4 * qd + kp;
-  float sv;
   {
-    constexpr int KR = 4 * 16 * kSpartRow;  // one key range's partials
-    const float* sp = spart + (tb * 16 + hk) * kSpartRow + col;
+    const int h = w, t = lane;  // head h, token t
+    constexpr int KR = 4 * kSpartTB;  // one key range's partials
+    const float* sp = spart + (t >> 4) * kSpartTB + h * kSpartRow + (t & 15);
     const float s = sp[0] + sp[KR] + sp[2 * KR] + sp[3 * KR];
-    sv = tl < n_tok ? s * sl2 : -INFINITY;
-    const float mx = row16_max(sv);
-    if (col == 0) smax[tb * 16 + hk] = mx;
-  }
-  __syncthreads();
-  float mnew[4], alpha[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = qd * 4 + i;
-    const float mt = fmaxf(fmaxf(smax[hh], smax[16 + hh]), fmaxf(smax[32 + hh], smax[48 + hh]));
-    mnew[i] = fmaxf(acc.m[i], mt);         // finite: every tile has a valid row
-    alpha[i] = exp2f(acc.m[i] - mnew[i]);  // 0 on the first tile
-  }
-  {
-    const float mk = kp == 0 ? mnew[0] : kp == 1 ? mnew[1] : kp == 2 ? mnew[2] : mnew[3];
-    const float pv = exp2f(sv - mk);
-    const float l = row16_sum(pv);
-    if (col == 0) ssum[tb * 16 + hk] = l;
-    const int bk = tl >> 5, kk = v_k(tl & 31);
+    const float sv = t < n_tok ? s * sl2 : -INFINITY;
+    const float bm = row16_max(sv);  // each 16-token block's maximum, in every lane of the block
+    const float mt = fmaxf(fmaxf(readlane_f(bm, 0), readlane_f(bm, 16)), fmaxf(readlane_f(bm, 32), readlane_f(bm, 48)));
+    // the running maximum of head h: element h % 4 of the lanes of quarter h / 4
+    const float mnew = fmaxf(readlane_f(pick4(acc.m, h & 3), 16 * (h >> 2)), mt);  // finite: every tile has a valid row
+    const float pv = exp2f(sv - mnew);
+    const float bs = row16_sum(pv);
+    // (read outside the store's branch: inside it only lane 0 would finish its block's sum)
+    const float lt = ((readlane_f(bs, 0) + readlane_f(bs, 16)) + readlane_f(bs, 32)) + readlane_f(bs, 48);
+    if (t == 0) {
+      smax[h] = mnew;
+      ssum[h] = lt;
+    }
+    const int bk = t >> 5, kk = v_k(t & 31);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       // a masked row (p = 0) takes no scale: a filler's scale must not turn 0 into NaN
-      const float pw = F8 ? (pv != 0.0f ? pv * scl8[4 * tl + b] : 0.0f) : pv;
+      const float pw = F8 ? (pv != 0.0f ? pv * scl8[4 * t + b] : 0.0f) : pv;
       const uint16_t hi = f32_to_bf16_rne(pw);
-      phi[((b * 2 + bk) * 16 + hk) * kPRow + kk] = hi;
-      plo[((b * 2 + bk) * 16 + hk) * kPRow + kk] = f32_to_bf16_rne(pw - __uint_as_float((uint32_t)hi << 16));
+      phi[((b * 2 + bk) * 16 + h) * kPRow + kk] = hi;
+      plo[((b * 2 + bk) * 16 + h) * kPRow + kk] = f32_to_bf16_rne(pw - __uint_as_float((uint32_t)hi << 16));
     }
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hh = qd * 4 + i;
-    acc.l[i] = acc.l[i] * alpha[i] + (ssum[hh] + ssum[16 + hh] + ssum[32 + hh] + ssum[48 + hh]);
-    acc.m[i] = mnew[i];
+    const float mnew = smax[hh];
+    const float alpha = exp2f(acc.m[i] - mnew);  // 0 on the first tile
+    acc.l[i] = acc.l[i] * alpha + ssum[hh];
+    acc.m[i] = mnew;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) acc.o[c][i] *= alpha[i];
+    for (int c = 0; c < 2; ++c) acc.o[c][i] *= alpha;
   }
   // o[head][channel] += p v over the tile; wave w owns channels 32 w .. 32 w + 31
 #pragma unroll

@@ -118,16 +118,21 @@ constexpr int kTileStride = 1168;    // LDS row stride of a 1152-byte record (29
                                      // 36 banks apart modulo 64, so the 16 rows of a QK^T operand
                                      // read, and the 4 rows of a 16-lane group of a V read, spread
 constexpr int kQStride = 1168;       // LDS stride of a query row (16-byte aligned, off the bank period)
-// maxima and sums, then the partial scores (4 key ranges x 4 token blocks x 16 heads, rows of
-// 16 tokens padded to kSpartRow fp32), whose space P hi and lo reuse (rows of 32 tokens padded
-// to kPRow bf16): the padding puts the four lane quarters of an access on distinct banks
+// the heads' new maxima and tile sums, the partial scores (4 key ranges x 4 token blocks x 16
+// heads, rows of 16 tokens padded to kSpartRow fp32, token blocks kSpartTB apart), then P hi
+// and lo (per P variant: 2 token halves x 16 heads, rows of 32 tokens padded to kPRow bf16);
+// the padding puts the four lane quarters of an access on distinct banks (writers' quarters
+// are 4 heads apart, readers' quarters one token block).  P has space of its own: the step
+// that writes it also reads the partial scores of other waves.
 constexpr int kSpartRow = 20, kPRow = 40;
-constexpr int kAttnSpart = 4 * 4 * 16 * kSpartRow * 4;
-constexpr int kAttnScratch = 2 * 4 * 16 * 4 + kAttnSpart;
-// FP8 records: the same (P hi and lo per 128-channel scale block fill the partials' space
-// exactly), and the tile's block scales
-constexpr int kAttnScratch8 = kAttnScratch + kTileRows * 4 * 4;
-static_assert(4 * 2 * 2 * 16 * kPRow * 2 == kAttnSpart, "FP8 P fills the partial scores' space");
+constexpr int kSpartTB = 16 * kSpartRow + 16;
+constexpr int kAttnSpart = 4 * 4 * kSpartTB * 4;
+constexpr int kAttnPOff = 2 * 16 * 4 + kAttnSpart;        // P hi, then P lo
+constexpr int kAttnPVariant = 2 * 2 * 16 * kPRow * 2;      // hi + lo bytes of one P variant
+constexpr int kAttnScratch = kAttnPOff + kAttnPVariant;
+// FP8 records: P per 128-channel scale block (4 variants), then the tile's block scales
+constexpr int kAttnScales8Off = kAttnPOff + 4 * kAttnPVariant;
+constexpr int kAttnScratch8 = kAttnScales8Off + kTileRows * 4 * 4;
 constexpr int kF8RecordBytes = 656;  // 512 E4M3 codes, 4 float32 block scales, 64 bf16
 struct FusedLds {
   size_t tile, qs, scratch, total;
