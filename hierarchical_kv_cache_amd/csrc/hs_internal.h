@@ -14,6 +14,11 @@ constexpr int kMaxSlots = 16384;
 constexpr int kMaxTopK = 16384;
 constexpr int kMaxRecordBytes = 16384;
 constexpr uint32_t kHasNewest = 1u << 8;  // internal resolve flag: slot B holds the newest token
+// internal resolve flags of a launch split by list length (a speculative union): the launch
+// serves only the requests whose list has <= kSplitKE * kResolveThreads entries, or only the
+// others
+constexpr uint32_t kSplitShort = 1u << 9, kSplitLong = 1u << 10;
+constexpr int kSplitKE = 4;
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

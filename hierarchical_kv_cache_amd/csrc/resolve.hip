@@ -195,7 +195,7 @@ __device__ __forceinline__ int16_t run16_at(const Run16<E>& a, int j) {
 // new position) and a per-request header, and the finish kernel that follows applies the
 // page-table updates and copies the missed records, which the fetch workgroups staged, into
 // their victim slots.  So the page table does not change while the fused kernel runs.
-template <int E, int KE, bool ATT>
+template <int E, int KE, bool ATT, bool SPLIT = false>
 __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned char* smem) {
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits, p.G);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
@@ -227,6 +227,11 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   // entries of this request's list (a speculative union is shorter than its k-entry row), spread
   // over all threads: EK = ceil(kr / NT) <= KE consecutive entries per thread
   const int kr = p.kvar ? min(p.kvar[r], p.k) : p.k;
+  if constexpr (SPLIT) {
+    // a launch split by list length serves only its side of kSplitKE NT entries: in the other
+    // launch the request's workgroups return here, before any other read or write
+    if (((p.flags & kSplitShort) && kr > kSplitKE * NT) || ((p.flags & kSplitLong) && kr <= kSplitKE * NT)) return;
+  }
   const int EK = (kr + NT - 1) / NT;
   const int i0 = tid * EK;  // first selection entry of this thread
   const uint32_t pre_err = p.kerr ? p.kerr[r] : 0u;
@@ -923,6 +928,13 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   resolve_body<E, KE, ATT>(p, smem);
 }
 
+// RESOLVE over a speculative union, in a launch split by list length (launch_resolve)
+template <int E, int KE>
+__global__ void __launch_bounds__(NT) resolve_split_kernel(ResolveParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  resolve_body<E, KE, false, true>(p, smem);
+}
+
 // The fused kernel over FP8 records: workgroup 0 as in resolve_kernel<E, KE, true>, the fetch
 // workgroups on FP8 tiles.
 template <int E, int KE>
@@ -1098,6 +1110,30 @@ hipError_t launch_e(const ResolveParams& p, size_t lds, hipStream_t s, const Ker
   return hipGetLastError();
 }
 
+// the two launches of a split (E >= 8: a union longer than kSplitKE NT entries needs that many)
+template <int E, int KE>
+hipError_t launch_split_e(const ResolveParams& p, size_t lds, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  if (start || stop) {
+    hipExtLaunchKernelGGL((resolve_split_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, start, stop,
+                          0u, p);
+  } else {
+    hipLaunchKernelGGL((resolve_split_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), lds, s, p);
+  }
+  return hipGetLastError();
+}
+template <int E>
+hipError_t launch_split(const ResolveParams& p, size_t lds, hipStream_t s, int KE, const KernelTiming* tm) {
+  static_assert(E >= 8, "a split launch needs more than kSplitKE entries per thread");
+  ResolveParams a = p, b = p;
+  a.flags |= kSplitShort;
+  b.flags |= kSplitLong;
+  hipError_t e = launch_split_e<E, kSplitKE>(a, lds, s, tm ? tm->start : nullptr, nullptr);
+  if (e != hipSuccess) return e;
+  if (KE <= 8) return launch_split_e<E, 8>(b, lds, s, nullptr, tm ? tm->stop : nullptr);
+  if constexpr (E >= 16) return launch_split_e<E, 16>(b, lds, s, nullptr, tm ? tm->stop : nullptr);
+  return hipErrorInvalidValue;
+}
+
 // The fused variant exists for KE <= 4 and E <= 8 (top_k <= 4096, B <= 8192): larger lists
 // leave no LDS for the record tile.
 constexpr int kFusedMaxE = 8, kFusedMaxKE = 4;
@@ -1132,6 +1168,11 @@ hipError_t set_limit_ke(int v) {
   if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 4, false>, v);
   if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 8, false>, v);
   if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 16, false>, v);
+  if constexpr (E >= 8) {
+    if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, kSplitKE>, v);
+    if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, 8>, v);
+  }
+  if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, 16>, v);
   if constexpr (E <= kFusedMaxE) {
     if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1, true>, v);
     if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 2, true>, v);
@@ -1193,7 +1234,21 @@ hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
 
 hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s, const KernelTiming* tm) {
   const int KE = pow2_at_least((p.k + NT - 1) / NT);
-  switch (resolve_elems_per_thread(p.k, p.B)) {
+  const int E = resolve_elems_per_thread(p.k, p.B);
+  // A speculative union is usually far shorter than its capacity (rows x k entries): lists of
+  // <= kSplitKE NT entries go to the instantiation with kSplitKE entries per thread, whose
+  // registers fit, and only longer ones to the full one.  Both launches go out; each request's
+  // workgroups return at entry in the launch that does not serve it.  The timing events span
+  // the two.
+  if (p.kvar && KE > kSplitKE) {
+    switch (E) {
+      case 8: return launch_split<8>(p, lds_bytes, s, KE, tm);
+      case 12: return launch_split<12>(p, lds_bytes, s, KE, tm);
+      case 16: return launch_split<16>(p, lds_bytes, s, KE, tm);
+      default: break;
+    }
+  }
+  switch (E) {
     case 1: return launch_ke<1, false>(p, lds_bytes, s, KE, tm);
     case 2: return launch_ke<2, false>(p, lds_bytes, s, KE, tm);
     case 4: return launch_ke<4, false>(p, lds_bytes, s, KE, tm);

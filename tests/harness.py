@@ -27,7 +27,8 @@ class Pair:
 
     def __init__(self, w: synth.Workload, steps: int | None = None, wgs: int = 0, all_hit=False,
                  oracle_host_copy: bool | None = None, compare_hot=True, resident: ResidentSpec | None = None,
-                 fp8: bool = False, rows: int = 1, fused_heads: int = 0, append_streams: str = "two"):
+                 fp8: bool = False, rows: int = 1, fused_heads: int = 0, append_streams: str = "two",
+                 rows_keep=0.9):
         self.w = w
         # hs_writeback's write-through: "two" (backup stream and events) or "one" (one kernel on
         # the compute stream); may be changed between steps
@@ -77,8 +78,11 @@ class Pair:
                                      device=self.dev)
         if rows > 1:
             from synth.traces import verify_rows
-            tr = np.stack([np.stack([verify_rows(w, r, l, self.steps, rows) for r in range(w.R)], axis=1)
-                           for l in self.anchors], axis=1)
+            # rows_keep: each row's chance of keeping an entry of the row before, for every
+            # request or per request (the lower, the longer the union)
+            keep = list(rows_keep) if hasattr(rows_keep, "__len__") else [rows_keep] * w.R
+            tr = np.stack([np.stack([verify_rows(w, r, l, self.steps, rows, keep=keep[r]) for r in range(w.R)],
+                                    axis=1) for l in self.anchors], axis=1)
         else:
             tr = np.stack([np.stack([synth.selection_trace(w, r, l, self.steps, all_hit=all_hit)
                                      for r in range(w.R)], axis=1) for l in self.anchors], axis=1)

@@ -56,6 +56,30 @@ def test_long_four_rows_with_write_through():
     p.close()
 
 
+def test_long_and_short_unions_in_one_call():
+    """Unions on both sides of 4096 entries in the same call: a union of at most 4 x 1024
+    entries is resolved by the launch with 4 list entries per thread, a longer one by the launch
+    with 8 (each request's workgroups return at entry in the other launch).  4 rows of k = 2048
+    into B = 10240 (12 slots per thread); request 0's rows keep 90 % of the row before (union
+    about 2650), request 1's 30 % (about 6300); 12 steps, past the buffer-fill point of request 1."""
+    w = W["long"].scaled(R=2, L=1, B=5 * 2048, append=False, force_newest=False)
+    p = Pair(w, steps=12, rows=4, rows_keep=(0.9, 0.3))
+    short = long_ = 0
+    for t in range(12):
+        res = p.step_gpu_and_oracle()
+        for (r, l), v in res.items():
+            n = int(v[1]) + int(v[2]) + int(v[5])
+            short += n <= 4096
+            long_ += n > 4096
+        if t in (5, 11):
+            p.check_state()
+    log("unions <= 4096: %d, > 4096: %d; occupied slots evicted %d" % (short, long_, p.evicted))
+    assert short >= 12 and long_ >= 12, (short, long_)
+    assert p.evicted > 0
+    p.check_hot()
+    p.close()
+
+
 def test_batched_rows():
     w = W["batched"].scaled(R=8, L=2, k=1024, B=3 * 1024)
     p = Pair(w, steps=5, rows=3)
