@@ -645,11 +645,9 @@ hs_status hs_resolve_rows(hs_handle h, int32_t layer, int32_t rows, const int32_
   p.rtable = h->rtable; p.rt_stride = h->rt_stride; p.res_rows = h->res_rows; p.page_shift = h->page_shift;
   p.plan_k = kmax;
   p.cap = h->cap_dev();
+  // the rows' slots from the union's (by the union's RESOLVE kernel, or a scatter kernel after it)
+  p.rows_out = d_slots_out; p.rows_map = umap; p.rows_n = rows * h->cfg.top_k;
   HS_HIP(launch_resolve(p, h->spec_lds_bytes, s, h->next_timing()));
-  ScatterParams c{};
-  c.uout = uout; c.map = umap; c.err = uerr; c.num_reqs = d_num_reqs; c.out = d_slots_out; c.R = R;
-  c.n = rows * h->cfg.top_k; c.kmax = kmax;
-  HS_HIP(launch_scatter(c, s));
   return HS_OK;
 }
 

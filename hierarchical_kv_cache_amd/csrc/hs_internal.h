@@ -14,10 +14,8 @@ constexpr int kMaxSlots = 16384;
 constexpr int kMaxTopK = 16384;
 constexpr int kMaxRecordBytes = 16384;
 constexpr uint32_t kHasNewest = 1u << 8;  // internal resolve flag: slot B holds the newest token
-// internal resolve flags of a launch split by list length (a speculative union): the launch
-// serves only the requests whose list has <= kSplitKE * kResolveThreads entries, or only the
-// others
-constexpr uint32_t kSplitShort = 1u << 9, kSplitLong = 1u << 10;
+// list entries per thread of the RESOLVE body for speculative unions of <= kSplitKE *
+// kResolveThreads entries
 constexpr int kSplitKE = 4;
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -200,6 +198,11 @@ struct ResolveParams {
   const uint8_t* att_zero;   // a zero record: the finite filler row of FP8 tiles
   const int32_t* cap;        // [R] LRU slots backed by device memory (on-demand hot buffer), or
                              // null: every slot is backed
+  // a speculative union (hs_resolve_rows): the rows' slots [R][rows_n] from the union's, entry
+  // f of a request taking the slot of union entry rows_map[r][f] (-1: none); null otherwise
+  int32_t* rows_out;
+  const int32_t* rows_map;   // [R][k]
+  int32_t rows_n;
 };
 
 // The finish kernel of the fused call: chunk merge (or NaN rows on error), the missed records

@@ -195,7 +195,7 @@ __device__ __forceinline__ int16_t run16_at(const Run16<E>& a, int j) {
 // new position) and a per-request header, and the finish kernel that follows applies the
 // page-table updates and copies the missed records, which the fetch workgroups staged, into
 // their victim slots.  So the page table does not change while the fused kernel runs.
-template <int E, int KE, bool ATT, bool SPLIT = false>
+template <int E, int KE, bool ATT>
 __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned char* smem) {
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits, p.G);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
@@ -227,11 +227,6 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   // entries of this request's list (a speculative union is shorter than its k-entry row), spread
   // over all threads: EK = ceil(kr / NT) <= KE consecutive entries per thread
   const int kr = p.kvar ? min(p.kvar[r], p.k) : p.k;
-  if constexpr (SPLIT) {
-    // a launch split by list length serves only its side of kSplitKE NT entries: in the other
-    // launch the request's workgroups return here, before any other read or write
-    if (((p.flags & kSplitShort) && kr > kSplitKE * NT) || ((p.flags & kSplitLong) && kr <= kSplitKE * NT)) return;
-  }
   const int EK = (kr + NT - 1) / NT;
   const int i0 = tid * EK;  // first selection entry of this thread
   const uint32_t pre_err = p.kerr ? p.kerr[r] : 0u;
@@ -928,11 +923,29 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   resolve_body<E, KE, ATT>(p, smem);
 }
 
-// RESOLVE over a speculative union, in a launch split by list length (launch_resolve)
+// RESOLVE over a speculative union (launch_resolve): a union of <= kSplitKE NT entries, the
+// usual case, takes the body with kSplitKE list entries per thread, whose registers fit; a
+// longer one the body with KE.  The choice is per request (every workgroup of the request reads
+// the same length).
+// Workgroup 0 then gives every row entry its union entry's slot (the scatter).
 template <int E, int KE>
 __global__ void __launch_bounds__(NT) resolve_split_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  resolve_body<E, KE, false, true>(p, smem);
+  const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
+  const int kr = min(p.kvar[r], p.k);
+  if (kr <= kSplitKE * NT) resolve_body<E, kSplitKE, false>(p, smem);
+  else resolve_body<E, KE, false>(p, smem);
+  // (every return in resolve_body is taken by the whole workgroup, so all its threads are here)
+  if (g != 0 || (p.num_reqs && r >= *p.num_reqs)) return;
+  __syncthreads();  // workgroup 0's writes of the union's slots are visible to all its threads
+  const bool bad = p.kerr[r] != 0;
+  const int32_t* uo = p.out + (size_t)r * p.k;
+  const int32_t* mp = p.rows_map + (size_t)r * p.k;
+  int32_t* ro = p.rows_out + (size_t)r * p.rows_n;
+  for (int f = threadIdx.x; f < p.rows_n; f += NT) {
+    const int32_t u = mp[f];
+    ro[f] = (bad || u < 0) ? -1 : uo[u];
+  }
 }
 
 // The fused kernel over FP8 records: workgroup 0 as in resolve_kernel<E, KE, true>, the fetch
@@ -1110,12 +1123,12 @@ hipError_t launch_e(const ResolveParams& p, size_t lds, hipStream_t s, const Ker
   return hipGetLastError();
 }
 
-// the two launches of a split (E >= 8: a union longer than kSplitKE NT entries needs that many)
+// the union kernel (E >= 8: a union longer than kSplitKE NT entries needs that many)
 template <int E, int KE>
-hipError_t launch_split_e(const ResolveParams& p, size_t lds, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  if (start || stop) {
-    hipExtLaunchKernelGGL((resolve_split_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, start, stop,
-                          0u, p);
+hipError_t launch_split_e(const ResolveParams& p, size_t lds, hipStream_t s, const KernelTiming* tm) {
+  if (tm && tm->start) {
+    hipExtLaunchKernelGGL((resolve_split_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, tm->start,
+                          tm->stop, 0u, p);
   } else {
     hipLaunchKernelGGL((resolve_split_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), lds, s, p);
   }
@@ -1123,14 +1136,9 @@ hipError_t launch_split_e(const ResolveParams& p, size_t lds, hipStream_t s, hip
 }
 template <int E>
 hipError_t launch_split(const ResolveParams& p, size_t lds, hipStream_t s, int KE, const KernelTiming* tm) {
-  static_assert(E >= 8, "a split launch needs more than kSplitKE entries per thread");
-  ResolveParams a = p, b = p;
-  a.flags |= kSplitShort;
-  b.flags |= kSplitLong;
-  hipError_t e = launch_split_e<E, kSplitKE>(a, lds, s, tm ? tm->start : nullptr, nullptr);
-  if (e != hipSuccess) return e;
-  if (KE <= 8) return launch_split_e<E, 8>(b, lds, s, nullptr, tm ? tm->stop : nullptr);
-  if constexpr (E >= 16) return launch_split_e<E, 16>(b, lds, s, nullptr, tm ? tm->stop : nullptr);
+  static_assert(E >= 8, "a union longer than kSplitKE NT entries");
+  if (KE <= 8) return launch_split_e<E, 8>(p, lds, s, tm);
+  if constexpr (E >= 16) return launch_split_e<E, 16>(p, lds, s, tm);
   return hipErrorInvalidValue;
 }
 
@@ -1168,10 +1176,7 @@ hipError_t set_limit_ke(int v) {
   if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 4, false>, v);
   if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 8, false>, v);
   if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 16, false>, v);
-  if constexpr (E >= 8) {
-    if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, kSplitKE>, v);
-    if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, 8>, v);
-  }
+  if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, 8>, v);
   if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, 16>, v);
   if constexpr (E <= kFusedMaxE) {
     if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1, true>, v);
@@ -1235,27 +1240,31 @@ hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
 hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s, const KernelTiming* tm) {
   const int KE = pow2_at_least((p.k + NT - 1) / NT);
   const int E = resolve_elems_per_thread(p.k, p.B);
-  // A speculative union is usually far shorter than its capacity (rows x k entries): lists of
-  // <= kSplitKE NT entries go to the instantiation with kSplitKE entries per thread, whose
-  // registers fit, and only longer ones to the full one.  Both launches go out; each request's
-  // workgroups return at entry in the launch that does not serve it.  The timing events span
-  // the two.
-  if (p.kvar && KE > kSplitKE) {
+  // A speculative union is usually far shorter than its capacity (rows x k entries): its kernel
+  // takes the body with kSplitKE list entries per thread for such a union (resolve_split_kernel).
+  // It also writes the rows' slots.  (KE > kSplitKE puts E at 8 or more.)
+  if (p.rows_out && KE > kSplitKE) {
     switch (E) {
       case 8: return launch_split<8>(p, lds_bytes, s, KE, tm);
       case 12: return launch_split<12>(p, lds_bytes, s, KE, tm);
-      case 16: return launch_split<16>(p, lds_bytes, s, KE, tm);
-      default: break;
+      default: return launch_split<16>(p, lds_bytes, s, KE, tm);
     }
   }
+  hipError_t e;
   switch (E) {
-    case 1: return launch_ke<1, false>(p, lds_bytes, s, KE, tm);
-    case 2: return launch_ke<2, false>(p, lds_bytes, s, KE, tm);
-    case 4: return launch_ke<4, false>(p, lds_bytes, s, KE, tm);
-    case 8: return launch_ke<8, false>(p, lds_bytes, s, KE, tm);
-    case 12: return launch_ke<12, false>(p, lds_bytes, s, KE, tm);
-    default: return launch_ke<16, false>(p, lds_bytes, s, KE, tm);
+    case 1: e = launch_ke<1, false>(p, lds_bytes, s, KE, tm); break;
+    case 2: e = launch_ke<2, false>(p, lds_bytes, s, KE, tm); break;
+    case 4: e = launch_ke<4, false>(p, lds_bytes, s, KE, tm); break;
+    case 8: e = launch_ke<8, false>(p, lds_bytes, s, KE, tm); break;
+    case 12: e = launch_ke<12, false>(p, lds_bytes, s, KE, tm); break;
+    default: e = launch_ke<16, false>(p, lds_bytes, s, KE, tm); break;
   }
+  if (e != hipSuccess || !p.rows_out) return e;
+  // a short union: the rows' slots by a kernel of their own
+  ScatterParams c{};
+  c.uout = p.out; c.map = p.rows_map; c.err = p.kerr; c.num_reqs = p.num_reqs; c.out = p.rows_out; c.R = p.R;
+  c.n = p.rows_n; c.kmax = p.k;
+  return launch_scatter(c, s);
 }
 
 bool fused_supported(int k, int B) {
