@@ -332,7 +332,11 @@ hipError_t launch_resolve_attn(const ResolveParams& p, size_t lds_bytes, hipStre
                                const KernelTiming* tm = nullptr);
 hipError_t launch_union(const UnionParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
-size_t union_lds_bytes(int hash_bits);
+// the union kernel's LDS: per bucket the position and the row mask / union index, then the
+// scan carries (2 x 2 per wave) and shared words
+inline size_t union_lds_bytes(int hash_bits) {
+  return (size_t(8) << hash_bits) + 4 * (4 * (kResolveThreads / 64) + 8);
+}
 hipError_t set_union_lds_limit(size_t lds_bytes);
 constexpr int kUnionMaxEntries = 8192;  // rows * top_k of one speculative resolve
 hipError_t set_resolve_lds_limit(size_t lds_bytes);

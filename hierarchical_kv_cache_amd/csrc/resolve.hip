@@ -1220,7 +1220,6 @@ hipError_t set_resolve_lds_limit(size_t lds_bytes) {
   return set_limit_ke<16>(v);
 }
 
-size_t union_lds_bytes(int hash_bits) { return (size_t(8) << hash_bits) + 4 * (4 * NW + 8); }
 
 hipError_t set_union_lds_limit(size_t lds_bytes) {
   return set_dynamic_lds((const void*)union_kernel, (int)lds_bytes);
