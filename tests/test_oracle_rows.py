@@ -5,8 +5,9 @@ KV offload architecture" (docs.vllm.ai), speculative decoding: the verification
 rows of one step are resolved together as the union of their selections, in
 first-reference order; rows that select the same position share its slot and
 no row evicts a slot another row reads.  Pinned by the one-row special case, by
-identical rows, and by the independent list model run on a union built here
-with a dictionary.
+identical rows, by a three-step example worked by hand (tests/golden), by the union's
+order against numpy's first-occurrence indices, and by the independent list model run on a
+union built here with a dictionary.
 """
 import numpy as np
 import pytest
@@ -100,6 +101,69 @@ def test_matches_list_model_on_the_union(newest):
             for q in range(Q):
                 for i in range(k):
                     assert np.array_equal(c.hot[got[0][q, i]], host[rows[q, i]])
+
+
+def _golden_steps(path):
+    """(B, positions, [(rows, slots, counts, plan, lru)]) from a worked example file."""
+    B = U = None
+    steps, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, val = line.partition(" ")
+        if key == "B":
+            B = int(val)
+        elif key == "positions":
+            U = int(val)
+        elif key == "step":
+            cur = {"rows": [[int(x) for x in r.split(",")] for r in val.split(" ", 1)[1].split(";")]}
+            steps.append(cur)
+        elif key == "expect_slots":
+            cur["slots"] = [[int(x) for x in r.split(",")] for r in val.split(";")]
+        elif key == "expect_counts":
+            cur["counts"] = [int(x) for x in val.split()]
+        elif key == "expect_plan":
+            cur["plan"] = [tuple(int(y) for y in x.split(":")) for x in val.split()]
+        elif key == "expect_lru":
+            cur["lru"] = [int(x) for x in val.split()]
+    return B, U, steps
+
+
+def test_worked_example_by_hand():
+    """Three steps of overlapping rows from an empty buffer, the expected slots, counts, plan
+    and LRU order worked out by hand from the union and stamp rules (tests/golden)."""
+    import os
+    B, U, steps = _golden_steps(os.path.join(os.path.dirname(__file__), "golden", "rows_union_example.txt"))
+    host = host_for(U)
+    c = oracle.Cache(B, U, REC)
+    for n, st in enumerate(steps):
+        got = c.resolve_rows(np.array(st["rows"], dtype=np.int32), U, host)
+        assert got[0].tolist() == st["slots"], n
+        assert [got[1], got[2], got[6]] == st["counts"], n
+        assert list(zip(got[4].tolist(), got[5].tolist())) == st["plan"], n
+        assert c.export()["lru"].tolist() == st["lru"], n
+
+
+def test_union_order_is_the_order_of_first_occurrence():
+    """From an empty buffer every union entry misses, so the miss plan lists the union in the
+    order the call resolved it: the positions sorted by the index of their first occurrence in
+    the rows laid end to end (numpy's unique gives those indices)."""
+    rng = np.random.default_rng(29)
+    for trial in range(200):
+        U = int(rng.integers(8, 40))
+        k = int(rng.integers(1, 6))
+        Q = int(rng.integers(1, 5))
+        rows = np.stack([rng.choice(U, size=k, replace=False) for _ in range(Q)]).astype(np.int32)
+        flat = rows.reshape(-1)
+        _, first = np.unique(flat, return_index=True)
+        want = flat[np.sort(first)]
+        c = oracle.Cache(Q * k, U, REC)
+        got = c.resolve_rows(rows, U, host_for(U, seed=trial))
+        assert got[1] == 0 and got[2] == want.size == got[6], trial
+        assert np.array_equal(got[4], want), trial
+        # the victims of an empty buffer are the slots in index order
+        assert np.array_equal(got[5], np.arange(want.size)), trial
 
 
 def test_duplicates_and_capacity():
