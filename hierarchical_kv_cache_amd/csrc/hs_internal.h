@@ -14,9 +14,9 @@ constexpr int kMaxSlots = 16384;
 constexpr int kMaxTopK = 16384;
 constexpr int kMaxRecordBytes = 16384;
 constexpr uint32_t kHasNewest = 1u << 8;  // internal resolve flag: slot B holds the newest token
-// list entries per thread of the RESOLVE body for speculative unions of <= kSplitKE *
+// list entries per thread of the RESOLVE body for speculative unions of <= kUnionShortKE *
 // kResolveThreads entries
-constexpr int kSplitKE = 4;
+constexpr int kUnionShortKE = 4;
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

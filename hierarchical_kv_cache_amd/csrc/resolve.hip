@@ -923,17 +923,17 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   resolve_body<E, KE, ATT>(p, smem);
 }
 
-// RESOLVE over a speculative union (launch_resolve): a union of <= kSplitKE NT entries, the
-// usual case, takes the body with kSplitKE list entries per thread, whose registers fit; a
-// longer one the body with KE.  The choice is per request (every workgroup of the request reads
-// the same length).
-// Workgroup 0 then gives every row entry its union entry's slot (the scatter).
+// RESOLVE over a speculative union whose capacity (rows x k entries) needs KE > kUnionShortKE
+// list entries per thread (launch_resolve).  A union of <= kUnionShortKE NT entries, the usual
+// case, takes the body with kUnionShortKE entries per thread, whose registers fit; a longer one
+// the body with KE.  The choice is per request (every workgroup of the request reads the same
+// length).  Workgroup 0 then gives every row entry its union entry's slot (the scatter).
 template <int E, int KE>
-__global__ void __launch_bounds__(NT) resolve_split_kernel(ResolveParams p) {
+__global__ void __launch_bounds__(NT) resolve_union_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
   const int kr = min(p.kvar[r], p.k);
-  if (kr <= kSplitKE * NT) resolve_body<E, kSplitKE, false>(p, smem);
+  if (kr <= kUnionShortKE * NT) resolve_body<E, kUnionShortKE, false>(p, smem);
   else resolve_body<E, KE, false>(p, smem);
   // (every return in resolve_body is taken by the whole workgroup, so all its threads are here)
   if (g != 0 || (p.num_reqs && r >= *p.num_reqs)) return;
@@ -1123,22 +1123,22 @@ hipError_t launch_e(const ResolveParams& p, size_t lds, hipStream_t s, const Ker
   return hipGetLastError();
 }
 
-// the union kernel (E >= 8: a union longer than kSplitKE NT entries needs that many)
+// the union kernel (E >= 8: a union longer than kUnionShortKE NT entries needs that many)
 template <int E, int KE>
-hipError_t launch_split_e(const ResolveParams& p, size_t lds, hipStream_t s, const KernelTiming* tm) {
+hipError_t launch_union_resolve_e(const ResolveParams& p, size_t lds, hipStream_t s, const KernelTiming* tm) {
   if (tm && tm->start) {
-    hipExtLaunchKernelGGL((resolve_split_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, tm->start,
+    hipExtLaunchKernelGGL((resolve_union_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, tm->start,
                           tm->stop, 0u, p);
   } else {
-    hipLaunchKernelGGL((resolve_split_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), lds, s, p);
+    hipLaunchKernelGGL((resolve_union_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), lds, s, p);
   }
   return hipGetLastError();
 }
 template <int E>
-hipError_t launch_split(const ResolveParams& p, size_t lds, hipStream_t s, int KE, const KernelTiming* tm) {
-  static_assert(E >= 8, "a union longer than kSplitKE NT entries");
-  if (KE <= 8) return launch_split_e<E, 8>(p, lds, s, tm);
-  if constexpr (E >= 16) return launch_split_e<E, 16>(p, lds, s, tm);
+hipError_t launch_union_resolve(const ResolveParams& p, size_t lds, hipStream_t s, int KE, const KernelTiming* tm) {
+  static_assert(E >= 8, "a union longer than kUnionShortKE NT entries");
+  if (KE <= 8) return launch_union_resolve_e<E, 8>(p, lds, s, tm);
+  if constexpr (E >= 16) return launch_union_resolve_e<E, 16>(p, lds, s, tm);
   return hipErrorInvalidValue;
 }
 
@@ -1176,8 +1176,8 @@ hipError_t set_limit_ke(int v) {
   if constexpr (E >= 4) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 4, false>, v);
   if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 8, false>, v);
   if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 16, false>, v);
-  if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, 8>, v);
-  if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_split_kernel<E, 16>, v);
+  if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_union_kernel<E, 8>, v);
+  if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_union_kernel<E, 16>, v);
   if constexpr (E <= kFusedMaxE) {
     if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1, true>, v);
     if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 2, true>, v);
@@ -1239,14 +1239,13 @@ hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
 hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t s, const KernelTiming* tm) {
   const int KE = pow2_at_least((p.k + NT - 1) / NT);
   const int E = resolve_elems_per_thread(p.k, p.B);
-  // A speculative union is usually far shorter than its capacity (rows x k entries): its kernel
-  // takes the body with kSplitKE list entries per thread for such a union (resolve_split_kernel).
-  // It also writes the rows' slots.  (KE > kSplitKE puts E at 8 or more.)
-  if (p.rows_out && KE > kSplitKE) {
+  // A speculative union longer than kUnionShortKE entries per thread at capacity: the union
+  // kernel, which also writes the rows' slots (KE > kUnionShortKE puts E at 8 or more)
+  if (p.rows_out && KE > kUnionShortKE) {
     switch (E) {
-      case 8: return launch_split<8>(p, lds_bytes, s, KE, tm);
-      case 12: return launch_split<12>(p, lds_bytes, s, KE, tm);
-      default: return launch_split<16>(p, lds_bytes, s, KE, tm);
+      case 8: return launch_union_resolve<8>(p, lds_bytes, s, KE, tm);
+      case 12: return launch_union_resolve<12>(p, lds_bytes, s, KE, tm);
+      default: return launch_union_resolve<16>(p, lds_bytes, s, KE, tm);
     }
   }
   hipError_t e;
