@@ -205,19 +205,21 @@ __global__ void __launch_bounds__(kFinishThreads) attn_finish_kernel(FinishParam
     merge_quarter(p.part + (size_t)r * p.S * kPartStride, p.S, hh, tid >> 6, tid & 63, fac[tid >> 6], orow);
     return;
   }
-  // pre[r] = misses of the applying requests before r (p.R <= kFinishThreads)
+  // pre[r] = misses of the applying requests before r (p.R <= kFinishThreads): an inclusive
+  // scan within each wave (shuffles), then the waves' totals added in through LDS
   const int nr = p.num_reqs ? min(*p.num_reqs, p.R) : p.R;
   const int mine = (tid < nr && p.hdr[tid * 4] == 0) ? (int)p.hdr[tid * 4 + 1] : 0;
-  pre[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < kFinishThreads; off <<= 1) {
-    const int add = tid >= off ? pre[tid - off] : 0;
-    __syncthreads();
-    pre[tid] += add;
-    __syncthreads();
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
   }
-  const int incl = pre[tid];
+  __shared__ int wsum[kFinishThreads / 64];
+  if (lane == 63) wsum[wv] = incl;
   __syncthreads();
+  for (int w = 0; w < wv; ++w) incl += wsum[w];
   pre[tid] = incl - mine;
   if (tid == kFinishThreads - 1) pre[kFinishThreads] = incl;
   __syncthreads();
