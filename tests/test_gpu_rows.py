@@ -80,6 +80,24 @@ def test_long_and_short_unions_in_one_call():
     p.close()
 
 
+@pytest.mark.parametrize("rows,B,keep", [(3, 8192, 0.9), (3, 8192, 0.2), (4, 16384, 0.9), (4, 16384, 0.25)])
+def test_union_kernel_layouts(rows, B, keep):
+    """The union RESOLVE kernel at 8 and 16 slots per thread (resolve_union_kernel<8, 8> and
+    <16, 8>): rows x k 2048 > 4096 entries of capacity, the union short (rows keep 90 % of the
+    row before: the 4-entries-per-thread body) or long (25-20 %: past 4096 entries, the full
+    body); 6 steps, the state after the last."""
+    w = W["long"].scaled(L=1, B=B, append=False, force_newest=False)
+    p = Pair(w, steps=6, rows=rows, rows_keep=keep)
+    sizes = []
+    for _ in range(6):
+        for (r, l), v in p.step_gpu_and_oracle().items():
+            sizes.append(int(v[1]) + int(v[2]) + int(v[5]))
+    log("rows %d B %d keep %.2f: union sizes %s" % (rows, B, keep, sizes))
+    assert (max(sizes) > 4096) == (keep < 0.5), sizes
+    p.check_state()
+    p.close()
+
+
 def test_batched_rows():
     w = W["batched"].scaled(R=8, L=2, k=1024, B=3 * 1024)
     p = Pair(w, steps=5, rows=3)
