@@ -436,13 +436,20 @@ def test_duplicates_in_many_patterns_then_valid_steps():
     c.close()
 
 
-def test_buffer_above_8192_slots():
-    """B = 12000 (16 slots per thread in the kernel's blocked layout), k = 512."""
-    w = W["tiny"].scaled(B=12000, k=512, ctx=65536, steps=6, R=2)
-    p = Pair(w, wgs=2)
+@pytest.mark.parametrize("B,k,keep,wgs", [(12000, 512, 0.85, 2), (16384, 2048, 0.85, 2), (16384, 8192, 0.5, 0)])
+def test_buffer_above_8192_slots(B, k, keep, wgs):
+    """Large buffers in the kernel's blocked layout: B = 12000 (12 slots per thread), B = 16384
+    (16 slots per thread) with 2 and 8 list entries per thread; the largest list fills the
+    buffer at its third step and then evicts (with the default 32 workgroups per request: at 2,
+    each wave's miss list would have to hold half the list, more LDS than a workgroup has).
+    State compared after every step."""
+    w = W["tiny"].scaled(B=B, k=k, ctx=65536, steps=6, R=2, keep_p=keep)
+    p = Pair(w, wgs=wgs)
     for _ in range(w.steps):
         p.step_gpu_and_oracle()
         p.check_state()
+    if k == 8192:
+        assert p.evicted > 0, p.evicted
     p.close()
 
 
