@@ -72,6 +72,21 @@ def test_long_with_write_through():
         p.close()
 
 
+@pytest.mark.parametrize("k,B,fp8", [(4096, 4096, False), (3000, 6000, False), (4096, 4096, True)])
+def test_four_entries_per_thread(k, B, fp8):
+    """Lists longer than 2048 entries (4 per thread in workgroup 0: resolve_kernel<4, 4, true>,
+    <8, 4, true> and the FP8 kernel <4, 4>), 2 requests of the long shape, write-through; 8
+    steps, the buffer filled and evicting from the third."""
+    w = W["long"].scaled(R=2, L=1, k=k, B=B, ctx=65536, steps=8, keep_p=0.6)
+    log("k=%d B=%d fp8=%s" % (k, B, fp8))
+    p = Pair(w, fused_heads=16, fp8=fp8)
+    try:
+        run(p)
+        assert p.evicted > 0, p.evicted
+    finally:
+        p.close()
+
+
 def test_batched_four_requests():
     w = W["batched"].scaled(R=4, L=2, steps=4, B=4096)
     log("batched R=4 L=2 B=4096")
