@@ -436,19 +436,21 @@ def test_duplicates_in_many_patterns_then_valid_steps():
     c.close()
 
 
-@pytest.mark.parametrize("B,k,keep,wgs", [(12000, 512, 0.85, 2), (16384, 2048, 0.85, 2), (16384, 8192, 0.5, 0)])
-def test_buffer_above_8192_slots(B, k, keep, wgs):
-    """Large buffers in the kernel's blocked layout: B = 12000 (12 slots per thread), B = 16384
-    (16 slots per thread) with 2 and 8 list entries per thread; the largest list fills the
-    buffer at its third step and then evicts (with the default 32 workgroups per request: at 2,
-    each wave's miss list would have to hold half the list, more LDS than a workgroup has).
-    State compared after every step."""
+@pytest.mark.parametrize("B,k,keep,wgs", [(12000, 512, 0.85, 2), (16384, 2048, 0.85, 2), (16384, 8192, 0.5, 0),
+                                          (4096, 4096, 0.6, 0), (6000, 3000, 0.6, 0)])
+def test_large_lists_and_buffers(B, k, keep, wgs):
+    """Large buffers and lists in the kernel's blocked layout: B = 12000 (12 slots per thread),
+    B = 16384 (16 slots per thread) with 2 and 8 list entries per thread, and lists of 4096 and
+    3000 entries (4 per thread) into B = 4096 and 6000.  The list of 8192 fills its buffer at
+    the third step and then evicts (with the default 32 workgroups per request: at 2, each
+    wave's miss list would have to hold half the list, more LDS than a workgroup has); so do
+    the lists of 4096 and 3000.  State compared after every step."""
     w = W["tiny"].scaled(B=B, k=k, ctx=65536, steps=6, R=2, keep_p=keep)
     p = Pair(w, wgs=wgs)
     for _ in range(w.steps):
         p.step_gpu_and_oracle()
         p.check_state()
-    if k == 8192:
+    if k >= 3000:
         assert p.evicted > 0, p.evicted
     p.close()
 
