@@ -92,6 +92,15 @@ def test_long_full_all_steps():
     p.close()
 
 
+def test_shared_full_context_eight_requests():
+    """The shared-index workload at its full context (131072 tokens) with 8 of its 16 requests
+    (38.6 GB of pinned records; 16 would need 77.3 GB, more than the box pins): 32 layers, 8
+    anchors + 24 shared layers replayed on a side stream, 12 steps.  Each (request, layer)
+    cache is independent, so the other 8 requests would resolve the same way; the 16-request
+    launch itself runs in the test below at ctx 98304."""
+    run(W["shared"].scaled(R=8), 12, (range(0, 32, 5), [0, 3, 7]), "shared R=8 ctx 131072")
+
+
 def test_shared_full_shape():
     """16 requests x 32 layers (8 anchors + 24 shared), the shared-index workload's full shape
     except the context: the box pins at most about 64 GiB of host memory, so the 131072-token
