@@ -227,10 +227,10 @@ class Pair:
                 for r in range(nr):
                     exp = results[(r, l)][0]
                     if not np.array_equal(got[r], exp):
-                        bad = np.nonzero(got[r] != exp)[0]
+                        bad = np.argwhere(got[r] != exp)  # (entry) or (row, entry) indices
                         raise AssertionError("slots differ at step %d r %d l %d: %d entries, first %s"
-                                             % (t, r, l, bad.size, [(int(i), int(got[r][i]), int(exp[i]))
-                                                                      for i in bad[:5]]))
+                                             % (t, r, l, len(bad), [(tuple(int(x) for x in i), int(got[r][tuple(i)]),
+                                                                     int(exp[tuple(i)])) for i in bad[:5]]))
                 if self.fused_heads:
                     self._check_attention(t, ai, l, q, nr)
         for l in range(w.L):
