@@ -188,6 +188,23 @@ __device__ __forceinline__ int16_t run16_at(const Run16<E>& a, int j) {
   else return (int16_t)(a.w[j >> 1] >> (16 * (j & 1)));
 }
 
+// A request's scalars read before anything else: the padded-request bound, a speculative union's
+// length and the error its union kernel found.  The three loads are issued together and a
+// compiler barrier keeps them from being moved to their uses, which would make one round trip
+// of each; an absent input costs no load.
+struct ReqScalars {
+  int32_t nreq, kvr;
+  uint32_t pre_err;
+};
+__device__ __forceinline__ ReqScalars read_req_scalars(const ResolveParams& p, int r) {
+  ReqScalars rs;
+  rs.nreq = p.num_reqs ? *p.num_reqs : INT32_MAX;
+  rs.kvr = p.kvar ? p.kvar[r] : p.k;
+  rs.pre_err = p.kerr ? p.kerr[r] : 0u;
+  asm volatile("" ::: "memory");
+  return rs;
+}
+
 // E: slots (and LRU positions) per thread, KE: selection entries per thread (both powers
 // of two, KE <= E, EK = ceil(k / NT) <= KE).  ATT: workgroup 0 of the fused kernel (its
 // other workgroups run fetch_attend instead).  It resolves as usual but leaves the page
@@ -196,7 +213,7 @@ __device__ __forceinline__ int16_t run16_at(const Run16<E>& a, int j) {
 // page-table updates and copies the missed records, which the fetch workgroups staged, into
 // their victim slots.  So the page table does not change while the fused kernel runs.
 template <int E, int KE, bool ATT>
-__device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned char* smem) {
+__device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned char* smem, const ReqScalars& rs) {
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits, p.G);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
   int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] position (hash key) of each entry
@@ -216,7 +233,8 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   const int r = blockIdx.x % p.R;
   const int g = blockIdx.x / p.R;
   const bool record = (p.flags & HS_RECORD_PLAN) != 0;
-  if (p.num_reqs && r >= *p.num_reqs) {
+  const uint32_t pre_err = rs.pre_err;
+  if (r >= rs.nreq) {
     // a padded request: untouched, and an empty plan so a replay copies nothing
     if (record && g == 0 && tid == 0) p.ctrl[r * 4 + 2] = 0;
     return;
@@ -226,10 +244,9 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   const int e0 = tid * E;  // first slot / LRU position of this thread
   // entries of this request's list (a speculative union is shorter than its k-entry row), spread
   // over all threads: EK = ceil(kr / NT) <= KE consecutive entries per thread
-  const int kr = p.kvar ? min(p.kvar[r], p.k) : p.k;
+  const int kr = min(rs.kvr, p.k);
   const int EK = (kr + NT - 1) / NT;
   const int i0 = tid * EK;  // first selection entry of this thread
-  const uint32_t pre_err = p.kerr ? p.kerr[r] : 0u;
   if (pre_err) {  // found before the launch (the union of verification rows): nothing changes
     if (g == 0) {
       for (int i = tid; i < p.k; i += NT) p.out[(size_t)r * p.k + i] = -1;
@@ -290,7 +307,9 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   auto share_raw = [&](int q) -> int32_t {
     const int e = q * NT + lane * NW + wid;
     const int i = f_lo + e;
-    return (share_fetch && e < f_n) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : -1;
+    // (unconditional, from entry 0 outside the share: the caller uses the value only inside it,
+    // and a load whose value a branch computes on is waited for in that branch)
+    return selr[(share_fetch && e < f_n) ? (i >> p.bt_shift) : 0];
   };
   const int32_t fraw0 = share_raw(0);
   // vector loads and stores of a thread's run: every half of the slot map starts 16-byte aligned
@@ -315,6 +334,9 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   // fused: workgroup 0's report to the finish kernel
   uint32_t* hdr = ATT ? p.att_hdr + (size_t)r * 4 : nullptr;
+  // (a compiler barrier: the loads above stay here, in the first round trip, instead of being
+  // moved past the short-path test to their first use; it emits no instruction)
+  asm volatile("" ::: "memory");
   // ---- short-sequence fast path ("HiSparse 深度解析" §5.4, §5.5): a request admitted short
   // keeps its tokens in slot order while its context fits B, so every position is its own
   // slot: no hash, no LRU, no host IO (only the range is checked)
@@ -356,22 +378,10 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     }
     return;
   }
-  // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
-  // map, so it names the slot of a hit) and, with a resident tier, its resident page: the
-  // second round trip (after the short-path test, which needs only the first).
+  // The second round trip (after the short-path test, which needs only the first): the
+  // page-table entries of the selected positions and, with a resident tier, their resident pages.
   const bool tiered = p.rtable != nullptr;
   const int32_t* rtr = p.rtable + (tiered ? (size_t)r * p.rt_stride : 0);
-  uint64_t ptv[KE];
-  int32_t rpg[KE];
-#pragma unroll
-  for (int j = 0; j < KE; ++j) {
-    const int i = i0 + j;
-    const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
-                                     : (int64_t)raw[j];
-    const bool ok = j < EK && i < kr && pos64 >= 0 && pos64 < ctx;
-    ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
-    rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
-  }
   // Misses known early from the page table: a selected position whose entry is -1 (and
   // that the resident tier does not serve) is not on the device.  Their host loads start
   // right after stage 1 and land while stage 3 runs; stage 3 names the slots they go to.
@@ -393,7 +403,22 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     se.res = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
     return se;
   };
+  // (the share's entry first: its page-table load waits only for its own selection entry, while
+  // a wait after the own entries' loads, some of which are skipped, would wait for all of them)
   const ShareEntry f0 = share_entry(0, fraw0);
+  // Each own entry's page-table entry (the page table is kept the exact inverse of the slot
+  // map, so it names the slot of a hit) and resident page.
+  uint64_t ptv[KE];
+  int32_t rpg[KE];
+#pragma unroll
+  for (int j = 0; j < KE; ++j) {
+    const int i = i0 + j;
+    const int64_t pos64 = p.bt_shift ? ((int64_t)raw[j] << p.bt_shift) + (i & ((1 << p.bt_shift) - 1))
+                                     : (int64_t)raw[j];
+    const bool ok = j < EK && i < kr && pos64 >= 0 && pos64 < ctx;
+    ptv[j] = ok ? ptr[pos64] : kPtHostOnly;
+    rpg[j] = (ok && tiered) ? rtr[pos64 >> p.page_shift] : -1;
+  }
   {
     u32x4* h4 = (u32x4*)htab;
     const u32x4 e4 = {~0u, ~0u, ~0u, ~0u};
@@ -402,6 +427,10 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     for (int h = tid; h < (p.B + 7) / 8; h += NT) s4[h] = e4;
   }
   if (tid == 0) {
+    // (an opaque use: without it the compiler folds the arithmetic below into the load's own
+    // branch at entry, and thread 0's wave then waits there for the counter before it issues
+    // its other loads, one more memory round trip for the whole workgroup)
+    asm volatile("" : "+v"(counter_raw));
     const uint64_t launches = launch_number(counter_raw);
     sh[0] = 0; sh[1] = 0; sh[3] = 0;
     sh[2] = (int)(launches & 1u);
@@ -920,7 +949,7 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
       return;
     }
   }
-  resolve_body<E, KE, ATT>(p, smem);
+  resolve_body<E, KE, ATT>(p, smem, read_req_scalars(p, blockIdx.x % p.R));
 }
 
 // RESOLVE over a speculative union whose capacity (rows x k entries) needs KE > kUnionShortKE
@@ -932,19 +961,34 @@ template <int E, int KE>
 __global__ void __launch_bounds__(NT) resolve_union_kernel(ResolveParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
-  const int kr = min(p.kvar[r], p.k);
-  if (kr <= kUnionShortKE * NT) resolve_body<E, kUnionShortKE, false>(p, smem);
-  else resolve_body<E, KE, false>(p, smem);
+  const ReqScalars rs = read_req_scalars(p, r);
+  const int kr = min(rs.kvr, p.k);
+  if (kr <= kUnionShortKE * NT) resolve_body<E, kUnionShortKE, false>(p, smem, rs);
+  else resolve_body<E, KE, false>(p, smem, rs);
   // (every return in resolve_body is taken by the whole workgroup, so all its threads are here)
-  if (g != 0 || (p.num_reqs && r >= *p.num_reqs)) return;
-  __syncthreads();  // workgroup 0's writes of the union's slots are visible to all its threads
-  const bool bad = p.kerr[r] != 0;
-  const int32_t* uo = p.out + (size_t)r * p.k;
+  if (g != 0) return;
+  // The rows' entries (rows_n <= kUnionMaxEntries): all union indices are loaded at once, then
+  // all union slots, so the scatter takes two memory round trips (a loop that loads and uses one
+  // entry at a time waits for both loads of every entry in turn).
+  constexpr int FR = kUnionMaxEntries / NT;
   const int32_t* mp = p.rows_map + (size_t)r * p.k;
+  int32_t u[FR], v[FR];
+#pragma unroll
+  for (int j = 0; j < FR; ++j) {
+    const int f = j * NT + (int)threadIdx.x;
+    u[j] = mp[f < p.rows_n ? f : 0];
+  }
+  const uint32_t bad = rs.pre_err;
+  if (r >= rs.nreq) return;
+  __syncthreads();  // workgroup 0's writes of the union's slots are visible to all its threads
+  const int32_t* uo = p.out + (size_t)r * p.k;
+#pragma unroll
+  for (int j = 0; j < FR; ++j) v[j] = uo[(u[j] >= 0 && u[j] < p.k) ? u[j] : 0];
   int32_t* ro = p.rows_out + (size_t)r * p.rows_n;
-  for (int f = threadIdx.x; f < p.rows_n; f += NT) {
-    const int32_t u = mp[f];
-    ro[f] = (bad || u < 0) ? -1 : uo[u];
+#pragma unroll
+  for (int j = 0; j < FR; ++j) {
+    const int f = j * NT + (int)threadIdx.x;
+    if (f < p.rows_n) ro[f] = (bad || u[j] < 0) ? -1 : v[j];
   }
 }
 
@@ -957,7 +1001,7 @@ __global__ void __launch_bounds__(NT) resolve_f8_kernel(ResolveParams p) {
     fetch_attend<true>(p, smem);
     return;
   }
-  resolve_body<E, KE, true>(p, smem);
+  resolve_body<E, KE, true>(p, smem, read_req_scalars(p, blockIdx.x % p.R));
 }
 
 // Union of the verification rows of one speculative step ("HiSparse 深度解析" §6.5
@@ -984,21 +1028,48 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
   uint32_t* carry = meta + H;             // scan carries
   int* sh = (int*)(carry + 4 * NW);       // [0] error bits
   const int r = blockIdx.x, tid = threadIdx.x;
-  if (p.num_reqs && r >= *p.num_reqs) return;
   const int n = p.rows * p.k;
   const int i0 = tid * EU;
-  const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
   const int32_t* selr = p.sel + (size_t)r * p.rows * p.kb;
+  // Row and index of the thread's first entry by a reciprocal and one correction step (the
+  // quotient is below 8192, so the float estimate is off by at most one), then stepped entry
+  // by entry: no integer division per entry.
+  int q = (int)((float)i0 * __builtin_amdgcn_rcpf((float)p.k));
+  int i = i0 - q * p.k;
+  if (i < 0) {
+    --q;
+    i += p.k;
+  } else if (i >= p.k) {
+    ++q;
+    i -= p.k;
+  }
+  const int bmask = (1 << p.bt_shift) - 1;
   uint32_t err = 0;
-  int32_t pos[EU];
+  int32_t pos[EU], raw[EU];
+  int qr[EU], ir[EU];  // row and index of each entry
+  // All loads first, unconditionally (an entry past the end reads the list's first one): a load
+  // whose value is used inside its own branch is waited for there, one round trip per entry.
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
-    const int f = i0 + j;
+    qr[j] = q;
+    ir[j] = i;
+    const bool in = i0 + j < n;
+    // with block selection (bt_shift > 0) entry i is token i & bmask of block i >> bt_shift
+    raw[j] = selr[in ? (size_t)q * p.kb + (i >> p.bt_shift) : 0];
+    if (++i == p.k) {
+      i = 0;
+      ++q;
+    }
+  }
+  // (a request past *num_reqs has its rows in the arrays too, so the loads above stay in bounds)
+  const int32_t ctx_r = p.ctx_len[r];
+  if (p.num_reqs && r >= *p.num_reqs) return;
+  const int64_t ctx = min((int64_t)ctx_r, p.max_positions);
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
     pos[j] = -1;
-    if (f >= n) continue;
-    const int q = f / p.k, i = f - q * p.k;
-    const int32_t raw = selr[(size_t)q * p.kb + (p.bt_shift ? (i >> p.bt_shift) : i)];
-    const int64_t pos64 = p.bt_shift ? ((int64_t)raw << p.bt_shift) + (i & ((1 << p.bt_shift) - 1)) : (int64_t)raw;
+    if (i0 + j >= n) continue;
+    const int64_t pos64 = ((int64_t)raw[j] << p.bt_shift) + (ir[j] & bmask);
     if (pos64 < 0 || pos64 >= ctx) err |= HS_ERR_RANGE;
     else pos[j] = (int32_t)pos64;
   }
@@ -1049,9 +1120,8 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
     if (bkt[j] < 0) continue;
-    const int q = (i0 + j) / p.k;
-    const uint32_t old = atomicOr(&meta[bkt[j]], 1u << q);
-    if (old & (1u << q)) {
+    const uint32_t old = atomicOr(&meta[bkt[j]], 1u << qr[j]);
+    if (old & (1u << qr[j])) {
       err |= HS_ERR_DUP;
       dupb |= 1u << j;
     }
@@ -1061,8 +1131,7 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
     if (bkt[j] < 0 || ((dupb >> j) & 1u)) continue;
-    const int q = (i0 + j) / p.k;
-    if ((meta[bkt[j]] & ((1u << q) - 1u)) == 0) first |= 1u << j;
+    if ((meta[bkt[j]] & ((1u << qr[j]) - 1u)) == 0) first |= 1u << j;
   }
   if (err) atomicOr((unsigned*)&sh[0], err);
   int ru, rz, nu, tz;
