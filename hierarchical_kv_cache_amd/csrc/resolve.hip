@@ -122,16 +122,24 @@ __device__ __forceinline__ void block_ranks2(uint32_t a, uint32_t b, uint32_t* b
   rb = bb + lb;
 }
 
-// E consecutive int32 elements base .. base+E-1 of src (n valid, `fill` past the end);
-// 16-byte vector loads when the run is whole and aligned.
+// E consecutive int32 elements base .. base+E-1 of src (n valid, `fill` past the end); 16-byte
+// vector loads with vec (n % 4 == 0, so every 4-element group of a run lies wholly inside or
+// wholly past the end).  E < 8: vector loads for a whole run, element loads otherwise.  E >= 8:
+// the buffer sizes that use these layouts leave the last waves' runs partial or empty, and a
+// branch that only some threads of a wave take runs both arms, the second one's loads waiting
+// for the first one's (they write the same registers), which waits for every earlier load of
+// the wave; so with vec every thread takes the vector loads, a group past the end reads the
+// last group instead, and the caller ignores elements past the end.  (At E = 4 the per-thread
+// test measured faster.)
 template <int E>
 __device__ __forceinline__ void load_run32(const int32_t* __restrict__ src, int n, int base, bool vec,
                                            int32_t (&out)[E], int32_t fill) {
   if constexpr (E % 4 == 0) {
-    if (vec && base + E <= n) {
+    if (vec && (E >= 8 || base + E <= n)) {
 #pragma unroll
       for (int v = 0; v < E / 4; ++v) {
-        const u32x4 x = *((const u32x4*)(src + base) + v);
+        const int gb = base + 4 * v;
+        const u32x4 x = *(const u32x4*)(src + (E < 8 || gb + 4 <= n ? gb : n - 4));
         out[4 * v + 0] = (int32_t)x[0];
         out[4 * v + 1] = (int32_t)x[1];
         out[4 * v + 2] = (int32_t)x[2];
@@ -146,27 +154,31 @@ __device__ __forceinline__ void load_run32(const int32_t* __restrict__ src, int 
 
 // The same for int16 elements (8 per 16-byte load, 4 per 8-byte load), kept as the packed
 // 32-bit words they arrive in (element j in half j & 1 of word j / 2) and unpacked where they
-// are used (run16_at), so nothing waits for the loads here.
+// are used (run16_at), so nothing waits for the loads here.  nalloc (a multiple of 8, >= n):
+// elements the array holds; at E >= 8 a 16-byte group may read elements n .. nalloc-1, which
+// the caller ignores like every element past n.
 template <int E>
 struct Run16 {
   uint32_t w[E >= 2 ? E / 2 : 1];
 };
 template <int E>
-__device__ __forceinline__ void load_run16(const int16_t* __restrict__ src, int n, int base, bool vec,
+__device__ __forceinline__ void load_run16(const int16_t* __restrict__ src, int n, int nalloc, int base, bool vec,
                                            Run16<E>& out, int16_t fill) {
   if constexpr (E >= 4 && E % 4 == 0) {
-    if (vec && base + E <= n) {
+    if (vec && (E >= 8 || base + E <= n)) {
       if constexpr (E % 8 != 0) {  // E = 4, 12: the run starts 8-byte aligned (8-byte loads)
 #pragma unroll
         for (int v = 0; v < E / 4; ++v) {
-          const u32x2 x = *((const u32x2*)(src + base) + v);
+          const int gb = base + 4 * v;
+          const u32x2 x = *(const u32x2*)(src + (E < 8 || gb + 4 <= n ? gb : n - 4));
           out.w[2 * v] = x[0];
           out.w[2 * v + 1] = x[1];
         }
       } else {
 #pragma unroll
         for (int v = 0; v < E / 8; ++v) {
-          const u32x4 x = *((const u32x4*)(src + base) + v);
+          const int gb = base + 8 * v;
+          const u32x4 x = *(const u32x4*)(src + (E < 8 || gb + 8 <= nalloc ? gb : nalloc - 8));
 #pragma unroll
           for (int q = 0; q < 4; ++q) out.w[4 * v + q] = x[q];
         }
@@ -327,8 +339,8 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
       load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
     }
   }
-  load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, e0, bvec, lra, 0);
-  load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, e0, bvec, lrb, 0);
+  load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, p.Bpad, e0, bvec, lra, 0);
+  load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, p.Bpad, e0, bvec, lrb, 0);
   // this (request, layer)'s host records (the pointer table is read at entry with the rest)
   const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
   uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
@@ -679,7 +691,7 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   {
     int16_t sf[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) sf[j] = sown[lro[j]];
+    for (int j = 0; j < E; ++j) sf[j] = sown[E < 8 || e0 + j < p.B ? lro[j] : 0];  // (past B: not a slot)
 #pragma unroll
     for (int j = 0; j < E; ++j)
       if (e0 + j < p.B && sf[j] == -1) ebits |= 1u << j;
