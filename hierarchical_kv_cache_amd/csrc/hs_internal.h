@@ -332,13 +332,13 @@ hipError_t launch_resolve_attn(const ResolveParams& p, size_t lds_bytes, hipStre
                                const KernelTiming* tm = nullptr);
 hipError_t launch_union(const UnionParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
-// the union kernel's LDS: per bucket the position and the row mask / union index, then the
-// scan carries (2 x 2 per wave) and shared words
-inline size_t union_lds_bytes(int hash_bits) {
-  return (size_t(8) << hash_bits) + 4 * (4 * (kResolveThreads / 64) + 8);
-}
 hipError_t set_union_lds_limit(size_t lds_bytes);
 constexpr int kUnionMaxEntries = 8192;  // rows * top_k of one speculative resolve
+// the union kernel's LDS: per bucket the position and the row mask / union index, then the
+// rank counts (one per wave and entry slot: kUnionMaxEntries / 64) and shared words
+inline size_t union_lds_bytes(int hash_bits) {
+  return (size_t(8) << hash_bits) + 4 * (kUnionMaxEntries / 64 + 8);
+}
 hipError_t set_resolve_lds_limit(size_t lds_bytes);
 hipError_t launch_append(const AppendParams& p, hipStream_t s, bool write_through);
 hipError_t launch_backup(const AppendParams& p, hipStream_t s);

@@ -1020,16 +1020,52 @@ __global__ void __launch_bounds__(NT) resolve_f8_kernel(ResolveParams p) {
 // comparison table; "HiSparse local KV offload architecture" (docs.vllm.ai),
 // speculative decoding): rows that select the same position share one slot, so the
 // rows are resolved as one list, their union in first-reference order (row by row,
-// list order within a row).  One workgroup per request:
+// list order within a row).  One workgroup per request; entry f (row-major over the rows)
+// belongs to thread f % NT as its slot f / NT, so every load and store of the entries is
+// coalesced:
 //   - every entry finds or inserts its position in an LDS hash (one bucket per distinct
 //     position: a plain store into the home bucket, then compare-and-swap linear probing
-//     for the entries whose home bucket holds another position);
+//     for the entries whose home bucket holds another position, all of a thread's entries
+//     probing together);
 //   - each entry ORs its row's bit into its bucket's mask: a bit already set is a
 //     duplicate inside the row; once every row's bits are in, an entry whose mask has no
 //     lower bit is its position's first reference;
-//   - the first references are ranked in list order (ballot + mbcnt scan); the rank is
-//     the position's index in the union, stored in the bucket for the other entries.
+//   - the first references are ranked in list order (per slot and wave a ballot count, then
+//     one scan of those counts); the rank is the position's index in the union, stored in
+//     the bucket for the other entries.
 constexpr int EU = kUnionMaxEntries / NT;  // entries per thread
+
+// Exclusive ranks in entry order (entry j NT + t for bit j of thread t) of the set bits of
+// `bits`, and their total.  cnt: EU x NW words of LDS.  Each wave ballots per slot and
+// stores its counts; after one barrier every wave scans all EU x NW counts (two per lane)
+// and takes its own prefixes by lane shuffles.
+__device__ __forceinline__ void union_ranks(uint32_t bits, uint32_t* cnt, int (&rank)[EU], int& total) {
+  static_assert(EU * NW == 128, "two counts per lane");
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int below[EU];
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
+    const uint64_t m = __ballot((bits >> j) & 1u);
+    below[j] = lanes_below(m);
+    if (lane == 0) cnt[j * NW + wid] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  const int c0 = (int)cnt[2 * lane], c1 = (int)cnt[2 * lane + 1];
+  int incl = c0 + c1;  // inclusive scan over the lanes of the pair sums
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  const int ex0 = incl - c0 - c1;  // exclusive prefix of count 2 lane; of 2 lane + 1: ex0 + c0
+  total = __shfl(incl, 63);
+#pragma unroll
+  for (int j = 0; j < EU; ++j) {
+    const int idx = j * NW + wid;
+    const int e = __shfl(ex0, idx >> 1), a = __shfl(c0, idx >> 1);
+    rank[j] = e + ((idx & 1) ? a : 0) + below[j];
+  }
+}
 
 __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1037,50 +1073,45 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
   const uint32_t hmask = (uint32_t)H - 1;
   int32_t* key = (int32_t*)smem;          // [H] position, -1 empty
   uint32_t* meta = (uint32_t*)(key + H);  // [H] row mask, then union index
-  uint32_t* carry = meta + H;             // scan carries
-  int* sh = (int*)(carry + 4 * NW);       // [0] error bits
+  uint32_t* cnt = meta + H;               // [EU x NW] rank counts
+  int* sh = (int*)(cnt + EU * NW);        // [0] error bits
   const int r = blockIdx.x, tid = threadIdx.x;
   const int n = p.rows * p.k;
-  const int i0 = tid * EU;
   const int32_t* selr = p.sel + (size_t)r * p.rows * p.kb;
-  // Row and index of the thread's first entry by a reciprocal and one correction step (the
-  // quotient is below 8192, so the float estimate is off by at most one), then stepped entry
-  // by entry: no integer division per entry.
-  int q = (int)((float)i0 * __builtin_amdgcn_rcpf((float)p.k));
-  int i = i0 - q * p.k;
-  if (i < 0) {
-    --q;
-    i += p.k;
-  } else if (i >= p.k) {
-    ++q;
-    i -= p.k;
-  }
+  // Row of each entry by a reciprocal and one correction step (the quotient is below 8192, so
+  // the float estimate is off by at most one): no integer division.
+  const float rk = __builtin_amdgcn_rcpf((float)p.k);
   const int bmask = (1 << p.bt_shift) - 1;
-  uint32_t err = 0;
   int32_t pos[EU], raw[EU];
   int qr[EU], ir[EU];  // row and index of each entry
   // All loads first, unconditionally (an entry past the end reads the list's first one): a load
   // whose value is used inside its own branch is waited for there, one round trip per entry.
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
+    const int f = j * NT + tid;
+    int q = (int)((float)f * rk);
+    int i = f - q * p.k;
+    if (i < 0) {
+      --q;
+      i += p.k;
+    } else if (i >= p.k) {
+      ++q;
+      i -= p.k;
+    }
     qr[j] = q;
     ir[j] = i;
-    const bool in = i0 + j < n;
     // with block selection (bt_shift > 0) entry i is token i & bmask of block i >> bt_shift
-    raw[j] = selr[in ? (size_t)q * p.kb + (i >> p.bt_shift) : 0];
-    if (++i == p.k) {
-      i = 0;
-      ++q;
-    }
+    raw[j] = selr[f < n ? (size_t)q * p.kb + (i >> p.bt_shift) : 0];
   }
   // (a request past *num_reqs has its rows in the arrays too, so the loads above stay in bounds)
   const int32_t ctx_r = p.ctx_len[r];
   if (p.num_reqs && r >= *p.num_reqs) return;
   const int64_t ctx = min((int64_t)ctx_r, p.max_positions);
+  uint32_t err = 0;
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
     pos[j] = -1;
-    if (i0 + j >= n) continue;
+    if (j * NT + tid >= n) continue;
     const int64_t pos64 = ((int64_t)raw[j] << p.bt_shift) + (ir[j] & bmask);
     if (pos64 < 0 || pos64 >= ctx) err |= HS_ERR_RANGE;
     else pos[j] = (int32_t)pos64;
@@ -1107,22 +1138,33 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
     if (pos[j] >= 0) key[hh[j]] = pos[j];
   }
   __syncthreads();
+  uint32_t pend = 0;  // entries still probing
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
     bkt[j] = -1;
     if (pos[j] < 0) continue;
-    if (key[hh[j]] == pos[j]) {
-      bkt[j] = (int32_t)hh[j];
-      continue;
+    if (key[hh[j]] == pos[j]) bkt[j] = (int32_t)hh[j];
+    else {
+      pend |= 1u << j;
+      hh[j] = (hh[j] + 1) & hmask;
     }
-    uint32_t h = (hh[j] + 1) & hmask;
-    for (int probe = 1; probe < H; ++probe) {  // the table is at most half full: this ends
-      const int32_t prev = atomicCAS(&key[h], -1, pos[j]);
-      if (prev == -1 || prev == pos[j]) {
-        bkt[j] = (int32_t)h;
-        break;
+  }
+  // The probing entries of a thread take one step each per round, their compare-and-swaps
+  // issued together.  (The table is at most half full, so every probe sequence meets an empty
+  // bucket or its position within H steps.)
+  for (int probe = 1; pend != 0 && probe < H; ++probe) {
+    int32_t prev[EU];
+#pragma unroll
+    for (int j = 0; j < EU; ++j) prev[j] = ((pend >> j) & 1u) ? atomicCAS(&key[hh[j]], -1, pos[j]) : 0;
+#pragma unroll
+    for (int j = 0; j < EU; ++j) {
+      if (!((pend >> j) & 1u)) continue;
+      if (prev[j] == -1 || prev[j] == pos[j]) {
+        bkt[j] = (int32_t)hh[j];
+        pend &= ~(1u << j);
+      } else {
+        hh[j] = (hh[j] + 1) & hmask;
       }
-      h = (h + 1) & hmask;
     }
   }
   // Each entry ORs its row's bit into its bucket's mask (one pass: the old mask already shows
@@ -1146,15 +1188,14 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
     if ((meta[bkt[j]] & ((1u << qr[j]) - 1u)) == 0) first |= 1u << j;
   }
   if (err) atomicOr((unsigned*)&sh[0], err);
-  int ru, rz, nu, tz;
-  block_ranks2<EU>(first, 0u, carry, ru, rz, nu, tz);  // (its barrier also publishes sh[0])
+  int ru[EU], nu;
+  union_ranks(first, cnt, ru, nu);  // (its barrier also publishes sh[0])
   int32_t* unir = p.uni + (size_t)r * p.kmax;
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
     if ((first >> j) & 1u) {
-      meta[bkt[j]] = (uint32_t)ru;
-      unir[ru] = pos[j];
-      ++ru;
+      meta[bkt[j]] = (uint32_t)ru[j];
+      unir[ru[j]] = pos[j];
     }
   }
   __syncthreads();
@@ -1162,7 +1203,7 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
   int32_t* mapr = p.map + (size_t)r * p.kmax;
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
-    const int f = i0 + j;
+    const int f = j * NT + tid;
     if (f < n) mapr[f] = bkt[j] >= 0 ? (int32_t)meta[bkt[j]] : -1;
   }
   if (tid == 0) {

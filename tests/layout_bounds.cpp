@@ -128,8 +128,11 @@ int main() {
     while ((size_t(1) << bits) < 2 * size_t(kmax)) ++bits;
     CHECK(union_lds_bytes(bits) <= kLdsMax && (size_t(1) << bits) >= 2 * size_t(kUnionMaxEntries),
           "union LDS %zu", union_lds_bytes(bits));
-    // the union kernel's thread runs: EU entries per thread cover every entry
+    // the union kernel's entries: EU slots per thread cover every entry, and after the table its
+    // rank counts (one per slot and wave) and the shared error word
     CHECK(size_t(kUnionMaxEntries / NT) * NT >= size_t(kUnionMaxEntries), "union entries per thread");
+    CHECK(union_lds_bytes(bits) >= (size_t(8) << bits) + 4 * (size_t(kUnionMaxEntries / NT) * NW + 1),
+          "union rank counts");
   }
   // the fused kernel: the fetch workgroups' tile, query rows and scratch
   for (int f8 = 0; f8 < 2; ++f8) {
