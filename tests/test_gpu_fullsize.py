@@ -95,10 +95,12 @@ def test_long_full_all_steps():
 def test_shared_full_context_eight_requests():
     """The shared-index workload at its full context (131072 tokens) with 8 of its 16 requests
     (38.6 GB of pinned records; 16 would need 77.3 GB, more than the box pins): 32 layers, 8
-    anchors + 24 shared layers replayed on a side stream, 12 steps.  Each (request, layer)
-    cache is independent, so the other 8 requests would resolve the same way; the 16-request
-    launch itself runs in the test below at ctx 98304."""
-    run(W["shared"].scaled(R=8), 12, (range(0, 32, 5), [0, 3, 7]), "shared R=8 ctx 131072")
+    anchors + 24 shared layers replayed on a side stream, all 64 steps (the buffer fills at
+    about step 9, so most of them evict).  Each (request, layer) cache is independent, so the
+    other 8 requests would resolve the same way; the 16-request launch itself runs in the test
+    below at ctx 98304."""
+    run(W["shared"].scaled(R=8), 64, (range(0, 32, 5), [0, 3, 7]), "shared R=8 ctx 131072",
+        min_evicting_steps=40)
 
 
 def test_shared_full_shape():
