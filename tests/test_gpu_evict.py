@@ -102,6 +102,24 @@ def test_eight_slots_per_thread_every_step(fused):
         p.close()
 
 
+@pytest.mark.parametrize("B", [2052, 3000, 3002])
+@pytest.mark.parametrize("fused", [False, True])
+def test_four_slots_per_thread_partial_tail(B, fused):
+    """4 slots per thread where the last threads' runs of slots lie past B (B = 2052 and 3000:
+    every thread loads a whole 16-byte group of the slot map and LRU order, the ones past the end
+    reading the last group and ignoring it; B = 3002, not a multiple of 4: element loads), k 2048,
+    2 requests, reuse 0.5, the state after every step for 10 steps past the buffer-fill point,
+    through hs_resolve and hs_resolve_attn."""
+    w = W["batched"].scaled(R=2, L=1, B=B, keep_p=0.5)
+    log("B=%d R=2 keep 0.5, %s" % (B, "hs_resolve_attn" if fused else "hs_resolve"))
+    p = Pair(w, steps=10, fused_heads=16 if fused else 0)
+    try:
+        first = drive(p, 10, every_step_state=True)
+        assert p.evicted > 0 and first is not None and first <= 4, (p.evicted, first)
+    finally:
+        p.close()
+
+
 def test_rows_sixteen_slots_per_thread_past_fill():
     """hs_resolve_rows: 4 verification rows of k 2048 into B = 10240 slots (16 slots per
     thread, the union of about 2650 positions resolved as one list), the long request with
