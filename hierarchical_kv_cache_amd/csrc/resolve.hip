@@ -1028,9 +1028,9 @@ __global__ void __launch_bounds__(NT) resolve_f8_kernel(ResolveParams p) {
 //     position: a plain store into the home bucket, then compare-and-swap linear probing
 //     for the entries whose home bucket holds another position, all of a thread's entries
 //     probing together);
-//   - each entry ORs its row's bit into its bucket's mask: a bit already set is a
-//     duplicate inside the row; once every row's bits are in, an entry whose mask has no
-//     lower bit is its position's first reference;
+//   - each entry adds its row's bit and a count into its bucket's word: once every row's
+//     entries are in, fewer set row bits than entries is a duplicate inside a row, and an
+//     entry whose word has no lower row bit is its position's first reference;
 //   - the first references are ranked in list order (per slot and wave a ballot count, then
 //     one scan of those counts); the rank is the position's index in the union, stored in
 //     the bucket for the other entries.
@@ -1168,25 +1168,25 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
       }
     }
   }
-  // Each entry ORs its row's bit into its bucket's mask (one pass: the old mask already shows
-  // a duplicate inside the row); after the barrier an entry is its position's first reference
-  // when no earlier row's bit is set.  A duplicate is never the first reference.
-  uint32_t dupb = 0;
+  // Each entry adds 2^16 + 2^row to its bucket's word, with no return value (the LDS takes
+  // these in a stream; returning atomics cost a round trip each): the high half counts the
+  // bucket's entries, the low half sums their row bits (rows <= 16).  After the barrier the
+  // row bits are all distinct -- no duplicate inside a row -- exactly when the low half has as
+  // many set bits as the high half counts (a repeated row bit carries, which leaves fewer set
+  // bits than entries).  Then an entry is its position's first reference when no earlier
+  // row's bit is set.  A bucket with a duplicate makes the request's error, and none of its
+  // entries is a first reference.
 #pragma unroll
-  for (int j = 0; j < EU; ++j) {
-    if (bkt[j] < 0) continue;
-    const uint32_t old = atomicOr(&meta[bkt[j]], 1u << qr[j]);
-    if (old & (1u << qr[j])) {
-      err |= HS_ERR_DUP;
-      dupb |= 1u << j;
-    }
-  }
+  for (int j = 0; j < EU; ++j)
+    if (bkt[j] >= 0) atomicAdd(&meta[bkt[j]], (1u << 16) + (1u << qr[j]));
   __syncthreads();
   uint32_t first = 0;
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
-    if (bkt[j] < 0 || ((dupb >> j) & 1u)) continue;
-    if ((meta[bkt[j]] & ((1u << qr[j]) - 1u)) == 0) first |= 1u << j;
+    if (bkt[j] < 0) continue;
+    const uint32_t mm = meta[bkt[j]];
+    if ((uint32_t)__popc(mm & 0xFFFFu) != (mm >> 16)) err |= HS_ERR_DUP;
+    else if ((mm & ((1u << qr[j]) - 1u)) == 0) first |= 1u << j;
   }
   if (err) atomicOr((unsigned*)&sh[0], err);
   int ru[EU], nu;

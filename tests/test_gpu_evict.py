@@ -73,6 +73,23 @@ def test_fused_batched_past_fill():
         p.close()
 
 
+def test_fused_fp8_past_fill():
+    """hs_resolve_attn with FP8 records (656 bytes: the fused kernel's FP8 tiles, the staged raw
+    records and the finish kernel's copies of them) at the long request's shape (k 2048, B 4096,
+    2 of the 8 layers, write-through) and at 32 requests (one layer), past the buffer-fill point:
+    24 and 20 steps, the state at checkpoints and the attention every step."""
+    for w, steps, label in ((W["long"].scaled(L=2), 24, "fp8 fused long 1x2"),
+                            (W["batched"].scaled(L=1, B=4096), 20, "fp8 fused batched 32x1")):
+        log("%s B=4096, %d steps" % (label, steps))
+        p = Pair(w, steps=steps, fused_heads=16, fp8=True)
+        try:
+            assert hk.hs_resolve_attn_wgs(p.h) > 0
+            first = drive(p, steps, check_at=(12, steps), hot_requests=[0, w.R - 1])
+            assert p.evicted > 0 and first is not None and steps - first >= 6, (p.evicted, first)
+        finally:
+            p.close()
+
+
 def test_fused_batched_b8192_past_fill():
     """hs_resolve_attn at 32 requests with B 8192 (8 slots per thread in the resolving
     workgroup), one layer, 36 steps: the buffers fill at about step 28."""
