@@ -61,7 +61,6 @@ namespace {
 
 constexpr int NT = kResolveThreads;
 constexpr int NW = NT / 64;
-constexpr uint64_t kEmpty = ~0ull;  // hash entry: low 32 bits position, high 32 bits list index
 constexpr int kUnroll = 4;
 constexpr int kEarly = 4;  // 16-byte chunks per lane loaded before the victims are known
 
@@ -75,13 +74,6 @@ __device__ __forceinline__ uint32_t hash_pos(int32_t pos, int bits) {
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// This wave's vector-memory operations complete (vmcnt 0).
-__device__ __forceinline__ void vm_wait() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Exclusive block-wide ranks for two flag sets at once.  Thread t owns elements
