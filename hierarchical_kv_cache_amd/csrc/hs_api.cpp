@@ -172,6 +172,7 @@ struct hs_ctx {
   size_t lds_bytes = 0;
   int spec_hash_bits = 0, union_hash_bits = 0;  // RESOLVE of a union, and the union kernel
   size_t spec_lds_bytes = 0;
+  size_t rows_lds_bytes = 0;  // one-launch speculative rows (0: the union kernel, then its RESOLVE)
   int att_G = 0, att_T = 1, att_hash_bits = 0;  // fused RESOLVE + attention; att_G 0: not available
   size_t att_lds = 0;
   // measurement aid: kernel-timed RESOLVE launches (hs_timing_start / hs_timing_read)
@@ -423,6 +424,12 @@ hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_han
       free_ctx(h);
       return fail(HS_EINVAL, "the union of %d rows needs too much LDS", cfg->verify_rows);
     }
+    // a union whose capacity needs more than kUnionShortKE entries per thread: built and resolved
+    // in one launch where the union's table and RESOLVE's carve-up (after the list) fit LDS
+    if ((h->lay.kmax + kResolveThreads - 1) / kResolveThreads > kUnionShortKE) {
+      const size_t lds = rows_lds(h->lay.kmax, cfg->buffer_slots, h->spec_hash_bits, h->G, h->union_hash_bits);
+      if (lds <= prop.sharedMemPerBlock) h->rows_lds_bytes = lds;
+    }
   }
   // fused RESOLVE + attention: G = chunks + 1, when its LDS fits (a half-full hash if need be)
   int T = 1;
@@ -630,7 +637,8 @@ hs_status hs_resolve_rows(hs_handle h, int32_t layer, int32_t rows, const int32_
   u.err = uerr; u.max_positions = h->cfg.max_positions; u.R = R; u.rows = rows; u.k = h->cfg.top_k;
   u.kb = h->cfg.top_k / h->cfg.block_tokens; u.bt_shift = ilog2(h->cfg.block_tokens); u.kmax = kmax;
   u.hash_bits = h->union_hash_bits;
-  HS_HIP(launch_union(u, s));
+  const bool one_launch = h->rows_lds_bytes != 0;
+  if (!one_launch) HS_HIP(launch_union(u, s));
   if ((flags & HS_RECORD_PLAN) && h->plan_free_pending[a]) HS_HIP(hipStreamWaitEvent(s, h->ev_plan_free[a], 0));
   ResolveParams p{};
   p.sel = uni; p.ctx_len = d_ctx_len; p.out = uout; p.stats = d_stats; p.num_reqs = d_num_reqs;
@@ -647,7 +655,8 @@ hs_status hs_resolve_rows(hs_handle h, int32_t layer, int32_t rows, const int32_
   p.cap = h->cap_dev();
   // the rows' slots from the union's (by the union's RESOLVE kernel, or a scatter kernel after it)
   p.rows_out = d_slots_out; p.rows_map = umap; p.rows_n = rows * h->cfg.top_k;
-  HS_HIP(launch_resolve(p, h->spec_lds_bytes, s, h->next_timing()));
+  if (one_launch) HS_HIP(launch_resolve_rows(p, u, h->rows_lds_bytes, s, h->next_timing()));
+  else HS_HIP(launch_resolve(p, h->spec_lds_bytes, s, h->next_timing()));
   return HS_OK;
 }
 

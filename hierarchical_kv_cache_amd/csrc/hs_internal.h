@@ -339,6 +339,18 @@ constexpr int kUnionMaxEntries = 8192;  // rows * top_k of one speculative resol
 inline size_t union_lds_bytes(int hash_bits) {
   return (size_t(8) << hash_bits) + 4 * (kUnionMaxEntries / 64 + 8);
 }
+// The one-launch speculative rows kernel (resolve_rows_kernel): the union's table first; once
+// the union is built its list stays in the table's first 4 kmax bytes (the position array's,
+// 4 H >= 8 kmax bytes) and RESOLVE's carve-up takes the bytes from rows_ulist_bytes(kmax) on.
+__host__ __device__ inline size_t rows_ulist_bytes(int kmax) { return align_up(size_t(4) * kmax, 16); }
+inline size_t rows_lds(int kmax, int B, int resolve_hash_bits, int G, int union_hash_bits) {
+  const size_t u = union_lds_bytes(union_hash_bits);
+  const size_t r = rows_ulist_bytes(kmax) + resolve_lds(kmax, B, resolve_hash_bits, G).total;
+  return u > r ? u : r;
+}
+// one launch for a union whose capacity needs more than kUnionShortKE entries per thread
+hipError_t launch_resolve_rows(const ResolveParams& p, const UnionParams& u, size_t lds_bytes, hipStream_t s,
+                               const KernelTiming* tm = nullptr);
 hipError_t set_resolve_lds_limit(size_t lds_bytes);
 hipError_t launch_append(const AppendParams& p, hipStream_t s, bool write_through);
 hipError_t launch_backup(const AppendParams& p, hipStream_t s);

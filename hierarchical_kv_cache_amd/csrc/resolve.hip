@@ -216,8 +216,11 @@ __device__ __forceinline__ ReqScalars read_req_scalars(const ResolveParams& p, i
 // new position) and a per-request header, and the finish kernel that follows applies the
 // page-table updates and copies the missed records, which the fetch workgroups staged, into
 // their victim slots.  So the page table does not change while the fused kernel runs.
-template <int E, int KE, bool ATT>
-__device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned char* smem, const ReqScalars& rs) {
+// SL: the list is in LDS (sl: kr positions; the rows' union built by resolve_rows_kernel), not
+// in global memory.
+template <int E, int KE, bool ATT, bool SL = false>
+__device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned char* smem, const ReqScalars& rs,
+                                             const int32_t* sl = nullptr) {
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits, p.G);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
   int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] position (hash key) of each entry
@@ -290,7 +293,8 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
 #pragma unroll
   for (int j = 0; j < KE; ++j) {
     const int i = i0 + j;
-    raw[j] = (j < EK && i < kr) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
+    if constexpr (SL) raw[j] = (j < EK && i < kr) ? sl[i] : 0;
+    else raw[j] = (j < EK && i < kr) ? selr[p.bt_shift ? (i >> p.bt_shift) : i] : 0;
   }
   // Fetch-only workgroups (g > 0 of a launch with several) also read the selection entries of
   // their share of the list, spread over the waves: entry e of the share belongs to wave
@@ -313,7 +317,8 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
     const int i = f_lo + e;
     // (unconditional, from entry 0 outside the share: the caller uses the value only inside it,
     // and a load whose value a branch computes on is waited for in that branch)
-    return selr[(share_fetch && e < f_n) ? (i >> p.bt_shift) : 0];
+    if constexpr (SL) return sl[(share_fetch && e < f_n) ? i : 0];
+    else return selr[(share_fetch && e < f_n) ? (i >> p.bt_shift) : 0];
   };
   const int32_t fraw0 = share_raw(0);
   // vector loads and stores of a thread's run: every half of the slot map starts 16-byte aligned
@@ -957,6 +962,33 @@ __global__ void __launch_bounds__(NT) resolve_kernel(ResolveParams p) {
   resolve_body<E, KE, ATT>(p, smem, read_req_scalars(p, blockIdx.x % p.R));
 }
 
+// Workgroup 0 of a union's RESOLVE, after resolve_body: every (row, entry) gets the slot of its
+// union entry (bad: the union's error bits, which make every row slot -1; real: r is a request
+// below *num_reqs).  The rows' entries (rows_n <= kUnionMaxEntries): all union indices are
+// loaded at once, then all union slots, so the scatter takes two memory round trips (a loop that
+// loads and uses one entry at a time waits for both loads of every entry in turn).
+__device__ __forceinline__ void rows_scatter(const ResolveParams& p, int r, uint32_t bad, bool real) {
+  constexpr int FR = kUnionMaxEntries / NT;
+  const int32_t* mp = p.rows_map + (size_t)r * p.k;
+  int32_t u[FR], v[FR];
+#pragma unroll
+  for (int j = 0; j < FR; ++j) {
+    const int f = j * NT + (int)threadIdx.x;
+    u[j] = mp[f < p.rows_n ? f : 0];
+  }
+  if (!real) return;
+  __syncthreads();  // workgroup 0's writes of the union's slots are visible to all its threads
+  const int32_t* uo = p.out + (size_t)r * p.k;
+#pragma unroll
+  for (int j = 0; j < FR; ++j) v[j] = uo[(u[j] >= 0 && u[j] < p.k) ? u[j] : 0];
+  int32_t* ro = p.rows_out + (size_t)r * p.rows_n;
+#pragma unroll
+  for (int j = 0; j < FR; ++j) {
+    const int f = j * NT + (int)threadIdx.x;
+    if (f < p.rows_n) ro[f] = (bad || u[j] < 0) ? -1 : v[j];
+  }
+}
+
 // RESOLVE over a speculative union whose capacity (rows x k entries) needs KE > kUnionShortKE
 // list entries per thread (launch_resolve).  A union of <= kUnionShortKE NT entries, the usual
 // case, takes the body with kUnionShortKE entries per thread, whose registers fit; a longer one
@@ -972,29 +1004,7 @@ __global__ void __launch_bounds__(NT) resolve_union_kernel(ResolveParams p) {
   else resolve_body<E, KE, false>(p, smem, rs);
   // (every return in resolve_body is taken by the whole workgroup, so all its threads are here)
   if (g != 0) return;
-  // The rows' entries (rows_n <= kUnionMaxEntries): all union indices are loaded at once, then
-  // all union slots, so the scatter takes two memory round trips (a loop that loads and uses one
-  // entry at a time waits for both loads of every entry in turn).
-  constexpr int FR = kUnionMaxEntries / NT;
-  const int32_t* mp = p.rows_map + (size_t)r * p.k;
-  int32_t u[FR], v[FR];
-#pragma unroll
-  for (int j = 0; j < FR; ++j) {
-    const int f = j * NT + (int)threadIdx.x;
-    u[j] = mp[f < p.rows_n ? f : 0];
-  }
-  const uint32_t bad = rs.pre_err;
-  if (r >= rs.nreq) return;
-  __syncthreads();  // workgroup 0's writes of the union's slots are visible to all its threads
-  const int32_t* uo = p.out + (size_t)r * p.k;
-#pragma unroll
-  for (int j = 0; j < FR; ++j) v[j] = uo[(u[j] >= 0 && u[j] < p.k) ? u[j] : 0];
-  int32_t* ro = p.rows_out + (size_t)r * p.rows_n;
-#pragma unroll
-  for (int j = 0; j < FR; ++j) {
-    const int f = j * NT + (int)threadIdx.x;
-    if (f < p.rows_n) ro[f] = (bad || u[j] < 0) ? -1 : v[j];
-  }
+  rows_scatter(p, r, rs.pre_err, r < rs.nreq);
 }
 
 // The fused kernel over FP8 records: workgroup 0 as in resolve_kernel<E, KE, true>, the fetch
@@ -1060,15 +1070,21 @@ __device__ __forceinline__ void union_ranks(uint32_t bits, uint32_t* cnt, int (&
   }
 }
 
-__global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// The union of request r's rows, in the union's LDS (smem, union_lds_bytes): the union list goes
+// to `ulist` (global memory, or the first 4 kmax bytes of smem: the position array, dead when
+// the list is written), and with `outputs` each entry's union index to p.map and the union
+// size and error bits to p.cnt / p.err.  nu: the union size (0 on an error), err: the error
+// bits.  Returns false, having written nothing, for a request past *num_reqs.  Every return is
+// taken by the whole workgroup.
+__device__ __forceinline__ bool union_build(const UnionParams& p, unsigned char* smem, int r, int32_t* ulist,
+                                            bool outputs, int& nu_out, uint32_t& err_out) {
   const int H = 1 << p.hash_bits;
   const uint32_t hmask = (uint32_t)H - 1;
   int32_t* key = (int32_t*)smem;          // [H] position, -1 empty
   uint32_t* meta = (uint32_t*)(key + H);  // [H] row mask, then union index
   uint32_t* cnt = meta + H;               // [EU x NW] rank counts
   int* sh = (int*)(cnt + EU * NW);        // [0] error bits
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int n = p.rows * p.k;
   const int32_t* selr = p.sel + (size_t)r * p.rows * p.kb;
   // Row of each entry by a reciprocal and one correction step (the quotient is below 8192, so
@@ -1098,7 +1114,7 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
   }
   // (a request past *num_reqs has its rows in the arrays too, so the loads above stay in bounds)
   const int32_t ctx_r = p.ctx_len[r];
-  if (p.num_reqs && r >= *p.num_reqs) return;
+  if (p.num_reqs && r >= *p.num_reqs) return false;
   const int64_t ctx = min((int64_t)ctx_r, p.max_positions);
   uint32_t err = 0;
 #pragma unroll
@@ -1183,26 +1199,69 @@ __global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
   if (err) atomicOr((unsigned*)&sh[0], err);
   int ru[EU], nu;
   union_ranks(first, cnt, ru, nu);  // (its barrier also publishes sh[0])
-  int32_t* unir = p.uni + (size_t)r * p.kmax;
 #pragma unroll
   for (int j = 0; j < EU; ++j) {
     if ((first >> j) & 1u) {
       meta[bkt[j]] = (uint32_t)ru[j];
-      unir[ru[j]] = pos[j];
+      ulist[ru[j]] = pos[j];
     }
   }
   __syncthreads();
   const uint32_t e = (uint32_t)sh[0];
-  int32_t* mapr = p.map + (size_t)r * p.kmax;
+  if (outputs) {
+    int32_t* mapr = p.map + (size_t)r * p.kmax;
 #pragma unroll
-  for (int j = 0; j < EU; ++j) {
-    const int f = j * NT + tid;
-    if (f < n) mapr[f] = bkt[j] >= 0 ? (int32_t)meta[bkt[j]] : -1;
+    for (int j = 0; j < EU; ++j) {
+      const int f = j * NT + tid;
+      if (f < n) mapr[f] = bkt[j] >= 0 ? (int32_t)meta[bkt[j]] : -1;
+    }
+    if (tid == 0) {
+      p.cnt[r] = e ? 0 : nu;
+      p.err[r] = e;
+    }
   }
-  if (tid == 0) {
-    p.cnt[r] = e ? 0 : nu;
-    p.err[r] = e;
+  nu_out = e ? 0 : nu;
+  err_out = e;
+  return true;
+}
+
+__global__ void __launch_bounds__(NT) union_kernel(UnionParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int nu;
+  uint32_t err;
+  union_build(p, smem, blockIdx.x, p.uni + (size_t)blockIdx.x * p.kmax, true, nu, err);
+}
+
+// Speculative rows in one launch (hs_resolve_rows, where its LDS fits): every workgroup of the
+// request builds the union of the rows in its own LDS (union_build), resolves it with the list
+// read from LDS (resolve_body<.., SL>), and workgroup 0 then gives the rows their slots.
+// Against the union kernel followed by resolve_union_kernel: one launch fewer, and the union
+// list does not go through global memory.  LDS (rows_lds): the union's table, the list then in
+// its first 4 kmax bytes; RESOLVE's carve-up from byte rows_ulist_bytes(kmax) on, once the
+// union is built.
+template <int E, int KE>
+__global__ void __launch_bounds__(NT) resolve_rows_kernel(ResolveParams p, UnionParams u) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
+  int nu = 0;
+  uint32_t uerr = 0;
+  if (!union_build(u, smem, r, (int32_t*)smem, g == 0, nu, uerr)) {
+    // a padded request: untouched, and an empty plan so a replay copies nothing
+    if ((p.flags & HS_RECORD_PLAN) && g == 0 && threadIdx.x == 0) p.ctrl[r * 4 + 2] = 0;
+    return;
   }
+  __syncthreads();  // the union list is complete; the rest of the union's LDS is free
+  ReqScalars rs;
+  rs.nreq = INT32_MAX;  // (a request past *num_reqs returned above)
+  rs.kvr = nu;
+  rs.pre_err = uerr;
+  const int32_t* ul = (const int32_t*)smem;
+  unsigned char* rsm = smem + rows_ulist_bytes(p.k);
+  if (nu <= kUnionShortKE * NT) resolve_body<E, kUnionShortKE, false, true>(p, rsm, rs, ul);
+  else resolve_body<E, KE, false, true>(p, rsm, rs, ul);
+  // (every return in resolve_body is taken by the whole workgroup, so all its threads are here)
+  if (g != 0) return;
+  rows_scatter(p, r, uerr, true);
 }
 
 // Slots of the union back to every (row, entry): out[r][f] = union slot of entry f.
@@ -1257,6 +1316,26 @@ hipError_t launch_union_resolve(const ResolveParams& p, size_t lds, hipStream_t 
   return hipErrorInvalidValue;
 }
 
+template <int E, int KE>
+hipError_t launch_rows_e(const ResolveParams& p, const UnionParams& u, size_t lds, hipStream_t s,
+                         const KernelTiming* tm) {
+  if (tm && tm->start) {
+    hipExtLaunchKernelGGL((resolve_rows_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), (uint32_t)lds, s, tm->start,
+                          tm->stop, 0u, p, u);
+  } else {
+    hipLaunchKernelGGL((resolve_rows_kernel<E, KE>), dim3(p.R * p.G), dim3(NT), lds, s, p, u);
+  }
+  return hipGetLastError();
+}
+template <int E>
+hipError_t launch_rows(const ResolveParams& p, const UnionParams& u, size_t lds, hipStream_t s, int KE,
+                       const KernelTiming* tm) {
+  static_assert(E >= 8, "a union longer than kUnionShortKE NT entries");
+  if (KE <= 8) return launch_rows_e<E, 8>(p, u, lds, s, tm);
+  if constexpr (E >= 16) return launch_rows_e<E, 16>(p, u, lds, s, tm);
+  return hipErrorInvalidValue;
+}
+
 // The fused variant exists for KE <= 4 and E <= 8 (top_k <= 4096, B <= 8192): larger lists
 // leave no LDS for the record tile.
 constexpr int kFusedMaxE = 8, kFusedMaxKE = 4;
@@ -1293,6 +1372,8 @@ hipError_t set_limit_ke(int v) {
   if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 16, false>, v);
   if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_union_kernel<E, 8>, v);
   if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_union_kernel<E, 16>, v);
+  if constexpr (E >= 8) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_rows_kernel<E, 8>, v);
+  if constexpr (E >= 16) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_rows_kernel<E, 16>, v);
   if constexpr (E <= kFusedMaxE) {
     if constexpr (E >= 1) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 1, true>, v);
     if constexpr (E >= 2) if (e == hipSuccess) e = set_dynamic_lds((const void*)resolve_kernel<E, 2, true>, v);
@@ -1378,6 +1459,17 @@ hipError_t launch_resolve(const ResolveParams& p, size_t lds_bytes, hipStream_t 
   c.uout = p.out; c.map = p.rows_map; c.err = p.kerr; c.num_reqs = p.num_reqs; c.out = p.rows_out; c.R = p.R;
   c.n = p.rows_n; c.kmax = p.k;
   return launch_scatter(c, s);
+}
+
+hipError_t launch_resolve_rows(const ResolveParams& p, const UnionParams& u, size_t lds_bytes, hipStream_t s,
+                               const KernelTiming* tm) {
+  const int KE = pow2_at_least((p.k + NT - 1) / NT);
+  if (!p.rows_out || KE <= kUnionShortKE) return hipErrorInvalidValue;
+  switch (resolve_elems_per_thread(p.k, p.B)) {
+    case 8: return launch_rows<8>(p, u, lds_bytes, s, KE, tm);
+    case 12: return launch_rows<12>(p, u, lds_bytes, s, KE, tm);
+    default: return launch_rows<16>(p, u, lds_bytes, s, KE, tm);
+  }
 }
 
 bool fused_supported(int k, int B) {

@@ -134,6 +134,38 @@ int main() {
     CHECK(union_lds_bytes(bits) >= (size_t(8) << bits) + 4 * (size_t(kUnionMaxEntries / NT) * NW + 1),
           "union rank counts");
   }
+  // the one-launch rows kernel: for every union capacity past kUnionShortKE entries per thread
+  // and every buffer size, where its LDS fits (the library takes it only then), the union list
+  // (4 kmax bytes) lies inside the union table's position array (4 H bytes, H >= 2 kmax), which
+  // is dead once the list is written, and RESOLVE's carve-up starts after the list
+  for (int kmax : {4097, 6144, 8192})
+    for (int B : Bs) {
+      if (B < kmax) continue;
+      for (int G = 1; G <= 33; ++G) {
+        int ubits = 6;
+        while ((size_t(1) << ubits) < 2 * size_t(kmax)) ++ubits;
+        int rbits = 6;
+        while ((size_t(1) << rbits) < 4 * size_t(kmax)) ++rbits;
+        for (int b = rbits - 1; b <= rbits; ++b) {
+          const size_t lds = rows_lds(kmax, B, b, G, ubits);
+          if (lds > kLdsMax) continue;
+          CHECK(rows_ulist_bytes(kmax) >= 4 * size_t(kmax) && rows_ulist_bytes(kmax) % 16 == 0 &&
+                    rows_ulist_bytes(kmax) <= (size_t(4) << ubits),
+                "rows list kmax %d", kmax);
+          CHECK(lds >= rows_ulist_bytes(kmax) + resolve_lds(kmax, B, b, G).total && lds >= union_lds_bytes(ubits),
+                "rows LDS kmax %d B %d G %d", kmax, B, G);
+          check_resolve(kmax, B, b, G);
+        }
+      }
+    }
+  {
+    // the pages' default shape takes the one-launch kernel: 4 rows of 2048 into B = 5 k, 32
+    // workgroups, with the table size the library picks (4 kmax entries, or 2 kmax when short)
+    int b = 15;
+    if (resolve_lds(8192, 10240, b, 32).total > kLdsMax) --b;
+    const size_t lds = rows_lds(8192, 10240, b, 32, 14);
+    CHECK(lds <= kLdsMax, "rows kernel LDS %zu at 4 x 2048 into B 10240", lds);
+  }
   // the fused kernel: the fetch workgroups' tile, query rows and scratch
   for (int f8 = 0; f8 < 2; ++f8) {
     const FusedLds F = fused_lds(2048, 4096, 13, 33, 1, f8 != 0);
