@@ -204,8 +204,10 @@ hs_status hs_resolve(hs_handle h, int32_t layer, const int32_t* d_sel, const int
  *   d_slots_out  device [R][rows][top_k] int32, the slot of every (row, entry)
  *   other arguments as hs_resolve.  A duplicate inside a row sets HS_ERR_DUP (nothing
  *   changes); repeats across rows are the point and are not errors.
- * Two kernel launches on `stream`: the union, then the RESOLVE of the union, which also
- * writes every row's slots (a third launch writes them when rows x top_k <= 4096); the union
+ * Kernel launches on `stream`: when verify_rows x top_k > 4096 and the configuration's LDS
+ * allows it, one (every workgroup builds the union in its own LDS, resolves it, and writes
+ * every row's slots); otherwise the union, then the RESOLVE of the union, which also writes
+ * every row's slots (a third launch writes them when verify_rows x top_k <= 4096).  The union
  * scratch is per handle, so calls on one handle must be ordered on one stream.
  */
 hs_status hs_resolve_rows(hs_handle h, int32_t layer, int32_t rows, const int32_t* d_sel,
