@@ -173,6 +173,79 @@ def test_duplicate_inside_a_row_is_an_error_repeats_across_rows_are_not():
     c.close()
 
 
+def test_one_launch_errors_and_padded_requests():
+    """The one-launch rows kernel (3 rows of k 2048 into B 8192: the union's capacity needs more
+    than 4 list entries per thread and its LDS fits): a duplicate inside a row and a position
+    out of range make only their request's rows -1 with the error and leave its state alone;
+    repeats across rows share slots; a request past num_reqs is untouched.  Every other request's
+    slots and counts against the oracle, 8 steps, and the state at the end."""
+    R, k, B, rows = 3, 2048, 8192, 3
+    lmax = 65536
+    cfg = hk.make_config(R, 1, lmax, k, B, verify_rows=rows)
+    c = hk.HiSparse(cfg)
+    for r in range(R):
+        synth.fill_request(c.host_pool_address(r), r, 1, lmax, lmax)
+    caches = [oracle.Cache(B, lmax, 1152) for _ in range(R)]
+    rng = np.random.default_rng(7)
+    dev = torch.device("cuda")
+    out = torch.full((R, rows, k), -7, dtype=torch.int32, device=dev)
+    st = torch.zeros((R, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
+    ctx = torch.full((R,), lmax, dtype=torch.int32, device=dev)
+    prev = [rng.choice(lmax, k, replace=False) for _ in range(R)]
+    n_err = n_ok = n_pad = 0
+    for step in range(8):
+        nreq = R - 1 if step in (3, 6) else R  # request 2 padded in two steps
+        sel = np.empty((R, rows, k), np.int32)
+        for r in range(R):
+            for q in range(rows):
+                row = prev[r].copy()
+                fresh = rng.choice(lmax, k, replace=False)
+                keep = rng.random(k) < 0.8
+                cand = np.where(keep, row, -1)
+                used = set(int(x) for x in cand if x >= 0)
+                fi = iter(int(x) for x in fresh if int(x) not in used)
+                sel[r, q] = [int(x) if x >= 0 else next(fi) for x in cand]
+                prev[r] = sel[r, q].copy()
+        if step % 3 == 1:
+            sel[1, 2, 5] = sel[1, 2, 9]        # a duplicate inside row 2 of request 1
+        if step % 3 == 2:
+            sel[0, 1, 100] = lmax + 3          # a position out of range in request 0
+        d_nr = torch.tensor([nreq], dtype=torch.int32, device=dev)
+        out.fill_(-7)
+        before = out.clone()
+        hk.hs_resolve_rows(c.h, 0, rows, torch.from_numpy(sel).cuda().data_ptr(), ctx.data_ptr(), out.data_ptr(),
+                           st.data_ptr(), d_nr.data_ptr(), 0, 0)
+        torch.cuda.synchronize()
+        got, s = out.cpu().numpy(), st.cpu().numpy()
+        for r in range(R):
+            if r >= nreq:
+                assert np.array_equal(got[r], before[r].cpu().numpy()), (step, r)  # untouched
+                n_pad += 1
+                continue
+            try:
+                ref = caches[r].resolve_rows(sel[r], lmax, c.host_pool(r)[0])
+            except oracle.OracleError as e:
+                assert s[r, 2] == e.code and (got[r] == -1).all(), (step, r, s[r])
+                n_err += 1
+                continue
+            assert s[r, 2] == 0 and s[r, 0] == ref[1] and s[r, 1] == ref[2], (step, r, s[r], ref[1:3])
+            assert np.array_equal(got[r], ref[0]), (step, r)
+            n_ok += 1
+    assert n_err >= 4 and n_ok >= 12 and n_pad == 2, (n_err, n_ok, n_pad)
+    # the state at the end: slot maps and LRU orders against the oracle (a failed step changed nothing)
+    sp = torch.empty((R, B), dtype=torch.int32, device=dev)
+    lru = torch.empty((R, B), dtype=torch.int32, device=dev)
+    nw = torch.empty((R,), dtype=torch.int32, device=dev)
+    hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), 0, nw.data_ptr(), 0)
+    torch.cuda.synchronize()
+    sp, lru = sp.cpu().numpy(), lru.cpu().numpy()
+    for r in range(R):
+        ex = caches[r].export()
+        assert np.array_equal(sp[r], ex["slot_pos"]), ("slot_pos", r)
+        assert np.array_equal(lru[r], ex["lru"]), ("lru", r)
+    c.close()
+
+
 def test_rows_refused_without_verify_rows():
     cfg = hk.make_config(1, 1, 1024, 64, 128)
     c = hk.HiSparse(cfg)
