@@ -216,11 +216,41 @@ __device__ __forceinline__ ReqScalars read_req_scalars(const ResolveParams& p, i
 // new position) and a per-request header, and the finish kernel that follows applies the
 // page-table updates and copies the missed records, which the fetch workgroups staged, into
 // their victim slots.  So the page table does not change while the fused kernel runs.
+// A request's metadata that RESOLVE reads first (the launch counter, the request's scalars, the
+// LRU order's two halves, its host records' base), loaded by resolve_rows_kernel before it builds
+// the union so that the loads land during that LDS work (resolve_body issues the same loads
+// itself otherwise).
+template <int E>
+struct EntryLoads {
+  uint64_t counter_raw;  // thread 0 only
+  uint32_t short_req;
+  int32_t newest, capr;
+  int64_t ctx;
+  Run16<E> lra, lrb;
+  const uint8_t* hbase;
+};
+template <int E>
+__device__ __forceinline__ void entry_loads(const ResolveParams& p, int r, EntryLoads<E>& en) {
+  const int e0 = (int)threadIdx.x * E;
+  const bool bvec = (p.B % 4) == 0;
+  en.counter_raw = 0;
+  if (threadIdx.x == 0)
+    en.counter_raw = __hip_atomic_load((uint64_t*)&p.ctrl[r * 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  en.short_req = p.ctrl[r * 4 + 3];
+  en.newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
+  en.ctx = min((int64_t)p.ctx_len[r], p.max_positions);
+  en.capr = p.cap ? p.cap[r] : p.B;
+  load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, p.Bpad, e0, bvec, en.lra, 0);
+  load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, p.Bpad, e0, bvec, en.lrb, 0);
+  en.hbase = p.host_base[r] + p.host_layer_off;
+}
+
 // SL: the list is in LDS (sl: kr positions; the rows' union built by resolve_rows_kernel), not
 // in global memory.
+// pre (with SL): the entry loads, already issued (entry_loads).
 template <int E, int KE, bool ATT, bool SL = false>
 __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned char* smem, const ReqScalars& rs,
-                                             const int32_t* sl = nullptr) {
+                                             const int32_t* sl = nullptr, const EntryLoads<E>* pre = nullptr) {
   const ResolveLds Ly = resolve_lds(p.k, p.B, p.hash_bits, p.G);
   int32_t* htab = (int32_t*)(smem + Ly.htab);        // [H] list index of the entry in each bucket
   int32_t* selp = (int32_t*)(smem + Ly.selp);        // [k] position (hash key) of each entry
@@ -281,12 +311,22 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   // issued.
   uint64_t* counter = (uint64_t*)&p.ctrl[r * 4];
   uint64_t counter_raw = 0;
-  if (tid == 0) counter_raw = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t short_req = p.ctrl[r * 4 + 3];
-  const int32_t newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
-  const int64_t ctx = min((int64_t)p.ctx_len[r], p.max_positions);
-  // LRU slots backed by device memory (an on-demand hot buffer grows with the request)
-  const int32_t capr = p.cap ? p.cap[r] : p.B;
+  uint32_t short_req;
+  int32_t newest, capr;  // capr: LRU slots backed by device memory (an on-demand hot buffer grows)
+  int64_t ctx;
+  if constexpr (SL) {
+    counter_raw = pre->counter_raw;
+    short_req = pre->short_req;
+    newest = pre->newest;
+    ctx = pre->ctx;
+    capr = pre->capr;
+  } else {
+    if (tid == 0) counter_raw = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    short_req = p.ctrl[r * 4 + 3];
+    newest = (p.flags & kHasNewest) ? p.newest[r] : -1;
+    ctx = min((int64_t)p.ctx_len[r], p.max_positions);
+    capr = p.cap ? p.cap[r] : p.B;
+  }
   const int32_t* selr = p.sel + (size_t)r * p.kb;
   const uint64_t* ptr = p.page_table + (size_t)r * p.max_positions;
   int32_t raw[KE];
@@ -336,10 +376,17 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
       load_run32<E>(p.slot_pos + ((size_t)r * 2 + 1) * p.B, p.B, e0, bvec, spb, -1);
     }
   }
-  load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, p.Bpad, e0, bvec, lra, 0);
-  load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, p.Bpad, e0, bvec, lrb, 0);
   // this (request, layer)'s host records (the pointer table is read at entry with the rest)
-  const uint8_t* hbase = p.host_base[r] + p.host_layer_off;
+  const uint8_t* hbase;
+  if constexpr (SL) {
+    lra = pre->lra;
+    lrb = pre->lrb;
+    hbase = pre->hbase;
+  } else {
+    load_run16<E>(p.lru + ((size_t)r * 2 + 0) * p.Bpad, p.B, p.Bpad, e0, bvec, lra, 0);
+    load_run16<E>(p.lru + ((size_t)r * 2 + 1) * p.Bpad, p.B, p.Bpad, e0, bvec, lrb, 0);
+    hbase = p.host_base[r] + p.host_layer_off;
+  }
   uint8_t* dbase = p.hot + (size_t)r * p.hot_req_stride + p.hot_layer_off;
   // fused: workgroup 0's report to the finish kernel
   uint32_t* hdr = ATT ? p.att_hdr + (size_t)r * 4 : nullptr;
@@ -1243,6 +1290,8 @@ template <int E, int KE>
 __global__ void __launch_bounds__(NT) resolve_rows_kernel(ResolveParams p, UnionParams u) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int r = blockIdx.x % p.R, g = blockIdx.x / p.R;
+  EntryLoads<E> en;
+  entry_loads<E>(p, r, en);  // (they land while the union is built)
   int nu = 0;
   uint32_t uerr = 0;
   if (!union_build(u, smem, r, (int32_t*)smem, g == 0, nu, uerr)) {
@@ -1257,8 +1306,8 @@ __global__ void __launch_bounds__(NT) resolve_rows_kernel(ResolveParams p, Union
   rs.pre_err = uerr;
   const int32_t* ul = (const int32_t*)smem;
   unsigned char* rsm = smem + rows_ulist_bytes(p.k);
-  if (nu <= kUnionShortKE * NT) resolve_body<E, kUnionShortKE, false, true>(p, rsm, rs, ul);
-  else resolve_body<E, KE, false, true>(p, rsm, rs, ul);
+  if (nu <= kUnionShortKE * NT) resolve_body<E, kUnionShortKE, false, true>(p, rsm, rs, ul, &en);
+  else resolve_body<E, KE, false, true>(p, rsm, rs, ul, &en);
   // (every return in resolve_body is taken by the whole workgroup, so all its threads are here)
   if (g != 0) return;
   rows_scatter(p, r, uerr, true);
