@@ -671,11 +671,12 @@ __device__ __forceinline__ void resolve_body(const ResolveParams& p, unsigned ch
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int wtotal = mw * C;  // 16-byte chunks of this wave's misses
-  // With 8 list entries or 16 slots per thread, or 12 slots and 4 entries, these registers
-  // would not last through stage 3 (the compiler then waits for each load and spills its
-  // value), so those layouts load none early; 12 slots with at most 2 entries load 2 chunks per
-  // lane early (their registers fit).
-  constexpr int kEarlyN = (KE >= 8 || E >= 16 || (E >= 12 && KE >= 4)) ? 0 : (E >= 12 ? 2 : kEarly);
+  // With 8 list entries or 16 slots per thread these registers would not last through stage 3
+  // (the compiler then waits for each load and spills its value), so those layouts load none
+  // early; 12 slots with at most 2 entries load 2 chunks per lane early (their registers fit).
+  // 12 slots and 4 entries load one chunk early when the entries come from the union list in
+  // LDS (the position registers of the list are free by then; measured faster), none otherwise.
+  constexpr int kEarlyN = (KE >= 8 || E >= 16) ? 0 : (E >= 12 ? (KE >= 4 ? (SL ? 1 : 0) : 2) : kEarly);
   u32x4 early[kEarlyN > 0 ? kEarlyN : 1];
 #pragma unroll
   for (int u = 0; u < kEarlyN; ++u) {
