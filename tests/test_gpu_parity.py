@@ -71,6 +71,72 @@ def test_example_a_through_the_c_abi(golden):
     c.close()
 
 
+NEWEST_IN_LRU = [([[1, 2], [2, 3], [1, 2]], [None, 2, 2]),
+                 ([[0, 1, 2], [2, 4, 5], [5, 0, 2]], [None, 2, 5])]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("seqs,newest,B", [(s, n, B) for s, n in NEWEST_IN_LRU for B in (2, 3, 4, 6)
+                                           if B >= len(s[0])])
+def test_newest_position_also_in_an_lru_slot(seqs, newest, B, fused):
+    """The corner case the pages leave open ("HiSparse 深度解析" (gentlecold.top) §3.4, §5.2
+    name the reserved newest slot but not a newest position that an LRU slot already holds):
+    a write-through of such a position.  Reading, as in the oracle: slot B serves it and the
+    LRU slot holding it counts as not selected (evictable).  Slots, hit/miss counts, slot
+    map, LRU order and page table through the C ABI against the oracle after every step; through
+    the fused call also the attention over the published slots against float64 attention."""
+    k = len(seqs[0])
+    U, lmax = 9, 16
+    cfg = hk.make_config(1, 1, lmax, k, B, newest_slot=True)
+    c = hk.HiSparse(cfg)
+    synth.fill_request(c.host_pool_address(0), 0, 1, lmax, lmax)
+    host = np.stack([synth.record(0, 0, q) for q in range(lmax)])
+    oc = oracle.Cache(B, lmax, synth.RECORD_BYTES, newest_slot=True)
+    dev = torch.device("cuda")
+    out = torch.empty((1, k), dtype=torch.int32, device=dev)
+    st = torch.zeros((1, hk.HS_STATS_WORDS), dtype=torch.int32, device=dev)
+    d_ctx = torch.tensor([U], dtype=torch.int32, device=dev)
+    sp = torch.empty((1, B), dtype=torch.int32, device=dev)
+    lru = torch.empty((1, B), dtype=torch.int32, device=dev)
+    pt = torch.empty((1, lmax), dtype=torch.int32, device=dev)
+    att = torch.empty((1, 16, 512), dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    for t, sel in enumerate(seqs):
+        log("newest-in-LRU case B=%d fused=%d step %d sel %s newest %s" % (B, fused, t, sel, newest[t]))
+        if newest[t] is not None:
+            oc.append(newest[t], host[newest[t]], None)
+            rec = torch.from_numpy(synth.records_at(1, 1, [newest[t]])).to(dev)
+            pos = torch.tensor([newest[t]], dtype=torch.int32, device=dev)
+            hk.hs_writeback(c.h, rec.data_ptr(), pos.data_ptr(), 0, side.cuda_stream)
+        o, hits, misses, _, _ = oc.resolve(np.asarray(sel, np.int32), U, host)
+        d_sel = torch.tensor([sel], dtype=torch.int32, device=dev)
+        if fused:
+            q = synth.queries(1, 1, t)[0, 0]
+            d_q = torch.from_numpy(q.view(np.int16).copy()).to(dev)
+            hk.hs_resolve_attn(c.h, 0, d_sel.data_ptr(), d_ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0,
+                               d_q.data_ptr(), 16, 512, att.data_ptr(), SCALE, 0)
+        else:
+            hk.hs_resolve(c.h, 0, d_sel.data_ptr(), d_ctx.data_ptr(), out.data_ptr(), st.data_ptr(), 0, 0, 0)
+        hk.hs_export_state(c.h, 0, sp.data_ptr(), lru.data_ptr(), pt.data_ptr(), 0, 0)
+        torch.cuda.synchronize()
+        stats = st.cpu().numpy()[0].tolist()
+        assert out.cpu().numpy()[0].tolist() == o.tolist(), (t, sel)
+        assert stats[:3] == [hits, misses, 0], (t, stats)
+        e = oc.export()
+        assert sp.cpu().numpy()[0].tolist() == e["slot_pos"].tolist(), t
+        assert lru.cpu().numpy()[0].tolist() == e["lru"].tolist(), t
+        assert pt.cpu().numpy()[0].tolist() == oc.page_table.tolist(), t
+        hot = c.hot[0, 0].cpu().numpy()
+        for i, s_ in enumerate(o.tolist()):
+            assert np.array_equal(hot[s_], host[sel[i]]), (t, i, s_)
+        if fused:
+            K = oracle.attention.bf16_to_f64(np.ascontiguousarray(host[sel]).view(np.uint16))
+            ref = oracle.attention.sparse_decode_attention_rows(q, K, SCALE)
+            got = att.cpu().numpy()[0]
+            assert np.abs(got - ref).max() <= 2e-3 * np.abs(ref).max(), t
+    c.close()
+
+
 # ---- the workloads ---------------------------------------------------------------------
 
 @pytest.mark.parametrize("B,wgs", [(64, 1), (100, 3), (128, 0), (128, 7), (256, 2)])
