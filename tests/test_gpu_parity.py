@@ -322,6 +322,26 @@ def test_padded_requests_are_untouched():
     p.close()
 
 
+@pytest.mark.parametrize("mode", ["resolve", "fused", "rows"])
+def test_empty_batch_changes_nothing(mode):
+    """A device request count of 0 (a captured batch with every request padded, gentlecold.top
+    §5.5) leaves every request as it was, through hs_resolve, hs_resolve_attn and
+    hs_resolve_rows, the write-through of that step aside; the steps after it match the
+    oracle, which skips that step for every request."""
+    w = W["tiny"].scaled(R=3, steps=6, B=192 if mode == "rows" else 128)  # rows: B >= 3 k
+    kw = {"fused": {"fused_heads": 16}, "rows": {"rows": 3}}.get(mode, {})
+    p = Pair(w, wgs=2, **kw)
+    log("empty batch through %s" % mode)
+    p.step_gpu_and_oracle()
+    p.step_gpu_and_oracle()
+    p.step_gpu_and_oracle(num_reqs=0)
+    p.check_state()
+    for _ in range(3):
+        p.step_gpu_and_oracle()
+    p.check_state()
+    p.close()
+
+
 def test_skip_io_moves_metadata_not_bytes():
     """The timing aid (gentlecold.top §4.4 no-IO oracle): same metadata, no record bytes."""
     w = W["tiny"]
