@@ -26,8 +26,8 @@
  *     hs_stats.error; they are never read back by the library.
  *   - The caller owns the hot buffer, the workspace and all streams; the
  *     library owns the pinned host pool and its events.
- *   - Positions and slot indices are int32.  B <= 32767, top_k <= 16384,
- *     max_positions < 2^31, record_bytes a multiple of 16.
+ *   - Positions and slot indices are int32.  top_k <= B <= 16384 (top_k <= 8192 in
+ *     practice: see hs_create), max_positions < 2^31, record_bytes a multiple of 16.
  *   - A handle may be used from one host thread at a time.
  */
 #ifndef HISPARSE_H
@@ -129,7 +129,10 @@ size_t hs_workspace_bytes(const hs_config* cfg);
  * Allocates the pinned host pool, one allocation per request of
  * [L][max_positions][record_bytes] ([NJ] §2.1: contiguous by (request, layer,
  * position)).  The caller fills it with the prefill records (hs_host_pool)
- * before the first hs_resolve.  Returns HS_ENOMEM when pinning fails.
+ * before the first hs_resolve.  Returns HS_ENOMEM when pinning fails, HS_EINVAL when a
+ * workgroup's LDS cannot hold RESOLVE's tables (the selection's hash of >= 2 top_k buckets,
+ * its positions and the slot owners): with MI355X's 160 KB per workgroup that is any
+ * top_k above 8192, whatever B.
  */
 hs_status hs_create(const hs_config* cfg, void* d_hot, void* d_workspace, hs_handle* out);
 

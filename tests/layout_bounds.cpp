@@ -102,7 +102,7 @@ int main() {
   // top_k and buffer sizes the library takes (k <= 16384 with B >= k; speculative unions up to
   // kUnionMaxEntries entries), workgroups per request 1 .. 32, hash sizes from a half-full
   // table up (the library picks 4k entries, or 2k when LDS is short)
-  const int ks[] = {1, 2, 3, 64, 100, 513, 1000, 2048, 2650, 4096, 5000, 8192};
+  const int ks[] = {1, 2, 3, 64, 100, 513, 1000, 2048, 2650, 4096, 5000, 8192, 12000, 16384};
   const int Bs[] = {2, 3, 4, 6, 8, 64, 128, 1040, 2048, 4096, 5120, 8192, 10240, 12000, 12288, 16384};
   long fits = 0;
   for (int k : ks)

@@ -526,8 +526,9 @@ def test_duplicates_in_many_patterns_then_valid_steps():
                                           (4096, 4096, 0.6, 0), (6000, 3000, 0.6, 0)])
 def test_large_lists_and_buffers(B, k, keep, wgs):
     """Large buffers and lists in the kernel's blocked layout: B = 12000 (12 slots per thread),
-    B = 16384 (16 slots per thread) with 2 and 8 list entries per thread, and lists of 4096 and
-    3000 entries (4 per thread) into B = 4096 and 6000.  The list of 8192 fills its buffer at
+    B = 16384 (16 slots per thread) with 2 and 8 list entries per thread (B = 16384 and
+    top_k = 8192 are the largest the library takes on this device), and lists of 4096 and 3000
+    entries (4 per thread) into B = 4096 and 6000.  The list of 8192 fills its buffer at
     the third step and then evicts (with the default 32 workgroups per request: at 2, each
     wave's miss list would have to hold half the list, more LDS than a workgroup has); so do
     the lists of 4096 and 3000.  State compared after every step."""
@@ -538,7 +539,18 @@ def test_large_lists_and_buffers(B, k, keep, wgs):
         p.check_state()
     if k >= 3000:
         assert p.evicted > 0, p.evicted
+    log("B=%d k=%d: occupied slots evicted %d" % (B, k, p.evicted))
     p.close()
+
+
+@pytest.mark.parametrize("k", [8256, 16384])
+def test_top_k_beyond_the_lds_is_refused(k):
+    """A top_k whose RESOLVE tables do not fit a workgroup's 160 KB of LDS (above 8192) is
+    refused by hs_create with HS_EINVAL and a message naming the bytes; nothing is launched."""
+    cfg = hk.make_config(1, 1, 65536, k, 16384)
+    with pytest.raises(hk.HsError) as e:
+        hk.HiSparse(cfg)
+    assert e.value.code == hk.HS_EINVAL and "LDS" in str(e.value), str(e.value)
 
 
 def test_graph_capture_replays_match_oracle():
